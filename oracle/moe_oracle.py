@@ -1,0 +1,432 @@
+"""CPU oracle for the sparse Mixture-of-Experts layer forward pass.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or
+execute this module: only the test-suite, the smoke check of the package entry
+file and the CPU-baseline leg of the benchmark use it. It shares no code with
+the HIP library; both receive the same seeded inputs from the input generator.
+
+Plain numpy. Arithmetic is float64, except where the pages fix the precision:
+the router works in float32 ("Router Precision: force float32 for the softmax",
+MoE From Scratch to DeepSeek V3, stability tricks; also the fp32-gating advice
+in the Moe(Mixtrue of Experts) survey, stability section), so router logits are
+float32 values and the top-k decision is taken on float32 keys. Library
+primitives used as steps: matrix product, stable argsort, bincount, erf.
+
+What is computed (one MoE layer forward, token choice):
+  h(x) = x . W_g (+ b_g)                       router logits
+  p = softmax(h)  or  s = sigmoid(h)           score function
+  top-k by key, gates renormalised over the k selected scores
+  capacity-limited dispatch in k-major, token-ascending queue order
+  E_e(x) = W2[e] act(W1[e] x + b1[e]) + b2[e]  (SwiGLU: W2[e](silu(W1 x) * W3 x))
+  y[t] = sum_j kept * g[t,j] * E_{i_j}(x_t)  (+ shared expert output)
+  L_aux = E * sum_i f_i * P_i,  z = mean_t logsumexp(h_t)^2
+
+Readings of the pages (where they are silent or ambiguous) are marked READING
+in the function that takes them. Every function here is pinned by a CPU test
+against values the pages print, closed forms, brute force or library routines.
+"""
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+from typing import Dict, Optional
+
+import numpy as np
+from scipy.special import erf as _erf
+
+F64 = np.float64
+F32 = np.float32
+
+
+# --------------------------------------------------------------------------
+# Capacity
+# --------------------------------------------------------------------------
+def capacity(tokens: int, num_experts: int, top_k: int, capacity_factor: float,
+             min_capacity: int, drop_tokens: bool) -> Optional[int]:
+    """Per-expert capacity, or None when there is no limit.
+
+    MoE Training Guide, "Core MoE Parameters" items 4-7: capacity is
+    (tokens / num_experts) x capacity_factor, at least min_capacity, and
+    disabling token dropping removes the limit.
+    READING: "tokens" counts the T*k token-expert assignments (with T alone a
+    top-2 layer at factor 1.25 would drop >= 37.5% under perfect balance, which
+    the guide's "no dropping at 2.0" and "< 5% drop rate" contradict), and the
+    quotient is rounded up. The factor is taken at its exact binary value.
+    """
+    if not drop_tokens:
+        return None
+    c = math.ceil(Fraction(capacity_factor) * (top_k * tokens) / num_experts)
+    return max(int(min_capacity), int(c))
+
+
+# --------------------------------------------------------------------------
+# Router
+# --------------------------------------------------------------------------
+def router_logits(x, w_gate, b_gate=None) -> np.ndarray:
+    """h(x) = x . W_g (+ b_g), W_g stored [E, d] as nn.Linear stores it.
+
+    MoE From Scratch to DeepSeek V3, token-choice formula (score h(x) = x W_g);
+    MoE Training: Mixture of Experts, "Basic MoE Architecture" (gate is an
+    nn.Linear, with bias). Accumulated in float64, delivered as float32: the
+    router's working precision.
+    """
+    h = np.asarray(x, F64) @ np.asarray(w_gate, F64).T
+    if b_gate is not None:
+        h = h + np.asarray(b_gate, F64)[None, :]
+    return h.astype(F32)
+
+
+def softmax_scores(logits) -> tuple:
+    """p = softmax over the expert axis, and the per-token logsumexp.
+
+    MoE From Scratch to DeepSeek V3, gating p = Softmax(h(x)); the survey's
+    summaries normalise along the expert dimension. Returns (p, lse) in float64
+    computed from the float32 logits.
+    """
+    h = np.asarray(logits, F64)
+    m = h.max(axis=1, keepdims=True)
+    e = np.exp(h - m)
+    s = e.sum(axis=1, keepdims=True)
+    return e / s, (m + np.log(s))[:, 0]
+
+
+def logsumexp(logits) -> np.ndarray:
+    """log(sum_e exp(h_e)) per token (router z-loss argument)."""
+    return softmax_scores(logits)[1]
+
+
+def sigmoid_scores(logits) -> np.ndarray:
+    """s = 1 / (1 + exp(-h)) per expert (DeepSeek V3 sigmoid routing)."""
+    h = np.asarray(logits, F64)
+    return 1.0 / (1.0 + np.exp(-h))
+
+
+def selection_keys(logits, score_fn: str, e_bias=None) -> np.ndarray:
+    """The float32 value each token ranks experts by.
+
+    softmax: top-k of p equals top-k of the logits because softmax is strictly
+    increasing in each logit, so the key is the float32 logit itself (the
+    Switch top-1 rule also selects on logits: MoE Training: Mixture of Experts,
+    "2. Routing Mechanisms").
+    sigmoid: key = s + b_i with the selection bias b_i (MoE From Scratch to
+    DeepSeek V3, auxiliary-loss-free balancing, Score_i = x e_i + b_i).
+    READING: the bias is added to the sigmoid score (not the raw logit) and the
+    sum is formed in float32, the router's precision: s is the correctly rounded
+    float32 sigmoid, then s + b in float32.
+    """
+    h = np.asarray(logits, F32)
+    if score_fn == "softmax":
+        return h.copy()
+    if score_fn == "sigmoid":
+        s32 = sigmoid_scores(h).astype(F32)
+        b = np.zeros(h.shape[1], F32) if e_bias is None else np.asarray(e_bias, F32)
+        return (s32 + b[None, :]).astype(F32)
+    raise ValueError(score_fn)
+
+
+def top_k(keys, k: int) -> np.ndarray:
+    """Indices of the k largest keys per token, in descending key order.
+
+    torch.topk in the pages' layers (MoE Training: Mixture of Experts, "Basic
+    MoE Architecture"; moe_code.py, MixtureOfExperts.forward step 2).
+    READING: equal keys go to the lower expert index first (torch.topk leaves
+    this open). A stable sort of the negated keys gives exactly that order.
+    """
+    keys = np.asarray(keys)
+    order = np.argsort(-keys, axis=1, kind="stable")
+    return order[:, :k].astype(np.int32)
+
+
+def topk_margin(keys, k: int) -> np.ndarray:
+    """key of the k-th choice minus key of the (k+1)-th (inf when k == E).
+
+    Used by parity tests to set aside tokens whose selection is a near tie.
+    """
+    keys = np.asarray(keys, F64)
+    T, E = keys.shape
+    if k >= E:
+        return np.full(T, np.inf)
+    srt = -np.sort(-keys, axis=1)
+    return srt[:, k - 1] - srt[:, k]
+
+
+def renormalised_gates(scores, idx) -> np.ndarray:
+    """g_j = score_{i_j} / sum_{j'} score_{i_j'} over the k selected experts.
+
+    moe_code.py, MixtureOfExperts.forward step 3, and MoE Training: Mixture of
+    Experts, "Top-2 Routing (Mixtral)": divide the top-k scores by their sum.
+    For the sigmoid router the scores are the unbiased sigmoid values (the
+    selection bias only steers selection). k = 1 gives g = 1 (SwitchMoE).
+    """
+    sel = np.take_along_axis(np.asarray(scores, F64), np.asarray(idx, np.int64), axis=1)
+    return sel / sel.sum(axis=1, keepdims=True)
+
+
+def route(logits, top_k_: int, score_fn: str, e_bias=None) -> Dict[str, np.ndarray]:
+    """Score function, top-k and gates from float32 logits."""
+    keys = selection_keys(logits, score_fn, e_bias)
+    idx = top_k(keys, top_k_)
+    if score_fn == "softmax":
+        scores, lse = softmax_scores(logits)
+    else:
+        scores = sigmoid_scores(logits)
+        lse = logsumexp(logits)
+    gates = renormalised_gates(scores, idx)
+    return dict(keys=keys, idx=idx, gates=gates, scores=scores, lse=lse,
+                margin=topk_margin(keys, top_k_))
+
+
+# --------------------------------------------------------------------------
+# Dispatch (capacity, histogram, expert-sorted order)
+# --------------------------------------------------------------------------
+def dispatch(idx, num_experts: int, cap: Optional[int]) -> Dict[str, np.ndarray]:
+    """Capacity-limited dispatch of the T*k assignments.
+
+    MoE From Scratch to DeepSeek V3, "Token Dropping": once an expert's buffer
+    is full the extra tokens are dropped. MoE Training Guide, "Core MoE
+    Parameters" items 4-7 (capacity, min capacity, no-drop mode).
+    READING: the queue order is k-major then token-ascending (every token's
+    first choice before any second choice), so a higher-ranked choice never
+    loses its slot to a lower-ranked one; a dropped assignment contributes
+    nothing and the surviving gates are not renormalised again.
+
+    Rows of the expert-sorted buffer are ordered by expert, then queue position.
+    Returns counts_pre [E] (picks before capacity), counts_kept [E],
+    expert_offsets [E+1], assign_row [T,k] (row or -1), row_token [R],
+    row_slot [R] (the choice j of each row), pos [T,k], dropped.
+    """
+    idx = np.asarray(idx, np.int64)
+    T, k = idx.shape
+    E = int(num_experts)
+    flat = idx.T.reshape(-1)                       # a = j*T + t
+    A = flat.size
+    counts_pre = np.bincount(flat, minlength=E)[:E]
+    order = np.argsort(flat, kind="stable")        # by expert, then queue order
+    starts = np.cumsum(counts_pre) - counts_pre
+    pos = np.empty(A, np.int64)
+    pos[order] = np.arange(A) - starts[flat[order]]
+    kept = np.ones(A, bool) if cap is None else pos < cap
+    counts_kept = counts_pre.copy() if cap is None else np.minimum(counts_pre, cap)
+    offsets = np.zeros(E + 1, np.int64)
+    offsets[1:] = np.cumsum(counts_kept)
+    row = np.where(kept, offsets[flat] + pos, -1)
+    R = int(offsets[-1])
+    row_token = np.empty(R, np.int64)
+    row_slot = np.empty(R, np.int64)
+    a_kept = np.nonzero(kept)[0]
+    row_token[row[a_kept]] = a_kept % T
+    row_slot[row[a_kept]] = a_kept // T
+    return dict(
+        counts_pre=counts_pre.astype(np.int64),
+        counts_kept=counts_kept.astype(np.int64),
+        expert_offsets=offsets,
+        assign_row=row.reshape(k, T).T.copy(),
+        row_token=row_token,
+        row_slot=row_slot,
+        pos=pos.reshape(k, T).T.copy(),
+        dropped=int(A - R),
+    )
+
+
+# --------------------------------------------------------------------------
+# Experts
+# --------------------------------------------------------------------------
+def gelu(z):
+    """Exact GELU, 0.5 z (1 + erf(z / sqrt 2)): nn.GELU() default, used by the
+    expert FFN in MoE Training: Mixture of Experts, "Basic MoE Architecture"."""
+    return 0.5 * z * (1.0 + _erf(z / math.sqrt(2.0)))
+
+
+def relu(z):
+    """max(z, 0): moe_code.py, class Expert."""
+    return np.maximum(z, 0.0)
+
+
+def silu(z):
+    """z / (1 + exp(-z)), the gate nonlinearity of SwiGLU."""
+    return z / (1.0 + np.exp(-z))
+
+
+def expert_ffn(xr, w1, b1, w2, b2, activation: str, w3=None) -> np.ndarray:
+    """One expert on rows xr [n, d]: W2 act(W1 x + b1) + b2, weights [out, in].
+
+    GELU/ReLU: MoE Training: Mixture of Experts, "Basic MoE Architecture"
+    (Linear(h, 4h), GELU, Linear(4h, h)) and moe_code.py, class Expert
+    (ReLU(x W1 + b1) W2 + b2; its dropout is the identity in a forward
+    evaluation).
+    SwiGLU: three matrices per expert (Moe survey, Mixtral parameter count).
+    READING: H = silu(W1 x) * (W3 x), output W2 H.
+    """
+    xr = np.asarray(xr, F64)
+    W1 = np.asarray(w1, F64)
+    h = xr @ W1.T
+    if b1 is not None:
+        h = h + np.asarray(b1, F64)[None, :]
+    if activation == "gelu":
+        h = gelu(h)
+    elif activation == "relu":
+        h = relu(h)
+    elif activation == "swiglu":
+        u = xr @ np.asarray(w3, F64).T
+        h = silu(h) * u
+    else:
+        raise ValueError(activation)
+    y = h @ np.asarray(w2, F64).T
+    if b2 is not None:
+        y = y + np.asarray(b2, F64)[None, :]
+    return y
+
+
+def experts_forward(x, disp: Dict[str, np.ndarray], params, activation: str) -> np.ndarray:
+    """Y[r] = E_e(x[row_token[r]]) for every kept row r of expert e."""
+    x = np.asarray(x, F64)
+    offsets = disp["expert_offsets"]
+    R = int(offsets[-1])
+    Y = np.zeros((R, x.shape[1]), F64)
+    E = len(offsets) - 1
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        rows = x[disp["row_token"][lo:hi]]
+        Y[lo:hi] = expert_ffn(rows, params["w1"][e], _opt(params.get("b1"), e),
+                              params["w2"][e], _opt(params.get("b2"), e), activation,
+                              _opt(params.get("w3"), e))
+    return Y
+
+
+def _opt(t, e):
+    return None if t is None else t[e]
+
+
+def combine(Y, gates, assign_row, T: int, d: int, y_shared=None) -> np.ndarray:
+    """y[t] = sum_j kept * g[t, j] * Y[assign_row[t, j]] (+ y_shared[t]).
+
+    MoE From Scratch to DeepSeek V3, output y = sum over TopK of Gate_i E_i(x);
+    MoE Training: Mixture of Experts, "Weighted Combination".
+    READING: the layer returns the mixture without the "+ x" residual of the
+    lecture's formula (the page's own layer code adds none; the residual belongs
+    to the transformer block). Shared experts are always active with gate 1
+    (MoE From Scratch to DeepSeek V3, "Shared Experts").
+    """
+    y = np.zeros((T, d), F64)
+    k = assign_row.shape[1]
+    for j in range(k):
+        r = assign_row[:, j]
+        ok = r >= 0
+        y[ok] += np.asarray(gates, F64)[ok, j:j + 1] * Y[r[ok]]
+    if y_shared is not None:
+        y += y_shared
+    return y
+
+
+# --------------------------------------------------------------------------
+# Balance statistics
+# --------------------------------------------------------------------------
+def balance_stats(scores, score_fn: str, lse, counts_pre, counts_kept, T: int, k: int,
+                  E: int) -> Dict[str, float]:
+    """f_i, P_i, L_aux = E sum f_i P_i, z-loss and the monitoring figures.
+
+    MoE Training: Mixture of Experts, "3. Load Balancing": f = bincount of the
+    top-k indices / their number, P = mean softmax probability, aux = E sum f P;
+    router z-loss = mean of logsumexp(logits)^2 (also MoE From Scratch to
+    DeepSeek V3, L_aux = N sum f_i P_i and L_z = log^2 sum e^logit).
+    MoE Training Guide, "Monitoring": load imbalance max/min counts, utilisation
+    (experts with a nonzero count / E), drop rate (dropped / total).
+    READING: f_i counts top-k picks before capacity (so sum f = 1 and uniform
+    routing gives L_aux = 1); for the sigmoid router P_i is the mean of the
+    per-token normalised affinities s_ti / sum_e s_te.
+    """
+    scores = np.asarray(scores, F64)
+    if score_fn == "sigmoid":
+        scores = scores / scores.sum(axis=1, keepdims=True)
+    counts_pre = np.asarray(counts_pre, np.int64)
+    counts_kept = np.asarray(counts_kept, np.int64)
+    A = T * k
+    f = counts_pre / float(A)
+    P = scores.mean(axis=0)
+    lse = np.asarray(lse, F64)
+    kept = int(counts_kept.sum())
+    cmin = int(counts_pre.min())
+    return dict(
+        f=f, P=P, l_aux=float(E * np.sum(f * P)), z_loss=float(np.mean(lse * lse)),
+        kept=kept, dropped=A - kept, drop_rate=(A - kept) / float(A),
+        utilization=float(np.count_nonzero(counts_kept > 0)) / E,
+        imbalance=(float(counts_pre.max()) / cmin) if cmin > 0 else math.inf,
+    )
+
+
+# --------------------------------------------------------------------------
+# Whole layer
+# --------------------------------------------------------------------------
+def forward(x, params, w, logits=None, idx=None) -> Dict[str, object]:
+    """The full layer forward for workload ``w`` (a workloads.Workload-like object).
+
+    ``params`` maps w_gate, b_gate, e_bias, w1, w3, b1, w2, b2 and the shared
+    expert's ws1, ws3, bs1, ws2, bs2 to arrays indexable per expert. ``logits``
+    (float32 [T, E]) may be given to run routing on another implementation's
+    router output; ``idx`` likewise overrides the top-k choice (stage-isolated
+    comparison). Returns every intermediate.
+    """
+    x = np.asarray(x, F64)
+    T, d = x.shape
+    E, k = w.num_experts, w.top_k
+    if logits is None:
+        logits = router_logits(x, params["w_gate"], params.get("b_gate"))
+    r = route(logits, k, w.score_fn, params.get("e_bias"))
+    if idx is not None:
+        idx = np.asarray(idx, np.int32)
+        r["idx"] = idx
+        r["gates"] = renormalised_gates(r["scores"], idx)
+    cap = capacity(T, E, k, w.capacity_factor, w.min_capacity, w.drop_tokens)
+    disp = dispatch(r["idx"], E, cap)
+    Y = experts_forward(x, disp, params, w.activation)
+    y_shared = None
+    if w.num_shared_experts:
+        y_shared = np.zeros((T, d), F64)
+        for s in range(w.num_shared_experts):
+            y_shared += expert_ffn(x, params["ws1"][s], _opt(params.get("bs1"), s),
+                                   params["ws2"][s], _opt(params.get("bs2"), s),
+                                   w.activation, _opt(params.get("ws3"), s))
+    y = combine(Y, r["gates"], disp["assign_row"], T, d, y_shared)
+    stats = balance_stats(r["scores"], w.score_fn, r["lse"], disp["counts_pre"],
+                          disp["counts_kept"], T, k, E)
+    return dict(logits=np.asarray(logits, F32), capacity=cap, y=y, Y=Y, y_shared=y_shared,
+                stats=stats, **r, **disp)
+
+
+# --------------------------------------------------------------------------
+# Parameter and FLOP accounting
+# --------------------------------------------------------------------------
+def ffn_params(d_model: int, d_ff: int, activation: str, bias: bool) -> int:
+    """Parameters of one expert: two d x d_ff matrices (three for SwiGLU).
+
+    moe_code.py, compare_moe_vs_dense (expert = 2 d d_ff, no biases counted);
+    Moe survey, Mixtral count (three matrices per expert).
+    """
+    mats = 3 if activation == "swiglu" else 2
+    n = mats * d_model * d_ff
+    if bias:
+        n += (mats - 1) * d_ff + d_model
+    return n
+
+
+def router_params(d_model: int, num_experts: int, bias: bool) -> int:
+    """Gate parameters: d x E (+ E with a bias)."""
+    return d_model * num_experts + (num_experts if bias else 0)
+
+
+def layer_params(d_model, d_ff, num_experts, top_k, activation, bias=False, gate_bias=False,
+                 num_shared=0) -> Dict[str, int]:
+    """Total and active (per token) parameters of one MoE layer."""
+    fe = ffn_params(d_model, d_ff, activation, bias)
+    rg = router_params(d_model, num_experts, gate_bias)
+    return dict(expert=fe, router=rg,
+                total=(num_experts + num_shared) * fe + rg,
+                active=(top_k + num_shared) * fe + rg)
+
+
+def expert_flops(rows: int, d_model: int, d_ff: int, activation: str) -> int:
+    """Multiply-add FLOPs (2 per MAC) of the expert matrices over ``rows`` rows."""
+    mats = 3 if activation == "swiglu" else 2
+    return 2 * rows * d_model * d_ff * mats
