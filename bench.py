@@ -1,0 +1,210 @@
+#!/usr/bin/env python3
+"""MoE-layer forward throughput on one MI355X, with the grouped expert GEMM
+measured against the bf16 MFMA roofline and the CPU oracle timed beside it.
+
+One step = the whole forward (router + top-k, capacity dispatch + gather,
+grouped GEMM 1 + activation, grouped GEMM 2, weighted combine, statistics) over
+one batch of synthetic tokens already resident in HBM, run through the C ABI
+stage entry points on one stream. Input and weight sets are rotated so the
+256 MB Infinity Cache does not hold the previous step's operands.
+Prints one JSON line.
+"""
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer forward tokens/sec on 1 MI355X; grouped-GEMM % of bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+GEMM_SOURCE = os.path.join(ROOT, "sparse_mixture_experts_38_amd", "csrc", "expert_gemm.hip")
+
+
+def kernel_source_hash():
+    return hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()[:16]
+
+
+def read_traffic(kernel_key):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    counter summary, if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "expert_gemm_deepspeed_gpt_moe_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_sha256_16") != kernel_source_hash():
+        return None
+    v = vals.get(f"{kernel_key}_hbm_bytes_per_launch")
+    return float(v) if v else None
+
+
+def cpu_baseline(w, inp_gpu, max_seconds=30.0):
+    """The oracle, as it stands, on the same workload's weights and tokens."""
+    import numpy as np
+    import torch
+    from oracle import moe_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+
+    def f64(t):
+        return None if t is None else t.detach().to("cpu", torch.float64).numpy()
+
+    class PerExpert:
+        def __init__(self, t):
+            self.t = t.cpu()
+
+        def __getitem__(self, e):
+            return self.t[e].to(torch.float64).numpy()
+
+    P = {n: f64(inp_gpu[n]) for n in ("w_gate", "b_gate", "e_bias")}
+    P.update({n: (None if inp_gpu[n] is None else PerExpert(inp_gpu[n]))
+              for n in ("w1", "w3", "b1", "w2", "b2", "ws1", "ws3", "bs1", "ws2", "bs2")})
+    x = f64(inp_gpu["x"])
+    times = []
+    t_end = time.perf_counter() + max_seconds
+    while len(times) < 3:
+        t0 = time.perf_counter()
+        O.forward(x, P, w)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() + times[-1] > t_end:
+            break
+    med = statistics.median(times)
+    return {"value": w.tokens / med, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"full {w.name} batch ({w.tokens} tokens), numpy float64 oracle, "
+                      f"median of {len(times)} run(s), {med:.2f} s each"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="deepspeed_gpt_moe")
+    ap.add_argument("--sets", type=int, default=3, help="rotated input/weight sets")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the layer runs "
+              "with all experts on one MI355X)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sparse_mixture_experts_38_amd import api as A
+    from sparse_mixture_experts_38_amd.workloads import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    cfg = A.make_config(w)
+    sets = [make_inputs(w, seed=s, device="cuda") for s in range(args.sets)]
+    T, d, F, E, k = w.tokens, w.d_model, w.d_ff, w.num_experts, w.top_k
+    act = A.TORCH_DTYPE[cfg.act_dtype]
+    ws = A.alloc_workspace(cfg)
+    plans = []
+    for s in sets:
+        R = A.alloc_routing(cfg, logits=False)
+        stats = A.alloc_stats()
+        y = torch.empty(T, d, dtype=act, device="cuda")
+        plans.append(A.Plan(cfg, s["x"], A.weights_of(s), y, R, stats, ws))
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        p = plans[i % len(plans)]
+        p.route()
+        p.permute()
+        if ev is not None:
+            ev[0].record()
+        p.expert_up()
+        if ev is not None:
+            ev[1].record()
+        p.expert_down()
+        if ev is not None:
+            ev[2].record()
+        p.combine()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        step(i, evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / args.steps
+    up_ms = statistics.mean(e[0].elapsed_time(e[1]) for e in evs)
+    down_ms = statistics.mean(e[1].elapsed_time(e[2]) for e in evs)
+
+    # the same kernels through the single moe_forward entry point
+    for i in range(args.warmup):
+        plans[i % len(plans)].forward()
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        plans[i % len(plans)].forward()
+    stop.record()
+    torch.cuda.synchronize()
+    fwd_ms = start.elapsed_time(stop) / args.steps
+
+    # algorithmic FLOPs per launch: kept rows only (no padding, no dropped rows)
+    kept = [A.read_stats(p.keep[4], E)["kept"] for p in plans]
+    rows = statistics.mean(kept)
+    up_mats = 2 if w.activation == "swiglu" else 1
+    up_flop = 2.0 * rows * d * F * up_mats
+    down_flop = 2.0 * rows * d * F
+    dom, dom_ms, dom_flop = (("expert_up", up_ms, up_flop) if up_ms >= down_ms
+                             else ("expert_down", down_ms, down_flop))
+    achieved = dom_flop / (dom_ms * 1e-3) / 1e12
+    traffic = read_traffic(dom)
+    result = {
+        "metric": METRIC,
+        "value": T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.act_dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "tokens": T, "d_model": d, "d_ff": F, "num_experts": E,
+                   "top_k": k, "activation": w.activation, "score_fn": w.score_fn,
+                   "capacity_factor": w.capacity_factor if w.drop_tokens else None,
+                   "min_capacity": w.min_capacity, "drop_tokens": w.drop_tokens,
+                   "router_dtype": w.router_dtype, "parallelism": "single-gpu",
+                   "rotated_sets": len(plans)},
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic},
+        "stages_ms": {"expert_up": up_ms, "expert_down": down_ms,
+                      "route_permute_combine": ms_per_step - up_ms - down_ms,
+                      "moe_forward_entry": fwd_ms},
+        "kept_rows": rows,
+        "wall_s": wall,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, sets[0])
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,279 @@
+/*
+ * moe.h — C ABI of the MI355X (gfx950) sparse Mixture-of-Experts layer forward.
+ *
+ * The layer (token-choice top-k routing):
+ *   h = x . W_g^T (+ b_g)                       router logits, float32
+ *   p = softmax(h)   or   s = sigmoid(h)         score function, float32
+ *   top-k experts per token by key (h for softmax, s + e_bias for sigmoid),
+ *   gates renormalised over the k selected (unbiased) scores
+ *   capacity-limited dispatch into an expert-sorted row buffer
+ *   E_e(x) = W2[e] act(W1[e] x + b1[e]) + b2[e]    (SwiGLU: W2[e](silu(W1 x) * W3 x))
+ *   y[t] = sum_j kept(t,j) g[t,j] E_{i_j}(x_t)  (+ shared expert E_s(x_t))
+ *   L_aux = E sum_i f_i P_i,   z = mean_t logsumexp(h_t)^2
+ *
+ * Sources (web pages on sparse Mixture-of-Experts):
+ *   [P1] "MoE Training: Mixture of Experts" (claudewave skill page): "Basic MoE
+ *        Architecture", "2. Routing Mechanisms", "3. Load Balancing".
+ *   [P2] "MoE Training Guide" (DeepSpeed-based guide): "Basic MoE Configuration",
+ *        "Core MoE Parameters" items 4-7, "Monitoring".
+ *   [P3] "moe_code.py" (Mixture of Experts: Complete Implementation): classes
+ *        Expert, Router, MixtureOfExperts, SwitchMoE.
+ *   [P4] "Mixture of Experts (MoE) From Scratch to DeepSeek V3" (CS336 lecture 4
+ *        notes): token-choice top-k formula, auxiliary loss, auxiliary-loss-free
+ *        bias, token dropping, router precision and z-loss, V3 sigmoid routing,
+ *        shared + fine-grained experts.
+ *   [P5] "Moe(Mixtrue of Experts)" survey: Mixtral parameter count.
+ *
+ * Conventions for every entry point:
+ *   - Pointers named x, w*, b*, logits, topk_*, expert_offsets, row_token,
+ *     assign_row, x_perm, y_perm, y, stats and workspace are DEVICE pointers; cfg
+ *     and the structs passed by pointer are HOST memory. The caller owns every
+ *     buffer; the library allocates nothing and keeps no state between calls.
+ *   - stream is a hipStream_t passed as void*; NULL means the default stream.
+ *     All device work is enqueued on it asynchronously; no entry point
+ *     synchronises. Host-only helpers do no device work at all.
+ *   - Tensors are dense row-major. Weights use the nn.Linear [out, in] layout,
+ *     stacked on a leading expert axis: W1, W3 [E, d_ff, d_model], W2
+ *     [E, d_model, d_ff], so both operands of every product are contiguous
+ *     along the reduction axis.
+ *   - Element types: activations, x, W1, W3, W2 and every row buffer have type
+ *     act_dtype; W_g has router_dtype; biases, logits, gates and statistics are
+ *     float32; indices are int32.
+ *   - Return value: MOE_OK or an error code. Arguments are validated before any
+ *     launch; on error nothing is enqueued. A failed launch returns MOE_ERR_HIP.
+ *     Entry points never abort, throw or print. Non-finite inputs give
+ *     unspecified (but memory-safe) results.
+ *   - tokens == 0 is a valid no-op: nothing is enqueued and nothing written.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_MAX_EXPERTS 256
+#define MOE_MAX_TOP_K 8
+
+enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* null pointer, out-of-range field, inconsistent sizes */
+  MOE_ERR_UNSUPPORTED = 2, /* valid layer this build does not run (shape multiple) */
+  MOE_ERR_WORKSPACE = 3,   /* workspace smaller than moe_workspace_size() */
+  MOE_ERR_HIP = 4          /* a HIP launch or runtime call failed */
+};
+
+enum moe_score_fn { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 };
+enum moe_activation { MOE_ACT_GELU = 0, MOE_ACT_RELU = 1, MOE_ACT_SWIGLU = 2 };
+enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 };
+
+/*
+ * Layer configuration (host struct). Field names follow the DeepSpeed MoE keys
+ * of [P2] "Basic MoE Configuration" / "Core MoE Parameters" and the module
+ * arguments of [P1] MoELayer(hidden_size, num_experts, top_k) and [P3]
+ * MixtureOfExperts(d_model, d_ff, num_experts, top_k).
+ */
+typedef struct moe_config {
+  int64_t tokens;             /* T = batch * sequence, >= 0                         */
+  int64_t d_model;            /* hidden size d, a multiple of 8                       */
+  int64_t d_ff;               /* expert inner size F, a multiple of 8                 */
+  int32_t num_experts;        /* routed experts E, 1..256                             */
+  int32_t top_k;              /* k, 1..min(E, 8)                                      */
+  int32_t num_shared_experts; /* 0 or 1: always-active expert with gate 1 [P4]       */
+  int32_t score_fn;           /* MOE_SCORE_SOFTMAX or MOE_SCORE_SIGMOID               */
+  int32_t activation;         /* MOE_ACT_GELU (exact erf), MOE_ACT_RELU, MOE_ACT_SWIGLU */
+  int32_t has_bias;           /* experts carry b1 [E,F] and b2 [E,d]                  */
+  int32_t has_gate_bias;      /* router carries b_g [E]                               */
+  int32_t drop_tokens;        /* 0: no capacity limit ([P2] item 7)                   */
+  int32_t min_capacity;       /* >= 0 ([P2] item 6)                                   */
+  int32_t act_dtype;          /* MOE_F32 or MOE_BF16                                  */
+  int32_t router_dtype;       /* dtype of W_g: MOE_F32 or MOE_BF16                    */
+  int32_t reserved;           /* must be 0                                            */
+  double capacity_factor;     /* > 0 and finite when drop_tokens ([P2] items 4-5)     */
+} moe_config;
+
+/*
+ * Device-resident statistics written by moe_route (prob_mean, z_loss) and
+ * moe_permute (everything else). [P1] "3. Load Balancing"; [P2] "Monitoring";
+ * [P3] MixtureOfExperts routing_info / expert usage; [P4] auxiliary loss and
+ * z-loss. f_i counts top-k picks before capacity, divided by T*k; for the
+ * sigmoid router P_i is the mean of s_ti / sum_e s_te.
+ */
+typedef struct moe_stats {
+  int32_t counts_pre[MOE_MAX_EXPERTS];  /* top-k picks per expert                    */
+  int32_t counts_kept[MOE_MAX_EXPERTS]; /* min(counts_pre, capacity)                 */
+  float frac[MOE_MAX_EXPERTS];          /* f_i = counts_pre / (T k)                  */
+  float prob_mean[MOE_MAX_EXPERTS];     /* P_i                                       */
+  float l_aux;                          /* E sum_i f_i P_i                           */
+  float z_loss;                         /* mean_t logsumexp(h_t)^2                   */
+  int32_t capacity;                     /* per-expert capacity, -1 when unlimited    */
+  int32_t kept;                         /* sum counts_kept (= R, the routed rows)    */
+  int32_t dropped;                      /* T k - kept                                */
+  int32_t reserved[3];
+} moe_stats;
+
+/* Weights for moe_forward (device pointers; NULL where the layer has none). */
+typedef struct moe_weights {
+  const void* w_gate;  /* [E, d] router_dtype                                  */
+  const float* b_gate; /* [E] if has_gate_bias, else NULL                      */
+  const float* e_bias; /* [E] sigmoid selection bias, or NULL ([P4] V3 bias b_i) */
+  const void* w1;      /* [E, F, d]                                            */
+  const void* w3;      /* [E, F, d] for SwiGLU, else NULL                      */
+  const float* b1;     /* [E, F] if has_bias, else NULL                        */
+  const void* w2;      /* [E, d, F]                                            */
+  const float* b2;     /* [E, d] if has_bias, else NULL                        */
+  const void* ws1;     /* shared expert [F, d] (num_shared_experts == 1)       */
+  const void* ws3;     /* shared expert [F, d] for SwiGLU                      */
+  const float* bs1;    /* shared expert [F] if has_bias                        */
+  const void* ws2;     /* shared expert [d, F]                                 */
+  const float* bs2;    /* shared expert [d] if has_bias                        */
+} moe_weights;
+
+/* Routing and dispatch results of moe_forward (device buffers the caller owns). */
+typedef struct moe_routing {
+  float* logits;           /* [T, E] float32, or NULL to skip writing them        */
+  int32_t* topk_idx;       /* [T, k]                                              */
+  float* topk_gate;        /* [T, k]                                              */
+  int32_t* expert_offsets; /* [E + S + 1], S = num_shared_experts                 */
+  int32_t* row_token;      /* [T k + S T]                                         */
+  int32_t* assign_row;     /* [T, k]                                              */
+} moe_routing;
+
+/* Human-readable name of a status code (static string). */
+const char* moe_status_string(int status);
+
+/* Library version string (static). */
+const char* moe_version(void);
+
+/* Host only. MOE_OK if cfg describes a layer this library runs, else the code
+ * moe_forward would return for it (MOE_ERR_INVALID_ARG or MOE_ERR_UNSUPPORTED). */
+int moe_validate_config(const moe_config* cfg);
+
+/*
+ * Host only. Per-expert capacity C = max(min_capacity, ceil(capacity_factor *
+ * top_k * tokens / num_experts)), or -1 when drop_tokens == 0.
+ * [P2] "Core MoE Parameters" items 4-7 give (tokens / num_experts) x factor and
+ * the minimum; this library counts the T*k assignments as "tokens" and rounds
+ * up, using the exact binary value of capacity_factor.
+ */
+int moe_capacity(const moe_config* cfg, int64_t* capacity_out);
+
+/* Host only. Workspace bytes needed by moe_forward (enough for every stage). */
+int moe_workspace_size(const moe_config* cfg, size_t* bytes_out);
+
+/*
+ * Router, score function, top-k and renormalised gates; writes stats->prob_mean
+ * and stats->z_loss.
+ * [P4] token-choice formula h(x) = x W_g, p = Softmax(h), TopK; router softmax
+ * in float32; [P1] "Basic MoE Architecture" (gate nn.Linear with bias, softmax,
+ * topk, renormalise); [P4] V3 sigmoid routing with selection bias b_i.
+ *   x         [T, d] act_dtype
+ *   w_gate    [E, d] router_dtype;  b_gate [E] or NULL;  e_bias [E] or NULL
+ *   logits    [T, E] float32 output, or NULL
+ *   topk_idx  [T, k] int32 output: experts in descending key order; equal keys
+ *             go to the lower index. Key = h (softmax) or s + e_bias (sigmoid).
+ *   topk_gate [T, k] float32 output: p_j / sum_sel p (softmax) or s_j / sum_sel s
+ *             (sigmoid, unbiased s)
+ *   stats     device moe_stats (prob_mean, z_loss written)
+ */
+int moe_route(const moe_config* cfg, const void* x, const void* w_gate, const float* b_gate,
+              const float* e_bias, float* logits, int32_t* topk_idx, float* topk_gate,
+              moe_stats* stats, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Capacity-limited dispatch: histogram, stable expert-sorted order, drop set,
+ * and the gather of token rows into the expert-sorted buffer. Completes the
+ * statistics (counts, f_i, L_aux from the P_i moe_route wrote, kept, dropped).
+ * [P4] "Token Dropping"; [P2] items 4-7. Queue order is k-major then
+ * token-ascending: assignment (t, j) has priority j*T + t; it is kept iff its
+ * position in its expert's queue is < capacity (always when drop_tokens == 0).
+ * Rows are ordered by expert, then queue position. With a shared expert, rows
+ * R..R+T-1 (R = kept routed rows) hold every token in order (group E).
+ *   topk_idx       [T, k] int32 input (values in [0, E))
+ *   x              [T, d] act_dtype
+ *   expert_offsets [E + S + 1] int32 output: exclusive scan of kept rows per group
+ *   row_token      [T k + S T] int32 output: source token of each row (first
+ *                  expert_offsets[E + S] entries written)
+ *   assign_row     [T, k] int32 output: row of (t, j) or -1 when dropped
+ *   x_perm         [T k + S T, d] act_dtype output (first expert_offsets[E+S]
+ *                  rows written), or NULL to skip the gather
+ *   stats          device moe_stats (reads prob_mean; writes the rest)
+ */
+int moe_permute(const moe_config* cfg, const int32_t* topk_idx, const void* x,
+                int32_t* expert_offsets, int32_t* row_token, int32_t* assign_row, void* x_perm,
+                moe_stats* stats, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Grouped expert FFN over the expert-sorted rows: for group g (routed expert
+ * g < E, shared expert g == E) and rows expert_offsets[g] .. expert_offsets[g+1]-1,
+ *   y_perm[r] = W2[g] act(W1[g] x_perm[r] + b1[g]) + b2[g]
+ * (SwiGLU: W2[g] (silu(W1[g] x) * (W3[g] x))), float32 accumulation, the
+ * intermediate rounded to act_dtype. [P1] expert nn.Sequential(Linear, GELU,
+ * Linear); [P3] Expert (ReLU; dropout is the identity in a forward pass); [P5]
+ * three matrices per Mixtral expert (SwiGLU).
+ *   x_perm         [rows, d] act_dtype, rows = expert_offsets[E + S]
+ *   expert_offsets [E + S + 1] int32, non-decreasing, expert_offsets[0] == 0,
+ *                  expert_offsets[E + S] <= T k + S T
+ *   w1, w3, b1, w2, b2   routed expert weights (w3 only for SwiGLU, b* iff has_bias)
+ *   ws1, ws3, bs1, ws2, bs2   shared expert weights (iff num_shared_experts)
+ *   y_perm         [rows, d] act_dtype output
+ */
+int moe_expert_ffn(const moe_config* cfg, const void* x_perm, const int32_t* expert_offsets,
+                   const void* w1, const void* w3, const float* b1, const void* w2,
+                   const float* b2, const void* ws1, const void* ws3, const float* bs1,
+                   const void* ws2, const float* bs2, void* y_perm, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/*
+ * First grouped GEMM of moe_expert_ffn alone, with the activation fused:
+ *   h[r] = act(W1[g] x_perm[r] + b1[g])   (SwiGLU: silu(W1[g] x) * (W3[g] x))
+ * for the rows r of each group g as in moe_expert_ffn; h is [T k + S T, d_ff]
+ * act_dtype (rows beyond expert_offsets[E + S] are not written). Same sources
+ * as moe_expert_ffn. Needs no workspace.
+ */
+int moe_expert_up(const moe_config* cfg, const void* x_perm, const int32_t* expert_offsets,
+                  const void* w1, const void* w3, const float* b1, const void* ws1,
+                  const void* ws3, const float* bs1, void* h, void* stream);
+
+/*
+ * Second grouped GEMM of moe_expert_ffn alone: y_perm[r] = W2[g] h[r] + b2[g]
+ * for the rows r of each group g. h as written by moe_expert_up; y_perm
+ * [T k + S T, d_model] act_dtype. Needs no workspace.
+ */
+int moe_expert_down(const moe_config* cfg, const void* h, const int32_t* expert_offsets,
+                    const void* w2, const float* b2, const void* ws2, const float* bs2,
+                    void* y_perm, void* stream);
+
+/*
+ * Gate-weighted combine: y[t] = sum_j [assign_row[t,j] >= 0] topk_gate[t,j] *
+ * y_perm[assign_row[t,j]] (+ y_perm[expert_offsets[E] + t] with a shared
+ * expert), float32 accumulation in j order, one rounding to act_dtype. A
+ * token whose every choice was dropped gets zeros. No residual is added.
+ * [P4] y = sum_{i in TopK} Gate_i E_i(x); [P1] "Weighted Combination";
+ * [P4] shared experts are always active.
+ *   y_perm [rows, d]; expert_offsets [E + S + 1] (read only with a shared expert,
+ *   may be NULL otherwise); assign_row, topk_gate [T, k]; y [T, d] output.
+ */
+int moe_combine(const moe_config* cfg, const void* y_perm, const int32_t* expert_offsets,
+                const int32_t* assign_row, const float* topk_gate, void* y, void* stream);
+
+/*
+ * The whole layer forward: moe_route, moe_permute, moe_expert_ffn and
+ * moe_combine on one stream, with the expert-sorted row buffers and the
+ * intermediate kept in the workspace.
+ *   x [T, d] act_dtype;  w: weights;  y [T, d] act_dtype output;
+ *   routing: caller buffers for the routing results (logits may be NULL);
+ *   stats: device moe_stats;  workspace >= moe_workspace_size(cfg) bytes.
+ */
+int moe_forward(const moe_config* cfg, const void* x, const moe_weights* w, void* y,
+                const moe_routing* routing, moe_stats* stats, void* workspace,
+                size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,271 @@
+// C ABI of the MoE-layer forward: validation, capacity, workspace layout and
+// the entry points declared in moe.h. Host code only; kernels live in the
+// other sources.
+#include <math.h>
+#include <string.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+static size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
+
+WsLayout workspace_layout(const moe_config& c) {
+  WsLayout L;
+  memset(&L, 0, sizeof(L));
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align_up(bytes);
+    return o;
+  };
+  const int64_t T = c.tokens;
+  const int E = c.num_experts, k = c.top_k, S = c.num_shared_experts;
+  const int64_t A = T * k;
+  const int gpb = 256 / route_lanes(E);
+  const int64_t groups = (T + gpb - 1) / gpb;
+  const int64_t iters = groups > 1024 ? (groups + 1023) / 1024 : 1;
+  L.route_iters = (int)iters;
+  L.route_blocks = (int)(groups > 0 ? (groups + iters - 1) / iters : 1);
+  L.logits = take((size_t)T * E * sizeof(float));
+  L.route_partials = take((size_t)L.route_blocks * (E + 1) * sizeof(float));
+  L.end_route = off;
+  L.chunks = (int)(A > 0 ? (A + kRankChunk - 1) / kRankChunk : 1);
+  L.chunk_hist = take((size_t)L.chunks * E * sizeof(int32_t));
+  L.chunk_base = take((size_t)L.chunks * E * sizeof(int32_t));
+  L.local_rank = take((size_t)A * sizeof(int32_t));
+  L.end_permute = off;
+  L.rows_max = A + (int64_t)S * T;
+  const size_t es = c.act_dtype == MOE_BF16 ? 2 : 4;
+  L.h = take((size_t)L.rows_max * c.d_ff * es);
+  L.end_ffn = off;
+  L.x_perm = take((size_t)L.rows_max * c.d_model * es);
+  L.y_perm = take((size_t)L.rows_max * c.d_model * es);
+  L.total = off;
+  return L;
+}
+
+static int validate(const moe_config* c) {
+  if (!c) return MOE_ERR_INVALID_ARG;
+  if (c->reserved != 0) return MOE_ERR_INVALID_ARG;
+  if (c->tokens < 0 || c->d_model <= 0 || c->d_ff <= 0) return MOE_ERR_INVALID_ARG;
+  if (c->num_experts < 1 || c->num_experts > MOE_MAX_EXPERTS) return MOE_ERR_INVALID_ARG;
+  if (c->top_k < 1 || c->top_k > MOE_MAX_TOP_K || c->top_k > c->num_experts)
+    return MOE_ERR_INVALID_ARG;
+  if (c->num_shared_experts < 0 || c->num_shared_experts > 1) return MOE_ERR_INVALID_ARG;
+  if (c->score_fn != MOE_SCORE_SOFTMAX && c->score_fn != MOE_SCORE_SIGMOID)
+    return MOE_ERR_INVALID_ARG;
+  if (c->activation < MOE_ACT_GELU || c->activation > MOE_ACT_SWIGLU) return MOE_ERR_INVALID_ARG;
+  if ((c->has_bias | c->has_gate_bias | c->drop_tokens) & ~1) return MOE_ERR_INVALID_ARG;
+  if ((c->act_dtype != MOE_F32 && c->act_dtype != MOE_BF16) ||
+      (c->router_dtype != MOE_F32 && c->router_dtype != MOE_BF16))
+    return MOE_ERR_INVALID_ARG;
+  if (c->drop_tokens) {
+    const double cf = c->capacity_factor;
+    if (!(cf >= 1e-9 && cf <= 1e6)) return MOE_ERR_INVALID_ARG;  // also rejects NaN
+    if (c->min_capacity < 0) return MOE_ERR_INVALID_ARG;
+  }
+  // Sizes this build runs: 32-bit row indices, 16-byte row vectors, and the
+  // MFMA tile multiples of the bf16 expert GEMM.
+  const int64_t rows = c->tokens * c->top_k + (int64_t)c->num_shared_experts * c->tokens;
+  if (c->tokens > (int64_t)1 << 28 || rows >= ((int64_t)1 << 31) - 4096) return MOE_ERR_UNSUPPORTED;
+  if (c->d_model > (1 << 20) || c->d_ff > (1 << 20)) return MOE_ERR_UNSUPPORTED;
+  if (c->d_model % 8 || c->d_ff % 8) return MOE_ERR_UNSUPPORTED;
+  if (c->act_dtype == MOE_BF16 && (c->d_model % kGemmBN || c->d_ff % kGemmBN))
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// ceil(cf * k * T / E) with cf taken at its exact binary value, at least
+// min_capacity; -1 when dropping is off.
+static int64_t capacity_exact(const moe_config& c) {
+  if (!c.drop_tokens) return -1;
+  int ex = 0;
+  const double fr = frexp(c.capacity_factor, &ex);  // cf = fr 2^ex, fr in [0.5, 1)
+  const int64_t m = (int64_t)ldexp(fr, 53);          // exact 53-bit integer
+  const int sh = 53 - ex;                            // cf = m / 2^sh, sh in [33, 83]
+  const __int128 num = (__int128)m * (__int128)(c.tokens * c.top_k);
+  const __int128 den = (__int128)c.num_experts << sh;
+  const __int128 q = (num + den - 1) / den;
+  int64_t cap = q > (__int128)INT64_MAX ? INT64_MAX : (int64_t)q;
+  if (cap < c.min_capacity) cap = c.min_capacity;
+  return cap;
+}
+
+static int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: layer shape not supported by this build";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace smaller than moe_workspace_size()";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP launch or runtime call failed";
+    default: return "unknown moe status";
+  }
+}
+
+const char* moe_version(void) { return "moe-mi355x 0.1.0 (gfx950)"; }
+
+int moe_validate_config(const moe_config* cfg) { return validate(cfg); }
+
+int moe_capacity(const moe_config* cfg, int64_t* capacity_out) {
+  const int v = validate(cfg);
+  if (v != MOE_OK) return v;
+  if (!capacity_out) return MOE_ERR_INVALID_ARG;
+  *capacity_out = capacity_exact(*cfg);
+  return MOE_OK;
+}
+
+int moe_workspace_size(const moe_config* cfg, size_t* bytes_out) {
+  const int v = validate(cfg);
+  if (v != MOE_OK) return v;
+  if (!bytes_out) return MOE_ERR_INVALID_ARG;
+  *bytes_out = workspace_layout(*cfg).total;
+  return MOE_OK;
+}
+
+int moe_route(const moe_config* cfg, const void* x, const void* w_gate, const float* b_gate,
+              const float* e_bias, float* logits, int32_t* topk_idx, float* topk_gate,
+              moe_stats* stats, void* workspace, size_t workspace_bytes, void* stream) {
+  const int v = validate(cfg);
+  if (v != MOE_OK) return v;
+  if (cfg->tokens == 0) return MOE_OK;
+  if (!x || !w_gate || !topk_idx || !topk_gate || !stats || !workspace)
+    return MOE_ERR_INVALID_ARG;
+  if (cfg->has_gate_bias && !b_gate) return MOE_ERR_INVALID_ARG;
+  const WsLayout L = workspace_layout(*cfg);
+  if (workspace_bytes < L.end_route) return MOE_ERR_WORKSPACE;
+  return hip_status(launch_route(*cfg, L, x, w_gate, b_gate, e_bias, logits, topk_idx, topk_gate,
+                                 stats, (char*)workspace, (hipStream_t)stream));
+}
+
+int moe_permute(const moe_config* cfg, const int32_t* topk_idx, const void* x,
+                int32_t* expert_offsets, int32_t* row_token, int32_t* assign_row, void* x_perm,
+                moe_stats* stats, void* workspace, size_t workspace_bytes, void* stream) {
+  const int v = validate(cfg);
+  if (v != MOE_OK) return v;
+  if (cfg->tokens == 0) return MOE_OK;
+  if (!topk_idx || !expert_offsets || !row_token || !assign_row || !stats || !workspace)
+    return MOE_ERR_INVALID_ARG;
+  if (x_perm && !x) return MOE_ERR_INVALID_ARG;
+  const WsLayout L = workspace_layout(*cfg);
+  if (workspace_bytes < L.end_permute) return MOE_ERR_WORKSPACE;
+  return hip_status(launch_permute(*cfg, L, capacity_exact(*cfg), topk_idx, x, expert_offsets,
+                                   row_token, assign_row, x_perm, stats, (char*)workspace,
+                                   (hipStream_t)stream));
+}
+
+static int check_weights(const moe_config* c, const void* w1, const void* w3, const float* b1,
+                         const void* w2, const float* b2, const void* ws1, const void* ws3,
+                         const float* bs1, const void* ws2, const float* bs2) {
+  const bool swiglu = c->activation == MOE_ACT_SWIGLU;
+  if (!w1 || !w2 || (swiglu && !w3)) return MOE_ERR_INVALID_ARG;
+  if (c->has_bias && (!b1 || !b2)) return MOE_ERR_INVALID_ARG;
+  if (c->num_shared_experts) {
+    if (!ws1 || !ws2 || (swiglu && !ws3)) return MOE_ERR_INVALID_ARG;
+    if (c->has_bias && (!bs1 || !bs2)) return MOE_ERR_INVALID_ARG;
+  }
+  return MOE_OK;
+}
+
+int moe_expert_ffn(const moe_config* cfg, const void* x_perm, const int32_t* expert_offsets,
+                   const void* w1, const void* w3, const float* b1, const void* w2,
+                   const float* b2, const void* ws1, const void* ws3, const float* bs1,
+                   const void* ws2, const float* bs2, void* y_perm, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  const int v = validate(cfg);
+  if (v != MOE_OK) return v;
+  if (cfg->tokens == 0) return MOE_OK;
+  if (!x_perm || !expert_offsets || !y_perm || !workspace) return MOE_ERR_INVALID_ARG;
+  const int wv = check_weights(cfg, w1, w3, b1, w2, b2, ws1, ws3, bs1, ws2, bs2);
+  if (wv != MOE_OK) return wv;
+  const WsLayout L = workspace_layout(*cfg);
+  if (workspace_bytes < L.end_ffn) return MOE_ERR_WORKSPACE;
+  const ExpertWeights w{w1, w3, w2, b1, b2, ws1, ws3, ws2, bs1, bs2};
+  void* h = (char*)workspace + L.h;
+  const hipError_t e = launch_expert_up(*cfg, x_perm, expert_offsets, w, h, (hipStream_t)stream);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(launch_expert_down(*cfg, h, expert_offsets, w, y_perm, (hipStream_t)stream));
+}
+
+int moe_expert_up(const moe_config* cfg, const void* x_perm, const int32_t* expert_offsets,
+                  const void* w1, const void* w3, const float* b1, const void* ws1,
+                  const void* ws3, const float* bs1, void* h, void* stream) {
+  const int v = validate(cfg);
+  if (v != MOE_OK) return v;
+  if (cfg->tokens == 0) return MOE_OK;
+  if (!x_perm || !expert_offsets || !h) return MOE_ERR_INVALID_ARG;
+  const bool swiglu = cfg->activation == MOE_ACT_SWIGLU;
+  if (!w1 || (swiglu && !w3) || (cfg->has_bias && !b1)) return MOE_ERR_INVALID_ARG;
+  if (cfg->num_shared_experts && (!ws1 || (swiglu && !ws3) || (cfg->has_bias && !bs1)))
+    return MOE_ERR_INVALID_ARG;
+  const ExpertWeights w{w1, w3, nullptr, b1, nullptr, ws1, ws3, nullptr, bs1, nullptr};
+  return hip_status(launch_expert_up(*cfg, x_perm, expert_offsets, w, h, (hipStream_t)stream));
+}
+
+int moe_expert_down(const moe_config* cfg, const void* h, const int32_t* expert_offsets,
+                    const void* w2, const float* b2, const void* ws2, const float* bs2,
+                    void* y_perm, void* stream) {
+  const int v = validate(cfg);
+  if (v != MOE_OK) return v;
+  if (cfg->tokens == 0) return MOE_OK;
+  if (!h || !expert_offsets || !y_perm || !w2 || (cfg->has_bias && !b2)) return MOE_ERR_INVALID_ARG;
+  if (cfg->num_shared_experts && (!ws2 || (cfg->has_bias && !bs2))) return MOE_ERR_INVALID_ARG;
+  const ExpertWeights w{nullptr, nullptr, w2, nullptr, b2, nullptr, nullptr, ws2, nullptr, bs2};
+  return hip_status(launch_expert_down(*cfg, h, expert_offsets, w, y_perm, (hipStream_t)stream));
+}
+
+int moe_combine(const moe_config* cfg, const void* y_perm, const int32_t* expert_offsets,
+                const int32_t* assign_row, const float* topk_gate, void* y, void* stream) {
+  const int v = validate(cfg);
+  if (v != MOE_OK) return v;
+  if (cfg->tokens == 0) return MOE_OK;
+  if (!y_perm || !assign_row || !topk_gate || !y) return MOE_ERR_INVALID_ARG;
+  if (cfg->num_shared_experts && !expert_offsets) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_combine(*cfg, y_perm, expert_offsets, assign_row, topk_gate, y,
+                                   (hipStream_t)stream));
+}
+
+int moe_forward(const moe_config* cfg, const void* x, const moe_weights* w, void* y,
+                const moe_routing* r, moe_stats* stats, void* workspace, size_t workspace_bytes,
+                void* stream) {
+  const int v = validate(cfg);
+  if (v != MOE_OK) return v;
+  if (cfg->tokens == 0) return MOE_OK;
+  if (!x || !w || !y || !r || !stats || !workspace) return MOE_ERR_INVALID_ARG;
+  if (!w->w_gate || (cfg->has_gate_bias && !w->b_gate)) return MOE_ERR_INVALID_ARG;
+  if (!r->topk_idx || !r->topk_gate || !r->expert_offsets || !r->row_token || !r->assign_row)
+    return MOE_ERR_INVALID_ARG;
+  const int wv = check_weights(cfg, w->w1, w->w3, w->b1, w->w2, w->b2, w->ws1, w->ws3, w->bs1,
+                               w->ws2, w->bs2);
+  if (wv != MOE_OK) return wv;
+  const WsLayout L = workspace_layout(*cfg);
+  if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
+  char* ws = (char*)workspace;
+  const hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_route(*cfg, L, x, w->w_gate, w->b_gate, w->e_bias, r->logits, r->topk_idx,
+                              r->topk_gate, stats, ws, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  void* x_perm = ws + L.x_perm;
+  void* y_perm = ws + L.y_perm;
+  e = launch_permute(*cfg, L, capacity_exact(*cfg), r->topk_idx, x, r->expert_offsets,
+                     r->row_token, r->assign_row, x_perm, stats, ws, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  const ExpertWeights ew{w->w1, w->w3, w->w2, w->b1, w->b2, w->ws1, w->ws3, w->ws2, w->bs1, w->bs2};
+  void* h = ws + L.h;
+  e = launch_expert_up(*cfg, x_perm, r->expert_offsets, ew, h, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = launch_expert_down(*cfg, h, r->expert_offsets, ew, y_perm, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = launch_combine(*cfg, y_perm, r->expert_offsets, r->assign_row, r->topk_gate, y, s);
+  return hip_status(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,132 @@
+// Internal declarations shared by the HIP sources of the MoE library (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;
+
+// Assignments ranked per block by the dispatch histogram kernel.
+constexpr int kRankChunk = 1024;
+
+// Block tile of the grouped expert GEMM.
+constexpr int kGemmBM = 128;
+constexpr int kGemmBN = 128;
+constexpr int kGemmBK = 64;
+
+// ------------------------------------------------------------------ helpers
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// float32 -> bfloat16, round to nearest even (gfx950 converts in hardware).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  bf16 b = (bf16)f;
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+__device__ __forceinline__ void load8(const float* p, float v[8]) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0];
+  const float4 b = reinterpret_cast<const float4*>(p)[1];
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+__device__ __forceinline__ void load8(const bf16* p, float v[8]) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  v[0] = bf16_bits_to_f32(u.x & 0xffffu); v[1] = bf16_bits_to_f32(u.x >> 16);
+  v[2] = bf16_bits_to_f32(u.y & 0xffffu); v[3] = bf16_bits_to_f32(u.y >> 16);
+  v[4] = bf16_bits_to_f32(u.z & 0xffffu); v[5] = bf16_bits_to_f32(u.z >> 16);
+  v[6] = bf16_bits_to_f32(u.w & 0xffffu); v[7] = bf16_bits_to_f32(u.w >> 16);
+}
+
+__device__ __forceinline__ void store8(float* p, const float v[8]) {
+  reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+  reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+__device__ __forceinline__ void store8(bf16* p, const float v[8]) {
+  uint4 u;
+  u.x = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
+  u.y = (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
+  u.z = (uint32_t)f32_to_bf16_bits(v[4]) | ((uint32_t)f32_to_bf16_bits(v[5]) << 16);
+  u.w = (uint32_t)f32_to_bf16_bits(v[6]) | ((uint32_t)f32_to_bf16_bits(v[7]) << 16);
+  *reinterpret_cast<uint4*>(p) = u;
+}
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16 v) { return (float)v; }
+
+__device__ __forceinline__ void store1(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store1(bf16* p, float v) {
+  *reinterpret_cast<uint16_t*>(p) = f32_to_bf16_bits(v);
+}
+
+// Expert activations. GELU is the exact erf form of nn.GELU().
+__device__ __forceinline__ float gelu_erf(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// ------------------------------------------------------------------ workspace
+struct WsLayout {
+  size_t logits;          // float [T][E] (when the caller does not keep them)
+  size_t route_partials;  // float [route_blocks][E + 1]
+  size_t chunk_hist;      // int32 [chunks][E]
+  size_t chunk_base;      // int32 [chunks][E]
+  size_t local_rank;      // int32 [T k]
+  size_t h;               // act [rows_max][F]
+  size_t x_perm;          // act [rows_max][d]
+  size_t y_perm;          // act [rows_max][d]
+  size_t end_route, end_permute, end_ffn, total;
+  int route_blocks, route_iters, chunks;
+  int64_t rows_max;
+};
+
+WsLayout workspace_layout(const moe_config& c);
+
+// Lanes of a wavefront that cooperate on one token in the top-k kernel.
+int route_lanes(int E);
+
+inline int64_t rows_max(const moe_config& c) {
+  return c.tokens * c.top_k + (int64_t)c.num_shared_experts * c.tokens;
+}
+
+// ------------------------------------------------------------------ launchers
+// Each returns hipSuccess or the first launch error. All enqueue on `stream`.
+hipError_t launch_route(const moe_config& c, const WsLayout& L, const void* x, const void* w_gate,
+                        const float* b_gate, const float* e_bias, float* logits, int32_t* topk_idx,
+                        float* topk_gate, moe_stats* stats, char* ws, hipStream_t stream);
+
+hipError_t launch_permute(const moe_config& c, const WsLayout& L, int64_t capacity,
+                          const int32_t* topk_idx, const void* x, int32_t* expert_offsets,
+                          int32_t* row_token, int32_t* assign_row, void* x_perm, moe_stats* stats,
+                          char* ws, hipStream_t stream);
+
+struct ExpertWeights {
+  const void *w1, *w3, *w2;
+  const float *b1, *b2;
+  const void *ws1, *ws3, *ws2;
+  const float *bs1, *bs2;
+};
+
+// Grouped GEMM 1 with the fused activation: h = act(x_perm W1^T + b1) per group.
+hipError_t launch_expert_up(const moe_config& c, const void* x_perm, const int32_t* expert_offsets,
+                            const ExpertWeights& w, void* h, hipStream_t stream);
+
+// Grouped GEMM 2: y_perm = h W2^T + b2 per group.
+hipError_t launch_expert_down(const moe_config& c, const void* h, const int32_t* expert_offsets,
+                              const ExpertWeights& w, void* y_perm, hipStream_t stream);
+
+hipError_t launch_combine(const moe_config& c, const void* y_perm, const int32_t* expert_offsets,
+                          const int32_t* assign_row, const float* topk_gate, void* y,
+                          hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,296 @@
+// Router: gate logits, score function, top-k with renormalised gates, and the
+// per-block partial sums of the balance statistics (P_i and logsumexp^2).
+//
+// MoE From Scratch to DeepSeek V3: token-choice formula h(x) = x W_g,
+// p = Softmax(h), Gate = TopK(p); router softmax forced to float32; z-loss
+// log^2(sum e^logit); V3 sigmoid scores with a selection-only bias b_i.
+// MoE Training: Mixture of Experts, "Basic MoE Architecture" (gate nn.Linear
+// with bias, softmax, topk, divide by the top-k sum) and "3. Load Balancing".
+#include "moe_internal.h"
+
+namespace moe {
+
+// logits[t][e] = sum_c x[t][c] w[e][c] (+ b[e]). One wavefront per token: lanes
+// split d into 8-element slices (16-byte loads of bf16 x), experts are taken
+// eight at a time with one float32 accumulator each, then reduced across the
+// wave in a fixed butterfly order (deterministic).
+template <typename XT, typename WT>
+__global__ __launch_bounds__(256) void router_logits_kernel(const XT* __restrict__ x,
+                                                            const WT* __restrict__ wg,
+                                                            const float* __restrict__ bg,
+                                                            float* __restrict__ logits, int64_t T,
+                                                            int d, int E) {
+  const int lane = threadIdx.x & 63;
+  const int64_t nwaves = (int64_t)gridDim.x * 4;
+  for (int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); t < T; t += nwaves) {
+    const XT* xr = x + t * d;
+    for (int e0 = 0; e0 < E; e0 += 8) {
+      const int ne = min(8, E - e0);
+      float acc[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+      for (int c = lane * 8; c < d; c += 512) {
+        float xv[8];
+        load8(xr + c, xv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          if (i < ne) {
+            float wv[8];
+            load8(wg + (int64_t)(e0 + i) * d + c, wv);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) acc[i] = fmaf(xv[q], wv[q], acc[i]);
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) acc[i] += __shfl_xor(acc[i], off, 64);
+      }
+      float v = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (lane == i) v = acc[i];
+      if (lane < ne) {
+        const int e = e0 + lane;
+        if (bg) v += bg[e];
+        logits[t * E + e] = v;
+      }
+    }
+  }
+}
+
+// (key, index) order used for selection: larger key first, then lower index.
+// An out-of-range index (>= E) never beats an in-range one.
+__device__ __forceinline__ bool better(float ka, int ia, float kb, int ib, int E) {
+  if (ia >= E) return false;
+  if (ib >= E) return true;
+  return ka > kb || (ka == kb && ia < ib);
+}
+
+// Score function + top-k + gates for L lanes per token, J experts per lane
+// (expert e = lane_in_group + L * jj). Also accumulates, per block and in a
+// fixed order, sum_t P-contribution per expert and sum_t lse_t^2.
+template <int L, int J>
+__global__ __launch_bounds__(256) void router_topk_kernel(
+    const float* __restrict__ logits, const float* __restrict__ e_bias, int64_t T, int E, int k,
+    int sigmoid, int iters, int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate,
+    float* __restrict__ partials) {
+  constexpr int GPB = 256 / L;
+  __shared__ float red[GPB * L * J];
+  __shared__ float red2[GPB];
+  const int tid = threadIdx.x;
+  const int g = tid / L;
+  const int lg = tid % L;
+  float pacc[J];
+#pragma unroll
+  for (int jj = 0; jj < J; ++jj) pacc[jj] = 0.f;
+  float lacc = 0.f;
+
+  for (int it = 0; it < iters; ++it) {
+    const int64_t t = ((int64_t)blockIdx.x * iters + it) * GPB + g;
+    const bool valid = t < T;
+    float l[J], key[J], sc[J];
+    bool taken[J];
+    float m = -INFINITY;
+#pragma unroll
+    for (int jj = 0; jj < J; ++jj) {
+      const int e = lg + L * jj;
+      l[jj] = (e < E) ? (valid ? logits[t * E + e] : 0.f) : -INFINITY;
+      taken[jj] = false;
+      if (e < E) m = fmaxf(m, l[jj]);
+    }
+#pragma unroll
+    for (int off = L / 2; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, L));
+    float ex[J];
+    float s = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < J; ++jj) {
+      const int e = lg + L * jj;
+      ex[jj] = (e < E) ? expf(l[jj] - m) : 0.f;
+      s += ex[jj];
+    }
+#pragma unroll
+    for (int off = L / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off, L);
+    const float lse = m + logf(s);
+    float ssum = 0.f;
+    if (!sigmoid) {
+      const float inv = 1.0f / s;
+#pragma unroll
+      for (int jj = 0; jj < J; ++jj) {
+        sc[jj] = ex[jj] * inv;   // p
+        key[jj] = l[jj];         // softmax is increasing: rank by logit
+      }
+    } else {
+#pragma unroll
+      for (int jj = 0; jj < J; ++jj) {
+        const int e = lg + L * jj;
+        if (e < E) {
+          sc[jj] = 1.0f / (1.0f + expf(-l[jj]));
+          key[jj] = e_bias ? sc[jj] + e_bias[e] : sc[jj];
+        } else {
+          sc[jj] = 0.f;
+          key[jj] = -INFINITY;
+        }
+        ssum += sc[jj];
+      }
+#pragma unroll
+      for (int off = L / 2; off >= 1; off >>= 1) ssum += __shfl_xor(ssum, off, L);
+    }
+
+    int sel_idx[MOE_MAX_TOP_K];
+    float sel_sc[MOE_MAX_TOP_K];
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOP_K; ++j) {
+      sel_idx[j] = 0;
+      sel_sc[j] = 0.f;
+      if (j < k) {
+        float bk = -INFINITY;
+        int bi = 0x7fffffff;
+#pragma unroll
+        for (int jj = 0; jj < J; ++jj) {
+          const int e = lg + L * jj;
+          if (e < E && !taken[jj] && better(key[jj], e, bk, bi, E)) {
+            bk = key[jj];
+            bi = e;
+          }
+        }
+#pragma unroll
+        for (int off = L / 2; off >= 1; off >>= 1) {
+          const float ok = __shfl_xor(bk, off, L);
+          const int oi = __shfl_xor(bi, off, L);
+          if (better(ok, oi, bk, bi, E)) {
+            bk = ok;
+            bi = oi;
+          }
+        }
+        // bi is uniform over the group; fetch its score from the owning lane.
+        const int owner_j = bi / L;
+        float mine = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < J; ++jj) {
+          if (jj == owner_j) mine = sc[jj];
+          if (jj == owner_j && lg == bi % L) taken[jj] = true;
+        }
+        sel_idx[j] = bi;
+        sel_sc[j] = __shfl(mine, (tid & ~(L - 1) & 63) + bi % L, 64);
+      }
+    }
+    float tsum = 0.f;
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOP_K; ++j)
+      if (j < k) tsum += sel_sc[j];
+    const float tinv = 1.0f / tsum;
+    if (valid) {
+#pragma unroll
+      for (int j = 0; j < MOE_MAX_TOP_K; ++j) {
+        if (j < k && lg == j) {
+          topk_idx[t * k + j] = sel_idx[j];
+          topk_gate[t * k + j] = sel_sc[j] * tinv;
+        }
+      }
+      const float pinv = sigmoid ? 1.0f / ssum : 1.0f;
+#pragma unroll
+      for (int jj = 0; jj < J; ++jj) pacc[jj] += sc[jj] * pinv;
+      lacc += lse * lse;
+    }
+  }
+
+#pragma unroll
+  for (int jj = 0; jj < J; ++jj) red[g * L * J + jj * L + lg] = pacc[jj];
+  if (lg == 0) red2[g] = lacc;
+  __syncthreads();
+  for (int e = tid; e < E; e += 256) {
+    float s = 0.f;
+    for (int gg = 0; gg < GPB; ++gg) s += red[gg * L * J + e];
+    partials[(int64_t)blockIdx.x * (E + 1) + e] = s;
+  }
+  if (tid == 0) {
+    float s = 0.f;
+    for (int gg = 0; gg < GPB; ++gg) s += red2[gg];
+    partials[(int64_t)blockIdx.x * (E + 1) + E] = s;
+  }
+}
+
+// P_i = (1/T) sum of the per-block partials (fixed order, float64 sum),
+// z = (1/T) sum_t lse_t^2.
+__global__ __launch_bounds__(256) void route_stats_kernel(const float* __restrict__ partials,
+                                                          int nblocks, int E, int64_t T,
+                                                          moe_stats* __restrict__ stats) {
+  const int e = threadIdx.x;
+  double s = 0.0;
+  if (e < E)
+    for (int b = 0; b < nblocks; ++b) s += partials[(int64_t)b * (E + 1) + e];
+  stats->prob_mean[e] = (e < E) ? (float)(s / (double)T) : 0.f;
+  if (e == 0) {
+    double z = 0.0;
+    for (int b = 0; b < nblocks; ++b) z += partials[(int64_t)b * (E + 1) + E];
+    stats->z_loss = (float)(z / (double)T);
+  }
+}
+
+template <int L, int J>
+static void launch_topk_lj(const moe_config& c, const WsLayout& Lw, const float* logits,
+                           const float* e_bias, int32_t* idx, float* gate, float* partials,
+                           hipStream_t s) {
+  hipLaunchKernelGGL((router_topk_kernel<L, J>), dim3(Lw.route_blocks), dim3(256), 0, s, logits,
+                     e_bias, (int64_t)c.tokens, c.num_experts, c.top_k,
+                     c.score_fn == MOE_SCORE_SIGMOID ? 1 : 0, Lw.route_iters, idx, gate, partials);
+}
+
+int route_lanes(int E) {
+  int L = 1;
+  while (L < E && L < 64) L <<= 1;
+  return L;
+}
+
+hipError_t launch_route(const moe_config& c, const WsLayout& L, const void* x, const void* w_gate,
+                        const float* b_gate, const float* e_bias, float* logits, int32_t* topk_idx,
+                        float* topk_gate, moe_stats* stats, char* ws, hipStream_t s) {
+  const int E = c.num_experts;
+  const int d = (int)c.d_model;
+  float* lg = logits ? logits : reinterpret_cast<float*>(ws + L.logits);
+  float* partials = reinterpret_cast<float*>(ws + L.route_partials);
+  const float* bg = c.has_gate_bias ? b_gate : nullptr;
+  const float* eb = c.score_fn == MOE_SCORE_SIGMOID ? e_bias : nullptr;
+  const int64_t waves = c.tokens;
+  const int blocks = (int)((waves + 3) / 4 < 4096 ? (waves + 3) / 4 : 4096);
+  if (c.act_dtype == MOE_BF16 && c.router_dtype == MOE_F32)
+    hipLaunchKernelGGL((router_logits_kernel<bf16, float>), dim3(blocks), dim3(256), 0, s,
+                       (const bf16*)x, (const float*)w_gate, bg, lg, (int64_t)c.tokens, d, E);
+  else if (c.act_dtype == MOE_BF16)
+    hipLaunchKernelGGL((router_logits_kernel<bf16, bf16>), dim3(blocks), dim3(256), 0, s,
+                       (const bf16*)x, (const bf16*)w_gate, bg, lg, (int64_t)c.tokens, d, E);
+  else if (c.router_dtype == MOE_F32)
+    hipLaunchKernelGGL((router_logits_kernel<float, float>), dim3(blocks), dim3(256), 0, s,
+                       (const float*)x, (const float*)w_gate, bg, lg, (int64_t)c.tokens, d, E);
+  else
+    hipLaunchKernelGGL((router_logits_kernel<float, bf16>), dim3(blocks), dim3(256), 0, s,
+                       (const float*)x, (const bf16*)w_gate, bg, lg, (int64_t)c.tokens, d, E);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+
+  const int Ln = route_lanes(E);
+  switch (Ln) {
+    case 1: launch_topk_lj<1, 1>(c, L, lg, eb, topk_idx, topk_gate, partials, s); break;
+    case 2: launch_topk_lj<2, 1>(c, L, lg, eb, topk_idx, topk_gate, partials, s); break;
+    case 4: launch_topk_lj<4, 1>(c, L, lg, eb, topk_idx, topk_gate, partials, s); break;
+    case 8: launch_topk_lj<8, 1>(c, L, lg, eb, topk_idx, topk_gate, partials, s); break;
+    case 16: launch_topk_lj<16, 1>(c, L, lg, eb, topk_idx, topk_gate, partials, s); break;
+    case 32: launch_topk_lj<32, 1>(c, L, lg, eb, topk_idx, topk_gate, partials, s); break;
+    default: {
+      const int J = (E + 63) / 64;
+      if (J == 1) launch_topk_lj<64, 1>(c, L, lg, eb, topk_idx, topk_gate, partials, s);
+      else if (J == 2) launch_topk_lj<64, 2>(c, L, lg, eb, topk_idx, topk_gate, partials, s);
+      else if (J == 3) launch_topk_lj<64, 3>(c, L, lg, eb, topk_idx, topk_gate, partials, s);
+      else launch_topk_lj<64, 4>(c, L, lg, eb, topk_idx, topk_gate, partials, s);
+    }
+  }
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(route_stats_kernel, dim3(1), dim3(MOE_MAX_EXPERTS), 0, s, partials,
+                     L.route_blocks, E, (int64_t)c.tokens, stats);
+  return hipGetLastError();
+}
+
+}  // namespace moe

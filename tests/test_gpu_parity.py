@@ -1,0 +1,197 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Sizes are chosen so the oracle finishes in seconds while the GPU kernels still
+span several tiles with ragged tails; each case keeps the recipe of one of the
+pages' workloads (dtype, router, activation, capacity, score function).
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+from sparse_mixture_experts_38_amd import api as A
+from sparse_mixture_experts_38_amd.workloads import WORKLOADS, make_inputs
+
+from parity_util import (TOL, check_dispatch, check_layer, check_route, full_check, gpu_forward,
+                         np64, oracle_params, rel_err, to_gpu)
+
+pytestmark = pytest.mark.gpu
+
+W = WORKLOADS
+
+CASES = {
+    # the tiny fp32 layer exactly as stated
+    "tiny_fp32": W["tiny_fp32"],
+    # DeepSpeed GPT-MoE recipe, fewer tokens, smaller d / F, ragged T
+    "gpt_moe_small": W["deepspeed_gpt_moe"].scaled(tokens=1000, d_model=256, d_ff=512),
+    # tight capacity so drops happen
+    "gpt_moe_drops": W["deepspeed_gpt_moe"].scaled(tokens=777, d_model=256, d_ff=384,
+                                                   capacity_factor=0.9),
+    # 128 experts, top-1, N(0,2) logit offsets: heavy imbalance and drops
+    "many_expert_train": W["many_expert_train"].scaled(tokens=1536, d_model=256, d_ff=256),
+    "many_expert_eval": W["many_expert_eval"].scaled(tokens=1536, d_model=256, d_ff=256),
+    # Mixtral recipe: SwiGLU, no bias, no capacity
+    "mixtral_small": W["mixtral_8x7b"].scaled(tokens=700, d_model=512, d_ff=768),
+    # DeepSeek-V3 recipe: sigmoid + selection bias, top-8 of 256, shared expert
+    "deepseek_small": W["deepseek_v3"].scaled(tokens=300, d_model=512, d_ff=256),
+    # ReLU expert (moe_code.py Expert), bf16
+    "relu_bf16": W["deepspeed_gpt_moe"].scaled(tokens=333, d_model=128, d_ff=256, activation="relu",
+                                               has_gate_bias=True, router_dtype="bf16"),
+    # fp32 layer with a binding capacity
+    "tiny_fp32_drops": W["tiny_fp32"].scaled(tokens=200, drop_tokens=True, capacity_factor=0.75,
+                                             min_capacity=4),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_forward_parity(name):
+    w = CASES[name]
+    print(f"[case] {name} T={w.tokens} d={w.d_model} F={w.d_ff} E={w.num_experts} k={w.top_k}",
+          flush=True)
+    out, err = full_check(w)
+    assert err <= TOL[w.act_dtype]
+
+
+def test_drops_happen_where_expected():
+    w = CASES["many_expert_train"]
+    out, _ = full_check(w)
+    assert out["stats"]["dropped"] > 0
+    fully = np.all(out["assign_row"].numpy() < 0, axis=1)
+    assert fully.any()
+    assert np.all(out["y"][torch.from_numpy(fully)].float().numpy() == 0.0)
+
+
+def test_stage_entry_points_match_forward_and_gather():
+    w = CASES["gpt_moe_drops"]
+    cfg = A.make_config(w)
+    inp = make_inputs(w, seed=1)
+    g = to_gpu(inp)
+    fw = gpu_forward(w, g, cfg)
+    T, d, E, k = w.tokens, w.d_model, w.num_experts, w.top_k
+    rows = T * k
+    R = A.alloc_routing(cfg)
+    stats = A.alloc_stats()
+    ws = A.alloc_workspace(cfg)
+    A.route(cfg, g["x"], g["w_gate"], g["b_gate"], g["e_bias"], R["logits"], R["topk_idx"],
+            R["topk_gate"], stats, ws)
+    x_perm = torch.zeros(rows, d, dtype=g["x"].dtype, device="cuda")
+    A.permute(cfg, R["topk_idx"], g["x"], R["expert_offsets"], R["row_token"], R["assign_row"],
+              x_perm, stats, ws)
+    y_perm = torch.zeros(rows, d, dtype=g["x"].dtype, device="cuda")
+    A.expert_ffn(cfg, x_perm, R["expert_offsets"], g["w1"], g["w3"], g["b1"], g["w2"], g["b2"],
+                 None, None, None, None, None, y_perm, ws)
+    y = torch.empty(T, d, dtype=g["x"].dtype, device="cuda")
+    A.combine(cfg, y_perm, R["expert_offsets"], R["assign_row"], R["topk_gate"], y)
+    torch.cuda.synchronize()
+    for n in ("logits", "topk_idx", "topk_gate", "expert_offsets", "row_token", "assign_row"):
+        assert torch.equal(R[n].cpu(), fw[n]), n
+    assert torch.equal(y.cpu(), fw["y"])
+    nkept = int(R["expert_offsets"][E].item())
+    rt = R["row_token"][:nkept].long()
+    assert torch.equal(x_perm[:nkept], g["x"][rt])
+
+
+def test_forward_is_deterministic():
+    w = CASES["deepseek_small"]
+    g = to_gpu(make_inputs(w, seed=3))
+    a = gpu_forward(w, g)
+    b = gpu_forward(w, g)
+    for n in ("y", "logits", "topk_idx", "topk_gate", "expert_offsets", "row_token", "assign_row"):
+        assert torch.equal(a[n], b[n]), n
+    assert a["stats"]["l_aux"] == b["stats"]["l_aux"] and a["stats"]["z_loss"] == b["stats"]["z_loss"]
+
+
+@pytest.mark.parametrize("case", ["one_token", "k_equals_E", "single_expert", "all_to_one",
+                                  "min_capacity_binds"])
+def test_edge_cases(case):
+    base = W["deepspeed_gpt_moe"].scaled(d_model=128, d_ff=128)
+    if case == "one_token":
+        w = base.scaled(tokens=1)
+    elif case == "k_equals_E":
+        w = base.scaled(tokens=130, num_experts=4, top_k=4, drop_tokens=False)
+    elif case == "single_expert":
+        w = base.scaled(tokens=257, num_experts=1, top_k=1, drop_tokens=False)
+    elif case == "all_to_one":
+        # one expert's logit offset dominates: capacity binds hard, most tokens drop
+        w = base.scaled(tokens=300, has_gate_bias=True, gate_bias_std=50.0, capacity_factor=1.0)
+    else:
+        w = base.scaled(tokens=8, num_experts=8, top_k=1, capacity_factor=1.0, min_capacity=4)
+    print(f"[case] edge {case}", flush=True)
+    out, err = full_check(w)
+    if case == "min_capacity_binds":
+        assert out["stats"]["capacity"] == 4
+
+
+def test_permute_without_gather():
+    w = CASES["gpt_moe_small"]
+    cfg = A.make_config(w)
+    g = to_gpu(make_inputs(w, seed=2))
+    R = A.alloc_routing(cfg)
+    stats = A.alloc_stats()
+    ws = A.alloc_workspace(cfg)
+    A.route(cfg, g["x"], g["w_gate"], None, None, R["logits"], R["topk_idx"], R["topk_gate"],
+            stats, ws)
+    A.permute(cfg, R["topk_idx"], None, R["expert_offsets"], R["row_token"], R["assign_row"], None,
+              stats, ws)
+    torch.cuda.synchronize()
+    out = {k: v.cpu() for k, v in R.items()}
+    out["stats"] = A.read_stats(stats, w.num_experts)
+    check_dispatch(w, out)
+
+
+@pytest.mark.parametrize("act", ["gelu", "swiglu"])
+def test_expert_ffn_on_arbitrary_groups(act):
+    # empty groups, a group spanning several tiles, ragged tails
+    base = W["mixtral_8x7b"] if act == "swiglu" else W["deepspeed_gpt_moe"]
+    w = base.scaled(tokens=300, d_model=256, d_ff=384, num_experts=6, top_k=2)
+    cfg = A.make_config(w)
+    inp = make_inputs(w, seed=5)
+    g = to_gpu(inp)
+    counts = np.array([0, 333, 1, 0, 129, 137])
+    assert counts.sum() == w.tokens * w.top_k
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    rows = int(off[-1])
+    gen = torch.Generator().manual_seed(7)
+    xp = torch.randn(rows, w.d_model, generator=gen).to(torch.bfloat16)
+    y_perm = torch.empty(rows, w.d_model, dtype=torch.bfloat16, device="cuda")
+    ws = A.alloc_workspace(cfg)
+    A.expert_ffn(cfg, xp.cuda(), torch.from_numpy(off).cuda(), g["w1"], g["w3"], g["b1"], g["w2"],
+                 g["b2"], None, None, None, None, None, y_perm, ws)
+    torch.cuda.synchronize()
+    P = oracle_params(inp)
+    X = np64(xp)
+    ref = np.zeros((rows, w.d_model))
+    for e in range(w.num_experts):
+        lo, hi = off[e], off[e + 1]
+        if hi > lo:
+            ref[lo:hi] = O.expert_ffn(X[lo:hi], P["w1"][e], None if P["b1"] is None else P["b1"][e],
+                                      P["w2"][e], None if P["b2"] is None else P["b2"][e], act,
+                                      None if P["w3"] is None else P["w3"][e])
+    assert rel_err(y_perm.float().cpu().numpy(), ref) <= TOL["bf16"]
+
+
+def test_combine_stage():
+    w = W["deepspeed_gpt_moe"].scaled(tokens=100, d_model=128, d_ff=128)
+    cfg = A.make_config(w)
+    gen = torch.Generator().manual_seed(11)
+    T, k, d = w.tokens, w.top_k, w.d_model
+    rows = T * k
+    y_perm = torch.randn(rows, d, generator=gen).to(torch.bfloat16)
+    perm = torch.randperm(rows, generator=gen).reshape(T, k).to(torch.int32)
+    perm[::7, 1] = -1                         # some dropped assignments
+    perm[::13, :] = -1                        # some fully dropped tokens
+    gate = torch.rand(T, k, generator=gen)
+    y = torch.empty(T, d, dtype=torch.bfloat16, device="cuda")
+    A.combine(cfg, y_perm.cuda(), None, perm.cuda(), gate.cuda(), y)
+    torch.cuda.synchronize()
+    ref = O.combine(np64(y_perm), gate.double().numpy(), perm.numpy().astype(np.int64), T, d)
+    assert rel_err(y.float().cpu().numpy(), ref) <= 1e-2
+    assert np.all(y.float().cpu().numpy()[::13] == 0)
+
+
+def test_zero_tokens_noop_on_gpu():
+    w = W["deepspeed_gpt_moe"].scaled(tokens=0, d_model=128, d_ff=128)
+    cfg = A.make_config(w)
+    y = torch.empty(0, 128, dtype=torch.bfloat16, device="cuda")
+    lib = A.lib()
+    assert lib.moe_forward(cfg, None, None, None, None, None, None, 0, None) == A.MOE_OK
