@@ -82,152 +82,256 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, i
   return true;
 }
 
-// C[r, n] = epi(sum_k A[r, k] W_g[n, k] + b_g[n]) for the rows of each tile.
-// Group g < E takes expert weights W + g N K; group E (shared expert) takes Ws.
+// Per-wave view of the grouped row space used by the persistent kernel: lane l
+// holds groups 5l .. 5l+4 (clamped offsets, tile counts) and the exclusive
+// prefix of tiles before its first group.
+struct TileSpace {
+  int o[6];
+  int n[5];
+  int excl, incl, total;
+};
+
+__device__ __forceinline__ void tile_space_init(TileSpace& ts, const int32_t* __restrict__ offsets,
+                                                int G, int rows_max, int BM) {
+  constexpr int PER = 5;
+  const int lane = threadIdx.x & 63;
+  const int g0 = lane * PER;
+#pragma unroll
+  for (int i = 0; i <= PER; ++i) {
+    const int gi = g0 + i;
+    ts.o[i] = gi <= G ? min(max(offsets[gi], 0), rows_max) : rows_max;
+  }
+  int s = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int gi = g0 + i;
+    ts.n[i] = (gi < G && ts.o[i + 1] > ts.o[i]) ? (ts.o[i + 1] - ts.o[i] + BM - 1) / BM : 0;
+    s += ts.n[i];
+  }
+  int incl = s;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += t;
+  }
+  ts.incl = incl;
+  ts.excl = incl - s;
+  ts.total = __shfl(incl, 63, 64);
+}
+
+// Group, first row and row count of M tile mt (< ts.total); uniform over the wave.
+__device__ __forceinline__ void tile_lookup(const TileSpace& ts, int mt, int BM, int& g_out,
+                                            int& row0_out, int& nrows_out) {
+  constexpr int PER = 5;
+  const int lane = threadIdx.x & 63;
+  const bool mine = mt >= ts.excl && mt < ts.incl;
+  const int owner = __ffsll((unsigned long long)__ballot(mine)) - 1;
+  int g = -1, row0 = 0, nrows = 0;
+  if (mine) {
+    int acc = ts.excl;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if (g < 0 && mt < acc + ts.n[i]) {
+        g = lane * PER + i;
+        row0 = ts.o[i] + (mt - acc) * BM;
+        nrows = min(BM, ts.o[i + 1] - row0);
+      }
+      acc += ts.n[i];
+    }
+  }
+  g_out = __shfl(g, owner, 64);
+  row0_out = __shfl(row0, owner, 64);
+  nrows_out = __shfl(nrows, owner, 64);
+}
+
+// Grouped GEMM, C[r, n] = epi(sum_k A[r, k] W_g[n, k] + b_g[n]); group g < E
+// takes expert weights W + g N K, group E (shared expert) takes Ws.
+//
+// One 128 x 128 output tile per block (SwiGLU: 128 x 64 of W1 and of W3 side by
+// side), K step 64, four waves as 2 x 2, each wave 64 x 64 (SwiGLU 64 x 32 per
+// operand) on v_mfma_f32_32x32x16_bf16 with 64 float32 accumulators per lane.
+// 64 KB of LDS and at most 256 registers per lane let two blocks share a CU,
+// so one block's load waits and epilogue overlap the other's MFMAs. Operands
+// move global -> registers -> LDS with a two-step register prefetch: the loads
+// of K step k + 2 are issued while step k is multiplied, and the registers of
+// step k + 1 go to the other LDS stage at the end of step k. A stage holds 256
+// rows of 128 bytes (128 A rows, then the B rows); 16-byte chunk c of row r
+// sits at chunk c ^ ((r >> 1) & 7), so the 16 lanes of one LDS cycle (16
+// consecutive rows, one chunk) cover all 64 banks once. The MFMA takes the
+// weight fragment first, so a lane's accumulators hold four consecutive output
+// columns of one row and the epilogue stores 8 bytes at a time. Blocks are
+// dispatched to the 8 XCDs round-robin; the block id is remapped so that each
+// XCD runs a contiguous range of tiles, ordered in groups of 8 M tiles, whose
+// operands then meet in that XCD's L2.
 template <int EPI, bool HAS_BIAS>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(
+__global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
     const bf16* __restrict__ A, const bf16* __restrict__ W, const bf16* __restrict__ W3,
     const float* __restrict__ bias, const bf16* __restrict__ Ws, const bf16* __restrict__ Ws3,
     const float* __restrict__ bias_s, int E, int G, const int32_t* __restrict__ offsets,
     int rows_max, bf16* __restrict__ C, int N, int K) {
   constexpr bool GATED = EPI == EPI_SWIGLU;
-  constexpr int BM = kGemmBM, BN = kGemmBN, BK = kGemmBK;
-  constexpr int CH = BK / 8;           // 16-byte chunks per tile row
-  constexpr int NB = GATED ? 2 : 1;    // B operands (W1 and W3 for SwiGLU)
-  __shared__ uint4 sA[2][BM * CH];
-  __shared__ uint4 sB[NB][2][BN * CH];
+  constexpr int BM = 128, BK = 64, CH = BK / 8;   // 8 chunks of 16 B per LDS row
+  constexpr int NB = GATED ? 2 : 1;
+  constexpr int BN = GATED ? 64 : 128;            // columns per B operand
+  constexpr int WN = BN / 2;                       // per wave, per operand
+  constexpr int TM = 2, TN = WN / 32;
+  constexpr int ROWS = BM + NB * BN;               // 256 LDS rows per stage
+  constexpr int STAGE = ROWS * CH;                 // u32x4 per stage (32 KB)
+  constexpr int GROUP_M = 8;
+  __shared__ u32x4 smem[2 * STAGE];
 
+  // XCD-aware order of the tiles
+  const int nblk = gridDim.x;
+  const int b = blockIdx.x;
+  const int nb8 = nblk & ~7;
+  const int lid = b < nb8 ? (b & 7) * (nb8 >> 3) + (b >> 3) : b;
   const int ntn = N / BN;
-  const int mt = blockIdx.x / ntn;
-  const int nt = blockIdx.x - mt * ntn;
+  const int per_group = GROUP_M * ntn;
+  const int grp = lid / per_group;
+  const int first_m = grp * GROUP_M;
+  const int in = lid - grp * per_group;
+
+  TileSpace ts;
+  tile_space_init(ts, offsets, G, rows_max, BM);
+  if (first_m >= ts.total) return;
+  const int gm = min(ts.total - first_m, GROUP_M);
+  const int mt = first_m + in % gm;
+  const int nt = in / gm;
+  if (nt >= ntn) return;
   int g, row0, nrows;
-  if (!find_tile(offsets, G, rows_max, BM, mt, g, row0, nrows)) return;
+  tile_lookup(ts, mt, BM, g, row0, nrows);
   const int n0 = nt * BN;
   const bf16* Wg = g < E ? W + (int64_t)g * N * K : Ws;
-  const bf16* W3g = GATED ? (g < E ? W3 + (int64_t)g * N * K : Ws3) : nullptr;
+  const bf16* W3g = GATED ? (g < E ? W3 + (int64_t)g * N * K : Ws3) : Wg;
   const float* bg = HAS_BIAS ? (g < E ? bias + (int64_t)g * N : bias_s) : nullptr;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-
-  // global -> register loads: thread covers chunk (tid & 7) of rows (tid >> 3) + 32 i
-  const int lc = tid & 7;
+  const int fr = lane & 31;
+  const int fk = lane >> 5;
+  // Loads: thread t covers chunk t & 7 of tile rows (t >> 3) + 32 i, i = 0..3,
+  // of A and of B; all of them share (row >> 1) & 7 = (t >> 4) & 7.
   const int lr = tid >> 3;
-  const int64_t a_base = (int64_t)row0 * K + lc * 8;
-  const int64_t b_base = (int64_t)(n0 + lr) * K + lc * 8;
-  const int64_t a_step[4] = {(int64_t)min(lr, nrows - 1) * K, (int64_t)min(lr + 32, nrows - 1) * K,
-                             (int64_t)min(lr + 64, nrows - 1) * K,
-                             (int64_t)min(lr + 96, nrows - 1) * K};
-  const bf16* Ab = A + a_base;
-  const bf16* Bb = Wg + b_base;
-  const bf16* B3b = GATED ? W3g + b_base : nullptr;
-  uint4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3, rc0, rc1, rc2, rc3;
-#define MOE_GLOAD(k0)                                                                 \
-  do {                                                                                \
-    ra0 = *reinterpret_cast<const uint4*>(Ab + a_step[0] + (k0));                     \
-    ra1 = *reinterpret_cast<const uint4*>(Ab + a_step[1] + (k0));                     \
-    ra2 = *reinterpret_cast<const uint4*>(Ab + a_step[2] + (k0));                     \
-    ra3 = *reinterpret_cast<const uint4*>(Ab + a_step[3] + (k0));                     \
-    rb0 = *reinterpret_cast<const uint4*>(Bb + (k0));                                 \
-    rb1 = *reinterpret_cast<const uint4*>(Bb + (int64_t)32 * K + (k0));               \
-    rb2 = *reinterpret_cast<const uint4*>(Bb + (int64_t)64 * K + (k0));               \
-    rb3 = *reinterpret_cast<const uint4*>(Bb + (int64_t)96 * K + (k0));               \
-    if constexpr (GATED) {                                                            \
-      rc0 = *reinterpret_cast<const uint4*>(B3b + (k0));                              \
-      rc1 = *reinterpret_cast<const uint4*>(B3b + (int64_t)32 * K + (k0));            \
-      rc2 = *reinterpret_cast<const uint4*>(B3b + (int64_t)64 * K + (k0));            \
-      rc3 = *reinterpret_cast<const uint4*>(B3b + (int64_t)96 * K + (k0));            \
-    }                                                                                 \
+  const int lc = tid & 7;
+  const int wslot = lr * CH + (lc ^ ((tid >> 4) & 7));
+  const int rsw = (fr >> 1) & 7;                   // fragment rows: (r >> 1) & 7
+
+  // per-thread source offsets (bf16 elements) from the tile's bases; A rows
+  // past the tile's end repeat its last row
+  const bf16* a_base = A + (int64_t)row0 * K + lc * 8;
+  const bf16* b_base = Wg + (int64_t)n0 * K + lc * 8;
+  // W3 rows of the B part start at LDS row BN (= 64) for SwiGLU
+  const bf16* b3_base = W3g + (int64_t)(n0 - BN) * K + lc * 8;
+  const uint32_t aoff[4] = {(uint32_t)(min(lr, nrows - 1) * K), (uint32_t)(min(lr + 32, nrows - 1) * K),
+                            (uint32_t)(min(lr + 64, nrows - 1) * K),
+                            (uint32_t)(min(lr + 96, nrows - 1) * K)};
+  const uint32_t boff0 = (uint32_t)(lr * K);
+
+  // register stages for even / odd K steps (named registers, not arrays, so
+  // that they stay in VGPRs)
+  struct Regs { u32x4 a0, a1, a2, a3, b0, b1, b2, b3; };
+  Regs r0, r1;
+  const bf16* bsrc2 = GATED ? b3_base : b_base;   // rows 64.. of the B part (W3 for SwiGLU)
+  const uint32_t K32 = (uint32_t)(32 * K);
+#define MOE_GLOAD(R, kt)                                                             \
+  do {                                                                               \
+    const int k0_ = (kt) * BK;                                                       \
+    R.a0 = *reinterpret_cast<const u32x4*>(a_base + k0_ + aoff[0]);                  \
+    R.a1 = *reinterpret_cast<const u32x4*>(a_base + k0_ + aoff[1]);                  \
+    R.a2 = *reinterpret_cast<const u32x4*>(a_base + k0_ + aoff[2]);                  \
+    R.a3 = *reinterpret_cast<const u32x4*>(a_base + k0_ + aoff[3]);                  \
+    R.b0 = *reinterpret_cast<const u32x4*>(b_base + k0_ + boff0);                    \
+    R.b1 = *reinterpret_cast<const u32x4*>(b_base + k0_ + boff0 + K32);              \
+    R.b2 = *reinterpret_cast<const u32x4*>(bsrc2 + k0_ + boff0 + 2 * K32);           \
+    R.b3 = *reinterpret_cast<const u32x4*>(bsrc2 + k0_ + boff0 + 3 * K32);           \
   } while (0)
-  // rows lr + 32 i share (row & 7) = lr & 7, so one swizzled chunk serves all four
-  const int slot = lr * CH + (lc ^ (lr & 7));
-#define MOE_LSTORE(buf)                                                               \
-  do {                                                                                \
-    sA[buf][slot] = ra0;                                                              \
-    sA[buf][slot + 32 * CH] = ra1;                                                    \
-    sA[buf][slot + 64 * CH] = ra2;                                                    \
-    sA[buf][slot + 96 * CH] = ra3;                                                    \
-    sB[0][buf][slot] = rb0;                                                           \
-    sB[0][buf][slot + 32 * CH] = rb1;                                                 \
-    sB[0][buf][slot + 64 * CH] = rb2;                                                 \
-    sB[0][buf][slot + 96 * CH] = rb3;                                                 \
-    if constexpr (GATED) {                                                            \
-      sB[NB - 1][buf][slot] = rc0;                                                    \
-      sB[NB - 1][buf][slot + 32 * CH] = rc1;                                          \
-      sB[NB - 1][buf][slot + 64 * CH] = rc2;                                          \
-      sB[NB - 1][buf][slot + 96 * CH] = rc3;                                          \
-    }                                                                                 \
+#define MOE_LSTORE(R, st)                                                            \
+  do {                                                                               \
+    u32x4* d_ = smem + (st) * STAGE + wslot;                                         \
+    d_[0] = R.a0;                                                                    \
+    d_[32 * CH] = R.a1;                                                              \
+    d_[64 * CH] = R.a2;                                                              \
+    d_[96 * CH] = R.a3;                                                              \
+    d_[BM * CH] = R.b0;                                                              \
+    d_[(BM + 32) * CH] = R.b1;                                                       \
+    d_[(BM + 64) * CH] = R.b2;                                                       \
+    d_[(BM + 96) * CH] = R.b3;                                                       \
+  } while (0)
+#define MOE_COMPUTE(st)                                                              \
+  do {                                                                               \
+    const u32x4* cur_ = smem + (st) * STAGE;                                         \
+    _Pragma("unroll") for (int s = 0; s < BK / 16; ++s) {                            \
+      const int ch_ = (s * 2 + fk) ^ rsw;                                            \
+      bf16x8 fa_[TM], fb_[NB][TN];                                                   \
+      _Pragma("unroll") for (int i = 0; i < TM; ++i) fa_[i] =                        \
+          __builtin_bit_cast(bf16x8, cur_[(wm * 64 + i * 32 + fr) * CH + ch_]);      \
+      _Pragma("unroll") for (int bb = 0; bb < NB; ++bb)                              \
+        _Pragma("unroll") for (int j = 0; j < TN; ++j) fb_[bb][j] = __builtin_bit_cast( \
+            bf16x8, cur_[(BM + bb * BN + wn * WN + j * 32 + fr) * CH + ch_]);        \
+      _Pragma("unroll") for (int bb = 0; bb < NB; ++bb)                              \
+        _Pragma("unroll") for (int i = 0; i < TM; ++i)                               \
+          _Pragma("unroll") for (int j = 0; j < TN; ++j) acc[bb][i][j] =             \
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb_[bb][j], fa_[i], acc[bb][i][j], \
+                                                      0, 0, 0);                      \
+    }                                                                                \
   } while (0)
 
-  f32x16 acc[NB][2][2];
+  f32x16 acc[NB][TM][TN];
 #pragma unroll
-  for (int b = 0; b < NB; ++b)
+  for (int bb = 0; bb < NB; ++bb)
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[b][i][j][r] = 0.f;
+        for (int r = 0; r < 16; ++r) acc[bb][i][j][r] = 0.f;
 
-  const int nk = K / BK;
-  MOE_GLOAD(0);
-  MOE_LSTORE(0);
+  const int nk = K / BK;   // even: K is a multiple of 256
+  MOE_GLOAD(r0, 0);
+  MOE_GLOAD(r1, 1);
+  MOE_LSTORE(r0, 0);
   __syncthreads();
-  const int fr = lane & 31;    // fragment row within a 32-row sub-tile
-  const int fk = lane >> 5;    // which 8-wide half of the 16-wide K step
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) MOE_GLOAD((kt + 1) * BK);
-#pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      const int ch = s * 2 + fk;
-      bf16x8 af[2], bfr[NB][2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int r = wm * 64 + i * 32 + fr;
-        af[i] = __builtin_bit_cast(bf16x8, sA[cur][r * CH + (ch ^ (r & 7))]);
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int r = wn * 64 + j * 32 + fr;
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-          bfr[b][j] = __builtin_bit_cast(bf16x8, sB[b][cur][r * CH + (ch ^ (r & 7))]);
-      }
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[b][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[b][j], acc[b][i][j],
-                                                                   0, 0, 0);
-    }
-    if (more) MOE_LSTORE(cur ^ 1);
+  for (int kt = 0; kt < nk; kt += 2) {
+    // even step kt: stage 0 holds it, r1 holds step kt + 1, r0 is free
+    if (kt + 2 < nk) MOE_GLOAD(r0, kt + 2);
+    MOE_COMPUTE(0);
+    MOE_LSTORE(r1, 1);
+    __syncthreads();
+    // odd step kt + 1: stage 1 holds it, r0 holds step kt + 2, r1 is free
+    if (kt + 3 < nk) MOE_GLOAD(r1, kt + 3);
+    MOE_COMPUTE(1);
+    if (kt + 2 < nk) MOE_LSTORE(r0, 0);
     __syncthreads();
   }
-
 #undef MOE_GLOAD
 #undef MOE_LSTORE
+#undef MOE_COMPUTE
 
-  // Epilogue. Accumulator register r of a 32x32 tile holds row
-  // 8 (r / 4) + 4 (lane / 32) + r % 4 and column lane % 32.
+  // Epilogue: register r of a 32x32 accumulator holds row (lane % 32) and
+  // column 8 (r / 4) + 4 (lane / 32) + r % 4 of the sub-tile.
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int n = n0 + wn * 64 + j * 32 + fr;
-    const float bv = HAS_BIAS ? bg[n] : 0.f;
+  for (int j = 0; j < TN; ++j) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int qd = 0; qd < 4; ++qd) {
+      const int n = n0 + wn * WN + j * 32 + qd * 8 + fk * 4;
+      float4 bv = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (HAS_BIAS) bv = *reinterpret_cast<const float4*>(bg + n);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = wm * 64 + i * 32 + (r >> 2) * 8 + fk * 4 + (r & 3);
+      for (int i = 0; i < TM; ++i) {
+        const int m = wm * 64 + i * 32 + fr;
         if (m < nrows) {
-          const float z1 = acc[0][i][j][r] + bv;
-          const float z3 = GATED ? acc[NB - 1][i][j][r] : 0.f;
-          store1(C + (int64_t)(row0 + m) * N + n, epilogue<EPI>(z1, z3));
+          const float z[4] = {acc[0][i][j][qd * 4 + 0] + bv.x, acc[0][i][j][qd * 4 + 1] + bv.y,
+                              acc[0][i][j][qd * 4 + 2] + bv.z, acc[0][i][j][qd * 4 + 3] + bv.w};
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            v[e] = epilogue<EPI>(z[e], GATED ? acc[NB - 1][i][j][qd * 4 + e] : 0.f);
+          uint2 u;
+          u.x = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
+          u.y = (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
+          *reinterpret_cast<uint2*>(C + (int64_t)(row0 + m) * N + n) = u;
         }
       }
     }
@@ -269,12 +373,14 @@ static hipError_t gemm_launch(const moe_config& c, const ET* A, const void* W, c
                               hipStream_t s) {
   const int E = c.num_experts, G = c.num_experts + c.num_shared_experts;
   const int64_t rows = rows_max(c);
-  const unsigned mtiles = (unsigned)((rows + kGemmBM - 1) / kGemmBM) + G;
   if constexpr (sizeof(ET) == 2) {
-    hipLaunchKernelGGL((gemm_bf16_kernel<EPI, HB>), dim3(mtiles * (N / kGemmBN)), dim3(256), 0, s,
-                       A, (const bf16*)W, (const bf16*)W3, bias, (const bf16*)Ws, (const bf16*)Ws3,
+    constexpr int BN = EPI == EPI_SWIGLU ? 64 : 128;
+    const unsigned mtiles = (unsigned)((rows + 127) / 128) + G;
+    hipLaunchKernelGGL((gemm_bf16_kernel<EPI, HB>), dim3(mtiles * (N / BN)), dim3(256), 0, s, A,
+                       (const bf16*)W, (const bf16*)W3, bias, (const bf16*)Ws, (const bf16*)Ws3,
                        bias_s, E, G, offsets, (int)rows, C, N, K);
   } else {
+    const unsigned mtiles = (unsigned)((rows + kGemmBM - 1) / kGemmBM) + G;
     hipLaunchKernelGGL((gemm_f32_kernel<EPI, HB>), dim3(mtiles * ((N + 255) / 256)), dim3(256), 0,
                        s, A, (const float*)W, (const float*)W3, bias, (const float*)Ws,
                        (const float*)Ws3, bias_s, E, G, offsets, (int)rows, C, N, K);

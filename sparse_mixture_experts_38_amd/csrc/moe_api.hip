@@ -71,7 +71,7 @@ static int validate(const moe_config* c) {
   if (c->tokens > (int64_t)1 << 28 || rows >= ((int64_t)1 << 31) - 4096) return MOE_ERR_UNSUPPORTED;
   if (c->d_model > (1 << 20) || c->d_ff > (1 << 20)) return MOE_ERR_UNSUPPORTED;
   if (c->d_model % 8 || c->d_ff % 8) return MOE_ERR_UNSUPPORTED;
-  if (c->act_dtype == MOE_BF16 && (c->d_model % kGemmBN || c->d_ff % kGemmBN))
+  if (c->act_dtype == MOE_BF16 && (c->d_model % kGemmAlign || c->d_ff % kGemmAlign))
     return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }

@@ -12,16 +12,17 @@ typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // 16-byte register value
 
 constexpr int kWave = 64;
 
 // Assignments ranked per block by the dispatch histogram kernel.
 constexpr int kRankChunk = 1024;
 
-// Block tile of the grouped expert GEMM.
+// Row tile of the float32 expert GEMM; the bf16 GEMM needs d_model and d_ff to
+// be multiples of kGemmAlign (its 256-wide N tiles and 64-deep K steps).
 constexpr int kGemmBM = 128;
-constexpr int kGemmBN = 128;
-constexpr int kGemmBK = 64;
+constexpr int kGemmAlign = 256;
 
 // ------------------------------------------------------------------ helpers
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {

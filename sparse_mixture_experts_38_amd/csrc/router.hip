@@ -212,20 +212,33 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
   }
 }
 
-// P_i = (1/T) sum of the per-block partials (fixed order, float64 sum),
-// z = (1/T) sum_t lse_t^2.
+// P_i = (1/T) sum of the per-block partials and z = (1/T) sum_t lse_t^2.
+// Block e < E reduces column e, block E the lse^2 column, and block E + 1
+// zero-fills the unused expert slots; each block sums in a fixed order (a
+// strided float64 pass per thread, then a tree in LDS), so the result is
+// deterministic.
 __global__ __launch_bounds__(256) void route_stats_kernel(const float* __restrict__ partials,
                                                           int nblocks, int E, int64_t T,
                                                           moe_stats* __restrict__ stats) {
-  const int e = threadIdx.x;
+  __shared__ double red[256];
+  const int col = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (col == E + 1) {
+    for (int e = E + tid; e < MOE_MAX_EXPERTS; e += 256) stats->prob_mean[e] = 0.f;
+    return;
+  }
   double s = 0.0;
-  if (e < E)
-    for (int b = 0; b < nblocks; ++b) s += partials[(int64_t)b * (E + 1) + e];
-  stats->prob_mean[e] = (e < E) ? (float)(s / (double)T) : 0.f;
-  if (e == 0) {
-    double z = 0.0;
-    for (int b = 0; b < nblocks; ++b) z += partials[(int64_t)b * (E + 1) + E];
-    stats->z_loss = (float)(z / (double)T);
+  for (int b = tid; b < nblocks; b += 256) s += partials[(int64_t)b * (E + 1) + col];
+  red[tid] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) red[tid] += red[tid + w];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    const float v = (float)(red[0] / (double)T);
+    if (col < E) stats->prob_mean[col] = v;
+    else stats->z_loss = v;
   }
 }
 
@@ -288,7 +301,7 @@ hipError_t launch_route(const moe_config& c, const WsLayout& L, const void* x, c
   }
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(route_stats_kernel, dim3(1), dim3(MOE_MAX_EXPERTS), 0, s, partials,
+  hipLaunchKernelGGL(route_stats_kernel, dim3(E + 2), dim3(256), 0, s, partials,
                      L.route_blocks, E, (int64_t)c.tokens, stats);
   return hipGetLastError();
 }

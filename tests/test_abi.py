@@ -74,13 +74,13 @@ def test_capacity_sweep_matches_oracle_exactly():
                                              [0, 4, 1000]):
         if k > E:
             continue
-        cfg = A.make_config(tokens=T, d_model=128, d_ff=128, num_experts=E, top_k=k,
+        cfg = A.make_config(tokens=T, d_model=256, d_ff=256, num_experts=E, top_k=k,
                             drop_tokens=True, capacity_factor=cf, min_capacity=mc)
         assert A.capacity(cfg) == O.capacity(T, E, k, cf, mc, True), (T, E, k, cf, mc)
 
 
 def _base(**kw):
-    v = dict(tokens=64, d_model=128, d_ff=256, num_experts=8, top_k=2, act_dtype="bf16")
+    v = dict(tokens=64, d_model=256, d_ff=512, num_experts=8, top_k=2, act_dtype="bf16")
     raw = {n: kw.pop(n) for n in ("has_bias",) if n in kw}   # passed through unnormalised
     v.update(kw)
     cfg = A.make_config(**v)
@@ -107,7 +107,8 @@ def _base(**kw):
     (dict(drop_tokens=True, capacity_factor=float("nan")), A.MOE_ERR_INVALID_ARG),
     (dict(drop_tokens=True, min_capacity=-1), A.MOE_ERR_INVALID_ARG),
     (dict(d_model=100), A.MOE_ERR_UNSUPPORTED),
-    (dict(d_model=136), A.MOE_ERR_UNSUPPORTED),      # bf16 GEMM tiles need multiples of 128
+    (dict(d_model=136), A.MOE_ERR_UNSUPPORTED),      # bf16 GEMM tiles need multiples of 256
+    (dict(d_ff=384), A.MOE_ERR_UNSUPPORTED),
     (dict(d_ff=200, act_dtype="f32"), A.MOE_OK),
     (dict(tokens=0), A.MOE_OK),
 ])

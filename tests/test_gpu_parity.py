@@ -25,7 +25,7 @@ CASES = {
     # DeepSpeed GPT-MoE recipe, fewer tokens, smaller d / F, ragged T
     "gpt_moe_small": W["deepspeed_gpt_moe"].scaled(tokens=1000, d_model=256, d_ff=512),
     # tight capacity so drops happen
-    "gpt_moe_drops": W["deepspeed_gpt_moe"].scaled(tokens=777, d_model=256, d_ff=384,
+    "gpt_moe_drops": W["deepspeed_gpt_moe"].scaled(tokens=777, d_model=256, d_ff=512,
                                                    capacity_factor=0.9),
     # 128 experts, top-1, N(0,2) logit offsets: heavy imbalance and drops
     "many_expert_train": W["many_expert_train"].scaled(tokens=1536, d_model=256, d_ff=256),
@@ -35,7 +35,7 @@ CASES = {
     # DeepSeek-V3 recipe: sigmoid + selection bias, top-8 of 256, shared expert
     "deepseek_small": W["deepseek_v3"].scaled(tokens=300, d_model=512, d_ff=256),
     # ReLU expert (moe_code.py Expert), bf16
-    "relu_bf16": W["deepspeed_gpt_moe"].scaled(tokens=333, d_model=128, d_ff=256, activation="relu",
+    "relu_bf16": W["deepspeed_gpt_moe"].scaled(tokens=333, d_model=256, d_ff=256, activation="relu",
                                                has_gate_bias=True, router_dtype="bf16"),
     # fp32 layer with a binding capacity
     "tiny_fp32_drops": W["tiny_fp32"].scaled(tokens=200, drop_tokens=True, capacity_factor=0.75,
@@ -104,7 +104,7 @@ def test_forward_is_deterministic():
 @pytest.mark.parametrize("case", ["one_token", "k_equals_E", "single_expert", "all_to_one",
                                   "min_capacity_binds"])
 def test_edge_cases(case):
-    base = W["deepspeed_gpt_moe"].scaled(d_model=128, d_ff=128)
+    base = W["deepspeed_gpt_moe"].scaled(d_model=256, d_ff=256)
     if case == "one_token":
         w = base.scaled(tokens=1)
     elif case == "k_equals_E":
@@ -143,7 +143,7 @@ def test_permute_without_gather():
 def test_expert_ffn_on_arbitrary_groups(act):
     # empty groups, a group spanning several tiles, ragged tails
     base = W["mixtral_8x7b"] if act == "swiglu" else W["deepspeed_gpt_moe"]
-    w = base.scaled(tokens=300, d_model=256, d_ff=384, num_experts=6, top_k=2)
+    w = base.scaled(tokens=300, d_model=256, d_ff=512, num_experts=6, top_k=2)
     cfg = A.make_config(w)
     inp = make_inputs(w, seed=5)
     g = to_gpu(inp)
@@ -171,7 +171,7 @@ def test_expert_ffn_on_arbitrary_groups(act):
 
 
 def test_combine_stage():
-    w = W["deepspeed_gpt_moe"].scaled(tokens=100, d_model=128, d_ff=128)
+    w = W["deepspeed_gpt_moe"].scaled(tokens=100, d_model=256, d_ff=256)
     cfg = A.make_config(w)
     gen = torch.Generator().manual_seed(11)
     T, k, d = w.tokens, w.top_k, w.d_model
@@ -190,8 +190,43 @@ def test_combine_stage():
 
 
 def test_zero_tokens_noop_on_gpu():
-    w = W["deepspeed_gpt_moe"].scaled(tokens=0, d_model=128, d_ff=128)
+    w = W["deepspeed_gpt_moe"].scaled(tokens=0, d_model=256, d_ff=256)
     cfg = A.make_config(w)
-    y = torch.empty(0, 128, dtype=torch.bfloat16, device="cuda")
     lib = A.lib()
     assert lib.moe_forward(cfg, None, None, None, None, None, None, 0, None) == A.MOE_OK
+
+
+@pytest.mark.parametrize("name", ["deepspeed_gpt_moe", "many_expert_train"])
+def test_full_size_workload_sampled(name):
+    """At the benchmark's full sizes: logits, top-k, counts, the permutation and
+    the drop set in full; the layer output on a sample of tokens (including
+    tokens that lost a choice to capacity) that the oracle computes row by row."""
+    w = W[name]
+    print(f"[case] full-size {name}", flush=True)
+    inp = make_inputs(w, seed=0, device="cuda")
+    cfg = A.make_config(w)
+    out = gpu_forward(w, inp, cfg)
+    x_np = np64(inp["x"])
+    P = oracle_params(inp)
+    r, bad = check_route(w, x_np, P, out)
+    d = check_dispatch(w, out)
+    T, k = w.tokens, w.top_k
+    rng = np.random.default_rng(0)
+    dropped_tok = np.nonzero(np.any(d["assign_row"] < 0, axis=1))[0]
+    sample = np.unique(np.concatenate([rng.choice(T, 96, replace=False), dropped_tok[:32]]))
+    gates = r["gates"]
+    idx = out["topk_idx"].numpy()
+    y_ref = np.zeros((len(sample), w.d_model))
+    for e in range(w.num_experts):
+        sel = [(si, j) for si, t in enumerate(sample) for j in range(k)
+               if idx[t, j] == e and d["assign_row"][t, j] >= 0]
+        if not sel:
+            continue
+        rows = x_np[[sample[si] for si, _ in sel]]
+        ye = O.expert_ffn(rows, P["w1"][e], None if P["b1"] is None else P["b1"][e], P["w2"][e],
+                          None if P["b2"] is None else P["b2"][e], w.activation,
+                          None if P["w3"] is None else P["w3"][e])
+        for (si, j), yrow in zip(sel, ye):
+            y_ref[si] += gates[sample[si], j] * yrow
+    y_gpu = out["y"].float().numpy()[sample]
+    assert rel_err(y_gpu, y_ref) <= TOL[w.act_dtype]
