@@ -23,6 +23,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer forward tokens/sec on 1 MI355X; grouped-GEMM % of bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
+COPY_BYTES = 256 << 20      # each of read and write for the calibration copy
 GEMM_SOURCE = os.path.join(ROOT, "sparse_mixture_experts_38_amd", "csrc", "expert_gemm.hip")
 
 
@@ -47,7 +48,7 @@ def read_traffic(kernel_key):
     return float(v) if v else None
 
 
-def cpu_baseline(w, inp_gpu, max_seconds=30.0):
+def cpu_baseline(w, inp_gpu, min_seconds=10.0, max_seconds=30.0):
     """The oracle, as it stands, on the same workload's weights and tokens."""
     import numpy as np
     import torch
@@ -73,13 +74,15 @@ def cpu_baseline(w, inp_gpu, max_seconds=30.0):
     P.update({n: (None if inp_gpu[n] is None else PerExpert(inp_gpu[n]))
               for n in ("w1", "w3", "b1", "w2", "b2", "ws1", "ws3", "bs1", "ws2", "bs2")})
     x = f64(inp_gpu["x"])
+    # repeat the full batch until about min_seconds of CPU work is timed (never past max_seconds)
     times = []
-    t_end = time.perf_counter() + max_seconds
-    while len(times) < 3:
+    t_start = time.perf_counter()
+    while True:
         t0 = time.perf_counter()
         O.forward(x, P, w)
         times.append(time.perf_counter() - t0)
-        if time.perf_counter() + times[-1] > t_end:
+        spent = time.perf_counter() - t_start
+        if spent >= min_seconds or spent + times[-1] > max_seconds:
             break
     med = statistics.median(times)
     return {"value": w.tokens / med, "unit": "tokens/s", "cores": threads, "kind": "oracle",
@@ -95,6 +98,9 @@ def main():
     ap.add_argument("--workload", default="deepspeed_gpt_moe")
     ap.add_argument("--sets", type=int, default=3, help="rotated input/weight sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB float32 copy kernel (torch.neg) three times, "
+                         "so that hardware byte counters can be scaled by a kernel of known traffic")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the layer runs "
@@ -119,6 +125,14 @@ def main():
         y = torch.empty(T, d, dtype=act, device="cuda")
         plans.append(A.Plan(cfg, s["x"], A.weights_of(s), y, R, stats, ws))
     torch.cuda.synchronize()
+    if args.copy_calibration:
+        n = COPY_BYTES // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step(i, ev=None):
         p = plans[i % len(plans)]
