@@ -144,6 +144,34 @@ __device__ __forceinline__ void tile_lookup(const TileSpace& ts, int mt, int BM,
   nrows_out = __shfl(nrows, owner, 64);
 }
 
+// GELU(x) = x Phi(x) with Phi(-|x|) = erfc(|x| / sqrt 2) / 2 from the rational
+// approximation of Abramowitz & Stegun, Handbook of Mathematical Functions,
+// formula 7.1.26 (absolute error of erf below 1.5e-7), evaluated with the
+// hardware reciprocal and base-2 exponential. Used where the result is rounded
+// to bf16 (relative step 2^-8), far above the approximation's error.
+__device__ __forceinline__ float gelu_as(float x) {
+  const float z = fabsf(x) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
+  float p = fmaf(1.061405429f, t, -1.453152027f);
+  p = fmaf(p, t, 1.421413741f);
+  p = fmaf(p, t, -0.284496736f);
+  p = fmaf(p, t, 0.254829592f);
+  const float q = 0.5f * p * t * __builtin_amdgcn_exp2f(-1.4426950408889634f * z * z);
+  return x * (x >= 0.f ? 1.0f - q : q);
+}
+
+__device__ __forceinline__ float silu_fast(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
+}
+
+template <int EPI>
+__device__ __forceinline__ float epilogue_bf16(float z1, float z3) {
+  if (EPI == EPI_GELU) return gelu_as(z1);
+  if (EPI == EPI_RELU) return fmaxf(z1, 0.f);
+  if (EPI == EPI_SWIGLU) return silu_fast(z1) * z3;
+  return z1;
+}
+
 // Grouped GEMM, C[r, n] = epi(sum_k A[r, k] W_g[n, k] + b_g[n]); group g < E
 // takes expert weights W + g N K, group E (shared expert) takes Ws.
 //
@@ -157,12 +185,14 @@ __device__ __forceinline__ void tile_lookup(const TileSpace& ts, int mt, int BM,
 // step k + 1 go to the other LDS stage at the end of step k. A stage holds 256
 // rows of 128 bytes (128 A rows, then the B rows); 16-byte chunk c of row r
 // sits at chunk c ^ ((r >> 1) & 7), so the 16 lanes of one LDS cycle (16
-// consecutive rows, one chunk) cover all 64 banks once. The MFMA takes the
-// weight fragment first, so a lane's accumulators hold four consecutive output
-// columns of one row and the epilogue stores 8 bytes at a time. Blocks are
-// dispatched to the 8 XCDs round-robin; the block id is remapped so that each
-// XCD runs a contiguous range of tiles, ordered in groups of 8 M tiles, whose
-// operands then meet in that XCD's L2.
+// consecutive rows, one chunk) cover all 64 banks once. Within a K step the
+// fragments of sub-step s + 1 are read while sub-step s multiplies. The MFMA
+// takes the weight fragment first, so a lane's accumulators hold four
+// consecutive output columns of one row. The epilogue adds the bias, applies
+// the activation, stages the bf16 tile in LDS and writes whole 256-byte row
+// segments. Blocks are dispatched to the 8 XCDs round-robin; the block id is
+// remapped so that each XCD runs a contiguous range of tiles, ordered in
+// groups of 8 M tiles, whose operands then meet in that XCD's L2.
 template <int EPI, bool HAS_BIAS>
 __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
     const bf16* __restrict__ A, const bf16* __restrict__ W, const bf16* __restrict__ W3,
@@ -178,6 +208,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
   constexpr int ROWS = BM + NB * BN;               // 256 LDS rows per stage
   constexpr int STAGE = ROWS * CH;                 // u32x4 per stage (32 KB)
   constexpr int GROUP_M = 8;
+  constexpr int CQ = BN / 8;                       // 16-byte chunks per output row
   __shared__ u32x4 smem[2 * STAGE];
 
   // XCD-aware order of the tiles
@@ -200,6 +231,10 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
   if (nt >= ntn) return;
   int g, row0, nrows;
   tile_lookup(ts, mt, BM, g, row0, nrows);
+  // uniform over the block: keep them in scalar registers
+  g = __builtin_amdgcn_readfirstlane(g);
+  row0 = __builtin_amdgcn_readfirstlane(row0);
+  nrows = __builtin_amdgcn_readfirstlane(nrows);
   const int n0 = nt * BN;
   const bf16* Wg = g < E ? W + (int64_t)g * N * K : Ws;
   const bf16* W3g = GATED ? (g < E ? W3 + (int64_t)g * N * K : Ws3) : Wg;
@@ -218,123 +253,180 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
   const int wslot = lr * CH + (lc ^ ((tid >> 4) & 7));
   const int rsw = (fr >> 1) & 7;                   // fragment rows: (r >> 1) & 7
 
-  // per-thread source offsets (bf16 elements) from the tile's bases; A rows
-  // past the tile's end repeat its last row
-  const bf16* a_base = A + (int64_t)row0 * K + lc * 8;
-  const bf16* b_base = Wg + (int64_t)n0 * K + lc * 8;
-  // W3 rows of the B part start at LDS row BN (= 64) for SwiGLU
-  const bf16* b3_base = W3g + (int64_t)(n0 - BN) * K + lc * 8;
-  const uint32_t aoff[4] = {(uint32_t)(min(lr, nrows - 1) * K), (uint32_t)(min(lr + 32, nrows - 1) * K),
-                            (uint32_t)(min(lr + 64, nrows - 1) * K),
-                            (uint32_t)(min(lr + 96, nrows - 1) * K)};
-  const uint32_t boff0 = (uint32_t)(lr * K);
+  // Uniform base addresses and per-thread 32-bit byte offsets (A rows past the
+  // tile's end repeat its last row). W3 rows of the B part start at LDS row
+  // BN (= 64) for SwiGLU.
+  const char* a_s = reinterpret_cast<const char*>(A + (int64_t)row0 * K);
+  const char* b_s = reinterpret_cast<const char*>(Wg + (int64_t)n0 * K);
+  const char* b3_s = GATED ? reinterpret_cast<const char*>(W3g + (int64_t)(n0 - BN) * K) : b_s;
+  const uint32_t ao0 = (uint32_t)(min(lr, nrows - 1) * K + lc * 8) * 2u;
+  const uint32_t ao1 = (uint32_t)(min(lr + 32, nrows - 1) * K + lc * 8) * 2u;
+  const uint32_t ao2 = (uint32_t)(min(lr + 64, nrows - 1) * K + lc * 8) * 2u;
+  const uint32_t ao3 = (uint32_t)(min(lr + 96, nrows - 1) * K + lc * 8) * 2u;
+  const uint32_t bo0 = (uint32_t)(lr * K + lc * 8) * 2u;
+  const uint32_t bo1 = bo0 + (uint32_t)(64 * K);    // + 32 rows
+  const uint32_t bo2 = bo0 + (uint32_t)(128 * K);
+  const uint32_t bo3 = bo0 + (uint32_t)(192 * K);
+
+  // LDS fragment rows: f = 0, 1 are A sub-tiles i = f; f = 2, 3 are B sub-tiles
+  // jb = f - 2 (column block j of W, or W1 / W3 for SwiGLU).
+  static_assert(TM == 2 && NB * TN == 2, "fragment plan");
+  int fbase[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    const int jb = f - 2;
+    const int row = f < 2 ? wm * 64 + f * 32 + fr
+                          : BM + (NB == 1 ? wn * WN + jb * 32 : jb * BN + wn * WN) + fr;
+    fbase[f] = row * CH;
+  }
+  constexpr int kRO[4] = {0, 2, 1, 3};   // fragment read order
+  int cidx[4];
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4) cidx[s4] = (s4 * 2 + fk) ^ rsw;
 
   // register stages for even / odd K steps (named registers, not arrays, so
   // that they stay in VGPRs)
-  struct Regs { u32x4 a0, a1, a2, a3, b0, b1, b2, b3; };
+  struct Regs { u32x4 v0, v1, v2, v3, v4, v5, v6, v7; };
   Regs r0, r1;
-  const bf16* bsrc2 = GATED ? b3_base : b_base;   // rows 64.. of the B part (W3 for SwiGLU)
-  const uint32_t K32 = (uint32_t)(32 * K);
-#define MOE_GLOAD(R, kt)                                                             \
+  bf16x8 fr0[4], fr1[4];   // fragments of two consecutive sub-steps
+  f32x16 acc[4];           // acc[i + 2 jb] = A sub-tile i times B sub-tile jb
+#pragma unroll
+  for (int k4 = 0; k4 < 4; ++k4)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[k4][r] = 0.f;
+
+#define MOE_SB() __builtin_amdgcn_sched_barrier(0)
+#define MOE_G(R, kt, i)                                                              \
   do {                                                                               \
-    const int k0_ = (kt) * BK;                                                       \
-    R.a0 = *reinterpret_cast<const u32x4*>(a_base + k0_ + aoff[0]);                  \
-    R.a1 = *reinterpret_cast<const u32x4*>(a_base + k0_ + aoff[1]);                  \
-    R.a2 = *reinterpret_cast<const u32x4*>(a_base + k0_ + aoff[2]);                  \
-    R.a3 = *reinterpret_cast<const u32x4*>(a_base + k0_ + aoff[3]);                  \
-    R.b0 = *reinterpret_cast<const u32x4*>(b_base + k0_ + boff0);                    \
-    R.b1 = *reinterpret_cast<const u32x4*>(b_base + k0_ + boff0 + K32);              \
-    R.b2 = *reinterpret_cast<const u32x4*>(bsrc2 + k0_ + boff0 + 2 * K32);           \
-    R.b3 = *reinterpret_cast<const u32x4*>(bsrc2 + k0_ + boff0 + 3 * K32);           \
+    const uint32_t kb_ = (uint32_t)(kt) * (BK * 2);                                  \
+    if ((i) == 0) R.v0 = *reinterpret_cast<const u32x4*>(a_s + kb_ + ao0);           \
+    if ((i) == 1) R.v1 = *reinterpret_cast<const u32x4*>(a_s + kb_ + ao1);           \
+    if ((i) == 2) R.v2 = *reinterpret_cast<const u32x4*>(a_s + kb_ + ao2);           \
+    if ((i) == 3) R.v3 = *reinterpret_cast<const u32x4*>(a_s + kb_ + ao3);           \
+    if ((i) == 4) R.v4 = *reinterpret_cast<const u32x4*>(b_s + kb_ + bo0);           \
+    if ((i) == 5) R.v5 = *reinterpret_cast<const u32x4*>(b_s + kb_ + bo1);           \
+    if ((i) == 6) R.v6 = *reinterpret_cast<const u32x4*>(b3_s + kb_ + bo2);          \
+    if ((i) == 7) R.v7 = *reinterpret_cast<const u32x4*>(b3_s + kb_ + bo3);          \
   } while (0)
-#define MOE_LSTORE(R, st)                                                            \
+#define MOE_W(R, st, i)                                                              \
   do {                                                                               \
     u32x4* d_ = smem + (st) * STAGE + wslot;                                         \
-    d_[0] = R.a0;                                                                    \
-    d_[32 * CH] = R.a1;                                                              \
-    d_[64 * CH] = R.a2;                                                              \
-    d_[96 * CH] = R.a3;                                                              \
-    d_[BM * CH] = R.b0;                                                              \
-    d_[(BM + 32) * CH] = R.b1;                                                       \
-    d_[(BM + 64) * CH] = R.b2;                                                       \
-    d_[(BM + 96) * CH] = R.b3;                                                       \
+    if ((i) == 0) d_[0] = R.v0;                                                      \
+    if ((i) == 1) d_[32 * CH] = R.v1;                                                \
+    if ((i) == 2) d_[64 * CH] = R.v2;                                                \
+    if ((i) == 3) d_[96 * CH] = R.v3;                                                \
+    if ((i) == 4) d_[BM * CH] = R.v4;                                                \
+    if ((i) == 5) d_[(BM + 32) * CH] = R.v5;                                         \
+    if ((i) == 6) d_[(BM + 64) * CH] = R.v6;                                         \
+    if ((i) == 7) d_[(BM + 96) * CH] = R.v7;                                         \
   } while (0)
-#define MOE_COMPUTE(st)                                                              \
+#define MOE_R(F, st, s4, f)                                                          \
+  F[f] = __builtin_bit_cast(bf16x8, smem[(st) * STAGE + fbase[f] + cidx[s4]])
+#define MOE_M(F, q)                                                                  \
+  acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F[2 + ((q) >> 1)], F[(q) & 1], acc[q], 0, 0, 0)
+  // One K step from LDS stage st: 16 MFMAs in four sub-steps, MFMA q taking
+  // A sub-tile q & 1 and B sub-tile q >> 1; fragments are read in the order
+  // A0 B0 A1 B1 so that each MFMA waits only for the reads it needs. Each MFMA
+  // is followed by one fragment read of the next sub-step and, in sub-steps 0 / 1,
+  // two global loads of register set RG (step KL) or, in sub-steps 2 / 3, one
+  // LDS write of register set RW to the other stage. LD / WR switch those off.
+#define MOE_STEP(st, RG, KL, LD, RW, WR)                                             \
   do {                                                                               \
-    const u32x4* cur_ = smem + (st) * STAGE;                                         \
-    _Pragma("unroll") for (int s = 0; s < BK / 16; ++s) {                            \
-      const int ch_ = (s * 2 + fk) ^ rsw;                                            \
-      bf16x8 fa_[TM], fb_[NB][TN];                                                   \
-      _Pragma("unroll") for (int i = 0; i < TM; ++i) fa_[i] =                        \
-          __builtin_bit_cast(bf16x8, cur_[(wm * 64 + i * 32 + fr) * CH + ch_]);      \
-      _Pragma("unroll") for (int bb = 0; bb < NB; ++bb)                              \
-        _Pragma("unroll") for (int j = 0; j < TN; ++j) fb_[bb][j] = __builtin_bit_cast( \
-            bf16x8, cur_[(BM + bb * BN + wn * WN + j * 32 + fr) * CH + ch_]);        \
-      _Pragma("unroll") for (int bb = 0; bb < NB; ++bb)                              \
-        _Pragma("unroll") for (int i = 0; i < TM; ++i)                               \
-          _Pragma("unroll") for (int j = 0; j < TN; ++j) acc[bb][i][j] =             \
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb_[bb][j], fa_[i], acc[bb][i][j], \
-                                                      0, 0, 0);                      \
+    MOE_R(fr0, st, 0, 0); MOE_R(fr0, st, 0, 2); MOE_R(fr0, st, 0, 1);                \
+    MOE_R(fr0, st, 0, 3); MOE_SB();                                                  \
+    _Pragma("unroll") for (int k_ = 0; k_ < 4; ++k_) {                               \
+      MOE_M(fr0, k_); MOE_SB(); MOE_R(fr1, st, 1, kRO[k_]); MOE_SB();                     \
+      if (LD) { MOE_G(RG, KL, 2 * k_); MOE_G(RG, KL, 2 * k_ + 1); }                  \
+      MOE_SB();                                                                      \
+    }                                                                                \
+    _Pragma("unroll") for (int k_ = 0; k_ < 4; ++k_) {                               \
+      MOE_M(fr1, k_); MOE_SB(); MOE_R(fr0, st, 2, kRO[k_]); MOE_SB();                     \
+    }                                                                                \
+    _Pragma("unroll") for (int k_ = 0; k_ < 4; ++k_) {                               \
+      MOE_M(fr0, k_); MOE_SB(); MOE_R(fr1, st, 3, kRO[k_]); MOE_SB();                     \
+      if (WR) MOE_W(RW, 1 - (st), k_);                                               \
+      MOE_SB();                                                                      \
+    }                                                                                \
+    _Pragma("unroll") for (int k_ = 0; k_ < 4; ++k_) {                               \
+      MOE_M(fr1, k_); MOE_SB();                                                      \
+      if (WR) MOE_W(RW, 1 - (st), 4 + k_);                                           \
+      MOE_SB();                                                                      \
     }                                                                                \
   } while (0)
 
-  f32x16 acc[NB][TM][TN];
+  // K is a multiple of 256, so nk >= 4 and even; the last two steps are
+  // peeled so that the loop body has no branches.
+  const int nk = K / BK;
 #pragma unroll
-  for (int bb = 0; bb < NB; ++bb)
+  for (int i = 0; i < 8; ++i) MOE_G(r0, 0, i);
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < 8; ++i) MOE_G(r1, 1, i);
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[bb][i][j][r] = 0.f;
-
-  const int nk = K / BK;   // even: K is a multiple of 256
-  MOE_GLOAD(r0, 0);
-  MOE_GLOAD(r1, 1);
-  MOE_LSTORE(r0, 0);
+  for (int i = 0; i < 8; ++i) MOE_W(r0, 0, i);
   __syncthreads();
-  for (int kt = 0; kt < nk; kt += 2) {
-    // even step kt: stage 0 holds it, r1 holds step kt + 1, r0 is free
-    if (kt + 2 < nk) MOE_GLOAD(r0, kt + 2);
-    MOE_COMPUTE(0);
-    MOE_LSTORE(r1, 1);
+  for (int kt = 0; kt < nk - 2; kt += 2) {
+    // even step kt: stage 0 holds it, r1 holds step kt + 1, r0 is loaded with kt + 2
+    MOE_STEP(0, r0, kt + 2, true, r1, true);
     __syncthreads();
-    // odd step kt + 1: stage 1 holds it, r0 holds step kt + 2, r1 is free
-    if (kt + 3 < nk) MOE_GLOAD(r1, kt + 3);
-    MOE_COMPUTE(1);
-    if (kt + 2 < nk) MOE_LSTORE(r0, 0);
+    // odd step kt + 1: stage 1 holds it, r0 holds step kt + 2, r1 is loaded with kt + 3
+    MOE_STEP(1, r1, kt + 3, true, r0, true);
     __syncthreads();
   }
-#undef MOE_GLOAD
-#undef MOE_LSTORE
-#undef MOE_COMPUTE
+  MOE_STEP(0, r0, 0, false, r1, true);
+  __syncthreads();
+  MOE_STEP(1, r1, 0, false, r0, false);
+#undef MOE_SB
+#undef MOE_G
+#undef MOE_W
+#undef MOE_R
+#undef MOE_M
+#undef MOE_STEP
 
-  // Epilogue: register r of a 32x32 accumulator holds row (lane % 32) and
-  // column 8 (r / 4) + 4 (lane / 32) + r % 4 of the sub-tile.
+  // Epilogue. Register r of a 32x32 accumulator holds row (lane % 32) and
+  // column 8 (r / 4) + 4 (lane / 32) + r % 4 of the sub-tile, so lane (fr, fk)
+  // owns 8 bytes of 16-byte output chunk q = wn WN / 8 + 4 j + r / 4.
+  float4 bv[TN][4];
 #pragma unroll
-  for (int j = 0; j < TN; ++j) {
+  for (int j = 0; j < TN; ++j)
 #pragma unroll
-    for (int qd = 0; qd < 4; ++qd) {
-      const int n = n0 + wn * WN + j * 32 + qd * 8 + fk * 4;
-      float4 bv = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (HAS_BIAS) bv = *reinterpret_cast<const float4*>(bg + n);
+    for (int qd = 0; qd < 4; ++qd)
+      bv[j][qd] = HAS_BIAS ? *reinterpret_cast<const float4*>(bg + n0 + wn * WN + j * 32 + qd * 8 + fk * 4)
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
+  __syncthreads();   // every wave is done reading the operand stages
+  // bf16 tile staged as BM rows of CQ chunks; chunk q of row m at q ^ swz(m)
+  uint2* st8 = reinterpret_cast<uint2*>(smem);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int m = wm * 64 + i * 32 + fr;
-        if (m < nrows) {
-          const float z[4] = {acc[0][i][j][qd * 4 + 0] + bv.x, acc[0][i][j][qd * 4 + 1] + bv.y,
-                              acc[0][i][j][qd * 4 + 2] + bv.z, acc[0][i][j][qd * 4 + 3] + bv.w};
-          float v[4];
+  for (int i = 0; i < TM; ++i) {
+    const int m = wm * 64 + i * 32 + fr;
+    const int swz = CQ == 16 ? (m & 15) : ((m >> 1) & 7);
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            v[e] = epilogue<EPI>(z[e], GATED ? acc[NB - 1][i][j][qd * 4 + e] : 0.f);
-          uint2 u;
-          u.x = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
-          u.y = (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
-          *reinterpret_cast<uint2*>(C + (int64_t)(row0 + m) * N + n) = u;
-        }
+    for (int j = 0; j < TN; ++j) {
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        const float4 bq = bv[j][qd];
+        const float z[4] = {acc[i + 2 * j][qd * 4 + 0] + bq.x, acc[i + 2 * j][qd * 4 + 1] + bq.y,
+                            acc[i + 2 * j][qd * 4 + 2] + bq.z, acc[i + 2 * j][qd * 4 + 3] + bq.w};
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          v[e] = epilogue_bf16<EPI>(z[e], GATED ? acc[i + 2][qd * 4 + e] : 0.f);
+        uint2 u;
+        u.x = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
+        u.y = (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
+        const int q = wn * (WN / 8) + j * 4 + qd;
+        st8[(m * CQ + (q ^ swz)) * 2 + fk] = u;
       }
     }
+  }
+  __syncthreads();
+  // 16 (SwiGLU 8) consecutive threads write one row's contiguous segment
+#pragma unroll
+  for (int p = 0; p < BM * CQ / 256; ++p) {
+    const int idx = p * 256 + tid;
+    const int m = idx / CQ, q = idx % CQ;
+    const int swz = CQ == 16 ? (m & 15) : ((m >> 1) & 7);
+    if (m < nrows)
+      *reinterpret_cast<u32x4*>(C + (int64_t)(row0 + m) * N + n0 + q * 8) = smem[m * CQ + (q ^ swz)];
   }
 }
 
