@@ -82,40 +82,48 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, i
   return true;
 }
 
-// Per-wave view of the grouped row space used by the persistent kernel: lane l
-// holds groups 5l .. 5l+4 (clamped offsets, tile counts) and the exclusive
-// prefix of tiles before its first group.
+// Per-wave view of the grouped row space: lane l holds groups 5l .. 5l+4
+// (first covered row, end row, tile count) and the exclusive prefix of tiles
+// before its first group. `part` selects the rows covered: 0 all rows of
+// every group in BM-row tiles; 1 the first floor(n / BM) BM-row tiles of each
+// group of n rows; 2 the rows that part 1 leaves over (fewer than `big`), in
+// BM-row tiles.
 struct TileSpace {
-  int o[6];
-  int n[5];
+  int s[5], e[5], n[5];
   int excl, incl, total;
 };
 
 __device__ __forceinline__ void tile_space_init(TileSpace& ts, const int32_t* __restrict__ offsets,
-                                                int G, int rows_max, int BM) {
+                                                int G, int rows_max, int BM, int part = 0,
+                                                int big = 256) {
   constexpr int PER = 5;
   const int lane = threadIdx.x & 63;
   const int g0 = lane * PER;
+  int o[PER + 1];
 #pragma unroll
   for (int i = 0; i <= PER; ++i) {
     const int gi = g0 + i;
-    ts.o[i] = gi <= G ? min(max(offsets[gi], 0), rows_max) : rows_max;
+    o[i] = gi <= G ? min(max(offsets[gi], 0), rows_max) : rows_max;
   }
-  int s = 0;
+  int sum = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int gi = g0 + i;
-    ts.n[i] = (gi < G && ts.o[i + 1] > ts.o[i]) ? (ts.o[i + 1] - ts.o[i] + BM - 1) / BM : 0;
-    s += ts.n[i];
+    const int rows = (gi < G && o[i + 1] > o[i]) ? o[i + 1] - o[i] : 0;
+    const int full = part == 0 ? 0 : rows / big * big;
+    ts.s[i] = o[i] + (part == 2 ? full : 0);
+    ts.e[i] = part == 1 ? o[i] + full : o[i] + rows;
+    ts.n[i] = (ts.e[i] - ts.s[i] + BM - 1) / BM;
+    sum += ts.n[i];
   }
-  int incl = s;
+  int incl = sum;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const int t = __shfl_up(incl, off, 64);
     if (lane >= off) incl += t;
   }
   ts.incl = incl;
-  ts.excl = incl - s;
+  ts.excl = incl - sum;
   ts.total = __shfl(incl, 63, 64);
 }
 
@@ -133,8 +141,8 @@ __device__ __forceinline__ void tile_lookup(const TileSpace& ts, int mt, int BM,
     for (int i = 0; i < PER; ++i) {
       if (g < 0 && mt < acc + ts.n[i]) {
         g = lane * PER + i;
-        row0 = ts.o[i] + (mt - acc) * BM;
-        nrows = min(BM, ts.o[i + 1] - row0);
+        row0 = ts.s[i] + (mt - acc) * BM;
+        nrows = min(BM, ts.e[i] - row0);
       }
       acc += ts.n[i];
     }
@@ -144,20 +152,21 @@ __device__ __forceinline__ void tile_lookup(const TileSpace& ts, int mt, int BM,
   nrows_out = __shfl(nrows, owner, 64);
 }
 
-// GELU(x) = x Phi(x) with Phi(-|x|) = erfc(|x| / sqrt 2) / 2 from the rational
-// approximation of Abramowitz & Stegun, Handbook of Mathematical Functions,
-// formula 7.1.26 (absolute error of erf below 1.5e-7), evaluated with the
-// hardware reciprocal and base-2 exponential. Used where the result is rounded
-// to bf16 (relative step 2^-8), far above the approximation's error.
+// GELU(x) = x Phi(x) = max(x, 0) - |x| Phi(-|x|), with Phi(-|x|) = erfc(|x| / sqrt 2) / 2
+// from the rational approximation of Abramowitz & Stegun, Handbook of
+// Mathematical Functions, formula 7.1.26 (absolute error of erf below 1.5e-7;
+// coefficients halved here), evaluated with the hardware reciprocal and
+// base-2 exponential. Used where the result is rounded to bf16 (relative step
+// 2^-8), far above the approximation's error.
 __device__ __forceinline__ float gelu_as(float x) {
-  const float z = fabsf(x) * 0.70710678118654752f;
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
-  float p = fmaf(1.061405429f, t, -1.453152027f);
-  p = fmaf(p, t, 1.421413741f);
-  p = fmaf(p, t, -0.284496736f);
-  p = fmaf(p, t, 0.254829592f);
-  const float q = 0.5f * p * t * __builtin_amdgcn_exp2f(-1.4426950408889634f * z * z);
-  return x * (x >= 0.f ? 1.0f - q : q);
+  const float ax = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f * 0.70710678118654752f, ax, 1.0f));
+  float p = fmaf(0.5f * 1.061405429f, t, 0.5f * -1.453152027f);
+  p = fmaf(p, t, 0.5f * 1.421413741f);
+  p = fmaf(p, t, 0.5f * -0.284496736f);
+  p = fmaf(p, t, 0.5f * 0.254829592f);
+  const float q = p * t * __builtin_amdgcn_exp2f(-0.72134752044448170f * x * x);
+  return fmaf(-ax, q, fmaxf(x, 0.f));
 }
 
 __device__ __forceinline__ float silu_fast(float z) {
@@ -198,7 +207,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
     const bf16* __restrict__ A, const bf16* __restrict__ W, const bf16* __restrict__ W3,
     const float* __restrict__ bias, const bf16* __restrict__ Ws, const bf16* __restrict__ Ws3,
     const float* __restrict__ bias_s, int E, int G, const int32_t* __restrict__ offsets,
-    int rows_max, bf16* __restrict__ C, int N, int K) {
+    int rows_max, bf16* __restrict__ C, int N, int K, int part) {
   constexpr bool GATED = EPI == EPI_SWIGLU;
   constexpr int BM = 128, BK = 64, CH = BK / 8;   // 8 chunks of 16 B per LDS row
   constexpr int NB = GATED ? 2 : 1;
@@ -211,24 +220,24 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
   constexpr int CQ = BN / 8;                       // 16-byte chunks per output row
   __shared__ u32x4 smem[2 * STAGE];
 
-  // XCD-aware order of the tiles
-  const int nblk = gridDim.x;
-  const int b = blockIdx.x;
-  const int nb8 = nblk & ~7;
-  const int lid = b < nb8 ? (b & 7) * (nb8 >> 3) + (b >> 3) : b;
-  const int ntn = N / BN;
-  const int per_group = GROUP_M * ntn;
-  const int grp = lid / per_group;
-  const int first_m = grp * GROUP_M;
-  const int in = lid - grp * per_group;
-
   TileSpace ts;
-  tile_space_init(ts, offsets, G, rows_max, BM);
-  if (first_m >= ts.total) return;
-  const int gm = min(ts.total - first_m, GROUP_M);
+  tile_space_init(ts, offsets, G, rows_max, BM, part, kGemmBigBM);
+  const int mtiles = __builtin_amdgcn_readfirstlane(ts.total);
+  const int ntn = N / BN;
+  const int tiles = mtiles * ntn;
+  const int b = blockIdx.x;
+  if (b >= tiles) return;
+  // XCD-aware order over the tiles that exist: XCD x (blocks b = x mod 8)
+  // runs a contiguous range of the tile order
+  const int t8 = tiles & ~7;
+  const int t = b < t8 ? (b & 7) * (t8 >> 3) + (b >> 3) : b;
+  const int per_group = GROUP_M * ntn;
+  const int grp = t / per_group;
+  const int first_m = grp * GROUP_M;
+  const int in = t - grp * per_group;
+  const int gm = min(mtiles - first_m, GROUP_M);
   const int mt = first_m + in % gm;
   const int nt = in / gm;
-  if (nt >= ntn) return;
   int g, row0, nrows;
   tile_lookup(ts, mt, BM, g, row0, nrows);
   // uniform over the block: keep them in scalar registers
@@ -430,6 +439,211 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
   }
 }
 
+// Grouped GEMM on the full 256-row tiles of each group (part 1 of the row
+// space): 256 x 256 output tiles (SwiGLU: 256 x 128 of W1 and of W3), one block
+// of four waves per CU, each wave 128 x 128 (SwiGLU 128 x 64 per operand) with
+// its 256 float32 accumulators in the accumulation registers. A 256 x 256 tile
+// needs half the bytes per FLOP of a 128 x 128 one, which keeps the CU's
+// address unit below saturation. Operands go global -> LDS directly
+// (global_load_lds_dwordx4), 64-deep K steps, two stages of 512 rows x 128 B
+// (A rows, then B rows) held in two separate LDS arrays so that the compiler
+// can tell the loads into one stage from the fragment reads of the other.
+// The loads of step k + 1 are issued during the first half of step k, and
+// every wave waits for its own loads before the barrier that ends step k.
+// Lane l of a load lands at LDS row (l >> 3) of its 8-row group and physical
+// chunk l & 7, which holds logical chunk (l & 7) ^ ((row >> 1) & 7): the
+// same conflict-free layout as the 128 x 128 kernel. The epilogue adds the
+// bias, applies the activation, stages the bf16 tile in LDS and writes whole
+// 512-byte row segments.
+template <int EPI, bool HAS_BIAS>
+__global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(
+    const bf16* __restrict__ A, const bf16* __restrict__ W, const bf16* __restrict__ W3,
+    const float* __restrict__ bias, const bf16* __restrict__ Ws, const bf16* __restrict__ Ws3,
+    const float* __restrict__ bias_s, int E, int G, const int32_t* __restrict__ offsets,
+    int rows_max, bf16* __restrict__ C, int N, int K) {
+  constexpr bool GATED = EPI == EPI_SWIGLU;
+  constexpr int BM = 256, BK = 64, CH = BK / 8;   // 8 chunks of 16 B per LDS row
+  constexpr int NB = GATED ? 2 : 1;
+  constexpr int BN = GATED ? 128 : 256;           // columns per B operand = output columns
+  constexpr int WN = BN / 2;                       // per wave, per operand
+  constexpr int TN = WN / 32;                      // 4 (SwiGLU 2)
+  constexpr int STAGE = 512 * CH;                  // u32x4 per stage (64 KB)
+  constexpr int GROUP_M = 8;
+  constexpr int CQ = BN / 8;                       // 16-byte chunks per output row
+  static_assert(NB * TN == 4, "four B fragments per sub-step");
+  static_assert(128 * CQ <= STAGE, "half of the output tile fits one stage");
+  __shared__ u32x4 sm0[STAGE], sm1[STAGE];
+
+  TileSpace ts;
+  tile_space_init(ts, offsets, G, rows_max, BM, 1, BM);
+  const int mtiles = __builtin_amdgcn_readfirstlane(ts.total);
+  const int ntn = N / BN;
+  const int tiles = mtiles * ntn;
+  const int b = blockIdx.x;
+  if (b >= tiles) return;
+  const int t8 = tiles & ~7;
+  const int t = b < t8 ? (b & 7) * (t8 >> 3) + (b >> 3) : b;
+  const int per_group = GROUP_M * ntn;
+  const int grp = t / per_group;
+  const int first_m = grp * GROUP_M;
+  const int in = t - grp * per_group;
+  const int gm = min(mtiles - first_m, GROUP_M);
+  const int mt = first_m + in % gm;
+  const int nt = in / gm;
+  int g, row0, nrows;
+  tile_lookup(ts, mt, BM, g, row0, nrows);
+  g = __builtin_amdgcn_readfirstlane(g);
+  row0 = __builtin_amdgcn_readfirstlane(row0);
+  nrows = __builtin_amdgcn_readfirstlane(nrows);   // BM: part 1 has only full tiles
+  const int n0 = nt * BN;
+  const bf16* Wg = g < E ? W + (int64_t)g * N * K : Ws;
+  const bf16* W3g = GATED ? (g < E ? W3 + (int64_t)g * N * K : Ws3) : Wg;
+  const float* bg = HAS_BIAS ? (g < E ? bias + (int64_t)g * N : bias_s) : nullptr;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int fr = lane & 31;
+  const int fk = lane >> 5;
+
+  // Direct-to-LDS loads: wave w fills stage rows 128 w .. 128 w + 127 (waves 0
+  // and 1: A rows; 2 and 3: W rows n0 .., or W1 then W3 rows for SwiGLU), 8 rows
+  // per instruction i; (row >> 1) & 7 = (4 (i & 1) + (lane >> 4)) & 7.
+  const bf16* src = wave < 2 ? A + (int64_t)(row0 + wave * 128) * K
+                   : GATED ? (wave == 2 ? Wg : W3g) + (int64_t)n0 * K
+                           : Wg + (int64_t)(n0 + (wave - 2) * 128) * K;
+  const char* dsrc = reinterpret_cast<const char*>(src);
+  const int pc = lane & 7, lq = lane >> 4;
+  uint32_t doff[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    doff[i] = (uint32_t)((8 * i + (lane >> 3)) * K + (pc ^ ((4 * (i & 1) + lq) & 7)) * 8) * 2u;
+  const int dl = wave * 128 * CH;
+
+  int fbase[8];
+#pragma unroll
+  for (int f = 0; f < 8; ++f) {
+    const int jb = f - 4;
+    const int row = f < 4 ? wm * 128 + f * 32 + fr
+                          : 256 + (jb / TN) * BN + wn * WN + (jb % TN) * 32 + fr;
+    fbase[f] = row * CH;
+  }
+  const int rsw = (fr >> 1) & 7;
+  int cidx[4];
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4) cidx[s4] = (s4 * 2 + fk) ^ rsw;
+  constexpr int kRO[8] = {0, 4, 1, 2, 3, 5, 6, 7};   // read order: A0 B0 A1 A2 A3 B1 B2 B3
+
+  bf16x8 fa[8], fb[8];
+  f32x16 acc[16];   // acc[i + 4 jb] = A sub-tile i times B sub-tile jb
+#pragma unroll
+  for (int q = 0; q < 16; ++q)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[q][r] = 0.f;
+
+#define MOE_SB() __builtin_amdgcn_sched_barrier(0)
+#define MOE_SM(x) ((x) == 0 ? sm0 : sm1)
+#define MOE_D(x, kt, i)                                                              \
+  __builtin_amdgcn_global_load_lds(dsrc + doff[i] + (uint32_t)(kt) * (BK * 2),       \
+                                   (void*)(MOE_SM(x) + dl + (i) * 8 * CH), 16, 0, 0)
+#define MOE_R(F, x, s4, f)                                                           \
+  F[f] = __builtin_bit_cast(bf16x8, MOE_SM(x)[fbase[f] + cidx[s4]])
+#define MOE_M(F, q)                                                                  \
+  acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F[4 + ((q) >> 2)], F[(q) & 3], acc[q], 0, 0, 0)
+  // wait for this wave's direct-to-LDS loads (vmcnt 0, expcnt and lgkmcnt free)
+#define MOE_WAIT_LOADS() __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8))
+  // One K step from stage x: 64 MFMAs in four sub-steps; each MFMA is
+  // followed by one fragment read of the next sub-step, and every third of
+  // the first 48 by one of the 16 loads of step KL into the other stage (LD):
+  // spread out, the loads do not queue up in the address unit and hold back
+  // the MFMAs behind them, and they still have a quarter step to land.
+#define MOE_STEP(x, KL, LD)                                                          \
+  do {                                                                               \
+    _Pragma("unroll") for (int f_ = 0; f_ < 8; ++f_) MOE_R(fa, x, 0, kRO[f_]);       \
+    MOE_SB();                                                                        \
+    _Pragma("unroll") for (int q_ = 0; q_ < 16; ++q_) {                              \
+      MOE_M(fa, q_); MOE_SB();                                                       \
+      if (q_ < 8) MOE_R(fb, x, 1, kRO[q_]);                                          \
+      if ((LD) && q_ % 3 == 0) MOE_D(1 - (x), KL, q_ / 3);                           \
+      MOE_SB();                                                                      \
+    }                                                                                \
+    _Pragma("unroll") for (int q_ = 0; q_ < 16; ++q_) {                              \
+      MOE_M(fb, q_); MOE_SB();                                                       \
+      if (q_ < 8) MOE_R(fa, x, 2, kRO[q_]);                                          \
+      if ((LD) && (16 + q_) % 3 == 0) MOE_D(1 - (x), KL, (16 + q_) / 3);             \
+      MOE_SB();                                                                      \
+    }                                                                                \
+    _Pragma("unroll") for (int q_ = 0; q_ < 16; ++q_) {                              \
+      MOE_M(fa, q_); MOE_SB();                                                       \
+      if (q_ < 8) MOE_R(fb, x, 3, kRO[q_]);                                          \
+      if ((LD) && (32 + q_) % 3 == 0 && 32 + q_ < 48) MOE_D(1 - (x), KL, (32 + q_) / 3); \
+      MOE_SB();                                                                      \
+    }                                                                                \
+    _Pragma("unroll") for (int q_ = 0; q_ < 16; ++q_) { MOE_M(fb, q_); MOE_SB(); }   \
+    MOE_WAIT_LOADS();                                                                \
+    __builtin_amdgcn_s_barrier();                                                    \
+    MOE_SB();                                                                        \
+  } while (0)
+
+  // K is a multiple of 256, so nk >= 4 and even
+  const int nk = K / BK;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) MOE_D(0, 0, i);
+  MOE_WAIT_LOADS();
+  __builtin_amdgcn_s_barrier();
+  MOE_SB();
+  for (int kt = 0; kt < nk - 2; kt += 2) {
+    MOE_STEP(0, kt + 1, true);
+    MOE_STEP(1, kt + 2, true);
+  }
+  MOE_STEP(0, nk - 1, true);
+  MOE_STEP(1, 0, false);
+#undef MOE_SB
+#undef MOE_D
+#undef MOE_R
+#undef MOE_M
+#undef MOE_WAIT_LOADS
+#undef MOE_STEP
+
+  // Epilogue: rows 0..127 of the tile are staged in sm0, rows 128..255 in sm1
+  // (wave row half wm); chunk q of row m at q ^ (m & 15). The last K step
+  // ended with a barrier, so the stages are free.
+  uint2* st8 = reinterpret_cast<uint2*>(wm ? sm1 : sm0);
+#pragma unroll
+  for (int jx = 0; jx < TN; ++jx) {
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) {
+      const float4 bq = HAS_BIAS ? *reinterpret_cast<const float4*>(bg + n0 + wn * WN + jx * 32 + qd * 8 + fk * 4)
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = i * 32 + fr;   // row within this wave's half
+        const f32x16& a1 = acc[i + 4 * jx];
+        const float z[4] = {a1[qd * 4 + 0] + bq.x, a1[qd * 4 + 1] + bq.y, a1[qd * 4 + 2] + bq.z,
+                            a1[qd * 4 + 3] + bq.w};
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          v[e] = epilogue_bf16<EPI>(z[e], GATED ? acc[i + 4 * (TN + jx)][qd * 4 + e] : 0.f);
+        uint2 uu;
+        uu.x = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
+        uu.y = (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
+        const int q = wn * (WN / 8) + jx * 4 + qd;
+        st8[(m * CQ + (q ^ (m & 15))) * 2 + fk] = uu;
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll 4
+  for (int p = 0; p < BM * CQ / 256; ++p) {
+    const int idx = p * 256 + tid;
+    const int m = idx / CQ, q = idx % CQ;
+    const u32x4 v = (m >> 7 ? sm1 : sm0)[(m & 127) * CQ + (q ^ (m & 15))];
+    if (m < nrows) *reinterpret_cast<u32x4*>(C + (int64_t)(row0 + m) * N + n0 + q * 8) = v;
+  }
+}
+
 // float32 layers: one thread per (row, column) of a tile, plain FMA loop.
 template <int EPI, bool HAS_BIAS>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(
@@ -466,11 +680,31 @@ static hipError_t gemm_launch(const moe_config& c, const ET* A, const void* W, c
   const int E = c.num_experts, G = c.num_experts + c.num_shared_experts;
   const int64_t rows = rows_max(c);
   if constexpr (sizeof(ET) == 2) {
+    constexpr int BNB = EPI == EPI_SWIGLU ? 128 : 256;
     constexpr int BN = EPI == EPI_SWIGLU ? 64 : 128;
-    const unsigned mtiles = (unsigned)((rows + 127) / 128) + G;
-    hipLaunchKernelGGL((gemm_bf16_kernel<EPI, HB>), dim3(mtiles * (N / BN)), dim3(256), 0, s, A,
-                       (const bf16*)W, (const bf16*)W3, bias, (const bf16*)Ws, (const bf16*)Ws3,
-                       bias_s, E, G, offsets, (int)rows, C, N, K);
+    // 256 x 256 tiles pay off where the K loop is long or there is no
+    // activation: one block per CU leaves the epilogue's VALU work exposed,
+    // which two 128 x 128 blocks per CU hide behind each other's MFMAs.
+    const bool big = rows >= kGemmBigBM && (EPI == EPI_NONE || K >= 2048);
+    if (big) {
+      // full 256-row tiles of each group, then the rows left over (< 256 per
+      // group) in 128-row tiles; both grids are bounds, surplus blocks exit
+      const unsigned big_tiles = (unsigned)(rows / kGemmBigBM) * (unsigned)(N / BNB);
+      hipLaunchKernelGGL((gemm_bf16_big_kernel<EPI, HB>), dim3(big_tiles), dim3(256), 0, s, A,
+                         (const bf16*)W, (const bf16*)W3, bias, (const bf16*)Ws, (const bf16*)Ws3,
+                         bias_s, E, G, offsets, (int)rows, C, N, K);
+      // each group leaves at most 255 rows, i.e. at most 2 tiles, and the
+      // tiles number at most ceil(rows / 128) + G
+      const int64_t rest = (rows + 127) / 128 + G < 2 * G ? (rows + 127) / 128 + G : 2 * G;
+      hipLaunchKernelGGL((gemm_bf16_kernel<EPI, HB>), dim3((unsigned)rest * (N / BN)), dim3(256), 0,
+                         s, A, (const bf16*)W, (const bf16*)W3, bias, (const bf16*)Ws,
+                         (const bf16*)Ws3, bias_s, E, G, offsets, (int)rows, C, N, K, 2);
+    } else {
+      const unsigned mtiles = (unsigned)((rows + 127) / 128) + G;
+      hipLaunchKernelGGL((gemm_bf16_kernel<EPI, HB>), dim3(mtiles * (N / BN)), dim3(256), 0, s, A,
+                         (const bf16*)W, (const bf16*)W3, bias, (const bf16*)Ws, (const bf16*)Ws3,
+                         bias_s, E, G, offsets, (int)rows, C, N, K, 0);
+    }
   } else {
     const unsigned mtiles = (unsigned)((rows + kGemmBM - 1) / kGemmBM) + G;
     hipLaunchKernelGGL((gemm_f32_kernel<EPI, HB>), dim3(mtiles * ((N + 255) / 256)), dim3(256), 0,

@@ -20,8 +20,11 @@ constexpr int kWave = 64;
 constexpr int kRankChunk = 1024;
 
 // Row tile of the float32 expert GEMM; the bf16 GEMM needs d_model and d_ff to
-// be multiples of kGemmAlign (its 256-wide N tiles and 64-deep K steps).
+// be multiples of kGemmAlign (its 256-wide N tiles and 64-deep K steps). The
+// bf16 GEMM covers each expert's first floor(rows / kGemmBigBM) * kGemmBigBM
+// rows with 256 x 256 tiles and the rest with 128 x 128 tiles.
 constexpr int kGemmBM = 128;
+constexpr int kGemmBigBM = 256;
 constexpr int kGemmAlign = 256;
 
 // ------------------------------------------------------------------ helpers

@@ -40,6 +40,12 @@ CASES = {
     # fp32 layer with a binding capacity
     "tiny_fp32_drops": W["tiny_fp32"].scaled(tokens=200, drop_tokens=True, capacity_factor=0.75,
                                              min_capacity=4),
+    # long K (d_model 2048) and > 256 rows per expert: both GEMMs use the
+    # 256 x 256 tiles for each expert's full 256-row blocks plus the 128 x 128
+    # tiles for its left-over rows (GELU + bias, and SwiGLU)
+    "gelu_long_k": W["deepspeed_gpt_moe"].scaled(tokens=600, d_model=2048, d_ff=512, num_experts=4,
+                                                 drop_tokens=False),
+    "swiglu_long_k": W["mixtral_8x7b"].scaled(tokens=600, d_model=2048, d_ff=512, num_experts=4),
 }
 
 
