@@ -262,8 +262,10 @@ int moe_combine(const moe_config* cfg, const void* y_perm, const int32_t* expert
 
 /*
  * The whole layer forward: moe_route, moe_permute, moe_expert_ffn and
- * moe_combine on one stream, with the expert-sorted row buffers and the
- * intermediate kept in the workspace.
+ * moe_combine on one stream, with the expert intermediate and outputs kept in
+ * the workspace. The expert-sorted copy of the token rows is not made: the
+ * first expert GEMM reads token rows of x through routing->row_token, which
+ * gives the same results as the staged path bit for bit.
  *   x [T, d] act_dtype;  w: weights;  y [T, d] act_dtype output;
  *   routing: caller buffers for the routing results (logits may be NULL);
  *   stats: device moe_stats;  workspace >= moe_workspace_size(cfg) bytes.

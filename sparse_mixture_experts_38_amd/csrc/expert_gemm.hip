@@ -207,7 +207,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
     const bf16* __restrict__ A, const bf16* __restrict__ W, const bf16* __restrict__ W3,
     const float* __restrict__ bias, const bf16* __restrict__ Ws, const bf16* __restrict__ Ws3,
     const float* __restrict__ bias_s, int E, int G, const int32_t* __restrict__ offsets,
-    int rows_max, bf16* __restrict__ C, int N, int K, int part) {
+    int rows_max, bf16* __restrict__ C, int N, int K, int part, const int32_t* __restrict__ arows) {
   constexpr bool GATED = EPI == EPI_SWIGLU;
   constexpr int BM = 128, BK = 64, CH = BK / 8;   // 8 chunks of 16 B per LDS row
   constexpr int NB = GATED ? 2 : 1;
@@ -265,13 +265,27 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
   // Uniform base addresses and per-thread 32-bit byte offsets (A rows past the
   // tile's end repeat its last row). W3 rows of the B part start at LDS row
   // BN (= 64) for SwiGLU.
-  const char* a_s = reinterpret_cast<const char*>(A + (int64_t)row0 * K);
+  // A row r of the tile is row row0 + r of A, or, with arows, row arows[row0 + r]
+  // (the expert-sorted gather of token rows, fused here).
   const char* b_s = reinterpret_cast<const char*>(Wg + (int64_t)n0 * K);
   const char* b3_s = GATED ? reinterpret_cast<const char*>(W3g + (int64_t)(n0 - BN) * K) : b_s;
-  const uint32_t ao0 = (uint32_t)(min(lr, nrows - 1) * K + lc * 8) * 2u;
-  const uint32_t ao1 = (uint32_t)(min(lr + 32, nrows - 1) * K + lc * 8) * 2u;
-  const uint32_t ao2 = (uint32_t)(min(lr + 64, nrows - 1) * K + lc * 8) * 2u;
-  const uint32_t ao3 = (uint32_t)(min(lr + 96, nrows - 1) * K + lc * 8) * 2u;
+  const char* ar0;
+  const char* ar1;
+  const char* ar2;
+  const char* ar3;
+  {
+    int rr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = row0 + min(lr + 32 * i, nrows - 1);
+      rr[i] = arows ? arows[r] : r;
+    }
+    const bf16* a0 = A + lc * 8;
+    ar0 = reinterpret_cast<const char*>(a0 + (int64_t)rr[0] * K);
+    ar1 = reinterpret_cast<const char*>(a0 + (int64_t)rr[1] * K);
+    ar2 = reinterpret_cast<const char*>(a0 + (int64_t)rr[2] * K);
+    ar3 = reinterpret_cast<const char*>(a0 + (int64_t)rr[3] * K);
+  }
   const uint32_t bo0 = (uint32_t)(lr * K + lc * 8) * 2u;
   const uint32_t bo1 = bo0 + (uint32_t)(64 * K);    // + 32 rows
   const uint32_t bo2 = bo0 + (uint32_t)(128 * K);
@@ -308,10 +322,10 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
 #define MOE_G(R, kt, i)                                                              \
   do {                                                                               \
     const uint32_t kb_ = (uint32_t)(kt) * (BK * 2);                                  \
-    if ((i) == 0) R.v0 = *reinterpret_cast<const u32x4*>(a_s + kb_ + ao0);           \
-    if ((i) == 1) R.v1 = *reinterpret_cast<const u32x4*>(a_s + kb_ + ao1);           \
-    if ((i) == 2) R.v2 = *reinterpret_cast<const u32x4*>(a_s + kb_ + ao2);           \
-    if ((i) == 3) R.v3 = *reinterpret_cast<const u32x4*>(a_s + kb_ + ao3);           \
+    if ((i) == 0) R.v0 = *reinterpret_cast<const u32x4*>(ar0 + kb_);                 \
+    if ((i) == 1) R.v1 = *reinterpret_cast<const u32x4*>(ar1 + kb_);                 \
+    if ((i) == 2) R.v2 = *reinterpret_cast<const u32x4*>(ar2 + kb_);                 \
+    if ((i) == 3) R.v3 = *reinterpret_cast<const u32x4*>(ar3 + kb_);                 \
     if ((i) == 4) R.v4 = *reinterpret_cast<const u32x4*>(b_s + kb_ + bo0);           \
     if ((i) == 5) R.v5 = *reinterpret_cast<const u32x4*>(b_s + kb_ + bo1);           \
     if ((i) == 6) R.v6 = *reinterpret_cast<const u32x4*>(b3_s + kb_ + bo2);          \
@@ -460,7 +474,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(
     const bf16* __restrict__ A, const bf16* __restrict__ W, const bf16* __restrict__ W3,
     const float* __restrict__ bias, const bf16* __restrict__ Ws, const bf16* __restrict__ Ws3,
     const float* __restrict__ bias_s, int E, int G, const int32_t* __restrict__ offsets,
-    int rows_max, bf16* __restrict__ C, int N, int K) {
+    int rows_max, bf16* __restrict__ C, int N, int K, const int32_t* __restrict__ arows) {
   constexpr bool GATED = EPI == EPI_SWIGLU;
   constexpr int BM = 256, BK = 64, CH = BK / 8;   // 8 chunks of 16 B per LDS row
   constexpr int NB = GATED ? 2 : 1;
@@ -510,15 +524,25 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(
   // Direct-to-LDS loads: wave w fills stage rows 128 w .. 128 w + 127 (waves 0
   // and 1: A rows; 2 and 3: W rows n0 .., or W1 then W3 rows for SwiGLU), 8 rows
   // per instruction i; (row >> 1) & 7 = (4 (i & 1) + (lane >> 4)) & 7.
-  const bf16* src = wave < 2 ? A + (int64_t)(row0 + wave * 128) * K
-                   : GATED ? (wave == 2 ? Wg : W3g) + (int64_t)n0 * K
-                           : Wg + (int64_t)(n0 + (wave - 2) * 128) * K;
-  const char* dsrc = reinterpret_cast<const char*>(src);
+  // A rows: row row0 + r of A, or, with arows, row arows[row0 + r] (the
+  // expert-sorted gather of token rows, fused here)
   const int pc = lane & 7, lq = lane >> 4;
-  uint32_t doff[16];
+  const char* dptr[16];
+  if (wave < 2) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i)
-    doff[i] = (uint32_t)((8 * i + (lane >> 3)) * K + (pc ^ ((4 * (i & 1) + lq) & 7)) * 8) * 2u;
+    for (int i = 0; i < 16; ++i) {
+      const int r = row0 + wave * 128 + 8 * i + (lane >> 3);
+      const int ar = arows ? arows[r] : r;
+      dptr[i] = reinterpret_cast<const char*>(A + (int64_t)ar * K + (pc ^ ((4 * (i & 1) + lq) & 7)) * 8);
+    }
+  } else {
+    const bf16* src = GATED ? (wave == 2 ? Wg : W3g) + (int64_t)n0 * K
+                            : Wg + (int64_t)(n0 + (wave - 2) * 128) * K;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      dptr[i] = reinterpret_cast<const char*>(src + (int64_t)(8 * i + (lane >> 3)) * K +
+                                              (pc ^ ((4 * (i & 1) + lq) & 7)) * 8);
+  }
   const int dl = wave * 128 * CH;
 
   int fbase[8];
@@ -545,7 +569,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(
 #define MOE_SB() __builtin_amdgcn_sched_barrier(0)
 #define MOE_SM(x) ((x) == 0 ? sm0 : sm1)
 #define MOE_D(x, kt, i)                                                              \
-  __builtin_amdgcn_global_load_lds(dsrc + doff[i] + (uint32_t)(kt) * (BK * 2),       \
+  __builtin_amdgcn_global_load_lds(dptr[i] + (uint32_t)(kt) * (BK * 2),              \
                                    (void*)(MOE_SM(x) + dl + (i) * 8 * CH), 16, 0, 0)
 #define MOE_R(F, x, s4, f)                                                           \
   F[f] = __builtin_bit_cast(bf16x8, MOE_SM(x)[fbase[f] + cidx[s4]])
@@ -650,7 +674,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(
     const float* __restrict__ A, const float* __restrict__ W, const float* __restrict__ W3,
     const float* __restrict__ bias, const float* __restrict__ Ws, const float* __restrict__ Ws3,
     const float* __restrict__ bias_s, int E, int G, const int32_t* __restrict__ offsets,
-    int rows_max, float* __restrict__ C, int N, int K) {
+    int rows_max, float* __restrict__ C, int N, int K, const int32_t* __restrict__ arows) {
   constexpr bool GATED = EPI == EPI_SWIGLU;
   const int ncb = (N + 255) / 256;
   const int mt = blockIdx.x / ncb;
@@ -662,7 +686,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(
   const float* w3 = GATED ? (g < E ? W3 + (int64_t)g * N * K : Ws3) + (int64_t)n * K : nullptr;
   const float bv = HAS_BIAS ? (g < E ? bias + (int64_t)g * N : bias_s)[n] : 0.f;
   for (int m = 0; m < nrows; ++m) {
-    const float* a = A + (int64_t)(row0 + m) * K;
+    const float* a = A + (int64_t)(arows ? arows[row0 + m] : row0 + m) * K;
     float s1 = 0.f, s3 = 0.f;
     for (int kk = 0; kk < K; ++kk) {
       s1 = fmaf(a[kk], w[kk], s1);
@@ -676,7 +700,7 @@ template <typename ET, int EPI, bool HB>
 static hipError_t gemm_launch(const moe_config& c, const ET* A, const void* W, const void* W3,
                               const float* bias, const void* Ws, const void* Ws3,
                               const float* bias_s, const int32_t* offsets, ET* C, int N, int K,
-                              hipStream_t s) {
+                              hipStream_t s, const int32_t* arows = nullptr) {
   const int E = c.num_experts, G = c.num_experts + c.num_shared_experts;
   const int64_t rows = rows_max(c);
   if constexpr (sizeof(ET) == 2) {
@@ -692,52 +716,52 @@ static hipError_t gemm_launch(const moe_config& c, const ET* A, const void* W, c
       const unsigned big_tiles = (unsigned)(rows / kGemmBigBM) * (unsigned)(N / BNB);
       hipLaunchKernelGGL((gemm_bf16_big_kernel<EPI, HB>), dim3(big_tiles), dim3(256), 0, s, A,
                          (const bf16*)W, (const bf16*)W3, bias, (const bf16*)Ws, (const bf16*)Ws3,
-                         bias_s, E, G, offsets, (int)rows, C, N, K);
+                         bias_s, E, G, offsets, (int)rows, C, N, K, arows);
       // each group leaves at most 255 rows, i.e. at most 2 tiles, and the
       // tiles number at most ceil(rows / 128) + G
       const int64_t rest = (rows + 127) / 128 + G < 2 * G ? (rows + 127) / 128 + G : 2 * G;
       hipLaunchKernelGGL((gemm_bf16_kernel<EPI, HB>), dim3((unsigned)rest * (N / BN)), dim3(256), 0,
                          s, A, (const bf16*)W, (const bf16*)W3, bias, (const bf16*)Ws,
-                         (const bf16*)Ws3, bias_s, E, G, offsets, (int)rows, C, N, K, 2);
+                         (const bf16*)Ws3, bias_s, E, G, offsets, (int)rows, C, N, K, 2, arows);
     } else {
       const unsigned mtiles = (unsigned)((rows + 127) / 128) + G;
       hipLaunchKernelGGL((gemm_bf16_kernel<EPI, HB>), dim3(mtiles * (N / BN)), dim3(256), 0, s, A,
                          (const bf16*)W, (const bf16*)W3, bias, (const bf16*)Ws, (const bf16*)Ws3,
-                         bias_s, E, G, offsets, (int)rows, C, N, K, 0);
+                         bias_s, E, G, offsets, (int)rows, C, N, K, 0, arows);
     }
   } else {
     const unsigned mtiles = (unsigned)((rows + kGemmBM - 1) / kGemmBM) + G;
     hipLaunchKernelGGL((gemm_f32_kernel<EPI, HB>), dim3(mtiles * ((N + 255) / 256)), dim3(256), 0,
                        s, A, (const float*)W, (const float*)W3, bias, (const float*)Ws,
-                       (const float*)Ws3, bias_s, E, G, offsets, (int)rows, C, N, K);
+                       (const float*)Ws3, bias_s, E, G, offsets, (int)rows, C, N, K, arows);
   }
   return hipGetLastError();
 }
 
 template <typename ET, bool HB>
-static hipError_t up_typed(const moe_config& c, const ET* x_perm, const int32_t* off,
-                           const ExpertWeights& w, ET* h, hipStream_t s) {
+static hipError_t up_typed(const moe_config& c, const ET* a, const int32_t* arows,
+                           const int32_t* off, const ExpertWeights& w, ET* h, hipStream_t s) {
   const int N = (int)c.d_ff, K = (int)c.d_model;
   switch (c.activation) {
     case MOE_ACT_GELU:
-      return gemm_launch<ET, EPI_GELU, HB>(c, x_perm, w.w1, nullptr, w.b1, w.ws1, nullptr, w.bs1,
-                                           off, h, N, K, s);
+      return gemm_launch<ET, EPI_GELU, HB>(c, a, w.w1, nullptr, w.b1, w.ws1, nullptr, w.bs1, off, h,
+                                           N, K, s, arows);
     case MOE_ACT_RELU:
-      return gemm_launch<ET, EPI_RELU, HB>(c, x_perm, w.w1, nullptr, w.b1, w.ws1, nullptr, w.bs1,
-                                           off, h, N, K, s);
+      return gemm_launch<ET, EPI_RELU, HB>(c, a, w.w1, nullptr, w.b1, w.ws1, nullptr, w.bs1, off, h,
+                                           N, K, s, arows);
     default:
-      return gemm_launch<ET, EPI_SWIGLU, HB>(c, x_perm, w.w1, w.w3, w.b1, w.ws1, w.ws3, w.bs1, off,
-                                             h, N, K, s);
+      return gemm_launch<ET, EPI_SWIGLU, HB>(c, a, w.w1, w.w3, w.b1, w.ws1, w.ws3, w.bs1, off, h, N,
+                                             K, s, arows);
   }
 }
 
-hipError_t launch_expert_up(const moe_config& c, const void* x_perm, const int32_t* offsets,
-                            const ExpertWeights& w, void* h, hipStream_t s) {
+hipError_t launch_expert_up(const moe_config& c, const void* a, const int32_t* offsets,
+                            const ExpertWeights& w, void* h, hipStream_t s, const int32_t* arows) {
   if (c.act_dtype == MOE_BF16)
-    return c.has_bias ? up_typed<bf16, true>(c, (const bf16*)x_perm, offsets, w, (bf16*)h, s)
-                      : up_typed<bf16, false>(c, (const bf16*)x_perm, offsets, w, (bf16*)h, s);
-  return c.has_bias ? up_typed<float, true>(c, (const float*)x_perm, offsets, w, (float*)h, s)
-                    : up_typed<float, false>(c, (const float*)x_perm, offsets, w, (float*)h, s);
+    return c.has_bias ? up_typed<bf16, true>(c, (const bf16*)a, arows, offsets, w, (bf16*)h, s)
+                      : up_typed<bf16, false>(c, (const bf16*)a, arows, offsets, w, (bf16*)h, s);
+  return c.has_bias ? up_typed<float, true>(c, (const float*)a, arows, offsets, w, (float*)h, s)
+                    : up_typed<float, false>(c, (const float*)a, arows, offsets, w, (float*)h, s);
 }
 
 hipError_t launch_expert_down(const moe_config& c, const void* h, const int32_t* offsets,

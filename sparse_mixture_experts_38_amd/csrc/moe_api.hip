@@ -39,7 +39,6 @@ WsLayout workspace_layout(const moe_config& c) {
   const size_t es = c.act_dtype == MOE_BF16 ? 2 : 4;
   L.h = take((size_t)L.rows_max * c.d_ff * es);
   L.end_ffn = off;
-  L.x_perm = take((size_t)L.rows_max * c.d_model * es);
   L.y_perm = take((size_t)L.rows_max * c.d_model * es);
   L.total = off;
   return L;
@@ -253,14 +252,15 @@ int moe_forward(const moe_config* cfg, const void* x, const moe_weights* w, void
   hipError_t e = launch_route(*cfg, L, x, w->w_gate, w->b_gate, w->e_bias, r->logits, r->topk_idx,
                               r->topk_gate, stats, ws, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  void* x_perm = ws + L.x_perm;
   void* y_perm = ws + L.y_perm;
+  // the expert-sorted token rows are not copied: GEMM 1 gathers them from x
+  // through row_token
   e = launch_permute(*cfg, L, capacity_exact(*cfg), r->topk_idx, x, r->expert_offsets,
-                     r->row_token, r->assign_row, x_perm, stats, ws, s);
+                     r->row_token, r->assign_row, nullptr, stats, ws, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
   const ExpertWeights ew{w->w1, w->w3, w->w2, w->b1, w->b2, w->ws1, w->ws3, w->ws2, w->bs1, w->bs2};
   void* h = ws + L.h;
-  e = launch_expert_up(*cfg, x_perm, r->expert_offsets, ew, h, s);
+  e = launch_expert_up(*cfg, x, r->expert_offsets, ew, h, s, r->row_token);
   if (e != hipSuccess) return MOE_ERR_HIP;
   e = launch_expert_down(*cfg, h, r->expert_offsets, ew, y_perm, s);
   if (e != hipSuccess) return MOE_ERR_HIP;

@@ -87,7 +87,6 @@ struct WsLayout {
   size_t chunk_base;      // int32 [chunks][E]
   size_t local_rank;      // int32 [T k]
   size_t h;               // act [rows_max][F]
-  size_t x_perm;          // act [rows_max][d]
   size_t y_perm;          // act [rows_max][d]
   size_t end_route, end_permute, end_ffn, total;
   int route_blocks, route_iters, chunks;
@@ -121,9 +120,11 @@ struct ExpertWeights {
   const float *bs1, *bs2;
 };
 
-// Grouped GEMM 1 with the fused activation: h = act(x_perm W1^T + b1) per group.
-hipError_t launch_expert_up(const moe_config& c, const void* x_perm, const int32_t* expert_offsets,
-                            const ExpertWeights& w, void* h, hipStream_t stream);
+// Grouped GEMM 1 with the fused activation: h = act(a W1^T + b1) per group, where
+// row r of the group's input is row r of a or, with arows, row arows[r] of a.
+hipError_t launch_expert_up(const moe_config& c, const void* a, const int32_t* expert_offsets,
+                            const ExpertWeights& w, void* h, hipStream_t stream,
+                            const int32_t* arows = nullptr);
 
 // Grouped GEMM 2: y_perm = h W2^T + b2 per group.
 hipError_t launch_expert_down(const moe_config& c, const void* h, const int32_t* expert_offsets,
