@@ -10,10 +10,13 @@
 
 namespace moe {
 
-// logits[t][e] = sum_c x[t][c] w[e][c] (+ b[e]). One wavefront per token: lanes
-// split d into 8-element slices (16-byte loads of bf16 x), experts are taken
-// eight at a time with one float32 accumulator each, then reduced across the
-// wave in a fixed butterfly order (deterministic).
+// logits[t][e] = sum_c x[t][c] w[e][c] (+ b[e]). One wavefront takes 8 tokens
+// and 8 experts at a time: lanes split d into 8-element slices (16-byte loads
+// of bf16 x), so each router weight load serves 8 tokens, and every lane keeps
+// 64 float32 partial sums, one per (token, expert). Those are summed over the
+// 64 lanes by a reduce-scatter (6 exchange steps, each lane keeping half of
+// its values), after which lane l holds the total of (token l / 8, expert
+// l % 8). The summation order is fixed, so the result is deterministic.
 template <typename XT, typename WT>
 __global__ __launch_bounds__(256) void router_logits_kernel(const XT* __restrict__ x,
                                                             const WT* __restrict__ wg,
@@ -21,41 +24,48 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const XT* __restrict
                                                             float* __restrict__ logits, int64_t T,
                                                             int d, int E) {
   const int lane = threadIdx.x & 63;
+  const int64_t ngroups = (T + 7) / 8;
   const int64_t nwaves = (int64_t)gridDim.x * 4;
-  for (int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); t < T; t += nwaves) {
-    const XT* xr = x + t * d;
+  for (int64_t tg = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); tg < ngroups; tg += nwaves) {
+    const int64_t t0 = tg * 8;
     for (int e0 = 0; e0 < E; e0 += 8) {
       const int ne = min(8, E - e0);
-      float acc[8];
+      float v[64];   // v[tok * 8 + e]
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+      for (int i = 0; i < 64; ++i) v[i] = 0.f;
       for (int c = lane * 8; c < d; c += 512) {
-        float xv[8];
-        load8(xr + c, xv);
+        float wv[8][8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          if (i < ne) {
-            float wv[8];
-            load8(wg + (int64_t)(e0 + i) * d + c, wv);
+        for (int e = 0; e < 8; ++e) {
+          const int ee = e0 + min(e, ne - 1);   // missing experts repeat the last (not stored)
+          load8(wg + (int64_t)ee * d + c, wv[e]);
+        }
 #pragma unroll
-            for (int q = 0; q < 8; ++q) acc[i] = fmaf(xv[q], wv[q], acc[i]);
-          }
+        for (int tk = 0; tk < 8; ++tk) {
+          float xv[8];
+          load8(x + min(t0 + tk, T - 1) * d + c, xv);
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[tk * 8 + e] = fmaf(xv[q], wv[e][q], v[tk * 8 + e]);
         }
       }
+      // reduce-scatter over the wave: at the step with lane bit s, the lane
+      // keeps the half of its n values selected by that bit and adds the
+      // partner's copy of it
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int s2 = 32, n = 64; s2 >= 1; s2 >>= 1, n >>= 1) {
+        const bool hi = (lane & s2) != 0;
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) acc[i] += __shfl_xor(acc[i], off, 64);
+        for (int i = 0; i < n / 2; ++i) {
+          const float send = hi ? v[i] : v[i + n / 2];
+          const float keep = hi ? v[i + n / 2] : v[i];
+          v[i] = keep + __shfl_xor(send, s2, 64);
+        }
       }
-      float v = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (lane == i) v = acc[i];
-      if (lane < ne) {
-        const int e = e0 + lane;
-        if (bg) v += bg[e];
-        logits[t * E + e] = v;
-      }
+      const int64_t t = t0 + (lane >> 3);
+      const int e = e0 + (lane & 7);
+      if (t < T && (lane & 7) < ne) logits[t * E + e] = bg ? v[0] + bg[e] : v[0];
     }
   }
 }
@@ -266,7 +276,7 @@ hipError_t launch_route(const moe_config& c, const WsLayout& L, const void* x, c
   float* partials = reinterpret_cast<float*>(ws + L.route_partials);
   const float* bg = c.has_gate_bias ? b_gate : nullptr;
   const float* eb = c.score_fn == MOE_SCORE_SIGMOID ? e_bias : nullptr;
-  const int64_t waves = c.tokens;
+  const int64_t waves = (c.tokens + 7) / 8;   // one wave per 8 tokens
   const int blocks = (int)((waves + 3) / 4 < 4096 ? (waves + 3) / 4 : 4096);
   if (c.act_dtype == MOE_BF16 && c.router_dtype == MOE_F32)
     hipLaunchKernelGGL((router_logits_kernel<bf16, float>), dim3(blocks), dim3(256), 0, s,
