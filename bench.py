@@ -95,8 +95,8 @@ def cpu_baseline(w, inp_gpu, min_seconds=10.0, max_seconds=30.0):
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="deepspeed_gpt_moe")
     ap.add_argument("--sets", type=int, default=3, help="rotated input/weight sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")

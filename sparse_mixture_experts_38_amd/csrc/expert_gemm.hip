@@ -152,21 +152,22 @@ __device__ __forceinline__ void tile_lookup(const TileSpace& ts, int mt, int BM,
   nrows_out = __shfl(nrows, owner, 64);
 }
 
-// GELU(x) = x Phi(x) = max(x, 0) - |x| Phi(-|x|), with Phi(-|x|) = erfc(|x| / sqrt 2) / 2
-// from the rational approximation of Abramowitz & Stegun, Handbook of
-// Mathematical Functions, formula 7.1.26 (absolute error of erf below 1.5e-7;
-// coefficients halved here), evaluated with the hardware reciprocal and
-// base-2 exponential. Used where the result is rounded to bf16 (relative step
-// 2^-8), far above the approximation's error.
-__device__ __forceinline__ float gelu_as(float x) {
-  const float ax = fabsf(x);
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f * 0.70710678118654752f, ax, 1.0f));
-  float p = fmaf(0.5f * 1.061405429f, t, 0.5f * -1.453152027f);
-  p = fmaf(p, t, 0.5f * 1.421413741f);
-  p = fmaf(p, t, 0.5f * -0.284496736f);
-  p = fmaf(p, t, 0.5f * 0.254829592f);
-  const float q = p * t * __builtin_amdgcn_exp2f(-0.72134752044448170f * x * x);
-  return fmaf(-ax, q, fmaxf(x, 0.f));
+// GELU(x) = x Phi(x) = max(x, 0) - a Phi(-a) with a = |x| clamped to 6 (where
+// a Phi(-a) < 1e-8). Phi(-a) = 2^P(a), P a degree-7 polynomial fitted to
+// log2 Phi(-a) on [0, 6] by least squares (csrc/gelu_fit.py prints the fit and
+// its error): seven FMAs and one hardware exp2, max absolute error 1e-6 and
+// relative error 1e-5 of the GELU. Used where the result is rounded to bf16
+// (relative step 2^-8).
+__device__ __forceinline__ float gelu_poly(float x) {
+  const float a = fminf(fabsf(x), 6.0f);
+  float p = fmaf(-1.9449223600531695e-06f, a, 6.386057066265494e-05f);
+  p = fmaf(p, a, -0.0009488713694736362f);
+  p = fmaf(p, a, 0.008582375012338161f);
+  p = fmaf(p, a, -0.0541183240711689f);
+  p = fmaf(p, a, -0.4582974314689636f);
+  p = fmaf(p, a, -1.1513246297836304f);
+  p = fmaf(p, a, -0.9999869465827942f);
+  return fmaf(-a, __builtin_amdgcn_exp2f(p), fmaxf(x, 0.f));
 }
 
 __device__ __forceinline__ float silu_fast(float z) {
@@ -175,7 +176,7 @@ __device__ __forceinline__ float silu_fast(float z) {
 
 template <int EPI>
 __device__ __forceinline__ float epilogue_bf16(float z1, float z3) {
-  if (EPI == EPI_GELU) return gelu_as(z1);
+  if (EPI == EPI_GELU) return gelu_poly(z1);
   if (EPI == EPI_RELU) return fmaxf(z1, 0.f);
   if (EPI == EPI_SWIGLU) return silu_fast(z1) * z3;
   return z1;
@@ -403,7 +404,8 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
 #undef MOE_W
 #undef MOE_R
 #undef MOE_M
-#undef MOE_STEP
+#undef MOE_SUB
+#undef MOE_PHASE
 
   // Epilogue. Register r of a 32x32 accumulator holds row (lane % 32) and
   // column 8 (r / 4) + 4 (lane / 32) + r % 4 of the sub-tile, so lane (fr, fk)
@@ -459,11 +461,14 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
 // its 256 float32 accumulators in the accumulation registers. A 256 x 256 tile
 // needs half the bytes per FLOP of a 128 x 128 one, which keeps the CU's
 // address unit below saturation. Operands go global -> LDS directly
-// (global_load_lds_dwordx4), 64-deep K steps, two stages of 512 rows x 128 B
-// (A rows, then B rows) held in two separate LDS arrays so that the compiler
-// can tell the loads into one stage from the fragment reads of the other.
-// The loads of step k + 1 are issued during the first half of step k, and
-// every wave waits for its own loads before the barrier that ends step k.
+// (buffer_load ... lds, 16 bytes per lane), 64-deep K steps, two stages of
+// 512 rows x 128 B (A rows, then B rows) held in two separate LDS arrays so
+// that the compiler can tell the loads into one stage from the fragment reads
+// of the other. There is one barrier per K step, placed after the last
+// fragment read of the step's stage rather than at the step's end: after it,
+// the step's last 16 MFMAs run from registers while the next step's first
+// fragments are read and its loads are issued, so no wave waits on LDS right
+// after a barrier.
 // Lane l of a load lands at LDS row (l >> 3) of its 8-row group and physical
 // chunk l & 7, which holds logical chunk (l & 7) ^ ((row >> 1) & 7): the
 // same conflict-free layout as the 128 x 128 kernel. The epilogue adds the
@@ -474,7 +479,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(
     const bf16* __restrict__ A, const bf16* __restrict__ W, const bf16* __restrict__ W3,
     const float* __restrict__ bias, const bf16* __restrict__ Ws, const bf16* __restrict__ Ws3,
     const float* __restrict__ bias_s, int E, int G, const int32_t* __restrict__ offsets,
-    int rows_max, bf16* __restrict__ C, int N, int K, const int32_t* __restrict__ arows) {
+    int rows_max, bf16* __restrict__ C, int N, int K, const int32_t* __restrict__ arows,
+    uint32_t a_bytes) {
   constexpr bool GATED = EPI == EPI_SWIGLU;
   constexpr int BM = 256, BK = 64, CH = BK / 8;   // 8 chunks of 16 B per LDS row
   constexpr int NB = GATED ? 2 : 1;
@@ -487,6 +493,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(
   static_assert(NB * TN == 4, "four B fragments per sub-step");
   static_assert(128 * CQ <= STAGE, "half of the output tile fits one stage");
   __shared__ u32x4 sm0[STAGE], sm1[STAGE];
+  __shared__ uint32_t pf_lds[512];   // landing area of the L2 prefetches, never read
 
   TileSpace ts;
   tile_space_init(ts, offsets, G, rows_max, BM, 1, BM);
@@ -527,23 +534,46 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(
   // A rows: row row0 + r of A, or, with arows, row arows[row0 + r] (the
   // expert-sorted gather of token rows, fused here)
   const int pc = lane & 7, lq = lane >> 4;
-  const char* dptr[16];
+  // Each wave reads through its own buffer resource (wave-uniform base and
+  // size) with 32-bit lane offsets; the K step enters as the scalar offset.
+  // Buffer loads, unlike flat/global ones, are not taken by the compiler as
+  // possible LDS accesses, so its LDS-read waits stay exact.
+  const char* wbase;
+  uint32_t wbytes;
   if (wave < 2) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = row0 + wave * 128 + 8 * i + (lane >> 3);
-      const int ar = arows ? arows[r] : r;
-      dptr[i] = reinterpret_cast<const char*>(A + (int64_t)ar * K + (pc ^ ((4 * (i & 1) + lq) & 7)) * 8);
-    }
+    wbase = arows ? reinterpret_cast<const char*>(A)
+                  : reinterpret_cast<const char*>(A + (int64_t)(row0 + wave * 128) * K);
+    wbytes = arows ? a_bytes : 128u * (uint32_t)K * 2u;
   } else {
-    const bf16* src = GATED ? (wave == 2 ? Wg : W3g) + (int64_t)n0 * K
-                            : Wg + (int64_t)(n0 + (wave - 2) * 128) * K;
+    wbase = reinterpret_cast<const char*>(GATED ? (wave == 2 ? Wg : W3g) + (int64_t)n0 * K
+                                                : Wg + (int64_t)(n0 + (wave - 2) * 128) * K);
+    wbytes = 128u * (uint32_t)K * 2u;
+  }
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)wbase, (short)0, (int)wbytes, 0x00020000);
+  uint32_t doff[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      dptr[i] = reinterpret_cast<const char*>(src + (int64_t)(8 * i + (lane >> 3)) * K +
-                                              (pc ^ ((4 * (i & 1) + lq) & 7)) * 8);
+  for (int i = 0; i < 16; ++i) {
+    const int rl = 8 * i + (lane >> 3);
+    const uint32_t rowoff = wave < 2 && arows ? (uint32_t)arows[row0 + wave * 128 + rl] * (uint32_t)K * 2u
+                                              : (uint32_t)rl * (uint32_t)K * 2u;
+    doff[i] = rowoff + (uint32_t)(pc ^ ((4 * (i & 1) + lq) & 7)) * 16u;
   }
   const int dl = wave * 128 * CH;
+  // L2 prefetch: in phase k (below), which loads step k + 1, each lane also
+  // loads one dword of the 128-byte K chunk of step k + 3 for rows l and
+  // l + 64 of its wave's 128 rows, so the loads of that step, issued in phase
+  // k + 2, find their lines in L2 instead of waiting on HBM. The dwords land in a small LDS area
+  // that is never read (a load with no register result, so nothing has to
+  // consume it and the waits stay exact).
+  uint32_t pfo[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int rl = lane + 64 * j;
+    pfo[j] = wave < 2 && arows ? (uint32_t)arows[row0 + wave * 128 + rl] * (uint32_t)K * 2u
+                               : (uint32_t)rl * (uint32_t)K * 2u;
+  }
+  const int nk = K / BK;   // K is a multiple of 256, so nk >= 4 and even
 
   int fbase[8];
 #pragma unroll
@@ -568,71 +598,102 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(
 
 #define MOE_SB() __builtin_amdgcn_sched_barrier(0)
 #define MOE_SM(x) ((x) == 0 ? sm0 : sm1)
+#define MOE_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 #define MOE_D(x, kt, i)                                                              \
-  __builtin_amdgcn_global_load_lds(dptr[i] + (uint32_t)(kt) * (BK * 2),              \
-                                   (void*)(MOE_SM(x) + dl + (i) * 8 * CH), 16, 0, 0)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, MOE_LDS(MOE_SM(x) + dl + (i) * 8 * CH), 16, \
+                                           doff[i], (uint32_t)(kt) * (BK * 2), 0, 0)
 #define MOE_R(F, x, s4, f)                                                           \
   F[f] = __builtin_bit_cast(bf16x8, MOE_SM(x)[fbase[f] + cidx[s4]])
 #define MOE_M(F, q)                                                                  \
   acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F[4 + ((q) >> 2)], F[(q) & 3], acc[q], 0, 0, 0)
   // wait for this wave's direct-to-LDS loads (vmcnt 0, expcnt and lgkmcnt free)
 #define MOE_WAIT_LOADS() __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8))
+  // the same but for the two prefetches issued last (vmcnt 2)
+#define MOE_WAIT_LOADS_PF() __builtin_amdgcn_s_waitcnt(2 | (7 << 4) | (15 << 8))
+#define MOE_PF(kt)                                                                   \
+  do {                                                                               \
+    const uint32_t o_ = (uint32_t)min((kt), nk - 1) * (BK * 2);                      \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, MOE_LDS(pf_lds + wave * 128), 4, pfo[0], o_, 0, 0); \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, MOE_LDS(pf_lds + wave * 128 + 64), 4, pfo[1], o_, 0, 0); \
+  } while (0)
   // One K step from stage x: 64 MFMAs in four sub-steps; each MFMA is
   // followed by one fragment read of the next sub-step, and every third of
   // the first 48 by one of the 16 loads of step KL into the other stage (LD):
   // spread out, the loads do not queue up in the address unit and hold back
   // the MFMAs behind them, and they still have a quarter step to land.
-#define MOE_STEP(x, KL, LD)                                                          \
-  do {                                                                               \
-    _Pragma("unroll") for (int f_ = 0; f_ < 8; ++f_) MOE_R(fa, x, 0, kRO[f_]);       \
+  // Phase k (between the barriers that end phases k - 1 and k): sub-step 3 of
+  // step k - 1 (its fragments are already in registers) while the first
+  // fragments of step k are read from stage x = k % 2 and the loads of step
+  // k + 1 go to the other stage (both are safe after the previous barrier:
+  // step k's loads have landed and every wave has read all of step k - 1 it
+  // needs); then sub-steps 0..2 of step k, the wait for this wave's loads and
+  // the barrier. No wave waits on LDS right after a barrier.
+#define MOE_SUB(FC, FN, x, s4n, RD, LD, KN, d0)                                      \
+  _Pragma("unroll") for (int q_ = 0; q_ < 16; ++q_) {                                \
+    MOE_M(FC, q_); MOE_SB();                                                         \
+    if ((RD) && q_ < 8) MOE_R(FN, x, s4n, kRO[q_]);                                  \
+    if ((LD) && (q_ & 1)) MOE_D(1 - (x), KN, (d0) + (q_ >> 1));                      \
     MOE_SB();                                                                        \
-    _Pragma("unroll") for (int q_ = 0; q_ < 16; ++q_) {                              \
-      MOE_M(fa, q_); MOE_SB();                                                       \
-      if (q_ < 8) MOE_R(fb, x, 1, kRO[q_]);                                          \
-      if ((LD) && q_ % 3 == 0) MOE_D(1 - (x), KL, q_ / 3);                           \
-      MOE_SB();                                                                      \
-    }                                                                                \
-    _Pragma("unroll") for (int q_ = 0; q_ < 16; ++q_) {                              \
-      MOE_M(fb, q_); MOE_SB();                                                       \
-      if (q_ < 8) MOE_R(fa, x, 2, kRO[q_]);                                          \
-      if ((LD) && (16 + q_) % 3 == 0) MOE_D(1 - (x), KL, (16 + q_) / 3);             \
-      MOE_SB();                                                                      \
-    }                                                                                \
-    _Pragma("unroll") for (int q_ = 0; q_ < 16; ++q_) {                              \
-      MOE_M(fa, q_); MOE_SB();                                                       \
-      if (q_ < 8) MOE_R(fb, x, 3, kRO[q_]);                                          \
-      if ((LD) && (32 + q_) % 3 == 0 && 32 + q_ < 48) MOE_D(1 - (x), KL, (32 + q_) / 3); \
-      MOE_SB();                                                                      \
-    }                                                                                \
-    _Pragma("unroll") for (int q_ = 0; q_ < 16; ++q_) { MOE_M(fb, q_); MOE_SB(); }   \
-    MOE_WAIT_LOADS();                                                                \
+  }
+#define MOE_PHASE(x, KN, LD)                                                         \
+  do {                                                                               \
+    MOE_SUB(fb, fa, x, 0, true, LD, KN, 0)                                           \
+    MOE_SUB(fa, fb, x, 1, true, LD, KN, 8)                                           \
+    if (LD) { MOE_PF((KN) + 2); MOE_SB(); }                                          \
+    MOE_SUB(fb, fa, x, 2, true, false, 0, 0)                                         \
+    MOE_SUB(fa, fb, x, 3, true, false, 0, 0)                                         \
+    if (LD) MOE_WAIT_LOADS_PF(); else MOE_WAIT_LOADS();                              \
     __builtin_amdgcn_s_barrier();                                                    \
     MOE_SB();                                                                        \
   } while (0)
 
-  // K is a multiple of 256, so nk >= 4 and even
-  const int nk = K / BK;
 #pragma unroll
   for (int i = 0; i < 16; ++i) MOE_D(0, 0, i);
-  MOE_WAIT_LOADS();
+  MOE_PF(2);
+  MOE_WAIT_LOADS_PF();
   __builtin_amdgcn_s_barrier();
   MOE_SB();
-  for (int kt = 0; kt < nk - 2; kt += 2) {
-    MOE_STEP(0, kt + 1, true);
-    MOE_STEP(1, kt + 2, true);
+  // phase 0: no previous step; all 16 loads of step 1 go out in sub-step 0
+#pragma unroll
+  for (int f = 0; f < 8; ++f) MOE_R(fa, 0, 0, kRO[f]);
+  MOE_SB();
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    MOE_M(fa, q); MOE_SB();
+    if (q < 8) MOE_R(fb, 0, 1, kRO[q]);
+    MOE_D(1, 1, q);
+    MOE_SB();
   }
-  MOE_STEP(0, nk - 1, true);
-  MOE_STEP(1, 0, false);
+  MOE_PF(3);
+  MOE_SB();
+  MOE_SUB(fb, fa, 0, 2, true, false, 0, 0)
+  MOE_SUB(fa, fb, 0, 3, true, false, 0, 0)
+  MOE_WAIT_LOADS_PF();
+  __builtin_amdgcn_s_barrier();
+  MOE_SB();
+  // phases 1 .. nk - 1 (nk is a multiple of 4)
+  for (int kt = 1; kt < nk - 1; kt += 2) {
+    MOE_PHASE(1, kt + 1, true);
+    MOE_PHASE(0, kt + 2, true);
+  }
+  MOE_PHASE(1, 0, false);
+  // sub-step 3 of the last step
+#pragma unroll
+  for (int q = 0; q < 16; ++q) { MOE_M(fb, q); MOE_SB(); }
 #undef MOE_SB
 #undef MOE_D
 #undef MOE_R
 #undef MOE_M
 #undef MOE_WAIT_LOADS
+#undef MOE_WAIT_LOADS_PF
+#undef MOE_PF
+#undef MOE_LDS
 #undef MOE_STEP
 
   // Epilogue: rows 0..127 of the tile are staged in sm0, rows 128..255 in sm1
-  // (wave row half wm); chunk q of row m at q ^ (m & 15). The last K step
-  // ended with a barrier, so the stages are free.
+  // (wave row half wm); chunk q of row m at q ^ (m & 15). Every fragment read
+  // came before the last barrier and no load is in flight, so the stages are
+  // free.
   uint2* st8 = reinterpret_cast<uint2*>(wm ? sm1 : sm0);
 #pragma unroll
   for (int jx = 0; jx < TN; ++jx) {
@@ -709,14 +770,18 @@ static hipError_t gemm_launch(const moe_config& c, const ET* A, const void* W, c
     // 256 x 256 tiles pay off where the K loop is long or there is no
     // activation: one block per CU leaves the epilogue's VALU work exposed,
     // which two 128 x 128 blocks per CU hide behind each other's MFMAs.
-    const bool big = rows >= kGemmBigBM && (EPI == EPI_NONE || K >= 2048);
+    // gathered A rows (arows) are addressed with 32-bit offsets from the start
+    // of x, which the 256 x 256 kernel's buffer loads need below 4 GiB
+    const int64_t a_bytes = arows ? c.tokens * (int64_t)K * 2 : 0;
+    const bool big = rows >= kGemmBigBM && (EPI == EPI_NONE || K >= 2048) &&
+                     a_bytes < ((int64_t)1 << 32);
     if (big) {
       // full 256-row tiles of each group, then the rows left over (< 256 per
       // group) in 128-row tiles; both grids are bounds, surplus blocks exit
       const unsigned big_tiles = (unsigned)(rows / kGemmBigBM) * (unsigned)(N / BNB);
       hipLaunchKernelGGL((gemm_bf16_big_kernel<EPI, HB>), dim3(big_tiles), dim3(256), 0, s, A,
                          (const bf16*)W, (const bf16*)W3, bias, (const bf16*)Ws, (const bf16*)Ws3,
-                         bias_s, E, G, offsets, (int)rows, C, N, K, arows);
+                         bias_s, E, G, offsets, (int)rows, C, N, K, arows, (uint32_t)a_bytes);
       // each group leaves at most 255 rows, i.e. at most 2 tiles, and the
       // tiles number at most ceil(rows / 128) + G
       const int64_t rest = (rows + 127) / 128 + G < 2 * G ? (rows + 127) / 128 + G : 2 * G;
