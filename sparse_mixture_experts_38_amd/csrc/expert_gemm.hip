@@ -226,30 +226,18 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
   const int mtiles = __builtin_amdgcn_readfirstlane(ts.total);
   const int ntn = N / BN;
   const int tiles = mtiles * ntn;
-  const int b = blockIdx.x;
-  if (b >= tiles) return;
-  // XCD-aware order over the tiles that exist: XCD x (blocks b = x mod 8)
-  // runs a contiguous range of the tile order
+  // Persistent blocks: block b takes tiles b, b + P, b + 2P, ... of the
+  // XCD-aware order (P = gridDim.x, a multiple of 8, so a block stays on its
+  // XCD's contiguous range of tiles).
+  const int P = gridDim.x;
+  int it = blockIdx.x;
+  if (it >= tiles) return;
   const int t8 = tiles & ~7;
-  const int t = b < t8 ? (b & 7) * (t8 >> 3) + (b >> 3) : b;
   const int per_group = GROUP_M * ntn;
-  const int grp = t / per_group;
-  const int first_m = grp * GROUP_M;
-  const int in = t - grp * per_group;
-  const int gm = min(mtiles - first_m, GROUP_M);
-  const int mt = first_m + in % gm;
-  const int nt = in / gm;
-  int g, row0, nrows;
-  tile_lookup(ts, mt, BM, g, row0, nrows);
-  // uniform over the block: keep them in scalar registers
-  g = __builtin_amdgcn_readfirstlane(g);
-  row0 = __builtin_amdgcn_readfirstlane(row0);
-  nrows = __builtin_amdgcn_readfirstlane(nrows);
-  const int n0 = nt * BN;
-  const bf16* Wg = g < E ? W + (int64_t)g * N * K : Ws;
-  const bf16* W3g = GATED ? (g < E ? W3 + (int64_t)g * N * K : Ws3) : Wg;
-  const float* bg = HAS_BIAS ? (g < E ? bias + (int64_t)g * N : bias_s) : nullptr;
-
+  int g, row0, nrows, n0;
+  const bf16* Wg;
+  const bf16* W3g;
+  const float* bg;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -268,13 +256,32 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
   // BN (= 64) for SwiGLU.
   // A row r of the tile is row row0 + r of A, or, with arows, row arows[row0 + r]
   // (the expert-sorted gather of token rows, fused here).
-  const char* b_s = reinterpret_cast<const char*>(Wg + (int64_t)n0 * K);
-  const char* b3_s = GATED ? reinterpret_cast<const char*>(W3g + (int64_t)(n0 - BN) * K) : b_s;
+  const char* b_s;
+  const char* b3_s;
   const char* ar0;
   const char* ar1;
   const char* ar2;
   const char* ar3;
-  {
+  // tile it of the XCD-aware order: group, rows, columns, operand addresses
+  auto setup = [&](int itx) {
+    const int t = itx < t8 ? (itx & 7) * (t8 >> 3) + (itx >> 3) : itx;
+    const int grp = t / per_group;
+    const int first_m = grp * GROUP_M;
+    const int in = t - grp * per_group;
+    const int gm = min(mtiles - first_m, GROUP_M);
+    const int mt = first_m + in % gm;
+    const int nt = in / gm;
+    tile_lookup(ts, mt, BM, g, row0, nrows);
+    // uniform over the block: keep them in scalar registers
+    g = __builtin_amdgcn_readfirstlane(g);
+    row0 = __builtin_amdgcn_readfirstlane(row0);
+    nrows = __builtin_amdgcn_readfirstlane(nrows);
+    n0 = nt * BN;
+    Wg = g < E ? W + (int64_t)g * N * K : Ws;
+    W3g = GATED ? (g < E ? W3 + (int64_t)g * N * K : Ws3) : Wg;
+    bg = HAS_BIAS ? (g < E ? bias + (int64_t)g * N : bias_s) : nullptr;
+    b_s = reinterpret_cast<const char*>(Wg + (int64_t)n0 * K);
+    b3_s = GATED ? reinterpret_cast<const char*>(W3g + (int64_t)(n0 - BN) * K) : b_s;
     int rr[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -286,7 +293,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
     ar1 = reinterpret_cast<const char*>(a0 + (int64_t)rr[1] * K);
     ar2 = reinterpret_cast<const char*>(a0 + (int64_t)rr[2] * K);
     ar3 = reinterpret_cast<const char*>(a0 + (int64_t)rr[3] * K);
-  }
+  };
   const uint32_t bo0 = (uint32_t)(lr * K + lc * 8) * 2u;
   const uint32_t bo1 = bo0 + (uint32_t)(64 * K);    // + 32 rows
   const uint32_t bo2 = bo0 + (uint32_t)(128 * K);
@@ -314,10 +321,6 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
   Regs r0, r1;
   bf16x8 fr0[4], fr1[4];   // fragments of two consecutive sub-steps
   f32x16 acc[4];           // acc[i + 2 jb] = A sub-tile i times B sub-tile jb
-#pragma unroll
-  for (int k4 = 0; k4 < 4; ++k4)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[k4][r] = 0.f;
 
 #define MOE_SB() __builtin_amdgcn_sched_barrier(0)
 #define MOE_G(R, kt, i)                                                              \
@@ -381,6 +384,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
   // K is a multiple of 256, so nk >= 4 and even; the last two steps are
   // peeled so that the loop body has no branches.
   const int nk = K / BK;
+  setup(it);
 #pragma unroll
   for (int i = 0; i < 8; ++i) MOE_G(r0, 0, i);
 #pragma unroll
@@ -388,6 +392,11 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
 #pragma unroll
   for (int i = 0; i < 8; ++i) MOE_W(r0, 0, i);
   __syncthreads();
+  for (;;) {
+#pragma unroll
+  for (int k4 = 0; k4 < 4; ++k4)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[k4][r] = 0.f;
   for (int kt = 0; kt < nk - 2; kt += 2) {
     // even step kt: stage 0 holds it, r1 holds step kt + 1, r0 is loaded with kt + 2
     MOE_STEP(0, r0, kt + 2, true, r1, true);
@@ -399,13 +408,21 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
   MOE_STEP(0, r0, 0, false, r1, true);
   __syncthreads();
   MOE_STEP(1, r1, 0, false, r0, false);
-#undef MOE_SB
-#undef MOE_G
-#undef MOE_W
-#undef MOE_R
-#undef MOE_M
-#undef MOE_SUB
-#undef MOE_PHASE
+
+  // The registers r0 / r1 are free now: the first two K steps of this block's
+  // next tile are loaded into them before the epilogue of this one, so their
+  // latency is spent under the epilogue instead of before the next K loop.
+  const int cur_row0 = row0, cur_nrows = nrows, cur_n0 = n0;
+  const float* cur_bg = bg;
+  const int itn = it + P;
+  const bool more = itn < tiles;
+  if (more) {
+    setup(itn);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) MOE_G(r0, 0, i);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) MOE_G(r1, 1, i);
+  }
 
   // Epilogue. Register r of a 32x32 accumulator holds row (lane % 32) and
   // column 8 (r / 4) + 4 (lane / 32) + r % 4 of the sub-tile, so lane (fr, fk)
@@ -415,7 +432,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
   for (int j = 0; j < TN; ++j)
 #pragma unroll
     for (int qd = 0; qd < 4; ++qd)
-      bv[j][qd] = HAS_BIAS ? *reinterpret_cast<const float4*>(bg + n0 + wn * WN + j * 32 + qd * 8 + fk * 4)
+      bv[j][qd] = HAS_BIAS ? *reinterpret_cast<const float4*>(cur_bg + cur_n0 + wn * WN + j * 32 + qd * 8 + fk * 4)
                            : make_float4(0.f, 0.f, 0.f, 0.f);
   __syncthreads();   // every wave is done reading the operand stages
   // bf16 tile staged as BM rows of CQ chunks; chunk q of row m at q ^ swz(m)
@@ -450,9 +467,22 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
     const int idx = p * 256 + tid;
     const int m = idx / CQ, q = idx % CQ;
     const int swz = CQ == 16 ? (m & 15) : ((m >> 1) & 7);
-    if (m < nrows)
-      *reinterpret_cast<u32x4*>(C + (int64_t)(row0 + m) * N + n0 + q * 8) = smem[m * CQ + (q ^ swz)];
+    if (m < cur_nrows)
+      *reinterpret_cast<u32x4*>(C + (int64_t)(cur_row0 + m) * N + cur_n0 + q * 8) = smem[m * CQ + (q ^ swz)];
   }
+  if (!more) break;
+  __syncthreads();   // the staged tile has been read out of stage 0
+#pragma unroll
+  for (int i = 0; i < 8; ++i) MOE_W(r0, 0, i);
+  __syncthreads();
+  it = itn;
+  }
+#undef MOE_SB
+#undef MOE_G
+#undef MOE_W
+#undef MOE_R
+#undef MOE_M
+#undef MOE_STEP
 }
 
 // Grouped GEMM on the full 256-row tiles of each group (part 1 of the row
@@ -688,7 +718,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(
 #undef MOE_WAIT_LOADS_PF
 #undef MOE_PF
 #undef MOE_LDS
-#undef MOE_STEP
+#undef MOE_SUB
+#undef MOE_PHASE
 
   // Epilogue: rows 0..127 of the tile are staged in sm0, rows 128..255 in sm1
   // (wave row half wm); chunk q of row m at q ^ (m & 15). Every fragment read
@@ -757,6 +788,22 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(
   }
 }
 
+// Block slots of the persistent 128 x 128 kernel on the current device: two
+// per CU, a multiple of 8 (one share per XCD), cached per device.
+static int gemm_slots() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    cached[dev] = (2 * cus) & ~7 ? (2 * cus) & ~7 : 8;
+  }
+  return cached[dev];
+}
+
 template <typename ET, int EPI, bool HB>
 static hipError_t gemm_launch(const moe_config& c, const ET* A, const void* W, const void* W3,
                               const float* bias, const void* Ws, const void* Ws3,
@@ -767,6 +814,9 @@ static hipError_t gemm_launch(const moe_config& c, const ET* A, const void* W, c
   if constexpr (sizeof(ET) == 2) {
     constexpr int BNB = EPI == EPI_SWIGLU ? 128 : 256;
     constexpr int BN = EPI == EPI_SWIGLU ? 64 : 128;
+    // the 128 x 128 kernel is persistent: at most two blocks per CU, each
+    // looping over the tiles (grid bounds below; surplus blocks exit)
+    const int slots = gemm_slots();
     // 256 x 256 tiles pay off where the K loop is long or there is no
     // activation: one block per CU leaves the epilogue's VALU work exposed,
     // which two 128 x 128 blocks per CU hide behind each other's MFMAs.
@@ -785,12 +835,14 @@ static hipError_t gemm_launch(const moe_config& c, const ET* A, const void* W, c
       // each group leaves at most 255 rows, i.e. at most 2 tiles, and the
       // tiles number at most ceil(rows / 128) + G
       const int64_t rest = (rows + 127) / 128 + G < 2 * G ? (rows + 127) / 128 + G : 2 * G;
-      hipLaunchKernelGGL((gemm_bf16_kernel<EPI, HB>), dim3((unsigned)rest * (N / BN)), dim3(256), 0,
-                         s, A, (const bf16*)W, (const bf16*)W3, bias, (const bf16*)Ws,
-                         (const bf16*)Ws3, bias_s, E, G, offsets, (int)rows, C, N, K, 2, arows);
+      const int64_t rgrid = rest * (N / BN) < slots ? rest * (N / BN) : slots;
+      hipLaunchKernelGGL((gemm_bf16_kernel<EPI, HB>), dim3((unsigned)rgrid), dim3(256), 0, s, A,
+                         (const bf16*)W, (const bf16*)W3, bias, (const bf16*)Ws, (const bf16*)Ws3,
+                         bias_s, E, G, offsets, (int)rows, C, N, K, 2, arows);
     } else {
-      const unsigned mtiles = (unsigned)((rows + 127) / 128) + G;
-      hipLaunchKernelGGL((gemm_bf16_kernel<EPI, HB>), dim3(mtiles * (N / BN)), dim3(256), 0, s, A,
+      const int64_t tiles = ((rows + 127) / 128 + G) * (N / BN);
+      const int64_t grid = tiles < slots ? tiles : slots;
+      hipLaunchKernelGGL((gemm_bf16_kernel<EPI, HB>), dim3((unsigned)grid), dim3(256), 0, s, A,
                          (const bf16*)W, (const bf16*)W3, bias, (const bf16*)Ws, (const bf16*)Ws3,
                          bias_s, E, G, offsets, (int)rows, C, N, K, 0, arows);
     }
