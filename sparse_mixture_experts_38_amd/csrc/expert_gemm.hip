@@ -16,7 +16,7 @@
 
 namespace moe {
 
-enum { EPI_GELU = 0, EPI_RELU = 1, EPI_SWIGLU = 2, EPI_NONE = 3 };
+enum { EPI_GELU = 0, EPI_RELU = 1, EPI_SWIGLU = 2, EPI_NONE = 3, EPI_PARTIAL = 4 };
 
 template <int EPI>
 __device__ __forceinline__ float epilogue(float z1, float z3) {
@@ -42,7 +42,8 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, i
 #pragma unroll
   for (int i = 0; i <= PER; ++i) {
     const int gi = g0 + i;
-    o[i] = gi <= G ? min(max(offsets[gi], 0), rows_max) : rows_max;
+    o[i] = !offsets ? (gi == 0 ? 0 : rows_max)
+                    : gi <= G ? min(max(offsets[gi], 0), rows_max) : rows_max;
   }
   int n[PER];
   int s = 0;
@@ -82,7 +83,8 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, i
   return true;
 }
 
-// Per-wave view of the grouped row space: lane l holds groups 5l .. 5l+4
+// Per-wave view of the grouped row space (offsets null: one group of
+// rows_max rows): lane l holds groups 5l .. 5l+4
 // (first covered row, end row, tile count) and the exclusive prefix of tiles
 // before its first group. `part` selects the rows covered: 0 all rows of
 // every group in BM-row tiles; 1 the first floor(n / BM) BM-row tiles of each
@@ -103,7 +105,8 @@ __device__ __forceinline__ void tile_space_init(TileSpace& ts, const int32_t* __
 #pragma unroll
   for (int i = 0; i <= PER; ++i) {
     const int gi = g0 + i;
-    o[i] = gi <= G ? min(max(offsets[gi], 0), rows_max) : rows_max;
+    o[i] = !offsets ? (gi == 0 ? 0 : rows_max)
+                    : gi <= G ? min(max(offsets[gi], 0), rows_max) : rows_max;
   }
   int sum = 0;
 #pragma unroll
@@ -208,7 +211,8 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
     const bf16* __restrict__ A, const bf16* __restrict__ W, const bf16* __restrict__ W3,
     const float* __restrict__ bias, const bf16* __restrict__ Ws, const bf16* __restrict__ Ws3,
     const float* __restrict__ bias_s, int E, int G, const int32_t* __restrict__ offsets,
-    int rows_max, bf16* __restrict__ C, int N, int K, int part, const int32_t* __restrict__ arows) {
+    int rows_max, void* __restrict__ Cv, int N, int K, int part, const int32_t* __restrict__ arows,
+    int kparts) {
   constexpr bool GATED = EPI == EPI_SWIGLU;
   constexpr int BM = 128, BK = 64, CH = BK / 8;   // 8 chunks of 16 B per LDS row
   constexpr int NB = GATED ? 2 : 1;
@@ -220,6 +224,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
   constexpr int GROUP_M = 8;
   constexpr int CQ = BN / 8;                       // 16-byte chunks per output row
   __shared__ u32x4 smem[2 * STAGE];
+  bf16* __restrict__ C = reinterpret_cast<bf16*>(Cv);
 
   TileSpace ts;
   tile_space_init(ts, offsets, G, rows_max, BM, part, kGemmBigBM);
@@ -229,9 +234,15 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
   // Persistent blocks: block b takes tiles b, b + P, b + 2P, ... of the
   // XCD-aware order (P = gridDim.x, a multiple of 8, so a block stays on its
   // XCD's contiguous range of tiles).
+  // With kparts > 1 (EPI_PARTIAL only) each tile's K steps are cut into kparts
+  // equal ranges, one work item each, whose float32 sums go to plane
+  // (item % kparts) of C; a separate pass adds the planes.
   const int P = gridDim.x;
+  const int nk = K / BK;
+  const int len = nk / kparts;   // >= 4 and even (host's choice of kparts)
+  const int items = tiles * kparts;
   int it = blockIdx.x;
-  if (it >= tiles) return;
+  if (it >= items) return;
   const int t8 = tiles & ~7;
   const int per_group = GROUP_M * ntn;
   int g, row0, nrows, n0;
@@ -262,9 +273,14 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
   const char* ar1;
   const char* ar2;
   const char* ar3;
-  // tile it of the XCD-aware order: group, rows, columns, operand addresses
+  int kp, kbase;   // K range of the current work item and its first K step
+  // work item itx: tile itx / kparts of the XCD-aware order (group, rows,
+  // columns, operand addresses) and K range itx % kparts
   auto setup = [&](int itx) {
-    const int t = itx < t8 ? (itx & 7) * (t8 >> 3) + (itx >> 3) : itx;
+    const int ti = itx / kparts;
+    kp = itx - ti * kparts;
+    kbase = kp * len;
+    const int t = ti < t8 ? (ti & 7) * (t8 >> 3) + (ti >> 3) : ti;
     const int grp = t / per_group;
     const int first_m = grp * GROUP_M;
     const int in = t - grp * per_group;
@@ -325,7 +341,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
 #define MOE_SB() __builtin_amdgcn_sched_barrier(0)
 #define MOE_G(R, kt, i)                                                              \
   do {                                                                               \
-    const uint32_t kb_ = (uint32_t)(kt) * (BK * 2);                                  \
+    const uint32_t kb_ = (uint32_t)(kbase + (kt)) * (BK * 2);                        \
     if ((i) == 0) R.v0 = *reinterpret_cast<const u32x4*>(ar0 + kb_);                 \
     if ((i) == 1) R.v1 = *reinterpret_cast<const u32x4*>(ar1 + kb_);                 \
     if ((i) == 2) R.v2 = *reinterpret_cast<const u32x4*>(ar2 + kb_);                 \
@@ -381,9 +397,8 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
     }                                                                                \
   } while (0)
 
-  // K is a multiple of 256, so nk >= 4 and even; the last two steps are
+  // Steps kbase .. kbase + len - 1 (len >= 4 and even); the last two are
   // peeled so that the loop body has no branches.
-  const int nk = K / BK;
   setup(it);
 #pragma unroll
   for (int i = 0; i < 8; ++i) MOE_G(r0, 0, i);
@@ -397,7 +412,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
   for (int k4 = 0; k4 < 4; ++k4)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[k4][r] = 0.f;
-  for (int kt = 0; kt < nk - 2; kt += 2) {
+  for (int kt = 0; kt < len - 2; kt += 2) {
     // even step kt: stage 0 holds it, r1 holds step kt + 1, r0 is loaded with kt + 2
     MOE_STEP(0, r0, kt + 2, true, r1, true);
     __syncthreads();
@@ -412,10 +427,10 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
   // The registers r0 / r1 are free now: the first two K steps of this block's
   // next tile are loaded into them before the epilogue of this one, so their
   // latency is spent under the epilogue instead of before the next K loop.
-  const int cur_row0 = row0, cur_nrows = nrows, cur_n0 = n0;
+  const int cur_row0 = row0, cur_nrows = nrows, cur_n0 = n0, cur_kp = kp;
   const float* cur_bg = bg;
   const int itn = it + P;
-  const bool more = itn < tiles;
+  const bool more = itn < items;
   if (more) {
     setup(itn);
 #pragma unroll
@@ -424,6 +439,26 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
     for (int i = 0; i < 8; ++i) MOE_G(r1, 1, i);
   }
 
+  if constexpr (EPI == EPI_PARTIAL) {
+    // float32 sums straight to plane cur_kp of C ([kparts][rows_max][N]):
+    // lane (fr, fk) holds 4 consecutive columns of each 8-column group
+    float* __restrict__ Cp = reinterpret_cast<float*>(Cv) + (int64_t)cur_kp * rows_max * N;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int m = wm * 64 + i * 32 + fr;
+      if (m < cur_nrows) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd) {
+            const f32x4 v = {acc[i + 2 * j][qd * 4 + 0], acc[i + 2 * j][qd * 4 + 1],
+                             acc[i + 2 * j][qd * 4 + 2], acc[i + 2 * j][qd * 4 + 3]};
+            *reinterpret_cast<f32x4*>(Cp + (int64_t)(cur_row0 + m) * N + cur_n0 + wn * WN + j * 32 +
+                                      qd * 8 + fk * 4) = v;
+          }
+      }
+    }
+  } else {
   // Epilogue. Register r of a 32x32 accumulator holds row (lane % 32) and
   // column 8 (r / 4) + 4 (lane / 32) + r % 4 of the sub-tile, so lane (fr, fk)
   // owns 8 bytes of 16-byte output chunk q = wn WN / 8 + 4 j + r / 4.
@@ -469,6 +504,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
     const int swz = CQ == 16 ? (m & 15) : ((m >> 1) & 7);
     if (m < cur_nrows)
       *reinterpret_cast<u32x4*>(C + (int64_t)(cur_row0 + m) * N + cur_n0 + q * 8) = smem[m * CQ + (q ^ swz)];
+  }
   }
   if (!more) break;
   __syncthreads();   // the staged tile has been read out of stage 0
@@ -838,13 +874,13 @@ static hipError_t gemm_launch(const moe_config& c, const ET* A, const void* W, c
       const int64_t rgrid = rest * (N / BN) < slots ? rest * (N / BN) : slots;
       hipLaunchKernelGGL((gemm_bf16_kernel<EPI, HB>), dim3((unsigned)rgrid), dim3(256), 0, s, A,
                          (const bf16*)W, (const bf16*)W3, bias, (const bf16*)Ws, (const bf16*)Ws3,
-                         bias_s, E, G, offsets, (int)rows, C, N, K, 2, arows);
+                         bias_s, E, G, offsets, (int)rows, C, N, K, 2, arows, 1);
     } else {
       const int64_t tiles = ((rows + 127) / 128 + G) * (N / BN);
       const int64_t grid = tiles < slots ? tiles : slots;
       hipLaunchKernelGGL((gemm_bf16_kernel<EPI, HB>), dim3((unsigned)grid), dim3(256), 0, s, A,
                          (const bf16*)W, (const bf16*)W3, bias, (const bf16*)Ws, (const bf16*)Ws3,
-                         bias_s, E, G, offsets, (int)rows, C, N, K, 0, arows);
+                         bias_s, E, G, offsets, (int)rows, C, N, K, 0, arows, 1);
     }
   } else {
     const unsigned mtiles = (unsigned)((rows + kGemmBM - 1) / kGemmBM) + G;
@@ -852,6 +888,67 @@ static hipError_t gemm_launch(const moe_config& c, const ET* A, const void* W, c
                        s, A, (const float*)W, (const float*)W3, bias, (const float*)Ws,
                        (const float*)Ws3, bias_s, E, G, offsets, (int)rows, C, N, K, arows);
   }
+  return hipGetLastError();
+}
+
+// Router logits on MFMA where both x and W_g are bf16 and E is a multiple of
+// 128 (the 128-expert and 256-expert layers, whose gate GEMM is 2-15 GFLOP):
+// the 128 x 128 kernel runs over the single group of T rows with its K loop
+// cut into kparts ranges (one 128-row tile x 128 experts per work item), each
+// range's float32 sums go to a plane of `partials`, and router_reduce_kernel
+// adds the planes in order, then the gate bias. Deterministic; float32
+// accumulation throughout.
+int router_kparts(const moe_config& c) {
+  if (c.act_dtype != MOE_BF16 || c.router_dtype != MOE_BF16 || c.num_experts % 128 != 0 ||
+      c.d_model % kGemmAlign != 0 || c.tokens <= 0)
+    return 0;
+  const int64_t tiles = (c.tokens + 127) / 128 * (c.num_experts / 128);
+  const int nk = (int)(c.d_model / 64);
+  int kp = 1;
+  // about 512 work items, each range at least 4 (even) K steps
+  while (tiles * kp * 2 <= 512 && nk % (kp * 2) == 0 && nk / (kp * 2) >= 4 &&
+         (nk / (kp * 2)) % 2 == 0)
+    kp *= 2;
+  return kp;
+}
+
+__global__ __launch_bounds__(256) void router_reduce_kernel(const float* __restrict__ P, int kparts,
+                                                            int64_t n4, int E,
+                                                            const float* __restrict__ bg,
+                                                            float* __restrict__ logits) {
+  const f32x4* __restrict__ P4 = reinterpret_cast<const f32x4*>(P);
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+    f32x4 s = P4[i];
+    for (int p = 1; p < kparts; ++p) s += P4[(int64_t)p * n4 + i];
+    if (bg) {
+      const int e = (int)((i * 4) % E);
+      const f32x4 b = {bg[e], bg[e + 1], bg[e + 2], bg[e + 3]};
+      s += b;
+    }
+    reinterpret_cast<f32x4*>(logits)[i] = s;
+  }
+}
+
+hipError_t launch_router_gemm(const moe_config& c, const void* x, const void* w_gate,
+                              const float* b_gate, float* partials, float* logits,
+                              hipStream_t s) {
+  const int kp = router_kparts(c);
+  const int E = c.num_experts, K = (int)c.d_model;
+  const int64_t T = c.tokens;
+  const int64_t items = (T + 127) / 128 * (E / 128) * kp;
+  const int slots = gemm_slots();
+  hipLaunchKernelGGL((gemm_bf16_kernel<EPI_PARTIAL, false>),
+                     dim3((unsigned)(items < slots ? items : slots)), dim3(256), 0, s,
+                     (const bf16*)x, (const bf16*)w_gate, (const bf16*)nullptr, (const float*)nullptr,
+                     (const bf16*)nullptr, (const bf16*)nullptr, (const float*)nullptr, 1, 1,
+                     (const int32_t*)nullptr, (int)T, (void*)partials, E, K, 0,
+                     (const int32_t*)nullptr, kp);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int64_t n4 = T * E / 4;
+  const int64_t blocks = (n4 + 255) / 256 < 2048 ? (n4 + 255) / 256 : 2048;
+  hipLaunchKernelGGL(router_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, s, partials, kp,
+                     n4, E, b_gate, logits);
   return hipGetLastError();
 }
 

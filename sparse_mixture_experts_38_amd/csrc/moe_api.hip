@@ -29,6 +29,7 @@ WsLayout workspace_layout(const moe_config& c) {
   L.route_blocks = (int)(groups > 0 ? (groups + iters - 1) / iters : 1);
   L.logits = take((size_t)T * E * sizeof(float));
   L.route_partials = take((size_t)L.route_blocks * (E + 1) * sizeof(float));
+  L.router_planes = take((size_t)router_kparts(c) * T * E * sizeof(float));
   L.end_route = off;
   L.chunks = (int)(A > 0 ? (A + kRankChunk - 1) / kRankChunk : 1);
   L.chunk_hist = take((size_t)L.chunks * E * sizeof(int32_t));

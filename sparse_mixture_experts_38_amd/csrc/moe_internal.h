@@ -83,6 +83,7 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 struct WsLayout {
   size_t logits;          // float [T][E] (when the caller does not keep them)
   size_t route_partials;  // float [route_blocks][E + 1]
+  size_t router_planes;   // float [router_kparts][T][E] (MFMA router only)
   size_t chunk_hist;      // int32 [chunks][E]
   size_t chunk_base;      // int32 [chunks][E]
   size_t local_rank;      // int32 [T k]
@@ -104,6 +105,14 @@ inline int64_t rows_max(const moe_config& c) {
 
 // ------------------------------------------------------------------ launchers
 // Each returns hipSuccess or the first launch error. All enqueue on `stream`.
+// Router logits on MFMA (bf16 x and W_g, E a multiple of 128): router_kparts
+// is the number of K ranges (0 where this path does not apply), partials holds
+// router_kparts planes of T x E float32.
+int router_kparts(const moe_config& c);
+hipError_t launch_router_gemm(const moe_config& c, const void* x, const void* w_gate,
+                              const float* b_gate, float* partials, float* logits,
+                              hipStream_t stream);
+
 hipError_t launch_route(const moe_config& c, const WsLayout& L, const void* x, const void* w_gate,
                         const float* b_gate, const float* e_bias, float* logits, int32_t* topk_idx,
                         float* topk_gate, moe_stats* stats, char* ws, hipStream_t stream);

@@ -278,7 +278,9 @@ hipError_t launch_route(const moe_config& c, const WsLayout& L, const void* x, c
   const float* eb = c.score_fn == MOE_SCORE_SIGMOID ? e_bias : nullptr;
   const int64_t waves = (c.tokens + 7) / 8;   // one wave per 8 tokens
   const int blocks = (int)((waves + 3) / 4 < 4096 ? (waves + 3) / 4 : 4096);
-  if (c.act_dtype == MOE_BF16 && c.router_dtype == MOE_F32)
+  if (router_kparts(c) > 0)
+    launch_router_gemm(c, x, w_gate, bg, reinterpret_cast<float*>(ws + L.router_planes), lg, s);
+  else if (c.act_dtype == MOE_BF16 && c.router_dtype == MOE_F32)
     hipLaunchKernelGGL((router_logits_kernel<bf16, float>), dim3(blocks), dim3(256), 0, s,
                        (const bf16*)x, (const float*)w_gate, bg, lg, (int64_t)c.tokens, d, E);
   else if (c.act_dtype == MOE_BF16)
