@@ -20,6 +20,9 @@ What is computed (one MoE layer forward, token choice):
   E_e(x) = W2[e] act(W1[e] x + b1[e]) + b2[e]  (SwiGLU: W2[e](silu(W1 x) * W3 x))
   y[t] = sum_j kept * g[t,j] * E_{i_j}(x_t)  (+ shared expert output)
   L_aux = E * sum_i f_i * P_i,  z = mean_t logsumexp(h_t)^2
+and its backward pass: the gradients of <dy, y> + aux_coef L_aux + z_coef z with
+respect to x, the router and every expert's weights (chain rule through each
+step above; pinned by finite differences).
 
 Readings of the pages (where they are silent or ambiguous) are marked READING
 in the function that takes them. Every function here is pinned by a CPU test
@@ -430,3 +433,214 @@ def expert_flops(rows: int, d_model: int, d_ff: int, activation: str) -> int:
     """Multiply-add FLOPs (2 per MAC) of the expert matrices over ``rows`` rows."""
     mats = 3 if activation == "swiglu" else 2
     return 2 * rows * d_model * d_ff * mats
+
+
+# --------------------------------------------------------------------------
+# Backward pass (gradients of the layer)
+# --------------------------------------------------------------------------
+# The layer is differentiated through every path the forward above defines,
+# with the scalar objective
+#   L = <dy, y> + aux_coef * L_aux + z_coef * z
+# i.e. dy is the gradient of the caller's loss with respect to the layer output
+# and aux_coef / z_coef are the weights the loss puts on the balance loss and
+# the router z-loss (MoE Training: Mixture of Experts, "3. Load Balancing":
+# the auxiliary loss is added to the task loss with a small coefficient; MoE
+# From Scratch to DeepSeek V3, router z-loss as a training loss).
+# READING: the top-k choice, the capacity decision and the counts f_i are
+# piecewise constant in the parameters and carry no gradient (the pages train
+# the router only through the gate values, the probabilities P_i and the
+# logsumexp); the sigmoid selection bias e_bias receives none either (it is
+# moved by the balancing rule, not by the gradient).
+
+def gelu_grad(z):
+    """d/dz of exact GELU z Phi(z): Phi(z) + z phi(z)."""
+    z = np.asarray(z, F64)
+    return 0.5 * (1.0 + _erf(z / math.sqrt(2.0))) + z * np.exp(-0.5 * z * z) / math.sqrt(2.0 * math.pi)
+
+
+def relu_grad(z):
+    """d/dz max(z, 0): 1 for z > 0, else 0 (0 at the kink, as autograd takes it)."""
+    return (np.asarray(z, F64) > 0.0).astype(F64)
+
+
+def silu_grad(z):
+    """d/dz z sigma(z) = sigma(z) (1 + z (1 - sigma(z)))."""
+    z = np.asarray(z, F64)
+    s = 1.0 / (1.0 + np.exp(-z))
+    return s * (1.0 + z * (1.0 - s))
+
+
+def expert_ffn_backward(xr, w1, b1, w2, b2, activation: str, dY, w3=None) -> Dict[str, np.ndarray]:
+    """Gradients of one expert E(x) = W2 act(W1 x + b1) + b2 on rows xr [n, d].
+
+    Chain rule through expert_ffn (MoE Training: Mixture of Experts, "Basic MoE
+    Architecture"; moe_code.py, class Expert; SwiGLU reading as in expert_ffn):
+      dH = dY W2,  dW2 = dY^T H,  db2 = sum_rows dY
+      dZ = dH * act'(Z)   (SwiGLU: dZ = dH * U * silu'(Z), dU = dH * silu(Z))
+      dX = dZ W1 (+ dU W3),  dW1 = dZ^T X,  db1 = sum_rows dZ  (dW3 = dU^T X)
+    Returns dx, dw1, db1, dw2, db2, dw3 (None where absent) and the
+    intermediates z, h, dz.
+    """
+    X = np.asarray(xr, F64)
+    W1 = np.asarray(w1, F64)
+    W2 = np.asarray(w2, F64)
+    dY = np.asarray(dY, F64)
+    Z = X @ W1.T
+    if b1 is not None:
+        Z = Z + np.asarray(b1, F64)[None, :]
+    U = None
+    if activation == "gelu":
+        H = gelu(Z)
+    elif activation == "relu":
+        H = relu(Z)
+    elif activation == "swiglu":
+        U = X @ np.asarray(w3, F64).T
+        H = silu(Z) * U
+    else:
+        raise ValueError(activation)
+    dH = dY @ W2
+    dW2 = dY.T @ H
+    db2 = dY.sum(axis=0) if b2 is not None else None
+    dW3 = None
+    if activation == "gelu":
+        dZ = dH * gelu_grad(Z)
+    elif activation == "relu":
+        dZ = dH * relu_grad(Z)
+    else:
+        dZ = dH * U * silu_grad(Z)
+        dU = dH * silu(Z)
+        dW3 = dU.T @ X
+    dX = dZ @ W1
+    if activation == "swiglu":
+        dX = dX + dU @ np.asarray(w3, F64)
+    dW1 = dZ.T @ X
+    db1 = dZ.sum(axis=0) if b1 is not None else None
+    return dict(dx=dX, dw1=dW1, db1=db1, dw2=dW2, db2=db2, dw3=dW3, z=Z, h=H, dz=dZ)
+
+
+def combine_backward(dy, Y, gates, assign_row) -> tuple:
+    """Gradients of combine: dY[r] = g[t,j] dy[t] and dg[t,j] = <dy[t], Y[r]>
+    for the kept assignments (r = assign_row[t,j] >= 0); dropped ones get 0.
+
+    MoE From Scratch to DeepSeek V3, y = sum_{TopK} Gate_i E_i(x); MoE Training:
+    Mixture of Experts, "Weighted Combination". The shared expert's rows receive
+    dy itself (gate 1); that part is handled by the caller.
+    """
+    dy = np.asarray(dy, F64)
+    Y = np.asarray(Y, F64)
+    gates = np.asarray(gates, F64)
+    T, k = assign_row.shape
+    dY = np.zeros_like(Y)
+    dg = np.zeros((T, k), F64)
+    for j in range(k):
+        r = assign_row[:, j]
+        ok = r >= 0
+        dY[r[ok]] = gates[ok, j:j + 1] * dy[ok]
+        dg[ok, j] = np.einsum("td,td->t", dy[ok], Y[r[ok]])
+    return dY, dg
+
+
+def router_backward(logits, idx, score_fn: str, dgate, f, aux_coef: float, z_coef: float) -> np.ndarray:
+    """Gradient of the objective with respect to the router logits h [T, E].
+
+    Three terms, each the derivative of a forward definition:
+    1. Gates g_j = s_{i_j} / S, S = sum of the k selected scores (renormalised_gates):
+       dS-rule gives ds_{i_m} = (dg_m - sum_j dg_j g_j) / S for the selected experts.
+    2. L_aux = E sum_i f_i P_i with P_i = mean_t q_ti (balance_stats): q = p for the
+       softmax router, q = s / sum_e s for the sigmoid router; f is constant, so
+       dL_aux/dq_ti = E f_i / T. For the sigmoid router this is taken back through the
+       normalisation: ds_ti += (dq_ti - sum_e dq_te q_te) / sum_e s_te.
+    3. Scores to logits: softmax Jacobian dh = p * (dp - sum_e dp_e p_e), or sigmoid
+       dh = ds * s (1 - s). Router z-loss z = mean_t lse_t^2 (MoE From Scratch to
+       DeepSeek V3, router z-loss) adds 2 lse_t softmax(h_t) / T whatever the score
+       function.
+    """
+    h = np.asarray(logits, F64)
+    T, E = h.shape
+    idx = np.asarray(idx, np.int64)
+    dgate = np.asarray(dgate, F64)
+    f = np.asarray(f, F64)
+    p, lse = softmax_scores(h)
+    s = p if score_fn == "softmax" else sigmoid_scores(h)
+    sel = np.take_along_axis(s, idx, axis=1)
+    S = sel.sum(axis=1, keepdims=True)
+    g = sel / S
+    dsel = (dgate - (dgate * g).sum(axis=1, keepdims=True)) / S
+    ds = np.zeros((T, E), F64)
+    np.put_along_axis(ds, idx, dsel, axis=1)   # the k selected experts are distinct
+    dq = np.broadcast_to(aux_coef * E * f[None, :] / T, (T, E))
+    if score_fn == "softmax":
+        ds = ds + dq
+        dh = p * (ds - (ds * p).sum(axis=1, keepdims=True))
+    else:
+        tot = s.sum(axis=1, keepdims=True)
+        q = s / tot
+        ds = ds + (dq - (dq * q).sum(axis=1, keepdims=True)) / tot
+        dh = ds * s * (1.0 - s)
+    dh = dh + z_coef * 2.0 * lse[:, None] * p / T
+    return dh
+
+
+def backward(x, params, w, dy, aux_coef: float = 0.0, z_coef: float = 0.0, fwd=None,
+             logits=None) -> Dict[str, object]:
+    """All gradients of the layer for workload ``w``.
+
+    ``fwd`` is the result of forward() for the same inputs (computed here when
+    None); passing one computed with another implementation's routing choice
+    gives the stage-isolated comparison; ``logits`` overrides the logits the
+    router gradient is taken at (default: the float32 logits of ``fwd``). Returns dx, dw_gate, db_gate, dw1, db1,
+    dw2, db2, dw3, the shared expert's dws1, dbs1, dws2, dbs2, dws3, and the
+    intermediates dY (expert-sorted rows), dgate, dlogits, z (pre-activation per
+    row) and dz.
+    """
+    x = np.asarray(x, F64)
+    T, d = x.shape
+    E, k = w.num_experts, w.top_k
+    if fwd is None:
+        fwd = forward(x, params, w)
+    act = w.activation
+    dy = np.asarray(dy, F64)
+    offsets = fwd["expert_offsets"]
+    R = int(offsets[-1])
+    dY, dgate = combine_backward(dy, fwd["Y"], fwd["gates"], fwd["assign_row"])
+    F = params["w1"].shape[1]
+    dx = np.zeros((T, d), F64)
+    out = dict(dw1=np.zeros((E, F, d), F64), dw2=np.zeros((E, d, F), F64),
+               db1=np.zeros((E, F), F64) if params.get("b1") is not None else None,
+               db2=np.zeros((E, d), F64) if params.get("b2") is not None else None,
+               dw3=np.zeros((E, F, d), F64) if act == "swiglu" else None)
+    Z = np.zeros((R, F), F64)
+    dZ = np.zeros((R, F), F64)
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        toks = fwd["row_token"][lo:hi]
+        gr = expert_ffn_backward(x[toks], params["w1"][e], _opt(params.get("b1"), e),
+                                 params["w2"][e], _opt(params.get("b2"), e), act, dY[lo:hi],
+                                 _opt(params.get("w3"), e))
+        np.add.at(dx, toks, gr["dx"])
+        out["dw1"][e] = gr["dw1"]
+        out["dw2"][e] = gr["dw2"]
+        if out["db1"] is not None:
+            out["db1"][e] = gr["db1"]
+            out["db2"][e] = gr["db2"]
+        if act == "swiglu":
+            out["dw3"][e] = gr["dw3"]
+        Z[lo:hi] = gr["z"]
+        dZ[lo:hi] = gr["dz"]
+    if w.num_shared_experts:
+        gs = expert_ffn_backward(x, params["ws1"][0], _opt(params.get("bs1"), 0), params["ws2"][0],
+                                 _opt(params.get("bs2"), 0), act, dy, _opt(params.get("ws3"), 0))
+        dx += gs["dx"]
+        out.update(dws1=gs["dw1"], dbs1=gs["db1"], dws2=gs["dw2"], dbs2=gs["db2"], dws3=gs["dw3"],
+                   z_shared=gs["z"], dz_shared=gs["dz"])
+    f = np.asarray(fwd["counts_pre"], F64) / float(T * k)
+    dlogits = router_backward(fwd["logits"] if logits is None else logits, fwd["idx"],
+                              w.score_fn, dgate, f, aux_coef, z_coef)
+    Wg = np.asarray(params["w_gate"], F64)
+    dx += dlogits @ Wg
+    out.update(dx=dx, dw_gate=dlogits.T @ x,
+               db_gate=dlogits.sum(axis=0) if params.get("b_gate") is not None else None,
+               dY=dY, dgate=dgate, dlogits=dlogits, z=Z, dz=dZ)
+    return out
