@@ -274,6 +274,76 @@ int moe_forward(const moe_config* cfg, const void* x, const moe_weights* w, void
                 const moe_routing* routing, moe_stats* stats, void* workspace,
                 size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------ training
+ * The layer's backward pass. The objective differentiated is
+ *   L = <dy, y> + aux_coef * L_aux + z_coef * z
+ * where dy is the gradient of the caller's loss with respect to the layer output
+ * and aux_coef, z_coef the weights of the balance loss and the router z-loss in
+ * that loss ([P1] "3. Load Balancing": the auxiliary loss is added to the task
+ * loss with a small coefficient; [P4] router z-loss). The top-k choices, the
+ * capacity decisions and the counts f_i are piecewise constant and carry no
+ * gradient; the sigmoid selection bias e_bias receives none.
+ * This build runs the backward for act_dtype MOE_BF16 with GELU or ReLU experts
+ * (other layers return MOE_ERR_UNSUPPORTED).
+ */
+
+/* Forward activations the backward reads (device buffers the caller owns). */
+typedef struct moe_saved {
+  void* z;      /* [T k + S T, F] act_dtype: W1 x + b1 per expert-sorted row    */
+  void* y_perm; /* [T k + S T, d] act_dtype: the expert outputs E_e(x) per row  */
+} moe_saved;
+
+/* Gradients written by moe_backward (device buffers; float32 except dx). Every
+ * buffer is overwritten (not accumulated into). NULL where the layer has no such
+ * parameter: db_gate iff has_gate_bias, db1/db2 iff has_bias, the ws* ones iff
+ * num_shared_experts. */
+typedef struct moe_grads {
+  void* dx;        /* [T, d] act_dtype                         */
+  float* dw_gate;  /* [E, d]                                   */
+  float* db_gate;  /* [E]                                      */
+  float* dw1;      /* [E, F, d]                                */
+  float* db1;      /* [E, F]                                   */
+  float* dw2;      /* [E, d, F]                                */
+  float* db2;      /* [E, d]                                   */
+  float* dws1;     /* [F, d]   shared expert                   */
+  float* dbs1;     /* [F]                                      */
+  float* dws2;     /* [d, F]                                   */
+  float* dbs2;     /* [d]                                      */
+} moe_grads;
+
+/*
+ * The layer forward of moe_forward that also keeps what the backward needs:
+ * routing->logits (required here) and saved->z, saved->y_perm. The expert
+ * activation is applied to z after its rounding to act_dtype, so the backward
+ * recomputes exactly the h the second GEMM used. Same arguments and workspace
+ * as moe_forward.
+ */
+int moe_forward_train(const moe_config* cfg, const void* x, const moe_weights* w, void* y,
+                      const moe_routing* routing, moe_stats* stats, const moe_saved* saved,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Host only. Workspace bytes needed by moe_backward. */
+int moe_backward_workspace_size(const moe_config* cfg, size_t* bytes_out);
+
+/*
+ * Gradients of the objective above for one layer, from the results of
+ * moe_forward_train on the same x and weights (routing, stats and saved must be
+ * unchanged since). Chain rule through combine ([P4] y = sum Gate_i E_i(x)), the
+ * expert FFN ([P1] "Basic MoE Architecture"), the renormalised top-k gates and
+ * the score function ([P1] "Basic MoE Architecture", [P4] V3 sigmoid routing),
+ * L_aux ([P1] "3. Load Balancing") and the z-loss ([P4]), and the gate linear
+ * layer. Expert GEMMs in bf16 with float32 accumulation; router math, weight and
+ * bias gradients in float32. Deterministic (no floating-point atomics).
+ *   x, w         the forward's inputs;  routing, stats, saved: the forward's outputs
+ *   dy           [T, d] act_dtype
+ *   grads        output buffers (moe_grads)
+ *   workspace    >= moe_backward_workspace_size(cfg) bytes
+ */
+int moe_backward(const moe_config* cfg, const void* x, const moe_weights* w,
+                 const moe_routing* routing, const moe_stats* stats, const moe_saved* saved,
+                 const void* dy, float aux_coef, float z_coef, const moe_grads* grads,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -46,6 +46,15 @@ class MoeRouting(ctypes.Structure):
                                         "row_token", "assign_row")]
 
 
+class MoeSaved(ctypes.Structure):
+    _fields_ = [(n, c_void_p) for n in ("z", "y_perm")]
+
+
+class MoeGrads(ctypes.Structure):
+    _fields_ = [(n, c_void_p) for n in ("dx", "dw_gate", "db_gate", "dw1", "db1", "dw2", "db2",
+                                        "dws1", "dbs1", "dws2", "dbs2")]
+
+
 STATS_DTYPE = np.dtype([
     ("counts_pre", "<i4", (MAX_EXPERTS,)), ("counts_kept", "<i4", (MAX_EXPERTS,)),
     ("frac", "<f4", (MAX_EXPERTS,)), ("prob_mean", "<f4", (MAX_EXPERTS,)),
@@ -90,9 +99,17 @@ def lib():
     L.moe_combine.argtypes = [cfgp, P, P, P, P, P, P]
     L.moe_forward.argtypes = [cfgp, P, ctypes.POINTER(MoeWeights), P, ctypes.POINTER(MoeRouting),
                               P, P, c_size_t, P]
+    L.moe_forward_train.argtypes = [cfgp, P, ctypes.POINTER(MoeWeights), P,
+                                    ctypes.POINTER(MoeRouting), P, ctypes.POINTER(MoeSaved), P,
+                                    c_size_t, P]
+    L.moe_backward_workspace_size.argtypes = [cfgp, ctypes.POINTER(c_size_t)]
+    L.moe_backward.argtypes = [cfgp, P, ctypes.POINTER(MoeWeights), ctypes.POINTER(MoeRouting), P,
+                               ctypes.POINTER(MoeSaved), P, ctypes.c_float, ctypes.c_float,
+                               ctypes.POINTER(MoeGrads), P, c_size_t, P]
     for name in ("moe_validate_config", "moe_capacity", "moe_workspace_size", "moe_route",
                  "moe_permute", "moe_expert_ffn", "moe_expert_up", "moe_expert_down",
-                 "moe_combine", "moe_forward"):
+                 "moe_combine", "moe_forward", "moe_forward_train", "moe_backward_workspace_size",
+                 "moe_backward"):
         getattr(L, name).restype = c_int
     _lib = L
     return L
@@ -309,14 +326,9 @@ def combine(cfg, y_perm, expert_offsets, assign_row, topk_gate, y):
                              _ptr(assign_row), _ptr(topk_gate), _ptr(y), _stream()), "moe_combine")
 
 
-def forward(cfg, x, weights: Dict[str, Optional[torch.Tensor]], y, routing: Dict[str, torch.Tensor],
-            stats, workspace):
+def _need_weights(cfg, W):
     T, d, F, E, k, S, act, rdt = _sizes(cfg)
-    rows = T * k + S * T
     swiglu = cfg.activation == ACTIVATION["swiglu"]
-    _need(x, "x", (T, d), act)
-    _need(y, "y", (T, d), act)
-    W = weights
     _need(W["w_gate"], "w_gate", (E, d), rdt)
     _need(W.get("b_gate"), "b_gate", (E,), torch.float32, optional=not cfg.has_gate_bias)
     _need(W.get("e_bias"), "e_bias", (E,), torch.float32, optional=True)
@@ -331,13 +343,27 @@ def forward(cfg, x, weights: Dict[str, Optional[torch.Tensor]], y, routing: Dict
         _need(W.get("bs1"), "bs1", (S, F), torch.float32, optional=not cfg.has_bias)
         _need(W.get("ws2"), "ws2", (S, d, F), act)
         _need(W.get("bs2"), "bs2", (S, d), torch.float32, optional=not cfg.has_bias)
-    R = routing
-    _need(R.get("logits"), "logits", (T, E), torch.float32, optional=True)
+
+
+def _need_routing(cfg, R, logits_required=False):
+    T, d, F, E, k, S, act, rdt = _sizes(cfg)
+    rows = T * k + S * T
+    _need(R.get("logits"), "logits", (T, E), torch.float32, optional=not logits_required)
     _need(R["topk_idx"], "topk_idx", (T, k), torch.int32)
     _need(R["topk_gate"], "topk_gate", (T, k), torch.float32)
     _need(R["expert_offsets"], "expert_offsets", (E + S + 1,), torch.int32)
     _need(R["row_token"], "row_token", (rows,), torch.int32)
     _need(R["assign_row"], "assign_row", (T, k), torch.int32)
+
+
+def forward(cfg, x, weights: Dict[str, Optional[torch.Tensor]], y, routing: Dict[str, torch.Tensor],
+            stats, workspace):
+    T, d, F, E, k, S, act, rdt = _sizes(cfg)
+    _need(x, "x", (T, d), act)
+    _need(y, "y", (T, d), act)
+    W, R = weights, routing
+    _need_weights(cfg, W)
+    _need_routing(cfg, R)
     _need_stats(stats)
     _need_ws(workspace)
     mw = MoeWeights(*[_ptr(W.get(n)) for n, _ in MoeWeights._fields_])
@@ -347,7 +373,102 @@ def forward(cfg, x, weights: Dict[str, Optional[torch.Tensor]], y, routing: Dict
            "moe_forward")
 
 
+def _need_saved(cfg, saved):
+    T, d, F, E, k, S, act, _ = _sizes(cfg)
+    rows = T * k + S * T
+    _need(saved.get("z"), "saved z", (rows, F), act)
+    _need(saved.get("y_perm"), "saved y_perm", (rows, d), act)
+
+
+def forward_train(cfg, x, weights, y, routing, stats, saved, workspace):
+    """moe_forward_train: the forward that also keeps logits, z and y_perm."""
+    T, d, F, E, k, S, act, rdt = _sizes(cfg)
+    _need(x, "x", (T, d), act)
+    _need(y, "y", (T, d), act)
+    _need_weights(cfg, weights)
+    _need_routing(cfg, routing, logits_required=True)
+    _need_saved(cfg, saved)
+    _need_stats(stats)
+    _need_ws(workspace)
+    mw = MoeWeights(*[_ptr(weights.get(n)) for n, _ in MoeWeights._fields_])
+    mr = MoeRouting(*[_ptr(routing.get(n)) for n, _ in MoeRouting._fields_])
+    ms = MoeSaved(*[_ptr(saved.get(n)) for n, _ in MoeSaved._fields_])
+    _check(lib().moe_forward_train(ctypes.byref(cfg), _ptr(x), ctypes.byref(mw), _ptr(y),
+                                   ctypes.byref(mr), _ptr(stats), ctypes.byref(ms), _ptr(workspace),
+                                   workspace.numel(), _stream()), "moe_forward_train")
+
+
+def backward_workspace_size(cfg: MoeConfig) -> int:
+    n = c_size_t(0)
+    _check(lib().moe_backward_workspace_size(ctypes.byref(cfg), ctypes.byref(n)),
+           "moe_backward_workspace_size")
+    return int(n.value)
+
+
+def _need_grads(cfg, g):
+    T, d, F, E, k, S, act, _ = _sizes(cfg)
+    f32 = torch.float32
+    _need(g.get("dx"), "dx", (T, d), act)
+    _need(g.get("dw_gate"), "dw_gate", (E, d), f32)
+    _need(g.get("db_gate"), "db_gate", (E,), f32, optional=not cfg.has_gate_bias)
+    _need(g.get("dw1"), "dw1", (E, F, d), f32)
+    _need(g.get("db1"), "db1", (E, F), f32, optional=not cfg.has_bias)
+    _need(g.get("dw2"), "dw2", (E, d, F), f32)
+    _need(g.get("db2"), "db2", (E, d), f32, optional=not cfg.has_bias)
+    if S:
+        _need(g.get("dws1"), "dws1", (F, d), f32)
+        _need(g.get("dbs1"), "dbs1", (F,), f32, optional=not cfg.has_bias)
+        _need(g.get("dws2"), "dws2", (d, F), f32)
+        _need(g.get("dbs2"), "dbs2", (d,), f32, optional=not cfg.has_bias)
+
+
+def backward(cfg, x, weights, routing, stats, saved, dy, aux_coef, z_coef, grads, workspace):
+    """moe_backward: gradients of <dy, y> + aux_coef L_aux + z_coef z."""
+    T, d, F, E, k, S, act, rdt = _sizes(cfg)
+    _need(x, "x", (T, d), act)
+    _need(dy, "dy", (T, d), act)
+    _need_weights(cfg, weights)
+    _need_routing(cfg, routing, logits_required=True)
+    _need_saved(cfg, saved)
+    _need_grads(cfg, grads)
+    _need_stats(stats)
+    _need_ws(workspace)
+    mw = MoeWeights(*[_ptr(weights.get(n)) for n, _ in MoeWeights._fields_])
+    mr = MoeRouting(*[_ptr(routing.get(n)) for n, _ in MoeRouting._fields_])
+    ms = MoeSaved(*[_ptr(saved.get(n)) for n, _ in MoeSaved._fields_])
+    mg = MoeGrads(*[_ptr(grads.get(n)) for n, _ in MoeGrads._fields_])
+    _check(lib().moe_backward(ctypes.byref(cfg), _ptr(x), ctypes.byref(mw), ctypes.byref(mr),
+                              _ptr(stats), ctypes.byref(ms), _ptr(dy), float(aux_coef),
+                              float(z_coef), ctypes.byref(mg), _ptr(workspace), workspace.numel(),
+                              _stream()), "moe_backward")
+
+
 # ------------------------------------------------------------------ helpers
+def alloc_saved(cfg, device="cuda") -> Dict[str, torch.Tensor]:
+    T, d, F, E, k, S, act, _ = _sizes(cfg)
+    rows = T * k + S * T
+    return dict(z=torch.empty(rows, F, dtype=act, device=device),
+                y_perm=torch.empty(rows, d, dtype=act, device=device))
+
+
+def alloc_grads(cfg, device="cuda") -> Dict[str, Optional[torch.Tensor]]:
+    T, d, F, E, k, S, act, _ = _sizes(cfg)
+    f = dict(dtype=torch.float32, device=device)
+    b, gb = bool(cfg.has_bias), bool(cfg.has_gate_bias)
+    return dict(dx=torch.empty(T, d, dtype=act, device=device), dw_gate=torch.empty(E, d, **f),
+                db_gate=torch.empty(E, **f) if gb else None, dw1=torch.empty(E, F, d, **f),
+                db1=torch.empty(E, F, **f) if b else None, dw2=torch.empty(E, d, F, **f),
+                db2=torch.empty(E, d, **f) if b else None,
+                dws1=torch.empty(F, d, **f) if S else None,
+                dbs1=torch.empty(F, **f) if S and b else None,
+                dws2=torch.empty(d, F, **f) if S else None,
+                dbs2=torch.empty(d, **f) if S and b else None)
+
+
+def alloc_backward_workspace(cfg, device="cuda") -> torch.Tensor:
+    return torch.empty(backward_workspace_size(cfg), dtype=torch.uint8, device=device)
+
+
 def alloc_routing(cfg, device="cuda", logits=True) -> Dict[str, torch.Tensor]:
     """Output buffers for the routing results of moe_forward."""
     T, d, F, E, k, S, _, _ = _sizes(cfg)
@@ -454,3 +575,35 @@ class Plan:
 
     def forward(self, stream=None):
         self._call(self._forward, "moe_forward", stream)
+
+
+class TrainPlan:
+    """Pre-marshalled moe_forward_train and moe_backward on fixed buffers (shapes
+    checked once, as in Plan)."""
+
+    def __init__(self, cfg, x, weights, y, routing, stats, saved, workspace, dy, grads, bwd_workspace,
+                 aux_coef=0.01, z_coef=0.001):
+        forward_train(cfg, x, weights, y, routing, stats, saved, workspace)   # validates
+        _need(dy, "dy", (cfg.tokens, cfg.d_model), TORCH_DTYPE[cfg.act_dtype])
+        _need_grads(cfg, grads)
+        _need_ws(bwd_workspace)
+        self.keep = (cfg, x, weights, y, routing, stats, saved, workspace, dy, grads, bwd_workspace)
+        self.mw = MoeWeights(*[_ptr(weights.get(n)) for n, _ in MoeWeights._fields_])
+        self.mr = MoeRouting(*[_ptr(routing.get(n)) for n, _ in MoeRouting._fields_])
+        self.ms = MoeSaved(*[_ptr(saved.get(n)) for n, _ in MoeSaved._fields_])
+        self.mg = MoeGrads(*[_ptr(grads.get(n)) for n, _ in MoeGrads._fields_])
+        c = ctypes.byref(cfg)
+        L = lib()
+        self._fwd = (L.moe_forward_train, (c, _ptr(x), ctypes.byref(self.mw), _ptr(y),
+                                           ctypes.byref(self.mr), _ptr(stats), ctypes.byref(self.ms),
+                                           _ptr(workspace), workspace.numel()))
+        self._bwd = (L.moe_backward, (c, _ptr(x), ctypes.byref(self.mw), ctypes.byref(self.mr),
+                                      _ptr(stats), ctypes.byref(self.ms), _ptr(dy), float(aux_coef),
+                                      float(z_coef), ctypes.byref(self.mg), _ptr(bwd_workspace),
+                                      bwd_workspace.numel()))
+
+    def forward(self, stream=None):
+        Plan._call(self._fwd, "moe_forward_train", stream)
+
+    def backward(self, stream=None):
+        Plan._call(self._bwd, "moe_backward", stream)

@@ -15,7 +15,8 @@ LIB_NAME = "libmoe_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["moe_api.hip", "router.hip", "permute.hip", "expert_gemm.hip", "combine.hip"]
+SOURCES = ["moe_api.hip", "router.hip", "permute.hip", "expert_gemm.hip", "combine.hip",
+           "backward.hip"]
 
 # Packed fp32 instructions are switched off for every device compilation.
 HIPCC_FLAGS = [

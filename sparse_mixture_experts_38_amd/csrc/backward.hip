@@ -1,0 +1,518 @@
+// Backward pass of the MoE layer (bf16 activations, float32 router and
+// gradients), and the activation step of the training forward that saves the
+// pre-activation. The grouped GEMMs of the backward are in expert_gemm.hip;
+// these are the memory-bound steps around them.
+//
+// Objective differentiated: L = <dy, y> + aux_coef L_aux + z_coef z, with the
+// forward of "MoE From Scratch to DeepSeek V3" (token-choice top-k, gate
+// renormalisation, auxiliary loss, router z-loss, sigmoid routing with a
+// selection bias, shared experts) and the expert FFN of "MoE Training: Mixture
+// of Experts" ("Basic MoE Architecture"). Top-k choices, capacity decisions and
+// the counts f_i carry no gradient; the selection bias receives none.
+#include "moe_internal.h"
+
+namespace moe {
+
+__device__ __forceinline__ float act_bf16(int act, float z) {
+  return act == MOE_ACT_GELU ? gelu_poly(z) : fmaxf(z, 0.f);
+}
+
+__device__ __forceinline__ int clamp_off(const int32_t* __restrict__ off, int g, int64_t rows_max) {
+  const int v = off[g];
+  return v < 0 ? 0 : (v > rows_max ? (int)rows_max : v);
+}
+
+// ------------------------------------------------------------------ training forward
+// h[r] = act(z[r]) for the rows r < expert_offsets[G] (z already rounded to
+// bf16, so the backward recomputes exactly this h). 8 elements per thread.
+__global__ __launch_bounds__(256) void act_rows_kernel(const bf16* __restrict__ z,
+                                                       const int32_t* __restrict__ off, int G,
+                                                       int64_t rows_max, int F, int act,
+                                                       bf16* __restrict__ h) {
+  const int64_t R = clamp_off(off, G, rows_max);
+  const int64_t n8 = R * F / 8;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n8;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    float v[8];
+    load8(z + i * 8, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = act_bf16(act, v[e]);
+    store8(h + i * 8, v);
+  }
+}
+
+// ------------------------------------------------------------------ combine backward
+// One wavefront per token t. For each choice j with row r = assign_row[t, j]
+// (kept): dYp[r] = g[t, j] dy[t] (bf16) and dgate[t, j] = <dy[t], y_perm[r]>
+// (float32, lanes then a wave reduction); dropped choices get dgate = 0. With a
+// shared expert, its row expert_offsets[E] + t receives dy[t] (gate 1).
+__global__ __launch_bounds__(256) void combine_bwd_kernel(
+    const bf16* __restrict__ dy, const bf16* __restrict__ y_perm, const float* __restrict__ gate,
+    const int32_t* __restrict__ assign_row, const int32_t* __restrict__ off, int64_t T, int d, int k,
+    int E, int S, int64_t rows_max, bf16* __restrict__ dyp, float* __restrict__ dgate) {
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= T) return;
+  const bf16* dyt = dy + t * d;
+  for (int j = 0; j < k; ++j) {
+    const int r = assign_row[t * k + j];
+    float dot = 0.f;
+    if (r >= 0 && r < rows_max) {
+      const float g = gate[t * k + j];
+      const bf16* yr = y_perm + (int64_t)r * d;
+      bf16* out = dyp + (int64_t)r * d;
+      for (int c = lane * 8; c < d; c += 512) {
+        float a[8], b[8];
+        load8(dyt + c, a);
+        load8(yr + c, b);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          dot = fmaf(a[e], b[e], dot);
+          a[e] *= g;
+        }
+        store8(out + c, a);
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) dot += __shfl_xor(dot, o, 64);
+    if (lane == 0) dgate[t * k + j] = dot;
+  }
+  if (S) {
+    const int64_t r = (int64_t)clamp_off(off, E, rows_max) + t;
+    if (r < rows_max) {
+      bf16* out = dyp + r * d;
+      for (int c = lane * 8; c < d; c += 512)
+        *reinterpret_cast<uint4*>(out + c) = *reinterpret_cast<const uint4*>(dyt + c);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ router backward
+// One wavefront per token; lane l holds experts l, l + 64, l + 128, l + 192.
+// Gates g_j = s_{i_j} / S (S = sum of the selected scores) give
+// ds_{i_j} = (dg_j - sum_m dg_m g_m) / S; L_aux = E sum_i f_i P_i adds
+// dq_i = aux_coef E f_i / T to the probabilities it averages (softmax: p;
+// sigmoid: q = s / sum s, taken back through the normalisation); then the
+// softmax Jacobian p (ds - <ds, p>) or the sigmoid derivative s (1 - s), and
+// the z-loss term z_coef 2 lse p / T. float32 throughout (the router's
+// precision).
+__global__ __launch_bounds__(256) void router_bwd_kernel(
+    const float* __restrict__ logits, const int32_t* __restrict__ topk_idx,
+    const float* __restrict__ dgate, const int32_t* __restrict__ counts_pre, int64_t T, int E,
+    int k, int sigmoid, float aux_coef, float z_coef, float* __restrict__ dlogits) {
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= T) return;
+  const float* h = logits + t * E;
+  float hv[4];
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + 64 * i;
+    hv[i] = e < E ? h[e] : -INFINITY;
+    m = fmaxf(m, hv[i]);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  float se = 0.f;
+  float ex[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ex[i] = lane + 64 * i < E ? expf(hv[i] - m) : 0.f;
+    se += ex[i];
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) se += __shfl_xor(se, o, 64);
+  const float lse = m + logf(se);
+  const float inv_se = 1.0f / se;
+  // selected scores and the renormalised gates
+  float ssel[MOE_MAX_TOP_K], dg[MOE_MAX_TOP_K];
+  int isel[MOE_MAX_TOP_K];
+  float S = 0.f;
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOP_K; ++j) {
+    isel[j] = -1;
+    ssel[j] = dg[j] = 0.f;
+    if (j < k) {
+      int e = topk_idx[t * k + j];
+      e = e < 0 ? 0 : (e >= E ? E - 1 : e);
+      isel[j] = e;
+      const float he = h[e];
+      ssel[j] = sigmoid ? 1.0f / (1.0f + expf(-he)) : expf(he - m) * inv_se;
+      dg[j] = dgate[t * k + j];
+      S += ssel[j];
+    }
+  }
+  float c0 = 0.f;
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOP_K; ++j) c0 += dg[j] * (ssel[j] / S);
+  const float aux_scale = aux_coef * (float)E / ((float)T * (float)T * (float)k);
+  float p[4], s[4], ds[4], dq[4];
+  float tot = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + 64 * i;
+    p[i] = ex[i] * inv_se;
+    s[i] = e < E ? (sigmoid ? 1.0f / (1.0f + expf(-hv[i])) : p[i]) : 0.f;
+    tot += s[i];
+    float v = 0.f;
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOP_K; ++j) v += isel[j] == e ? (dg[j] - c0) / S : 0.f;
+    ds[i] = v;
+    dq[i] = e < E ? aux_scale * (float)counts_pre[e] : 0.f;   // aux_coef E f_e / T
+  }
+  float dh[4];
+  if (!sigmoid) {
+    float dot = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ds[i] += dq[i];
+      dot += ds[i] * p[i];
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) dot += __shfl_xor(dot, o, 64);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dh[i] = p[i] * (ds[i] - dot);
+  } else {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) tot += __shfl_xor(tot, o, 64);
+    float dotq = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dotq += dq[i] * (s[i] / tot);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) dotq += __shfl_xor(dotq, o, 64);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ds[i] += (dq[i] - dotq) / tot;
+      dh[i] = ds[i] * s[i] * (1.0f - s[i]);
+    }
+  }
+  const float zs = z_coef * 2.0f * lse / (float)T;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + 64 * i;
+    if (e < E) dlogits[t * E + e] = fmaf(zs, p[i], dh[i]);
+  }
+}
+
+// ------------------------------------------------------------------ transposes
+// Batched bf16 transpose in[b][M][N] -> out[b][N][M] through a 64 x 64 LDS tile
+// (16-byte loads and stores; M and N multiples of 64).
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16* __restrict__ in,
+                                                             bf16* __restrict__ out, int M, int N) {
+  __shared__ uint16_t tile[64][66];
+  const int n0 = blockIdx.x * 64, m0 = blockIdx.y * 64;
+  const int64_t b = blockIdx.z;
+  const bf16* src = in + b * (int64_t)M * N;
+  bf16* dst = out + b * (int64_t)M * N;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = (tid >> 3) + 32 * i, c = (tid & 7) * 8;
+    const uint4 u = *reinterpret_cast<const uint4*>(src + (int64_t)(m0 + r) * N + n0 + c);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      tile[r][c + 2 * e] = (uint16_t)(w[e] & 0xffffu);
+      tile[r][c + 2 * e + 1] = (uint16_t)(w[e] >> 16);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = (tid >> 3) + 32 * i, c = (tid & 7) * 8;   // r: row of out (n), c: first m
+    uint4 u;
+    u.x = (uint32_t)tile[c + 0][r] | ((uint32_t)tile[c + 1][r] << 16);
+    u.y = (uint32_t)tile[c + 2][r] | ((uint32_t)tile[c + 3][r] << 16);
+    u.z = (uint32_t)tile[c + 4][r] | ((uint32_t)tile[c + 5][r] << 16);
+    u.w = (uint32_t)tile[c + 6][r] | ((uint32_t)tile[c + 7][r] << 16);
+    *reinterpret_cast<uint4*>(dst + (int64_t)(n0 + r) * M + m0 + c) = u;
+  }
+}
+
+// so[g]: expert_offsets clamped to [0, rows_max] and made non-decreasing, so the
+// groups' rows never sum past rows_max; po[g] = sum over g' < g of the padded
+// row count of group g' (its rows rounded up to a multiple of 128, at least
+// 128), hence po[G] <= rows_max + 128 G (one thread; G <= 257).
+__global__ void pad_offsets_kernel(const int32_t* __restrict__ off, int G, int64_t rows_max,
+                                   int32_t* __restrict__ po, int32_t* __restrict__ so) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  int acc = 0, prev = clamp_off(off, 0, rows_max);
+  po[0] = 0;
+  so[0] = prev;
+  for (int g = 0; g < G; ++g) {
+    int hi = clamp_off(off, g + 1, rows_max);
+    hi = hi < prev ? prev : hi;
+    const int r = hi - prev;
+    const int p = r <= 128 ? 128 : (r + 127) & ~127;
+    acc += p;
+    po[g + 1] = acc;
+    so[g + 1] = hi;
+    prev = hi;
+  }
+}
+
+// Expert-sorted rows -> transposed, group-padded layout for the weight
+// gradient: out[c][k] for k in group g's padded range [po[g], po[g+1]) holds
+// row r = so[g] + (k - po[g]) of the source (zero past the group's rows; so
+// and po as written by pad_offsets_kernel).
+// MODE 0: rows of src [rows][C]; MODE 1: token rows of src (x [T][C]) through
+// row_token; MODE 2: act(src) (src = z, the saved pre-activation). With
+// partial != nullptr also writes the 64-row column sums of the (bf16) values
+// of its block to partial[k / 64][c] (bias gradients).
+template <int MODE>
+__global__ __launch_bounds__(256) void transpose_rows_kernel(
+    const bf16* __restrict__ src, const int32_t* __restrict__ row_token,
+    const int32_t* __restrict__ so, const int32_t* __restrict__ po, int G, int64_t src_rows, int C,
+    int ldk, int act, bf16* __restrict__ out, float* __restrict__ partial) {
+  __shared__ float tile[64][65];
+  const int k0 = blockIdx.x * 64;
+  const int c0 = blockIdx.y * 64;
+  if (k0 >= po[G]) return;
+  int lo = 0, hi = G;   // group of column k0: po[lo] <= k0 < po[lo + 1]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (po[mid] <= k0) lo = mid; else hi = mid;
+  }
+  const int g = lo;
+  const int gs = so[g];
+  const int R = so[g + 1] - gs;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int kk = (tid >> 3) + 32 * i, c = (tid & 7) * 8;
+    const int local = k0 + kk - po[g];
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (local < R) {
+      int64_t row = gs + local;
+      if (MODE == 1) {
+        row = row_token[row];
+        row = row < 0 ? 0 : (row >= src_rows ? src_rows - 1 : row);
+      }
+      load8(src + row * C + c0 + c, v);
+      if (MODE == 2) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = bf16_bits_to_f32(f32_to_bf16_bits(act_bf16(act, v[e])));
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tile[kk][c + e] = v[e];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = (tid >> 3) + 32 * i, kc = (tid & 7) * 8;   // r: column of src, kc: first k
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = tile[kc + e][r];
+    store8(out + (int64_t)(c0 + r) * ldk + k0 + kc, v);
+  }
+  if (partial && tid < 64) {
+    float sum = 0.f;
+    for (int kk = 0; kk < 64; ++kk) sum += tile[kk][tid];
+    partial[(int64_t)blockIdx.x * C + c0 + tid] = sum;
+  }
+}
+
+// db[g][c] = sum of the column-sum partials of group g's 64-row blocks, in
+// block order (deterministic). Routed groups write db + g C, the shared expert
+// (g == E) writes dbs.
+__global__ __launch_bounds__(256) void colsum_reduce_kernel(const float* __restrict__ partial,
+                                                            const int32_t* __restrict__ po, int C,
+                                                            int E, float* __restrict__ db,
+                                                            float* __restrict__ dbs) {
+  const int g = blockIdx.y;
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= C) return;
+  const int b0 = po[g] / 64, b1 = po[g + 1] / 64;
+  float s = 0.f;
+  for (int b = b0; b < b1; ++b) s += partial[(int64_t)b * C + c];
+  if (g < E) db[(int64_t)g * C + c] = s;
+  else dbs[c] = s;
+}
+
+// ------------------------------------------------------------------ router weights
+// dW_g[e][c] = sum_t dlogits[t][e] x[t][c]: block (expert group of 8, 256
+// columns, token slice) accumulates 8 x 256 sums over its tokens and writes them
+// to partial[slice][e][c]; gate_wgrad_reduce_kernel adds the slices in order.
+__global__ __launch_bounds__(256) void gate_wgrad_kernel(const bf16* __restrict__ x,
+                                                         const float* __restrict__ dlogits,
+                                                         int64_t T, int d, int E, int slice_len,
+                                                         float* __restrict__ partial) {
+  const int e0 = blockIdx.x * 8;
+  const int c = blockIdx.y * 256 + threadIdx.x;
+  const int64_t t0 = (int64_t)blockIdx.z * slice_len;
+  const int64_t t1 = t0 + slice_len < T ? t0 + slice_len : T;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int64_t t = t0; t < t1; ++t) {
+    const float xv = to_f32(x[t * d + c]);
+    const float* dl = dlogits + t * E + e0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (e0 + e < E) acc[e] = fmaf(dl[e], xv, acc[e]);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if (e0 + e < E) partial[((int64_t)blockIdx.z * E + e0 + e) * d + c] = acc[e];
+}
+
+__global__ __launch_bounds__(256) void gate_wgrad_reduce_kernel(const float* __restrict__ partial,
+                                                                int slices, int64_t n,
+                                                                float* __restrict__ dw) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float s = 0.f;
+  for (int z = 0; z < slices; ++z) s += partial[z * n + i];
+  dw[i] = s;
+}
+
+// db_g[e] = sum_t dlogits[t][e]: one block per expert, a fixed-order tree.
+__global__ __launch_bounds__(256) void gate_bias_grad_kernel(const float* __restrict__ dlogits,
+                                                             int64_t T, int E,
+                                                             float* __restrict__ db) {
+  __shared__ float red[256];
+  const int e = blockIdx.x;
+  float s = 0.f;
+  for (int64_t t = threadIdx.x; t < T; t += 256) s += dlogits[t * E + e];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) db[e] = red[0];
+}
+
+// ------------------------------------------------------------------ dx
+// dx[t][c] = sum_j dXp[assign_row[t, j]][c] (kept choices) + dXp[off[E] + t][c]
+// (shared expert) + sum_e dlogits[t][e] W_g[e][c]. Block: 32 tokens x 256
+// columns; each W_g element is loaded once per block and used for 32 tokens.
+template <typename WT>
+__global__ __launch_bounds__(256) void unpermute_dx_kernel(
+    const bf16* __restrict__ dxp, const int32_t* __restrict__ assign_row,
+    const int32_t* __restrict__ off, const float* __restrict__ dlogits, const WT* __restrict__ wg,
+    int64_t T, int d, int k, int E, int S, int64_t rows_max, bf16* __restrict__ dx) {
+  constexpr int TB = 32;
+  const int c = blockIdx.y * 256 + threadIdx.x;
+  const int64_t t0 = (int64_t)blockIdx.x * TB;
+  float acc[TB];
+#pragma unroll
+  for (int i = 0; i < TB; ++i) acc[i] = 0.f;
+  for (int e = 0; e < E; ++e) {
+    const float w = to_f32(wg[(int64_t)e * d + c]);
+#pragma unroll
+    for (int i = 0; i < TB; ++i)
+      if (t0 + i < T) acc[i] = fmaf(dlogits[(t0 + i) * E + e], w, acc[i]);
+  }
+  const int64_t shared0 = S ? clamp_off(off, E, rows_max) : 0;
+#pragma unroll
+  for (int i = 0; i < TB; ++i) {
+    const int64_t t = t0 + i;
+    if (t >= T) break;
+    float v = acc[i];
+    for (int j = 0; j < k; ++j) {
+      const int r = assign_row[t * k + j];
+      if (r >= 0 && r < rows_max) v += to_f32(dxp[(int64_t)r * d + c]);
+    }
+    if (S && shared0 + t < rows_max) v += to_f32(dxp[(shared0 + t) * d + c]);
+    store1(dx + t * d + c, v);
+  }
+}
+
+// ------------------------------------------------------------------ launchers
+hipError_t launch_act_rows(const moe_config& c, const void* z, const int32_t* off, void* h,
+                           hipStream_t s) {
+  const int G = c.num_experts + c.num_shared_experts;
+  const int64_t n8 = rows_max(c) * c.d_ff / 8;
+  const int64_t blocks = (n8 + 255) / 256 < 4096 ? (n8 + 255) / 256 : 4096;
+  hipLaunchKernelGGL(act_rows_kernel, dim3((unsigned)(blocks > 0 ? blocks : 1)), dim3(256), 0, s,
+                     (const bf16*)z, off, G, rows_max(c), (int)c.d_ff, c.activation, (bf16*)h);
+  return hipGetLastError();
+}
+
+hipError_t launch_backward_misc(const moe_config& c, const BwdLayout& B, const void* x,
+                                const moe_weights& w, const moe_routing& r, const moe_stats* stats,
+                                const moe_saved& sv, const void* dy, float aux_coef, float z_coef,
+                                const moe_grads& gr, char* ws, hipStream_t s, int phase) {
+  const int64_t T = c.tokens, rmax = rows_max(c);
+  const int d = (int)c.d_model, F = (int)c.d_ff, E = c.num_experts, k = c.top_k;
+  const int S = c.num_shared_experts, G = E + S;
+  bf16* dyp = (bf16*)(ws + B.dyp);
+  float* dgate = (float*)(ws + B.dgate);
+  float* dlogits = (float*)(ws + B.dlogits);
+  int32_t* po = (int32_t*)(ws + B.po);
+  int32_t* so = po + (G + 1);
+  const unsigned tb = (unsigned)((T + 3) / 4);
+  if (phase == 0) {
+    // combine and router backward, weight transposes
+    hipLaunchKernelGGL(combine_bwd_kernel, dim3(tb), dim3(256), 0, s, (const bf16*)dy,
+                       (const bf16*)sv.y_perm, r.topk_gate, r.assign_row, r.expert_offsets, T, d, k,
+                       E, S, rmax, dyp, dgate);
+    hipLaunchKernelGGL(router_bwd_kernel, dim3(tb), dim3(256), 0, s, r.logits, r.topk_idx, dgate,
+                       stats->counts_pre, T, E, k, (int)(c.score_fn == MOE_SCORE_SIGMOID), aux_coef,
+                       z_coef, dlogits);
+    hipLaunchKernelGGL(transpose_bf16_kernel, dim3(F / 64, d / 64, E), dim3(256), 0, s,
+                       (const bf16*)w.w2, (bf16*)(ws + B.w2t), d, F);
+    hipLaunchKernelGGL(transpose_bf16_kernel, dim3(d / 64, F / 64, E), dim3(256), 0, s,
+                       (const bf16*)w.w1, (bf16*)(ws + B.w1t), F, d);
+    if (S) {
+      hipLaunchKernelGGL(transpose_bf16_kernel, dim3(F / 64, d / 64, 1), dim3(256), 0, s,
+                         (const bf16*)w.ws2, (bf16*)(ws + B.ws2t), d, F);
+      hipLaunchKernelGGL(transpose_bf16_kernel, dim3(d / 64, F / 64, 1), dim3(256), 0, s,
+                         (const bf16*)w.ws1, (bf16*)(ws + B.ws1t), F, d);
+    }
+    hipLaunchKernelGGL(pad_offsets_kernel, dim3(1), dim3(64), 0, s, r.expert_offsets, G, rmax, po,
+                       so);
+    return hipGetLastError();
+  }
+  // phase 1 (after the dZ and dX GEMMs): transposed row buffers, weight
+  // gradients, bias gradients, router weights, dx
+  const int ldk = (int)B.ldk;
+  const unsigned kb = (unsigned)(B.ldk / 64);
+  const bool bias = c.has_bias;
+  float* p2 = bias ? (float*)(ws + B.colsum2) : nullptr;
+  float* p1 = bias ? (float*)(ws + B.colsum1) : nullptr;
+  hipLaunchKernelGGL((transpose_rows_kernel<0>), dim3(kb, d / 64), dim3(256), 0, s,
+                     (const bf16*)dyp, (const int32_t*)nullptr, (const int32_t*)so, po, G, rmax,
+                     d, ldk, c.activation, (bf16*)(ws + B.dypT), p2);
+  hipLaunchKernelGGL((transpose_rows_kernel<2>), dim3(kb, F / 64), dim3(256), 0, s,
+                     (const bf16*)sv.z, (const int32_t*)nullptr, (const int32_t*)so, po, G, rmax,
+                     F, ldk, c.activation, (bf16*)(ws + B.hT), (float*)nullptr);
+  hipLaunchKernelGGL((transpose_rows_kernel<0>), dim3(kb, F / 64), dim3(256), 0, s,
+                     (const bf16*)(ws + B.dz), (const int32_t*)nullptr, (const int32_t*)so, po, G,
+                     rmax, F, ldk, c.activation, (bf16*)(ws + B.dzT), p1);
+  hipLaunchKernelGGL((transpose_rows_kernel<1>), dim3(kb, d / 64), dim3(256), 0, s, (const bf16*)x,
+                     r.row_token, (const int32_t*)so, po, G, T, d, ldk, c.activation,
+                     (bf16*)(ws + B.xT), (float*)nullptr);
+  hipError_t e = launch_wgrad(ws + B.dypT, ws + B.hT, po, G, E, d, F, ldk, gr.dw2, gr.dws2, s);
+  if (e != hipSuccess) return e;
+  e = launch_wgrad(ws + B.dzT, ws + B.xT, po, G, E, F, d, ldk, gr.dw1, gr.dws1, s);
+  if (e != hipSuccess) return e;
+  if (bias) {
+    hipLaunchKernelGGL(colsum_reduce_kernel, dim3((d + 255) / 256, G), dim3(256), 0, s,
+                       (const float*)p2, (const int32_t*)po, d, E, gr.db2, gr.dbs2);
+    hipLaunchKernelGGL(colsum_reduce_kernel, dim3((F + 255) / 256, G), dim3(256), 0, s,
+                       (const float*)p1, (const int32_t*)po, F, E, gr.db1, gr.dbs1);
+  }
+  hipLaunchKernelGGL(gate_wgrad_kernel, dim3((E + 7) / 8, d / 256, B.gate_slices), dim3(256), 0, s,
+                     (const bf16*)x, (const float*)dlogits, T, d, E, (int)B.gate_slice_len,
+                     (float*)(ws + B.gate_partial));
+  const int64_t n = (int64_t)E * d;
+  hipLaunchKernelGGL(gate_wgrad_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                     (const float*)(ws + B.gate_partial), (int)B.gate_slices, n, gr.dw_gate);
+  if (c.has_gate_bias)
+    hipLaunchKernelGGL(gate_bias_grad_kernel, dim3(E), dim3(256), 0, s, (const float*)dlogits, T, E,
+                       gr.db_gate);
+  const dim3 ug((unsigned)((T + 31) / 32), (unsigned)(d / 256));
+  if (c.router_dtype == MOE_BF16)
+    hipLaunchKernelGGL((unpermute_dx_kernel<bf16>), ug, dim3(256), 0, s, (const bf16*)(ws + B.dxp),
+                       r.assign_row, r.expert_offsets, (const float*)dlogits, (const bf16*)w.w_gate,
+                       T, d, k, E, S, rmax, (bf16*)gr.dx);
+  else
+    hipLaunchKernelGGL((unpermute_dx_kernel<float>), ug, dim3(256), 0, s, (const bf16*)(ws + B.dxp),
+                       r.assign_row, r.expert_offsets, (const float*)dlogits, (const float*)w.w_gate,
+                       T, d, k, E, S, rmax, (bf16*)gr.dx);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -16,7 +16,10 @@
 
 namespace moe {
 
-enum { EPI_GELU = 0, EPI_RELU = 1, EPI_SWIGLU = 2, EPI_NONE = 3, EPI_PARTIAL = 4 };
+// EPI_DGELU / EPI_DRELU (backward): C = acc * act'(z) with z read from Zin, the
+// saved pre-activation laid out like C.
+enum { EPI_GELU = 0, EPI_RELU = 1, EPI_SWIGLU = 2, EPI_NONE = 3, EPI_PARTIAL = 4, EPI_DGELU = 5,
+       EPI_DRELU = 6 };
 
 template <int EPI>
 __device__ __forceinline__ float epilogue(float z1, float z3) {
@@ -155,24 +158,6 @@ __device__ __forceinline__ void tile_lookup(const TileSpace& ts, int mt, int BM,
   nrows_out = __shfl(nrows, owner, 64);
 }
 
-// GELU(x) = x Phi(x) = max(x, 0) - a Phi(-a) with a = |x| clamped to 6 (where
-// a Phi(-a) < 1e-8). Phi(-a) = 2^P(a), P a degree-7 polynomial fitted to
-// log2 Phi(-a) on [0, 6] by least squares (csrc/gelu_fit.py prints the fit and
-// its error): seven FMAs and one hardware exp2, max absolute error 1e-6 and
-// relative error 1e-5 of the GELU. Used where the result is rounded to bf16
-// (relative step 2^-8).
-__device__ __forceinline__ float gelu_poly(float x) {
-  const float a = fminf(fabsf(x), 6.0f);
-  float p = fmaf(-1.9449223600531695e-06f, a, 6.386057066265494e-05f);
-  p = fmaf(p, a, -0.0009488713694736362f);
-  p = fmaf(p, a, 0.008582375012338161f);
-  p = fmaf(p, a, -0.0541183240711689f);
-  p = fmaf(p, a, -0.4582974314689636f);
-  p = fmaf(p, a, -1.1513246297836304f);
-  p = fmaf(p, a, -0.9999869465827942f);
-  return fmaf(-a, __builtin_amdgcn_exp2f(p), fmaxf(x, 0.f));
-}
-
 __device__ __forceinline__ float silu_fast(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
 }
@@ -182,6 +167,8 @@ __device__ __forceinline__ float epilogue_bf16(float z1, float z3) {
   if (EPI == EPI_GELU) return gelu_poly(z1);
   if (EPI == EPI_RELU) return fmaxf(z1, 0.f);
   if (EPI == EPI_SWIGLU) return silu_fast(z1) * z3;
+  if (EPI == EPI_DGELU) return z1 * gelu_grad_poly(z3);
+  if (EPI == EPI_DRELU) return z3 > 0.f ? z1 : 0.f;
   return z1;
 }
 
@@ -212,8 +199,9 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
     const float* __restrict__ bias, const bf16* __restrict__ Ws, const bf16* __restrict__ Ws3,
     const float* __restrict__ bias_s, int E, int G, const int32_t* __restrict__ offsets,
     int rows_max, void* __restrict__ Cv, int N, int K, int part, const int32_t* __restrict__ arows,
-    int kparts) {
+    int kparts, const bf16* __restrict__ Zin) {
   constexpr bool GATED = EPI == EPI_SWIGLU;
+  constexpr bool DACT = EPI == EPI_DGELU || EPI == EPI_DRELU;
   constexpr int BM = 128, BK = 64, CH = BK / 8;   // 8 chunks of 16 B per LDS row
   constexpr int NB = GATED ? 2 : 1;
   constexpr int BN = GATED ? 64 : 128;            // columns per B operand
@@ -469,6 +457,22 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
     for (int qd = 0; qd < 4; ++qd)
       bv[j][qd] = HAS_BIAS ? *reinterpret_cast<const float4*>(cur_bg + cur_n0 + wn * WN + j * 32 + qd * 8 + fk * 4)
                            : make_float4(0.f, 0.f, 0.f, 0.f);
+  // backward epilogues: the 4 saved pre-activations of each accumulator quad
+  uint2 zv[DACT ? TM : 1][DACT ? TN : 1][4];
+  if constexpr (DACT) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int m = wm * 64 + i * 32 + fr;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd)
+          zv[i][j][qd] = m < cur_nrows
+                             ? *reinterpret_cast<const uint2*>(Zin + (int64_t)(cur_row0 + m) * N + cur_n0 +
+                                                               wn * WN + j * 32 + qd * 8 + fk * 4)
+                             : make_uint2(0u, 0u);
+    }
+  }
   __syncthreads();   // every wave is done reading the operand stages
   // bf16 tile staged as BM rows of CQ chunks; chunk q of row m at q ^ swz(m)
   uint2* st8 = reinterpret_cast<uint2*>(smem);
@@ -484,9 +488,15 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
         const float z[4] = {acc[i + 2 * j][qd * 4 + 0] + bq.x, acc[i + 2 * j][qd * 4 + 1] + bq.y,
                             acc[i + 2 * j][qd * 4 + 2] + bq.z, acc[i + 2 * j][qd * 4 + 3] + bq.w};
         float v[4];
+        float zs[4] = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (DACT) {
+          const uint2 u = zv[i][j][qd];
+          zs[0] = bf16_bits_to_f32(u.x & 0xffffu); zs[1] = bf16_bits_to_f32(u.x >> 16);
+          zs[2] = bf16_bits_to_f32(u.y & 0xffffu); zs[3] = bf16_bits_to_f32(u.y >> 16);
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          v[e] = epilogue_bf16<EPI>(z[e], GATED ? acc[i + 2][qd * 4 + e] : 0.f);
+          v[e] = epilogue_bf16<EPI>(z[e], GATED ? acc[i + 2][qd * 4 + e] : zs[e]);
         uint2 u;
         u.x = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
         u.y = (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
@@ -512,6 +522,111 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
   for (int i = 0; i < 8; ++i) MOE_W(r0, 0, i);
   __syncthreads();
   it = itn;
+  }
+}
+
+// Weight-gradient GEMM with a ragged K range per group (backward pass): for
+// group g,
+//   C_g[m, n] = sum over k in [po[g], po[g + 1]) of A[m, k] B[n, k],
+// A [M][ldk] and B [N][ldk] bf16 hold the expert-sorted row buffers transposed,
+// each group's rows padded with zeros to a multiple of 128 columns (at least
+// 128), so every K range is a whole, even number of 64-deep steps. C_g is
+// float32 [M][N] at C + g M N for a routed expert (g < E) and Cs for the shared
+// expert (g == E). Same 128 x 128 tile, LDS layout, fragment order and two-step
+// register pipeline as gemm_bf16_kernel (its macros), one tile per block; the
+// XCD-aware order keeps a group's tiles on one XCD in groups of 8 M tiles.
+// Requires M, N multiples of 128 and 256 ldk < 2^31 (checked by the host).
+__global__ __launch_bounds__(256, 2) void gemm_wgrad_kernel(
+    const bf16* __restrict__ A, const bf16* __restrict__ B, const int32_t* __restrict__ po, int G,
+    int E, int M, int N, int ldk, float* __restrict__ C, float* __restrict__ Cs) {
+  constexpr int BM = 128, BN = 128, BK = 64, CH = BK / 8;
+  constexpr int WN = BN / 2, TM = 2, TN = WN / 32;
+  constexpr int ROWS = BM + BN, STAGE = ROWS * CH, GROUP_M = 8;
+  __shared__ u32x4 smem[2 * STAGE];
+  const int mtn = M / BM, ntn = N / BN, per = mtn * ntn;
+  const int tiles = G * per;
+  const int b = blockIdx.x;
+  if (b >= tiles) return;
+  const int t8 = tiles & ~7;
+  const int t = b < t8 ? (b & 7) * (t8 >> 3) + (b >> 3) : b;
+  const int g = t / per;
+  const int in = t - g * per;
+  const int grp = in / (GROUP_M * ntn);
+  const int first_m = grp * GROUP_M;
+  const int gm = min(mtn - first_m, GROUP_M);
+  const int in2 = in - grp * GROUP_M * ntn;
+  const int row0 = (first_m + in2 % gm) * BM;
+  const int n0 = (in2 / gm) * BN;
+  const int kbase = po[g] / BK;
+  const int len = (po[g + 1] - po[g]) / BK;   // even, >= 2
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int fr = lane & 31;
+  const int fk = lane >> 5;
+  const int lr = tid >> 3;
+  const int lc = tid & 7;
+  const int wslot = lr * CH + (lc ^ ((tid >> 4) & 7));
+  const int rsw = (fr >> 1) & 7;
+  const bf16* a0 = A + lc * 8;
+  const char* ar0 = reinterpret_cast<const char*>(a0 + (int64_t)(row0 + lr) * ldk);
+  const char* ar1 = reinterpret_cast<const char*>(a0 + (int64_t)(row0 + lr + 32) * ldk);
+  const char* ar2 = reinterpret_cast<const char*>(a0 + (int64_t)(row0 + lr + 64) * ldk);
+  const char* ar3 = reinterpret_cast<const char*>(a0 + (int64_t)(row0 + lr + 96) * ldk);
+  const char* b_s = reinterpret_cast<const char*>(B + (int64_t)n0 * ldk);
+  const char* b3_s = b_s;
+  const uint32_t bo0 = (uint32_t)(lr * ldk + lc * 8) * 2u;
+  const uint32_t bo1 = bo0 + (uint32_t)(64 * ldk);
+  const uint32_t bo2 = bo0 + (uint32_t)(128 * ldk);
+  const uint32_t bo3 = bo0 + (uint32_t)(192 * ldk);
+  int fbase[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    const int row = f < 2 ? wm * 64 + f * 32 + fr : BM + wn * WN + (f - 2) * 32 + fr;
+    fbase[f] = row * CH;
+  }
+  constexpr int kRO[4] = {0, 2, 1, 3};
+  int cidx[4];
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4) cidx[s4] = (s4 * 2 + fk) ^ rsw;
+  struct Regs { u32x4 v0, v1, v2, v3, v4, v5, v6, v7; };
+  Regs r0, r1;
+  bf16x8 fr0[4], fr1[4];
+  f32x16 acc[4];
+#pragma unroll
+  for (int k4 = 0; k4 < 4; ++k4)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[k4][r] = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) MOE_G(r0, 0, i);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) MOE_G(r1, 1, i);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) MOE_W(r0, 0, i);
+  __syncthreads();
+  for (int kt = 0; kt < len - 2; kt += 2) {
+    MOE_STEP(0, r0, kt + 2, true, r1, true);
+    __syncthreads();
+    MOE_STEP(1, r1, kt + 3, true, r0, true);
+    __syncthreads();
+  }
+  MOE_STEP(0, r0, 0, false, r1, true);
+  __syncthreads();
+  MOE_STEP(1, r1, 0, false, r0, false);
+  float* __restrict__ Cg = g < E ? C + (int64_t)g * M * N : Cs;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int m = wm * 64 + i * 32 + fr;
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        const f32x4 v = {acc[i + 2 * j][qd * 4 + 0], acc[i + 2 * j][qd * 4 + 1],
+                         acc[i + 2 * j][qd * 4 + 2], acc[i + 2 * j][qd * 4 + 3]};
+        *reinterpret_cast<f32x4*>(Cg + (int64_t)(row0 + m) * N + n0 + wn * WN + j * 32 + qd * 8 +
+                                  fk * 4) = v;
+      }
   }
 #undef MOE_SB
 #undef MOE_G
@@ -844,7 +959,8 @@ template <typename ET, int EPI, bool HB>
 static hipError_t gemm_launch(const moe_config& c, const ET* A, const void* W, const void* W3,
                               const float* bias, const void* Ws, const void* Ws3,
                               const float* bias_s, const int32_t* offsets, ET* C, int N, int K,
-                              hipStream_t s, const int32_t* arows = nullptr) {
+                              hipStream_t s, const int32_t* arows = nullptr,
+                              const bf16* zin = nullptr) {
   const int E = c.num_experts, G = c.num_experts + c.num_shared_experts;
   const int64_t rows = rows_max(c);
   if constexpr (sizeof(ET) == 2) {
@@ -859,28 +975,30 @@ static hipError_t gemm_launch(const moe_config& c, const ET* A, const void* W, c
     // gathered A rows (arows) are addressed with 32-bit offsets from the start
     // of x, which the 256 x 256 kernel's buffer loads need below 4 GiB
     const int64_t a_bytes = arows ? c.tokens * (int64_t)K * 2 : 0;
+    // (the backward epilogues EPI_DGELU / EPI_DRELU exist in the 128 x 128 kernel only)
     const bool big = rows >= kGemmBigBM && (EPI == EPI_NONE || K >= 2048) &&
-                     a_bytes < ((int64_t)1 << 32);
+                     EPI != EPI_DGELU && EPI != EPI_DRELU && a_bytes < ((int64_t)1 << 32);
     if (big) {
       // full 256-row tiles of each group, then the rows left over (< 256 per
       // group) in 128-row tiles; both grids are bounds, surplus blocks exit
       const unsigned big_tiles = (unsigned)(rows / kGemmBigBM) * (unsigned)(N / BNB);
-      hipLaunchKernelGGL((gemm_bf16_big_kernel<EPI, HB>), dim3(big_tiles), dim3(256), 0, s, A,
-                         (const bf16*)W, (const bf16*)W3, bias, (const bf16*)Ws, (const bf16*)Ws3,
-                         bias_s, E, G, offsets, (int)rows, C, N, K, arows, (uint32_t)a_bytes);
+      if constexpr (EPI != EPI_DGELU && EPI != EPI_DRELU)
+        hipLaunchKernelGGL((gemm_bf16_big_kernel<EPI, HB>), dim3(big_tiles), dim3(256), 0, s, A,
+                           (const bf16*)W, (const bf16*)W3, bias, (const bf16*)Ws, (const bf16*)Ws3,
+                           bias_s, E, G, offsets, (int)rows, C, N, K, arows, (uint32_t)a_bytes);
       // each group leaves at most 255 rows, i.e. at most 2 tiles, and the
       // tiles number at most ceil(rows / 128) + G
       const int64_t rest = (rows + 127) / 128 + G < 2 * G ? (rows + 127) / 128 + G : 2 * G;
       const int64_t rgrid = rest * (N / BN) < slots ? rest * (N / BN) : slots;
       hipLaunchKernelGGL((gemm_bf16_kernel<EPI, HB>), dim3((unsigned)rgrid), dim3(256), 0, s, A,
                          (const bf16*)W, (const bf16*)W3, bias, (const bf16*)Ws, (const bf16*)Ws3,
-                         bias_s, E, G, offsets, (int)rows, C, N, K, 2, arows, 1);
+                         bias_s, E, G, offsets, (int)rows, C, N, K, 2, arows, 1, zin);
     } else {
       const int64_t tiles = ((rows + 127) / 128 + G) * (N / BN);
       const int64_t grid = tiles < slots ? tiles : slots;
       hipLaunchKernelGGL((gemm_bf16_kernel<EPI, HB>), dim3((unsigned)grid), dim3(256), 0, s, A,
                          (const bf16*)W, (const bf16*)W3, bias, (const bf16*)Ws, (const bf16*)Ws3,
-                         bias_s, E, G, offsets, (int)rows, C, N, K, 0, arows, 1);
+                         bias_s, E, G, offsets, (int)rows, C, N, K, 0, arows, 1, zin);
     }
   } else {
     const unsigned mtiles = (unsigned)((rows + kGemmBM - 1) / kGemmBM) + G;
@@ -942,7 +1060,7 @@ hipError_t launch_router_gemm(const moe_config& c, const void* x, const void* w_
                      (const bf16*)x, (const bf16*)w_gate, (const bf16*)nullptr, (const float*)nullptr,
                      (const bf16*)nullptr, (const bf16*)nullptr, (const float*)nullptr, 1, 1,
                      (const int32_t*)nullptr, (int)T, (void*)partials, E, K, 0,
-                     (const int32_t*)nullptr, kp);
+                     (const int32_t*)nullptr, kp, (const bf16*)nullptr);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int64_t n4 = T * E / 4;
@@ -994,6 +1112,47 @@ hipError_t launch_expert_down(const moe_config& c, const void* h, const int32_t*
              : gemm_launch<float, EPI_NONE, false>(c, (const float*)h, w.w2, nullptr, w.b2, w.ws2,
                                                    nullptr, w.bs2, offsets, (float*)y_perm, N, K,
                                                    s);
+}
+
+// ------------------------------------------------------------------ backward
+hipError_t launch_backward_dz(const moe_config& c, const void* dyp, const int32_t* offsets,
+                              const void* w2t, const void* ws2t, const void* z, void* dz,
+                              hipStream_t s) {
+  const int N = (int)c.d_ff, K = (int)c.d_model;
+  if (c.activation == MOE_ACT_GELU)
+    return gemm_launch<bf16, EPI_DGELU, false>(c, (const bf16*)dyp, w2t, nullptr, nullptr, ws2t,
+                                               nullptr, nullptr, offsets, (bf16*)dz, N, K, s,
+                                               nullptr, (const bf16*)z);
+  return gemm_launch<bf16, EPI_DRELU, false>(c, (const bf16*)dyp, w2t, nullptr, nullptr, ws2t,
+                                             nullptr, nullptr, offsets, (bf16*)dz, N, K, s, nullptr,
+                                             (const bf16*)z);
+}
+
+hipError_t launch_expert_up_linear(const moe_config& c, const void* a, const int32_t* offsets,
+                                   const ExpertWeights& w, void* z, hipStream_t s,
+                                   const int32_t* arows) {
+  const int N = (int)c.d_ff, K = (int)c.d_model;
+  return c.has_bias
+             ? gemm_launch<bf16, EPI_NONE, true>(c, (const bf16*)a, w.w1, nullptr, w.b1, w.ws1,
+                                                 nullptr, w.bs1, offsets, (bf16*)z, N, K, s, arows)
+             : gemm_launch<bf16, EPI_NONE, false>(c, (const bf16*)a, w.w1, nullptr, w.b1, w.ws1,
+                                                  nullptr, w.bs1, offsets, (bf16*)z, N, K, s, arows);
+}
+
+hipError_t launch_backward_dx(const moe_config& c, const void* dz, const int32_t* offsets,
+                              const void* w1t, const void* ws1t, void* dxp, hipStream_t s) {
+  const int N = (int)c.d_model, K = (int)c.d_ff;
+  return gemm_launch<bf16, EPI_NONE, false>(c, (const bf16*)dz, w1t, nullptr, nullptr, ws1t, nullptr,
+                                            nullptr, offsets, (bf16*)dxp, N, K, s);
+}
+
+hipError_t launch_wgrad(const void* a, const void* b, const int32_t* po, int G, int E, int M, int N,
+                        int ldk, float* C, float* Cs, hipStream_t s) {
+  const int64_t tiles = (int64_t)G * (M / 128) * (N / 128);
+  if (tiles <= 0) return hipSuccess;
+  hipLaunchKernelGGL(gemm_wgrad_kernel, dim3((unsigned)tiles), dim3(256), 0, s, (const bf16*)a,
+                     (const bf16*)b, po, G, E, M, N, ldk, C, Cs);
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -45,6 +45,48 @@ WsLayout workspace_layout(const moe_config& c) {
   return L;
 }
 
+BwdLayout backward_layout(const moe_config& c) {
+  BwdLayout B;
+  memset(&B, 0, sizeof(B));
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align_up(bytes);
+    return o;
+  };
+  const int64_t T = c.tokens, d = c.d_model, F = c.d_ff;
+  const int E = c.num_experts, k = c.top_k, S = c.num_shared_experts, G = E + S;
+  const int64_t rmax = rows_max(c);
+  B.ldk = (rmax + 128 * (int64_t)G + 127) / 128 * 128;
+  B.dyp = take((size_t)(rmax * d * 2));
+  B.dgate = take((size_t)(T * k * 4));
+  B.dlogits = take((size_t)(T * E * 4));
+  B.w1t = take((size_t)E * d * F * 2);
+  B.w2t = take((size_t)E * F * d * 2);
+  B.ws1t = take((size_t)S * d * F * 2);
+  B.ws2t = take((size_t)S * F * d * 2);
+  B.dz = take((size_t)(rmax * F * 2));
+  B.dxp = take((size_t)(rmax * d * 2));
+  B.po = take((size_t)(G + 1) * 8);   // po [G + 1], then the sanitized offsets [G + 1]
+  B.dypT = take((size_t)(d * B.ldk * 2));
+  B.hT = take((size_t)(F * B.ldk * 2));
+  B.dzT = take((size_t)(F * B.ldk * 2));
+  B.xT = take((size_t)(d * B.ldk * 2));
+  B.colsum1 = take(c.has_bias ? (size_t)(B.ldk / 64 * F * 4) : 0);
+  B.colsum2 = take(c.has_bias ? (size_t)(B.ldk / 64 * d * 4) : 0);
+  // router weight gradient: about 512 blocks of (8 experts x 256 columns x a token slice)
+  const int64_t xy = (int64_t)((E + 7) / 8) * (d / 256 > 0 ? d / 256 : 1);
+  int64_t slices = 512 / xy;
+  slices = slices < 1 ? 1 : (slices > 128 ? 128 : slices);
+  if (slices > T) slices = T > 0 ? T : 1;
+  const int64_t slice_len = T > 0 ? (T + slices - 1) / slices : 1;
+  B.gate_slice_len = (int)slice_len;
+  B.gate_slices = (int)(T > 0 ? (T + slice_len - 1) / slice_len : 1);
+  B.gate_partial = take((size_t)B.gate_slices * E * d * 4);
+  B.total = off;
+  return B;
+}
+
 static int validate(const moe_config* c) {
   if (!c) return MOE_ERR_INVALID_ARG;
   if (c->reserved != 0) return MOE_ERR_INVALID_ARG;
@@ -93,6 +135,18 @@ static int64_t capacity_exact(const moe_config& c) {
 }
 
 static int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// Layers the training forward and the backward run: bf16 activations, GELU or
+// ReLU experts, and transposed row buffers short enough for the 32-bit
+// operand offsets of the weight-gradient GEMM (256 ldk < 2^31).
+static int validate_train(const moe_config* c) {
+  const int v = validate(c);
+  if (v != MOE_OK) return v;
+  if (c->act_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (c->activation != MOE_ACT_GELU && c->activation != MOE_ACT_RELU) return MOE_ERR_UNSUPPORTED;
+  if (backward_layout(*c).ldk >= ((int64_t)1 << 23)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
 
 }  // namespace moe
 
@@ -267,6 +321,87 @@ int moe_forward(const moe_config* cfg, const void* x, const moe_weights* w, void
   if (e != hipSuccess) return MOE_ERR_HIP;
   e = launch_combine(*cfg, y_perm, r->expert_offsets, r->assign_row, r->topk_gate, y, s);
   return hip_status(e);
+}
+
+int moe_forward_train(const moe_config* cfg, const void* x, const moe_weights* w, void* y,
+                      const moe_routing* r, moe_stats* stats, const moe_saved* saved,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  const int v = validate_train(cfg);
+  if (v != MOE_OK) return v;
+  if (cfg->tokens == 0) return MOE_OK;
+  if (!x || !w || !y || !r || !stats || !saved || !workspace) return MOE_ERR_INVALID_ARG;
+  if (!saved->z || !saved->y_perm) return MOE_ERR_INVALID_ARG;
+  if (!w->w_gate || (cfg->has_gate_bias && !w->b_gate)) return MOE_ERR_INVALID_ARG;
+  if (!r->logits || !r->topk_idx || !r->topk_gate || !r->expert_offsets || !r->row_token ||
+      !r->assign_row)
+    return MOE_ERR_INVALID_ARG;
+  const int wv = check_weights(cfg, w->w1, w->w3, w->b1, w->w2, w->b2, w->ws1, w->ws3, w->bs1,
+                               w->ws2, w->bs2);
+  if (wv != MOE_OK) return wv;
+  const WsLayout L = workspace_layout(*cfg);
+  if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
+  char* ws = (char*)workspace;
+  const hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_route(*cfg, L, x, w->w_gate, w->b_gate, w->e_bias, r->logits, r->topk_idx,
+                              r->topk_gate, stats, ws, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = launch_permute(*cfg, L, capacity_exact(*cfg), r->topk_idx, x, r->expert_offsets,
+                     r->row_token, r->assign_row, nullptr, stats, ws, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  const ExpertWeights ew{w->w1, w->w3, w->w2, w->b1, w->b2, w->ws1, w->ws3, w->ws2, w->bs1, w->bs2};
+  void* h = ws + L.h;
+  e = launch_expert_up_linear(*cfg, x, r->expert_offsets, ew, saved->z, s, r->row_token);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = launch_act_rows(*cfg, saved->z, r->expert_offsets, h, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = launch_expert_down(*cfg, h, r->expert_offsets, ew, saved->y_perm, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = launch_combine(*cfg, saved->y_perm, r->expert_offsets, r->assign_row, r->topk_gate, y, s);
+  return hip_status(e);
+}
+
+int moe_backward_workspace_size(const moe_config* cfg, size_t* bytes_out) {
+  const int v = validate_train(cfg);
+  if (v != MOE_OK) return v;
+  if (!bytes_out) return MOE_ERR_INVALID_ARG;
+  *bytes_out = backward_layout(*cfg).total;
+  return MOE_OK;
+}
+
+int moe_backward(const moe_config* cfg, const void* x, const moe_weights* w, const moe_routing* r,
+                 const moe_stats* stats, const moe_saved* saved, const void* dy, float aux_coef,
+                 float z_coef, const moe_grads* g, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  const int v = validate_train(cfg);
+  if (v != MOE_OK) return v;
+  if (cfg->tokens == 0) return MOE_OK;
+  if (!x || !w || !r || !stats || !saved || !dy || !g || !workspace) return MOE_ERR_INVALID_ARG;
+  if (!saved->z || !saved->y_perm) return MOE_ERR_INVALID_ARG;
+  if (!w->w_gate || !w->w1 || !w->w2) return MOE_ERR_INVALID_ARG;
+  if (!r->logits || !r->topk_idx || !r->topk_gate || !r->expert_offsets || !r->row_token ||
+      !r->assign_row)
+    return MOE_ERR_INVALID_ARG;
+  const bool shared = cfg->num_shared_experts == 1, bias = cfg->has_bias != 0;
+  if (shared && (!w->ws1 || !w->ws2)) return MOE_ERR_INVALID_ARG;
+  if (!g->dx || !g->dw_gate || !g->dw1 || !g->dw2) return MOE_ERR_INVALID_ARG;
+  if (cfg->has_gate_bias && !g->db_gate) return MOE_ERR_INVALID_ARG;
+  if (bias && (!g->db1 || !g->db2)) return MOE_ERR_INVALID_ARG;
+  if (shared && (!g->dws1 || !g->dws2 || (bias && (!g->dbs1 || !g->dbs2))))
+    return MOE_ERR_INVALID_ARG;
+  const BwdLayout B = backward_layout(*cfg);
+  if (workspace_bytes < B.total) return MOE_ERR_WORKSPACE;
+  char* ws = (char*)workspace;
+  const hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_backward_misc(*cfg, B, x, *w, *r, stats, *saved, dy, aux_coef, z_coef, *g,
+                                      ws, s, 0);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = launch_backward_dz(*cfg, ws + B.dyp, r->expert_offsets, ws + B.w2t, ws + B.ws2t, saved->z,
+                         ws + B.dz, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = launch_backward_dx(*cfg, ws + B.dz, r->expert_offsets, ws + B.w1t, ws + B.ws1t, ws + B.dxp, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(launch_backward_misc(*cfg, B, x, *w, *r, stats, *saved, dy, aux_coef, z_coef,
+                                         *g, ws, s, 1));
 }
 
 }  // extern "C"

@@ -79,6 +79,39 @@ __device__ __forceinline__ void store1(bf16* p, float v) {
 __device__ __forceinline__ float gelu_erf(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
+// Phi(-a), the standard normal tail, for a in [0, 6] as 2^P(a): P is a degree-7
+// polynomial fitted to log2 Phi(-a) on [0, 6] by least squares (csrc/gelu_fit.py
+// prints the fit and its error). Seven FMAs and one hardware exp2.
+__device__ __forceinline__ float phi_neg_poly(float a) {
+  float p = fmaf(-1.9449223600531695e-06f, a, 6.386057066265494e-05f);
+  p = fmaf(p, a, -0.0009488713694736362f);
+  p = fmaf(p, a, 0.008582375012338161f);
+  p = fmaf(p, a, -0.0541183240711689f);
+  p = fmaf(p, a, -0.4582974314689636f);
+  p = fmaf(p, a, -1.1513246297836304f);
+  p = fmaf(p, a, -0.9999869465827942f);
+  return __builtin_amdgcn_exp2f(p);
+}
+
+// GELU(x) = x Phi(x) = max(x, 0) - a Phi(-a) with a = |x| clamped to 6 (where
+// a Phi(-a) < 1e-8): max absolute error 1e-6 and relative error 1e-5 of the
+// GELU. Used where the result is rounded to bf16 (relative step 2^-8).
+__device__ __forceinline__ float gelu_poly(float x) {
+  const float a = fminf(fabsf(x), 6.0f);
+  return fmaf(-a, phi_neg_poly(a), fmaxf(x, 0.f));
+}
+
+// d/dx GELU(x) = Phi(x) + x phi(x), with Phi from the same fit (Phi(x) =
+// 1 - Phi(-x) for x >= 0) and phi(x) = 2^(-x^2 log2(e) / 2) / sqrt(2 pi).
+// Absolute error below 1e-5.
+__device__ __forceinline__ float gelu_grad_poly(float x) {
+  const float a = fminf(fabsf(x), 6.0f);
+  const float q = phi_neg_poly(a);
+  const float Phi = x >= 0.f ? 1.0f - q : q;
+  const float dens = 0.3989422804014327f * __builtin_amdgcn_exp2f(-0.7213475204444817f * x * x);
+  return fmaf(x, dens, Phi);
+}
+
 // ------------------------------------------------------------------ workspace
 struct WsLayout {
   size_t logits;          // float [T][E] (when the caller does not keep them)
@@ -142,5 +175,44 @@ hipError_t launch_expert_down(const moe_config& c, const void* h, const int32_t*
 hipError_t launch_combine(const moe_config& c, const void* y_perm, const int32_t* expert_offsets,
                           const int32_t* assign_row, const float* topk_gate, void* y,
                           hipStream_t stream);
+
+// ------------------------------------------------------------------ backward
+// Workspace of moe_backward (byte offsets). ldk is the row length of the
+// transposed, group-padded row buffers (each group's rows rounded up to a
+// multiple of 128, at least 128).
+struct BwdLayout {
+  size_t dyp, dgate, dlogits, w1t, w2t, ws1t, ws2t, dz, dxp, po;   // po: padded then sanitized offsets
+  size_t dypT, hT, dzT, xT, colsum1, colsum2, gate_partial, total;
+  int64_t ldk;
+  int gate_slices, gate_slice_len;
+};
+BwdLayout backward_layout(const moe_config& c);
+
+// Training forward: z = a W1^T + b1 per group (no activation), then h = act(z).
+hipError_t launch_expert_up_linear(const moe_config& c, const void* a, const int32_t* expert_offsets,
+                                   const ExpertWeights& w, void* z, hipStream_t stream,
+                                   const int32_t* arows);
+hipError_t launch_act_rows(const moe_config& c, const void* z, const int32_t* expert_offsets,
+                           void* h, hipStream_t stream);
+// The non-GEMM steps of the backward: phase 0 (combine and router backward,
+// weight transposes, padded offsets) before the dZ / dX GEMMs, phase 1 (row
+// transposes, weight, bias and router gradients, dx) after them.
+hipError_t launch_backward_misc(const moe_config& c, const BwdLayout& B, const void* x,
+                                const moe_weights& w, const moe_routing& r, const moe_stats* stats,
+                                const moe_saved& sv, const void* dy, float aux_coef, float z_coef,
+                                const moe_grads& gr, char* ws, hipStream_t stream, int phase);
+
+// dZ = (dYp W2) * act'(z) per group: dYp [rows][d], w2t [E][F][d] (W2 transposed),
+// ws2t [F][d] (shared expert), z and dZ [rows][F] bf16; GELU or ReLU.
+hipError_t launch_backward_dz(const moe_config& c, const void* dyp, const int32_t* expert_offsets,
+                              const void* w2t, const void* ws2t, const void* z, void* dz,
+                              hipStream_t stream);
+// dXp = dZ W1 per group: w1t [E][d][F] (W1 transposed), ws1t [d][F]; dXp [rows][d] bf16.
+hipError_t launch_backward_dx(const moe_config& c, const void* dz, const int32_t* expert_offsets,
+                              const void* w1t, const void* ws1t, void* dxp, hipStream_t stream);
+// Ragged-K grouped weight gradient C_g = A[:, po[g]:po[g+1]] B[:, po[g]:po[g+1]]^T,
+// A [M][ldk], B [N][ldk] bf16; C float32 [E][M][N], Cs [M][N] for group E.
+hipError_t launch_wgrad(const void* a, const void* b, const int32_t* po, int G, int E, int M, int N,
+                        int ldk, float* C, float* Cs, hipStream_t stream);
 
 }  // namespace moe

@@ -27,6 +27,10 @@ class ExpertView:
     def __len__(self):
         return self.t.shape[0]
 
+    @property
+    def shape(self):
+        return tuple(self.t.shape)
+
 
 def np64(t):
     return None if t is None else t.detach().to("cpu", torch.float64).numpy()

@@ -150,3 +150,54 @@ def test_zero_tokens_is_a_noop():
     lib = A.lib()
     cfg = _base(tokens=0)
     assert lib.moe_forward(ctypes.byref(cfg), None, None, None, None, None, None, 0, None) == A.MOE_OK
+
+
+def test_training_structs_match_header(tmp_path):
+    prog = tmp_path / "tsizes.c"
+    prog.write_text('#include <stdio.h>\n#include "moe.h"\n'
+                    'int main(void){printf("%zu %zu\\n", sizeof(moe_saved), sizeof(moe_grads));'
+                    'return 0;}\n')
+    exe = tmp_path / "tsizes"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), str(prog), "-o", str(exe)],
+                   check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    assert got == [ctypes.sizeof(A.MoeSaved), ctypes.sizeof(A.MoeGrads)]
+
+
+def test_training_entry_points_validate_before_any_launch():
+    lib = A.lib()
+    cfg = _base()
+    n = ctypes.c_size_t(0)
+    assert lib.moe_backward_workspace_size(ctypes.byref(cfg), ctypes.byref(n)) == A.MOE_OK
+    assert n.value > 0
+    assert lib.moe_backward_workspace_size(ctypes.byref(cfg), None) == A.MOE_ERR_INVALID_ARG
+    assert lib.moe_forward_train(ctypes.byref(cfg), None, None, None, None, None, None, None, 0,
+                                 None) == A.MOE_ERR_INVALID_ARG
+    assert lib.moe_backward(ctypes.byref(cfg), None, None, None, None, None, None, 0.0, 0.0, None,
+                            None, 0, None) == A.MOE_ERR_INVALID_ARG
+    # layers the backward does not run in this build
+    for bad in (_base(act_dtype="f32", d_ff=200), _base(activation="swiglu")):
+        assert lib.moe_backward_workspace_size(ctypes.byref(bad), ctypes.byref(n)) == \
+            A.MOE_ERR_UNSUPPORTED
+        assert lib.moe_backward(ctypes.byref(bad), None, None, None, None, None, None, 0.0, 0.0,
+                                None, None, 0, None) == A.MOE_ERR_UNSUPPORTED
+        assert lib.moe_forward_train(ctypes.byref(bad), None, None, None, None, None, None, None, 0,
+                                     None) == A.MOE_ERR_UNSUPPORTED
+    # zero tokens: no-op
+    z = _base(tokens=0)
+    assert lib.moe_backward(ctypes.byref(z), None, None, None, None, None, None, 0.0, 0.0, None,
+                            None, 0, None) == A.MOE_OK
+
+
+def test_backward_workspace_too_small_is_reported():
+    lib = A.lib()
+    cfg = _base()
+    fake = ctypes.c_void_p(0x1000)   # never dereferenced: the size check comes first
+    w = A.MoeWeights(w_gate=fake, w1=fake, w2=fake, b1=fake, b2=fake)
+    r = A.MoeRouting(*([fake] * 6))
+    sv = A.MoeSaved(fake, fake)
+    g = A.MoeGrads(dx=fake, dw_gate=fake, dw1=fake, dw2=fake, db1=fake, db2=fake)
+    st = lib.moe_backward(ctypes.byref(cfg), fake, ctypes.byref(w), ctypes.byref(r), fake,
+                          ctypes.byref(sv), fake, 0.0, 0.0, ctypes.byref(g), fake, 16, None)
+    assert st == A.MOE_ERR_WORKSPACE

@@ -1,0 +1,266 @@
+"""GPU parity of the training forward and the backward pass (through the C ABI)
+against the CPU oracle.
+
+Stage isolation: the oracle runs on the GPU's routing (logits and top-k choice),
+so near ties cannot make the two sides differ in a discrete decision; the
+routing itself is checked bit-exact by the forward parity tests. Every
+gradient is compared over the whole tensor with the max-norm relative error
+max|g - r| / max|r| against the bf16 bar (the operands of the expert GEMMs are
+bf16, as in the forward).
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+from sparse_mixture_experts_38_amd import api as A
+from sparse_mixture_experts_38_amd.workloads import WORKLOADS, make_inputs
+
+from parity_util import TOL, check_dispatch, np64, oracle_params, rel_err, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+W = WORKLOADS
+AUX, ZC = 0.01, 0.001
+
+CASES = {
+    # DeepSpeed GPT-MoE recipe (GELU, biases, softmax top-2, capacity 1.25), ragged T
+    "gpt_moe_small": W["deepspeed_gpt_moe"].scaled(tokens=1000, d_model=256, d_ff=512),
+    # tight capacity so assignments are dropped
+    "gpt_moe_drops": W["deepspeed_gpt_moe"].scaled(tokens=777, d_model=256, d_ff=512,
+                                                   capacity_factor=0.9),
+    # ReLU experts, gate bias, bf16 router weights
+    "relu_bf16": W["deepspeed_gpt_moe"].scaled(tokens=333, d_model=256, d_ff=256, activation="relu",
+                                               has_gate_bias=True, router_dtype="bf16"),
+    # sigmoid router with selection bias, top-8 of 256, shared expert (GELU experts)
+    "deepseek_small_gelu": W["deepseek_v3"].scaled(tokens=300, d_model=512, d_ff=256,
+                                                   activation="gelu"),
+    # 128 experts, top-1, heavy imbalance: many empty and near-empty groups
+    "many_expert": W["many_expert_train"].scaled(tokens=1536, d_model=256, d_ff=256),
+    # d_model 2048: the dX GEMM takes the 256 x 256 tiles for full 256-row blocks
+    "long_k": W["deepspeed_gpt_moe"].scaled(tokens=600, d_model=2048, d_ff=512, num_experts=4,
+                                            drop_tokens=False),
+}
+
+
+def gpu_train_step(w, g, dy, cfg=None, aux=AUX, zc=ZC):
+    cfg = cfg or A.make_config(w)
+    R = A.alloc_routing(cfg)
+    stats = A.alloc_stats()
+    ws = A.alloc_workspace(cfg)
+    saved = A.alloc_saved(cfg)
+    y = torch.empty(w.tokens, w.d_model, dtype=g["x"].dtype, device="cuda")
+    A.forward_train(cfg, g["x"], A.weights_of(g), y, R, stats, saved, ws)
+    grads = A.alloc_grads(cfg)
+    bws = A.alloc_backward_workspace(cfg)
+    A.backward(cfg, g["x"], A.weights_of(g), R, stats, saved, dy, aux, zc, grads, bws)
+    torch.cuda.synchronize()
+    out = {k: v.cpu() for k, v in R.items() if v is not None}
+    out["y"] = y.cpu()
+    out["stats"] = A.read_stats(stats, w.num_experts)
+    out["z"] = saved["z"].cpu()
+    out["y_perm"] = saved["y_perm"].cpu()
+    out["grads"] = {k: (None if v is None else v.cpu()) for k, v in grads.items()}
+    return out
+
+
+def make_dy(w, seed, device="cpu"):
+    gen = torch.Generator(device=device)
+    gen.manual_seed(1000 + seed)
+    return torch.randn(w.tokens, w.d_model, generator=gen, device=device).to(torch.bfloat16)
+
+
+def check_backward(w, inp, dy, out):
+    x_np = np64(inp["x"])
+    P = oracle_params(inp)
+    logits = out["logits"].numpy().astype(np.float64)
+    fwd = O.forward(x_np, P, w, logits=out["logits"].numpy(), idx=out["topk_idx"].numpy())
+    check_dispatch(w, out)
+    tol = TOL["bf16"]
+    errs = {}
+    # training forward: output, saved pre-activation and expert outputs
+    errs["y"] = rel_err(out["y"].float().numpy(), fwd["y"])
+    g = O.backward(x_np, P, w, np64(dy), AUX, ZC, fwd=fwd, logits=logits)
+    R = int(fwd["expert_offsets"][-1])
+    errs["z"] = rel_err(out["z"].float().numpy()[:R], g["z"][:R])
+    errs["y_perm"] = rel_err(out["y_perm"].float().numpy()[:R], fwd["Y"][:R])
+    G = out["grads"]
+    pairs = [("dx", "dx"), ("dw_gate", "dw_gate"), ("dw1", "dw1"), ("dw2", "dw2")]
+    if w.has_bias:
+        pairs += [("db1", "db1"), ("db2", "db2")]
+    if w.has_gate_bias:
+        pairs += [("db_gate", "db_gate")]
+    if w.num_shared_experts:
+        pairs += [("dws1", "dws1"), ("dws2", "dws2")]
+        if w.has_bias:
+            pairs += [("dbs1", "dbs1"), ("dbs2", "dbs2")]
+    for gk, ok in pairs:
+        ref = g[ok]
+        got = G[gk].float().numpy()
+        assert got.shape == ref.shape, gk
+        errs[gk] = rel_err(got, ref)
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, f"max rel err above {tol}: {bad} (all: {errs})"
+    return errs
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_backward_parity(name):
+    w = CASES[name]
+    print(f"[case] backward {name} T={w.tokens} d={w.d_model} F={w.d_ff} E={w.num_experts} "
+          f"k={w.top_k} {w.activation} {w.score_fn}", flush=True)
+    inp = make_inputs(w, seed=0, device="cpu")
+    dy = make_dy(w, 0)
+    out = gpu_train_step(w, to_gpu(inp), dy.cuda())
+    errs = check_backward(w, inp, dy, out)
+    print("  errs", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    if name == "gpt_moe_drops":
+        assert out["stats"]["dropped"] > 0
+
+
+def test_training_forward_matches_inference_forward():
+    """moe_forward_train gives the routing of moe_forward bit for bit and the same
+    output up to the bf16 rounding of the saved pre-activation."""
+    w = CASES["gpt_moe_small"]
+    print("[case] forward_train vs forward", flush=True)
+    inp = make_inputs(w, seed=3, device="cuda")
+    cfg = A.make_config(w)
+    R1, R2 = A.alloc_routing(cfg), A.alloc_routing(cfg)
+    s1, s2 = A.alloc_stats(), A.alloc_stats()
+    ws = A.alloc_workspace(cfg)
+    y1 = torch.empty(w.tokens, w.d_model, dtype=torch.bfloat16, device="cuda")
+    y2 = torch.empty_like(y1)
+    A.forward(cfg, inp["x"], A.weights_of(inp), y1, R1, s1, ws)
+    A.forward_train(cfg, inp["x"], A.weights_of(inp), y2, R2, s2, A.alloc_saved(cfg), ws)
+    torch.cuda.synchronize()
+    for k in ("logits", "topk_idx", "topk_gate", "expert_offsets", "assign_row"):
+        assert torch.equal(R1[k], R2[k]), k
+    assert torch.equal(s1, s2)
+    assert rel_err(y2.float().cpu().numpy(), y1.float().cpu().numpy()) <= 1e-2
+
+
+def test_backward_is_deterministic():
+    w = CASES["gpt_moe_drops"]
+    print("[case] backward determinism", flush=True)
+    inp = to_gpu(make_inputs(w, seed=1, device="cpu"))
+    dy = make_dy(w, 1).cuda()
+    a = gpu_train_step(w, inp, dy)["grads"]
+    b = gpu_train_step(w, inp, dy)["grads"]
+    for k, v in a.items():
+        if v is not None:
+            assert torch.equal(v, b[k]), k
+
+
+def test_backward_loss_coefficients_enter_linearly():
+    """The gradient is linear in (dy, aux_coef, z_coef): with dy = 0 only the
+    router receives a gradient, and doubling both coefficients doubles dw_gate
+    and leaves the expert weights' gradients at zero."""
+    w = CASES["relu_bf16"]
+    print("[case] backward with dy = 0", flush=True)
+    inp = to_gpu(make_inputs(w, seed=2, device="cpu"))
+    dy = torch.zeros(w.tokens, w.d_model, dtype=torch.bfloat16, device="cuda")
+    o1 = gpu_train_step(w, inp, dy, aux=0.01, zc=0.001)["grads"]
+    o2 = gpu_train_step(w, inp, dy, aux=0.02, zc=0.002)["grads"]
+    for k in ("dw1", "dw2", "db1", "db2"):
+        assert float(o1[k].abs().max()) == 0.0, k
+    assert float(o1["dw_gate"].abs().max()) > 0
+    np.testing.assert_allclose(o2["dw_gate"].numpy(), 2 * o1["dw_gate"].numpy(), rtol=1e-5,
+                               atol=1e-7 * float(o1["dw_gate"].abs().max()))
+
+
+def test_backward_edge_cases():
+    """One token; k = E; a single expert; every token routed to one expert (the
+    other groups are empty and padded to 128 zero columns)."""
+    base = W["deepspeed_gpt_moe"].scaled(d_model=256, d_ff=256)
+    cases = {
+        "one_token": base.scaled(tokens=1),
+        "k_equals_E": base.scaled(tokens=200, num_experts=4, top_k=4, drop_tokens=False),
+        "single_expert": base.scaled(tokens=150, num_experts=1, top_k=1, drop_tokens=False),
+    }
+    for name, w in cases.items():
+        print(f"[case] backward edge {name}", flush=True)
+        inp = make_inputs(w, seed=4, device="cpu")
+        dy = make_dy(w, 4)
+        out = gpu_train_step(w, to_gpu(inp), dy.cuda())
+        check_backward(w, inp, dy, out)
+    # all tokens to expert 0: a large gate bias on expert 0
+    w = base.scaled(tokens=300, num_experts=8, top_k=1, has_gate_bias=True, drop_tokens=False)
+    print("[case] backward edge all_to_one", flush=True)
+    inp = make_inputs(w, seed=5, device="cpu")
+    inp["b_gate"] = torch.zeros(8)
+    inp["b_gate"][0] = 50.0
+    dy = make_dy(w, 5)
+    out = gpu_train_step(w, to_gpu(inp), dy.cuda())
+    assert int(out["stats"]["counts_kept"][0]) == 300
+    check_backward(w, inp, dy, out)
+
+
+def test_backward_full_size_sampled():
+    """DeepSpeed GPT-MoE at its full size (T = 8192, d = 1024, F = 4096, 8 experts):
+    the router weight gradient in full and sampled rows of every other gradient,
+    each computed by the oracle from its definition for just those entries,
+    on the GPU's routing and saved forward activations."""
+    w = W["deepspeed_gpt_moe"]
+    print("[case] backward full-size deepspeed_gpt_moe", flush=True)
+    inp = make_inputs(w, seed=0, device="cuda")
+    dy = make_dy(w, 0, device="cuda")
+    out = gpu_train_step(w, inp, dy)
+    T, d, F, E, k = w.tokens, w.d_model, w.d_ff, w.num_experts, w.top_k
+    x = np64(inp["x"])
+    dyn = np64(dy)
+    P = oracle_params(inp)
+    dsp = check_dispatch(w, out)
+    off = dsp["expert_offsets"]
+    rt = dsp["row_token"]
+    Y = out["y_perm"].float().numpy().astype(np.float64)
+    Z = out["z"].float().numpy().astype(np.float64)
+    logits = out["logits"].numpy().astype(np.float64)
+    idx = out["topk_idx"].numpy()
+    gates = out["topk_gate"].numpy().astype(np.float64)
+    # combine backward on the saved expert outputs, then the router backward
+    dYp, dgate = O.combine_backward(dyn, Y, gates, dsp["assign_row"])
+    f = dsp["counts_pre"] / float(T * k)
+    dlog = O.router_backward(logits, idx, w.score_fn, dgate, f, AUX, ZC)
+    G = out["grads"]
+    tol = TOL["bf16"]
+    assert rel_err(G["dw_gate"].numpy(), dlog.T @ x) <= tol, "dw_gate"
+    # host float64 copies of the expert weights, made once
+    W1s = [P["w1"][e] for e in range(E)]
+    W2s = [P["w2"][e] for e in range(E)]
+    B1s = [P["b1"][e] for e in range(E)]
+    # saved pre-activation on sampled rows
+    rng = np.random.default_rng(0)
+    rows = rng.choice(int(off[-1]), 64, replace=False)
+    row_e = np.searchsorted(off, rows, side="right") - 1
+    z_ref = np.stack([x[rt[r]] @ W1s[e].T + B1s[e] for r, e in zip(rows, row_e)])
+    assert rel_err(Z[rows], z_ref) <= tol, "z"
+    # expert gradients on sampled rows / columns of two experts
+    for e in (0, E - 1):
+        lo, hi = int(off[e]), int(off[e + 1])
+        W1, W2 = W1s[e], W2s[e]
+        Ze = Z[lo:hi]
+        He = O.gelu(Ze)
+        dYe = dYp[lo:hi]
+        i_s = rng.choice(d, 8, replace=False)
+        f_s = rng.choice(F, 8, replace=False)
+        # dW2[e][i, :] = sum_r dY[r, i] h[r, :]
+        assert rel_err(G["dw2"][e].numpy()[i_s], dYe[:, i_s].T @ He) <= tol, f"dw2[{e}]"
+        # dZ[:, f] = (dY W2[:, f]) * gelu'(z[:, f]); dW1[e][f, :] = sum_r dZ[r, f] x[r, :]
+        dZf = (dYe @ W2[:, f_s]) * O.gelu_grad(Ze[:, f_s])
+        assert rel_err(G["dw1"][e].numpy()[f_s], dZf.T @ x[rt[lo:hi]]) <= tol, f"dw1[{e}]"
+        assert rel_err(G["db2"][e].numpy(), dYe.sum(axis=0)) <= tol, f"db2[{e}]"
+        dZ_all = (dYe @ W2) * O.gelu_grad(Ze)
+        assert rel_err(G["db1"][e].numpy(), dZ_all.sum(axis=0)) <= tol, f"db1[{e}]"
+    # dx on sampled tokens (including tokens that lost a choice to capacity)
+    dropped_tok = np.nonzero(np.any(dsp["assign_row"] < 0, axis=1))[0]
+    toks = np.unique(np.concatenate([rng.choice(T, 48, replace=False), dropped_tok[:16]]))
+    dx_ref = dlog[toks] @ P["w_gate"]
+    for si, t in enumerate(toks):
+        for j in range(k):
+            r = dsp["assign_row"][t, j]
+            if r < 0:
+                continue
+            e = int(idx[t, j])
+            dz = (dYp[r] @ W2s[e]) * O.gelu_grad(Z[r])
+            dx_ref[si] += dz @ W1s[e]
+    assert rel_err(G["dx"].float().numpy()[toks], dx_ref) <= tol, "dx"
