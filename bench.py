@@ -8,10 +8,13 @@ statistics) over one batch of synthetic tokens already resident in HBM, through
 the moe_forward C-ABI entry point on one stream. Input and weight sets are
 rotated so the 256 MB Infinity Cache does not hold the previous step's
 operands. The stage entry points are then run over the same sets with HIP
-events around the two grouped GEMMs, for the roofline figure. Prints one JSON
-line.
+events around the two grouped GEMMs, for the roofline figure. Then, where the
+layer has a backward in this build, one training step (moe_forward_train +
+moe_backward) is timed the same way and reported under "train". Prints one
+JSON line.
 """
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -100,6 +103,8 @@ def main():
     ap.add_argument("--workload", default="deepspeed_gpt_moe")
     ap.add_argument("--sets", type=int, default=3, help="rotated input/weight sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-train", action="store_true",
+                    help="skip the training-step measurement (moe_forward_train + moe_backward)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB float32 copy kernel (torch.neg) three times, "
                          "so that hardware byte counters can be scaled by a kernel of known traffic")
@@ -214,9 +219,56 @@ def main():
         "kept_rows": rows,
         "wall_s": wall,
     }
+    if not args.no_train and A.lib().moe_backward_workspace_size(
+            ctypes.byref(cfg), ctypes.byref(ctypes.c_size_t(0))) == A.MOE_OK:
+        del plans
+        result["train"] = train_step(A, torch, w, cfg, sets, ws, args.steps, args.warmup, rows)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, sets[0])
     print(json.dumps(result), flush=True)
+
+
+def train_step(A, torch, w, cfg, sets, ws, steps, warmup, rows):
+    """One training step of the layer: moe_forward_train then moe_backward (with
+    L_aux and z-loss weights 0.01 and 0.001), on the same rotated input sets.
+    The backward's algorithmic FLOPs are its four expert GEMMs, 4 x 2 R d F
+    (dH and dX, dW2 and dW1), R = kept rows."""
+    T, d, F = w.tokens, w.d_model, w.d_ff
+    act = A.TORCH_DTYPE[cfg.act_dtype]
+    grads = A.alloc_grads(cfg)
+    bws = A.alloc_backward_workspace(cfg)
+    tplans = []
+    for i, s in enumerate(sets):
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(1000 + i)
+        dy = torch.randn(T, d, generator=gen, device="cuda").to(act)
+        R = A.alloc_routing(cfg)
+        tplans.append(A.TrainPlan(cfg, s["x"], A.weights_of(s), torch.empty(T, d, dtype=act, device="cuda"),
+                                  R, A.alloc_stats(), A.alloc_saved(cfg), ws, dy, grads, bws))
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for i in range(warmup):
+        p = tplans[i % len(tplans)]
+        p.forward()
+        p.backward()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        p = tplans[i % len(tplans)]
+        p.forward()
+        ev[i][0].record()
+        p.backward()
+        ev[i][1].record()
+    stop.record()
+    torch.cuda.synchronize()
+    step_ms = start.elapsed_time(stop) / steps
+    bwd_ms = statistics.mean(e[0].elapsed_time(e[1]) for e in ev)
+    bwd_flop = 4 * 2.0 * rows * d * F
+    tf = bwd_flop / (bwd_ms * 1e-3) / 1e12
+    return {"step_ms": step_ms, "forward_train_ms": step_ms - bwd_ms, "backward_ms": bwd_ms,
+            "tokens_per_s": T / (step_ms * 1e-3), "backward_gemm_flop": bwd_flop,
+            "backward_tflops": tf, "backward_frac_of_peak": tf / PEAK_BF16_TFLOPS,
+            "aux_coef": 0.01, "z_coef": 0.001}
 
 
 if __name__ == "__main__":

@@ -324,9 +324,17 @@ __global__ __launch_bounds__(256) void colsum_reduce_kernel(const float* __restr
   const int g = blockIdx.y;
   const int c = blockIdx.x * 256 + threadIdx.x;
   if (c >= C) return;
-  const int b0 = po[g] / 64, b1 = po[g + 1] / 64;
+  const int b0 = po[g] / 64, b1 = po[g + 1] / 64;   // b1 - b0 is even (po: multiples of 128)
   float s = 0.f;
-  for (int b = b0; b < b1; ++b) s += partial[(int64_t)b * C + c];
+  int b = b0;
+  for (; b + 8 <= b1; b += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = partial[(int64_t)(b + u) * C + c];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  for (; b < b1; ++b) s += partial[(int64_t)b * C + c];
   if (g < E) db[(int64_t)g * C + c] = s;
   else dbs[c] = s;
 }
@@ -344,7 +352,20 @@ __global__ __launch_bounds__(256) void gate_wgrad_kernel(const bf16* __restrict_
   const int64_t t0 = (int64_t)blockIdx.z * slice_len;
   const int64_t t1 = t0 + slice_len < T ? t0 + slice_len : T;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int64_t t = t0; t < t1; ++t) {
+  int64_t t = t0;
+  for (; t + 8 <= t1; t += 8) {
+    float xv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) xv[u] = to_f32(x[(t + u) * d + c]);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float* dl = dlogits + (t + u) * E + e0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (e0 + e < E) acc[e] = fmaf(dl[e], xv[u], acc[e]);
+    }
+  }
+  for (; t < t1; ++t) {
     const float xv = to_f32(x[t * d + c]);
     const float* dl = dlogits + t * E + e0;
 #pragma unroll
@@ -362,7 +383,15 @@ __global__ __launch_bounds__(256) void gate_wgrad_reduce_kernel(const float* __r
   const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (i >= n) return;
   float s = 0.f;
-  for (int z = 0; z < slices; ++z) s += partial[z * n + i];
+  int z = 0;
+  for (; z + 8 <= slices; z += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = partial[(z + u) * n + i];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  for (; z < slices; ++z) s += partial[z * n + i];
   dw[i] = s;
 }
 
@@ -384,38 +413,50 @@ __global__ __launch_bounds__(256) void gate_bias_grad_kernel(const float* __rest
 }
 
 // ------------------------------------------------------------------ dx
-// dx[t][c] = sum_j dXp[assign_row[t, j]][c] (kept choices) + dXp[off[E] + t][c]
-// (shared expert) + sum_e dlogits[t][e] W_g[e][c]. Block: 32 tokens x 256
-// columns; each W_g element is loaded once per block and used for 32 tokens.
+// dx[t] = sum_j dXp[assign_row[t, j]] (kept choices, j order) + dXp[off[E] + t]
+// (shared expert) + sum_e dlogits[t][e] W_g[e] (router), float32 sums, one
+// rounding. One wavefront per token; lanes take 16-byte column chunks.
 template <typename WT>
 __global__ __launch_bounds__(256) void unpermute_dx_kernel(
     const bf16* __restrict__ dxp, const int32_t* __restrict__ assign_row,
     const int32_t* __restrict__ off, const float* __restrict__ dlogits, const WT* __restrict__ wg,
     int64_t T, int d, int k, int E, int S, int64_t rows_max, bf16* __restrict__ dx) {
-  constexpr int TB = 32;
-  const int c = blockIdx.y * 256 + threadIdx.x;
-  const int64_t t0 = (int64_t)blockIdx.x * TB;
-  float acc[TB];
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= T) return;
+  int rj[MOE_MAX_TOP_K];
 #pragma unroll
-  for (int i = 0; i < TB; ++i) acc[i] = 0.f;
-  for (int e = 0; e < E; ++e) {
-    const float w = to_f32(wg[(int64_t)e * d + c]);
-#pragma unroll
-    for (int i = 0; i < TB; ++i)
-      if (t0 + i < T) acc[i] = fmaf(dlogits[(t0 + i) * E + e], w, acc[i]);
+  for (int j = 0; j < MOE_MAX_TOP_K; ++j) {
+    const int r = j < k ? assign_row[t * k + j] : -1;
+    rj[j] = (r >= 0 && r < rows_max) ? r : -1;
   }
-  const int64_t shared0 = S ? clamp_off(off, E, rows_max) : 0;
+  const int64_t rs = S ? (int64_t)clamp_off(off, E, rows_max) + t : rows_max;
+  const float* dl = dlogits + t * E;
+  for (int c = lane * 8; c < d; c += 512) {
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int e = 0; e < E; ++e) {
+      float wv[8];
+      load8(wg + (int64_t)e * d + c, wv);
+      const float g = dl[e];
 #pragma unroll
-  for (int i = 0; i < TB; ++i) {
-    const int64_t t = t0 + i;
-    if (t >= T) break;
-    float v = acc[i];
-    for (int j = 0; j < k; ++j) {
-      const int r = assign_row[t * k + j];
-      if (r >= 0 && r < rows_max) v += to_f32(dxp[(int64_t)r * d + c]);
+      for (int u = 0; u < 8; ++u) v[u] = fmaf(g, wv[u], v[u]);
     }
-    if (S && shared0 + t < rows_max) v += to_f32(dxp[(shared0 + t) * d + c]);
-    store1(dx + t * d + c, v);
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOP_K; ++j) {
+      if (rj[j] >= 0) {
+        float a[8];
+        load8(dxp + (int64_t)rj[j] * d + c, a);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] += a[u];
+      }
+    }
+    if (rs < rows_max) {
+      float a[8];
+      load8(dxp + rs * d + c, a);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] += a[u];
+    }
+    store8(dx + t * d + c, v);
   }
 }
 
@@ -503,7 +544,7 @@ hipError_t launch_backward_misc(const moe_config& c, const BwdLayout& B, const v
   if (c.has_gate_bias)
     hipLaunchKernelGGL(gate_bias_grad_kernel, dim3(E), dim3(256), 0, s, (const float*)dlogits, T, E,
                        gr.db_gate);
-  const dim3 ug((unsigned)((T + 31) / 32), (unsigned)(d / 256));
+  const dim3 ug((unsigned)((T + 3) / 4));
   if (c.router_dtype == MOE_BF16)
     hipLaunchKernelGGL((unpermute_dx_kernel<bf16>), ug, dim3(256), 0, s, (const bf16*)(ws + B.dxp),
                        r.assign_row, r.expert_offsets, (const float*)dlogits, (const bf16*)w.w_gate,
