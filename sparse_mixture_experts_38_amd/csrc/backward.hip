@@ -340,41 +340,73 @@ __global__ __launch_bounds__(256) void colsum_reduce_kernel(const float* __restr
 }
 
 // ------------------------------------------------------------------ router weights
-// dW_g[e][c] = sum_t dlogits[t][e] x[t][c]: block (expert group of 8, 256
-// columns, token slice) accumulates 8 x 256 sums over its tokens and writes them
-// to partial[slice][e][c]; gate_wgrad_reduce_kernel adds the slices in order.
+// dW_g[e][c] = sum_t dlogits[t][e] x[t][c]. Block (8 experts, 1024 columns, a
+// token slice): thread = 8 consecutive columns (one 16-byte load per token) x 8
+// experts, the two halves of the block take alternate tokens and are added in
+// LDS; the block's sums go to partial[slice][e][c] and
+// gate_wgrad_reduce_kernel adds the slices in order.
 __global__ __launch_bounds__(256) void gate_wgrad_kernel(const bf16* __restrict__ x,
                                                          const float* __restrict__ dlogits,
                                                          int64_t T, int d, int E, int slice_len,
                                                          float* __restrict__ partial) {
+  __shared__ float red[128][65];
   const int e0 = blockIdx.x * 8;
-  const int c = blockIdx.y * 256 + threadIdx.x;
+  const int half = threadIdx.x >> 7;
+  const int c = (blockIdx.y * 128 + (threadIdx.x & 127)) * 8;
   const int64_t t0 = (int64_t)blockIdx.z * slice_len;
   const int64_t t1 = t0 + slice_len < T ? t0 + slice_len : T;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  int64_t t = t0;
-  for (; t + 8 <= t1; t += 8) {
-    float xv[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) xv[u] = to_f32(x[(t + u) * d + c]);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float* dl = dlogits + (t + u) * E + e0;
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (e0 + e < E) acc[e] = fmaf(dl[e], xv[u], acc[e]);
-    }
-  }
-  for (; t < t1; ++t) {
-    const float xv = to_f32(x[t * d + c]);
-    const float* dl = dlogits + t * E + e0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (e0 + e < E) acc[e] = fmaf(dl[e], xv, acc[e]);
-  }
+  float acc[8][8];
 #pragma unroll
   for (int e = 0; e < 8; ++e)
-    if (e0 + e < E) partial[((int64_t)blockIdx.z * E + e0 + e) * d + c] = acc[e];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[e][u] = 0.f;
+  if (c < d) {
+    // four tokens per iteration, their loads issued together
+    for (int64_t tb = t0 + half; tb < t1; tb += 8) {
+      float xv[4][8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t t = tb + 2 * q;
+        if (t < t1) {
+          load8(x + t * d + c, xv[q]);
+        } else {
+#pragma unroll
+          for (int u = 0; u < 8; ++u) xv[q][u] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t t = tb + 2 * q;
+        if (t < t1) {
+          const float* dl = dlogits + t * E + e0;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float g = e0 + e < E ? dl[e] : 0.f;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) acc[e][u] = fmaf(g, xv[q][u], acc[e][u]);
+          }
+        }
+      }
+    }
+  }
+  if (half == 1) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) red[threadIdx.x & 127][e * 8 + u] = acc[e][u];
+  }
+  __syncthreads();
+  if (half == 0 && c < d) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (e0 + e < E) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = acc[e][u] + red[threadIdx.x][e * 8 + u];
+        store8(partial + ((int64_t)blockIdx.z * E + e0 + e) * d + c, v);
+      }
+    }
+  }
 }
 
 __global__ __launch_bounds__(256) void gate_wgrad_reduce_kernel(const float* __restrict__ partial,
@@ -535,7 +567,7 @@ hipError_t launch_backward_misc(const moe_config& c, const BwdLayout& B, const v
     hipLaunchKernelGGL(colsum_reduce_kernel, dim3((F + 255) / 256, G), dim3(256), 0, s,
                        (const float*)p1, (const int32_t*)po, F, E, gr.db1, gr.dbs1);
   }
-  hipLaunchKernelGGL(gate_wgrad_kernel, dim3((E + 7) / 8, d / 256, B.gate_slices), dim3(256), 0, s,
+  hipLaunchKernelGGL(gate_wgrad_kernel, dim3((E + 7) / 8, (d + 1023) / 1024, B.gate_slices), dim3(256), 0, s,
                      (const bf16*)x, (const float*)dlogits, T, d, E, (int)B.gate_slice_len,
                      (float*)(ws + B.gate_partial));
   const int64_t n = (int64_t)E * d;

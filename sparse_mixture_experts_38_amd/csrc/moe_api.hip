@@ -74,10 +74,10 @@ BwdLayout backward_layout(const moe_config& c) {
   B.xT = take((size_t)(d * B.ldk * 2));
   B.colsum1 = take(c.has_bias ? (size_t)(B.ldk / 64 * F * 4) : 0);
   B.colsum2 = take(c.has_bias ? (size_t)(B.ldk / 64 * d * 4) : 0);
-  // router weight gradient: about 512 blocks of (8 experts x 256 columns x a token slice)
-  const int64_t xy = (int64_t)((E + 7) / 8) * (d / 256 > 0 ? d / 256 : 1);
+  // router weight gradient: about 512 blocks of (8 experts x 1024 columns x a token slice)
+  const int64_t xy = (int64_t)((E + 7) / 8) * ((d + 1023) / 1024);
   int64_t slices = 512 / xy;
-  slices = slices < 1 ? 1 : (slices > 128 ? 128 : slices);
+  slices = slices < 1 ? 1 : (slices > 256 ? 256 : slices);
   if (slices > T) slices = T > 0 ? T : 1;
   const int64_t slice_len = T > 0 ? (T + slices - 1) / slices : 1;
   B.gate_slice_len = (int)slice_len;
