@@ -644,3 +644,81 @@ def backward(x, params, w, dy, aux_coef: float = 0.0, z_coef: float = 0.0, fwd=N
                db_gate=dlogits.sum(axis=0) if params.get("b_gate") is not None else None,
                dY=dY, dgate=dgate, dlogits=dlogits, z=Z, dz=dZ)
     return out
+
+
+# --------------------------------------------------------------------------
+# Expert-choice routing
+# --------------------------------------------------------------------------
+# Each expert picks its C best tokens over the transposed [E, T] scores, so every
+# expert is exactly full (MoE Training: Mixture of Experts, "2. Routing
+# Mechanisms", expert choice routing: experts choose top-k tokens, which
+# guarantees perfect load balancing; MoE From Scratch to DeepSeek V3: expert
+# choice keeps the load balanced but may treat tokens unevenly; the survey's
+# expert-choice routing entry).
+# READINGS: the score an expert ranks tokens by is the router logit (the page's
+# router(x) is the logit, as in its top-1 code), in float32; equal scores go to
+# the lower token index first; the weight of an expert's output for a token is
+# the softmax probability p[t, e] over experts (the token-choice gate p =
+# Softmax(h(x)) of MoE From Scratch to DeepSeek V3; there is no top-k set to
+# renormalise over); a token no expert picks gets zero (plus the shared expert);
+# C is the capacity rule of capacity() with k the average experts per token,
+# ceil(k T / E) when dropping is off, and never more than T; an expert's rows are
+# its chosen tokens in ascending token order.
+
+def expert_choice_capacity(tokens: int, num_experts: int, top_k: int, capacity_factor: float,
+                           min_capacity: int, drop_tokens: bool) -> int:
+    """Tokens per expert C for expert-choice routing (see the readings above)."""
+    c = capacity(tokens, num_experts, top_k, capacity_factor, min_capacity, drop_tokens)
+    if c is None:
+        c = -(-top_k * tokens // num_experts)
+    return int(min(c, tokens))
+
+
+def expert_choice_route(logits, C: int) -> Dict[str, np.ndarray]:
+    """Per expert, the C tokens with the largest float32 logit (ties: lower token
+    first), listed in ascending token order; their gates p[t, e] (softmax over
+    experts, float64 from the float32 logits); the row of (t, e) or -1.
+
+    Rows: expert e's chosen tokens occupy rows e C .. e C + C - 1.
+    """
+    h32 = np.asarray(logits, F32)
+    T, E = h32.shape
+    p, lse = softmax_scores(h32)
+    tokens = np.empty((E, C), np.int64)
+    for e in range(E):
+        order = np.argsort(-h32[:, e], kind="stable")   # descending, lower token first on ties
+        tokens[e] = np.sort(order[:C])
+    gates = np.take_along_axis(p.T, tokens, axis=1)       # [E, C]
+    row = np.full((T, E), -1, np.int64)
+    for e in range(E):
+        row[tokens[e], e] = e * C + np.arange(C)
+    picks = (row >= 0).sum(axis=1)
+    return dict(tokens=tokens, gates=gates, row=row, p=p, lse=lse, picks=picks)
+
+
+def expert_choice_forward(x, params, w, logits=None) -> Dict[str, object]:
+    """The layer with expert-choice routing: y[t] = sum over the experts e that
+    picked t of p[t, e] E_e(x_t) (+ shared expert). Statistics: every expert takes
+    C tokens; "unpicked" counts the tokens no expert chose; P_i and the z-loss as
+    for token choice."""
+    x = np.asarray(x, F64)
+    T, d = x.shape
+    E = w.num_experts
+    C = expert_choice_capacity(T, E, w.top_k, w.capacity_factor, w.min_capacity, w.drop_tokens)
+    if logits is None:
+        logits = router_logits(x, params["w_gate"], params.get("b_gate"))
+    r = expert_choice_route(logits, C)
+    Y = np.zeros((E * C, d), F64)
+    for e in range(E):
+        Y[e * C:(e + 1) * C] = expert_ffn(x[r["tokens"][e]], params["w1"][e], _opt(params.get("b1"), e),
+                                          params["w2"][e], _opt(params.get("b2"), e), w.activation,
+                                          _opt(params.get("w3"), e))
+    y = np.zeros((T, d), F64)
+    for e in range(E):
+        y[r["tokens"][e]] += r["gates"][e][:, None] * Y[e * C:(e + 1) * C]
+    if w.num_shared_experts:
+        y += expert_ffn(x, params["ws1"][0], _opt(params.get("bs1"), 0), params["ws2"][0],
+                        _opt(params.get("bs2"), 0), w.activation, _opt(params.get("ws3"), 0))
+    stats = dict(capacity=C, P=r["p"].mean(axis=0), z_loss=float(np.mean(r["lse"] ** 2)),
+                 unpicked=int(np.count_nonzero(r["picks"] == 0)), max_picks=int(r["picks"].max()))
+    return dict(logits=np.asarray(logits, F32), y=y, Y=Y, stats=stats, C=C, **r)
