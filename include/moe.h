@@ -274,6 +274,47 @@ int moe_forward(const moe_config* cfg, const void* x, const moe_weights* w, void
                 const moe_routing* routing, moe_stats* stats, void* workspace,
                 size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------ expert choice
+ * Expert-choice routing ([P1] "2. Routing Mechanisms", expert choice routing;
+ * [P4] routing strategies; [P5] expert-choice routing): every expert takes its
+ * C best tokens over the transposed [E, T] router scores, so each expert is
+ * exactly full, while a token may be served by several experts or by none.
+ * Score = the float32 router logit; equal scores go to the lower token; the
+ * output of expert e for token t is weighted by the softmax probability
+ * p[t, e] over experts; y[t] = sum over the experts that chose t of
+ * p[t, e] E_e(x_t) (+ the shared expert). C = max(min_capacity,
+ * ceil(capacity_factor k T / E)) (ceil(k T / E) when drop_tokens == 0), at most
+ * T. This build runs it for the softmax router (score_fn MOE_SCORE_SIGMOID
+ * returns MOE_ERR_UNSUPPORTED).
+ */
+
+/* Expert-choice routing results (device buffers the caller owns). */
+typedef struct moe_ec_routing {
+  float* logits;      /* [T, E] float32, or NULL                                        */
+  int32_t* tokens;    /* [E, C]: expert e's chosen tokens, ascending (rows e C .. e C+C-1) */
+  float* gates;       /* [E, C]: p[t, e] of those tokens                                 */
+  int32_t* token_row; /* [T, E]: row of (t, e), or -1 when expert e did not choose t     */
+} moe_ec_routing;
+
+/* Host only. Tokens per expert C of expert-choice routing. */
+int moe_expert_choice_capacity(const moe_config* cfg, int64_t* capacity_out);
+
+/* Host only. Workspace bytes needed by moe_forward_expert_choice. */
+int moe_expert_choice_workspace_size(const moe_config* cfg, size_t* bytes_out);
+
+/*
+ * The layer forward with expert-choice routing on one stream: router logits,
+ * per-expert top-C selection, the grouped GEMMs of moe_forward on the E C rows
+ * (+ T shared rows), and the gate-weighted combine. stats: counts_pre =
+ * counts_kept = C, f_i = 1/E, P_i and z as for token choice, L_aux = E sum f_i
+ * P_i, capacity = C, kept = E C, dropped = the number of tokens no expert chose.
+ *   x [T, d];  w: weights (e_bias unused);  y [T, d] output;  r: routing buffers;
+ *   stats: device moe_stats;  workspace >= moe_expert_choice_workspace_size(cfg).
+ */
+int moe_forward_expert_choice(const moe_config* cfg, const void* x, const moe_weights* w,
+                              void* y, const moe_ec_routing* r, moe_stats* stats,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------ training
  * The layer's backward pass. The objective differentiated is
  *   L = <dy, y> + aux_coef * L_aux + z_coef * z

@@ -46,6 +46,10 @@ class MoeRouting(ctypes.Structure):
                                         "row_token", "assign_row")]
 
 
+class MoeEcRouting(ctypes.Structure):
+    _fields_ = [(n, c_void_p) for n in ("logits", "tokens", "gates", "token_row")]
+
+
 class MoeSaved(ctypes.Structure):
     _fields_ = [(n, c_void_p) for n in ("z", "y_perm")]
 
@@ -99,6 +103,10 @@ def lib():
     L.moe_combine.argtypes = [cfgp, P, P, P, P, P, P]
     L.moe_forward.argtypes = [cfgp, P, ctypes.POINTER(MoeWeights), P, ctypes.POINTER(MoeRouting),
                               P, P, c_size_t, P]
+    L.moe_expert_choice_capacity.argtypes = [cfgp, ctypes.POINTER(c_int64)]
+    L.moe_expert_choice_workspace_size.argtypes = [cfgp, ctypes.POINTER(c_size_t)]
+    L.moe_forward_expert_choice.argtypes = [cfgp, P, ctypes.POINTER(MoeWeights), P,
+                                            ctypes.POINTER(MoeEcRouting), P, P, c_size_t, P]
     L.moe_forward_train.argtypes = [cfgp, P, ctypes.POINTER(MoeWeights), P,
                                     ctypes.POINTER(MoeRouting), P, ctypes.POINTER(MoeSaved), P,
                                     c_size_t, P]
@@ -109,7 +117,8 @@ def lib():
     for name in ("moe_validate_config", "moe_capacity", "moe_workspace_size", "moe_route",
                  "moe_permute", "moe_expert_ffn", "moe_expert_up", "moe_expert_down",
                  "moe_combine", "moe_forward", "moe_forward_train", "moe_backward_workspace_size",
-                 "moe_backward"):
+                 "moe_backward", "moe_expert_choice_capacity", "moe_expert_choice_workspace_size",
+                 "moe_forward_expert_choice"):
         getattr(L, name).restype = c_int
     _lib = L
     return L
@@ -371,6 +380,71 @@ def forward(cfg, x, weights: Dict[str, Optional[torch.Tensor]], y, routing: Dict
     _check(lib().moe_forward(ctypes.byref(cfg), _ptr(x), ctypes.byref(mw), _ptr(y), ctypes.byref(mr),
                              _ptr(stats), _ptr(workspace), workspace.numel(), _stream()),
            "moe_forward")
+
+
+def expert_choice_capacity(cfg: MoeConfig) -> int:
+    n = c_int64(0)
+    _check(lib().moe_expert_choice_capacity(ctypes.byref(cfg), ctypes.byref(n)),
+           "moe_expert_choice_capacity")
+    return int(n.value)
+
+
+def expert_choice_workspace_size(cfg: MoeConfig) -> int:
+    n = c_size_t(0)
+    _check(lib().moe_expert_choice_workspace_size(ctypes.byref(cfg), ctypes.byref(n)),
+           "moe_expert_choice_workspace_size")
+    return int(n.value)
+
+
+def alloc_ec_routing(cfg, device="cuda", logits=True) -> Dict[str, torch.Tensor]:
+    T, d, F, E, k, S, _, _ = _sizes(cfg)
+    C = expert_choice_capacity(cfg)
+    return dict(logits=torch.empty(T, E, dtype=torch.float32, device=device) if logits else None,
+                tokens=torch.empty(E, C, dtype=torch.int32, device=device),
+                gates=torch.empty(E, C, dtype=torch.float32, device=device),
+                token_row=torch.empty(T, E, dtype=torch.int32, device=device))
+
+
+def alloc_ec_workspace(cfg, device="cuda") -> torch.Tensor:
+    return torch.empty(expert_choice_workspace_size(cfg), dtype=torch.uint8, device=device)
+
+
+def forward_expert_choice(cfg, x, weights, y, ec_routing, stats, workspace):
+    """moe_forward_expert_choice: the layer with experts choosing their top-C tokens."""
+    T, d, F, E, k, S, act, rdt = _sizes(cfg)
+    C = expert_choice_capacity(cfg)
+    _need(x, "x", (T, d), act)
+    _need(y, "y", (T, d), act)
+    _need_weights(cfg, weights)
+    R = ec_routing
+    _need(R.get("logits"), "logits", (T, E), torch.float32, optional=True)
+    _need(R["tokens"], "tokens", (E, C), torch.int32)
+    _need(R["gates"], "gates", (E, C), torch.float32)
+    _need(R["token_row"], "token_row", (T, E), torch.int32)
+    _need_stats(stats)
+    _need_ws(workspace)
+    mw = MoeWeights(*[_ptr(weights.get(n)) for n, _ in MoeWeights._fields_])
+    mr = MoeEcRouting(*[_ptr(R.get(n)) for n, _ in MoeEcRouting._fields_])
+    _check(lib().moe_forward_expert_choice(ctypes.byref(cfg), _ptr(x), ctypes.byref(mw), _ptr(y),
+                                           ctypes.byref(mr), _ptr(stats), _ptr(workspace),
+                                           workspace.numel(), _stream()),
+           "moe_forward_expert_choice")
+
+
+class EcPlan:
+    """Pre-marshalled moe_forward_expert_choice on fixed buffers (as Plan)."""
+
+    def __init__(self, cfg, x, weights, y, ec_routing, stats, workspace):
+        forward_expert_choice(cfg, x, weights, y, ec_routing, stats, workspace)   # validates
+        self.keep = (cfg, x, weights, y, ec_routing, stats, workspace)
+        self.mw = MoeWeights(*[_ptr(weights.get(n)) for n, _ in MoeWeights._fields_])
+        self.mr = MoeEcRouting(*[_ptr(ec_routing.get(n)) for n, _ in MoeEcRouting._fields_])
+        self._fwd = (lib().moe_forward_expert_choice,
+                     (ctypes.byref(cfg), _ptr(x), ctypes.byref(self.mw), _ptr(y),
+                      ctypes.byref(self.mr), _ptr(stats), _ptr(workspace), workspace.numel()))
+
+    def forward(self, stream=None):
+        Plan._call(self._fwd, "moe_forward_expert_choice", stream)
 
 
 def _need_saved(cfg, saved):

@@ -323,6 +323,53 @@ int moe_forward(const moe_config* cfg, const void* x, const moe_weights* w, void
   return hip_status(e);
 }
 
+int moe_expert_choice_capacity(const moe_config* cfg, int64_t* capacity_out) {
+  const int v = validate(cfg);
+  if (v != MOE_OK) return v;
+  if (!capacity_out) return MOE_ERR_INVALID_ARG;
+  *capacity_out = expert_choice_capacity(*cfg, capacity_exact(*cfg));
+  return MOE_OK;
+}
+
+static int validate_ec(const moe_config* c) {
+  const int v = validate(c);
+  if (v != MOE_OK) return v;
+  if (c->score_fn != MOE_SCORE_SOFTMAX) return MOE_ERR_UNSUPPORTED;
+  // expert rows E C + S T addressed with 32-bit row indices
+  const int64_t C = expert_choice_capacity(*c, capacity_exact(*c));
+  if ((int64_t)c->num_experts * C + (int64_t)c->num_shared_experts * c->tokens >=
+      ((int64_t)1 << 31) - 4096)
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int moe_expert_choice_workspace_size(const moe_config* cfg, size_t* bytes_out) {
+  const int v = validate_ec(cfg);
+  if (v != MOE_OK) return v;
+  if (!bytes_out) return MOE_ERR_INVALID_ARG;
+  *bytes_out = expert_choice_layout(*cfg, expert_choice_capacity(*cfg, capacity_exact(*cfg))).total;
+  return MOE_OK;
+}
+
+int moe_forward_expert_choice(const moe_config* cfg, const void* x, const moe_weights* w, void* y,
+                              const moe_ec_routing* r, moe_stats* stats, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  const int v = validate_ec(cfg);
+  if (v != MOE_OK) return v;
+  if (cfg->tokens == 0) return MOE_OK;
+  if (!x || !w || !y || !r || !stats || !workspace) return MOE_ERR_INVALID_ARG;
+  if (!r->tokens || !r->gates || !r->token_row) return MOE_ERR_INVALID_ARG;
+  if (!w->w_gate || (cfg->has_gate_bias && !w->b_gate)) return MOE_ERR_INVALID_ARG;
+  const int wv = check_weights(cfg, w->w1, w->w3, w->b1, w->w2, w->b2, w->ws1, w->ws3, w->bs1,
+                               w->ws2, w->bs2);
+  if (wv != MOE_OK) return wv;
+  const int64_t C = expert_choice_capacity(*cfg, capacity_exact(*cfg));
+  const EcLayout L = expert_choice_layout(*cfg, C);
+  if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
+  return hip_status(launch_expert_choice_forward(*cfg, L, C, x, *w, y, *r, stats,
+                                                 (char*)workspace, (hipStream_t)stream));
+}
+
 int moe_forward_train(const moe_config* cfg, const void* x, const moe_weights* w, void* y,
                       const moe_routing* r, moe_stats* stats, const moe_saved* saved,
                       void* workspace, size_t workspace_bytes, void* stream) {

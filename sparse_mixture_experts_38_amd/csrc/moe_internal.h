@@ -146,6 +146,11 @@ hipError_t launch_router_gemm(const moe_config& c, const void* x, const void* w_
                               const float* b_gate, float* partials, float* logits,
                               hipStream_t stream);
 
+// Router logits alone (VALU kernel, or the MFMA path with its partial planes).
+hipError_t launch_router_logits(const moe_config& c, const void* x, const void* w_gate,
+                                const float* b_gate, float* logits, float* router_planes,
+                                hipStream_t stream);
+
 hipError_t launch_route(const moe_config& c, const WsLayout& L, const void* x, const void* w_gate,
                         const float* b_gate, const float* e_bias, float* logits, int32_t* topk_idx,
                         float* topk_gate, moe_stats* stats, char* ws, hipStream_t stream);
@@ -175,6 +180,22 @@ hipError_t launch_expert_down(const moe_config& c, const void* h, const int32_t*
 hipError_t launch_combine(const moe_config& c, const void* y_perm, const int32_t* expert_offsets,
                           const int32_t* assign_row, const float* topk_gate, void* y,
                           hipStream_t stream);
+
+// ------------------------------------------------------------------ expert choice
+// Workspace of moe_forward_expert_choice (byte offsets); gemm_cfg is the layer
+// with top_k raised so that its row space T k + S T covers the E C expert rows.
+struct EcLayout {
+  moe_config gemm_cfg;
+  int64_t rows;
+  size_t logits, router_planes, lse, row_token, offsets, h, y_perm, total;
+};
+// C = the token-choice capacity (or ceil(k T / E) without a limit), at most T.
+int64_t expert_choice_capacity(const moe_config& c, int64_t token_choice_capacity);
+EcLayout expert_choice_layout(const moe_config& c, int64_t C);
+hipError_t launch_expert_choice_forward(const moe_config& c, const EcLayout& L, int64_t C,
+                                        const void* x, const moe_weights& w, void* y,
+                                        const moe_ec_routing& r, moe_stats* stats, char* ws,
+                                        hipStream_t stream);
 
 // ------------------------------------------------------------------ backward
 // Workspace of moe_backward (byte offsets). ldk is the row length of the

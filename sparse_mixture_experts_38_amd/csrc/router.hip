@@ -267,19 +267,16 @@ int route_lanes(int E) {
   return L;
 }
 
-hipError_t launch_route(const moe_config& c, const WsLayout& L, const void* x, const void* w_gate,
-                        const float* b_gate, const float* e_bias, float* logits, int32_t* topk_idx,
-                        float* topk_gate, moe_stats* stats, char* ws, hipStream_t s) {
+hipError_t launch_router_logits(const moe_config& c, const void* x, const void* w_gate,
+                                const float* b_gate, float* lg, float* router_planes,
+                                hipStream_t s) {
   const int E = c.num_experts;
   const int d = (int)c.d_model;
-  float* lg = logits ? logits : reinterpret_cast<float*>(ws + L.logits);
-  float* partials = reinterpret_cast<float*>(ws + L.route_partials);
   const float* bg = c.has_gate_bias ? b_gate : nullptr;
-  const float* eb = c.score_fn == MOE_SCORE_SIGMOID ? e_bias : nullptr;
   const int64_t waves = (c.tokens + 7) / 8;   // one wave per 8 tokens
   const int blocks = (int)((waves + 3) / 4 < 4096 ? (waves + 3) / 4 : 4096);
   if (router_kparts(c) > 0)
-    launch_router_gemm(c, x, w_gate, bg, reinterpret_cast<float*>(ws + L.router_planes), lg, s);
+    return launch_router_gemm(c, x, w_gate, bg, router_planes, lg, s);
   else if (c.act_dtype == MOE_BF16 && c.router_dtype == MOE_F32)
     hipLaunchKernelGGL((router_logits_kernel<bf16, float>), dim3(blocks), dim3(256), 0, s,
                        (const bf16*)x, (const float*)w_gate, bg, lg, (int64_t)c.tokens, d, E);
@@ -292,7 +289,18 @@ hipError_t launch_route(const moe_config& c, const WsLayout& L, const void* x, c
   else
     hipLaunchKernelGGL((router_logits_kernel<float, bf16>), dim3(blocks), dim3(256), 0, s,
                        (const float*)x, (const bf16*)w_gate, bg, lg, (int64_t)c.tokens, d, E);
-  hipError_t err = hipGetLastError();
+  return hipGetLastError();
+}
+
+hipError_t launch_route(const moe_config& c, const WsLayout& L, const void* x, const void* w_gate,
+                        const float* b_gate, const float* e_bias, float* logits, int32_t* topk_idx,
+                        float* topk_gate, moe_stats* stats, char* ws, hipStream_t s) {
+  const int E = c.num_experts;
+  float* lg = logits ? logits : reinterpret_cast<float*>(ws + L.logits);
+  float* partials = reinterpret_cast<float*>(ws + L.route_partials);
+  const float* eb = c.score_fn == MOE_SCORE_SIGMOID ? e_bias : nullptr;
+  hipError_t err = launch_router_logits(c, x, w_gate, b_gate, lg,
+                                        reinterpret_cast<float*>(ws + L.router_planes), s);
   if (err != hipSuccess) return err;
 
   const int Ln = route_lanes(E);

@@ -201,3 +201,32 @@ def test_backward_workspace_too_small_is_reported():
     st = lib.moe_backward(ctypes.byref(cfg), fake, ctypes.byref(w), ctypes.byref(r), fake,
                           ctypes.byref(sv), fake, 0.0, 0.0, ctypes.byref(g), fake, 16, None)
     assert st == A.MOE_ERR_WORKSPACE
+
+
+def test_expert_choice_entry_points_validate_before_any_launch(tmp_path):
+    lib = A.lib()
+    prog = tmp_path / "ecsize.c"
+    prog.write_text('#include <stdio.h>\n#include "moe.h"\n'
+                    'int main(void){printf("%zu\\n", sizeof(moe_ec_routing));return 0;}\n')
+    exe = tmp_path / "ecsize"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), str(prog), "-o", str(exe)],
+                   check=True)
+    assert int(subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout) == \
+        ctypes.sizeof(A.MoeEcRouting)
+    cfg = _base(drop_tokens=True, capacity_factor=1.25, min_capacity=4)
+    assert A.expert_choice_capacity(cfg) == O.expert_choice_capacity(64, 8, 2, 1.25, 4, True)
+    for T, E, k, cf, mc, drop in [(8192, 8, 2, 1.25, 4, True), (8192, 8, 2, 1.0, 4, False),
+                                  (10, 4, 1, 1.0, 0, False), (6, 2, 2, 4.0, 1, True),
+                                  (5, 8, 1, 1.0, 4, True), (1000, 128, 1, 2.0, 4, True)]:
+        c = A.make_config(tokens=T, d_model=256, d_ff=256, num_experts=E, top_k=k,
+                          drop_tokens=drop, capacity_factor=cf, min_capacity=mc)
+        assert A.expert_choice_capacity(c) == O.expert_choice_capacity(T, E, k, cf, mc, drop)
+    assert A.expert_choice_workspace_size(cfg) > 0
+    assert lib.moe_forward_expert_choice(ctypes.byref(cfg), None, None, None, None, None, None, 0,
+                                         None) == A.MOE_ERR_INVALID_ARG
+    sig = _base(score_fn="sigmoid")
+    assert lib.moe_forward_expert_choice(ctypes.byref(sig), None, None, None, None, None, None, 0,
+                                         None) == A.MOE_ERR_UNSUPPORTED
+    z = _base(tokens=0)
+    assert lib.moe_forward_expert_choice(ctypes.byref(z), None, None, None, None, None, None, 0,
+                                         None) == A.MOE_OK

@@ -1,0 +1,140 @@
+"""GPU parity of expert-choice routing (moe_forward_expert_choice, through the C
+ABI) against the CPU oracle: the router logits within float32 accumulation
+error; on the GPU's logits, every expert's chosen token set, the row map and
+the counts bit-exact (both sides compare the same float32 keys); gates and the
+layer output within the tolerance bar."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+from sparse_mixture_experts_38_amd import api as A
+from sparse_mixture_experts_38_amd.workloads import WORKLOADS, make_inputs
+
+from parity_util import TOL, np64, oracle_params, rel_err, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+W = WORKLOADS
+base = W["deepspeed_gpt_moe"]
+
+CASES = {
+    # DeepSpeed GPT-MoE recipe: E = 8, k = 2, cf 1.25 -> C = 313 of T = 1000
+    "gpt_moe_small": base.scaled(tokens=1000, d_model=256, d_ff=512),
+    # no capacity factor: C = k T / E
+    "gpt_moe_nodrop": base.scaled(tokens=777, d_model=256, d_ff=512, drop_tokens=False),
+    # 128 experts with N(0, 2) logit offsets: skewed scores, many tokens chosen by none
+    "many_expert": W["many_expert_train"].scaled(tokens=1536, d_model=256, d_ff=256),
+    # fp32 layer (the float32 GEMM path)
+    "tiny_fp32": W["tiny_fp32"],
+    # ReLU, bf16 gate, shared expert
+    "relu_shared": base.scaled(tokens=333, d_model=256, d_ff=256, activation="relu",
+                               router_dtype="bf16", num_shared_experts=1),
+    # d_model 2048: GEMM 1 on 256 x 256 tiles
+    "long_k": base.scaled(tokens=600, d_model=2048, d_ff=512, num_experts=4),
+    # capacity T: every expert takes every token (the soft mixture)
+    "all_tokens": base.scaled(tokens=200, d_model=256, d_ff=256, num_experts=4, top_k=2,
+                              capacity_factor=8.0),
+}
+
+
+def gpu_ec_forward(w, g, cfg=None):
+    cfg = cfg or A.make_config(w)
+    R = A.alloc_ec_routing(cfg)
+    stats = A.alloc_stats()
+    ws = A.alloc_ec_workspace(cfg)
+    y = torch.empty(w.tokens, w.d_model, dtype=g["x"].dtype, device="cuda")
+    A.forward_expert_choice(cfg, g["x"], A.weights_of(g), y, R, stats, ws)
+    torch.cuda.synchronize()
+    out = {k: v.cpu() for k, v in R.items() if v is not None}
+    out["y"] = y.cpu()
+    out["stats"] = A.read_stats(stats, w.num_experts)
+    return out
+
+
+def check_ec(w, inp, out, sample=None):
+    x = np64(inp["x"])
+    P = oracle_params(inp)
+    T, E = w.tokens, w.num_experts
+    C = O.expert_choice_capacity(T, E, w.top_k, w.capacity_factor, w.min_capacity, w.drop_tokens)
+    ref_logits = O.router_logits(x, P["w_gate"], P.get("b_gate")).astype(np.float64)
+    gl = out["logits"].numpy()
+    assert np.abs(gl - ref_logits).max() <= 2e-5 * (np.abs(ref_logits).max() + 1.0), "logits"
+    r = O.expert_choice_route(gl, C)
+    assert out["tokens"].shape == (E, C)
+    assert np.array_equal(out["tokens"].numpy(), r["tokens"]), "chosen tokens"
+    assert np.array_equal(out["token_row"].numpy(), r["row"]), "token_row"
+    np.testing.assert_allclose(out["gates"].numpy(), r["gates"], rtol=2e-5, atol=1e-7)
+    st = out["stats"]
+    assert st["capacity"] == C and st["kept"] == E * C
+    assert np.all(st["counts_pre"] == C) and np.all(st["counts_kept"] == C)
+    assert st["dropped"] == int(np.count_nonzero(r["picks"] == 0)), "unpicked tokens"
+    assert np.allclose(st["prob_mean"], r["p"].mean(axis=0), rtol=1e-4, atol=1e-7), "P_i"
+    assert abs(st["z_loss"] - np.mean(r["lse"] ** 2)) <= 1e-4 * max(1.0, abs(np.mean(r["lse"] ** 2)))
+    assert abs(st["l_aux"] - r["p"].mean(axis=0).sum()) <= 1e-4
+    if sample is None:
+        ref = O.expert_choice_forward(x, P, w, logits=gl)
+        err = rel_err(out["y"].float().numpy(), ref["y"])
+    else:
+        # only the sampled tokens, each from its own chosen experts
+        y_ref = np.zeros((len(sample), w.d_model))
+        for e in range(E):
+            rows = [(si, r["row"][t, e] - e * C) for si, t in enumerate(sample) if r["row"][t, e] >= 0]
+            if not rows:
+                continue
+            toks = np.array([sample[si] for si, _ in rows])
+            ye = O.expert_ffn(x[toks], P["w1"][e], None if P["b1"] is None else P["b1"][e],
+                              P["w2"][e], None if P["b2"] is None else P["b2"][e], w.activation)
+            for (si, i), yrow in zip(rows, ye):
+                y_ref[si] += r["gates"][e][i] * yrow
+        err = rel_err(out["y"].float().numpy()[sample], y_ref)
+    assert err <= TOL[w.act_dtype], f"layer output max rel err {err}"
+    return r, err
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_expert_choice_parity(name):
+    w = CASES[name]
+    print(f"[case] expert choice {name} T={w.tokens} d={w.d_model} F={w.d_ff} E={w.num_experts}",
+          flush=True)
+    inp = make_inputs(w, seed=0, device="cpu")
+    out = gpu_ec_forward(w, to_gpu(inp))
+    r, err = check_ec(w, inp, out)
+    print(f"  C={r['tokens'].shape[1]} unpicked={int((r['picks'] == 0).sum())} err={err:.2e}",
+          flush=True)
+    if name == "many_expert":
+        assert (r["picks"] == 0).sum() > 0
+    if name == "all_tokens":
+        assert r["tokens"].shape[1] == w.tokens and (r["picks"] == w.num_experts).all()
+
+
+def test_expert_choice_ties_go_to_the_lower_token():
+    """W_g = 0 and no gate bias: every logit is 0, so each expert takes tokens 0 .. C-1."""
+    w = base.scaled(tokens=300, d_model=256, d_ff=256, num_experts=4, top_k=1)
+    print("[case] expert choice all ties", flush=True)
+    inp = make_inputs(w, seed=1, device="cpu")
+    inp["w_gate"] = torch.zeros_like(inp["w_gate"])
+    out = gpu_ec_forward(w, to_gpu(inp))
+    C = out["tokens"].shape[1]
+    assert np.array_equal(out["tokens"].numpy(), np.tile(np.arange(C), (4, 1)))
+    check_ec(w, inp, out)
+
+
+def test_expert_choice_deterministic():
+    w = CASES["many_expert"]
+    print("[case] expert choice determinism", flush=True)
+    inp = to_gpu(make_inputs(w, seed=2, device="cpu"))
+    a, b = gpu_ec_forward(w, inp), gpu_ec_forward(w, inp)
+    for k in ("tokens", "gates", "token_row", "y"):
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_expert_choice_full_size_sampled():
+    w = W["deepspeed_gpt_moe"]
+    print("[case] expert choice full-size deepspeed_gpt_moe", flush=True)
+    inp = make_inputs(w, seed=0, device="cuda")
+    out = gpu_ec_forward(w, inp)
+    rng = np.random.default_rng(0)
+    sample = np.sort(rng.choice(w.tokens, 96, replace=False))
+    r, err = check_ec(w, inp, out, sample=sample)
+    assert r["tokens"].shape[1] == 2560
