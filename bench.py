@@ -10,8 +10,8 @@ rotated so the 256 MB Infinity Cache does not hold the previous step's
 operands. The stage entry points are then run over the same sets with HIP
 events around the two grouped GEMMs, for the roofline figure. Then, where the
 layer has a backward in this build, one training step (moe_forward_train +
-moe_backward) is timed the same way and reported under "train". Prints one
-JSON line.
+moe_backward) is timed the same way and reported under "train", and the layer
+with expert-choice routing under "expert_choice". Prints one JSON line.
 """
 import argparse
 import ctypes
@@ -103,6 +103,8 @@ def main():
     ap.add_argument("--workload", default="deepspeed_gpt_moe")
     ap.add_argument("--sets", type=int, default=3, help="rotated input/weight sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-expert-choice", action="store_true",
+                    help="skip the expert-choice routing measurement")
     ap.add_argument("--no-train", action="store_true",
                     help="skip the training-step measurement (moe_forward_train + moe_backward)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -219,6 +221,10 @@ def main():
         "kept_rows": rows,
         "wall_s": wall,
     }
+    if not args.no_expert_choice and A.lib().moe_expert_choice_workspace_size(
+            ctypes.byref(cfg), ctypes.byref(ctypes.c_size_t(0))) == A.MOE_OK:
+        result["expert_choice"] = expert_choice_step(A, torch, w, cfg, sets, args.steps,
+                                                     args.warmup)
     if not args.no_train and A.lib().moe_backward_workspace_size(
             ctypes.byref(cfg), ctypes.byref(ctypes.c_size_t(0))) == A.MOE_OK:
         del plans
@@ -226,6 +232,33 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, sets[0])
     print(json.dumps(result), flush=True)
+
+
+def expert_choice_step(A, torch, w, cfg, sets, steps, warmup):
+    """The same layer with expert-choice routing (moe_forward_expert_choice): every
+    expert takes C tokens, so its GEMMs run on E C rows (algorithmic FLOPs
+    2 x 2 E C d F)."""
+    T, d, F, E = w.tokens, w.d_model, w.d_ff, w.num_experts
+    act = A.TORCH_DTYPE[cfg.act_dtype]
+    C = A.expert_choice_capacity(cfg)
+    ws = A.alloc_ec_workspace(cfg)
+    plans = [A.EcPlan(cfg, s["x"], A.weights_of(s), torch.empty(T, d, dtype=act, device="cuda"),
+                      A.alloc_ec_routing(cfg, logits=False), A.alloc_stats(), ws) for s in sets]
+    for i in range(warmup):
+        plans[i % len(plans)].forward()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        plans[i % len(plans)].forward()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    st = A.read_stats(plans[0].keep[5], E)
+    flop = 2 * 2.0 * E * C * d * F * (1.5 if w.activation == "swiglu" else 1.0)
+    return {"ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3), "capacity": C,
+            "expert_rows": E * C, "unpicked_tokens": st["dropped"],
+            "gemm_tflops_over_step": flop / (ms * 1e-3) / 1e12}
 
 
 def train_step(A, torch, w, cfg, sets, ws, steps, warmup, rows):

@@ -20,50 +20,79 @@ __device__ __forceinline__ uint32_t score_key(float f) {
 }
 
 // Per token: lse[t] = logsumexp of its logits; the (t, e) -> row map cleared to
-// -1; with a shared expert, row E C + t takes token t.
+// -1; with a shared expert, row E C + t takes token t. Each block writes the
+// float64 sum of its tokens' lse^2 to zpart[block] (z-loss).
 __global__ __launch_bounds__(256) void ec_lse_kernel(const float* __restrict__ logits, int64_t T,
                                                      int E, int64_t C, int S,
                                                      float* __restrict__ lse,
                                                      int32_t* __restrict__ token_row,
-                                                     int32_t* __restrict__ rows) {
+                                                     int32_t* __restrict__ rows,
+                                                     double* __restrict__ zpart) {
+  __shared__ double red[256];
   const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (t >= T) return;
-  const float* h = logits + t * E;
-  float m = -INFINITY;
-  for (int e = 0; e < E; ++e) m = fmaxf(m, h[e]);
-  float s = 0.f;
-  for (int e = 0; e < E; ++e) s += expf(h[e] - m);
-  lse[t] = m + logf(s);
-  for (int e = 0; e < E; ++e) token_row[t * E + e] = -1;
-  if (S) rows[(int64_t)E * C + t] = (int32_t)t;
+  double z = 0.0;
+  if (t < T) {
+    const float* h = logits + t * E;
+    float m = -INFINITY;
+    for (int e = 0; e < E; ++e) m = fmaxf(m, h[e]);
+    float s = 0.f;
+    for (int e = 0; e < E; ++e) s += expf(h[e] - m);
+    const float l = m + logf(s);
+    lse[t] = l;
+    z = (double)l * (double)l;
+    for (int e = 0; e < E; ++e) token_row[t * E + e] = -1;
+    if (S) rows[(int64_t)E * C + t] = (int32_t)t;
+  }
+  red[threadIdx.x] = z;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) zpart[blockIdx.x] = red[0];
 }
 
-// Block-wide exclusive prefix of a 0/1 flag over 256 threads (4 wavefronts) via
-// ballots; returns the prefix and writes the block total to *total.
-__device__ __forceinline__ int block_flag_scan(bool flag, int* wave_tot, int* total) {
+// Block-wide exclusive prefix sum of one int per thread (256 threads, 4
+// wavefronts): wave scans by shuffles, then the wave totals. Returns the prefix
+// and writes the block total to *total.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* wave_tot, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint64_t bal = __ballot(flag);
-  const int in_wave = __popcll(bal & ((1ull << lane) - 1ull));
-  if (lane == 0) wave_tot[wave] = __popcll(bal);
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += u;
+  }
+  if (lane == 63) wave_tot[wave] = incl;
   __syncthreads();
   int before = 0;
   for (int w = 0; w < wave; ++w) before += wave_tot[w];
   *total = wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
   __syncthreads();   // wave_tot is reused by the next call
-  return before + in_wave;
+  return before + incl - v;
 }
 
+__device__ __forceinline__ float key_score(uint32_t u) {
+  return __uint_as_float((u & 0x80000000u) ? (u ^ 0x80000000u) : ~u);
+}
+
+constexpr int kEcLdsKeys = 16384;   // keys and lse of one expert kept in LDS (128 KB)
+
 // One block per expert e: the C tokens with the largest key(logits[t][e]), ties
-// to the lower token. An exact radix select over four 8-bit digits finds the
-// C-th largest key K and how many tokens equal to K to take; one ordered pass
-// over the tokens (256 per round, ballot scans) then writes the chosen tokens in
-// ascending order: tokens[e][i] = t, gates[e][i] = p[t][e], token_row[t][e] =
-// e C + i, rows[e C + i] = t. It also writes P_e (mean of p[t][e], float64
-// tree) and the balance counts of expert e into stats.
+// to the lower token. The expert's keys are staged in LDS when T <= 16384 (else
+// read from L2). An exact radix select over four 8-bit digits finds the C-th
+// largest key K and how many tokens equal to K to take. Then each thread takes a
+// contiguous range of tokens (lse staged in LDS with the keys): two block scans (of its count of keys equal to K,
+// then of its count of taken tokens) place its chosen tokens in ascending order:
+// tokens[e][i] = t, gates[e][i] = p[t][e], token_row[t][e] = e C + i,
+// rows[e C + i] = t. It also writes P_e (mean of p[t][e], float64 tree) and the
+// balance counts of expert e into stats.
 __global__ __launch_bounds__(256) void ec_select_kernel(
     const float* __restrict__ logits, const float* __restrict__ lse, int64_t T, int E, int64_t C,
     int32_t* __restrict__ tokens, float* __restrict__ gates, int32_t* __restrict__ token_row,
     int32_t* __restrict__ rows, moe_stats* __restrict__ stats) {
+  __shared__ uint32_t keys[kEcLdsKeys];
+  __shared__ float lse_s[kEcLdsKeys];
   __shared__ int hist[256];
   __shared__ int wave_tot[4];
   __shared__ uint32_t s_prefix;
@@ -71,27 +100,51 @@ __global__ __launch_bounds__(256) void ec_select_kernel(
   __shared__ double red[256];
   const int e = blockIdx.x;
   const int tid = threadIdx.x;
+  const bool in_lds = T <= kEcLdsKeys;
+  auto key_at = [&](int64_t t) -> uint32_t {
+    return in_lds ? keys[t] : score_key(logits[t * E + e]);
+  };
+  auto lse_at = [&](int64_t t) -> float { return in_lds ? lse_s[t] : lse[t]; };
+  if (in_lds) {
+    // eight loads in flight per thread
+    for (int64_t t0 = 0; t0 < T; t0 += 8 * 256) {
+      float v[8], l[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t t = t0 + u * 256 + tid;
+        v[u] = t < T ? logits[t * E + e] : 0.f;
+        l[u] = t < T ? lse[t] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t t = t0 + u * 256 + tid;
+        if (t < T) {
+          keys[t] = score_key(v[u]);
+          lse_s[t] = l[u];
+        }
+      }
+    }
+  }
   uint32_t prefix = 0, mask = 0;
   int remaining = (int)C;
   for (int shift = 24; shift >= 0; shift -= 8) {
     hist[tid] = 0;
     __syncthreads();
     for (int64_t t = tid; t < T; t += 256) {
-      const uint32_t u = score_key(logits[t * E + e]);
+      const uint32_t u = key_at(t);
       if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1);
     }
     __syncthreads();
-    if (tid == 0) {
-      int cum = 0, D = 0;
-      for (int dg = 255; dg >= 0; --dg) {
-        if (cum + hist[dg] >= remaining) {
-          D = dg;
-          break;
-        }
-        cum += hist[dg];
-      }
-      s_prefix = prefix | ((uint32_t)D << shift);
-      s_remaining = remaining - cum;
+    // digits in descending order, thread i holding digit 255 - i: the digit D is
+    // the one at which the running count of larger-or-equal digits first
+    // reaches `remaining`
+    const int dg = 255 - tid;
+    const int cnt = hist[dg];
+    int tot = 0;
+    const int above = block_exclusive_scan(cnt, wave_tot, &tot);
+    if (above < remaining && above + cnt >= remaining) {
+      s_prefix = prefix | ((uint32_t)dg << shift);
+      s_remaining = remaining - above;
     }
     __syncthreads();
     prefix = s_prefix;
@@ -99,34 +152,40 @@ __global__ __launch_bounds__(256) void ec_select_kernel(
     mask |= 0xFFu << shift;
   }
   // prefix = K; remaining = tokens with key == K to take (lowest tokens first)
-  int taken_base = 0, eq_base = 0;
+  const int64_t chunk = (T + 255) / 256;
+  const int64_t lo = tid * chunk < T ? tid * chunk : T;
+  const int64_t hi = lo + chunk < T ? lo + chunk : T;
+  int n_gt = 0, n_eq = 0;
+  for (int64_t t = lo; t < hi; ++t) {
+    const uint32_t u = key_at(t);
+    n_gt += u > prefix;
+    n_eq += u == prefix;
+  }
+  int tot = 0;
+  const int eq_before = block_exclusive_scan(n_eq, wave_tot, &tot);
+  int eq_take = remaining - eq_before;
+  eq_take = eq_take < 0 ? 0 : (eq_take > n_eq ? n_eq : eq_take);
+  const int pos0 = block_exclusive_scan(n_gt + eq_take, wave_tot, &tot);
+  int pos = pos0, eq_seen = 0;
   double psum = 0.0;
-  for (int64_t t0 = 0; t0 < T; t0 += 256) {
-    const int64_t t = t0 + tid;
-    uint32_t u = 0;
-    float p = 0.f;
-    if (t < T) {
-      const float h = logits[t * E + e];
-      u = score_key(h);
-      p = expf(h - lse[t]);
-      psum += (double)p;
+  for (int64_t t = lo; t < hi; ++t) {
+    const uint32_t u = key_at(t);
+    const float h = key_score(u);
+    const float p = expf(h - lse_at(t));
+    psum += (double)p;
+    bool take = u > prefix;
+    if (u == prefix) {
+      take = eq_seen < eq_take;
+      ++eq_seen;
     }
-    const bool gt = t < T && u > prefix;
-    const bool eq = t < T && u == prefix;
-    int eq_total = 0;
-    const int eq_rank = eq_base + block_flag_scan(eq, wave_tot, &eq_total);
-    const bool take = gt || (eq && eq_rank < remaining);
-    int take_total = 0;
-    const int pos = taken_base + block_flag_scan(take, wave_tot, &take_total);
     if (take && pos < C) {
       const int64_t r = (int64_t)e * C + pos;
       tokens[r] = (int32_t)t;
       gates[r] = p;
       token_row[t * E + e] = (int32_t)r;
       rows[r] = (int32_t)t;
+      ++pos;
     }
-    eq_base += eq_total;
-    taken_base += take_total;
   }
   red[tid] = psum;
   __syncthreads();
@@ -142,16 +201,15 @@ __global__ __launch_bounds__(256) void ec_select_kernel(
   }
 }
 
-// One block: group offsets (e C; the shared group after E C), the z-loss, the
-// number of tokens no expert chose (reported as "dropped"), L_aux from the P_i
-// (= sum_i P_i, since every f_i = 1 / E), zeroed unused expert slots.
-__global__ __launch_bounds__(256) void ec_finalize_kernel(const float* __restrict__ lse,
-                                                          const int32_t* __restrict__ token_row,
-                                                          int64_t T, int E, int64_t C, int S,
-                                                          int32_t* __restrict__ offsets,
+// One block: group offsets (e C; the shared group after E C), the z-loss from
+// the per-block partials of ec_lse_kernel (added in block order), L_aux from
+// the P_i (= sum_i P_i, since every f_i = 1 / E), the unpicked-token count
+// zeroed for ec_combine_kernel to add to, and the unused expert slots cleared.
+__global__ __launch_bounds__(256) void ec_finalize_kernel(const double* __restrict__ zpart,
+                                                          int nzpart, int64_t T, int E, int64_t C,
+                                                          int S, int32_t* __restrict__ offsets,
                                                           moe_stats* __restrict__ stats) {
   __shared__ double red[256];
-  __shared__ int cnt[256];
   const int tid = threadIdx.x;
   for (int g = tid; g <= E + S; g += 256)
     offsets[g] = (int32_t)(g <= E ? (int64_t)g * C : (int64_t)E * C + T);
@@ -162,22 +220,11 @@ __global__ __launch_bounds__(256) void ec_finalize_kernel(const float* __restric
     stats->prob_mean[e] = 0.f;
   }
   double z = 0.0;
-  int unpicked = 0;
-  for (int64_t t = tid; t < T; t += 256) {
-    const double l = (double)lse[t];
-    z += l * l;
-    bool any = false;
-    for (int e = 0; e < E; ++e) any |= token_row[t * E + e] >= 0;
-    unpicked += any ? 0 : 1;
-  }
+  for (int b = tid; b < nzpart; b += 256) z += zpart[b];
   red[tid] = z;
-  cnt[tid] = unpicked;
   __syncthreads();
   for (int w = 128; w > 0; w >>= 1) {
-    if (tid < w) {
-      red[tid] += red[tid + w];
-      cnt[tid] += cnt[tid + w];
-    }
+    if (tid < w) red[tid] += red[tid + w];
     __syncthreads();
   }
   if (tid == 0) {
@@ -187,7 +234,7 @@ __global__ __launch_bounds__(256) void ec_finalize_kernel(const float* __restric
     stats->l_aux = (float)laux;   // E sum_i f_i P_i with f_i = 1 / E
     stats->capacity = (int32_t)C;
     stats->kept = (int32_t)((int64_t)E * C);
-    stats->dropped = cnt[0];
+    stats->dropped = 0;
   }
 }
 
@@ -199,11 +246,17 @@ __global__ __launch_bounds__(256) void ec_combine_kernel(const T_* __restrict__ 
                                                          const int32_t* __restrict__ token_row,
                                                          const float* __restrict__ gates,
                                                          int64_t T, int d, int E, int64_t C, int S,
-                                                         T_* __restrict__ y) {
+                                                         T_* __restrict__ y,
+                                                         moe_stats* __restrict__ stats) {
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (t >= T) return;
   const int64_t nrows = (int64_t)E * C;
+  // tokens no expert chose are counted into stats->dropped (integer sum)
+  bool picked = false;
+  for (int e = lane; e < E; e += 64) picked |= token_row[t * E + e] >= 0;
+  const uint64_t any_picked = __ballot(picked);   // every lane takes part in the ballot
+  if (lane == 0 && any_picked == 0ull) atomicAdd(&stats->dropped, 1);
   for (int c = lane * 8; c < d; c += 512) {
     float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int e = 0; e < E; ++e) {
@@ -250,6 +303,7 @@ EcLayout expert_choice_layout(const moe_config& c, int64_t C) {
   L.logits = take((size_t)T * E * 4);
   L.router_planes = take((size_t)router_kparts(c) * T * E * 4);
   L.lse = take((size_t)T * 4);
+  L.zpart = take((size_t)((T + 255) / 256) * 8);
   L.row_token = take((size_t)L.rows * 4);
   L.offsets = take((size_t)(E + S + 1) * 4);
   const size_t es = c.act_dtype == MOE_BF16 ? 2 : 4;
@@ -271,12 +325,14 @@ hipError_t launch_expert_choice_forward(const moe_config& c, const EcLayout& L, 
   int32_t* off = (int32_t*)(ws + L.offsets);
   hipError_t e = launch_router_logits(c, x, w.w_gate, w.b_gate, lg, (float*)(ws + L.router_planes), s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(ec_lse_kernel, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, s,
-                     (const float*)lg, T, E, C, S, lse, r.token_row, rows);
+  const unsigned lb = (unsigned)((T + 255) / 256);
+  double* zpart = (double*)(ws + L.zpart);
+  hipLaunchKernelGGL(ec_lse_kernel, dim3(lb), dim3(256), 0, s, (const float*)lg, T, E, C, S, lse,
+                     r.token_row, rows, zpart);
   hipLaunchKernelGGL(ec_select_kernel, dim3(E), dim3(256), 0, s, (const float*)lg,
                      (const float*)lse, T, E, C, r.tokens, r.gates, r.token_row, rows, stats);
-  hipLaunchKernelGGL(ec_finalize_kernel, dim3(1), dim3(256), 0, s, (const float*)lse,
-                     (const int32_t*)r.token_row, T, E, C, S, off, stats);
+  hipLaunchKernelGGL(ec_finalize_kernel, dim3(1), dim3(256), 0, s, (const double*)zpart, (int)lb,
+                     T, E, C, S, off, stats);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const ExpertWeights ew{w.w1, w.w3, w.w2, w.b1, w.b2, w.ws1, w.ws3, w.ws2, w.bs1, w.bs2};
@@ -290,11 +346,12 @@ hipError_t launch_expert_choice_forward(const moe_config& c, const EcLayout& L, 
   const int d = (int)c.d_model;
   if (c.act_dtype == MOE_BF16)
     hipLaunchKernelGGL((ec_combine_kernel<bf16>), dim3(tb), dim3(256), 0, s, (const bf16*)yp,
-                       (const int32_t*)r.token_row, (const float*)r.gates, T, d, E, C, S, (bf16*)y);
+                       (const int32_t*)r.token_row, (const float*)r.gates, T, d, E, C, S, (bf16*)y,
+                       stats);
   else
     hipLaunchKernelGGL((ec_combine_kernel<float>), dim3(tb), dim3(256), 0, s, (const float*)yp,
                        (const int32_t*)r.token_row, (const float*)r.gates, T, d, E, C, S,
-                       (float*)y);
+                       (float*)y, stats);
   return hipGetLastError();
 }
 

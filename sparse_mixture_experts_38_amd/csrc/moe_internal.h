@@ -187,7 +187,7 @@ hipError_t launch_combine(const moe_config& c, const void* y_perm, const int32_t
 struct EcLayout {
   moe_config gemm_cfg;
   int64_t rows;
-  size_t logits, router_planes, lse, row_token, offsets, h, y_perm, total;
+  size_t logits, router_planes, lse, zpart, row_token, offsets, h, y_perm, total;
 };
 // C = the token-choice capacity (or ceil(k T / E) without a limit), at most T.
 int64_t expert_choice_capacity(const moe_config& c, int64_t token_choice_capacity);
