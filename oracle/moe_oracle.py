@@ -722,3 +722,63 @@ def expert_choice_forward(x, params, w, logits=None) -> Dict[str, object]:
     stats = dict(capacity=C, P=r["p"].mean(axis=0), z_loss=float(np.mean(r["lse"] ** 2)),
                  unpicked=int(np.count_nonzero(r["picks"] == 0)), max_picks=int(r["picks"].max()))
     return dict(logits=np.asarray(logits, F32), y=y, Y=Y, stats=stats, C=C, **r)
+
+
+# --------------------------------------------------------------------------
+# Auxiliary-loss-free balancing: the selection-bias update
+# --------------------------------------------------------------------------
+def update_selection_bias(e_bias, counts_pre, tokens: int, top_k: int, gamma: float) -> np.ndarray:
+    """One update of the sigmoid router's selection bias b_i.
+
+    MoE From Scratch to DeepSeek V3, auxiliary-loss-free balancing: b_i is lowered
+    when expert i is overloaded and raised when it is idle.
+    READING: "overloaded" / "idle" compare the expert's top-k picks (before
+    capacity) with the mean load T k / E, exactly (in integers: c_i E against
+    T k); the step is a caller-given gamma (the pages give none), b_i <- b_i -
+    gamma sign(c_i - T k / E), evaluated in float32 (the bias is a float32
+    router quantity).
+    """
+    b = np.asarray(e_bias, F32).copy()
+    c = np.asarray(counts_pre, np.int64)
+    E = b.shape[0]
+    s = np.sign(c * E - tokens * top_k)            # exact: +1 over, -1 under, 0 at the mean
+    return (b - F32(gamma) * s.astype(F32)).astype(F32)
+
+
+# --------------------------------------------------------------------------
+# Hash routing
+# --------------------------------------------------------------------------
+def hash_route(token_ids, table) -> np.ndarray:
+    """Expert of each token from a fixed token-id -> expert map.
+
+    Moe(Mixtrue of Experts) survey: hash-based routing fixes the token -> expert
+    mapping in advance (no gating network), which removes the fluctuation of a
+    learned router; its "Hash layers for large sparse models" entry routes each
+    token by hashing it.
+    READING: the map is a table indexed by token id, given by the caller (how it
+    is generated is the caller's choice); one expert per token (k = 1) with gate
+    1. Ids outside [0, V) and table entries outside [0, E) are clamped (the
+    library has to stay memory-safe on any input).
+    """
+    ids = np.clip(np.asarray(token_ids, np.int64), 0, len(table) - 1)
+    return np.asarray(table, np.int64)[ids].reshape(-1, 1)
+
+
+def hash_forward(x, params, w, token_ids, table) -> Dict[str, object]:
+    """The layer with hash routing: idx = table[token id] (k = 1, gate 1), then
+    the capacity-limited dispatch, the experts and the combine of the token-choice
+    layer (plus the shared expert). No router: P_i and the z-loss are 0."""
+    x = np.asarray(x, F64)
+    T, d = x.shape
+    E = w.num_experts
+    idx = np.clip(hash_route(token_ids, table), 0, E - 1)
+    gates = np.ones((T, 1), F64)
+    cap = capacity(T, E, 1, w.capacity_factor, w.min_capacity, w.drop_tokens)
+    disp = dispatch(idx, E, cap)
+    Y = experts_forward(x, disp, params, w.activation)
+    y_shared = None
+    if w.num_shared_experts:
+        y_shared = expert_ffn(x, params["ws1"][0], _opt(params.get("bs1"), 0), params["ws2"][0],
+                              _opt(params.get("bs2"), 0), w.activation, _opt(params.get("ws3"), 0))
+    y = combine(Y, gates, disp["assign_row"], T, d, y_shared)
+    return dict(idx=idx.astype(np.int32), gates=gates, y=y, Y=Y, capacity=cap, **disp)
