@@ -274,6 +274,43 @@ int moe_forward(const moe_config* cfg, const void* x, const moe_weights* w, void
                 const moe_routing* routing, moe_stats* stats, void* workspace,
                 size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------ balancing, hash routing */
+
+/*
+ * One update of the sigmoid router's selection bias ([P4] auxiliary-loss-free
+ * balancing: b_i is lowered when expert i is overloaded and raised when it is
+ * idle): e_bias[i] -= gamma * sign(c_i E - T k), with c_i = stats->counts_pre[i]
+ * (top-k picks before capacity, as moe_permute / moe_forward wrote them) and T k /
+ * E the mean load, compared exactly in integers; float32 arithmetic. The step
+ * gamma is the caller's (the pages give none).
+ *   stats   device moe_stats of the routing step to balance
+ *   e_bias  [E] float32 device buffer, updated in place
+ */
+int moe_update_selection_bias(const moe_config* cfg, const moe_stats* stats, float* e_bias,
+                              float gamma, void* stream);
+
+/*
+ * Hash routing ([P5] hash-based routing: a token -> expert map fixed in advance
+ * replaces the gating network): topk_idx[t] = table[token_ids[t]], topk_gate[t]
+ * = 1, for a layer with top_k == 1 (other k: MOE_ERR_UNSUPPORTED). Ids outside
+ * [0, table_size) and table entries outside [0, E) are clamped. Writes
+ * stats->prob_mean = 0 and stats->z_loss = 0 (no router).
+ *   token_ids [T] int32;  table [table_size] int32;  topk_idx, topk_gate [T, 1]
+ */
+int moe_route_hash(const moe_config* cfg, const int32_t* token_ids, const int32_t* table,
+                   int64_t table_size, int32_t* topk_idx, float* topk_gate, moe_stats* stats,
+                   void* stream);
+
+/*
+ * The layer forward with hash routing: moe_route_hash, then moe_permute,
+ * moe_expert_ffn and moe_combine as in moe_forward (capacity applies; the gate
+ * weights are not read and may be NULL; routing->logits is not written).
+ */
+int moe_forward_hash(const moe_config* cfg, const void* x, const int32_t* token_ids,
+                     const int32_t* table, int64_t table_size, const moe_weights* w, void* y,
+                     const moe_routing* routing, moe_stats* stats, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------ expert choice
  * Expert-choice routing ([P1] "2. Routing Mechanisms", expert choice routing;
  * [P4] routing strategies; [P5] expert-choice routing): every expert takes its

@@ -103,6 +103,10 @@ def lib():
     L.moe_combine.argtypes = [cfgp, P, P, P, P, P, P]
     L.moe_forward.argtypes = [cfgp, P, ctypes.POINTER(MoeWeights), P, ctypes.POINTER(MoeRouting),
                               P, P, c_size_t, P]
+    L.moe_update_selection_bias.argtypes = [cfgp, P, P, ctypes.c_float, P]
+    L.moe_route_hash.argtypes = [cfgp, P, P, c_int64, P, P, P, P]
+    L.moe_forward_hash.argtypes = [cfgp, P, P, P, c_int64, ctypes.POINTER(MoeWeights), P,
+                                   ctypes.POINTER(MoeRouting), P, P, c_size_t, P]
     L.moe_expert_choice_capacity.argtypes = [cfgp, ctypes.POINTER(c_int64)]
     L.moe_expert_choice_workspace_size.argtypes = [cfgp, ctypes.POINTER(c_size_t)]
     L.moe_forward_expert_choice.argtypes = [cfgp, P, ctypes.POINTER(MoeWeights), P,
@@ -118,7 +122,8 @@ def lib():
                  "moe_permute", "moe_expert_ffn", "moe_expert_up", "moe_expert_down",
                  "moe_combine", "moe_forward", "moe_forward_train", "moe_backward_workspace_size",
                  "moe_backward", "moe_expert_choice_capacity", "moe_expert_choice_workspace_size",
-                 "moe_forward_expert_choice"):
+                 "moe_forward_expert_choice", "moe_update_selection_bias", "moe_route_hash",
+                 "moe_forward_hash"):
         getattr(L, name).restype = c_int
     _lib = L
     return L
@@ -380,6 +385,53 @@ def forward(cfg, x, weights: Dict[str, Optional[torch.Tensor]], y, routing: Dict
     _check(lib().moe_forward(ctypes.byref(cfg), _ptr(x), ctypes.byref(mw), _ptr(y), ctypes.byref(mr),
                              _ptr(stats), _ptr(workspace), workspace.numel(), _stream()),
            "moe_forward")
+
+
+def update_selection_bias(cfg, stats, e_bias, gamma):
+    """moe_update_selection_bias: e_bias -= gamma sign(c_i E - T k), in place."""
+    _need_stats(stats)
+    _need(e_bias, "e_bias", (cfg.num_experts,), torch.float32)
+    _check(lib().moe_update_selection_bias(ctypes.byref(cfg), _ptr(stats), _ptr(e_bias),
+                                           float(gamma), _stream()), "moe_update_selection_bias")
+
+
+def _need_hash(cfg, token_ids, table):
+    _need(token_ids, "token_ids", (cfg.tokens,), torch.int32)
+    if table is None or table.dim() != 1 or table.numel() == 0:
+        raise ValueError("table must be a non-empty 1-D tensor")
+    _need(table, "table", (table.numel(),), torch.int32)
+
+
+def route_hash(cfg, token_ids, table, topk_idx, topk_gate, stats):
+    """moe_route_hash: topk_idx = table[token_ids], gate 1 (k = 1)."""
+    _need_hash(cfg, token_ids, table)
+    _need(topk_idx, "topk_idx", (cfg.tokens, cfg.top_k), torch.int32)
+    _need(topk_gate, "topk_gate", (cfg.tokens, cfg.top_k), torch.float32)
+    _need_stats(stats)
+    _check(lib().moe_route_hash(ctypes.byref(cfg), _ptr(token_ids), _ptr(table), table.numel(),
+                                _ptr(topk_idx), _ptr(topk_gate), _ptr(stats), _stream()),
+           "moe_route_hash")
+
+
+def forward_hash(cfg, x, token_ids, table, weights, y, routing, stats, workspace):
+    """moe_forward_hash: hash routing, then dispatch, experts and combine."""
+    T, d, F, E, k, S, act, rdt = _sizes(cfg)
+    _need(x, "x", (T, d), act)
+    _need(y, "y", (T, d), act)
+    _need_hash(cfg, token_ids, table)
+    W = dict(weights)
+    W["w_gate"] = W.get("w_gate")
+    _need(W["w1"], "w1", (E, F, d), act)
+    _need(W["w2"], "w2", (E, d, F), act)
+    _need_routing(cfg, routing)
+    _need_stats(stats)
+    _need_ws(workspace)
+    mw = MoeWeights(*[_ptr(W.get(n)) for n, _ in MoeWeights._fields_])
+    mr = MoeRouting(*[_ptr(routing.get(n)) for n, _ in MoeRouting._fields_])
+    _check(lib().moe_forward_hash(ctypes.byref(cfg), _ptr(x), _ptr(token_ids), _ptr(table),
+                                  table.numel(), ctypes.byref(mw), _ptr(y), ctypes.byref(mr),
+                                  _ptr(stats), _ptr(workspace), workspace.numel(), _stream()),
+           "moe_forward_hash")
 
 
 def expert_choice_capacity(cfg: MoeConfig) -> int:

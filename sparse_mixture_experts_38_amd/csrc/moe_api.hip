@@ -323,6 +323,62 @@ int moe_forward(const moe_config* cfg, const void* x, const moe_weights* w, void
   return hip_status(e);
 }
 
+int moe_update_selection_bias(const moe_config* cfg, const moe_stats* stats, float* e_bias,
+                              float gamma, void* stream) {
+  const int v = validate(cfg);
+  if (v != MOE_OK) return v;
+  if (!stats || !e_bias) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_bias_update(*cfg, stats, e_bias, gamma, (hipStream_t)stream));
+}
+
+int moe_route_hash(const moe_config* cfg, const int32_t* token_ids, const int32_t* table,
+                   int64_t table_size, int32_t* topk_idx, float* topk_gate, moe_stats* stats,
+                   void* stream) {
+  const int v = validate(cfg);
+  if (v != MOE_OK) return v;
+  if (cfg->top_k != 1) return MOE_ERR_UNSUPPORTED;
+  if (cfg->tokens == 0) return MOE_OK;
+  if (!token_ids || !table || table_size <= 0 || !topk_idx || !topk_gate || !stats)
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_hash_route(*cfg, token_ids, table, table_size, topk_idx, topk_gate,
+                                      stats, (hipStream_t)stream));
+}
+
+int moe_forward_hash(const moe_config* cfg, const void* x, const int32_t* token_ids,
+                     const int32_t* table, int64_t table_size, const moe_weights* w, void* y,
+                     const moe_routing* r, moe_stats* stats, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  const int v = validate(cfg);
+  if (v != MOE_OK) return v;
+  if (cfg->top_k != 1) return MOE_ERR_UNSUPPORTED;
+  if (cfg->tokens == 0) return MOE_OK;
+  if (!x || !token_ids || !table || table_size <= 0 || !w || !y || !r || !stats || !workspace)
+    return MOE_ERR_INVALID_ARG;
+  if (!r->topk_idx || !r->topk_gate || !r->expert_offsets || !r->row_token || !r->assign_row)
+    return MOE_ERR_INVALID_ARG;
+  const int wv = check_weights(cfg, w->w1, w->w3, w->b1, w->w2, w->b2, w->ws1, w->ws3, w->bs1,
+                               w->ws2, w->bs2);
+  if (wv != MOE_OK) return wv;
+  const WsLayout L = workspace_layout(*cfg);
+  if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
+  char* ws = (char*)workspace;
+  const hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_hash_route(*cfg, token_ids, table, table_size, r->topk_idx, r->topk_gate,
+                                   stats, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = launch_permute(*cfg, L, capacity_exact(*cfg), r->topk_idx, x, r->expert_offsets,
+                     r->row_token, r->assign_row, nullptr, stats, ws, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  const ExpertWeights ew{w->w1, w->w3, w->w2, w->b1, w->b2, w->ws1, w->ws3, w->ws2, w->bs1, w->bs2};
+  void* h = ws + L.h;
+  e = launch_expert_up(*cfg, x, r->expert_offsets, ew, h, s, r->row_token);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = launch_expert_down(*cfg, h, r->expert_offsets, ew, ws + L.y_perm, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(launch_combine(*cfg, ws + L.y_perm, r->expert_offsets, r->assign_row,
+                                   r->topk_gate, y, s));
+}
+
 int moe_expert_choice_capacity(const moe_config* cfg, int64_t* capacity_out) {
   const int v = validate(cfg);
   if (v != MOE_OK) return v;

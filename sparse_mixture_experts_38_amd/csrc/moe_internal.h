@@ -181,6 +181,13 @@ hipError_t launch_combine(const moe_config& c, const void* y_perm, const int32_t
                           const int32_t* assign_row, const float* topk_gate, void* y,
                           hipStream_t stream);
 
+// ------------------------------------------------------------------ balancing, hash routing
+hipError_t launch_bias_update(const moe_config& c, const moe_stats* stats, float* e_bias,
+                              float gamma, hipStream_t stream);
+hipError_t launch_hash_route(const moe_config& c, const int32_t* ids, const int32_t* table,
+                             int64_t table_size, int32_t* topk_idx, float* topk_gate,
+                             moe_stats* stats, hipStream_t stream);
+
 // ------------------------------------------------------------------ expert choice
 // Workspace of moe_forward_expert_choice (byte offsets); gemm_cfg is the layer
 // with top_k raised so that its row space T k + S T covers the E C expert rows.

@@ -230,3 +230,22 @@ def test_expert_choice_entry_points_validate_before_any_launch(tmp_path):
     z = _base(tokens=0)
     assert lib.moe_forward_expert_choice(ctypes.byref(z), None, None, None, None, None, None, 0,
                                          None) == A.MOE_OK
+
+
+def test_hash_and_bias_entry_points_validate_before_any_launch():
+    lib = A.lib()
+    cfg = _base(top_k=1)
+    assert lib.moe_route_hash(ctypes.byref(cfg), None, None, 0, None, None, None, None) == \
+        A.MOE_ERR_INVALID_ARG
+    assert lib.moe_forward_hash(ctypes.byref(cfg), None, None, None, 0, None, None, None, None,
+                                None, 0, None) == A.MOE_ERR_INVALID_ARG
+    two = _base(top_k=2)
+    assert lib.moe_route_hash(ctypes.byref(two), None, None, 0, None, None, None, None) == \
+        A.MOE_ERR_UNSUPPORTED
+    assert lib.moe_forward_hash(ctypes.byref(two), None, None, None, 0, None, None, None, None,
+                                None, 0, None) == A.MOE_ERR_UNSUPPORTED
+    assert lib.moe_update_selection_bias(ctypes.byref(cfg), None, None, 0.1, None) == \
+        A.MOE_ERR_INVALID_ARG
+    z = _base(tokens=0, top_k=1)
+    assert lib.moe_forward_hash(ctypes.byref(z), None, None, None, 0, None, None, None, None,
+                                None, 0, None) == A.MOE_OK
