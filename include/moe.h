@@ -361,20 +361,21 @@ int moe_forward_expert_choice(const moe_config* cfg, const void* x, const moe_we
  * loss with a small coefficient; [P4] router z-loss). The top-k choices, the
  * capacity decisions and the counts f_i are piecewise constant and carry no
  * gradient; the sigmoid selection bias e_bias receives none.
- * This build runs the backward for act_dtype MOE_BF16 with GELU or ReLU experts
- * (other layers return MOE_ERR_UNSUPPORTED).
+ * This build runs the backward for act_dtype MOE_BF16 with GELU, ReLU or SwiGLU
+ * experts (float32 layers return MOE_ERR_UNSUPPORTED).
  */
 
 /* Forward activations the backward reads (device buffers the caller owns). */
 typedef struct moe_saved {
-  void* z;      /* [T k + S T, F] act_dtype: W1 x + b1 per expert-sorted row    */
+  void* z;      /* [T k + S T, F] act_dtype: W1 x + b1 per expert-sorted row;
+                   SwiGLU: [2, T k + S T, F], the planes W1 x + b1 and W3 x       */
   void* y_perm; /* [T k + S T, d] act_dtype: the expert outputs E_e(x) per row  */
 } moe_saved;
 
 /* Gradients written by moe_backward (device buffers; float32 except dx). Every
  * buffer is overwritten (not accumulated into). NULL where the layer has no such
  * parameter: db_gate iff has_gate_bias, db1/db2 iff has_bias, the ws* ones iff
- * num_shared_experts. */
+ * num_shared_experts, dw3 / dws3 iff SwiGLU. */
 typedef struct moe_grads {
   void* dx;        /* [T, d] act_dtype                         */
   float* dw_gate;  /* [E, d]                                   */
@@ -387,14 +388,16 @@ typedef struct moe_grads {
   float* dbs1;     /* [F]                                      */
   float* dws2;     /* [d, F]                                   */
   float* dbs2;     /* [d]                                      */
+  float* dw3;      /* [E, F, d]  SwiGLU only                   */
+  float* dws3;     /* [F, d]     SwiGLU with a shared expert   */
 } moe_grads;
 
 /*
  * The layer forward of moe_forward that also keeps what the backward needs:
  * routing->logits (required here) and saved->z, saved->y_perm. The expert
  * activation is applied to z after its rounding to act_dtype, so the backward
- * recomputes exactly the h the second GEMM used. Same arguments and workspace
- * as moe_forward.
+ * recomputes exactly the h the second GEMM used (SwiGLU: h = silu(z1) u from the
+ * two rounded planes). Same arguments and workspace as moe_forward.
  */
 int moe_forward_train(const moe_config* cfg, const void* x, const moe_weights* w, void* y,
                       const moe_routing* routing, moe_stats* stats, const moe_saved* saved,

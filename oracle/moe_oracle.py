@@ -479,7 +479,7 @@ def expert_ffn_backward(xr, w1, b1, w2, b2, activation: str, dY, w3=None) -> Dic
       dZ = dH * act'(Z)   (SwiGLU: dZ = dH * U * silu'(Z), dU = dH * silu(Z))
       dX = dZ W1 (+ dU W3),  dW1 = dZ^T X,  db1 = sum_rows dZ  (dW3 = dU^T X)
     Returns dx, dw1, db1, dw2, db2, dw3 (None where absent) and the
-    intermediates z, h, dz.
+    intermediates z, u (SwiGLU), h, dz.
     """
     X = np.asarray(xr, F64)
     W1 = np.asarray(w1, F64)
@@ -515,7 +515,7 @@ def expert_ffn_backward(xr, w1, b1, w2, b2, activation: str, dY, w3=None) -> Dic
         dX = dX + dU @ np.asarray(w3, F64)
     dW1 = dZ.T @ X
     db1 = dZ.sum(axis=0) if b1 is not None else None
-    return dict(dx=dX, dw1=dW1, db1=db1, dw2=dW2, db2=db2, dw3=dW3, z=Z, h=H, dz=dZ)
+    return dict(dx=dX, dw1=dW1, db1=db1, dw2=dW2, db2=db2, dw3=dW3, z=Z, u=U, h=H, dz=dZ)
 
 
 def combine_backward(dy, Y, gates, assign_row) -> tuple:
@@ -610,6 +610,7 @@ def backward(x, params, w, dy, aux_coef: float = 0.0, z_coef: float = 0.0, fwd=N
                db2=np.zeros((E, d), F64) if params.get("b2") is not None else None,
                dw3=np.zeros((E, F, d), F64) if act == "swiglu" else None)
     Z = np.zeros((R, F), F64)
+    U = np.zeros((R, F), F64) if act == "swiglu" else None
     dZ = np.zeros((R, F), F64)
     for e in range(E):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
@@ -628,13 +629,15 @@ def backward(x, params, w, dy, aux_coef: float = 0.0, z_coef: float = 0.0, fwd=N
         if act == "swiglu":
             out["dw3"][e] = gr["dw3"]
         Z[lo:hi] = gr["z"]
+        if U is not None:
+            U[lo:hi] = gr["u"]
         dZ[lo:hi] = gr["dz"]
     if w.num_shared_experts:
         gs = expert_ffn_backward(x, params["ws1"][0], _opt(params.get("bs1"), 0), params["ws2"][0],
                                  _opt(params.get("bs2"), 0), act, dy, _opt(params.get("ws3"), 0))
         dx += gs["dx"]
         out.update(dws1=gs["dw1"], dbs1=gs["db1"], dws2=gs["dw2"], dbs2=gs["db2"], dws3=gs["dw3"],
-                   z_shared=gs["z"], dz_shared=gs["dz"])
+                   z_shared=gs["z"], u_shared=gs["u"], dz_shared=gs["dz"])
     f = np.asarray(fwd["counts_pre"], F64) / float(T * k)
     dlogits = router_backward(fwd["logits"] if logits is None else logits, fwd["idx"],
                               w.score_fn, dgate, f, aux_coef, z_coef)
@@ -642,7 +645,7 @@ def backward(x, params, w, dy, aux_coef: float = 0.0, z_coef: float = 0.0, fwd=N
     dx += dlogits @ Wg
     out.update(dx=dx, dw_gate=dlogits.T @ x,
                db_gate=dlogits.sum(axis=0) if params.get("b_gate") is not None else None,
-               dY=dY, dgate=dgate, dlogits=dlogits, z=Z, dz=dZ)
+               dY=dY, dgate=dgate, dlogits=dlogits, z=Z, u=U, dz=dZ)
     return out
 
 

@@ -56,7 +56,7 @@ class MoeSaved(ctypes.Structure):
 
 class MoeGrads(ctypes.Structure):
     _fields_ = [(n, c_void_p) for n in ("dx", "dw_gate", "db_gate", "dw1", "db1", "dw2", "db2",
-                                        "dws1", "dbs1", "dws2", "dbs2")]
+                                        "dws1", "dbs1", "dws2", "dbs2", "dw3", "dws3")]
 
 
 STATS_DTYPE = np.dtype([
@@ -502,7 +502,8 @@ class EcPlan:
 def _need_saved(cfg, saved):
     T, d, F, E, k, S, act, _ = _sizes(cfg)
     rows = T * k + S * T
-    _need(saved.get("z"), "saved z", (rows, F), act)
+    zshape = (2, rows, F) if cfg.activation == ACTIVATION["swiglu"] else (rows, F)
+    _need(saved.get("z"), "saved z", zshape, act)
     _need(saved.get("y_perm"), "saved y_perm", (rows, d), act)
 
 
@@ -546,6 +547,10 @@ def _need_grads(cfg, g):
         _need(g.get("dbs1"), "dbs1", (F,), f32, optional=not cfg.has_bias)
         _need(g.get("dws2"), "dws2", (d, F), f32)
         _need(g.get("dbs2"), "dbs2", (d,), f32, optional=not cfg.has_bias)
+    if cfg.activation == ACTIVATION["swiglu"]:
+        _need(g.get("dw3"), "dw3", (E, F, d), f32)
+        if S:
+            _need(g.get("dws3"), "dws3", (F, d), f32)
 
 
 def backward(cfg, x, weights, routing, stats, saved, dy, aux_coef, z_coef, grads, workspace):
@@ -573,7 +578,8 @@ def backward(cfg, x, weights, routing, stats, saved, dy, aux_coef, z_coef, grads
 def alloc_saved(cfg, device="cuda") -> Dict[str, torch.Tensor]:
     T, d, F, E, k, S, act, _ = _sizes(cfg)
     rows = T * k + S * T
-    return dict(z=torch.empty(rows, F, dtype=act, device=device),
+    zshape = (2, rows, F) if cfg.activation == ACTIVATION["swiglu"] else (rows, F)
+    return dict(z=torch.empty(*zshape, dtype=act, device=device),
                 y_perm=torch.empty(rows, d, dtype=act, device=device))
 
 
@@ -581,6 +587,7 @@ def alloc_grads(cfg, device="cuda") -> Dict[str, Optional[torch.Tensor]]:
     T, d, F, E, k, S, act, _ = _sizes(cfg)
     f = dict(dtype=torch.float32, device=device)
     b, gb = bool(cfg.has_bias), bool(cfg.has_gate_bias)
+    sw = cfg.activation == ACTIVATION["swiglu"]
     return dict(dx=torch.empty(T, d, dtype=act, device=device), dw_gate=torch.empty(E, d, **f),
                 db_gate=torch.empty(E, **f) if gb else None, dw1=torch.empty(E, F, d, **f),
                 db1=torch.empty(E, F, **f) if b else None, dw2=torch.empty(E, d, F, **f),
@@ -588,7 +595,9 @@ def alloc_grads(cfg, device="cuda") -> Dict[str, Optional[torch.Tensor]]:
                 dws1=torch.empty(F, d, **f) if S else None,
                 dbs1=torch.empty(F, **f) if S and b else None,
                 dws2=torch.empty(d, F, **f) if S else None,
-                dbs2=torch.empty(d, **f) if S and b else None)
+                dbs2=torch.empty(d, **f) if S and b else None,
+                dw3=torch.empty(E, F, d, **f) if sw else None,
+                dws3=torch.empty(F, d, **f) if sw and S else None)
 
 
 def alloc_backward_workspace(cfg, device="cuda") -> torch.Tensor:

@@ -17,6 +17,9 @@ __device__ __forceinline__ float act_bf16(int act, float z) {
   return act == MOE_ACT_GELU ? gelu_poly(z) : fmaxf(z, 0.f);
 }
 
+// SwiGLU on the saved planes: h = silu(z1) u.
+__device__ __forceinline__ float swiglu_h(float z1, float u) { return silu(z1) * u; }
+
 __device__ __forceinline__ int clamp_off(const int32_t* __restrict__ off, int g, int64_t rows_max) {
   const int v = off[g];
   return v < 0 ? 0 : (v > rows_max ? (int)rows_max : v);
@@ -24,8 +27,10 @@ __device__ __forceinline__ int clamp_off(const int32_t* __restrict__ off, int g,
 
 // ------------------------------------------------------------------ training forward
 // h[r] = act(z[r]) for the rows r < expert_offsets[G] (z already rounded to
-// bf16, so the backward recomputes exactly this h). 8 elements per thread.
+// bf16, so the backward recomputes exactly this h); SwiGLU: h = silu(z1) u with
+// u the second plane (u != nullptr). 8 elements per thread.
 __global__ __launch_bounds__(256) void act_rows_kernel(const bf16* __restrict__ z,
+                                                       const bf16* __restrict__ u,
                                                        const int32_t* __restrict__ off, int G,
                                                        int64_t rows_max, int F, int act,
                                                        bf16* __restrict__ h) {
@@ -35,9 +40,46 @@ __global__ __launch_bounds__(256) void act_rows_kernel(const bf16* __restrict__ 
        i += (int64_t)gridDim.x * blockDim.x) {
     float v[8];
     load8(z + i * 8, v);
+    if (u) {
+      float w[8];
+      load8(u + i * 8, w);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = act_bf16(act, v[e]);
+      for (int e = 0; e < 8; ++e) v[e] = swiglu_h(v[e], w[e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = act_bf16(act, v[e]);
+    }
     store8(h + i * 8, v);
+  }
+}
+
+// SwiGLU backward, elementwise: from dH, z1 and u (rows r < expert_offsets[G]),
+// dz1 = dH u silu'(z1) and du = dH silu(z1), written side by side as row r of
+// dZ [rows][2F] (dz1 in columns 0..F-1, du in F..2F-1).
+__global__ __launch_bounds__(256) void dswiglu_kernel(const bf16* __restrict__ dh,
+                                                      const bf16* __restrict__ z1,
+                                                      const bf16* __restrict__ u,
+                                                      const int32_t* __restrict__ off, int G,
+                                                      int64_t rows_max, int F,
+                                                      bf16* __restrict__ dz) {
+  const int64_t R = clamp_off(off, G, rows_max);
+  const int64_t n8 = R * F / 8;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n8;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i * 8 / F, c = i * 8 - r * F;
+    float g[8], a[8], b[8], o1[8], o2[8];
+    load8(dh + i * 8, g);
+    load8(z1 + i * 8, a);
+    load8(u + i * 8, b);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float sg = 1.0f / (1.0f + expf(-a[e]));
+      const float si = a[e] * sg;
+      o1[e] = g[e] * b[e] * sg * (1.0f + a[e] * (1.0f - sg));
+      o2[e] = g[e] * si;
+    }
+    store8(dz + r * 2 * F + c, o1);
+    store8(dz + r * 2 * F + F + c, o2);
   }
 }
 
@@ -196,15 +238,17 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(
 }
 
 // ------------------------------------------------------------------ transposes
-// Batched bf16 transpose in[b][M][N] -> out[b][N][M] through a 64 x 64 LDS tile
-// (16-byte loads and stores; M and N multiples of 64).
+// Batched bf16 transpose in[b][M][N] -> out[b][n][col0 + m] (out rows of ldo
+// elements, so two matrices can be placed side by side) through a 64 x 64 LDS
+// tile (16-byte loads and stores; M and N multiples of 64).
 __global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16* __restrict__ in,
-                                                             bf16* __restrict__ out, int M, int N) {
+                                                             bf16* __restrict__ out, int M, int N,
+                                                             int ldo, int col0) {
   __shared__ uint16_t tile[64][66];
   const int n0 = blockIdx.x * 64, m0 = blockIdx.y * 64;
   const int64_t b = blockIdx.z;
   const bf16* src = in + b * (int64_t)M * N;
-  bf16* dst = out + b * (int64_t)M * N;
+  bf16* dst = out + b * (int64_t)N * ldo + col0;
   const int tid = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -226,7 +270,7 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16* __restr
     u.y = (uint32_t)tile[c + 2][r] | ((uint32_t)tile[c + 3][r] << 16);
     u.z = (uint32_t)tile[c + 4][r] | ((uint32_t)tile[c + 5][r] << 16);
     u.w = (uint32_t)tile[c + 6][r] | ((uint32_t)tile[c + 7][r] << 16);
-    *reinterpret_cast<uint4*>(dst + (int64_t)(n0 + r) * M + m0 + c) = u;
+    *reinterpret_cast<uint4*>(dst + (int64_t)(n0 + r) * ldo + m0 + c) = u;
   }
 }
 
@@ -257,12 +301,13 @@ __global__ void pad_offsets_kernel(const int32_t* __restrict__ off, int G, int64
 // row r = so[g] + (k - po[g]) of the source (zero past the group's rows; so
 // and po as written by pad_offsets_kernel).
 // MODE 0: rows of src [rows][C]; MODE 1: token rows of src (x [T][C]) through
-// row_token; MODE 2: act(src) (src = z, the saved pre-activation). With
+// row_token; MODE 2: act(src) (src = z, the saved pre-activation); MODE 3:
+// silu(src) src2 (SwiGLU, src = z1, src2 = u). With
 // partial != nullptr also writes the 64-row column sums of the (bf16) values
 // of its block to partial[k / 64][c] (bias gradients).
 template <int MODE>
 __global__ __launch_bounds__(256) void transpose_rows_kernel(
-    const bf16* __restrict__ src, const int32_t* __restrict__ row_token,
+    const bf16* __restrict__ src, const bf16* __restrict__ src2, const int32_t* __restrict__ row_token,
     const int32_t* __restrict__ so, const int32_t* __restrict__ po, int G, int64_t src_rows, int C,
     int ldk, int act, bf16* __restrict__ out, float* __restrict__ partial) {
   __shared__ float tile[64][65];
@@ -294,6 +339,12 @@ __global__ __launch_bounds__(256) void transpose_rows_kernel(
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = bf16_bits_to_f32(f32_to_bf16_bits(act_bf16(act, v[e])));
       }
+      if (MODE == 3) {
+        float w[8];
+        load8(src2 + row * C + c0 + c, w);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = bf16_bits_to_f32(f32_to_bf16_bits(swiglu_h(v[e], w[e])));
+      }
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) tile[kk][c + e] = v[e];
@@ -318,8 +369,8 @@ __global__ __launch_bounds__(256) void transpose_rows_kernel(
 // block order (deterministic). Routed groups write db + g C, the shared expert
 // (g == E) writes dbs.
 __global__ __launch_bounds__(256) void colsum_reduce_kernel(const float* __restrict__ partial,
-                                                            const int32_t* __restrict__ po, int C,
-                                                            int E, float* __restrict__ db,
+                                                            int ldp, const int32_t* __restrict__ po,
+                                                            int C, int E, float* __restrict__ db,
                                                             float* __restrict__ dbs) {
   const int g = blockIdx.y;
   const int c = blockIdx.x * 256 + threadIdx.x;
@@ -330,11 +381,11 @@ __global__ __launch_bounds__(256) void colsum_reduce_kernel(const float* __restr
   for (; b + 8 <= b1; b += 8) {
     float v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = partial[(int64_t)(b + u) * C + c];
+    for (int u = 0; u < 8; ++u) v[u] = partial[(int64_t)(b + u) * ldp + c];
 #pragma unroll
     for (int u = 0; u < 8; ++u) s += v[u];
   }
-  for (; b < b1; ++b) s += partial[(int64_t)b * C + c];
+  for (; b < b1; ++b) s += partial[(int64_t)b * ldp + c];
   if (g < E) db[(int64_t)g * C + c] = s;
   else dbs[c] = s;
 }
@@ -497,9 +548,22 @@ hipError_t launch_act_rows(const moe_config& c, const void* z, const int32_t* of
                            hipStream_t s) {
   const int G = c.num_experts + c.num_shared_experts;
   const int64_t n8 = rows_max(c) * c.d_ff / 8;
+  const bf16* u = c.activation == MOE_ACT_SWIGLU ? (const bf16*)z + rows_max(c) * c.d_ff : nullptr;
   const int64_t blocks = (n8 + 255) / 256 < 4096 ? (n8 + 255) / 256 : 4096;
   hipLaunchKernelGGL(act_rows_kernel, dim3((unsigned)(blocks > 0 ? blocks : 1)), dim3(256), 0, s,
-                     (const bf16*)z, off, G, rows_max(c), (int)c.d_ff, c.activation, (bf16*)h);
+                     (const bf16*)z, u, off, G, rows_max(c), (int)c.d_ff, c.activation, (bf16*)h);
+  return hipGetLastError();
+}
+
+hipError_t launch_dswiglu(const moe_config& c, const void* dh, const void* z, void* dz,
+                          const int32_t* off, hipStream_t s) {
+  const int G = c.num_experts + c.num_shared_experts;
+  const int64_t rmax = rows_max(c);
+  const int64_t n8 = rmax * c.d_ff / 8;
+  const int64_t blocks = (n8 + 255) / 256 < 4096 ? (n8 + 255) / 256 : 4096;
+  hipLaunchKernelGGL(dswiglu_kernel, dim3((unsigned)(blocks > 0 ? blocks : 1)), dim3(256), 0, s,
+                     (const bf16*)dh, (const bf16*)z, (const bf16*)z + rmax * c.d_ff, off, G, rmax,
+                     (int)c.d_ff, (bf16*)dz);
   return hipGetLastError();
 }
 
@@ -524,15 +588,23 @@ hipError_t launch_backward_misc(const moe_config& c, const BwdLayout& B, const v
     hipLaunchKernelGGL(router_bwd_kernel, dim3(tb), dim3(256), 0, s, r.logits, r.topk_idx, dgate,
                        stats->counts_pre, T, E, k, (int)(c.score_fn == MOE_SCORE_SIGMOID), aux_coef,
                        z_coef, dlogits);
+    // W2^T [E][F][d]; W1^T [E][d][F], for SwiGLU [W1^T | W3^T] as [E][d][2F]
+    const int NZ = c.activation == MOE_ACT_SWIGLU ? 2 : 1;
     hipLaunchKernelGGL(transpose_bf16_kernel, dim3(F / 64, d / 64, E), dim3(256), 0, s,
-                       (const bf16*)w.w2, (bf16*)(ws + B.w2t), d, F);
+                       (const bf16*)w.w2, (bf16*)(ws + B.w2t), d, F, d, 0);
     hipLaunchKernelGGL(transpose_bf16_kernel, dim3(d / 64, F / 64, E), dim3(256), 0, s,
-                       (const bf16*)w.w1, (bf16*)(ws + B.w1t), F, d);
+                       (const bf16*)w.w1, (bf16*)(ws + B.w1t), F, d, NZ * F, 0);
+    if (NZ == 2)
+      hipLaunchKernelGGL(transpose_bf16_kernel, dim3(d / 64, F / 64, E), dim3(256), 0, s,
+                         (const bf16*)w.w3, (bf16*)(ws + B.w1t), F, d, 2 * F, F);
     if (S) {
       hipLaunchKernelGGL(transpose_bf16_kernel, dim3(F / 64, d / 64, 1), dim3(256), 0, s,
-                         (const bf16*)w.ws2, (bf16*)(ws + B.ws2t), d, F);
+                         (const bf16*)w.ws2, (bf16*)(ws + B.ws2t), d, F, d, 0);
       hipLaunchKernelGGL(transpose_bf16_kernel, dim3(d / 64, F / 64, 1), dim3(256), 0, s,
-                         (const bf16*)w.ws1, (bf16*)(ws + B.ws1t), F, d);
+                         (const bf16*)w.ws1, (bf16*)(ws + B.ws1t), F, d, NZ * F, 0);
+      if (NZ == 2)
+        hipLaunchKernelGGL(transpose_bf16_kernel, dim3(d / 64, F / 64, 1), dim3(256), 0, s,
+                           (const bf16*)w.ws3, (bf16*)(ws + B.ws1t), F, d, 2 * F, F);
     }
     hipLaunchKernelGGL(pad_offsets_kernel, dim3(1), dim3(64), 0, s, r.expert_offsets, G, rmax, po,
                        so);
@@ -545,27 +617,45 @@ hipError_t launch_backward_misc(const moe_config& c, const BwdLayout& B, const v
   const bool bias = c.has_bias;
   float* p2 = bias ? (float*)(ws + B.colsum2) : nullptr;
   float* p1 = bias ? (float*)(ws + B.colsum1) : nullptr;
+  const bool sw = c.activation == MOE_ACT_SWIGLU;
+  const int NZ = sw ? 2 : 1;   // dZ = [dz1 | du] for SwiGLU
+  const bf16* z1 = (const bf16*)sv.z;
+  const bf16* u = sw ? z1 + rmax * F : nullptr;
   hipLaunchKernelGGL((transpose_rows_kernel<0>), dim3(kb, d / 64), dim3(256), 0, s,
-                     (const bf16*)dyp, (const int32_t*)nullptr, (const int32_t*)so, po, G, rmax,
-                     d, ldk, c.activation, (bf16*)(ws + B.dypT), p2);
-  hipLaunchKernelGGL((transpose_rows_kernel<2>), dim3(kb, F / 64), dim3(256), 0, s,
-                     (const bf16*)sv.z, (const int32_t*)nullptr, (const int32_t*)so, po, G, rmax,
-                     F, ldk, c.activation, (bf16*)(ws + B.hT), (float*)nullptr);
-  hipLaunchKernelGGL((transpose_rows_kernel<0>), dim3(kb, F / 64), dim3(256), 0, s,
-                     (const bf16*)(ws + B.dz), (const int32_t*)nullptr, (const int32_t*)so, po, G,
-                     rmax, F, ldk, c.activation, (bf16*)(ws + B.dzT), p1);
+                     (const bf16*)dyp, (const bf16*)nullptr, (const int32_t*)nullptr,
+                     (const int32_t*)so, po, G, rmax, d, ldk, c.activation, (bf16*)(ws + B.dypT),
+                     p2);
+  if (sw)
+    hipLaunchKernelGGL((transpose_rows_kernel<3>), dim3(kb, F / 64), dim3(256), 0, s, z1, u,
+                       (const int32_t*)nullptr, (const int32_t*)so, po, G, rmax, F, ldk,
+                       c.activation, (bf16*)(ws + B.hT), (float*)nullptr);
+  else
+    hipLaunchKernelGGL((transpose_rows_kernel<2>), dim3(kb, F / 64), dim3(256), 0, s, z1,
+                       (const bf16*)nullptr, (const int32_t*)nullptr, (const int32_t*)so, po, G, rmax,
+                       F, ldk, c.activation, (bf16*)(ws + B.hT), (float*)nullptr);
+  hipLaunchKernelGGL((transpose_rows_kernel<0>), dim3(kb, NZ * F / 64), dim3(256), 0, s,
+                     (const bf16*)(ws + B.dz), (const bf16*)nullptr, (const int32_t*)nullptr,
+                     (const int32_t*)so, po, G, rmax, NZ * F, ldk, c.activation,
+                     (bf16*)(ws + B.dzT), p1);
   hipLaunchKernelGGL((transpose_rows_kernel<1>), dim3(kb, d / 64), dim3(256), 0, s, (const bf16*)x,
-                     r.row_token, (const int32_t*)so, po, G, T, d, ldk, c.activation,
-                     (bf16*)(ws + B.xT), (float*)nullptr);
+                     (const bf16*)nullptr, r.row_token, (const int32_t*)so, po, G, T, d, ldk,
+                     c.activation, (bf16*)(ws + B.xT), (float*)nullptr);
   hipError_t e = launch_wgrad(ws + B.dypT, ws + B.hT, po, G, E, d, F, ldk, gr.dw2, gr.dws2, s);
   if (e != hipSuccess) return e;
   e = launch_wgrad(ws + B.dzT, ws + B.xT, po, G, E, F, d, ldk, gr.dw1, gr.dws1, s);
   if (e != hipSuccess) return e;
+  if (sw) {
+    // dW3 from the du rows of dZ^T
+    e = launch_wgrad(ws + B.dzT + (size_t)F * ldk * 2, ws + B.xT, po, G, E, F, d, ldk, gr.dw3,
+                     gr.dws3, s);
+    if (e != hipSuccess) return e;
+  }
   if (bias) {
     hipLaunchKernelGGL(colsum_reduce_kernel, dim3((d + 255) / 256, G), dim3(256), 0, s,
-                       (const float*)p2, (const int32_t*)po, d, E, gr.db2, gr.dbs2);
+                       (const float*)p2, d, (const int32_t*)po, d, E, gr.db2, gr.dbs2);
+    // b1 sits on W1 only: the dz1 columns
     hipLaunchKernelGGL(colsum_reduce_kernel, dim3((F + 255) / 256, G), dim3(256), 0, s,
-                       (const float*)p1, (const int32_t*)po, F, E, gr.db1, gr.dbs1);
+                       (const float*)p1, NZ * F, (const int32_t*)po, F, E, gr.db1, gr.dbs1);
   }
   hipLaunchKernelGGL(gate_wgrad_kernel, dim3((E + 7) / 8, (d + 1023) / 1024, B.gate_slices), dim3(256), 0, s,
                      (const bf16*)x, (const float*)dlogits, T, d, E, (int)B.gate_slice_len,

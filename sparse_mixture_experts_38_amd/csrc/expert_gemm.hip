@@ -1123,25 +1123,40 @@ hipError_t launch_backward_dz(const moe_config& c, const void* dyp, const int32_
     return gemm_launch<bf16, EPI_DGELU, false>(c, (const bf16*)dyp, w2t, nullptr, nullptr, ws2t,
                                                nullptr, nullptr, offsets, (bf16*)dz, N, K, s,
                                                nullptr, (const bf16*)z);
-  return gemm_launch<bf16, EPI_DRELU, false>(c, (const bf16*)dyp, w2t, nullptr, nullptr, ws2t,
-                                             nullptr, nullptr, offsets, (bf16*)dz, N, K, s, nullptr,
-                                             (const bf16*)z);
+  if (c.activation == MOE_ACT_RELU)
+    return gemm_launch<bf16, EPI_DRELU, false>(c, (const bf16*)dyp, w2t, nullptr, nullptr, ws2t,
+                                               nullptr, nullptr, offsets, (bf16*)dz, N, K, s,
+                                               nullptr, (const bf16*)z);
+  // SwiGLU: dH itself (the elementwise step forms dz1 and du)
+  return gemm_launch<bf16, EPI_NONE, false>(c, (const bf16*)dyp, w2t, nullptr, nullptr, ws2t,
+                                            nullptr, nullptr, offsets, (bf16*)dz, N, K, s);
+}
+
+hipError_t launch_linear_rows(const moe_config& c, const void* a, const int32_t* offsets,
+                              const void* W, const float* b, const void* Ws, const float* bs,
+                              void* out, int N, int K, hipStream_t s, const int32_t* arows) {
+  return b ? gemm_launch<bf16, EPI_NONE, true>(c, (const bf16*)a, W, nullptr, b, Ws, nullptr, bs,
+                                               offsets, (bf16*)out, N, K, s, arows)
+           : gemm_launch<bf16, EPI_NONE, false>(c, (const bf16*)a, W, nullptr, nullptr, Ws, nullptr,
+                                                nullptr, offsets, (bf16*)out, N, K, s, arows);
 }
 
 hipError_t launch_expert_up_linear(const moe_config& c, const void* a, const int32_t* offsets,
                                    const ExpertWeights& w, void* z, hipStream_t s,
                                    const int32_t* arows) {
   const int N = (int)c.d_ff, K = (int)c.d_model;
-  return c.has_bias
-             ? gemm_launch<bf16, EPI_NONE, true>(c, (const bf16*)a, w.w1, nullptr, w.b1, w.ws1,
-                                                 nullptr, w.bs1, offsets, (bf16*)z, N, K, s, arows)
-             : gemm_launch<bf16, EPI_NONE, false>(c, (const bf16*)a, w.w1, nullptr, w.b1, w.ws1,
-                                                  nullptr, w.bs1, offsets, (bf16*)z, N, K, s, arows);
+  hipError_t e = launch_linear_rows(c, a, offsets, w.w1, c.has_bias ? w.b1 : nullptr, w.ws1,
+                                    c.has_bias ? w.bs1 : nullptr, z, N, K, s, arows);
+  if (e != hipSuccess || c.activation != MOE_ACT_SWIGLU) return e;
+  // SwiGLU: the second plane u = x W3^T (no bias)
+  return launch_linear_rows(c, a, offsets, w.w3, nullptr, w.ws3, nullptr,
+                            (bf16*)z + rows_max(c) * c.d_ff, N, K, s, arows);
 }
 
 hipError_t launch_backward_dx(const moe_config& c, const void* dz, const int32_t* offsets,
                               const void* w1t, const void* ws1t, void* dxp, hipStream_t s) {
-  const int N = (int)c.d_model, K = (int)c.d_ff;
+  const int N = (int)c.d_model;
+  const int K = (int)c.d_ff * (c.activation == MOE_ACT_SWIGLU ? 2 : 1);
   return gemm_launch<bf16, EPI_NONE, false>(c, (const bf16*)dz, w1t, nullptr, nullptr, ws1t, nullptr,
                                             nullptr, offsets, (bf16*)dxp, N, K, s);
 }

@@ -61,18 +61,20 @@ BwdLayout backward_layout(const moe_config& c) {
   B.dyp = take((size_t)(rmax * d * 2));
   B.dgate = take((size_t)(T * k * 4));
   B.dlogits = take((size_t)(T * E * 4));
-  B.w1t = take((size_t)E * d * F * 2);
+  const int64_t NZ = c.activation == MOE_ACT_SWIGLU ? 2 : 1;   // SwiGLU: [dz1 | du]
+  B.w1t = take((size_t)(E * d * NZ * F * 2));
   B.w2t = take((size_t)E * F * d * 2);
-  B.ws1t = take((size_t)S * d * F * 2);
+  B.ws1t = take((size_t)(S * d * NZ * F * 2));
   B.ws2t = take((size_t)S * F * d * 2);
-  B.dz = take((size_t)(rmax * F * 2));
+  B.dz = take((size_t)(rmax * NZ * F * 2));
+  B.dh = take(NZ == 2 ? (size_t)(rmax * F * 2) : 0);
   B.dxp = take((size_t)(rmax * d * 2));
   B.po = take((size_t)(G + 1) * 8);   // po [G + 1], then the sanitized offsets [G + 1]
   B.dypT = take((size_t)(d * B.ldk * 2));
   B.hT = take((size_t)(F * B.ldk * 2));
-  B.dzT = take((size_t)(F * B.ldk * 2));
+  B.dzT = take((size_t)(NZ * F * B.ldk * 2));
   B.xT = take((size_t)(d * B.ldk * 2));
-  B.colsum1 = take(c.has_bias ? (size_t)(B.ldk / 64 * F * 4) : 0);
+  B.colsum1 = take(c.has_bias ? (size_t)(B.ldk / 64 * NZ * F * 4) : 0);
   B.colsum2 = take(c.has_bias ? (size_t)(B.ldk / 64 * d * 4) : 0);
   // router weight gradient: about 512 blocks of (8 experts x 1024 columns x a token slice)
   const int64_t xy = (int64_t)((E + 7) / 8) * ((d + 1023) / 1024);
@@ -136,14 +138,13 @@ static int64_t capacity_exact(const moe_config& c) {
 
 static int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
-// Layers the training forward and the backward run: bf16 activations, GELU or
-// ReLU experts, and transposed row buffers short enough for the 32-bit
-// operand offsets of the weight-gradient GEMM (256 ldk < 2^31).
+// Layers the training forward and the backward run: bf16 activations (GELU,
+// ReLU or SwiGLU experts), and transposed row buffers short enough for the
+// 32-bit operand offsets of the weight-gradient GEMM (256 ldk < 2^31).
 static int validate_train(const moe_config* c) {
   const int v = validate(c);
   if (v != MOE_OK) return v;
   if (c->act_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
-  if (c->activation != MOE_ACT_GELU && c->activation != MOE_ACT_RELU) return MOE_ERR_UNSUPPORTED;
   if (backward_layout(*c).ldk >= ((int64_t)1 << 23)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
@@ -491,6 +492,8 @@ int moe_backward(const moe_config* cfg, const void* x, const moe_weights* w, con
   if (bias && (!g->db1 || !g->db2)) return MOE_ERR_INVALID_ARG;
   if (shared && (!g->dws1 || !g->dws2 || (bias && (!g->dbs1 || !g->dbs2))))
     return MOE_ERR_INVALID_ARG;
+  const bool swiglu = cfg->activation == MOE_ACT_SWIGLU;
+  if (swiglu && (!w->w3 || !g->dw3 || (shared && (!w->ws3 || !g->dws3)))) return MOE_ERR_INVALID_ARG;
   const BwdLayout B = backward_layout(*cfg);
   if (workspace_bytes < B.total) return MOE_ERR_WORKSPACE;
   char* ws = (char*)workspace;
@@ -499,8 +502,12 @@ int moe_backward(const moe_config* cfg, const void* x, const moe_weights* w, con
                                       ws, s, 0);
   if (e != hipSuccess) return MOE_ERR_HIP;
   e = launch_backward_dz(*cfg, ws + B.dyp, r->expert_offsets, ws + B.w2t, ws + B.ws2t, saved->z,
-                         ws + B.dz, s);
+                         ws + (swiglu ? B.dh : B.dz), s);
   if (e != hipSuccess) return MOE_ERR_HIP;
+  if (swiglu) {
+    e = launch_dswiglu(*cfg, ws + B.dh, saved->z, ws + B.dz, r->expert_offsets, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
   e = launch_backward_dx(*cfg, ws + B.dz, r->expert_offsets, ws + B.w1t, ws + B.ws1t, ws + B.dxp, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
   return hip_status(launch_backward_misc(*cfg, B, x, *w, *r, stats, *saved, dy, aux_coef, z_coef,

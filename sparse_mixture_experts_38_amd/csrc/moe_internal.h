@@ -209,14 +209,15 @@ hipError_t launch_expert_choice_forward(const moe_config& c, const EcLayout& L, 
 // transposed, group-padded row buffers (each group's rows rounded up to a
 // multiple of 128, at least 128).
 struct BwdLayout {
-  size_t dyp, dgate, dlogits, w1t, w2t, ws1t, ws2t, dz, dxp, po;   // po: padded then sanitized offsets
+  size_t dyp, dgate, dlogits, w1t, w2t, ws1t, ws2t, dz, dh, dxp, po;   // po: padded then sanitized offsets
   size_t dypT, hT, dzT, xT, colsum1, colsum2, gate_partial, total;
   int64_t ldk;
   int gate_slices, gate_slice_len;
 };
 BwdLayout backward_layout(const moe_config& c);
 
-// Training forward: z = a W1^T + b1 per group (no activation), then h = act(z).
+// Training forward: z = a W1^T + b1 per group (no activation; SwiGLU: a second
+// plane u = a W3^T after rows_max x F elements), then h = act(z) (silu(z) u).
 hipError_t launch_expert_up_linear(const moe_config& c, const void* a, const int32_t* expert_offsets,
                                    const ExpertWeights& w, void* z, hipStream_t stream,
                                    const int32_t* arows);
@@ -231,11 +232,15 @@ hipError_t launch_backward_misc(const moe_config& c, const BwdLayout& B, const v
                                 const moe_grads& gr, char* ws, hipStream_t stream, int phase);
 
 // dZ = (dYp W2) * act'(z) per group: dYp [rows][d], w2t [E][F][d] (W2 transposed),
-// ws2t [F][d] (shared expert), z and dZ [rows][F] bf16; GELU or ReLU.
+// ws2t [F][d] (shared expert), z and dZ [rows][F] bf16 (GELU, ReLU); for SwiGLU the
+// product dH = dYp W2 alone, which launch_dswiglu turns into dZ = [dz1 | du].
 hipError_t launch_backward_dz(const moe_config& c, const void* dyp, const int32_t* expert_offsets,
                               const void* w2t, const void* ws2t, const void* z, void* dz,
                               hipStream_t stream);
-// dXp = dZ W1 per group: w1t [E][d][F] (W1 transposed), ws1t [d][F]; dXp [rows][d] bf16.
+// dXp = dZ W1 per group: w1t [E][d][F] (W1 transposed; SwiGLU: [W1^T | W3^T], K = 2F),
+// ws1t [d][F] (or [d][2F]); dXp [rows][d] bf16.
+hipError_t launch_dswiglu(const moe_config& c, const void* dh, const void* z, void* dz,
+                          const int32_t* expert_offsets, hipStream_t stream);
 hipError_t launch_backward_dx(const moe_config& c, const void* dz, const int32_t* expert_offsets,
                               const void* w1t, const void* ws1t, void* dxp, hipStream_t stream);
 // Ragged-K grouped weight gradient C_g = A[:, po[g]:po[g+1]] B[:, po[g]:po[g+1]]^T,

@@ -37,6 +37,10 @@ CASES = {
                                                    activation="gelu"),
     # 128 experts, top-1, heavy imbalance: many empty and near-empty groups
     "many_expert": W["many_expert_train"].scaled(tokens=1536, d_model=256, d_ff=256),
+    # Mixtral recipe: SwiGLU experts, no biases, no capacity limit
+    "mixtral_small": W["mixtral_8x7b"].scaled(tokens=700, d_model=512, d_ff=768),
+    # DeepSeek-V3 recipe with its SwiGLU experts: sigmoid + selection bias, top-8 of 256, shared
+    "deepseek_small": W["deepseek_v3"].scaled(tokens=300, d_model=512, d_ff=256),
     # d_model 2048: the dX GEMM takes the 256 x 256 tiles for full 256-row blocks
     "long_k": W["deepspeed_gpt_moe"].scaled(tokens=600, d_model=2048, d_ff=512, num_experts=4,
                                             drop_tokens=False),
@@ -82,7 +86,12 @@ def check_backward(w, inp, dy, out):
     errs["y"] = rel_err(out["y"].float().numpy(), fwd["y"])
     g = O.backward(x_np, P, w, np64(dy), AUX, ZC, fwd=fwd, logits=logits)
     R = int(fwd["expert_offsets"][-1])
-    errs["z"] = rel_err(out["z"].float().numpy()[:R], g["z"][:R])
+    zs = out["z"].float().numpy()
+    if w.activation == "swiglu":
+        errs["z"] = rel_err(zs[0, :R], g["z"][:R])
+        errs["u"] = rel_err(zs[1, :R], g["u"][:R])
+    else:
+        errs["z"] = rel_err(zs[:R], g["z"][:R])
     errs["y_perm"] = rel_err(out["y_perm"].float().numpy()[:R], fwd["Y"][:R])
     G = out["grads"]
     pairs = [("dx", "dx"), ("dw_gate", "dw_gate"), ("dw1", "dw1"), ("dw2", "dw2")]
@@ -94,6 +103,8 @@ def check_backward(w, inp, dy, out):
         pairs += [("dws1", "dws1"), ("dws2", "dws2")]
         if w.has_bias:
             pairs += [("dbs1", "dbs1"), ("dbs2", "dbs2")]
+    if w.activation == "swiglu":
+        pairs += [("dw3", "dw3")] + ([("dws3", "dws3")] if w.num_shared_experts else [])
     for gk, ok in pairs:
         ref = g[ok]
         got = G[gk].float().numpy()
