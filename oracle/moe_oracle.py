@@ -603,7 +603,7 @@ def backward(x, params, w, dy, aux_coef: float = 0.0, z_coef: float = 0.0, fwd=N
     offsets = fwd["expert_offsets"]
     R = int(offsets[-1])
     dY, dgate = combine_backward(dy, fwd["Y"], fwd["gates"], fwd["assign_row"])
-    F = params["w1"].shape[1]
+    F = np.asarray(params["w1"][0]).shape[0]
     dx = np.zeros((T, d), F64)
     out = dict(dw1=np.zeros((E, F, d), F64), dw2=np.zeros((E, d, F), F64),
                db1=np.zeros((E, F), F64) if params.get("b1") is not None else None,
