@@ -498,8 +498,8 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
         for (int e = 0; e < 4; ++e)
           v[e] = epilogue_bf16<EPI>(z[e], GATED ? acc[i + 2][qd * 4 + e] : zs[e]);
         uint2 u;
-        u.x = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
-        u.y = (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
+        u.x = pack_bf16x2(v[0], v[1]);
+        u.y = pack_bf16x2(v[2], v[3]);
         const int q = wn * (WN / 8) + j * 4 + qd;
         st8[(m * CQ + (q ^ swz)) * 2 + fk] = u;
       }
@@ -894,8 +894,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(
         for (int e = 0; e < 4; ++e)
           v[e] = epilogue_bf16<EPI>(z[e], GATED ? acc[i + 4 * (TN + jx)][qd * 4 + e] : 0.f);
         uint2 uu;
-        uu.x = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
-        uu.y = (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
+        uu.x = pack_bf16x2(v[0], v[1]);
+        uu.y = pack_bf16x2(v[2], v[3]);
         const int q = wn * (WN / 8) + jx * 4 + qd;
         st8[(m * CQ + (q ^ (m & 15))) * 2 + fk] = uu;
       }

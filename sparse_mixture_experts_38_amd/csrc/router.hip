@@ -70,6 +70,119 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const XT* __restrict
   }
 }
 
+// logits on MFMA for up to 16 experts with bf16 x (v_mfma_f32_16x16x32_bf16,
+// tokens as rows, experts as columns, experts past E held at zero weight).
+// A float32 W_g enters as three bf16 planes, w = hi + mid + lo with hi the
+// bf16 rounding of w, mid that of w - hi and lo that of the rest (all 24
+// significand bits), so x w = x hi + x mid + x lo with every product exact
+// in float32: the logits match a float32 dot product to within float32
+// accumulation error. A bf16 W_g is one plane. One block takes 32 tokens and
+// K in 1024-deep chunks: a chunk's x fragments (16 per lane) and W_g values
+// (64 per thread: 8 experts x 2 adjacent k x 4 tiles of 256) are loaded at
+// once, W_g is written to LDS as bf16 planes, and after one barrier wave w
+// multiplies k in [64 w, 64 w + 64) of each 256-deep tile; the four waves'
+// sums are added in wave order at the end.
+template <bool W_F32>
+__global__ __launch_bounds__(256) void router_logits_mfma_kernel(
+    const bf16* __restrict__ x, const void* __restrict__ wg, const float* __restrict__ bg,
+    float* __restrict__ logits, int64_t T, int d, int E) {
+  constexpr int NP = W_F32 ? 3 : 1;
+  constexpr int KC = 1024, ROW = KC + 8;   // padded LDS row (bf16)
+  __shared__ bf16 wp[NP][16][ROW];
+  __shared__ float red[4][32][17];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15, kq = lane >> 4;
+  const int e0 = (tid >> 7) * 8;      // this thread's 8 experts (staging)
+  const int kp = (tid & 127) * 2;     // and its 2 adjacent k of each tile
+  const int64_t t0 = (int64_t)blockIdx.x * 32;
+  const int64_t ta = min(t0 + r, T - 1), tb = min(t0 + 16 + r, T - 1);
+  f32x4 acc[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) acc[m] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int kc = 0; kc < d; kc += KC) {
+    const int ntile = min(4, (d - kc) / 256);
+    bf16x8 xa[4][2][2];
+    float2 wv[4][8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (j < ntile) {
+        const int kb = kc + j * 256;
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const int kk = kb + wave * 64 + s2 * 32 + kq * 8;
+          xa[j][s2][0] = *reinterpret_cast<const bf16x8*>(x + ta * d + kk);
+          xa[j][s2][1] = *reinterpret_cast<const bf16x8*>(x + tb * d + kk);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          wv[j][e] = make_float2(0.f, 0.f);
+          if (e0 + e < E) {
+            const int64_t o = (int64_t)(e0 + e) * d + kb + kp;
+            if constexpr (W_F32) {
+              wv[j][e] = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(wg) + o);
+            } else {
+              const uint32_t u = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const bf16*>(wg) + o);
+              wv[j][e] = make_float2(bf16_bits_to_f32(u & 0xffffu), bf16_bits_to_f32(u >> 16));
+            }
+          }
+        }
+      }
+    }
+    if (kc > 0) __syncthreads();   // the previous chunk's planes have been read
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (j < ntile) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float2 w = wv[j][e];
+          const uint32_t hq = pack_bf16x2(w.x, w.y);
+          *reinterpret_cast<uint32_t*>(&wp[0][e0 + e][j * 256 + kp]) = hq;
+          if constexpr (W_F32) {
+            const float hx = bf16_bits_to_f32(hq & 0xffffu), hy = bf16_bits_to_f32(hq >> 16);
+            const float rx = w.x - hx, ry = w.y - hy;
+            const uint32_t mq = pack_bf16x2(rx, ry);
+            *reinterpret_cast<uint32_t*>(&wp[1][e0 + e][j * 256 + kp]) = mq;
+            *reinterpret_cast<uint32_t*>(&wp[2][e0 + e][j * 256 + kp]) =
+                pack_bf16x2(rx - bf16_bits_to_f32(mq & 0xffffu), ry - bf16_bits_to_f32(mq >> 16));
+          }
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (j < ntile) {
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const int kk = j * 256 + wave * 64 + s2 * 32 + kq * 8;
+#pragma unroll
+          for (int pl = 0; pl < NP; ++pl) {
+            const bf16x8 b = *reinterpret_cast<const bf16x8*>(&wp[pl][r][kk]);
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+              acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[j][s2][m], b, acc[m], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+  // element i of lane l holds token 4 (l / 16) + i and expert l % 16 of a subtile
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[wave][m * 16 + 4 * kq + i][r] = acc[m][i];
+  __syncthreads();
+#pragma unroll
+  for (int o = tid; o < 32 * 16; o += 256) {
+    const int tt = o >> 4, e = o & 15;
+    const int64_t t = t0 + tt;
+    if (e < E && t < T) {
+      const float v = ((red[0][tt][e] + red[1][tt][e]) + red[2][tt][e]) + red[3][tt][e];
+      logits[t * E + e] = bg ? v + bg[e] : v;
+    }
+  }
+}
+
 // (key, index) order used for selection: larger key first, then lower index.
 // An out-of-range index (>= E) never beats an in-range one.
 __device__ __forceinline__ bool better(float ka, int ia, float kb, int ib, int E) {
@@ -277,7 +390,15 @@ hipError_t launch_router_logits(const moe_config& c, const void* x, const void* 
   const int blocks = (int)((waves + 3) / 4 < 4096 ? (waves + 3) / 4 : 4096);
   if (router_kparts(c) > 0)
     return launch_router_gemm(c, x, w_gate, bg, router_planes, lg, s);
-  else if (c.act_dtype == MOE_BF16 && c.router_dtype == MOE_F32)
+  if (c.act_dtype == MOE_BF16 && E <= 16 && d % 256 == 0) {
+    const unsigned mblocks = (unsigned)((c.tokens + 31) / 32);
+    if (c.router_dtype == MOE_F32)
+      hipLaunchKernelGGL((router_logits_mfma_kernel<true>), dim3(mblocks), dim3(256), 0, s,
+                         (const bf16*)x, w_gate, bg, lg, (int64_t)c.tokens, d, E);
+    else
+      hipLaunchKernelGGL((router_logits_mfma_kernel<false>), dim3(mblocks), dim3(256), 0, s,
+                         (const bf16*)x, w_gate, bg, lg, (int64_t)c.tokens, d, E);
+  } else if (c.act_dtype == MOE_BF16 && c.router_dtype == MOE_F32)
     hipLaunchKernelGGL((router_logits_kernel<bf16, float>), dim3(blocks), dim3(256), 0, s,
                        (const bf16*)x, (const float*)w_gate, bg, lg, (int64_t)c.tokens, d, E);
   else if (c.act_dtype == MOE_BF16)
