@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -28,7 +30,9 @@ WsLayout workspace_layout(const moe_config& c) {
   L.route_iters = (int)iters;
   L.route_blocks = (int)(groups > 0 ? (groups + iters - 1) / iters : 1);
   L.logits = take((size_t)T * E * sizeof(float));
-  L.route_partials = take((size_t)L.route_blocks * (E + 1) * sizeof(float));
+  // (the MFMA router for a few experts writes one row per 32 tokens instead)
+  const int64_t pblocks = std::max<int64_t>(L.route_blocks, (T + 31) / 32);
+  L.route_partials = take((size_t)pblocks * (E + 1) * sizeof(float));
   L.router_planes = take((size_t)router_kparts(c) * T * E * sizeof(float));
   L.end_route = off;
   L.chunks = (int)(A > 0 ? (A + kRankChunk - 1) / kRankChunk : 1);

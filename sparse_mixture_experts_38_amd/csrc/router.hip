@@ -70,6 +70,177 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const XT* __restrict
   }
 }
 
+// (key, index) order used for selection: larger key first, then lower index.
+// An out-of-range index (>= E) never beats an in-range one.
+__device__ __forceinline__ bool better(float ka, int ia, float kb, int ib, int E) {
+  if (ia >= E) return false;
+  if (ib >= E) return true;
+  return ka > kb || (ka == kb && ia < ib);
+}
+
+// Score function + top-k + gates of one token, held by L lanes with J experts
+// per lane (expert e = lane_in_group + L * jj, l[jj] its logit, -inf past E):
+// writes the token's top-k when valid and adds its P contribution per expert
+// to pacc and its lse^2 to lacc.
+template <int L, int J>
+__device__ __forceinline__ void route_token(const float l[J], bool valid, int64_t t, int lg, int tid,
+                                            int E, int k, int sigmoid,
+                                            const float* __restrict__ e_bias,
+                                            int32_t* __restrict__ topk_idx,
+                                            float* __restrict__ topk_gate, float pacc[J],
+                                            float& lacc) {
+  float key[J], sc[J];
+  bool taken[J];
+  float m = -INFINITY;
+#pragma unroll
+  for (int jj = 0; jj < J; ++jj) {
+    const int e = lg + L * jj;
+    taken[jj] = false;
+    if (e < E) m = fmaxf(m, l[jj]);
+  }
+#pragma unroll
+  for (int off = L / 2; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, L));
+  float ex[J];
+  float s = 0.f;
+#pragma unroll
+  for (int jj = 0; jj < J; ++jj) {
+    const int e = lg + L * jj;
+    ex[jj] = (e < E) ? expf(l[jj] - m) : 0.f;
+    s += ex[jj];
+  }
+#pragma unroll
+  for (int off = L / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off, L);
+  const float lse = m + logf(s);
+  float ssum = 0.f;
+  if (!sigmoid) {
+    const float inv = 1.0f / s;
+#pragma unroll
+    for (int jj = 0; jj < J; ++jj) {
+      sc[jj] = ex[jj] * inv;   // p
+      key[jj] = l[jj];         // softmax is increasing: rank by logit
+    }
+  } else {
+#pragma unroll
+    for (int jj = 0; jj < J; ++jj) {
+      const int e = lg + L * jj;
+      if (e < E) {
+        sc[jj] = 1.0f / (1.0f + expf(-l[jj]));
+        key[jj] = e_bias ? sc[jj] + e_bias[e] : sc[jj];
+      } else {
+        sc[jj] = 0.f;
+        key[jj] = -INFINITY;
+      }
+      ssum += sc[jj];
+    }
+#pragma unroll
+    for (int off = L / 2; off >= 1; off >>= 1) ssum += __shfl_xor(ssum, off, L);
+  }
+
+  int sel_idx[MOE_MAX_TOP_K];
+  float sel_sc[MOE_MAX_TOP_K];
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOP_K; ++j) {
+    sel_idx[j] = 0;
+    sel_sc[j] = 0.f;
+    if (j < k) {
+      float bk = -INFINITY;
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int jj = 0; jj < J; ++jj) {
+        const int e = lg + L * jj;
+        if (e < E && !taken[jj] && better(key[jj], e, bk, bi, E)) {
+          bk = key[jj];
+          bi = e;
+        }
+      }
+#pragma unroll
+      for (int off = L / 2; off >= 1; off >>= 1) {
+        const float ok = __shfl_xor(bk, off, L);
+        const int oi = __shfl_xor(bi, off, L);
+        if (better(ok, oi, bk, bi, E)) {
+          bk = ok;
+          bi = oi;
+        }
+      }
+      // bi is uniform over the group; fetch its score from the owning lane.
+      const int owner_j = bi / L;
+      float mine = 0.f;
+#pragma unroll
+      for (int jj = 0; jj < J; ++jj) {
+        if (jj == owner_j) mine = sc[jj];
+        if (jj == owner_j && lg == bi % L) taken[jj] = true;
+      }
+      sel_idx[j] = bi;
+      sel_sc[j] = __shfl(mine, (tid & ~(L - 1) & 63) + bi % L, 64);
+    }
+  }
+  float tsum = 0.f;
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOP_K; ++j)
+    if (j < k) tsum += sel_sc[j];
+  const float tinv = 1.0f / tsum;
+  if (valid) {
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOP_K; ++j) {
+      if (j < k && lg == j) {
+        topk_idx[t * k + j] = sel_idx[j];
+        topk_gate[t * k + j] = sel_sc[j] * tinv;
+      }
+    }
+    const float pinv = sigmoid ? 1.0f / ssum : 1.0f;
+#pragma unroll
+    for (int jj = 0; jj < J; ++jj) pacc[jj] += sc[jj] * pinv;
+    lacc += lse * lse;
+  }
+}
+
+// Score function + top-k + gates for L lanes per token, J experts per lane
+// (expert e = lane_in_group + L * jj). Also accumulates, per block and in a
+// fixed order, sum_t P-contribution per expert and sum_t lse_t^2.
+template <int L, int J>
+__global__ __launch_bounds__(256) void router_topk_kernel(
+    const float* __restrict__ logits, const float* __restrict__ e_bias, int64_t T, int E, int k,
+    int sigmoid, int iters, int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate,
+    float* __restrict__ partials) {
+  constexpr int GPB = 256 / L;
+  __shared__ float red[GPB * L * J];
+  __shared__ float red2[GPB];
+  const int tid = threadIdx.x;
+  const int g = tid / L;
+  const int lg = tid % L;
+  float pacc[J];
+#pragma unroll
+  for (int jj = 0; jj < J; ++jj) pacc[jj] = 0.f;
+  float lacc = 0.f;
+
+  for (int it = 0; it < iters; ++it) {
+    const int64_t t = ((int64_t)blockIdx.x * iters + it) * GPB + g;
+    const bool valid = t < T;
+    float l[J];
+#pragma unroll
+    for (int jj = 0; jj < J; ++jj) {
+      const int e = lg + L * jj;
+      l[jj] = (e < E) ? (valid ? logits[t * E + e] : 0.f) : -INFINITY;
+    }
+    route_token<L, J>(l, valid, t, lg, tid, E, k, sigmoid, e_bias, topk_idx, topk_gate, pacc, lacc);
+  }
+
+#pragma unroll
+  for (int jj = 0; jj < J; ++jj) red[g * L * J + jj * L + lg] = pacc[jj];
+  if (lg == 0) red2[g] = lacc;
+  __syncthreads();
+  for (int e = tid; e < E; e += 256) {
+    float s = 0.f;
+    for (int gg = 0; gg < GPB; ++gg) s += red[gg * L * J + e];
+    partials[(int64_t)blockIdx.x * (E + 1) + e] = s;
+  }
+  if (tid == 0) {
+    float s = 0.f;
+    for (int gg = 0; gg < GPB; ++gg) s += red2[gg];
+    partials[(int64_t)blockIdx.x * (E + 1) + E] = s;
+  }
+}
+
 // logits on MFMA for up to 16 experts with bf16 x (v_mfma_f32_16x16x32_bf16,
 // tokens as rows, experts as columns, experts past E held at zero weight).
 // A float32 W_g enters as three bf16 planes, w = hi + mid + lo with hi the
@@ -82,10 +253,15 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const XT* __restrict
 // once, W_g is written to LDS as bf16 planes, and after one barrier wave w
 // multiplies k in [64 w, 64 w + 64) of each 256-deep tile; the four waves'
 // sums are added in wave order at the end.
-template <bool W_F32>
+// With LR > 0 the same block then routes its 32 tokens (route_token with LR
+// lanes per token, on exactly the logits it stored) and writes its partial
+// sums of P_i and lse^2, as router_topk_kernel does.
+template <bool W_F32, int LR>
 __global__ __launch_bounds__(256) void router_logits_mfma_kernel(
     const bf16* __restrict__ x, const void* __restrict__ wg, const float* __restrict__ bg,
-    float* __restrict__ logits, int64_t T, int d, int E) {
+    float* __restrict__ logits, int64_t T, int d, int E, const float* __restrict__ e_bias,
+    int k, int sigmoid, int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate,
+    float* __restrict__ partials) {
   constexpr int NP = W_F32 ? 3 : 1;
   constexpr int KC = 1024, ROW = KC + 8;   // padded LDS row (bf16)
   __shared__ bf16 wp[NP][16][ROW];
@@ -181,157 +357,42 @@ __global__ __launch_bounds__(256) void router_logits_mfma_kernel(
       logits[t * E + e] = bg ? v + bg[e] : v;
     }
   }
-}
-
-// (key, index) order used for selection: larger key first, then lower index.
-// An out-of-range index (>= E) never beats an in-range one.
-__device__ __forceinline__ bool better(float ka, int ia, float kb, int ib, int E) {
-  if (ia >= E) return false;
-  if (ib >= E) return true;
-  return ka > kb || (ka == kb && ia < ib);
-}
-
-// Score function + top-k + gates for L lanes per token, J experts per lane
-// (expert e = lane_in_group + L * jj). Also accumulates, per block and in a
-// fixed order, sum_t P-contribution per expert and sum_t lse_t^2.
-template <int L, int J>
-__global__ __launch_bounds__(256) void router_topk_kernel(
-    const float* __restrict__ logits, const float* __restrict__ e_bias, int64_t T, int E, int k,
-    int sigmoid, int iters, int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate,
-    float* __restrict__ partials) {
-  constexpr int GPB = 256 / L;
-  __shared__ float red[GPB * L * J];
-  __shared__ float red2[GPB];
-  const int tid = threadIdx.x;
-  const int g = tid / L;
-  const int lg = tid % L;
-  float pacc[J];
+  if constexpr (LR > 0) {
+    constexpr int TPP = 256 / LR;   // tokens per pass
+    __shared__ float rp[256], rl[256];
+    const int lg = tid % LR;
+    float pacc[1] = {0.f};
+    float lacc = 0.f;
 #pragma unroll
-  for (int jj = 0; jj < J; ++jj) pacc[jj] = 0.f;
-  float lacc = 0.f;
-
-  for (int it = 0; it < iters; ++it) {
-    const int64_t t = ((int64_t)blockIdx.x * iters + it) * GPB + g;
-    const bool valid = t < T;
-    float l[J], key[J], sc[J];
-    bool taken[J];
-    float m = -INFINITY;
-#pragma unroll
-    for (int jj = 0; jj < J; ++jj) {
-      const int e = lg + L * jj;
-      l[jj] = (e < E) ? (valid ? logits[t * E + e] : 0.f) : -INFINITY;
-      taken[jj] = false;
-      if (e < E) m = fmaxf(m, l[jj]);
-    }
-#pragma unroll
-    for (int off = L / 2; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, L));
-    float ex[J];
-    float s = 0.f;
-#pragma unroll
-    for (int jj = 0; jj < J; ++jj) {
-      const int e = lg + L * jj;
-      ex[jj] = (e < E) ? expf(l[jj] - m) : 0.f;
-      s += ex[jj];
-    }
-#pragma unroll
-    for (int off = L / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off, L);
-    const float lse = m + logf(s);
-    float ssum = 0.f;
-    if (!sigmoid) {
-      const float inv = 1.0f / s;
-#pragma unroll
-      for (int jj = 0; jj < J; ++jj) {
-        sc[jj] = ex[jj] * inv;   // p
-        key[jj] = l[jj];         // softmax is increasing: rank by logit
-      }
-    } else {
-#pragma unroll
-      for (int jj = 0; jj < J; ++jj) {
-        const int e = lg + L * jj;
-        if (e < E) {
-          sc[jj] = 1.0f / (1.0f + expf(-l[jj]));
-          key[jj] = e_bias ? sc[jj] + e_bias[e] : sc[jj];
-        } else {
-          sc[jj] = 0.f;
-          key[jj] = -INFINITY;
-        }
-        ssum += sc[jj];
-      }
-#pragma unroll
-      for (int off = L / 2; off >= 1; off >>= 1) ssum += __shfl_xor(ssum, off, L);
-    }
-
-    int sel_idx[MOE_MAX_TOP_K];
-    float sel_sc[MOE_MAX_TOP_K];
-#pragma unroll
-    for (int j = 0; j < MOE_MAX_TOP_K; ++j) {
-      sel_idx[j] = 0;
-      sel_sc[j] = 0.f;
-      if (j < k) {
-        float bk = -INFINITY;
-        int bi = 0x7fffffff;
-#pragma unroll
-        for (int jj = 0; jj < J; ++jj) {
-          const int e = lg + L * jj;
-          if (e < E && !taken[jj] && better(key[jj], e, bk, bi, E)) {
-            bk = key[jj];
-            bi = e;
-          }
-        }
-#pragma unroll
-        for (int off = L / 2; off >= 1; off >>= 1) {
-          const float ok = __shfl_xor(bk, off, L);
-          const int oi = __shfl_xor(bi, off, L);
-          if (better(ok, oi, bk, bi, E)) {
-            bk = ok;
-            bi = oi;
-          }
-        }
-        // bi is uniform over the group; fetch its score from the owning lane.
-        const int owner_j = bi / L;
-        float mine = 0.f;
-#pragma unroll
-        for (int jj = 0; jj < J; ++jj) {
-          if (jj == owner_j) mine = sc[jj];
-          if (jj == owner_j && lg == bi % L) taken[jj] = true;
-        }
-        sel_idx[j] = bi;
-        sel_sc[j] = __shfl(mine, (tid & ~(L - 1) & 63) + bi % L, 64);
-      }
-    }
-    float tsum = 0.f;
-#pragma unroll
-    for (int j = 0; j < MOE_MAX_TOP_K; ++j)
-      if (j < k) tsum += sel_sc[j];
-    const float tinv = 1.0f / tsum;
-    if (valid) {
-#pragma unroll
-      for (int j = 0; j < MOE_MAX_TOP_K; ++j) {
-        if (j < k && lg == j) {
-          topk_idx[t * k + j] = sel_idx[j];
-          topk_gate[t * k + j] = sel_sc[j] * tinv;
+    for (int tt0 = 0; tt0 < 32; tt0 += TPP) {
+      const int tt = tt0 + tid / LR;
+      const int64_t t = t0 + tt;
+      const bool valid = tt < 32 && t < T;
+      float l[1];
+      l[0] = -INFINITY;
+      if (lg < E) {
+        l[0] = 0.f;
+        if (valid) {
+          const float v = ((red[0][tt][lg] + red[1][tt][lg]) + red[2][tt][lg]) + red[3][tt][lg];
+          l[0] = bg ? v + bg[lg] : v;
         }
       }
-      const float pinv = sigmoid ? 1.0f / ssum : 1.0f;
-#pragma unroll
-      for (int jj = 0; jj < J; ++jj) pacc[jj] += sc[jj] * pinv;
-      lacc += lse * lse;
+      route_token<LR, 1>(l, valid, t, lg, tid, E, k, sigmoid, e_bias, topk_idx, topk_gate, pacc,
+                         lacc);
     }
-  }
-
-#pragma unroll
-  for (int jj = 0; jj < J; ++jj) red[g * L * J + jj * L + lg] = pacc[jj];
-  if (lg == 0) red2[g] = lacc;
-  __syncthreads();
-  for (int e = tid; e < E; e += 256) {
-    float s = 0.f;
-    for (int gg = 0; gg < GPB; ++gg) s += red[gg * L * J + e];
-    partials[(int64_t)blockIdx.x * (E + 1) + e] = s;
-  }
-  if (tid == 0) {
-    float s = 0.f;
-    for (int gg = 0; gg < GPB; ++gg) s += red2[gg];
-    partials[(int64_t)blockIdx.x * (E + 1) + E] = s;
+    rp[tid] = pacc[0];
+    rl[tid] = lacc;
+    __syncthreads();
+    if (tid < E) {
+      float sum = 0.f;
+      for (int g = 0; g < TPP; ++g) sum += rp[g * LR + tid];
+      partials[(int64_t)blockIdx.x * (E + 1) + tid] = sum;
+    }
+    if (tid == 0) {
+      float sum = 0.f;
+      for (int g = 0; g < TPP; ++g) sum += rl[g * LR];
+      partials[(int64_t)blockIdx.x * (E + 1) + E] = sum;
+    }
   }
 }
 
@@ -380,6 +441,23 @@ int route_lanes(int E) {
   return L;
 }
 
+// The MFMA logits kernel for a few experts (bf16 x, at most 16 experts).
+static bool router_mfma_small(const moe_config& c) {
+  return router_kparts(c) == 0 && c.act_dtype == MOE_BF16 && c.num_experts <= 16 &&
+         c.d_model % 256 == 0;
+}
+
+template <bool W_F32, int LR>
+static void launch_route_fused(const moe_config& c, const void* x, const void* w_gate,
+                               const float* bg, float* lg, const float* eb, int32_t* idx,
+                               float* gate, float* partials, hipStream_t s) {
+  const unsigned mblocks = (unsigned)((c.tokens + 31) / 32);
+  hipLaunchKernelGGL((router_logits_mfma_kernel<W_F32, LR>), dim3(mblocks), dim3(256), 0, s,
+                     (const bf16*)x, w_gate, bg, lg, (int64_t)c.tokens, (int)c.d_model,
+                     c.num_experts, eb, c.top_k, c.score_fn == MOE_SCORE_SIGMOID ? 1 : 0, idx,
+                     gate, partials);
+}
+
 hipError_t launch_router_logits(const moe_config& c, const void* x, const void* w_gate,
                                 const float* b_gate, float* lg, float* router_planes,
                                 hipStream_t s) {
@@ -390,14 +468,16 @@ hipError_t launch_router_logits(const moe_config& c, const void* x, const void* 
   const int blocks = (int)((waves + 3) / 4 < 4096 ? (waves + 3) / 4 : 4096);
   if (router_kparts(c) > 0)
     return launch_router_gemm(c, x, w_gate, bg, router_planes, lg, s);
-  if (c.act_dtype == MOE_BF16 && E <= 16 && d % 256 == 0) {
+  if (router_mfma_small(c)) {
     const unsigned mblocks = (unsigned)((c.tokens + 31) / 32);
     if (c.router_dtype == MOE_F32)
-      hipLaunchKernelGGL((router_logits_mfma_kernel<true>), dim3(mblocks), dim3(256), 0, s,
-                         (const bf16*)x, w_gate, bg, lg, (int64_t)c.tokens, d, E);
+      hipLaunchKernelGGL((router_logits_mfma_kernel<true, 0>), dim3(mblocks), dim3(256), 0, s,
+                         (const bf16*)x, w_gate, bg, lg, (int64_t)c.tokens, d, E, nullptr, 0, 0,
+                         nullptr, nullptr, nullptr);
     else
-      hipLaunchKernelGGL((router_logits_mfma_kernel<false>), dim3(mblocks), dim3(256), 0, s,
-                         (const bf16*)x, w_gate, bg, lg, (int64_t)c.tokens, d, E);
+      hipLaunchKernelGGL((router_logits_mfma_kernel<false, 0>), dim3(mblocks), dim3(256), 0, s,
+                         (const bf16*)x, w_gate, bg, lg, (int64_t)c.tokens, d, E, nullptr, 0, 0,
+                         nullptr, nullptr, nullptr);
   } else if (c.act_dtype == MOE_BF16 && c.router_dtype == MOE_F32)
     hipLaunchKernelGGL((router_logits_kernel<bf16, float>), dim3(blocks), dim3(256), 0, s,
                        (const bf16*)x, (const float*)w_gate, bg, lg, (int64_t)c.tokens, d, E);
@@ -420,11 +500,33 @@ hipError_t launch_route(const moe_config& c, const WsLayout& L, const void* x, c
   float* lg = logits ? logits : reinterpret_cast<float*>(ws + L.logits);
   float* partials = reinterpret_cast<float*>(ws + L.route_partials);
   const float* eb = c.score_fn == MOE_SCORE_SIGMOID ? e_bias : nullptr;
+  const int Ln = route_lanes(E);
+  if (router_mfma_small(c)) {
+    // logits, top-k and the block partials in one kernel
+    const float* bg = c.has_gate_bias ? b_gate : nullptr;
+    const bool f32w = c.router_dtype == MOE_F32;
+    switch (Ln) {
+      case 1: f32w ? launch_route_fused<true, 1>(c, x, w_gate, bg, lg, eb, topk_idx, topk_gate, partials, s)
+                   : launch_route_fused<false, 1>(c, x, w_gate, bg, lg, eb, topk_idx, topk_gate, partials, s); break;
+      case 2: f32w ? launch_route_fused<true, 2>(c, x, w_gate, bg, lg, eb, topk_idx, topk_gate, partials, s)
+                   : launch_route_fused<false, 2>(c, x, w_gate, bg, lg, eb, topk_idx, topk_gate, partials, s); break;
+      case 4: f32w ? launch_route_fused<true, 4>(c, x, w_gate, bg, lg, eb, topk_idx, topk_gate, partials, s)
+                   : launch_route_fused<false, 4>(c, x, w_gate, bg, lg, eb, topk_idx, topk_gate, partials, s); break;
+      case 8: f32w ? launch_route_fused<true, 8>(c, x, w_gate, bg, lg, eb, topk_idx, topk_gate, partials, s)
+                   : launch_route_fused<false, 8>(c, x, w_gate, bg, lg, eb, topk_idx, topk_gate, partials, s); break;
+      default: f32w ? launch_route_fused<true, 16>(c, x, w_gate, bg, lg, eb, topk_idx, topk_gate, partials, s)
+                    : launch_route_fused<false, 16>(c, x, w_gate, bg, lg, eb, topk_idx, topk_gate, partials, s);
+    }
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(route_stats_kernel, dim3(E + 2), dim3(256), 0, s, partials,
+                       (int)((c.tokens + 31) / 32), E, (int64_t)c.tokens, stats);
+    return hipGetLastError();
+  }
   hipError_t err = launch_router_logits(c, x, w_gate, b_gate, lg,
                                         reinterpret_cast<float*>(ws + L.router_planes), s);
   if (err != hipSuccess) return err;
 
-  const int Ln = route_lanes(E);
   switch (Ln) {
     case 1: launch_topk_lj<1, 1>(c, L, lg, eb, topk_idx, topk_gate, partials, s); break;
     case 2: launch_topk_lj<2, 1>(c, L, lg, eb, topk_idx, topk_gate, partials, s); break;

@@ -46,6 +46,13 @@ CASES = {
     "gelu_long_k": W["deepspeed_gpt_moe"].scaled(tokens=600, d_model=2048, d_ff=512, num_experts=4,
                                                  drop_tokens=False),
     "swiglu_long_k": W["mixtral_8x7b"].scaled(tokens=600, d_model=2048, d_ff=512, num_experts=4),
+    # the fused MFMA router at its widest (16 experts, 16 lanes per token, two
+    # routing passes per block): sigmoid scores with the selection bias, top-4
+    "sigmoid_16": W["deepseek_v3"].scaled(tokens=999, d_model=512, d_ff=256, num_experts=16,
+                                          top_k=4),
+    # and at its narrowest: two experts, top-1, fp32 W_g, gate bias
+    "two_experts": W["deepspeed_gpt_moe"].scaled(tokens=517, d_model=256, d_ff=256,
+                                                 num_experts=2, top_k=1, has_gate_bias=True),
 }
 
 
