@@ -53,6 +53,10 @@ CASES = {
     # and at its narrowest: two experts, top-1, fp32 W_g, gate bias
     "two_experts": W["deepspeed_gpt_moe"].scaled(tokens=517, d_model=256, d_ff=256,
                                                  num_experts=2, top_k=1, has_gate_bias=True),
+    # 16 experts with an fp32 W_g (three bf16 planes), top-3; d_model 1280 gives the
+    # router a second, one-tile K chunk and GEMM 1 a K loop of 20 steps
+    "f32_router_16": W["deepspeed_gpt_moe"].scaled(tokens=640, d_model=1280, d_ff=512,
+                                                   num_experts=16, top_k=3, has_gate_bias=True),
 }
 
 
