@@ -257,17 +257,55 @@ __global__ __launch_bounds__(256) void ec_combine_kernel(const T_* __restrict__ 
   for (int e = lane; e < E; e += 64) picked |= token_row[t * E + e] >= 0;
   const uint64_t any_picked = __ballot(picked);   // every lane takes part in the ballot
   if (lane == 0 && any_picked == 0ull) atomicAdd(&stats->dropped, 1);
-  for (int c = lane * 8; c < d; c += 512) {
+  // every lane runs every column step (the ballots and shuffles below need the
+  // whole wavefront); lanes past d only skip their loads and stores
+  for (int c0 = 0; c0 < d; c0 += 512) {
+    const int c = c0 + lane * 8;
+    const bool active = c < d;
     float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int e = 0; e < E; ++e) {
-      const int r = token_row[t * E + e];
-      if (r < 0 || r >= nrows) continue;
-      const float g = gates[r];
-      float a[8];
-      load8(y_perm + (int64_t)r * d + c, a);
+    // experts in ascending order, 64 at a time: lane e holds expert e0 + e's row
+    // and gate; the picked rows are then read four at a time (loads in flight
+    // together) and added in expert order
+    for (int e0 = 0; e0 < E; e0 += 64) {
+      int myr = -1;
+      float myg = 0.f;
+      if (e0 + lane < E) {
+        const int r = token_row[t * E + e0 + lane];
+        if (r >= 0 && r < nrows) {
+          myr = r;
+          myg = gates[r];
+        }
+      }
+      uint64_t mask = __ballot(myr >= 0);
+      while (mask) {
+        int rr[4];
+        float gg[4];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = fmaf(g, a[u], v[u]);
+        for (int q = 0; q < 4; ++q) {
+          rr[q] = -1;
+          gg[q] = 0.f;
+          if (mask) {
+            const int e = __ffsll((unsigned long long)mask) - 1;
+            mask &= mask - 1;
+            rr[q] = __shfl(myr, e, 64);
+            gg[q] = __shfl(myg, e, 64);
+          }
+        }
+        float a[4][8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (active && rr[q] >= 0) load8(y_perm + (int64_t)rr[q] * d + c, a[q]);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (active && rr[q] >= 0) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = fmaf(gg[q], a[q][u], v[u]);
+          }
+        }
+      }
     }
+    if (!active) continue;
     if (S) {
       float a[8];
       load8(y_perm + (nrows + t) * d + c, a);
