@@ -55,6 +55,7 @@ __global__ __launch_bounds__(256) void ec_lse_kernel(const float* __restrict__ l
 // Block-wide exclusive prefix sum of one int per thread (256 threads, 4
 // wavefronts): wave scans by shuffles, then the wave totals. Returns the prefix
 // and writes the block total to *total.
+template <int NW>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* wave_tot, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int incl = v;
@@ -65,9 +66,13 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wave_tot, int* t
   }
   if (lane == 63) wave_tot[wave] = incl;
   __syncthreads();
-  int before = 0;
-  for (int w = 0; w < wave; ++w) before += wave_tot[w];
-  *total = wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    before += w < wave ? wave_tot[w] : 0;
+    all += wave_tot[w];
+  }
+  *total = all;
   __syncthreads();   // wave_tot is reused by the next call
   return before + incl - v;
 }
@@ -87,17 +92,19 @@ constexpr int kEcLdsKeys = 16384;   // keys and lse of one expert kept in LDS (1
 // tokens[e][i] = t, gates[e][i] = p[t][e], token_row[t][e] = e C + i,
 // rows[e C + i] = t. It also writes P_e (mean of p[t][e], float64 tree) and the
 // balance counts of expert e into stats.
-__global__ __launch_bounds__(256) void ec_select_kernel(
+constexpr int kEcSelectThreads = 1024;
+__global__ __launch_bounds__(kEcSelectThreads) void ec_select_kernel(
     const float* __restrict__ logits, const float* __restrict__ lse, int64_t T, int E, int64_t C,
     int32_t* __restrict__ tokens, float* __restrict__ gates, int32_t* __restrict__ token_row,
     int32_t* __restrict__ rows, moe_stats* __restrict__ stats) {
   __shared__ uint32_t keys[kEcLdsKeys];
   __shared__ float lse_s[kEcLdsKeys];
+  constexpr int NT = kEcSelectThreads, NW = NT / 64;
   __shared__ int hist[256];
-  __shared__ int wave_tot[4];
+  __shared__ int wave_tot[NW];
   __shared__ uint32_t s_prefix;
   __shared__ int s_remaining;
-  __shared__ double red[256];
+  __shared__ double red[NT];
   const int e = blockIdx.x;
   const int tid = threadIdx.x;
   const bool in_lds = T <= kEcLdsKeys;
@@ -107,17 +114,17 @@ __global__ __launch_bounds__(256) void ec_select_kernel(
   auto lse_at = [&](int64_t t) -> float { return in_lds ? lse_s[t] : lse[t]; };
   if (in_lds) {
     // eight loads in flight per thread
-    for (int64_t t0 = 0; t0 < T; t0 += 8 * 256) {
+    for (int64_t t0 = 0; t0 < T; t0 += 8 * NT) {
       float v[8], l[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int64_t t = t0 + u * 256 + tid;
+        const int64_t t = t0 + u * NT + tid;
         v[u] = t < T ? logits[t * E + e] : 0.f;
         l[u] = t < T ? lse[t] : 0.f;
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int64_t t = t0 + u * 256 + tid;
+        const int64_t t = t0 + u * NT + tid;
         if (t < T) {
           keys[t] = score_key(v[u]);
           lse_s[t] = l[u];
@@ -128,9 +135,9 @@ __global__ __launch_bounds__(256) void ec_select_kernel(
   uint32_t prefix = 0, mask = 0;
   int remaining = (int)C;
   for (int shift = 24; shift >= 0; shift -= 8) {
-    hist[tid] = 0;
+    if (tid < 256) hist[tid] = 0;
     __syncthreads();
-    for (int64_t t = tid; t < T; t += 256) {
+    for (int64_t t = tid; t < T; t += NT) {
       const uint32_t u = key_at(t);
       if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1);
     }
@@ -138,11 +145,12 @@ __global__ __launch_bounds__(256) void ec_select_kernel(
     // digits in descending order, thread i holding digit 255 - i: the digit D is
     // the one at which the running count of larger-or-equal digits first
     // reaches `remaining`
+    // (threads past 256 hold no digit)
     const int dg = 255 - tid;
-    const int cnt = hist[dg];
+    const int cnt = tid < 256 ? hist[dg] : 0;
     int tot = 0;
-    const int above = block_exclusive_scan(cnt, wave_tot, &tot);
-    if (above < remaining && above + cnt >= remaining) {
+    const int above = block_exclusive_scan<NW>(cnt, wave_tot, &tot);
+    if (tid < 256 && above < remaining && above + cnt >= remaining) {
       s_prefix = prefix | ((uint32_t)dg << shift);
       s_remaining = remaining - above;
     }
@@ -152,7 +160,7 @@ __global__ __launch_bounds__(256) void ec_select_kernel(
     mask |= 0xFFu << shift;
   }
   // prefix = K; remaining = tokens with key == K to take (lowest tokens first)
-  const int64_t chunk = (T + 255) / 256;
+  const int64_t chunk = (T + NT - 1) / NT;
   const int64_t lo = tid * chunk < T ? tid * chunk : T;
   const int64_t hi = lo + chunk < T ? lo + chunk : T;
   int n_gt = 0, n_eq = 0;
@@ -162,10 +170,10 @@ __global__ __launch_bounds__(256) void ec_select_kernel(
     n_eq += u == prefix;
   }
   int tot = 0;
-  const int eq_before = block_exclusive_scan(n_eq, wave_tot, &tot);
+  const int eq_before = block_exclusive_scan<NW>(n_eq, wave_tot, &tot);
   int eq_take = remaining - eq_before;
   eq_take = eq_take < 0 ? 0 : (eq_take > n_eq ? n_eq : eq_take);
-  const int pos0 = block_exclusive_scan(n_gt + eq_take, wave_tot, &tot);
+  const int pos0 = block_exclusive_scan<NW>(n_gt + eq_take, wave_tot, &tot);
   int pos = pos0, eq_seen = 0;
   double psum = 0.0;
   for (int64_t t = lo; t < hi; ++t) {
@@ -189,7 +197,7 @@ __global__ __launch_bounds__(256) void ec_select_kernel(
   }
   red[tid] = psum;
   __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
+  for (int w = NT / 2; w > 0; w >>= 1) {
     if (tid < w) red[tid] += red[tid + w];
     __syncthreads();
   }
@@ -367,7 +375,7 @@ hipError_t launch_expert_choice_forward(const moe_config& c, const EcLayout& L, 
   double* zpart = (double*)(ws + L.zpart);
   hipLaunchKernelGGL(ec_lse_kernel, dim3(lb), dim3(256), 0, s, (const float*)lg, T, E, C, S, lse,
                      r.token_row, rows, zpart);
-  hipLaunchKernelGGL(ec_select_kernel, dim3(E), dim3(256), 0, s, (const float*)lg,
+  hipLaunchKernelGGL(ec_select_kernel, dim3(E), dim3(kEcSelectThreads), 0, s, (const float*)lg,
                      (const float*)lse, T, E, C, r.tokens, r.gates, r.token_row, rows, stats);
   hipLaunchKernelGGL(ec_finalize_kernel, dim3(1), dim3(256), 0, s, (const double*)zpart, (int)lb,
                      T, E, C, S, off, stats);
