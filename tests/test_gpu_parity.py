@@ -57,6 +57,10 @@ CASES = {
     # router a second, one-tile K chunk and GEMM 1 a K loop of 20 steps
     "f32_router_16": W["deepspeed_gpt_moe"].scaled(tokens=640, d_model=1280, d_ff=512,
                                                    num_experts=16, top_k=3, has_gate_bias=True),
+    # T above 32768: the fused router writes one partial row per 32 tokens (1250
+    # here), more than the separate top-k kernel's blocks; the dispatch ranks span
+    # many 1024-assignment chunks
+    "many_tokens": W["deepspeed_gpt_moe"].scaled(tokens=40000, d_model=256, d_ff=256),
 }
 
 
