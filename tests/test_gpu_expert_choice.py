@@ -35,6 +35,8 @@ CASES = {
     # capacity T: every expert takes every token (the soft mixture)
     "all_tokens": base.scaled(tokens=200, d_model=256, d_ff=256, num_experts=4, top_k=2,
                               capacity_factor=8.0),
+    # more tokens than the selection keeps in LDS (16384): keys read from the logits
+    "many_tokens": base.scaled(tokens=20000, d_model=256, d_ff=256, num_experts=4),
 }
 
 
