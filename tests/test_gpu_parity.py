@@ -61,6 +61,9 @@ CASES = {
     # here), more than the separate top-k kernel's blocks; the dispatch ranks span
     # many 1024-assignment chunks
     "many_tokens": W["deepspeed_gpt_moe"].scaled(tokens=40000, d_model=256, d_ff=256),
+    # 48 experts: neither the fused router (<= 16) nor the MFMA router (multiples of
+    # 128) applies, so the VALU logits kernel and the separate top-k kernel run
+    "experts_48": W["deepspeed_gpt_moe"].scaled(tokens=900, d_model=256, d_ff=256, num_experts=48),
 }
 
 
