@@ -36,11 +36,14 @@ def kernel_source_hash():
     return hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()[:16]
 
 
-def read_traffic(kernel_key):
+TRAFFIC_WORKLOAD = "deepspeed_gpt_moe"
+
+
+def read_traffic(kernel_key, workload):
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3
-    counter summary, if it was taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", "expert_gemm_deepspeed_gpt_moe_traffic.txt")
-    if not os.path.exists(path):
+    counter summary, if it was taken on this workload and on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"expert_gemm_{TRAFFIC_WORKLOAD}_traffic.txt")
+    if workload != TRAFFIC_WORKLOAD or not os.path.exists(path):
         return None
     vals = {}
     for line in open(path):
@@ -192,7 +195,7 @@ def main():
     dom, dom_ms, dom_flop = (("expert_up", up_ms, up_flop) if up_ms >= down_ms
                              else ("expert_down", down_ms, down_flop))
     achieved = dom_flop / (dom_ms * 1e-3) / 1e12
-    traffic = read_traffic(dom)
+    traffic = read_traffic(dom, w.name)
     result = {
         "metric": METRIC,
         "value": T / (ms_per_step * 1e-3),

@@ -279,28 +279,30 @@ __global__ __launch_bounds__(256) void router_logits_mfma_kernel(
     const int ntile = min(4, (d - kc) / 256);
     bf16x8 xa[4][2][2];
     float2 wv[4][8];
+    // all loads are unconditional so that they issue back to back: tiles past
+    // the chunk's end reload its last tile (never used), and experts past E
+    // read row E - 1 and are zeroed after the load (a load under a branch
+    // gets its own wait for every load in flight)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      if (j < ntile) {
-        const int kb = kc + j * 256;
+      const int kb = kc + min(j, ntile - 1) * 256;
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const int kk = kb + wave * 64 + s2 * 32 + kq * 8;
-          xa[j][s2][0] = *reinterpret_cast<const bf16x8*>(x + ta * d + kk);
-          xa[j][s2][1] = *reinterpret_cast<const bf16x8*>(x + tb * d + kk);
-        }
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int kk = kb + wave * 64 + s2 * 32 + kq * 8;
+        xa[j][s2][0] = *reinterpret_cast<const bf16x8*>(x + ta * d + kk);
+        xa[j][s2][1] = *reinterpret_cast<const bf16x8*>(x + tb * d + kk);
+      }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          wv[j][e] = make_float2(0.f, 0.f);
-          if (e0 + e < E) {
-            const int64_t o = (int64_t)(e0 + e) * d + kb + kp;
-            if constexpr (W_F32) {
-              wv[j][e] = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(wg) + o);
-            } else {
-              const uint32_t u = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const bf16*>(wg) + o);
-              wv[j][e] = make_float2(bf16_bits_to_f32(u & 0xffffu), bf16_bits_to_f32(u >> 16));
-            }
-          }
+      for (int e = 0; e < 8; ++e) {
+        const bool live = e0 + e < E;
+        const int64_t o = (int64_t)min(e0 + e, E - 1) * d + kb + kp;
+        if constexpr (W_F32) {
+          const float2 w = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(wg) + o);
+          wv[j][e] = make_float2(live ? w.x : 0.f, live ? w.y : 0.f);
+        } else {
+          uint32_t u = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const bf16*>(wg) + o);
+          u = live ? u : 0u;
+          wv[j][e] = make_float2(bf16_bits_to_f32(u & 0xffffu), bf16_bits_to_f32(u >> 16));
         }
       }
     }
