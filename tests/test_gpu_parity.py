@@ -64,6 +64,15 @@ CASES = {
     # 48 experts: neither the fused router (<= 16) nor the MFMA router (multiples of
     # 128) applies, so the VALU logits kernel and the separate top-k kernel run
     "experts_48": W["deepspeed_gpt_moe"].scaled(tokens=900, d_model=256, d_ff=256, num_experts=48),
+    # top-5 under a tight capacity: the combine's slots past k (5..7 of its 8) and
+    # tokens that lost every choice (those store zeros)
+    "top5_drops": W["deepspeed_gpt_moe"].scaled(tokens=450, d_model=256, d_ff=256, top_k=5,
+                                                capacity_factor=0.1),
+    # top-6 with a shared expert under a tight capacity: a token whose routed
+    # choices all dropped still gets the shared expert's row
+    "top6_shared_drops": W["deepseek_v3"].scaled(tokens=450, d_model=256, d_ff=256,
+                                                 num_experts=16, top_k=6, drop_tokens=True,
+                                                 capacity_factor=0.1, min_capacity=4),
 }
 
 
@@ -83,6 +92,22 @@ def test_drops_happen_where_expected():
     fully = np.all(out["assign_row"].numpy() < 0, axis=1)
     assert fully.any()
     assert np.all(out["y"][torch.from_numpy(fully)].float().numpy() == 0.0)
+
+
+def test_combine_paths_for_dropped_slots():
+    """Tokens that lost every routed choice: zeros without a shared expert, the
+    shared expert's row with one; the rest of the layer within tolerance."""
+    for name in ("top5_drops", "top6_shared_drops"):
+        w = CASES[name]
+        out, err = full_check(w)
+        assert err <= TOL[w.act_dtype]
+        fully = np.all(out["assign_row"].numpy() < 0, axis=1)
+        assert fully.sum() > 100
+        yf = out["y"][torch.from_numpy(fully)].float().numpy()
+        if w.num_shared_experts == 0:
+            assert np.all(yf == 0.0)
+        else:
+            assert np.all(np.abs(yf).max(axis=1) > 0)
 
 
 def test_stage_entry_points_match_forward_and_gather():
