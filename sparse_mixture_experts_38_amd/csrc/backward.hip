@@ -499,7 +499,12 @@ __global__ __launch_bounds__(256) void gate_bias_grad_kernel(const float* __rest
 // dx[t] = sum_j dXp[assign_row[t, j]] (kept choices, j order) + dXp[off[E] + t]
 // (shared expert) + sum_e dlogits[t][e] W_g[e] (router), float32 sums, one
 // rounding. One wavefront per token; lanes take 16-byte column chunks.
-template <typename WT>
+// KM >= k bounds the row slots at compile time. Loads are unconditional so a
+// lane's loads issue before the first use (a load under a branch gets a wait
+// of its own): W_g rows in batches of 8 (rows past E reread row E - 1), and
+// row slots that are dropped or past k reread the token's first live row; all
+// of them are masked out of the sums, which keep the order above.
+template <typename WT, int KM>
 __global__ __launch_bounds__(256) void unpermute_dx_kernel(
     const bf16* __restrict__ dxp, const int32_t* __restrict__ assign_row,
     const int32_t* __restrict__ off, const float* __restrict__ dlogits, const WT* __restrict__ wg,
@@ -507,40 +512,68 @@ __global__ __launch_bounds__(256) void unpermute_dx_kernel(
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (t >= T) return;
-  int rj[MOE_MAX_TOP_K];
+  int64_t rj[KM];
+  bool live[KM];
 #pragma unroll
-  for (int j = 0; j < MOE_MAX_TOP_K; ++j) {
-    const int r = j < k ? assign_row[t * k + j] : -1;
-    rj[j] = (r >= 0 && r < rows_max) ? r : -1;
+  for (int j = 0; j < KM; ++j) {
+    const int r = assign_row[t * k + min(j, k - 1)];
+    live[j] = j < k && r >= 0 && r < rows_max;
+    rj[j] = r;
   }
   const int64_t rs = S ? (int64_t)clamp_off(off, E, rows_max) + t : rows_max;
+  const bool shared = rs < rows_max;
+  int64_t first = shared ? rs : -1;
+#pragma unroll
+  for (int j = KM - 1; j >= 0; --j)
+    if (live[j]) first = rj[j];
+#pragma unroll
+  for (int j = 0; j < KM; ++j)
+    if (!live[j]) rj[j] = first;
   const float* dl = dlogits + t * E;
   for (int c = lane * 8; c < d; c += 512) {
     float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int e = 0; e < E; ++e) {
-      float wv[8];
-      load8(wg + (int64_t)e * d + c, wv);
-      const float g = dl[e];
+    for (int e0 = 0; e0 < E; e0 += 8) {
+      float wv[8][8], g[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = fmaf(g, wv[u], v[u]);
-    }
-#pragma unroll
-    for (int j = 0; j < MOE_MAX_TOP_K; ++j) {
-      if (rj[j] >= 0) {
-        float a[8];
-        load8(dxp + (int64_t)rj[j] * d + c, a);
-#pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] += a[u];
+      for (int u = 0; u < 8; ++u) {
+        const int e = min(e0 + u, E - 1);
+        load8(wg + (int64_t)e * d + c, wv[u]);
+        g[u] = dl[e];
       }
-    }
-    if (rs < rows_max) {
-      float a[8];
-      load8(dxp + rs * d + c, a);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] += a[u];
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = e0 + u < E ? fmaf(g[u], wv[u][q], v[q]) : v[q];
+    }
+    if (first >= 0) {
+      float a[KM][8], as[8];
+#pragma unroll
+      for (int j = 0; j < KM; ++j) load8(dxp + rj[j] * d + c, a[j]);
+      load8(dxp + (shared ? rs : first) * d + c, as);
+#pragma unroll
+      for (int j = 0; j < KM; ++j)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = live[j] ? v[q] + a[j][q] : v[q];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = shared ? v[q] + as[q] : v[q];
     }
     store8(dx + t * d + c, v);
   }
+}
+
+template <typename WT>
+static void launch_unpermute_dx(dim3 grid, hipStream_t s, const bf16* dxp, const int32_t* assign_row,
+                                const int32_t* off, const float* dlogits, const WT* wg, int64_t T,
+                                int d, int k, int E, int S, int64_t rows_max, bf16* dx) {
+  if (k <= 2)
+    hipLaunchKernelGGL((unpermute_dx_kernel<WT, 2>), grid, dim3(256), 0, s, dxp, assign_row, off,
+                       dlogits, wg, T, d, k, E, S, rows_max, dx);
+  else if (k <= 4)
+    hipLaunchKernelGGL((unpermute_dx_kernel<WT, 4>), grid, dim3(256), 0, s, dxp, assign_row, off,
+                       dlogits, wg, T, d, k, E, S, rows_max, dx);
+  else
+    hipLaunchKernelGGL((unpermute_dx_kernel<WT, MOE_MAX_TOP_K>), grid, dim3(256), 0, s, dxp,
+                       assign_row, off, dlogits, wg, T, d, k, E, S, rows_max, dx);
 }
 
 // ------------------------------------------------------------------ launchers
@@ -668,13 +701,13 @@ hipError_t launch_backward_misc(const moe_config& c, const BwdLayout& B, const v
                        gr.db_gate);
   const dim3 ug((unsigned)((T + 3) / 4));
   if (c.router_dtype == MOE_BF16)
-    hipLaunchKernelGGL((unpermute_dx_kernel<bf16>), ug, dim3(256), 0, s, (const bf16*)(ws + B.dxp),
-                       r.assign_row, r.expert_offsets, (const float*)dlogits, (const bf16*)w.w_gate,
-                       T, d, k, E, S, rmax, (bf16*)gr.dx);
+    launch_unpermute_dx<bf16>(ug, s, (const bf16*)(ws + B.dxp), r.assign_row, r.expert_offsets,
+                              (const float*)dlogits, (const bf16*)w.w_gate, T, d, k, E, S, rmax,
+                              (bf16*)gr.dx);
   else
-    hipLaunchKernelGGL((unpermute_dx_kernel<float>), ug, dim3(256), 0, s, (const bf16*)(ws + B.dxp),
-                       r.assign_row, r.expert_offsets, (const float*)dlogits, (const float*)w.w_gate,
-                       T, d, k, E, S, rmax, (bf16*)gr.dx);
+    launch_unpermute_dx<float>(ug, s, (const bf16*)(ws + B.dxp), r.assign_row, r.expert_offsets,
+                               (const float*)dlogits, (const float*)w.w_gate, T, d, k, E, S, rmax,
+                               (bf16*)gr.dx);
   return hipGetLastError();
 }
 
