@@ -142,6 +142,15 @@ typedef struct moe_routing {
   int32_t* assign_row;     /* [T, k]                                              */
 } moe_routing;
 
+/* Monitoring figures of one routed batch, derived from its statistics. */
+typedef struct moe_monitor {
+  double load_imbalance;   /* max_i counts_pre / min_i counts_pre; +inf when an expert got no pick */
+  double utilization_rate; /* (experts with counts_kept > 0) / E                                    */
+  double drop_rate;        /* dropped / (T k); 0 when T = 0                                         */
+  int32_t max_count;       /* max_i counts_pre                                                      */
+  int32_t min_count;       /* min_i counts_pre                                                      */
+} moe_monitor;
+
 /* Human-readable name of a status code (static string). */
 const char* moe_status_string(int status);
 
@@ -151,6 +160,20 @@ const char* moe_version(void);
 /* Host only. MOE_OK if cfg describes a layer this library runs, else the code
  * moe_forward would return for it (MOE_ERR_INVALID_ARG or MOE_ERR_UNSUPPORTED). */
 int moe_validate_config(const moe_config* cfg);
+
+/*
+ * Host only. The monitoring figures of [P2] "Monitoring" (the load imbalance as
+ * the ratio of the largest to the smallest per-expert count, the utilisation as
+ * the share of experts that receive tokens, the drop rate as dropped over total
+ * assignments) from a HOST copy of the moe_stats a forward wrote for cfg.
+ * Counts are the top-k picks before capacity (counts_pre) for the imbalance and
+ * the kept rows (counts_kept) for the utilisation. Reads only the first E
+ * entries of the count arrays and `dropped`. Returns MOE_ERR_INVALID_ARG for a
+ * NULL pointer, an invalid cfg, or counts that are negative or that contradict
+ * the layer (sum counts_pre != T k, counts_kept > counts_pre, dropped !=
+ * T k - sum counts_kept); `out` is written only on MOE_OK.
+ */
+int moe_monitoring(const moe_config* cfg, const moe_stats* host_stats, moe_monitor* out);
 
 /*
  * Host only. Per-expert capacity C = max(min_capacity, ceil(capacity_factor *

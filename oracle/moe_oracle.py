@@ -6,9 +6,9 @@ file and the CPU-baseline leg of the benchmark use it. It shares no code with
 the HIP library; both receive the same seeded inputs from the input generator.
 
 Plain numpy. Arithmetic is float64, except where the pages fix the precision:
-the router works in float32 ("Router Precision: force float32 for the softmax",
-MoE From Scratch to DeepSeek V3, stability tricks; also the fp32-gating advice
-in the Moe(Mixtrue of Experts) survey, stability section), so router logits are
+the router's softmax is taken in float32 (MoE From Scratch to DeepSeek V3,
+stability tricks, router precision; the Moe(Mixtrue of Experts) survey gives
+the same advice in its stability section), so router logits are
 float32 values and the top-k decision is taken on float32 keys. Library
 primitives used as steps: matrix product, stable argsort, bincount, erf.
 
@@ -143,7 +143,9 @@ def top_k(keys, k: int) -> np.ndarray:
 def topk_margin(keys, k: int) -> np.ndarray:
     """key of the k-th choice minus key of the (k+1)-th (inf when k == E).
 
-    Used by parity tests to set aside tokens whose selection is a near tie.
+    Used by parity tests to set aside tokens whose selection is a near tie
+    (the top-k decision taken on keys closer than a threshold may go either
+    way). Pinned against a brute force over all k-subsets and hand cases.
     """
     keys = np.asarray(keys, F64)
     T, E = keys.shape

@@ -68,6 +68,12 @@ STATS_DTYPE = np.dtype([
 STATS_BYTES = STATS_DTYPE.itemsize
 
 
+class MoeMonitor(ctypes.Structure):
+    _fields_ = [("load_imbalance", ctypes.c_double), ("utilization_rate", ctypes.c_double),
+                ("drop_rate", ctypes.c_double), ("max_count", ctypes.c_int32),
+                ("min_count", ctypes.c_int32)]
+
+
 class MoEError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
@@ -94,6 +100,7 @@ def lib():
     L.moe_version.argtypes = []
     L.moe_validate_config.argtypes = [cfgp]
     L.moe_capacity.argtypes = [cfgp, ctypes.POINTER(c_int64)]
+    L.moe_monitoring.argtypes = [cfgp, P, ctypes.POINTER(MoeMonitor)]
     L.moe_workspace_size.argtypes = [cfgp, ctypes.POINTER(c_size_t)]
     L.moe_route.argtypes = [cfgp, P, P, P, P, P, P, P, P, P, c_size_t, P]
     L.moe_permute.argtypes = [cfgp, P, P, P, P, P, P, P, P, c_size_t, P]
@@ -118,7 +125,7 @@ def lib():
     L.moe_backward.argtypes = [cfgp, P, ctypes.POINTER(MoeWeights), ctypes.POINTER(MoeRouting), P,
                                ctypes.POINTER(MoeSaved), P, ctypes.c_float, ctypes.c_float,
                                ctypes.POINTER(MoeGrads), P, c_size_t, P]
-    for name in ("moe_validate_config", "moe_capacity", "moe_workspace_size", "moe_route",
+    for name in ("moe_validate_config", "moe_capacity", "moe_monitoring", "moe_workspace_size", "moe_route",
                  "moe_permute", "moe_expert_ffn", "moe_expert_up", "moe_expert_down",
                  "moe_combine", "moe_forward", "moe_forward_train", "moe_backward_workspace_size",
                  "moe_backward", "moe_expert_choice_capacity", "moe_expert_choice_workspace_size",
@@ -636,6 +643,19 @@ def read_stats(stats: torch.Tensor, num_experts: int) -> dict:
                 l_aux=float(a["l_aux"]), z_loss=float(a["z_loss"]),
                 capacity=None if int(a["capacity"]) < 0 else int(a["capacity"]),
                 kept=int(a["kept"]), dropped=int(a["dropped"]))
+
+
+def monitoring(cfg: MoeConfig, stats: torch.Tensor) -> dict:
+    """The monitoring figures (load imbalance, utilisation, drop rate) of the
+    batch whose statistics `stats` holds (device or host moe_stats buffer),
+    computed by the library's host helper moe_monitoring."""
+    host = stats.detach().cpu().contiguous()
+    if host.numel() * host.element_size() < STATS_BYTES:
+        raise ValueError("stats: too small for a moe_stats")
+    m = MoeMonitor()
+    _check(lib().moe_monitoring(cfg, c_void_p(host.data_ptr()), ctypes.byref(m)), "moe_monitoring")
+    return dict(load_imbalance=m.load_imbalance, utilization_rate=m.utilization_rate,
+                drop_rate=m.drop_rate, max_count=m.max_count, min_count=m.min_count)
 
 
 def weights_of(inputs: Dict[str, Optional[torch.Tensor]]) -> Dict[str, Optional[torch.Tensor]]:

@@ -174,6 +174,35 @@ const char* moe_version(void) { return "moe-mi355x 0.1.0 (gfx950)"; }
 
 int moe_validate_config(const moe_config* cfg) { return validate(cfg); }
 
+int moe_monitoring(const moe_config* cfg, const moe_stats* st, moe_monitor* out) {
+  const int v = validate(cfg);
+  if (v != MOE_OK) return v;
+  if (!st || !out) return MOE_ERR_INVALID_ARG;
+  const int E = cfg->num_experts;
+  const int64_t A = cfg->tokens * cfg->top_k;
+  int64_t pre = 0, kept = 0;
+  int32_t cmax = st->counts_pre[0], cmin = st->counts_pre[0];
+  int used = 0;
+  for (int e = 0; e < E; ++e) {
+    const int32_t cp = st->counts_pre[e], ck = st->counts_kept[e];
+    if (cp < 0 || ck < 0 || ck > cp) return MOE_ERR_INVALID_ARG;
+    pre += cp;
+    kept += ck;
+    cmax = std::max(cmax, cp);
+    cmin = std::min(cmin, cp);
+    used += ck > 0;
+  }
+  if (pre != A || (int64_t)st->dropped != A - kept) return MOE_ERR_INVALID_ARG;
+  moe_monitor m;
+  m.max_count = cmax;
+  m.min_count = cmin;
+  m.load_imbalance = cmin > 0 ? (double)cmax / (double)cmin : (double)INFINITY;
+  m.utilization_rate = (double)used / (double)E;
+  m.drop_rate = A > 0 ? (double)st->dropped / (double)A : 0.0;
+  *out = m;
+  return MOE_OK;
+}
+
 int moe_capacity(const moe_config* cfg, int64_t* capacity_out) {
   const int v = validate(cfg);
   if (v != MOE_OK) return v;

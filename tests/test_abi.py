@@ -251,3 +251,53 @@ def test_hash_and_bias_entry_points_validate_before_any_launch():
     z = _base(tokens=0, top_k=1)
     assert lib.moe_forward_hash(ctypes.byref(z), None, None, None, 0, None, None, None, None,
                                 None, 0, None) == A.MOE_OK
+
+
+def _host_stats(counts_pre, counts_kept, dropped):
+    import numpy as np
+    import torch
+    a = np.zeros(1, dtype=A.STATS_DTYPE)
+    a["counts_pre"][0, :len(counts_pre)] = counts_pre
+    a["counts_kept"][0, :len(counts_kept)] = counts_kept
+    a["dropped"] = dropped
+    return torch.from_numpy(np.frombuffer(a.tobytes(), dtype=np.uint8).copy())
+
+
+@pytest.mark.parametrize("seed,T,E,k,cap", [(0, 64, 4, 1, 12), (1, 200, 8, 2, 40), (2, 500, 16, 3, None),
+                                            (3, 37, 5, 2, 6), (4, 8, 8, 1, 4)])
+def test_monitoring_helper_matches_oracle(seed, T, E, k, cap):
+    """moe_monitoring (host only) against the oracle's monitoring figures
+    (MoE Training Guide, "Monitoring") on skewed routings with and without drops."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    p = rng.dirichlet(np.ones(E) * 0.7)
+    idx = np.stack([rng.choice(E, k, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+    d = O.dispatch(idx, E, cap)
+    ref = O.balance_stats(np.full((T, E), 1.0 / E), "softmax", np.zeros(T), d["counts_pre"],
+                          d["counts_kept"], T, k, E)
+    cfg = A.make_config(tokens=T, d_model=256, d_ff=256, num_experts=E, top_k=k,
+                        drop_tokens=cap is not None, capacity_factor=1.0)
+    got = A.monitoring(cfg, _host_stats(d["counts_pre"], d["counts_kept"], d["dropped"]))
+    assert got["load_imbalance"] == ref["imbalance"]
+    assert got["utilization_rate"] == ref["utilization"]
+    assert got["drop_rate"] == ref["drop_rate"]
+    assert got["max_count"] == d["counts_pre"].max() and got["min_count"] == d["counts_pre"].min()
+
+
+def test_monitoring_helper_rejects_inconsistent_counts():
+    cfg = A.make_config(tokens=10, d_model=256, d_ff=256, num_experts=2, top_k=1,
+                        drop_tokens=True, capacity_factor=1.0)
+    ok = A.monitoring(cfg, _host_stats([6, 4], [5, 4], 1))
+    assert ok["load_imbalance"] == 1.5 and ok["utilization_rate"] == 1.0 and ok["drop_rate"] == 0.1
+    for pre, kept, dropped in [([6, 5], [5, 4], 2),      # picks do not sum to T k
+                               ([6, 4], [7, 4], -1),     # kept above picks
+                               ([6, 4], [5, 4], 0),      # dropped disagrees
+                               ([11, -1], [5, 0], 5)]:   # negative count
+        with pytest.raises(A.MoEError):
+            A.monitoring(cfg, _host_stats(pre, kept, dropped))
+    lib = A.lib()
+    assert lib.moe_monitoring(ctypes.byref(cfg), None, None) == A.MOE_ERR_INVALID_ARG
+    # no tokens: nothing dropped, no expert used, every count 0 (imbalance +inf)
+    cfg0 = A.make_config(tokens=0, d_model=256, d_ff=256, num_experts=4, top_k=2)
+    z = A.monitoring(cfg0, _host_stats([0] * 4, [0] * 4, 0))
+    assert z["drop_rate"] == 0.0 and z["utilization_rate"] == 0.0 and z["load_imbalance"] == float("inf")

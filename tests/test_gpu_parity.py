@@ -245,11 +245,16 @@ def test_zero_tokens_noop_on_gpu():
     assert lib.moe_forward(cfg, None, None, None, None, None, None, 0, None) == A.MOE_OK
 
 
-@pytest.mark.parametrize("name", ["deepspeed_gpt_moe", "many_expert_train"])
-def test_full_size_workload_sampled(name):
-    """At the benchmark's full sizes: logits, top-k, counts, the permutation and
+@pytest.mark.parametrize("name,n_sample", [("deepspeed_gpt_moe", 96), ("many_expert_train", 96),
+                                           ("mixtral_8x7b", 64), ("deepseek_v3", 48)])
+def test_full_size_workload_sampled(name, n_sample):
+    """At the workloads' full sizes: logits, top-k, counts, the permutation and
     the drop set in full; the layer output on a sample of tokens (including
-    tokens that lost a choice to capacity) that the oracle computes row by row."""
+    tokens that lost a choice to capacity) that the oracle computes row by row,
+    with the shared expert's output where the layer has one. The Mixtral shape
+    runs the router over four K chunks (d = 4096) and GEMM 2 at K = 14336; the
+    DeepSeek-V3 shape runs 257 groups, its shared group of 4096 rows at
+    K = 7168, and the router on MFMA with 256 experts."""
     w = W[name]
     print(f"[case] full-size {name}", flush=True)
     inp = make_inputs(w, seed=0, device="cuda")
@@ -262,7 +267,7 @@ def test_full_size_workload_sampled(name):
     T, k = w.tokens, w.top_k
     rng = np.random.default_rng(0)
     dropped_tok = np.nonzero(np.any(d["assign_row"] < 0, axis=1))[0]
-    sample = np.unique(np.concatenate([rng.choice(T, 96, replace=False), dropped_tok[:32]]))
+    sample = np.unique(np.concatenate([rng.choice(T, n_sample, replace=False), dropped_tok[:32]]))
     gates = r["gates"]
     idx = out["topk_idx"].numpy()
     y_ref = np.zeros((len(sample), w.d_model))
@@ -277,5 +282,11 @@ def test_full_size_workload_sampled(name):
                           None if P["w3"] is None else P["w3"][e])
         for (si, j), yrow in zip(sel, ye):
             y_ref[si] += gates[sample[si], j] * yrow
+    if w.num_shared_experts:
+        y_ref += O.expert_ffn(x_np[sample], P["ws1"][0], None if P["bs1"] is None else P["bs1"][0],
+                              P["ws2"][0], None if P["bs2"] is None else P["bs2"][0],
+                              w.activation, None if P["ws3"] is None else P["ws3"][0])
     y_gpu = out["y"].float().numpy()[sample]
-    assert rel_err(y_gpu, y_ref) <= TOL[w.act_dtype]
+    err = rel_err(y_gpu, y_ref)
+    print(f"[case] full-size {name}: sampled tokens {len(sample)}, max rel err {err:.2e}", flush=True)
+    assert err <= TOL[w.act_dtype]

@@ -147,6 +147,53 @@ def test_sigmoid_scores_match_torch():
                        rtol=1e-14, atol=0)
 
 
+
+# ---------------------------------------------------------------- top-k margin
+def _margin_by_subsets(keys, k):
+    """The selection's margin as a brute force over every k-subset S of the
+    experts: the largest value of min(keys in S) - max(keys outside S). The
+    top-k set attains key_(k) - key_(k+1) >= 0; every other set scores <= 0;
+    with k = E there is nothing outside S (margin +inf)."""
+    E = len(keys)
+    if k >= E:
+        return math.inf
+    best = -math.inf
+    for S in itertools.combinations(range(E), k):
+        inside = min(keys[i] for i in S)
+        outside = max(keys[i] for i in range(E) if i not in S)
+        best = max(best, inside - outside)
+    return best
+
+
+@pytest.mark.parametrize("E,k", [(4, 1), (5, 2), (6, 3), (7, 6), (8, 4)])
+def test_topk_margin_matches_subset_brute_force(E, k):
+    rng = np.random.default_rng(100 + E * 10 + k)
+    # integer keys with many ties, plus continuous keys
+    keys = np.concatenate([rng.integers(-3, 4, size=(30, E)).astype(np.float32),
+                           rng.normal(size=(30, E)).astype(np.float32)])
+    m = O.topk_margin(keys, k)
+    ref = np.array([_margin_by_subsets([float(v) for v in row], k) for row in keys])
+    assert np.array_equal(m, ref)
+    assert np.all(m >= 0)
+
+
+def test_topk_margin_hand_cases():
+    # keys 0.5, 0.9, 0.1, 0.7: top-2 = {0.9, 0.7}, the next key is 0.5
+    keys = np.array([[0.5, 0.9, 0.1, 0.7]], np.float64)
+    assert O.topk_margin(keys, 2)[0] == pytest.approx(0.2, abs=1e-15)
+    assert O.topk_margin(keys, 1)[0] == pytest.approx(0.2, abs=1e-15)   # 0.9 - 0.7
+    assert O.topk_margin(keys, 3)[0] == pytest.approx(0.4, abs=1e-15)   # 0.5 - 0.1
+    # k = E: no competitor, the choice cannot flip
+    assert O.topk_margin(keys, 4)[0] == math.inf
+    # an exact tie at the boundary gives 0 (either expert is a correct choice)
+    tie = np.array([[1.0, 3.0, 1.0, -2.0]], np.float32)
+    assert O.topk_margin(tie, 2)[0] == 0.0
+    assert O.topk_margin(tie, 1)[0] == 2.0
+    # the margin is on the keys the routing ranks by (sigmoid: s + bias)
+    l = np.array([[0.0, 0.0]], np.float32)
+    keys_s = O.selection_keys(l, "sigmoid", np.array([0.25, 0.0], np.float32))
+    assert O.topk_margin(keys_s, 1)[0] == 0.25
+
 # ---------------------------------------------------------------- statistics
 @pytest.mark.parametrize("E,k", [(4, 1), (8, 2), (16, 4)])
 def test_laux_is_one_under_uniform_routing(E, k):
@@ -161,6 +208,43 @@ def test_laux_is_one_under_uniform_routing(E, k):
     assert abs(s["l_aux"] - 1.0) < 1e-13
     assert s["imbalance"] == 1.0 and s["utilization"] == 1.0
 
+
+
+@pytest.mark.parametrize("E,k", [(4, 1), (8, 2), (16, 4)])
+def test_sigmoid_laux_is_one_under_uniform_routing(E, k):
+    """Sigmoid router: token t's logits are a cyclic shift by t of one vector,
+    T a multiple of E, so the normalised affinities s_ti / sum_e s_te average to
+    1/E for every expert and the picks are uniform: P_i = f_i = 1/E, L_aux = 1.
+    (Without the normalisation, P_i would be the mean of the raw sigmoids.)"""
+    v = np.linspace(2.0, -1.5, E).astype(np.float32)
+    T = 2 * E
+    logits = np.stack([np.roll(v, t) for t in range(T)])
+    r = O.route(logits, k, "sigmoid")
+    d = O.dispatch(r["idx"], E, None)
+    s = O.balance_stats(r["scores"], "sigmoid", r["lse"], d["counts_pre"], d["counts_kept"], T, k, E)
+    assert np.allclose(s["f"], 1.0 / E, rtol=0, atol=1e-15)
+    assert np.allclose(s["P"], 1.0 / E, rtol=0, atol=1e-15)
+    assert abs(s["l_aux"] - 1.0) < 1e-13
+
+
+def test_sigmoid_prob_mean_hand_case():
+    """Two tokens, two experts, top-1, sigmoid router.
+    token 0: logits (0, ln 3) -> s = (1/2, 3/4), normalised (2/5, 3/5), picks expert 1;
+    token 1: logits (-ln 3, ln 3) -> s = (1/4, 3/4), normalised (1/4, 3/4), picks expert 1.
+    P = ((2/5 + 1/4)/2, (3/5 + 3/4)/2) = (0.325, 0.675); f = (0, 1);
+    L_aux = 2 (0 * 0.325 + 1 * 0.675) = 1.35."""
+    l3 = math.log(3.0)
+    logits = np.array([[0.0, l3], [-l3, l3]], np.float32)
+    r = O.route(logits, 1, "sigmoid")
+    assert list(r["idx"][:, 0]) == [1, 1]
+    d = O.dispatch(r["idx"], 2, None)
+    s = O.balance_stats(r["scores"], "sigmoid", r["lse"], d["counts_pre"], d["counts_kept"], 2, 1, 2)
+    assert np.allclose(s["P"], [0.325, 0.675], rtol=0, atol=1e-7)
+    assert np.array_equal(s["f"], [0.0, 1.0])
+    assert s["l_aux"] == pytest.approx(1.35, abs=1e-7)
+    # z-loss is the same logsumexp statistic for both routers:
+    # lse(0, ln 3) = ln 4, lse(-ln 3, ln 3) = ln(10/3)
+    assert s["z_loss"] == pytest.approx((math.log(4.0) ** 2 + math.log(10 / 3) ** 2) / 2, abs=1e-6)
 
 def test_laux_all_mass_on_one_expert_is_E():
     E, T = 8, 32
