@@ -130,6 +130,13 @@ typedef struct moe_weights {
   const float* bs1;    /* shared expert [F] if has_bias                        */
   const void* ws2;     /* shared expert [d, F]                                 */
   const float* bs2;    /* shared expert [d] if has_bias                        */
+  /* Optional packed copies written by moe_pack_weights (NULL: not used). When
+   * given, the grouped GEMM reads the weights of groups with few rows from
+   * them (same values, the weight-streaming kernel's order); every other read
+   * uses w1 / w3 / w2 / ws*. Read by moe_forward, moe_forward_profiled and
+   * moe_forward_hash; the other entry points ignore them. */
+  const void* up_packed;   /* moe_packed_weights_size up_bytes: W1 (and W3) of every group */
+  const void* down_packed; /* moe_packed_weights_size down_bytes: W2 of every group        */
 } moe_weights;
 
 /* Routing and dispatch results of moe_forward (device buffers the caller owns). */
@@ -160,6 +167,28 @@ const char* moe_version(void);
 /* Host only. MOE_OK if cfg describes a layer this library runs, else the code
  * moe_forward would return for it (MOE_ERR_INVALID_ARG or MOE_ERR_UNSUPPORTED). */
 int moe_validate_config(const moe_config* cfg);
+
+/*
+ * Host only. Bytes of the packed weight copies moe_pack_weights writes, over
+ * the E + S groups: up_bytes for GEMM 1's W1 (and W3), down_bytes for GEMM 2's
+ * W2 (each the size of the matrices it copies). bf16 layers only
+ * (MOE_ERR_UNSUPPORTED for float32 layers).
+ */
+int moe_packed_weights_size(const moe_config* cfg, size_t* up_bytes, size_t* down_bytes);
+
+/*
+ * Copies the expert weights of w (w1, w3, w2 and the shared expert's ws1,
+ * ws3, ws2) into up_packed / down_packed (device buffers of the sizes above;
+ * either may be NULL to skip it) in the order the weight-streaming grouped
+ * GEMM reads them: for each group, slab of 256 weight rows (SwiGLU: 128 rows
+ * of W1 with the same rows of W3), 64-deep K step and wave, 8 KB in MFMA
+ * fragment order. The values are unchanged; pass the buffers as
+ * moe_weights.up_packed / down_packed to forward calls. A one-time conversion
+ * for a set of weights (the copy must be redone when the weights change).
+ * bf16 layers only. Enqueued on `stream`; returns MOE_ERR_HIP on a failed launch.
+ */
+int moe_pack_weights(const moe_config* cfg, const moe_weights* w, void* up_packed,
+                     void* down_packed, void* stream);
 
 /*
  * Host only. The monitoring figures of [P2] "Monitoring" (the load imbalance as
@@ -296,6 +325,30 @@ int moe_combine(const moe_config* cfg, const void* y_perm, const int32_t* expert
 int moe_forward(const moe_config* cfg, const void* x, const moe_weights* w, void* y,
                 const moe_routing* routing, moe_stats* stats, void* workspace,
                 size_t workspace_bytes, void* stream);
+
+/* Stage boundaries moe_forward_profiled marks with events. */
+enum {
+  MOE_EV_START = 0,     /* before the router                                   */
+  MOE_EV_ROUTED = 1,    /* after moe_route's kernels                           */
+  MOE_EV_DISPATCHED = 2,/* after moe_permute's kernels                         */
+  MOE_EV_UP = 3,        /* after expert GEMM 1 (every group)                   */
+  MOE_EV_DOWN = 4,      /* after expert GEMM 2 (every group)                   */
+  MOE_EV_END = 5,       /* after the combine                                   */
+  MOE_FORWARD_EVENTS = 6
+};
+
+/*
+ * moe_forward with timing markers, for measuring the stages of the real
+ * forward path: the same kernels with the same arguments on the same stream,
+ * plus hipEventRecord(events[i], stream) at each boundary i of the enum above.
+ *   events  host array of MOE_FORWARD_EVENTS hipEvent_t handles the caller
+ *           created (NULL entries are skipped; events itself may be NULL,
+ *           which makes the call identical to moe_forward).
+ * Returns MOE_ERR_HIP if recording an event fails.
+ */
+int moe_forward_profiled(const moe_config* cfg, const void* x, const moe_weights* w, void* y,
+                         const moe_routing* routing, moe_stats* stats, void* workspace,
+                         size_t workspace_bytes, void* stream, void* const* events);
 
 /* ------------------------------------------------------------------ balancing, hash routing */
 

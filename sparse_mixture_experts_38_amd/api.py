@@ -38,7 +38,8 @@ class MoeConfig(ctypes.Structure):
 
 class MoeWeights(ctypes.Structure):
     _fields_ = [(n, c_void_p) for n in ("w_gate", "b_gate", "e_bias", "w1", "w3", "b1", "w2", "b2",
-                                        "ws1", "ws3", "bs1", "ws2", "bs2")]
+                                        "ws1", "ws3", "bs1", "ws2", "bs2", "up_packed",
+                                        "down_packed")]
 
 
 class MoeRouting(ctypes.Structure):
@@ -66,6 +67,10 @@ STATS_DTYPE = np.dtype([
     ("dropped", "<i4"), ("reserved", "<i4", (3,)),
 ])
 STATS_BYTES = STATS_DTYPE.itemsize
+
+
+# Stage boundaries of moe_forward_profiled (moe.h, MOE_EV_*).
+FORWARD_EVENTS = ("start", "routed", "dispatched", "up", "down", "end")
 
 
 class MoeMonitor(ctypes.Structure):
@@ -101,6 +106,8 @@ def lib():
     L.moe_validate_config.argtypes = [cfgp]
     L.moe_capacity.argtypes = [cfgp, ctypes.POINTER(c_int64)]
     L.moe_monitoring.argtypes = [cfgp, P, ctypes.POINTER(MoeMonitor)]
+    L.moe_packed_weights_size.argtypes = [cfgp, ctypes.POINTER(c_size_t), ctypes.POINTER(c_size_t)]
+    L.moe_pack_weights.argtypes = [cfgp, ctypes.POINTER(MoeWeights), P, P, P]
     L.moe_workspace_size.argtypes = [cfgp, ctypes.POINTER(c_size_t)]
     L.moe_route.argtypes = [cfgp, P, P, P, P, P, P, P, P, P, c_size_t, P]
     L.moe_permute.argtypes = [cfgp, P, P, P, P, P, P, P, P, c_size_t, P]
@@ -110,6 +117,8 @@ def lib():
     L.moe_combine.argtypes = [cfgp, P, P, P, P, P, P]
     L.moe_forward.argtypes = [cfgp, P, ctypes.POINTER(MoeWeights), P, ctypes.POINTER(MoeRouting),
                               P, P, c_size_t, P]
+    L.moe_forward_profiled.argtypes = [cfgp, P, ctypes.POINTER(MoeWeights), P,
+                                       ctypes.POINTER(MoeRouting), P, P, c_size_t, P, P]
     L.moe_update_selection_bias.argtypes = [cfgp, P, P, ctypes.c_float, P]
     L.moe_route_hash.argtypes = [cfgp, P, P, c_int64, P, P, P, P]
     L.moe_forward_hash.argtypes = [cfgp, P, P, P, c_int64, ctypes.POINTER(MoeWeights), P,
@@ -125,9 +134,9 @@ def lib():
     L.moe_backward.argtypes = [cfgp, P, ctypes.POINTER(MoeWeights), ctypes.POINTER(MoeRouting), P,
                                ctypes.POINTER(MoeSaved), P, ctypes.c_float, ctypes.c_float,
                                ctypes.POINTER(MoeGrads), P, c_size_t, P]
-    for name in ("moe_validate_config", "moe_capacity", "moe_monitoring", "moe_workspace_size", "moe_route",
+    for name in ("moe_validate_config", "moe_capacity", "moe_monitoring", "moe_packed_weights_size", "moe_pack_weights", "moe_workspace_size", "moe_route",
                  "moe_permute", "moe_expert_ffn", "moe_expert_up", "moe_expert_down",
-                 "moe_combine", "moe_forward", "moe_forward_train", "moe_backward_workspace_size",
+                 "moe_combine", "moe_forward", "moe_forward_profiled", "moe_forward_train", "moe_backward_workspace_size",
                  "moe_backward", "moe_expert_choice_capacity", "moe_expert_choice_workspace_size",
                  "moe_forward_expert_choice", "moe_update_selection_bias", "moe_route_hash",
                  "moe_forward_hash"):
@@ -364,6 +373,13 @@ def _need_weights(cfg, W):
         _need(W.get("bs1"), "bs1", (S, F), torch.float32, optional=not cfg.has_bias)
         _need(W.get("ws2"), "ws2", (S, d, F), act)
         _need(W.get("bs2"), "bs2", (S, d), torch.float32, optional=not cfg.has_bias)
+    up, down = W.get("up_packed"), W.get("down_packed")
+    if up is not None or down is not None:
+        ub, db = packed_weights_size(cfg)
+        for t, nb, name in ((up, ub, "up_packed"), (down, db, "down_packed")):
+            if t is not None and (t.device.type != "cuda" or not t.is_contiguous()
+                                  or t.numel() * t.element_size() < nb):
+                raise ValueError(f"{name}: needs a contiguous device buffer of at least {nb} bytes")
 
 
 def _need_routing(cfg, R, logits_required=False):
@@ -645,6 +661,30 @@ def read_stats(stats: torch.Tensor, num_experts: int) -> dict:
                 kept=int(a["kept"]), dropped=int(a["dropped"]))
 
 
+def packed_weights_size(cfg: MoeConfig):
+    """(up_bytes, down_bytes) of the packed weight copies (moe_packed_weights_size)."""
+    up, down = c_size_t(0), c_size_t(0)
+    _check(lib().moe_packed_weights_size(ctypes.byref(cfg), ctypes.byref(up), ctypes.byref(down)),
+           "moe_packed_weights_size")
+    return up.value, down.value
+
+
+def pack_weights(cfg: MoeConfig, weights: Dict[str, Optional[torch.Tensor]], device="cuda"):
+    """Packed copies of the expert weights for the weight-streaming GEMM
+    (moe_pack_weights), returned as the weights dict with "up_packed" and
+    "down_packed" added (the other entries unchanged)."""
+    _need_weights(cfg, weights)
+    up_b, down_b = packed_weights_size(cfg)
+    up = torch.empty(up_b, dtype=torch.uint8, device=device)
+    down = torch.empty(down_b, dtype=torch.uint8, device=device)
+    mw = MoeWeights(*[_ptr(weights.get(n)) for n, _ in MoeWeights._fields_])
+    _check(lib().moe_pack_weights(ctypes.byref(cfg), ctypes.byref(mw), _ptr(up), _ptr(down),
+                                  _stream()), "moe_pack_weights")
+    out = dict(weights)
+    out["up_packed"], out["down_packed"] = up, down
+    return out
+
+
 def monitoring(cfg: MoeConfig, stats: torch.Tensor) -> dict:
     """The monitoring figures (load imbalance, utilisation, drop rate) of the
     batch whose statistics `stats` holds (device or host moe_stats buffer),
@@ -730,6 +770,17 @@ class Plan:
 
     def forward(self, stream=None):
         self._call(self._forward, "moe_forward", stream)
+
+    def forward_profiled(self, events, stream=None):
+        """moe_forward with events[i] recorded at stage boundary FORWARD_EVENTS[i].
+        `events` are torch.cuda.Event objects that have been recorded once (so
+        that their HIP events exist)."""
+        if len(events) != len(FORWARD_EVENTS) or any(e.cuda_event == 0 for e in events):
+            raise ValueError("forward_profiled: needs one created event per stage boundary")
+        arr = (c_void_p * len(events))(*[e.cuda_event for e in events])
+        f, args = self._forward
+        _check(lib().moe_forward_profiled(*args, stream if stream is not None else _stream(), arr),
+               "moe_forward_profiled")
 
 
 class TrainPlan:

@@ -92,7 +92,8 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, i
 // before its first group. `part` selects the rows covered: 0 all rows of
 // every group in BM-row tiles; 1 the first floor(n / BM) BM-row tiles of each
 // group of n rows; 2 the rows that part 1 leaves over (fewer than `big`), in
-// BM-row tiles.
+// BM-row tiles. Groups of at most skip_rows rows are left out (the streaming
+// GEMM runs them).
 struct TileSpace {
   int s[5], e[5], n[5];
   int excl, incl, total;
@@ -100,7 +101,7 @@ struct TileSpace {
 
 __device__ __forceinline__ void tile_space_init(TileSpace& ts, const int32_t* __restrict__ offsets,
                                                 int G, int rows_max, int BM, int part = 0,
-                                                int big = 256) {
+                                                int big = 256, int skip_rows = 0) {
   constexpr int PER = 5;
   const int lane = threadIdx.x & 63;
   const int g0 = lane * PER;
@@ -115,7 +116,8 @@ __device__ __forceinline__ void tile_space_init(TileSpace& ts, const int32_t* __
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int gi = g0 + i;
-    const int rows = (gi < G && o[i + 1] > o[i]) ? o[i + 1] - o[i] : 0;
+    const int rows0 = (gi < G && o[i + 1] > o[i]) ? o[i + 1] - o[i] : 0;
+    const int rows = rows0 > skip_rows ? rows0 : 0;   // (groups the streaming GEMM takes)
     const int full = part == 0 ? 0 : rows / big * big;
     ts.s[i] = o[i] + (part == 2 ? full : 0);
     ts.e[i] = part == 1 ? o[i] + full : o[i] + rows;
@@ -199,7 +201,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
     const float* __restrict__ bias, const bf16* __restrict__ Ws, const bf16* __restrict__ Ws3,
     const float* __restrict__ bias_s, int E, int G, const int32_t* __restrict__ offsets,
     int rows_max, void* __restrict__ Cv, int N, int K, int part, const int32_t* __restrict__ arows,
-    int kparts, const bf16* __restrict__ Zin) {
+    int kparts, const bf16* __restrict__ Zin, int skip_rows) {
   constexpr bool GATED = EPI == EPI_SWIGLU;
   constexpr bool DACT = EPI == EPI_DGELU || EPI == EPI_DRELU;
   constexpr int BM = 128, BK = 64, CH = BK / 8;   // 8 chunks of 16 B per LDS row
@@ -215,7 +217,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
   bf16* __restrict__ C = reinterpret_cast<bf16*>(Cv);
 
   TileSpace ts;
-  tile_space_init(ts, offsets, G, rows_max, BM, part, kGemmBigBM);
+  tile_space_init(ts, offsets, G, rows_max, BM, part, kGemmBigBM, skip_rows);
   const int mtiles = __builtin_amdgcn_readfirstlane(ts.total);
   const int ntn = N / BN;
   const int tiles = mtiles * ntn;
@@ -661,7 +663,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(
     const float* __restrict__ bias, const bf16* __restrict__ Ws, const bf16* __restrict__ Ws3,
     const float* __restrict__ bias_s, int E, int G, const int32_t* __restrict__ offsets,
     int rows_max, bf16* __restrict__ C, int N, int K, const int32_t* __restrict__ arows,
-    uint32_t a_bytes) {
+    uint32_t a_bytes, int skip_rows) {
   constexpr bool GATED = EPI == EPI_SWIGLU;
   constexpr int BM = 256, BK = 64, CH = BK / 8;   // 8 chunks of 16 B per LDS row
   constexpr int NB = GATED ? 2 : 1;
@@ -677,7 +679,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(
   __shared__ uint32_t pf_lds[512];   // landing area of the L2 prefetches, never read
 
   TileSpace ts;
-  tile_space_init(ts, offsets, G, rows_max, BM, 1, BM);
+  tile_space_init(ts, offsets, G, rows_max, BM, 1, BM, skip_rows);
   const int mtiles = __builtin_amdgcn_readfirstlane(ts.total);
   const int ntn = N / BN;
   const int tiles = mtiles * ntn;
@@ -911,6 +913,546 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(
   }
 }
 
+// ------------------------------------------------------------------ weight-streaming grouped GEMM
+// Groups with few rows (the fine-grained experts of a DeepSeek-V3-shaped layer
+// hold tens to a few hundred rows each) make the grouped GEMM a stream of the
+// weights: each weight byte feeds only that many rows, below the ridge point of
+// the chip, so the kernel must read every weight byte once, at full HBM rate.
+// Here a block takes all rows of one group (in equal parts of at most 256
+// rows) against one slab of 256 weight rows (SwiGLU: 128 rows of W1 and the
+// same 128 rows of W3), and each wave owns 64 of those weight rows (32 of W1 +
+// 32 of W3) for the whole K loop. Per 64-deep K step:
+//   * each wave loads its weight rows into registers, three steps ahead, every
+//     load instruction covering eight whole 128-byte lines (lane l: row l / 8,
+//     16-byte chunk l % 8), with the non-temporal cache policy (read once):
+//     HBM delivers whole lines per instruction at about 6-7 TB/s, where the
+//     MFMA fragment layout loaded straight into registers (32 rows x 32 bytes
+//     per instruction) reaches about 4 TB/s. When its step comes, the wave
+//     stores the rows into its own LDS area and reads them back as fragments
+//     (each weight byte crosses LDS once, with no barrier between waves);
+//   * the group's token rows (gathered through arows for GEMM 1) go global ->
+//     LDS directly (buffer_load ... lds), four stages, three steps ahead,
+//     cached (the group's other slabs read the same rows), read by every wave.
+// v_mfma_f32_32x32x16_bf16 takes the weight fragment first, so a lane's
+// accumulators hold four consecutive output columns of one row. LDS rows are
+// 128 bytes with 16-byte chunk c of row r at c ^ ((r >> 1) & 7), conflict-free
+// for the fragment reads. Within a K step, sub-step s of lane half h multiplies
+// K elements 32 h + 8 s .. + 7, the same order on both operands.
+// The parts of one slab are consecutive work items and a group's slabs are
+// consecutive, and each XCD runs a contiguous range of items, so the slabs of a
+// group run side by side on one XCD: its token rows are fetched into that
+// XCD's L2 once, and the parts of a group with more than 256 rows (equal in
+// size, so they run at the same pace) read the same weight lines at about the
+// same time, the second reader finding them in L2.
+// Rows per part are rounded up to 64, 128, 192 or 256 (template MF = 2, 4, 6,
+// 8 fragments of 32 rows); rows past the part's end repeat its last row and are
+// not stored.
+constexpr int kStreamRows = 256;   // rows per part
+constexpr int kStreamMaxRows = 512;   // groups with more rows use the tiled kernels
+constexpr int kStreamLds = 10240;     // u32x4 (160 KB)
+// Work items of the streaming GEMM: group g with rows in (0, max_rows]
+// contributes ns slabs x ceil(rows / 256) parts. Lane l of every wave holds
+// groups 5 l .. 5 l + 4 (first row, row count, item count) and the prefix of
+// items before them.
+struct StreamSpace {
+  int s[5], r[5], n[5];
+  int excl, incl, total;
+};
+
+__device__ __forceinline__ void stream_space_init(StreamSpace& ss, const int32_t* __restrict__ offsets,
+                                                  int G, int rows_max, int max_rows, int ns) {
+  constexpr int PER = 5;
+  const int lane = threadIdx.x & 63;
+  const int g0 = lane * PER;
+  int o[PER + 1];
+#pragma unroll
+  for (int i = 0; i <= PER; ++i) {
+    const int gi = g0 + i;
+    o[i] = gi <= G ? min(max(offsets[gi], 0), rows_max) : rows_max;
+  }
+  int sum = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int gi = g0 + i;
+    const int rows = (gi < G && o[i + 1] > o[i]) ? o[i + 1] - o[i] : 0;
+    const bool mine = rows > 0 && rows <= max_rows;
+    ss.s[i] = o[i];
+    ss.r[i] = mine ? rows : 0;
+    ss.n[i] = mine ? (rows + kStreamRows - 1) / kStreamRows * ns : 0;
+    sum += ss.n[i];
+  }
+  int incl = sum;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += t;
+  }
+  ss.incl = incl;
+  ss.excl = incl - sum;
+  ss.total = __shfl(incl, 63, 64);
+}
+
+// Group, first row, row count and slab of item t (< ss.total); uniform over the wave.
+__device__ __forceinline__ void stream_lookup(const StreamSpace& ss, int t, int ns, int& g_out,
+                                              int& row0_out, int& nrows_out, int& slab_out) {
+  constexpr int PER = 5;
+  const int lane = threadIdx.x & 63;
+  const bool mine = t >= ss.excl && t < ss.incl;
+  const int owner = __ffsll((unsigned long long)__ballot(mine)) - 1;
+  int g = 0, row0 = 0, nrows = 0, slab = 0;
+  if (mine) {
+    int acc = ss.excl;
+    bool found = false;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if (!found && t < acc + ss.n[i]) {
+        found = true;
+        const int parts = ss.n[i] / ns;
+        const int local = t - acc;
+        slab = local / parts;
+        const int part = local - slab * parts;
+        g = lane * PER + i;
+        // equal parts (within one row), so that the parts of a slab run at the
+        // same pace and read its weight lines at about the same time
+        const int lo = part * ss.r[i] / parts, hi = (part + 1) * ss.r[i] / parts;
+        row0 = ss.s[i] + lo;
+        nrows = hi - lo;
+      }
+      acc += ss.n[i];
+    }
+  }
+  g_out = __shfl(g, owner, 64);
+  row0_out = __shfl(row0, owner, 64);
+  nrows_out = __shfl(nrows, owner, 64);
+  slab_out = __shfl(slab, owner, 64);
+}
+
+// s_waitcnt immediate: vmcnt <= n (0..63), lgkmcnt 0, expcnt not waited for.
+__device__ __forceinline__ constexpr int stream_wait_imm(int n) {
+  return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4);
+}
+
+// Epilogue of the streaming GEMM: lane (fr, fh) of wave w holds row 32 i + fr
+// and, of weight fragment j, columns 8 q + 4 fh .. + 3 in registers
+// 4 q .. 4 q + 3; bias, activation (SwiGLU: silu(W1 part) * W3 part), bf16
+// rounding, stored as 8-byte pieces; rows past mrows are not stored.
+template <int EPI, bool HAS_BIAS, int MF>
+__device__ __forceinline__ void stream_epilogue(const f32x16 (&acc)[MF][2], const float* __restrict__ bg,
+                                                int row0, int mrows, int n0, bf16* __restrict__ C,
+                                                int N) {
+  constexpr bool GATED = EPI == EPI_SWIGLU;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int fr = lane & 31, fh = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < MF; ++i) {
+    const int m = 32 * i + fr;
+    if (m >= mrows) continue;
+    bf16* crow = C + (int64_t)(row0 + m) * N;
+#pragma unroll
+    for (int j = 0; j < (GATED ? 1 : 2); ++j) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = (GATED ? n0 + 32 * wave : n0 + 64 * wave + 32 * j) + 8 * q + 4 * fh;
+        const float4 bq = HAS_BIAS ? *reinterpret_cast<const float4*>(bg + c)
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float bb[4] = {bq.x, bq.y, bq.z, bq.w};
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          v[e] = epilogue_bf16<EPI>(acc[i][j][4 * q + e] + bb[e], GATED ? acc[i][1][4 * q + e] : 0.f);
+        uint2 u;
+        u.x = pack_bf16x2(v[0], v[1]);
+        u.y = pack_bf16x2(v[2], v[3]);
+        *reinterpret_cast<uint2*>(crow + c) = u;
+      }
+    }
+  }
+}
+
+template <int EPI, bool HAS_BIAS, int MF>
+__device__ __forceinline__ void stream_tile(u32x4* __restrict__ smem, const bf16* __restrict__ A,
+                                            uint32_t a_bytes, const int32_t* __restrict__ arows,
+                                            const bf16* __restrict__ Wg, const bf16* __restrict__ W3g,
+                                            const float* __restrict__ bg, int row0, int mrows,
+                                            int n0, bf16* __restrict__ C, int N, int K) {
+  constexpr bool GATED = EPI == EPI_SWIGLU;
+  constexpr int CH = 8;                        // 16-byte chunks per 128-byte LDS row
+  constexpr int WAREA = 64 * CH;               // u32x4: one wave's 64 weight rows
+  constexpr int ABASE = 4 * WAREA;             // token-row stages after the weight areas
+  constexpr int ASTAGE = 32 * MF * CH;         // u32x4 per token-row stage
+  constexpr int NW = 8;                        // weight loads per wave per K step
+  constexpr int NA = MF;                       // token-row loads per wave per K step
+  constexpr int NL = NW + NA;
+  static_assert(ABASE + 4 * ASTAGE <= kStreamLds, "LDS");
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int fr = lane & 31, fh = lane >> 5;
+  const int nk = K / 64;                       // multiple of 4
+  const int lr = lane >> 3;                    // row of a load within its 8-row group
+  const int lc = lane & 7;                     // 16-byte chunk of a load
+
+  // token rows: wave w loads stage rows 8 (w MF + i) + lr
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, (int)a_bytes, 0x00020000);
+  uint32_t aoff[MF];
+#pragma unroll
+  for (int i = 0; i < MF; ++i) {
+    const int rl = 8 * (wave * MF + i) + lr;
+    const int r = row0 + min(rl, mrows - 1);
+    const uint32_t rowoff = (uint32_t)(arows ? arows[r] : r) * (uint32_t)K * 2u;
+    aoff[i] = rowoff + (uint32_t)(lc ^ ((rl >> 1) & 7)) * 16u;
+  }
+  // weight rows of this wave: fragment j = 32 consecutive rows of W (SwiGLU:
+  // j = 0 of W1, j = 1 of W3); load i (fragment i / 4) brings rows 8 (i % 4) + lr
+  // of the fragment, chunk lc, into registers, then into the wave's LDS area
+  // at row 8 i + lr, chunk lc ^ ((row >> 1) & 7)
+  const bf16* wrow0 = GATED ? Wg + (int64_t)(n0 + 32 * wave) * K
+                            : Wg + (int64_t)(n0 + 64 * wave) * K;
+  const bf16* wrow1 = GATED ? W3g + (int64_t)(n0 + 32 * wave) * K
+                            : Wg + (int64_t)(n0 + 64 * wave + 32) * K;
+  const __amdgpu_buffer_rsrc_t rw0 =
+      __builtin_amdgcn_make_buffer_rsrc((void*)wrow0, (short)0, 32 * K * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rw1 =
+      __builtin_amdgcn_make_buffer_rsrc((void*)wrow1, (short)0, 32 * K * 2, 0x00020000);
+  uint32_t woff[4];
+  int wput[NW];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) woff[q] = (uint32_t)(8 * q + lr) * (uint32_t)K * 2u + (uint32_t)lc * 16u;
+  const int warea = wave * WAREA;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const int rw = 8 * i + lr;
+    wput[i] = warea + rw * CH + (lc ^ ((rw >> 1) & 7));
+  }
+  // fragment reads: row 32 i + fr of a 32-row block, logical chunk 4 fh + s
+  const int rsw = (fr >> 1) & 7;
+  int cread[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) cread[s] = fr * CH + ((4 * fh + s) ^ rsw);
+
+  u32x4 wr[4][NW];      // weight rows in flight, slot = K step % 4
+  bf16x8 fw[2][2];      // weight fragments [sub-step parity][j]
+  bf16x8 fa[2][MF];     // token fragments [sub-step parity][i]
+  f32x16 acc[MF][2];
+#pragma unroll
+  for (int i = 0; i < MF; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+#define MOE_SB() __builtin_amdgcn_sched_barrier(0)
+#define MOE_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+  // weight loads of K step kt into register slot sl (non-temporal: read once)
+#define MOE_LW(kt, sl, i0, i1)                                                        \
+  do {                                                                                \
+    _Pragma("unroll") for (int i_ = (i0); i_ < (i1); ++i_)                            \
+      wr[sl][i_] = __builtin_amdgcn_raw_buffer_load_b128(i_ < 4 ? rw0 : rw1, woff[i_ & 3], \
+                                                         (kt) * 128, 2);             \
+  } while (0)
+  // token-row loads of K step kt into stage st (cached: the group's other slabs
+  // read the same rows)
+#define MOE_LA(kt, st)                                                                \
+  do {                                                                                \
+    _Pragma("unroll") for (int i_ = 0; i_ < NA; ++i_)                                 \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, MOE_LDS(smem + ABASE + (st) * ASTAGE + (wave * MF + i_) * 64), \
+                                               16, aoff[i_], (uint32_t)(kt) * 128u, 0, 0); \
+  } while (0)
+  // the weight rows of slot sl into this wave's LDS area
+#define MOE_PUT(sl)                                                                   \
+  do {                                                                                \
+    _Pragma("unroll") for (int i_ = 0; i_ < NW; ++i_) smem[wput[i_]] = wr[sl][i_];    \
+  } while (0)
+#define MOE_RD(b, st, s)                                                              \
+  do {                                                                                \
+    fw[b][0] = __builtin_bit_cast(bf16x8, smem[warea + cread[s]]);                    \
+    fw[b][1] = __builtin_bit_cast(bf16x8, smem[warea + 32 * CH + cread[s]]);          \
+    _Pragma("unroll") for (int i_ = 0; i_ < MF; ++i_)                                 \
+      fa[b][i_] = __builtin_bit_cast(bf16x8, smem[ABASE + (st) * ASTAGE + i_ * 32 * CH + cread[s]]); \
+  } while (0)
+#define MOE_MM(b)                                                                     \
+  do {                                                                                \
+    _Pragma("unroll") for (int i_ = 0; i_ < MF; ++i_) {                               \
+      acc[i_][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[b][0], fa[b][i_], acc[i_][0], 0, 0, 0); \
+      acc[i_][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[b][1], fa[b][i_], acc[i_][1], 0, 0, 0); \
+    }                                                                                 \
+  } while (0)
+  // K step kt (register slot and token stage sl = kt % 4; its weights already
+  // in the wave's LDS area and its first fragments in fa[0] / fw[0]). LOAD
+  // issues the loads of step kt + 3 (weights spread over the sub-steps, then
+  // the token rows). Before the last sub-step's MFMAs: wait until the loads of
+  // step kt + 1 have landed (vmcnt WAITN; all LDS reads of this step done),
+  // barrier (publishes token stage kt + 1, retires stage kt), store the
+  // weights of step kt + 1 into the wave's area and read the first fragments
+  // of step kt + 1.
+#define MOE_KSTEP(kt, sl, LOAD, WAITN, LAST)                                          \
+  do {                                                                                \
+    if (LOAD) MOE_LW((kt) + 3, ((sl) + 3) & 3, 0, 2);                                 \
+    MOE_RD(1, sl, 1);                                                                 \
+    MOE_SB();                                                                         \
+    MOE_MM(0);                                                                        \
+    MOE_SB();                                                                         \
+    if (LOAD) MOE_LW((kt) + 3, ((sl) + 3) & 3, 2, 5);                                 \
+    MOE_RD(0, sl, 2);                                                                 \
+    MOE_SB();                                                                         \
+    MOE_MM(1);                                                                        \
+    MOE_SB();                                                                         \
+    if (LOAD) MOE_LW((kt) + 3, ((sl) + 3) & 3, 5, 8);                                 \
+    if (LOAD) MOE_LA((kt) + 3, ((sl) + 3) & 3);                                       \
+    MOE_RD(1, sl, 3);                                                                 \
+    MOE_SB();                                                                         \
+    MOE_MM(0);                                                                        \
+    MOE_SB();                                                                         \
+    if (!(LAST)) {                                                                    \
+      __builtin_amdgcn_s_waitcnt(stream_wait_imm(WAITN));                             \
+      __builtin_amdgcn_s_barrier();                                                   \
+      MOE_SB();                                                                       \
+      MOE_PUT(((sl) + 1) & 3);                                                        \
+      MOE_RD(0, ((sl) + 1) & 3, 0);                                                   \
+      MOE_SB();                                                                       \
+    }                                                                                 \
+    MOE_MM(1);                                                                        \
+    MOE_SB();                                                                         \
+  } while (0)
+
+  // prologue: steps 0, 1, 2 in flight (weights then token rows of each)
+#pragma unroll
+  for (int kt = 0; kt < 3; ++kt) {
+    MOE_LW(kt, kt, 0, NW);
+    MOE_LA(kt, kt);
+  }
+  __builtin_amdgcn_s_waitcnt(stream_wait_imm(2 * NL));
+  __builtin_amdgcn_s_barrier();
+  MOE_SB();
+  MOE_PUT(0);
+  MOE_RD(0, 0, 0);
+  for (int kt = 0; kt < nk - 4; kt += 4) {
+    MOE_KSTEP(kt + 0, 0, true, 2 * NL, false);
+    MOE_KSTEP(kt + 1, 1, true, 2 * NL, false);
+    MOE_KSTEP(kt + 2, 2, true, 2 * NL, false);
+    MOE_KSTEP(kt + 3, 3, true, 2 * NL, false);
+  }
+  MOE_KSTEP(nk - 4, 0, true, 2 * NL, false);
+  MOE_KSTEP(nk - 3, 1, false, NL, false);
+  MOE_KSTEP(nk - 2, 2, false, 0, false);
+  MOE_KSTEP(nk - 1, 3, false, 0, true);
+#undef MOE_KSTEP
+#undef MOE_MM
+#undef MOE_RD
+#undef MOE_PUT
+#undef MOE_LA
+#undef MOE_LW
+#undef MOE_LDS
+#undef MOE_SB
+
+  stream_epilogue<EPI, HAS_BIAS, MF>(acc, bg, row0, mrows, n0, C, N);
+}
+
+// The same tile on a packed copy of the weights (moe_pack_weights): per slab
+// and K step, wave w's weight fragments are 8 KB in fragment order (fragment j,
+// sub-step q, lane l: 16 bytes = row 32 j + l % 32 of the wave's 64 rows, K
+// elements 32 (l / 32) + 8 q .. + 7 of the step), so each wave streams
+// contiguous 1 KB runs from HBM straight into its MFMA operand registers,
+// three K steps ahead, with no trip through LDS; only the token rows are
+// staged in LDS (four stages, three ahead).
+template <int EPI, bool HAS_BIAS, int MF>
+__device__ __forceinline__ void stream_tile_packed(u32x4* __restrict__ smem,
+                                                   const bf16* __restrict__ A, uint32_t a_bytes,
+                                                   const int32_t* __restrict__ arows,
+                                                   const bf16* __restrict__ Wpg, int slab,
+                                                   const float* __restrict__ bg, int row0,
+                                                   int mrows, int n0, bf16* __restrict__ C, int N,
+                                                   int K) {
+  constexpr int CH = 8;
+  constexpr int ASTAGE = 32 * MF * CH;         // u32x4 per token-row stage
+  constexpr int NW = 8, NA = MF, NL = NW + NA;
+  static_assert(4 * ASTAGE <= kStreamLds, "LDS");
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int fr = lane & 31, fh = lane >> 5;
+  const int nk = K / 64;                       // multiple of 4
+  const int lr = lane >> 3, lc = lane & 7;
+
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, (int)a_bytes, 0x00020000);
+  uint32_t aoff[MF];
+#pragma unroll
+  for (int i = 0; i < MF; ++i) {
+    const int rl = 8 * (wave * MF + i) + lr;
+    const int r = row0 + min(rl, mrows - 1);
+    const uint32_t rowoff = (uint32_t)(arows ? arows[r] : r) * (uint32_t)K * 2u;
+    aoff[i] = rowoff + (uint32_t)(lc ^ ((rl >> 1) & 7)) * 16u;
+  }
+  // this wave's packed weights: 8 KB per K step, K steps 32 KB apart
+  const char* wbase = reinterpret_cast<const char*>(Wpg) + ((int64_t)slab * nk * 4 + wave) * 8192;
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)wbase, (short)0, (nk - 1) * 32768 + 8192, 0x00020000);
+  const uint32_t wlane = (uint32_t)lane * 16u;
+  const int rsw = (fr >> 1) & 7;
+  int cread[4];
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4) cread[s4] = fr * CH + ((4 * fh + s4) ^ rsw);
+
+  bf16x8 wr[4][2][4];   // weight fragments in flight [slot = K step % 4][j][sub-step]
+  bf16x8 fa[MF];        // token fragments of the current sub-step
+  f32x16 acc[MF][2];
+#pragma unroll
+  for (int i = 0; i < MF; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+#define MOE_SB() __builtin_amdgcn_sched_barrier(0)
+#define MOE_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+#define MOE_LW(kt, sl, q)                                                             \
+  do {                                                                                \
+    wr[sl][0][q] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(  \
+                                                 rw, wlane + (q) * 1024u, (kt) * 32768, 2)); \
+    wr[sl][1][q] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(  \
+                                                 rw, wlane + (4 + (q)) * 1024u, (kt) * 32768, 2)); \
+  } while (0)
+#define MOE_LA(kt, st)                                                                \
+  do {                                                                                \
+    _Pragma("unroll") for (int i_ = 0; i_ < NA; ++i_)                                 \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, MOE_LDS(smem + (st) * ASTAGE + (wave * MF + i_) * 64), \
+                                               16, aoff[i_], (uint32_t)(kt) * 128u, 0, 0); \
+  } while (0)
+  // Sub-step s of the step in slot sl: for each token fragment i, its two
+  // MFMAs, then the read of fragment i for (stage srd, sub-step s2) into the
+  // same registers; then (LOAD) the weight loads of step kl, sub-step s, into
+  // slot (sl + 3) & 3, in the registers sub-step s has just consumed.
+#define MOE_SUB(sl, s, srd, s2, LOAD, kl)                                             \
+  do {                                                                                \
+    _Pragma("unroll") for (int i_ = 0; i_ < MF; ++i_) {                               \
+      acc[i_][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wr[sl][0][s], fa[i_], acc[i_][0], 0, 0, 0); \
+      acc[i_][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wr[sl][1][s], fa[i_], acc[i_][1], 0, 0, 0); \
+      fa[i_] = __builtin_bit_cast(bf16x8, smem[(srd) * ASTAGE + i_ * 32 * CH + cread[s2]]); \
+      MOE_SB();                                                                       \
+    }                                                                                 \
+    if (LOAD) MOE_LW(kl, ((sl) + 3) & 3, s);                                          \
+    MOE_SB();                                                                         \
+  } while (0)
+  // K step kt (register slot and token stage sl = kt % 4). Issue order per
+  // step: weights of step kt + 3 for sub-steps 0..2, its token rows, then (after
+  // the barrier) its weights for sub-step 3. Before the last sub-step: wait
+  // until the token rows of step kt + 1 have landed (vmcnt WAITN) and all LDS
+  // reads of this step are done, barrier; the last sub-step then reads the
+  // first token fragments of step kt + 1.
+#define MOE_KSTEP(kt, sl, LOAD, WAITN, LAST)                                          \
+  do {                                                                                \
+    MOE_SUB(sl, 0, sl, 1, LOAD, (kt) + 3);                                            \
+    MOE_SUB(sl, 1, sl, 2, LOAD, (kt) + 3);                                            \
+    MOE_SUB(sl, 2, sl, 3, LOAD, (kt) + 3);                                            \
+    if (LOAD) MOE_LA((kt) + 3, ((sl) + 3) & 3);                                       \
+    if (!(LAST)) {                                                                    \
+      __builtin_amdgcn_s_waitcnt(stream_wait_imm(WAITN));                             \
+      __builtin_amdgcn_s_barrier();                                                   \
+      MOE_SB();                                                                       \
+      MOE_SUB(sl, 3, ((sl) + 1) & 3, 0, LOAD, (kt) + 3);                              \
+    } else {                                                                          \
+      _Pragma("unroll") for (int i_ = 0; i_ < MF; ++i_) {                             \
+        acc[i_][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wr[sl][0][3], fa[i_], acc[i_][0], 0, 0, 0); \
+        acc[i_][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wr[sl][1][3], fa[i_], acc[i_][1], 0, 0, 0); \
+      }                                                                               \
+    }                                                                                 \
+  } while (0)
+
+  // prologue: steps 0, 1, 2 in the steady-state issue order (sub-steps 0..2,
+  // token rows, sub-step 3); wait for the token rows of step 0
+#pragma unroll
+  for (int kt = 0; kt < 3; ++kt) {
+#pragma unroll
+    for (int q = 0; q < 3; ++q) MOE_LW(kt, kt, q);
+    MOE_LA(kt, kt);
+    MOE_LW(kt, kt, 3);
+  }
+  __builtin_amdgcn_s_waitcnt(stream_wait_imm(2 * NL + 2));
+  __builtin_amdgcn_s_barrier();
+  MOE_SB();
+#pragma unroll
+  for (int i = 0; i < MF; ++i) fa[i] = __builtin_bit_cast(bf16x8, smem[i * 32 * CH + cread[0]]);
+  MOE_SB();
+  // loads issued after the token rows of step kt + 1, at the wait of step kt:
+  // steady state 2 NL; then NL + 2 and 2 for the last two waits
+  for (int kt = 0; kt < nk - 4; kt += 4) {
+    MOE_KSTEP(kt + 0, 0, true, 2 * NL, false);
+    MOE_KSTEP(kt + 1, 1, true, 2 * NL, false);
+    MOE_KSTEP(kt + 2, 2, true, 2 * NL, false);
+    MOE_KSTEP(kt + 3, 3, true, 2 * NL, false);
+  }
+  MOE_KSTEP(nk - 4, 0, true, 2 * NL, false);
+  MOE_KSTEP(nk - 3, 1, false, NL + 2, false);
+  MOE_KSTEP(nk - 2, 2, false, 2, false);
+  MOE_KSTEP(nk - 1, 3, false, 0, true);
+#undef MOE_KSTEP
+#undef MOE_SUB
+#undef MOE_LA
+#undef MOE_LW
+#undef MOE_LDS
+#undef MOE_SB
+  stream_epilogue<EPI, HAS_BIAS, MF>(acc, bg, row0, mrows, n0, C, N);
+}
+
+// One launch over every group with rows in (0, max_rows]: work items (group,
+// slab, part) in the XCD-aware order; blocks past the item count exit.
+// Requires N a multiple of 256, K a multiple of 256, and the A operand
+// addressable with 32-bit byte offsets (a_bytes < 2^32; checked by the host).
+template <int EPI, bool HAS_BIAS>
+__global__ __launch_bounds__(256, 1) void gemm_stream_kernel(
+    const bf16* __restrict__ A, const bf16* __restrict__ W, const bf16* __restrict__ W3,
+    const float* __restrict__ bias, const bf16* __restrict__ Ws, const bf16* __restrict__ Ws3,
+    const float* __restrict__ bias_s, int E, int G, const int32_t* __restrict__ offsets,
+    int rows_max, bf16* __restrict__ C, int N, int K, const int32_t* __restrict__ arows,
+    uint32_t a_bytes, int max_rows, const bf16* __restrict__ Wp) {
+  constexpr bool GATED = EPI == EPI_SWIGLU;
+  constexpr int BNO = GATED ? 128 : 256;   // output columns per slab
+  __shared__ u32x4 smem[kStreamLds];   // the K-step stages (160 KB)
+  const int ns = N / BNO;
+  StreamSpace ss;
+  stream_space_init(ss, offsets, G, rows_max, max_rows, ns);
+  const int items = __builtin_amdgcn_readfirstlane(ss.total);
+  const int b = blockIdx.x;
+  if (b >= items) return;
+  const int t8 = items & ~7;
+  const int t = b < t8 ? (b & 7) * (t8 >> 3) + (b >> 3) : b;
+  int g, row0, nrows, slab;
+  stream_lookup(ss, t, ns, g, row0, nrows, slab);
+  g = __builtin_amdgcn_readfirstlane(g);
+  row0 = __builtin_amdgcn_readfirstlane(row0);
+  nrows = __builtin_amdgcn_readfirstlane(nrows);
+  slab = __builtin_amdgcn_readfirstlane(slab);
+  const int n0 = slab * BNO;
+  const bf16* Wg = g < E ? W + (int64_t)g * N * K : Ws;
+  const bf16* W3g = GATED ? (g < E ? W3 + (int64_t)g * N * K : Ws3) : Wg;
+  const float* bg = HAS_BIAS ? (g < E ? bias + (int64_t)g * N : bias_s) : nullptr;
+  const int mf = (nrows + 31) / 32;
+  if (Wp) {
+    // packed weights of group g: (SwiGLU: 2 x) N x K elements per group
+    const bf16* Wpg = Wp + (int64_t)g * (GATED ? 2 : 1) * N * K;
+    if (mf <= 2)
+      stream_tile_packed<EPI, HAS_BIAS, 2>(smem, A, a_bytes, arows, Wpg, slab, bg, row0, nrows, n0, C, N, K);
+    else if (mf <= 4)
+      stream_tile_packed<EPI, HAS_BIAS, 4>(smem, A, a_bytes, arows, Wpg, slab, bg, row0, nrows, n0, C, N, K);
+    else if (mf <= 6)
+      stream_tile_packed<EPI, HAS_BIAS, 6>(smem, A, a_bytes, arows, Wpg, slab, bg, row0, nrows, n0, C, N, K);
+    else
+      stream_tile_packed<EPI, HAS_BIAS, 8>(smem, A, a_bytes, arows, Wpg, slab, bg, row0, nrows, n0, C, N, K);
+    return;
+  }
+  if (mf <= 2)
+    stream_tile<EPI, HAS_BIAS, 2>(smem, A, a_bytes, arows, Wg, W3g, bg, row0, nrows, n0, C, N, K);
+  else if (mf <= 4)
+    stream_tile<EPI, HAS_BIAS, 4>(smem, A, a_bytes, arows, Wg, W3g, bg, row0, nrows, n0, C, N, K);
+  else if (mf <= 6)
+    stream_tile<EPI, HAS_BIAS, 6>(smem, A, a_bytes, arows, Wg, W3g, bg, row0, nrows, n0, C, N, K);
+  else
+    stream_tile<EPI, HAS_BIAS, 8>(smem, A, a_bytes, arows, Wg, W3g, bg, row0, nrows, n0, C, N, K);
+}
+
 // float32 layers: one thread per (row, column) of a tile, plain FMA loop.
 template <int EPI, bool HAS_BIAS>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(
@@ -939,6 +1481,41 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(
   }
 }
 
+// Packed copy of a group's weights in the order the streaming GEMM's packed
+// tile reads them. 16-byte unit u of group g: lane l = u % 64, sub-step
+// q = (u / 64) % 4, fragment j = (u / 256) % 2, wave w = (u / 512) % 4, K step
+// k and slab s from u / 2048; it holds K elements 64 k + 32 (l / 32) + 8 q ..
+// + 7 of weight row (SwiGLU: j = 0 row 128 s + 32 w + l % 32 of W1, j = 1 the
+// same row of W3; otherwise row 256 s + 64 w + 32 j + l % 32 of W). Groups
+// g < E come from W (W3) + g N K, group E from Ws (Ws3).
+template <bool GATED>
+__global__ __launch_bounds__(256) void pack_weights_kernel(
+    const bf16* __restrict__ W, const bf16* __restrict__ W3, const bf16* __restrict__ Ws,
+    const bf16* __restrict__ Ws3, int E, int G, int N, int K, u32x4* __restrict__ out) {
+  const int nk = K / 64;
+  const int64_t per_group = (int64_t)(GATED ? 2 : 1) * N * K / 8;   // 16-byte units
+  const int64_t total = per_group * G;
+  for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < total; u += (int64_t)gridDim.x * 256) {
+    const int g = (int)(u / per_group);
+    const int64_t v = u - (int64_t)g * per_group;
+    const int l = (int)(v & 63), q = (int)((v >> 6) & 3), j = (int)((v >> 8) & 1),
+              w = (int)((v >> 9) & 3);
+    const int64_t rest = v >> 11;
+    const int k = (int)(rest % nk);
+    const int s = (int)(rest / nk);
+    const bf16* src;
+    int row;
+    if (GATED) {
+      src = j == 0 ? (g < E ? W + (int64_t)g * N * K : Ws) : (g < E ? W3 + (int64_t)g * N * K : Ws3);
+      row = 128 * s + 32 * w + (l & 31);
+    } else {
+      src = g < E ? W + (int64_t)g * N * K : Ws;
+      row = 256 * s + 64 * w + 32 * j + (l & 31);
+    }
+    out[u] = *reinterpret_cast<const u32x4*>(src + (int64_t)row * K + 64 * k + 32 * (l >> 5) + 8 * q);
+  }
+}
+
 // Block slots of the persistent 128 x 128 kernel on the current device: two
 // per CU, a multiple of 8 (one share per XCD), cached per device.
 static int gemm_slots() {
@@ -960,7 +1537,7 @@ static hipError_t gemm_launch(const moe_config& c, const ET* A, const void* W, c
                               const float* bias, const void* Ws, const void* Ws3,
                               const float* bias_s, const int32_t* offsets, ET* C, int N, int K,
                               hipStream_t s, const int32_t* arows = nullptr,
-                              const bf16* zin = nullptr) {
+                              const bf16* zin = nullptr, const void* wpacked = nullptr) {
   const int E = c.num_experts, G = c.num_experts + c.num_shared_experts;
   const int64_t rows = rows_max(c);
   if constexpr (sizeof(ET) == 2) {
@@ -975,6 +1552,24 @@ static hipError_t gemm_launch(const moe_config& c, const ET* A, const void* W, c
     // gathered A rows (arows) are addressed with 32-bit offsets from the start
     // of x, which the 256 x 256 kernel's buffer loads need below 4 GiB
     const int64_t a_bytes = arows ? c.tokens * (int64_t)K * 2 : 0;
+    // Groups of at most kStreamMaxRows rows go to the weight-streaming kernel
+    // (forward epilogues; its A operand addressed with 32-bit byte offsets),
+    // the others to the 256 x 256 and 128 x 128 kernels below.
+    constexpr bool kStreamEpi = EPI == EPI_GELU || EPI == EPI_RELU || EPI == EPI_SWIGLU ||
+                                EPI == EPI_NONE;
+    const int64_t a_span = arows ? a_bytes : rows * (int64_t)K * 2;
+    const int skip = kStreamEpi && a_span < ((int64_t)1 << 32) ? kStreamMaxRows : 0;
+    if constexpr (kStreamEpi) {
+      if (skip > 0) {
+        constexpr int BNO = EPI == EPI_SWIGLU ? 128 : 256;
+        // items: at most (ceil(rows / 256) + G) parts x N / BNO slabs
+        const int64_t items = ((rows + kStreamRows - 1) / kStreamRows + G) * (N / BNO);
+        hipLaunchKernelGGL((gemm_stream_kernel<EPI, HB>), dim3((unsigned)items), dim3(256), 0, s, A,
+                           (const bf16*)W, (const bf16*)W3, bias, (const bf16*)Ws, (const bf16*)Ws3,
+                           bias_s, E, G, offsets, (int)rows, C, N, K, arows, (uint32_t)a_span, skip,
+                           (const bf16*)wpacked);
+      }
+    }
     // (the backward epilogues EPI_DGELU / EPI_DRELU exist in the 128 x 128 kernel only)
     const bool big = rows >= kGemmBigBM && (EPI == EPI_NONE || K >= 2048) &&
                      EPI != EPI_DGELU && EPI != EPI_DRELU && a_bytes < ((int64_t)1 << 32);
@@ -985,20 +1580,21 @@ static hipError_t gemm_launch(const moe_config& c, const ET* A, const void* W, c
       if constexpr (EPI != EPI_DGELU && EPI != EPI_DRELU)
         hipLaunchKernelGGL((gemm_bf16_big_kernel<EPI, HB>), dim3(big_tiles), dim3(256), 0, s, A,
                            (const bf16*)W, (const bf16*)W3, bias, (const bf16*)Ws, (const bf16*)Ws3,
-                           bias_s, E, G, offsets, (int)rows, C, N, K, arows, (uint32_t)a_bytes);
+                           bias_s, E, G, offsets, (int)rows, C, N, K, arows, (uint32_t)a_bytes,
+                           skip);
       // each group leaves at most 255 rows, i.e. at most 2 tiles, and the
       // tiles number at most ceil(rows / 128) + G
       const int64_t rest = (rows + 127) / 128 + G < 2 * G ? (rows + 127) / 128 + G : 2 * G;
       const int64_t rgrid = rest * (N / BN) < slots ? rest * (N / BN) : slots;
       hipLaunchKernelGGL((gemm_bf16_kernel<EPI, HB>), dim3((unsigned)rgrid), dim3(256), 0, s, A,
                          (const bf16*)W, (const bf16*)W3, bias, (const bf16*)Ws, (const bf16*)Ws3,
-                         bias_s, E, G, offsets, (int)rows, C, N, K, 2, arows, 1, zin);
+                         bias_s, E, G, offsets, (int)rows, C, N, K, 2, arows, 1, zin, skip);
     } else {
       const int64_t tiles = ((rows + 127) / 128 + G) * (N / BN);
       const int64_t grid = tiles < slots ? tiles : slots;
       hipLaunchKernelGGL((gemm_bf16_kernel<EPI, HB>), dim3((unsigned)grid), dim3(256), 0, s, A,
                          (const bf16*)W, (const bf16*)W3, bias, (const bf16*)Ws, (const bf16*)Ws3,
-                         bias_s, E, G, offsets, (int)rows, C, N, K, 0, arows, 1, zin);
+                         bias_s, E, G, offsets, (int)rows, C, N, K, 0, arows, 1, zin, skip);
     }
   } else {
     const unsigned mtiles = (unsigned)((rows + kGemmBM - 1) / kGemmBM) + G;
@@ -1060,7 +1656,7 @@ hipError_t launch_router_gemm(const moe_config& c, const void* x, const void* w_
                      (const bf16*)x, (const bf16*)w_gate, (const bf16*)nullptr, (const float*)nullptr,
                      (const bf16*)nullptr, (const bf16*)nullptr, (const float*)nullptr, 1, 1,
                      (const int32_t*)nullptr, (int)T, (void*)partials, E, K, 0,
-                     (const int32_t*)nullptr, kp, (const bf16*)nullptr);
+                     (const int32_t*)nullptr, kp, (const bf16*)nullptr, 0);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int64_t n4 = T * E / 4;
@@ -1077,13 +1673,13 @@ static hipError_t up_typed(const moe_config& c, const ET* a, const int32_t* arow
   switch (c.activation) {
     case MOE_ACT_GELU:
       return gemm_launch<ET, EPI_GELU, HB>(c, a, w.w1, nullptr, w.b1, w.ws1, nullptr, w.bs1, off, h,
-                                           N, K, s, arows);
+                                           N, K, s, arows, nullptr, w.up_packed);
     case MOE_ACT_RELU:
       return gemm_launch<ET, EPI_RELU, HB>(c, a, w.w1, nullptr, w.b1, w.ws1, nullptr, w.bs1, off, h,
-                                           N, K, s, arows);
+                                           N, K, s, arows, nullptr, w.up_packed);
     default:
       return gemm_launch<ET, EPI_SWIGLU, HB>(c, a, w.w1, w.w3, w.b1, w.ws1, w.ws3, w.bs1, off, h, N,
-                                             K, s, arows);
+                                             K, s, arows, nullptr, w.up_packed);
   }
 }
 
@@ -1102,10 +1698,11 @@ hipError_t launch_expert_down(const moe_config& c, const void* h, const int32_t*
   if (c.act_dtype == MOE_BF16)
     return c.has_bias
                ? gemm_launch<bf16, EPI_NONE, true>(c, (const bf16*)h, w.w2, nullptr, w.b2, w.ws2,
-                                                   nullptr, w.bs2, offsets, (bf16*)y_perm, N, K, s)
+                                                   nullptr, w.bs2, offsets, (bf16*)y_perm, N, K, s,
+                                                   nullptr, nullptr, w.down_packed)
                : gemm_launch<bf16, EPI_NONE, false>(c, (const bf16*)h, w.w2, nullptr, w.b2, w.ws2,
                                                     nullptr, w.bs2, offsets, (bf16*)y_perm, N, K,
-                                                    s);
+                                                    s, nullptr, nullptr, w.down_packed);
   return c.has_bias
              ? gemm_launch<float, EPI_NONE, true>(c, (const float*)h, w.w2, nullptr, w.b2, w.ws2,
                                                   nullptr, w.bs2, offsets, (float*)y_perm, N, K, s)
@@ -1159,6 +1756,42 @@ hipError_t launch_backward_dx(const moe_config& c, const void* dz, const int32_t
   const int K = (int)c.d_ff * (c.activation == MOE_ACT_SWIGLU ? 2 : 1);
   return gemm_launch<bf16, EPI_NONE, false>(c, (const bf16*)dz, w1t, nullptr, nullptr, ws1t, nullptr,
                                             nullptr, offsets, (bf16*)dxp, N, K, s);
+}
+
+size_t packed_weights_bytes(const moe_config& c, int which) {
+  const int64_t G = c.num_experts + c.num_shared_experts;
+  const int64_t mats = which == 0 && c.activation == MOE_ACT_SWIGLU ? 2 : 1;
+  return (size_t)(G * mats * c.d_ff * c.d_model * 2);
+}
+
+hipError_t launch_pack_weights(const moe_config& c, const moe_weights& w, void* up, void* down,
+                               hipStream_t s) {
+  const int E = c.num_experts, G = c.num_experts + c.num_shared_experts;
+  const int F = (int)c.d_ff, d = (int)c.d_model;
+  auto grid = [](size_t bytes) {
+    const size_t units = bytes / 16;
+    const size_t b = (units + 255) / 256;
+    return (unsigned)(b < 8192 ? (b > 0 ? b : 1) : 8192);
+  };
+  if (up) {
+    if (c.activation == MOE_ACT_SWIGLU)
+      hipLaunchKernelGGL(pack_weights_kernel<true>, dim3(grid(packed_weights_bytes(c, 0))), dim3(256), 0,
+                         s, (const bf16*)w.w1, (const bf16*)w.w3, (const bf16*)w.ws1,
+                         (const bf16*)w.ws3, E, G, F, d, (u32x4*)up);
+    else
+      hipLaunchKernelGGL(pack_weights_kernel<false>, dim3(grid(packed_weights_bytes(c, 0))), dim3(256),
+                         0, s, (const bf16*)w.w1, (const bf16*)nullptr, (const bf16*)w.ws1,
+                         (const bf16*)nullptr, E, G, F, d, (u32x4*)up);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (down) {
+    hipLaunchKernelGGL(pack_weights_kernel<false>, dim3(grid(packed_weights_bytes(c, 1))), dim3(256), 0,
+                       s, (const bf16*)w.w2, (const bf16*)nullptr, (const bf16*)w.ws2,
+                       (const bf16*)nullptr, E, G, d, F, (u32x4*)down);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_wgrad(const void* a, const void* b, const int32_t* po, int G, int E, int M, int N,

@@ -203,6 +203,29 @@ int moe_monitoring(const moe_config* cfg, const moe_stats* st, moe_monitor* out)
   return MOE_OK;
 }
 
+int moe_packed_weights_size(const moe_config* cfg, size_t* up_bytes, size_t* down_bytes) {
+  const int v = validate(cfg);
+  if (v != MOE_OK) return v;
+  if (!up_bytes || !down_bytes) return MOE_ERR_INVALID_ARG;
+  if (cfg->act_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  *up_bytes = packed_weights_bytes(*cfg, 0);
+  *down_bytes = packed_weights_bytes(*cfg, 1);
+  return MOE_OK;
+}
+
+int moe_pack_weights(const moe_config* cfg, const moe_weights* w, void* up_packed,
+                     void* down_packed, void* stream) {
+  const int v = validate(cfg);
+  if (v != MOE_OK) return v;
+  if (cfg->act_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (!w) return MOE_ERR_INVALID_ARG;
+  const bool swiglu = cfg->activation == MOE_ACT_SWIGLU, shared = cfg->num_shared_experts == 1;
+  if (up_packed && (!w->w1 || (swiglu && !w->w3) || (shared && (!w->ws1 || (swiglu && !w->ws3)))))
+    return MOE_ERR_INVALID_ARG;
+  if (down_packed && (!w->w2 || (shared && !w->ws2))) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_pack_weights(*cfg, *w, up_packed, down_packed, (hipStream_t)stream));
+}
+
 int moe_capacity(const moe_config* cfg, int64_t* capacity_out) {
   const int v = validate(cfg);
   if (v != MOE_OK) return v;
@@ -324,6 +347,12 @@ int moe_combine(const moe_config* cfg, const void* y_perm, const int32_t* expert
 int moe_forward(const moe_config* cfg, const void* x, const moe_weights* w, void* y,
                 const moe_routing* r, moe_stats* stats, void* workspace, size_t workspace_bytes,
                 void* stream) {
+  return moe_forward_profiled(cfg, x, w, y, r, stats, workspace, workspace_bytes, stream, nullptr);
+}
+
+int moe_forward_profiled(const moe_config* cfg, const void* x, const moe_weights* w, void* y,
+                         const moe_routing* r, moe_stats* stats, void* workspace,
+                         size_t workspace_bytes, void* stream, void* const* events) {
   const int v = validate(cfg);
   if (v != MOE_OK) return v;
   if (cfg->tokens == 0) return MOE_OK;
@@ -338,23 +367,29 @@ int moe_forward(const moe_config* cfg, const void* x, const moe_weights* w, void
   if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
   char* ws = (char*)workspace;
   const hipStream_t s = (hipStream_t)stream;
+  auto mark = [&](int i) {
+    return events && events[i] ? hipEventRecord((hipEvent_t)events[i], s) : hipSuccess;
+  };
+  if (mark(MOE_EV_START) != hipSuccess) return MOE_ERR_HIP;
   hipError_t e = launch_route(*cfg, L, x, w->w_gate, w->b_gate, w->e_bias, r->logits, r->topk_idx,
                               r->topk_gate, stats, ws, s);
-  if (e != hipSuccess) return MOE_ERR_HIP;
+  if (e != hipSuccess || mark(MOE_EV_ROUTED) != hipSuccess) return MOE_ERR_HIP;
   void* y_perm = ws + L.y_perm;
   // the expert-sorted token rows are not copied: GEMM 1 gathers them from x
   // through row_token
   e = launch_permute(*cfg, L, capacity_exact(*cfg), r->topk_idx, x, r->expert_offsets,
                      r->row_token, r->assign_row, nullptr, stats, ws, s);
-  if (e != hipSuccess) return MOE_ERR_HIP;
-  const ExpertWeights ew{w->w1, w->w3, w->w2, w->b1, w->b2, w->ws1, w->ws3, w->ws2, w->bs1, w->bs2};
+  if (e != hipSuccess || mark(MOE_EV_DISPATCHED) != hipSuccess) return MOE_ERR_HIP;
+  const ExpertWeights ew{w->w1,  w->w3,  w->w2,  w->b1,  w->b2,        w->ws1,
+                         w->ws3, w->ws2, w->bs1, w->bs2, w->up_packed, w->down_packed};
   void* h = ws + L.h;
   e = launch_expert_up(*cfg, x, r->expert_offsets, ew, h, s, r->row_token);
-  if (e != hipSuccess) return MOE_ERR_HIP;
+  if (e != hipSuccess || mark(MOE_EV_UP) != hipSuccess) return MOE_ERR_HIP;
   e = launch_expert_down(*cfg, h, r->expert_offsets, ew, y_perm, s);
-  if (e != hipSuccess) return MOE_ERR_HIP;
+  if (e != hipSuccess || mark(MOE_EV_DOWN) != hipSuccess) return MOE_ERR_HIP;
   e = launch_combine(*cfg, y_perm, r->expert_offsets, r->assign_row, r->topk_gate, y, s);
-  return hip_status(e);
+  if (e != hipSuccess || mark(MOE_EV_END) != hipSuccess) return MOE_ERR_HIP;
+  return MOE_OK;
 }
 
 int moe_update_selection_bias(const moe_config* cfg, const moe_stats* stats, float* e_bias,
@@ -403,7 +438,8 @@ int moe_forward_hash(const moe_config* cfg, const void* x, const int32_t* token_
   e = launch_permute(*cfg, L, capacity_exact(*cfg), r->topk_idx, x, r->expert_offsets,
                      r->row_token, r->assign_row, nullptr, stats, ws, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  const ExpertWeights ew{w->w1, w->w3, w->w2, w->b1, w->b2, w->ws1, w->ws3, w->ws2, w->bs1, w->bs2};
+  const ExpertWeights ew{w->w1,  w->w3,  w->w2,  w->b1,  w->b2,        w->ws1,
+                         w->ws3, w->ws2, w->bs1, w->bs2, w->up_packed, w->down_packed};
   void* h = ws + L.h;
   e = launch_expert_up(*cfg, x, r->expert_offsets, ew, h, s, r->row_token);
   if (e != hipSuccess) return MOE_ERR_HIP;

@@ -174,7 +174,16 @@ struct ExpertWeights {
   const float *b1, *b2;
   const void *ws1, *ws3, *ws2;
   const float *bs1, *bs2;
+  // packed copies (moe_pack_weights) read by the weight-streaming GEMM, or null
+  const void* up_packed = nullptr;
+  const void* down_packed = nullptr;
 };
+
+// Bytes of the packed weight copy of GEMM 1 (which = 0: W1, W3) or GEMM 2
+// (which = 1: W2) over every group, and the kernels that write them.
+size_t packed_weights_bytes(const moe_config& c, int which);
+hipError_t launch_pack_weights(const moe_config& c, const moe_weights& w, void* up, void* down,
+                               hipStream_t stream);
 
 // Grouped GEMM 1 with the fused activation: h = act(a W1^T + b1) per group, where
 // row r of the group's input is row r of a or, with arows, row arows[r] of a.
