@@ -133,8 +133,8 @@ typedef struct moe_weights {
   /* Optional packed copies written by moe_pack_weights (NULL: not used). When
    * given, the grouped GEMM reads the weights of groups with few rows from
    * them (same values, the weight-streaming kernel's order); every other read
-   * uses w1 / w3 / w2 / ws*. Read by moe_forward, moe_forward_profiled and
-   * moe_forward_hash; the other entry points ignore them. */
+   * uses w1 / w3 / w2 / ws*. Read by moe_forward, moe_forward_profiled,
+   * moe_forward_noalloc and moe_forward_hash; the other entry points ignore them. */
   const void* up_packed;   /* moe_packed_weights_size up_bytes: W1 (and W3) of every group */
   const void* down_packed; /* moe_packed_weights_size down_bytes: W2 of every group        */
 } moe_weights;
@@ -349,6 +349,30 @@ enum {
 int moe_forward_profiled(const moe_config* cfg, const void* x, const moe_weights* w, void* y,
                          const moe_routing* routing, moe_stats* stats, void* workspace,
                          size_t workspace_bytes, void* stream, void* const* events);
+
+/* Size of the device buffer moe_forward_noalloc works in (per GPU). */
+#define MOE_NOALLOC_WORKSPACE_BYTES ((size_t)128 << 20)
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): moe_forward
+ * with its workspace taken from a buffer the library holds in static device
+ * memory, MOE_NOALLOC_WORKSPACE_BYTES (128 MiB) on each GPU it runs on, kept
+ * until the process ends. Same kernels, arguments and results as moe_forward
+ * with a caller workspace. Allocates nothing and calls no allocating routine.
+ *   The stream must belong to the current device (NULL: its null stream).
+ *   Returns MOE_ERR_WORKSPACE if moe_workspace_size(cfg) exceeds the limit
+ *   (checked before anything else touches the GPU), MOE_ERR_INVALID_ARG if the
+ *   stream belongs to another device.
+ *   Every call on one GPU shares that GPU's buffer, and the buffer keeps the
+ *   last call's contents (the forward needs no zeroed workspace): calls that
+ *   overlap on one GPU (on different streams, or from several threads) race.
+ *   The first call on a device resolves the buffer's address (HIP loads the
+ *   library's device code there if it has not done so yet): make that first
+ *   call outside graph capture.
+ */
+int moe_forward_noalloc(const moe_config* cfg, const void* x, const moe_weights* w, void* y,
+                        const moe_routing* routing, moe_stats* stats, void* stream);
 
 /* ------------------------------------------------------------------ balancing, hash routing */
 

@@ -119,6 +119,8 @@ def lib():
                               P, P, c_size_t, P]
     L.moe_forward_profiled.argtypes = [cfgp, P, ctypes.POINTER(MoeWeights), P,
                                        ctypes.POINTER(MoeRouting), P, P, c_size_t, P, P]
+    L.moe_forward_noalloc.argtypes = [cfgp, P, ctypes.POINTER(MoeWeights), P,
+                                      ctypes.POINTER(MoeRouting), P, P]
     L.moe_update_selection_bias.argtypes = [cfgp, P, P, ctypes.c_float, P]
     L.moe_route_hash.argtypes = [cfgp, P, P, c_int64, P, P, P, P]
     L.moe_forward_hash.argtypes = [cfgp, P, P, P, c_int64, ctypes.POINTER(MoeWeights), P,
@@ -136,7 +138,7 @@ def lib():
                                ctypes.POINTER(MoeGrads), P, c_size_t, P]
     for name in ("moe_validate_config", "moe_capacity", "moe_monitoring", "moe_packed_weights_size", "moe_pack_weights", "moe_workspace_size", "moe_route",
                  "moe_permute", "moe_expert_ffn", "moe_expert_up", "moe_expert_down",
-                 "moe_combine", "moe_forward", "moe_forward_profiled", "moe_forward_train", "moe_backward_workspace_size",
+                 "moe_combine", "moe_forward", "moe_forward_profiled", "moe_forward_noalloc", "moe_forward_train", "moe_backward_workspace_size",
                  "moe_backward", "moe_expert_choice_capacity", "moe_expert_choice_workspace_size",
                  "moe_forward_expert_choice", "moe_update_selection_bias", "moe_route_hash",
                  "moe_forward_hash"):
@@ -408,6 +410,28 @@ def forward(cfg, x, weights: Dict[str, Optional[torch.Tensor]], y, routing: Dict
     _check(lib().moe_forward(ctypes.byref(cfg), _ptr(x), ctypes.byref(mw), _ptr(y), ctypes.byref(mr),
                              _ptr(stats), _ptr(workspace), workspace.numel(), _stream()),
            "moe_forward")
+
+
+NOALLOC_WORKSPACE_BYTES = 128 << 20   # moe.h MOE_NOALLOC_WORKSPACE_BYTES
+
+
+def forward_noalloc(cfg, x, weights: Dict[str, Optional[torch.Tensor]], y,
+                    routing: Dict[str, torch.Tensor], stats):
+    """moe_forward_noalloc: the forward with the library's static per-GPU
+    workspace (no workspace argument; layers whose workspace exceeds
+    NOALLOC_WORKSPACE_BYTES are refused with MOE_ERR_WORKSPACE)."""
+    T, d, F, E, k, S, act, _ = _sizes(cfg)
+    _need(x, "x", (T, d), act)
+    _need(y, "y", (T, d), act)
+    W, R = weights, routing
+    _need_weights(cfg, W)
+    _need_routing(cfg, R)
+    _need_stats(stats)
+    mw = MoeWeights(*[_ptr(W.get(n)) for n, _ in MoeWeights._fields_])
+    mr = MoeRouting(*[_ptr(R.get(n)) for n, _ in MoeRouting._fields_])
+    _check(lib().moe_forward_noalloc(ctypes.byref(cfg), _ptr(x), ctypes.byref(mw), _ptr(y),
+                                     ctypes.byref(mr), _ptr(stats), _stream()),
+           "moe_forward_noalloc")
 
 
 def update_selection_bias(cfg, stats, e_bias, gamma):

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "moe_internal.h"
 
@@ -141,6 +142,35 @@ static int64_t capacity_exact(const moe_config& c) {
 }
 
 static int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// Workspace of moe_forward_noalloc: static device memory, one copy per GPU. In
+// host code `scratch` names a host-side stand-in, not the device address: the
+// address is resolved per device with hipGetSymbolAddress and only that
+// pointer is passed to kernels.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_WORKSPACE_BYTES];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mutex;
+static void* g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device (resolved once per device).
+static int scratch_of_current_device(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+  if (stream) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return MOE_ERR_HIP;
+    if (sdev != dev) return MOE_ERR_INVALID_ARG;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
 
 // Layers the training forward and the backward run: bf16 activations (GELU,
 // ReLU or SwiGLU experts), and transposed row buffers short enough for the
@@ -390,6 +420,19 @@ int moe_forward_profiled(const moe_config* cfg, const void* x, const moe_weights
   e = launch_combine(*cfg, y_perm, r->expert_offsets, r->assign_row, r->topk_gate, y, s);
   if (e != hipSuccess || mark(MOE_EV_END) != hipSuccess) return MOE_ERR_HIP;
   return MOE_OK;
+}
+
+int moe_forward_noalloc(const moe_config* cfg, const void* x, const moe_weights* w, void* y,
+                        const moe_routing* r, moe_stats* stats, void* stream) {
+  const int v = validate(cfg);
+  if (v != MOE_OK) return v;
+  const size_t need = workspace_layout(*cfg).total;
+  if (need > MOE_NOALLOC_WORKSPACE_BYTES) return MOE_ERR_WORKSPACE;
+  if (cfg->tokens == 0) return MOE_OK;
+  void* ws = nullptr;
+  const int st = scratch_of_current_device((hipStream_t)stream, &ws);
+  if (st != MOE_OK) return st;
+  return moe_forward_profiled(cfg, x, w, y, r, stats, ws, need, stream, nullptr);
 }
 
 int moe_update_selection_bias(const moe_config* cfg, const moe_stats* stats, float* e_bias,
