@@ -938,17 +938,23 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(
 // 128 bytes with 16-byte chunk c of row r at c ^ ((r >> 1) & 7), conflict-free
 // for the fragment reads. Within a K step, sub-step s of lane half h multiplies
 // K elements 32 h + 8 s .. + 7, the same order on both operands.
+// Groups of up to 1536 rows take this kernel (measured on one MI355X: the
+// DeepSeek-V3-shaped layer's routed experts of 0-527 rows, and the Mixtral-
+// shaped layer's experts of about 1024 rows, four parts each, where it beats
+// the 256 x 256 tiles); groups of 2048 rows or more (the DeepSpeed-GPT shape,
+// the 4096-row shared expert) are faster on the tiled kernels.
 // The parts of one slab are consecutive work items and a group's slabs are
 // consecutive, and each XCD runs a contiguous range of items, so the slabs of a
 // group run side by side on one XCD: its token rows are fetched into that
 // XCD's L2 once, and the parts of a group with more than 256 rows (equal in
 // size, so they run at the same pace) read the same weight lines at about the
 // same time, the second reader finding them in L2.
-// Rows per part are rounded up to 64, 128, 192 or 256 (template MF = 2, 4, 6,
-// 8 fragments of 32 rows); rows past the part's end repeat its last row and are
-// not stored.
+// Rows per part are rounded up to a multiple of 32 (template MF = 1 .. 8
+// fragments of 32 rows) on packed weights, to 64, 128, 192 or 256 (MF = 2, 4,
+// 6, 8) on the standard layout; rows past the part's end repeat its last row
+// and are not stored.
 constexpr int kStreamRows = 256;   // rows per part
-constexpr int kStreamMaxRows = 512;   // groups with more rows use the tiled kernels
+constexpr int kStreamMaxRows = 1536;  // groups with more rows use the tiled kernels
 constexpr int kStreamLds = 10240;     // u32x4 (160 KB)
 // Work items of the streaming GEMM: group g with rows in (0, max_rows]
 // contributes ns slabs x ceil(rows / 256) parts. Lane l of every wave holds
@@ -1067,6 +1073,59 @@ __device__ __forceinline__ void stream_epilogue(const f32x16 (&acc)[MF][2], cons
         *reinterpret_cast<uint2*>(crow + c) = u;
       }
     }
+  }
+}
+
+// The same epilogue through LDS: the block's output tile (32 MF rows x 256
+// columns, SwiGLU 128) is staged in LDS (rows padded by 16 bytes so that the
+// 32 rows of one store land in different banks) and written as whole row
+// segments, 16 bytes per lane. Starts with a barrier: every wave must be done
+// reading the token-row stages it overwrites.
+template <int EPI, bool HAS_BIAS, int MF>
+__device__ __forceinline__ void stream_epilogue_lds(const f32x16 (&acc)[MF][2], u32x4* __restrict__ smem,
+                                                    const float* __restrict__ bg, int row0, int mrows,
+                                                    int n0, bf16* __restrict__ C, int N) {
+  constexpr bool GATED = EPI == EPI_SWIGLU;
+  constexpr int BNO = GATED ? 128 : 256;       // output columns of the tile
+  constexpr int RB = BNO * 2 + 16;             // bytes per staged row
+  static_assert(32 * MF * RB <= kStreamLds * 16, "output tile fits in LDS");
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int fr = lane & 31, fh = lane >> 5;
+  char* st = reinterpret_cast<char*>(smem);
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < MF; ++i) {
+    const int m = 32 * i + fr;
+#pragma unroll
+    for (int j = 0; j < (GATED ? 1 : 2); ++j) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int cl = (GATED ? 32 * wave : 64 * wave + 32 * j) + 8 * q + 4 * fh;   // column in tile
+        const float4 bq = HAS_BIAS ? *reinterpret_cast<const float4*>(bg + n0 + cl)
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float bb[4] = {bq.x, bq.y, bq.z, bq.w};
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          v[e] = epilogue_bf16<EPI>(acc[i][j][4 * q + e] + bb[e], GATED ? acc[i][1][4 * q + e] : 0.f);
+        uint2 u;
+        u.x = pack_bf16x2(v[0], v[1]);
+        u.y = pack_bf16x2(v[2], v[3]);
+        *reinterpret_cast<uint2*>(st + m * RB + cl * 2) = u;
+      }
+    }
+  }
+  __syncthreads();
+  constexpr int CPR = BNO / 8;                 // 16-byte chunks per row
+#pragma unroll
+  for (int p = 0; p < 32 * MF * CPR / 256; ++p) {
+    const int idx = p * 256 + tid;
+    const int m = idx / CPR, c = idx % CPR;
+    if (m < mrows)
+      *reinterpret_cast<u32x4*>(C + (int64_t)(row0 + m) * N + n0 + c * 8) =
+          *reinterpret_cast<const u32x4*>(st + m * RB + c * 16);
   }
 }
 
@@ -1394,7 +1453,7 @@ __device__ __forceinline__ void stream_tile_packed(u32x4* __restrict__ smem,
 #undef MOE_LW
 #undef MOE_LDS
 #undef MOE_SB
-  stream_epilogue<EPI, HAS_BIAS, MF>(acc, bg, row0, mrows, n0, C, N);
+  stream_epilogue_lds<EPI, HAS_BIAS, MF>(acc, smem, bg, row0, mrows, n0, C, N);
 }
 
 // One launch over every group with rows in (0, max_rows]: work items (group,
@@ -1433,14 +1492,20 @@ __global__ __launch_bounds__(256, 1) void gemm_stream_kernel(
   if (Wp) {
     // packed weights of group g: (SwiGLU: 2 x) N x K elements per group
     const bf16* Wpg = Wp + (int64_t)g * (GATED ? 2 : 1) * N * K;
-    if (mf <= 2)
-      stream_tile_packed<EPI, HAS_BIAS, 2>(smem, A, a_bytes, arows, Wpg, slab, bg, row0, nrows, n0, C, N, K);
-    else if (mf <= 4)
-      stream_tile_packed<EPI, HAS_BIAS, 4>(smem, A, a_bytes, arows, Wpg, slab, bg, row0, nrows, n0, C, N, K);
-    else if (mf <= 6)
-      stream_tile_packed<EPI, HAS_BIAS, 6>(smem, A, a_bytes, arows, Wpg, slab, bg, row0, nrows, n0, C, N, K);
-    else
-      stream_tile_packed<EPI, HAS_BIAS, 8>(smem, A, a_bytes, arows, Wpg, slab, bg, row0, nrows, n0, C, N, K);
+    // rows rounded up to the next multiple of 32 (MF = 1 .. 8 fragments)
+#define MOE_PT(M)                                                                     \
+  stream_tile_packed<EPI, HAS_BIAS, M>(smem, A, a_bytes, arows, Wpg, slab, bg, row0, nrows, n0, C, N, K)
+    switch (mf) {
+      case 1: MOE_PT(1); break;
+      case 2: MOE_PT(2); break;
+      case 3: MOE_PT(3); break;
+      case 4: MOE_PT(4); break;
+      case 5: MOE_PT(5); break;
+      case 6: MOE_PT(6); break;
+      case 7: MOE_PT(7); break;
+      default: MOE_PT(8); break;
+    }
+#undef MOE_PT
     return;
   }
   if (mf <= 2)
