@@ -313,6 +313,8 @@ def main():
                     help="only the headline workload (no other workloads, training or expert choice)")
     ap.add_argument("--no-expert-choice", action="store_true")
     ap.add_argument("--no-train", action="store_true")
+    ap.add_argument("--no-standard-layout", action="store_true",
+                    help="skip the second measurement with the weights in the standard layout only")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB float32 copy kernel (torch.neg) three times, "
                          "so that hardware byte counters can be scaled by a kernel of known traffic")
@@ -371,7 +373,7 @@ def main():
         result["cpu_baseline"] = cpu_baseline(w, sets[0])
     sets = ws = None
     release(torch)
-    if head["weights"] == "packed":
+    if head["weights"] == "packed" and not args.no_standard_layout:
         # the same layer with the weights in the standard [out, in] layout only
         r, _, sx, wx = measure_forward(A, torch, w, args.sets, args.steps, args.warmup, packed=False)
         result["standard_layout"] = {k2: r[k2] for k2 in ("ms_per_step", "tokens_per_s", "stages_ms",
