@@ -1611,9 +1611,13 @@ static hipError_t gemm_launch(const moe_config& c, const ET* A, const void* W, c
     // the 128 x 128 kernel is persistent: at most two blocks per CU, each
     // looping over the tiles (grid bounds below; surplus blocks exit)
     const int slots = gemm_slots();
-    // 256 x 256 tiles pay off where the K loop is long or there is no
-    // activation: one block per CU leaves the epilogue's VALU work exposed,
-    // which two 128 x 128 blocks per CU hide behind each other's MFMAs.
+    // 256 x 256 tiles pay off for the GEMMs without an activation whose
+    // output is at most 4096 wide (the DeepSpeed-GPT shape's GEMM 2: 256 tiles,
+    // one per CU): with an activation, one block per CU leaves the epilogue's
+    // VALU work exposed, which two 128 x 128 blocks per CU hide behind each
+    // other's MFMAs; and at N = 7168 or a long K (the DeepSeek-V3 shared expert)
+    // the 128 x 128 kernel's two K steps in flight and finer tail were faster
+    // (one MI355X: 2.60 -> 2.56 ms GEMM 1, 1.53 -> 1.50 ms GEMM 2 stages).
     // gathered A rows (arows) are addressed with 32-bit offsets from the start
     // of x, which the 256 x 256 kernel's buffer loads need below 4 GiB
     const int64_t a_bytes = arows ? c.tokens * (int64_t)K * 2 : 0;
@@ -1636,7 +1640,7 @@ static hipError_t gemm_launch(const moe_config& c, const ET* A, const void* W, c
       }
     }
     // (the backward epilogues EPI_DGELU / EPI_DRELU exist in the 128 x 128 kernel only)
-    const bool big = rows >= kGemmBigBM && (EPI == EPI_NONE || K >= 2048) &&
+    const bool big = rows >= kGemmBigBM && EPI == EPI_NONE && N <= 4096 &&
                      EPI != EPI_DGELU && EPI != EPI_DRELU && a_bytes < ((int64_t)1 << 32);
     if (big) {
       // full 256-row tiles of each group, then the rows left over (< 256 per

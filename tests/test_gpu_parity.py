@@ -73,6 +73,21 @@ CASES = {
     "top6_shared_drops": W["deepseek_v3"].scaled(tokens=450, d_model=256, d_ff=256,
                                                  num_experts=16, top_k=6, drop_tokens=True,
                                                  capacity_factor=0.1, min_capacity=4),
+    # groups above the weight-streaming kernel's 1536 rows run on the tiled
+    # kernels: the persistent 128 x 128 kernel with the GELU / ReLU / SwiGLU
+    # epilogue for GEMM 1, the 256 x 256 kernel for GEMM 2's full 256-row tiles
+    # (N <= 4096) and the 128 x 128 kernel for each group's rows left over
+    "tiled_gelu": W["deepspeed_gpt_moe"].scaled(tokens=4001, d_model=512, d_ff=768, num_experts=2,
+                                               top_k=1, drop_tokens=False),
+    "tiled_relu": W["deepspeed_gpt_moe"].scaled(tokens=3333, d_model=256, d_ff=512, num_experts=2,
+                                               top_k=1, activation="relu", drop_tokens=False),
+    # a 1700-row shared expert on the tiled kernels next to 16 routed experts
+    # (about 210 rows each) on the streaming kernel, in the same launches
+    "tiled_swiglu_shared": W["deepseek_v3"].scaled(tokens=1700, d_model=512, d_ff=256,
+                                                   num_experts=16, top_k=2),
+    # N = d above 4096: GEMM 2 on the 128 x 128 kernel (no 256 x 256 tiles)
+    "tiled_wide_down": W["mixtral_8x7b"].scaled(tokens=1800, d_model=4352, d_ff=256, num_experts=1,
+                                                top_k=1),
 }
 
 
