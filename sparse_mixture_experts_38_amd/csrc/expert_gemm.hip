@@ -1631,8 +1631,13 @@ static hipError_t gemm_launch(const moe_config& c, const ET* A, const void* W, c
     if constexpr (kStreamEpi) {
       if (skip > 0) {
         constexpr int BNO = EPI == EPI_SWIGLU ? 128 : 256;
-        // items: at most (ceil(rows / 256) + G) parts x N / BNO slabs
-        const int64_t items = ((rows + kStreamRows - 1) / kStreamRows + G) * (N / BNO);
+        // items: parts x N / BNO slabs, where the parts, ceil(r_g / 256) summed
+        // over the groups with r_g in (0, skip] rows, are at most
+        // (rows + 255 G) / 256 and at most ceil(skip / 256) G
+        const int64_t parts = std::min<int64_t>((rows + (int64_t)(kStreamRows - 1) * G) / kStreamRows,
+                                                (int64_t)G * ((skip + kStreamRows - 1) / kStreamRows));
+        const int64_t items = parts * (N / BNO);
+        if (items > 0)
         hipLaunchKernelGGL((gemm_stream_kernel<EPI, HB>), dim3((unsigned)items), dim3(256), 0, s, A,
                            (const bf16*)W, (const bf16*)W3, bias, (const bf16*)Ws, (const bf16*)Ws3,
                            bias_s, E, G, offsets, (int)rows, C, N, K, arows, (uint32_t)a_span, skip,
