@@ -679,40 +679,58 @@ def expert_choice_capacity(tokens: int, num_experts: int, top_k: int, capacity_f
     return int(min(c, tokens))
 
 
-def expert_choice_route(logits, C: int) -> Dict[str, np.ndarray]:
+def expert_choice_route(logits, C: int, score_fn: str = "softmax") -> Dict[str, np.ndarray]:
     """Per expert, the C tokens with the largest float32 logit (ties: lower token
-    first), listed in ascending token order; their gates p[t, e] (softmax over
-    experts, float64 from the float32 logits); the row of (t, e) or -1.
+    first), listed in ascending token order; their gates; the row of (t, e) or -1.
+
+    Gates: softmax router, p[t, e] (softmax over experts); sigmoid router, the
+    sigmoid score s[t, e] itself. READING: the pages weight an expert's output
+    by the router's score for (t, e) and give no renormalisation for expert
+    choice (a token has no fixed number of picks), so the sigmoid gate is the
+    raw score. Both scores increase with the logit, so an expert's C best tokens
+    by score are its C best by logit; the logit is the key (float32 rounding of
+    the score could make distinct logits equal). affinity: the per-token
+    distribution over experts that P_i averages (p, or s / sum_e s as in the
+    token-choice statistics).
 
     Rows: expert e's chosen tokens occupy rows e C .. e C + C - 1.
     """
     h32 = np.asarray(logits, F32)
     T, E = h32.shape
-    p, lse = softmax_scores(h32)
+    if score_fn == "softmax":
+        scores, lse = softmax_scores(h32)
+        affinity = scores
+    elif score_fn == "sigmoid":
+        scores = sigmoid_scores(h32)
+        lse = logsumexp(h32)
+        affinity = scores / scores.sum(axis=1, keepdims=True)
+    else:
+        raise ValueError(score_fn)
     tokens = np.empty((E, C), np.int64)
     for e in range(E):
         order = np.argsort(-h32[:, e], kind="stable")   # descending, lower token first on ties
         tokens[e] = np.sort(order[:C])
-    gates = np.take_along_axis(p.T, tokens, axis=1)       # [E, C]
+    gates = np.take_along_axis(scores.T, tokens, axis=1)  # [E, C]
     row = np.full((T, E), -1, np.int64)
     for e in range(E):
         row[tokens[e], e] = e * C + np.arange(C)
     picks = (row >= 0).sum(axis=1)
-    return dict(tokens=tokens, gates=gates, row=row, p=p, lse=lse, picks=picks)
+    return dict(tokens=tokens, gates=gates, row=row, scores=scores, affinity=affinity, lse=lse,
+                picks=picks)
 
 
 def expert_choice_forward(x, params, w, logits=None) -> Dict[str, object]:
     """The layer with expert-choice routing: y[t] = sum over the experts e that
-    picked t of p[t, e] E_e(x_t) (+ shared expert). Statistics: every expert takes
-    C tokens; "unpicked" counts the tokens no expert chose; P_i and the z-loss as
-    for token choice."""
+    picked t of gate[t, e] E_e(x_t) (+ shared expert). Statistics: every expert
+    takes C tokens; "unpicked" counts the tokens no expert chose; P_i (mean
+    affinity) and the z-loss as for token choice."""
     x = np.asarray(x, F64)
     T, d = x.shape
     E = w.num_experts
     C = expert_choice_capacity(T, E, w.top_k, w.capacity_factor, w.min_capacity, w.drop_tokens)
     if logits is None:
         logits = router_logits(x, params["w_gate"], params.get("b_gate"))
-    r = expert_choice_route(logits, C)
+    r = expert_choice_route(logits, C, w.score_fn)
     Y = np.zeros((E * C, d), F64)
     for e in range(E):
         Y[e * C:(e + 1) * C] = expert_ffn(x[r["tokens"][e]], params["w1"][e], _opt(params.get("b1"), e),
@@ -724,7 +742,7 @@ def expert_choice_forward(x, params, w, logits=None) -> Dict[str, object]:
     if w.num_shared_experts:
         y += expert_ffn(x, params["ws1"][0], _opt(params.get("bs1"), 0), params["ws2"][0],
                         _opt(params.get("bs2"), 0), w.activation, _opt(params.get("ws3"), 0))
-    stats = dict(capacity=C, P=r["p"].mean(axis=0), z_loss=float(np.mean(r["lse"] ** 2)),
+    stats = dict(capacity=C, P=r["affinity"].mean(axis=0), z_loss=float(np.mean(r["lse"] ** 2)),
                  unpicked=int(np.count_nonzero(r["picks"] == 0)), max_picks=int(r["picks"].max()))
     return dict(logits=np.asarray(logits, F32), y=y, Y=Y, stats=stats, C=C, **r)
 

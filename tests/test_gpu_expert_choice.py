@@ -62,7 +62,7 @@ def check_ec(w, inp, out, sample=None):
     ref_logits = O.router_logits(x, P["w_gate"], P.get("b_gate")).astype(np.float64)
     gl = out["logits"].numpy()
     assert np.abs(gl - ref_logits).max() <= 2e-5 * (np.abs(ref_logits).max() + 1.0), "logits"
-    r = O.expert_choice_route(gl, C)
+    r = O.expert_choice_route(gl, C, w.score_fn)
     assert out["tokens"].shape == (E, C)
     assert np.array_equal(out["tokens"].numpy(), r["tokens"]), "chosen tokens"
     assert np.array_equal(out["token_row"].numpy(), r["row"]), "token_row"
@@ -71,9 +71,9 @@ def check_ec(w, inp, out, sample=None):
     assert st["capacity"] == C and st["kept"] == E * C
     assert np.all(st["counts_pre"] == C) and np.all(st["counts_kept"] == C)
     assert st["dropped"] == int(np.count_nonzero(r["picks"] == 0)), "unpicked tokens"
-    assert np.allclose(st["prob_mean"], r["p"].mean(axis=0), rtol=1e-4, atol=1e-7), "P_i"
+    assert np.allclose(st["prob_mean"], r["affinity"].mean(axis=0), rtol=1e-4, atol=1e-7), "P_i"
     assert abs(st["z_loss"] - np.mean(r["lse"] ** 2)) <= 1e-4 * max(1.0, abs(np.mean(r["lse"] ** 2)))
-    assert abs(st["l_aux"] - r["p"].mean(axis=0).sum()) <= 1e-4
+    assert abs(st["l_aux"] - r["affinity"].mean(axis=0).sum()) <= 1e-4
     if sample is None:
         ref = O.expert_choice_forward(x, P, w, logits=gl)
         err = rel_err(out["y"].float().numpy(), ref["y"])

@@ -2,7 +2,9 @@
 (torch.topk over the transposed scores), brute force on tied keys, the
 balance guarantee, a torch float64 formulation of the combine, and the closed
 case C = T (every expert takes every token: the soft mixture, which token
-choice with k = E also gives)."""
+choice with k = E also gives). The sigmoid router's branch: hand cases with
+exact sigmoid values (1/2, 3/4), brute force over token subsets, the identity
+sum_i P_i = 1, and a torch float64 formulation of the layer."""
 import math
 
 import numpy as np
@@ -141,3 +143,84 @@ def test_unpicked_token_gets_only_the_shared_expert():
     assert ec["picks"][7] == 0
     shared = O.expert_ffn(x[7:8], p["ws1"][0], None, p["ws2"][0], None, "relu")
     np.testing.assert_allclose(ec["y"][7], shared[0], rtol=1e-12, atol=1e-12)
+
+
+# --- the sigmoid router (DeepSeek-V3 scores) under expert choice -------------
+
+_LN3 = math.log(3.0)
+
+
+def test_sigmoid_hand_case():
+    # sigmoid(0) = 1/2, sigmoid(ln 3) = 3/4; ties at logit 0 go to the lower token
+    h = np.array([[0.0, _LN3], [_LN3, 0.0], [-_LN3, 0.0], [0.0, -_LN3]], np.float32)
+    r = O.expert_choice_route(h, 2, "sigmoid")
+    assert r["tokens"].tolist() == [[0, 1], [0, 1]]
+    np.testing.assert_allclose(r["gates"], [[0.5, 0.75], [0.75, 0.5]], rtol=1e-6)
+    assert r["row"].tolist() == [[0, 2], [1, 3], [-1, -1], [-1, -1]]
+
+
+def test_sigmoid_affinity_hand_case():
+    # s = [[3/4, 3/4], [1/2, 1/4]] -> s / sum s = [[1/2, 1/2], [2/3, 1/3]] -> P = [7/12, 5/12]
+    h = np.array([[_LN3, _LN3], [0.0, -_LN3]], np.float32)
+    r = O.expert_choice_route(h, 1, "sigmoid")
+    np.testing.assert_allclose(r["affinity"].mean(axis=0), [7 / 12, 5 / 12], rtol=1e-6)
+    # the z-loss argument is the logsumexp of the logits, whatever the score function
+    np.testing.assert_allclose(r["lse"], [_LN3 + math.log(2.0), math.log(1.0 + 1.0 / 3.0)],
+                               rtol=1e-6)
+
+
+def test_sigmoid_selection_maximises_the_summed_score_brute_force():
+    import itertools
+    rng = np.random.default_rng(7)
+    T, E, C = 9, 3, 4
+    h = rng.normal(0, 2.0, size=(T, E)).astype(np.float32)
+    r = O.expert_choice_route(h, C, "sigmoid")
+    for e in range(E):
+        sig = [1.0 / (1.0 + math.exp(-float(h[t, e]))) for t in range(T)]
+        best = max(itertools.combinations(range(T), C), key=lambda c: sum(sig[t] for t in c))
+        assert list(r["tokens"][e]) == list(best)
+        np.testing.assert_allclose(r["gates"][e], [sig[t] for t in best], rtol=1e-12)
+
+
+def test_sigmoid_l_aux_is_one_for_any_logits():
+    # every f_i = 1/E under expert choice, and the affinities of a token sum to 1,
+    # so E sum_i f_i P_i = sum_i P_i = 1
+    rng = np.random.default_rng(8)
+    h = rng.normal(0, 3.0, size=(50, 7)).astype(np.float32)
+    r = O.expert_choice_route(h, 10, "sigmoid")
+    assert abs(r["affinity"].mean(axis=0).sum() - 1.0) < 1e-12
+    # a softmax router gives the same identity with p
+    r = O.expert_choice_route(h, 10, "softmax")
+    assert abs(r["affinity"].mean(axis=0).sum() - 1.0) < 1e-12
+
+
+def _torch_sigmoid_expert_choice(x, p, w, C):
+    """torch float64: logits, per expert the C largest, outputs weighted by
+    torch.sigmoid of the float32 logit and added back with index_add (no oracle
+    code)."""
+    X = torch.from_numpy(x)
+    logits = (X @ torch.from_numpy(p["w_gate"]).T).float()
+    out = torch.zeros_like(X)
+    for e in range(w.num_experts):
+        idx = torch.topk(logits.T[e], k=C).indices
+        z = X[idx] @ torch.from_numpy(p["w1"][e]).T
+        if p["b1"] is not None:
+            z = z + torch.from_numpy(p["b1"][e])
+        ye = torch.nn.functional.gelu(z) @ torch.from_numpy(p["w2"][e]).T
+        if p["b2"] is not None:
+            ye = ye + torch.from_numpy(p["b2"][e])
+        out.index_add_(0, idx, torch.sigmoid(logits[idx, e:e + 1].double()) * ye)
+    return out.numpy(), logits.numpy()
+
+
+def test_sigmoid_layer_matches_a_torch_formulation():
+    w = Workload("ec_sig", tokens=40, d_model=8, d_ff=16, num_experts=4, top_k=2,
+                 activation="gelu", has_bias=True, capacity_factor=1.0, drop_tokens=True,
+                 min_capacity=1, score_fn="sigmoid", act_dtype="f32")
+    x, p = _params(w, 9)
+    C = O.expert_choice_capacity(w.tokens, 4, 2, 1.0, 1, True)
+    assert C == 20
+    ref, logits = _torch_sigmoid_expert_choice(x, p, w, C)
+    got = O.expert_choice_forward(x, p, w, logits=logits)
+    np.testing.assert_allclose(got["y"], ref, rtol=1e-12, atol=1e-12)
+    assert abs(got["stats"]["P"].sum() - 1.0) < 1e-12
