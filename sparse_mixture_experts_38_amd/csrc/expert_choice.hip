@@ -2,9 +2,11 @@
 // transposed [E, T] router scores ("MoE Training: Mixture of Experts",
 // "2. Routing Mechanisms", expert choice routing: perfect load balance by
 // construction; "MoE From Scratch to DeepSeek V3": tokens may be served by
-// several experts or none). Score = the float32 router logit; equal scores go to
-// the lower token; an expert's output for a token is weighted by the softmax
-// probability p[t, e] over experts; expert e's chosen tokens, in ascending
+// several experts or none). Key = the float32 router logit (softmax and sigmoid
+// scores both increase with it); equal keys go to the lower token; an expert's
+// output for a token is weighted by the router score g[t, e]: the softmax
+// probability p[t, e] over experts, or the sigmoid score itself (DeepSeek-V3
+// scores, no renormalisation over a token's picks); expert e's chosen tokens, in ascending
 // token order, fill rows e C .. e C + C - 1, and a shared expert takes rows
 // E C .. E C + T - 1. The grouped GEMMs are those of the token-choice path.
 #include <string.h>
@@ -19,12 +21,14 @@ __device__ __forceinline__ uint32_t score_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Per token: lse[t] = logsumexp of its logits; the (t, e) -> row map cleared to
-// -1; with a shared expert, row E C + t takes token t. Each block writes the
-// float64 sum of its tokens' lse^2 to zpart[block] (z-loss).
+// Per token: norm[t] = logsumexp of its logits (softmax), or the float32 sum
+// over experts, in ascending order, of its sigmoid scores (sigmoid); the
+// (t, e) -> row map cleared to -1; with a shared expert, row E C + t takes
+// token t. Each block writes the float64 sum of its tokens' lse^2 to
+// zpart[block] (z-loss, for both score functions).
 __global__ __launch_bounds__(256) void ec_lse_kernel(const float* __restrict__ logits, int64_t T,
-                                                     int E, int64_t C, int S,
-                                                     float* __restrict__ lse,
+                                                     int E, int64_t C, int S, int sigmoid,
+                                                     float* __restrict__ norm,
                                                      int32_t* __restrict__ token_row,
                                                      int32_t* __restrict__ rows,
                                                      double* __restrict__ zpart) {
@@ -38,7 +42,10 @@ __global__ __launch_bounds__(256) void ec_lse_kernel(const float* __restrict__ l
     float s = 0.f;
     for (int e = 0; e < E; ++e) s += expf(h[e] - m);
     const float l = m + logf(s);
-    lse[t] = l;
+    float ss = 0.f;
+    if (sigmoid)
+      for (int e = 0; e < E; ++e) ss += 1.0f / (1.0f + expf(-h[e]));
+    norm[t] = sigmoid ? ss : l;
     z = (double)l * (double)l;
     for (int e = 0; e < E; ++e) token_row[t * E + e] = -1;
     if (S) rows[(int64_t)E * C + t] = (int32_t)t;
@@ -86,16 +93,18 @@ constexpr int kEcLdsKeys = 16384;   // keys and lse of one expert kept in LDS (1
 // One block per expert e: the C tokens with the largest key(logits[t][e]), ties
 // to the lower token. The expert's keys are staged in LDS when T <= 16384 (else
 // read from L2). An exact radix select over four 8-bit digits finds the C-th
-// largest key K and how many tokens equal to K to take. Then each thread takes a
-// contiguous range of tokens (lse staged in LDS with the keys): two block scans (of its count of keys equal to K,
-// then of its count of taken tokens) place its chosen tokens in ascending order:
-// tokens[e][i] = t, gates[e][i] = p[t][e], token_row[t][e] = e C + i,
-// rows[e C + i] = t. It also writes P_e (mean of p[t][e], float64 tree) and the
-// balance counts of expert e into stats.
+// largest key K and how many tokens equal to K to take. Then each thread takes
+// a contiguous range of tokens (norm staged in
+// LDS with the keys): two block scans (of its count of keys equal to K, then of
+// its count of taken tokens) place its chosen tokens in ascending order:
+// tokens[e][i] = t, gates[e][i] = g[t][e], token_row[t][e] = e C + i,
+// rows[e C + i] = t. It also writes P_e (mean over all tokens of p[t][e], or of
+// s[t][e] / norm[t] for the sigmoid router; float64 tree) and the balance
+// counts of expert e into stats.
 constexpr int kEcSelectThreads = 1024;
 __global__ __launch_bounds__(kEcSelectThreads) void ec_select_kernel(
     const float* __restrict__ logits, const float* __restrict__ lse, int64_t T, int E, int64_t C,
-    int32_t* __restrict__ tokens, float* __restrict__ gates, int32_t* __restrict__ token_row,
+    int sigmoid, int32_t* __restrict__ tokens, float* __restrict__ gates, int32_t* __restrict__ token_row,
     int32_t* __restrict__ rows, moe_stats* __restrict__ stats) {
   __shared__ uint32_t keys[kEcLdsKeys];
   __shared__ float lse_s[kEcLdsKeys];
@@ -179,8 +188,15 @@ __global__ __launch_bounds__(kEcSelectThreads) void ec_select_kernel(
   for (int64_t t = lo; t < hi; ++t) {
     const uint32_t u = key_at(t);
     const float h = key_score(u);
-    const float p = expf(h - lse_at(t));
-    psum += (double)p;
+    float p, a;
+    if (sigmoid) {
+      p = 1.0f / (1.0f + expf(-h));
+      a = p / lse_at(t);
+    } else {
+      p = expf(h - lse_at(t));
+      a = p;
+    }
+    psum += (double)a;
     bool take = u > prefix;
     if (u == prefix) {
       take = eq_seen < eq_take;
@@ -373,10 +389,11 @@ hipError_t launch_expert_choice_forward(const moe_config& c, const EcLayout& L, 
   if (e != hipSuccess) return e;
   const unsigned lb = (unsigned)((T + 255) / 256);
   double* zpart = (double*)(ws + L.zpart);
-  hipLaunchKernelGGL(ec_lse_kernel, dim3(lb), dim3(256), 0, s, (const float*)lg, T, E, C, S, lse,
-                     r.token_row, rows, zpart);
+  const int sig = c.score_fn == MOE_SCORE_SIGMOID ? 1 : 0;
+  hipLaunchKernelGGL(ec_lse_kernel, dim3(lb), dim3(256), 0, s, (const float*)lg, T, E, C, S, sig,
+                     lse, r.token_row, rows, zpart);
   hipLaunchKernelGGL(ec_select_kernel, dim3(E), dim3(kEcSelectThreads), 0, s, (const float*)lg,
-                     (const float*)lse, T, E, C, r.tokens, r.gates, r.token_row, rows, stats);
+                     (const float*)lse, T, E, C, sig, r.tokens, r.gates, r.token_row, rows, stats);
   hipLaunchKernelGGL(ec_finalize_kernel, dim3(1), dim3(256), 0, s, (const double*)zpart, (int)lb,
                      T, E, C, S, off, stats);
   e = hipGetLastError();

@@ -503,7 +503,6 @@ int moe_expert_choice_capacity(const moe_config* cfg, int64_t* capacity_out) {
 static int validate_ec(const moe_config* c) {
   const int v = validate(c);
   if (v != MOE_OK) return v;
-  if (c->score_fn != MOE_SCORE_SOFTMAX) return MOE_ERR_UNSUPPORTED;
   // expert rows E C + S T addressed with 32-bit row indices
   const int64_t C = expert_choice_capacity(*c, capacity_exact(*c));
   if ((int64_t)c->num_experts * C + (int64_t)c->num_shared_experts * c->tokens >=

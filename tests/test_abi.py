@@ -226,9 +226,11 @@ def test_expert_choice_entry_points_validate_before_any_launch(tmp_path):
     assert A.expert_choice_workspace_size(cfg) > 0
     assert lib.moe_forward_expert_choice(ctypes.byref(cfg), None, None, None, None, None, None, 0,
                                          None) == A.MOE_ERR_INVALID_ARG
+    # the sigmoid router is accepted: its null pointers are what is refused
     sig = _base(score_fn="sigmoid")
+    assert A.expert_choice_workspace_size(sig) > 0
     assert lib.moe_forward_expert_choice(ctypes.byref(sig), None, None, None, None, None, None, 0,
-                                         None) == A.MOE_ERR_UNSUPPORTED
+                                         None) == A.MOE_ERR_INVALID_ARG
     z = _base(tokens=0)
     assert lib.moe_forward_expert_choice(ctypes.byref(z), None, None, None, None, None, None, 0,
                                          None) == A.MOE_OK

@@ -37,6 +37,14 @@ CASES = {
                               capacity_factor=8.0),
     # more tokens than the selection keeps in LDS (16384): keys read from the logits
     "many_tokens": base.scaled(tokens=20000, d_model=256, d_ff=256, num_experts=4),
+    # the DeepSeek-V3 recipe's sigmoid router (selection bias unused by expert
+    # choice), SwiGLU experts and a shared expert
+    "sigmoid_shared": W["deepseek_v3"].scaled(tokens=1500, d_model=512, d_ff=256, num_experts=16,
+                                              top_k=2),
+    # sigmoid router over more tokens than fit in LDS
+    "sigmoid_many_tokens": W["deepseek_v3"].scaled(tokens=17000, d_model=256, d_ff=256,
+                                                   num_experts=8, top_k=1,
+                                                   num_shared_experts=0),
 }
 
 
