@@ -466,8 +466,9 @@ int moe_forward_expert_choice(const moe_config* cfg, const void* x, const moe_we
  * loss with a small coefficient; [P4] router z-loss). The top-k choices, the
  * capacity decisions and the counts f_i are piecewise constant and carry no
  * gradient; the sigmoid selection bias e_bias receives none.
- * This build runs the backward for act_dtype MOE_BF16 with GELU, ReLU or SwiGLU
- * experts (float32 layers return MOE_ERR_UNSUPPORTED).
+ * Both layer types run it, with GELU, ReLU or SwiGLU experts: bf16 layers on
+ * the MFMA GEMMs, float32 layers in float32 throughout (plain kernels, one
+ * output per thread).
  */
 
 /* Forward activations the backward reads (device buffers the caller owns). */
@@ -518,8 +519,9 @@ int moe_backward_workspace_size(const moe_config* cfg, size_t* bytes_out);
  * expert FFN ([P1] "Basic MoE Architecture"), the renormalised top-k gates and
  * the score function ([P1] "Basic MoE Architecture", [P4] V3 sigmoid routing),
  * L_aux ([P1] "3. Load Balancing") and the z-loss ([P4]), and the gate linear
- * layer. Expert GEMMs in bf16 with float32 accumulation; router math, weight and
- * bias gradients in float32. Deterministic (no floating-point atomics).
+ * layer. bf16 layers: expert GEMMs in bf16 with float32 accumulation; router
+ * math, weight and bias gradients in float32. float32 layers: float32 for every
+ * step. Deterministic (no floating-point atomics).
  *   x, w         the forward's inputs;  routing, stats, saved: the forward's outputs
  *   dy           [T, d] act_dtype
  *   grads        output buffers (moe_grads)

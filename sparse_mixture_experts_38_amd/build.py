@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 BUILD_DIR = os.path.join(PKG, "_build")
 
 SOURCES = ["moe_api.hip", "router.hip", "permute.hip", "expert_gemm.hip", "combine.hip",
-           "backward.hip", "expert_choice.hip", "routing_extra.hip"]
+           "backward.hip", "backward_f32.hip", "expert_choice.hip", "routing_extra.hip"]
 
 # Packed fp32 instructions are switched off for every device compilation.
 HIPCC_FLAGS = [

@@ -88,21 +88,23 @@ __global__ __launch_bounds__(256) void dswiglu_kernel(const bf16* __restrict__ d
 // (kept): dYp[r] = g[t, j] dy[t] (bf16) and dgate[t, j] = <dy[t], y_perm[r]>
 // (float32, lanes then a wave reduction); dropped choices get dgate = 0. With a
 // shared expert, its row expert_offsets[E] + t receives dy[t] (gate 1).
+// ET: the layer's activation type (bf16, or float for float32 layers).
+template <typename ET>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(
-    const bf16* __restrict__ dy, const bf16* __restrict__ y_perm, const float* __restrict__ gate,
+    const ET* __restrict__ dy, const ET* __restrict__ y_perm, const float* __restrict__ gate,
     const int32_t* __restrict__ assign_row, const int32_t* __restrict__ off, int64_t T, int d, int k,
-    int E, int S, int64_t rows_max, bf16* __restrict__ dyp, float* __restrict__ dgate) {
+    int E, int S, int64_t rows_max, ET* __restrict__ dyp, float* __restrict__ dgate) {
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (t >= T) return;
-  const bf16* dyt = dy + t * d;
+  const ET* dyt = dy + t * d;
   for (int j = 0; j < k; ++j) {
     const int r = assign_row[t * k + j];
     float dot = 0.f;
     if (r >= 0 && r < rows_max) {
       const float g = gate[t * k + j];
-      const bf16* yr = y_perm + (int64_t)r * d;
-      bf16* out = dyp + (int64_t)r * d;
+      const ET* yr = y_perm + (int64_t)r * d;
+      ET* out = dyp + (int64_t)r * d;
       for (int c = lane * 8; c < d; c += 512) {
         float a[8], b[8];
         load8(dyt + c, a);
@@ -122,9 +124,12 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
   if (S) {
     const int64_t r = (int64_t)clamp_off(off, E, rows_max) + t;
     if (r < rows_max) {
-      bf16* out = dyp + r * d;
-      for (int c = lane * 8; c < d; c += 512)
-        *reinterpret_cast<uint4*>(out + c) = *reinterpret_cast<const uint4*>(dyt + c);
+      ET* out = dyp + r * d;
+      for (int c = lane * 8; c < d; c += 512) {
+        float a[8];
+        load8(dyt + c, a);
+        store8(out + c, a);
+      }
     }
   }
 }
@@ -504,11 +509,11 @@ __global__ __launch_bounds__(256) void gate_bias_grad_kernel(const float* __rest
 // of its own): W_g rows in batches of 8 (rows past E reread row E - 1), and
 // row slots that are dropped or past k reread the token's first live row; all
 // of them are masked out of the sums, which keep the order above.
-template <typename WT, int KM>
+template <typename ET, typename WT, int KM>
 __global__ __launch_bounds__(256) void unpermute_dx_kernel(
-    const bf16* __restrict__ dxp, const int32_t* __restrict__ assign_row,
+    const ET* __restrict__ dxp, const int32_t* __restrict__ assign_row,
     const int32_t* __restrict__ off, const float* __restrict__ dlogits, const WT* __restrict__ wg,
-    int64_t T, int d, int k, int E, int S, int64_t rows_max, bf16* __restrict__ dx) {
+    int64_t T, int d, int k, int E, int S, int64_t rows_max, ET* __restrict__ dx) {
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (t >= T) return;
@@ -561,24 +566,81 @@ __global__ __launch_bounds__(256) void unpermute_dx_kernel(
   }
 }
 
-template <typename WT>
-static void launch_unpermute_dx(dim3 grid, hipStream_t s, const bf16* dxp, const int32_t* assign_row,
+template <typename ET, typename WT>
+static void launch_unpermute_dx(dim3 grid, hipStream_t s, const ET* dxp, const int32_t* assign_row,
                                 const int32_t* off, const float* dlogits, const WT* wg, int64_t T,
-                                int d, int k, int E, int S, int64_t rows_max, bf16* dx) {
+                                int d, int k, int E, int S, int64_t rows_max, ET* dx) {
   if (k <= 2)
-    hipLaunchKernelGGL((unpermute_dx_kernel<WT, 2>), grid, dim3(256), 0, s, dxp, assign_row, off,
-                       dlogits, wg, T, d, k, E, S, rows_max, dx);
+    hipLaunchKernelGGL((unpermute_dx_kernel<ET, WT, 2>), grid, dim3(256), 0, s, dxp, assign_row,
+                       off, dlogits, wg, T, d, k, E, S, rows_max, dx);
   else if (k <= 4)
-    hipLaunchKernelGGL((unpermute_dx_kernel<WT, 4>), grid, dim3(256), 0, s, dxp, assign_row, off,
-                       dlogits, wg, T, d, k, E, S, rows_max, dx);
+    hipLaunchKernelGGL((unpermute_dx_kernel<ET, WT, 4>), grid, dim3(256), 0, s, dxp, assign_row,
+                       off, dlogits, wg, T, d, k, E, S, rows_max, dx);
   else
-    hipLaunchKernelGGL((unpermute_dx_kernel<WT, MOE_MAX_TOP_K>), grid, dim3(256), 0, s, dxp,
+    hipLaunchKernelGGL((unpermute_dx_kernel<ET, WT, MOE_MAX_TOP_K>), grid, dim3(256), 0, s, dxp,
                        assign_row, off, dlogits, wg, T, d, k, E, S, rows_max, dx);
+}
+
+template <typename ET>
+static void combine_bwd_t(const moe_config& c, const void* dy, const void* y_perm,
+                          const moe_routing& r, void* dyp, float* dgate, hipStream_t s) {
+  const int64_t T = c.tokens;
+  hipLaunchKernelGGL(combine_bwd_kernel<ET>, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s,
+                     (const ET*)dy, (const ET*)y_perm, r.topk_gate, r.assign_row, r.expert_offsets,
+                     T, (int)c.d_model, c.top_k, c.num_experts, c.num_shared_experts, rows_max(c),
+                     (ET*)dyp, dgate);
+}
+
+hipError_t launch_combine_backward(const moe_config& c, const void* dy, const void* y_perm,
+                                   const moe_routing& r, void* dyp, float* dgate, hipStream_t s) {
+  if (c.act_dtype == MOE_BF16)
+    combine_bwd_t<bf16>(c, dy, y_perm, r, dyp, dgate, s);
+  else
+    combine_bwd_t<float>(c, dy, y_perm, r, dyp, dgate, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_backward(const moe_config& c, const moe_routing& r, const moe_stats* stats,
+                                  const float* dgate, float aux_coef, float z_coef, float* dlogits,
+                                  hipStream_t s) {
+  const int64_t T = c.tokens;
+  hipLaunchKernelGGL(router_bwd_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, r.logits,
+                     r.topk_idx, dgate, stats->counts_pre, T, c.num_experts, c.top_k,
+                     (int)(c.score_fn == MOE_SCORE_SIGMOID), aux_coef, z_coef, dlogits);
+  return hipGetLastError();
+}
+
+template <typename ET>
+static void dx_t(const moe_config& c, const float* dlogits, const void* dxp, const moe_routing& r,
+                 const moe_weights& w, const moe_grads& gr, hipStream_t s) {
+  const int64_t T = c.tokens;
+  const dim3 ug((unsigned)((T + 3) / 4));
+  const int d = (int)c.d_model, k = c.top_k, E = c.num_experts, S = c.num_shared_experts;
+  if (c.router_dtype == MOE_BF16)
+    launch_unpermute_dx<ET, bf16>(ug, s, (const ET*)dxp, r.assign_row, r.expert_offsets, dlogits,
+                                  (const bf16*)w.w_gate, T, d, k, E, S, rows_max(c), (ET*)gr.dx);
+  else
+    launch_unpermute_dx<ET, float>(ug, s, (const ET*)dxp, r.assign_row, r.expert_offsets, dlogits,
+                                   (const float*)w.w_gate, T, d, k, E, S, rows_max(c), (ET*)gr.dx);
+}
+
+hipError_t launch_router_bias_and_dx(const moe_config& c, const float* dlogits, const void* dxp,
+                                     const moe_routing& r, const moe_weights& w,
+                                     const moe_grads& gr, hipStream_t s) {
+  if (c.has_gate_bias)
+    hipLaunchKernelGGL(gate_bias_grad_kernel, dim3(c.num_experts), dim3(256), 0, s, dlogits,
+                       (int64_t)c.tokens, c.num_experts, gr.db_gate);
+  if (c.act_dtype == MOE_BF16)
+    dx_t<bf16>(c, dlogits, dxp, r, w, gr, s);
+  else
+    dx_t<float>(c, dlogits, dxp, r, w, gr, s);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ launchers
 hipError_t launch_act_rows(const moe_config& c, const void* z, const int32_t* off, void* h,
                            hipStream_t s) {
+  if (c.act_dtype != MOE_BF16) return launch_act_rows_f32(c, z, off, h, s);
   const int G = c.num_experts + c.num_shared_experts;
   const int64_t n8 = rows_max(c) * c.d_ff / 8;
   const bf16* u = c.activation == MOE_ACT_SWIGLU ? (const bf16*)z + rows_max(c) * c.d_ff : nullptr;
@@ -612,15 +674,12 @@ hipError_t launch_backward_misc(const moe_config& c, const BwdLayout& B, const v
   float* dlogits = (float*)(ws + B.dlogits);
   int32_t* po = (int32_t*)(ws + B.po);
   int32_t* so = po + (G + 1);
-  const unsigned tb = (unsigned)((T + 3) / 4);
   if (phase == 0) {
     // combine and router backward, weight transposes
-    hipLaunchKernelGGL(combine_bwd_kernel, dim3(tb), dim3(256), 0, s, (const bf16*)dy,
-                       (const bf16*)sv.y_perm, r.topk_gate, r.assign_row, r.expert_offsets, T, d, k,
-                       E, S, rmax, dyp, dgate);
-    hipLaunchKernelGGL(router_bwd_kernel, dim3(tb), dim3(256), 0, s, r.logits, r.topk_idx, dgate,
-                       stats->counts_pre, T, E, k, (int)(c.score_fn == MOE_SCORE_SIGMOID), aux_coef,
-                       z_coef, dlogits);
+    hipError_t e = launch_combine_backward(c, dy, sv.y_perm, r, dyp, dgate, s);
+    if (e != hipSuccess) return e;
+    e = launch_router_backward(c, r, stats, dgate, aux_coef, z_coef, dlogits, s);
+    if (e != hipSuccess) return e;
     // W2^T [E][F][d]; W1^T [E][d][F], for SwiGLU [W1^T | W3^T] as [E][d][2F]
     const int NZ = c.activation == MOE_ACT_SWIGLU ? 2 : 1;
     hipLaunchKernelGGL(transpose_bf16_kernel, dim3(F / 64, d / 64, E), dim3(256), 0, s,
@@ -696,19 +755,9 @@ hipError_t launch_backward_misc(const moe_config& c, const BwdLayout& B, const v
   const int64_t n = (int64_t)E * d;
   hipLaunchKernelGGL(gate_wgrad_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                      (const float*)(ws + B.gate_partial), (int)B.gate_slices, n, gr.dw_gate);
-  if (c.has_gate_bias)
-    hipLaunchKernelGGL(gate_bias_grad_kernel, dim3(E), dim3(256), 0, s, (const float*)dlogits, T, E,
-                       gr.db_gate);
-  const dim3 ug((unsigned)((T + 3) / 4));
-  if (c.router_dtype == MOE_BF16)
-    launch_unpermute_dx<bf16>(ug, s, (const bf16*)(ws + B.dxp), r.assign_row, r.expert_offsets,
-                              (const float*)dlogits, (const bf16*)w.w_gate, T, d, k, E, S, rmax,
-                              (bf16*)gr.dx);
-  else
-    launch_unpermute_dx<float>(ug, s, (const bf16*)(ws + B.dxp), r.assign_row, r.expert_offsets,
-                               (const float*)dlogits, (const float*)w.w_gate, T, d, k, E, S, rmax,
-                               (bf16*)gr.dx);
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_router_bias_and_dx(c, dlogits, ws + B.dxp, r, w, gr, s);
 }
 
 }  // namespace moe

@@ -1806,6 +1806,12 @@ hipError_t launch_backward_dz(const moe_config& c, const void* dyp, const int32_
 hipError_t launch_linear_rows(const moe_config& c, const void* a, const int32_t* offsets,
                               const void* W, const float* b, const void* Ws, const float* bs,
                               void* out, int N, int K, hipStream_t s, const int32_t* arows) {
+  if (c.act_dtype != MOE_BF16)
+    return b ? gemm_launch<float, EPI_NONE, true>(c, (const float*)a, W, nullptr, b, Ws, nullptr,
+                                                  bs, offsets, (float*)out, N, K, s, arows)
+             : gemm_launch<float, EPI_NONE, false>(c, (const float*)a, W, nullptr, nullptr, Ws,
+                                                   nullptr, nullptr, offsets, (float*)out, N, K, s,
+                                                   arows);
   return b ? gemm_launch<bf16, EPI_NONE, true>(c, (const bf16*)a, W, nullptr, b, Ws, nullptr, bs,
                                                offsets, (bf16*)out, N, K, s, arows)
            : gemm_launch<bf16, EPI_NONE, false>(c, (const bf16*)a, W, nullptr, nullptr, Ws, nullptr,
@@ -1820,8 +1826,9 @@ hipError_t launch_expert_up_linear(const moe_config& c, const void* a, const int
                                     c.has_bias ? w.bs1 : nullptr, z, N, K, s, arows);
   if (e != hipSuccess || c.activation != MOE_ACT_SWIGLU) return e;
   // SwiGLU: the second plane u = x W3^T (no bias)
+  const size_t es = c.act_dtype == MOE_BF16 ? 2 : 4;
   return launch_linear_rows(c, a, offsets, w.w3, nullptr, w.ws3, nullptr,
-                            (bf16*)z + rows_max(c) * c.d_ff, N, K, s, arows);
+                            (char*)z + (size_t)rows_max(c) * c.d_ff * es, N, K, s, arows);
 }
 
 hipError_t launch_backward_dx(const moe_config& c, const void* dz, const int32_t* offsets,

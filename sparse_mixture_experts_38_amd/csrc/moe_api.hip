@@ -178,8 +178,8 @@ static int scratch_of_current_device(hipStream_t stream, void** out) {
 static int validate_train(const moe_config* c) {
   const int v = validate(c);
   if (v != MOE_OK) return v;
-  if (c->act_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
-  if (backward_layout(*c).ldk >= ((int64_t)1 << 23)) return MOE_ERR_UNSUPPORTED;
+  if (c->act_dtype == MOE_BF16 && backward_layout(*c).ldk >= ((int64_t)1 << 23))
+    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -579,7 +579,7 @@ int moe_backward_workspace_size(const moe_config* cfg, size_t* bytes_out) {
   const int v = validate_train(cfg);
   if (v != MOE_OK) return v;
   if (!bytes_out) return MOE_ERR_INVALID_ARG;
-  *bytes_out = backward_layout(*cfg).total;
+  *bytes_out = (cfg->act_dtype == MOE_BF16 ? backward_layout(*cfg) : backward_layout_f32(*cfg)).total;
   return MOE_OK;
 }
 
@@ -605,10 +605,13 @@ int moe_backward(const moe_config* cfg, const void* x, const moe_weights* w, con
     return MOE_ERR_INVALID_ARG;
   const bool swiglu = cfg->activation == MOE_ACT_SWIGLU;
   if (swiglu && (!w->w3 || !g->dw3 || (shared && (!w->ws3 || !g->dws3)))) return MOE_ERR_INVALID_ARG;
-  const BwdLayout B = backward_layout(*cfg);
+  const BwdLayout B = cfg->act_dtype == MOE_BF16 ? backward_layout(*cfg) : backward_layout_f32(*cfg);
   if (workspace_bytes < B.total) return MOE_ERR_WORKSPACE;
   char* ws = (char*)workspace;
   const hipStream_t s = (hipStream_t)stream;
+  if (cfg->act_dtype != MOE_BF16)
+    return hip_status(launch_backward_f32(*cfg, B, x, *w, *r, stats, *saved, dy, aux_coef, z_coef,
+                                          *g, ws, s));
   hipError_t e = launch_backward_misc(*cfg, B, x, *w, *r, stats, *saved, dy, aux_coef, z_coef, *g,
                                       ws, s, 0);
   if (e != hipSuccess) return MOE_ERR_HIP;

@@ -241,6 +241,25 @@ hipError_t launch_expert_up_linear(const moe_config& c, const void* a, const int
                                    const int32_t* arows);
 hipError_t launch_act_rows(const moe_config& c, const void* z, const int32_t* expert_offsets,
                            void* h, hipStream_t stream);
+// Backward steps shared by the bf16 and float32 paths: combine (dYp, dgate),
+// router (dlogits), and the gate-bias gradient with dx.
+hipError_t launch_combine_backward(const moe_config& c, const void* dy, const void* y_perm,
+                                   const moe_routing& r, void* dyp, float* dgate, hipStream_t s);
+hipError_t launch_router_backward(const moe_config& c, const moe_routing& r, const moe_stats* stats,
+                                  const float* dgate, float aux_coef, float z_coef, float* dlogits,
+                                  hipStream_t s);
+hipError_t launch_router_bias_and_dx(const moe_config& c, const float* dlogits, const void* dxp,
+                                     const moe_routing& r, const moe_weights& w,
+                                     const moe_grads& gr, hipStream_t s);
+// float32 layers: h = act(z) of the training forward, the backward workspace
+// layout (dyp, dgate, dlogits, dz, dh, hT = h row-major, dxp) and the whole backward.
+hipError_t launch_act_rows_f32(const moe_config& c, const void* z, const int32_t* expert_offsets,
+                               void* h, hipStream_t stream);
+BwdLayout backward_layout_f32(const moe_config& c);
+hipError_t launch_backward_f32(const moe_config& c, const BwdLayout& B, const void* x,
+                               const moe_weights& w, const moe_routing& r, const moe_stats* stats,
+                               const moe_saved& sv, const void* dy, float aux_coef, float z_coef,
+                               const moe_grads& gr, char* ws, hipStream_t stream);
 // The non-GEMM steps of the backward: phase 0 (combine and router backward,
 // weight transposes, padded offsets) before the dZ / dX GEMMs, phase 1 (row
 // transposes, weight, bias and router gradients, dx) after them.

@@ -176,16 +176,18 @@ def test_training_entry_points_validate_before_any_launch():
                                  None) == A.MOE_ERR_INVALID_ARG
     assert lib.moe_backward(ctypes.byref(cfg), None, None, None, None, None, None, 0.0, 0.0, None,
                             None, 0, None) == A.MOE_ERR_INVALID_ARG
-    # layers the backward does not run in this build: float32 activations
     sw = _base(activation="swiglu")
     assert lib.moe_backward_workspace_size(ctypes.byref(sw), ctypes.byref(n)) == A.MOE_OK
-    for bad in (_base(act_dtype="f32", d_ff=200),):
-        assert lib.moe_backward_workspace_size(ctypes.byref(bad), ctypes.byref(n)) == \
-            A.MOE_ERR_UNSUPPORTED
-        assert lib.moe_backward(ctypes.byref(bad), None, None, None, None, None, None, 0.0, 0.0,
-                                None, None, 0, None) == A.MOE_ERR_UNSUPPORTED
-        assert lib.moe_forward_train(ctypes.byref(bad), None, None, None, None, None, None, None, 0,
-                                     None) == A.MOE_ERR_UNSUPPORTED
+    # float32 layers: their own (float32) backward workspace; null pointers refused
+    f32 = _base(act_dtype="f32", router_dtype="f32", d_model=32, d_ff=200)
+    assert lib.moe_backward_workspace_size(ctypes.byref(f32), ctypes.byref(n)) == A.MOE_OK
+    T, d, F, k = f32.tokens, 32, 200, f32.top_k
+    rows = T * k
+    assert n.value >= 4 * (rows * d * 2 + rows * F * 2 + T * k + T * f32.num_experts)
+    assert lib.moe_backward(ctypes.byref(f32), None, None, None, None, None, None, 0.0, 0.0,
+                            None, None, 0, None) == A.MOE_ERR_INVALID_ARG
+    assert lib.moe_forward_train(ctypes.byref(f32), None, None, None, None, None, None, None, 0,
+                                 None) == A.MOE_ERR_INVALID_ARG
     # zero tokens: no-op
     z = _base(tokens=0)
     assert lib.moe_backward(ctypes.byref(z), None, None, None, None, None, None, 0.0, 0.0, None,

@@ -5,8 +5,8 @@ Stage isolation: the oracle runs on the GPU's routing (logits and top-k choice),
 so near ties cannot make the two sides differ in a discrete decision; the
 routing itself is checked bit-exact by the forward parity tests. Every
 gradient is compared over the whole tensor with the max-norm relative error
-max|g - r| / max|r| against the bf16 bar (the operands of the expert GEMMs are
-bf16, as in the forward).
+max|g - r| / max|r| against the bar of the layer's type: bf16 (the operands of
+the expert GEMMs are bf16, as in the forward) or float32.
 """
 import numpy as np
 import pytest
@@ -44,6 +44,15 @@ CASES = {
     # d_model 2048: the dX GEMM takes the 256 x 256 tiles for full 256-row blocks
     "long_k": W["deepspeed_gpt_moe"].scaled(tokens=600, d_model=2048, d_ff=512, num_experts=4,
                                             drop_tokens=False),
+    # the float32 layer as given (T = 64, d = 32, GELU experts with biases, gate bias)
+    "tiny_fp32": W["tiny_fp32"],
+    # float32 with capacity drops and ReLU
+    "fp32_relu_drops": W["tiny_fp32"].scaled(tokens=97, d_model=40, d_ff=72, num_experts=5,
+                                             activation="relu", drop_tokens=True,
+                                             capacity_factor=0.8, min_capacity=2),
+    # float32 DeepSeek-V3 recipe: sigmoid + selection bias, SwiGLU, shared expert
+    "fp32_deepseek": W["deepseek_v3"].scaled(tokens=130, d_model=48, d_ff=64, num_experts=16,
+                                             top_k=4, act_dtype="f32", router_dtype="f32"),
 }
 
 
@@ -71,7 +80,8 @@ def gpu_train_step(w, g, dy, cfg=None, aux=AUX, zc=ZC):
 def make_dy(w, seed, device="cpu"):
     gen = torch.Generator(device=device)
     gen.manual_seed(1000 + seed)
-    return torch.randn(w.tokens, w.d_model, generator=gen, device=device).to(torch.bfloat16)
+    dt = torch.bfloat16 if w.act_dtype == "bf16" else torch.float32
+    return torch.randn(w.tokens, w.d_model, generator=gen, device=device).to(dt)
 
 
 def check_backward(w, inp, dy, out):
@@ -80,7 +90,7 @@ def check_backward(w, inp, dy, out):
     logits = out["logits"].numpy().astype(np.float64)
     fwd = O.forward(x_np, P, w, logits=out["logits"].numpy(), idx=out["topk_idx"].numpy())
     check_dispatch(w, out)
-    tol = TOL["bf16"]
+    tol = TOL[w.act_dtype]
     errs = {}
     # training forward: output, saved pre-activation and expert outputs
     errs["y"] = rel_err(out["y"].float().numpy(), fwd["y"])
