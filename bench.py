@@ -42,6 +42,7 @@ COPY_BYTES = 256 << 20      # each of read and write for the calibration copy
 GEMM_SOURCE = os.path.join(ROOT, "sparse_mixture_experts_38_amd", "csrc", "expert_gemm.hip")
 EXTRA_WORKLOADS = ("deepspeed_gpt_moe", "mixtral_8x7b")
 SECONDARY = "deepspeed_gpt_moe"   # workload of the training and expert-choice figures
+TRAIN_LARGE = "mixtral_8x7b"     # a second training figure at a large dense-expert layer
 
 
 def kernel_source_hash():
@@ -256,8 +257,8 @@ def expert_choice_step(A, torch, w, cfg, sets, steps, warmup):
 def train_step(A, torch, w, cfg, sets, ws, steps, warmup, rows):
     """One training step of the layer: moe_forward_train then moe_backward (with
     L_aux and z-loss weights 0.01 and 0.001), on the same rotated input sets.
-    The backward's algorithmic FLOPs are its four expert GEMMs, 4 x 2 R d F
-    (dH and dX, dW2 and dW1), R = kept rows."""
+    The backward's algorithmic FLOPs are its expert GEMMs, 4 x 2 R d F (dH and
+    dX, dW2 and dW1; 6 x 2 R d F for SwiGLU: dX at K = 2F and dW3), R = kept rows."""
     T, d, F = w.tokens, w.d_model, w.d_ff
     act = A.TORCH_DTYPE[cfg.act_dtype]
     grads = A.alloc_grads(cfg)
@@ -287,7 +288,8 @@ def train_step(A, torch, w, cfg, sets, ws, steps, warmup, rows):
     step_ms = statistics.median(e[0].elapsed_time(e[2]) for e in ev)
     fwd_ms = statistics.median(e[0].elapsed_time(e[1]) for e in ev)
     bwd_ms = statistics.median(e[1].elapsed_time(e[2]) for e in ev)
-    bwd_flop = 4 * 2.0 * rows * d * F
+    # dH and dX (K = 2F for SwiGLU), dW2 and dW1 (+ dW3 for SwiGLU)
+    bwd_flop = (6 if w.activation == "swiglu" else 4) * 2.0 * rows * d * F
     tf = bwd_flop / (bwd_ms * 1e-3) / 1e12
     return {"workload": w.name, "step_ms": step_ms, "forward_train_ms": fwd_ms,
             "backward_ms": bwd_ms, "tokens_per_s": T / (step_ms * 1e-3),
@@ -399,6 +401,9 @@ def main():
                         ctypes.byref(cfgx), ctypes.byref(ctypes.c_size_t(0))) == A.MOE_OK:
                     result["train"] = train_step(A, torch, wx, cfgx, setsx, wsx, steps, args.warmup,
                                                  r["kept_rows"])
+            if name == TRAIN_LARGE and not args.no_train:
+                result["train_" + name] = train_step(A, torch, wx, cfgx, setsx, wsx, max(5, steps // 4),
+                                                     2, r["kept_rows"])
             setsx = wsx = None
             release(torch)
     print(json.dumps(result), flush=True)

@@ -293,3 +293,91 @@ def test_backward_full_size_sampled():
             dz = (dYp[r] @ W2s[e]) * O.gelu_grad(Z[r])
             dx_ref[si] += dz @ W1s[e]
     assert rel_err(G["dx"].float().numpy()[toks], dx_ref) <= tol, "dx"
+
+
+def test_backward_full_size_mixtral_sampled_tokens():
+    """Mixtral 8x7B at its full size (T = 4096, d = 4096, F = 14336, 8 SwiGLU
+    experts, top-2, no capacity limit), trained on a dy that is zero except on
+    64 sampled tokens, with aux_coef = z_coef = 0: then only those tokens' rows
+    carry gradient, so every gradient tensor has an exact reference the oracle
+    computes from those rows alone (x, the weights and the GPU's routing): dx in
+    full (zero off the sample), dW_g, dW1, dW3 and dW2 of every expert in full,
+    and the saved planes z1, u and the expert outputs on the sampled rows."""
+    w = W["mixtral_8x7b"]
+    print("[case] backward full-size mixtral_8x7b (sampled tokens)", flush=True)
+    inp = make_inputs(w, seed=0, device="cuda")
+    T, d, F, E, k = w.tokens, w.d_model, w.d_ff, w.num_experts, w.top_k
+    rng = np.random.default_rng(0)
+    sample = np.sort(rng.choice(T, 64, replace=False))
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(77)
+    dy = torch.zeros(T, d, dtype=torch.bfloat16)
+    dy[torch.from_numpy(sample)] = torch.randn(len(sample), d, generator=gen).to(torch.bfloat16)
+    out = gpu_train_step(w, inp, dy.cuda(), aux=0.0, zc=0.0)
+    x = np64(inp["x"])
+    dyn = np64(dy)
+    P = oracle_params(inp)
+    dsp = check_dispatch(w, out)
+    idx = out["topk_idx"].numpy()
+    logits = out["logits"].numpy()
+    gates = O.renormalised_gates(O.route(logits, k, w.score_fn)["scores"], idx)
+    tol = TOL["bf16"]
+    zs = out["z"].float().numpy()
+    yp = out["y_perm"].float().numpy()
+    # per expert, its sampled rows: the oracle's forward and backward of each row
+    # (weights converted to float64 once per expert)
+    pairs = [(si, j) for si in range(len(sample)) for j in range(k)]
+    dgate = np.zeros((len(sample), k))
+    dxp = np.zeros((len(sample), d))
+    rows, z1r, ur, yr, dz1r, dur, hr, dypr, toks_of, exp_of = ([] for _ in range(10))
+    for e in range(E):
+        sel = [(si, j) for si, j in pairs if int(idx[sample[si], j]) == e]
+        if not sel:
+            continue
+        W1, W3, W2 = P["w1"][e], P["w3"][e], P["w2"][e]
+        ts = np.array([sample[si] for si, _ in sel])
+        z1 = x[ts] @ W1.T
+        u = x[ts] @ W3.T
+        h = O.silu(z1) * u
+        y = h @ W2.T
+        g = np.array([gates[sample[si], j] for si, j in sel])
+        dY = g[:, None] * dyn[ts]
+        dH = dY @ W2
+        dz1 = dH * u * O.silu_grad(z1)
+        du = dH * O.silu(z1)
+        dxe = dz1 @ W1 + du @ W3
+        for q, (si, j) in enumerate(sel):
+            dgate[si, j] = dyn[ts[q]] @ y[q]
+            dxp[si] += dxe[q]
+            rows.append(int(dsp["assign_row"][sample[si], j]))
+        z1r += list(z1); ur += list(u); yr += list(y); dz1r += list(dz1); dur += list(du)
+        hr += list(h); dypr += list(dY); toks_of += list(ts); exp_of += [e] * len(sel)
+    rows = np.array(rows)
+    assert rel_err(zs[0, rows], np.array(z1r)) <= tol, "saved z1"
+    assert rel_err(zs[1, rows], np.array(ur)) <= tol, "saved u"
+    assert rel_err(yp[rows], np.array(yr)) <= tol, "y_perm"
+    # router: the sampled tokens alone (every other token has dgate = 0 and no
+    # aux or z term)
+    f = dsp["counts_pre"] / float(T * k)
+    dlog = O.router_backward(logits[sample].astype(np.float64), idx[sample], w.score_fn, dgate,
+                             f, 0.0, 0.0)
+    G = out["grads"]
+    assert rel_err(G["dw_gate"].numpy(), dlog.T @ x[sample]) <= tol, "dw_gate"
+    dx_ref = np.zeros((T, d))
+    dx_ref[sample] = dxp + dlog @ P["w_gate"]
+    assert rel_err(G["dx"].float().numpy(), dx_ref) <= tol, "dx"
+    others = np.setdiff1d(np.arange(T), sample)
+    assert float(G["dx"][torch.from_numpy(others)].abs().max()) == 0.0, "dx off the sample"
+    exp_of = np.array(exp_of)
+    toks_of = np.array(toks_of)
+    for e in range(E):
+        m = exp_of == e
+        xs = x[toks_of[m]]
+        for name, ref in (("dw1", np.array(dz1r)[m].T @ xs), ("dw3", np.array(dur)[m].T @ xs),
+                          ("dw2", np.array(dypr)[m].T @ np.array(hr)[m])):
+            got = G[name][e].numpy()
+            if not m.any():
+                assert float(np.abs(got).max()) == 0.0, f"{name}[{e}] without rows"
+                continue
+            assert rel_err(got, ref) <= tol, f"{name}[{e}]"
+    print(f"[case] mixtral training: {len(sample)} tokens, {len(rows)} rows checked", flush=True)
