@@ -93,7 +93,7 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, i
 // every group in BM-row tiles; 1 the first floor(n / BM) BM-row tiles of each
 // group of n rows; 2 the rows that part 1 leaves over (fewer than `big`), in
 // BM-row tiles. Groups of at most skip_rows rows are left out (the streaming
-// GEMM runs them).
+// GEMM runs them); for the last group (g = G - 1) the bound is skip_last.
 struct TileSpace {
   int s[5], e[5], n[5];
   int excl, incl, total;
@@ -101,7 +101,8 @@ struct TileSpace {
 
 __device__ __forceinline__ void tile_space_init(TileSpace& ts, const int32_t* __restrict__ offsets,
                                                 int G, int rows_max, int BM, int part = 0,
-                                                int big = 256, int skip_rows = 0) {
+                                                int big = 256, int skip_rows = 0,
+                                                int skip_last = 0) {
   constexpr int PER = 5;
   const int lane = threadIdx.x & 63;
   const int g0 = lane * PER;
@@ -117,7 +118,8 @@ __device__ __forceinline__ void tile_space_init(TileSpace& ts, const int32_t* __
   for (int i = 0; i < PER; ++i) {
     const int gi = g0 + i;
     const int rows0 = (gi < G && o[i + 1] > o[i]) ? o[i + 1] - o[i] : 0;
-    const int rows = rows0 > skip_rows ? rows0 : 0;   // (groups the streaming GEMM takes)
+    // (groups the streaming GEMM takes)
+    const int rows = rows0 > (gi == G - 1 ? skip_last : skip_rows) ? rows0 : 0;
     const int full = part == 0 ? 0 : rows / big * big;
     ts.s[i] = o[i] + (part == 2 ? full : 0);
     ts.e[i] = part == 1 ? o[i] + full : o[i] + rows;
@@ -201,7 +203,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
     const float* __restrict__ bias, const bf16* __restrict__ Ws, const bf16* __restrict__ Ws3,
     const float* __restrict__ bias_s, int E, int G, const int32_t* __restrict__ offsets,
     int rows_max, void* __restrict__ Cv, int N, int K, int part, const int32_t* __restrict__ arows,
-    int kparts, const bf16* __restrict__ Zin, int skip_rows) {
+    int kparts, const bf16* __restrict__ Zin, int skip_rows, int skip_last) {
   constexpr bool GATED = EPI == EPI_SWIGLU;
   constexpr bool DACT = EPI == EPI_DGELU || EPI == EPI_DRELU;
   constexpr int BM = 128, BK = 64, CH = BK / 8;   // 8 chunks of 16 B per LDS row
@@ -217,7 +219,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
   bf16* __restrict__ C = reinterpret_cast<bf16*>(Cv);
 
   TileSpace ts;
-  tile_space_init(ts, offsets, G, rows_max, BM, part, kGemmBigBM, skip_rows);
+  tile_space_init(ts, offsets, G, rows_max, BM, part, kGemmBigBM, skip_rows, skip_last);
   const int mtiles = __builtin_amdgcn_readfirstlane(ts.total);
   const int ntn = N / BN;
   const int tiles = mtiles * ntn;
@@ -663,7 +665,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(
     const float* __restrict__ bias, const bf16* __restrict__ Ws, const bf16* __restrict__ Ws3,
     const float* __restrict__ bias_s, int E, int G, const int32_t* __restrict__ offsets,
     int rows_max, bf16* __restrict__ C, int N, int K, const int32_t* __restrict__ arows,
-    uint32_t a_bytes, int skip_rows) {
+    uint32_t a_bytes, int skip_rows, int skip_last) {
   constexpr bool GATED = EPI == EPI_SWIGLU;
   constexpr int BM = 256, BK = 64, CH = BK / 8;   // 8 chunks of 16 B per LDS row
   constexpr int NB = GATED ? 2 : 1;
@@ -679,7 +681,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(
   __shared__ uint32_t pf_lds[512];   // landing area of the L2 prefetches, never read
 
   TileSpace ts;
-  tile_space_init(ts, offsets, G, rows_max, BM, 1, BM, skip_rows);
+  tile_space_init(ts, offsets, G, rows_max, BM, 1, BM, skip_rows, skip_last);
   const int mtiles = __builtin_amdgcn_readfirstlane(ts.total);
   const int ntn = N / BN;
   const int tiles = mtiles * ntn;
@@ -954,7 +956,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(
 // 6, 8) on the standard layout; rows past the part's end repeat its last row
 // and are not stored.
 constexpr int kStreamRows = 256;   // rows per part
-constexpr int kStreamMaxRows = 1536;  // groups with more rows use the tiled kernels
+constexpr int kStreamMaxRows = 1536;  // groups with more rows use the tiled kernels,
+constexpr int kStreamSharedMaxRows = 4096;   // except a shared group of up to this many
 constexpr int kStreamLds = 10240;     // u32x4 (160 KB)
 // Work items of the streaming GEMM: group g with rows in (0, max_rows]
 // contributes ns slabs x ceil(rows / 256) parts. Lane l of every wave holds
@@ -966,7 +969,8 @@ struct StreamSpace {
 };
 
 __device__ __forceinline__ void stream_space_init(StreamSpace& ss, const int32_t* __restrict__ offsets,
-                                                  int G, int rows_max, int max_rows, int ns) {
+                                                  int G, int rows_max, int min_rows, int max_rows,
+                                                  int ns) {
   constexpr int PER = 5;
   const int lane = threadIdx.x & 63;
   const int g0 = lane * PER;
@@ -981,7 +985,7 @@ __device__ __forceinline__ void stream_space_init(StreamSpace& ss, const int32_t
   for (int i = 0; i < PER; ++i) {
     const int gi = g0 + i;
     const int rows = (gi < G && o[i + 1] > o[i]) ? o[i + 1] - o[i] : 0;
-    const bool mine = rows > 0 && rows <= max_rows;
+    const bool mine = rows > 0 && rows > min_rows && rows <= max_rows;
     ss.s[i] = o[i];
     ss.r[i] = mine ? rows : 0;
     ss.n[i] = mine ? (rows + kStreamRows - 1) / kStreamRows * ns : 0;
@@ -1456,7 +1460,7 @@ __device__ __forceinline__ void stream_tile_packed(u32x4* __restrict__ smem,
   stream_epilogue_lds<EPI, HAS_BIAS, MF>(acc, smem, bg, row0, mrows, n0, C, N);
 }
 
-// One launch over every group with rows in (0, max_rows]: work items (group,
+// One launch over every group with rows in (min_rows, max_rows]: work items (group,
 // slab, part) in the XCD-aware order; blocks past the item count exit.
 // Requires N a multiple of 256, K a multiple of 256, and the A operand
 // addressable with 32-bit byte offsets (a_bytes < 2^32; checked by the host).
@@ -1466,13 +1470,13 @@ __global__ __launch_bounds__(256, 1) void gemm_stream_kernel(
     const float* __restrict__ bias, const bf16* __restrict__ Ws, const bf16* __restrict__ Ws3,
     const float* __restrict__ bias_s, int E, int G, const int32_t* __restrict__ offsets,
     int rows_max, bf16* __restrict__ C, int N, int K, const int32_t* __restrict__ arows,
-    uint32_t a_bytes, int max_rows, const bf16* __restrict__ Wp) {
+    uint32_t a_bytes, int min_rows, int max_rows, const bf16* __restrict__ Wp) {
   constexpr bool GATED = EPI == EPI_SWIGLU;
   constexpr int BNO = GATED ? 128 : 256;   // output columns per slab
   __shared__ u32x4 smem[kStreamLds];   // the K-step stages (160 KB)
   const int ns = N / BNO;
   StreamSpace ss;
-  stream_space_init(ss, offsets, G, rows_max, max_rows, ns);
+  stream_space_init(ss, offsets, G, rows_max, min_rows, max_rows, ns);
   const int items = __builtin_amdgcn_readfirstlane(ss.total);
   const int b = blockIdx.x;
   if (b >= items) return;
@@ -1628,6 +1632,9 @@ static hipError_t gemm_launch(const moe_config& c, const ET* A, const void* W, c
                                 EPI == EPI_NONE;
     const int64_t a_span = arows ? a_bytes : rows * (int64_t)K * 2;
     const int skip = kStreamEpi && a_span < ((int64_t)1 << 32) ? kStreamMaxRows : 0;
+    const int skip_last =
+        skip > 0 && G > E && c.tokens > skip && c.tokens <= kStreamSharedMaxRows ? kStreamSharedMaxRows
+                                                                                  : skip;
     if constexpr (kStreamEpi) {
       if (skip > 0) {
         constexpr int BNO = EPI == EPI_SWIGLU ? 128 : 256;
@@ -1640,8 +1647,22 @@ static hipError_t gemm_launch(const moe_config& c, const ET* A, const void* W, c
         if (items > 0)
         hipLaunchKernelGGL((gemm_stream_kernel<EPI, HB>), dim3((unsigned)items), dim3(256), 0, s, A,
                            (const bf16*)W, (const bf16*)W3, bias, (const bf16*)Ws, (const bf16*)Ws3,
-                           bias_s, E, G, offsets, (int)rows, C, N, K, arows, (uint32_t)a_span, skip,
-                           (const bf16*)wpacked);
+                           bias_s, E, G, offsets, (int)rows, C, N, K, arows, (uint32_t)a_span, 0,
+                           skip, (const bf16*)wpacked);
+        // A shared expert (group E, nominally T rows) of more than kStreamMaxRows
+        // and at most kStreamSharedMaxRows rows: a streaming launch of its own,
+        // over group E alone (at most 16 parts of 256 rows per slab), in place of
+        // the tiled kernels (at the DeepSeek-V3 shape, T = 4096 and K = 7168:
+        // GEMM 1 stage 2.76 -> 2.69 ms, paired timing on one MI355X).
+        if (skip_last > skip) {
+          const size_t per_group = (size_t)(EPI == EPI_SWIGLU ? 2 : 1) * N * K;
+          hipLaunchKernelGGL((gemm_stream_kernel<EPI, HB>),
+                             dim3((unsigned)(kStreamSharedMaxRows / kStreamRows * (N / BNO))),
+                             dim3(256), 0, s, A, (const bf16*)W, (const bf16*)W3, bias,
+                             (const bf16*)Ws, (const bf16*)Ws3, bias_s, 0, 1, offsets + E,
+                             (int)rows, C, N, K, arows, (uint32_t)a_span, skip, skip_last,
+                             wpacked ? (const bf16*)wpacked + (size_t)E * per_group : nullptr);
+        }
       }
     }
     // (the backward epilogues EPI_DGELU / EPI_DRELU exist in the 128 x 128 kernel only)
@@ -1655,20 +1676,22 @@ static hipError_t gemm_launch(const moe_config& c, const ET* A, const void* W, c
         hipLaunchKernelGGL((gemm_bf16_big_kernel<EPI, HB>), dim3(big_tiles), dim3(256), 0, s, A,
                            (const bf16*)W, (const bf16*)W3, bias, (const bf16*)Ws, (const bf16*)Ws3,
                            bias_s, E, G, offsets, (int)rows, C, N, K, arows, (uint32_t)a_bytes,
-                           skip);
+                           skip, skip_last);
       // each group leaves at most 255 rows, i.e. at most 2 tiles, and the
       // tiles number at most ceil(rows / 128) + G
       const int64_t rest = (rows + 127) / 128 + G < 2 * G ? (rows + 127) / 128 + G : 2 * G;
       const int64_t rgrid = rest * (N / BN) < slots ? rest * (N / BN) : slots;
       hipLaunchKernelGGL((gemm_bf16_kernel<EPI, HB>), dim3((unsigned)rgrid), dim3(256), 0, s, A,
                          (const bf16*)W, (const bf16*)W3, bias, (const bf16*)Ws, (const bf16*)Ws3,
-                         bias_s, E, G, offsets, (int)rows, C, N, K, 2, arows, 1, zin, skip);
+                         bias_s, E, G, offsets, (int)rows, C, N, K, 2, arows, 1, zin, skip,
+                         skip_last);
     } else {
       const int64_t tiles = ((rows + 127) / 128 + G) * (N / BN);
       const int64_t grid = tiles < slots ? tiles : slots;
       hipLaunchKernelGGL((gemm_bf16_kernel<EPI, HB>), dim3((unsigned)grid), dim3(256), 0, s, A,
                          (const bf16*)W, (const bf16*)W3, bias, (const bf16*)Ws, (const bf16*)Ws3,
-                         bias_s, E, G, offsets, (int)rows, C, N, K, 0, arows, 1, zin, skip);
+                         bias_s, E, G, offsets, (int)rows, C, N, K, 0, arows, 1, zin, skip,
+                         skip_last);
     }
   } else {
     const unsigned mtiles = (unsigned)((rows + kGemmBM - 1) / kGemmBM) + G;
@@ -1730,7 +1753,7 @@ hipError_t launch_router_gemm(const moe_config& c, const void* x, const void* w_
                      (const bf16*)x, (const bf16*)w_gate, (const bf16*)nullptr, (const float*)nullptr,
                      (const bf16*)nullptr, (const bf16*)nullptr, (const float*)nullptr, 1, 1,
                      (const int32_t*)nullptr, (int)T, (void*)partials, E, K, 0,
-                     (const int32_t*)nullptr, kp, (const bf16*)nullptr, 0);
+                     (const int32_t*)nullptr, kp, (const bf16*)nullptr, 0, 0);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int64_t n4 = T * E / 4;
