@@ -1385,16 +1385,18 @@ __device__ __forceinline__ void stream_tile_packed(u32x4* __restrict__ smem,
                                                16, aoff[i_], (uint32_t)(kt) * 128u, 0, 0); \
   } while (0)
   // Sub-step s of the step in slot sl: for each token fragment i, its two
-  // MFMAs, then the read of fragment i for (stage srd, sub-step s2) into the
-  // same registers; then (LOAD) the weight loads of step kl, sub-step s, into
-  // slot (sl + 3) & 3, in the registers sub-step s has just consumed.
+  // MFMAs and the read of fragment i for (stage srd, sub-step s2) into the same
+  // registers (the compiler interleaves these freely: fixing the order pair by
+  // pair with scheduling barriers cost 1.5-2.5 % of the GEMM stages); then
+  // (LOAD) the weight loads of step kl, sub-step s, into slot (sl + 3) & 3, the
+  // previous step's slot, behind a scheduling barrier so that the order of the
+  // loads, which the vmcnt waits count, stays fixed.
 #define MOE_SUB(sl, s, srd, s2, LOAD, kl)                                             \
   do {                                                                                \
     _Pragma("unroll") for (int i_ = 0; i_ < MF; ++i_) {                               \
       acc[i_][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wr[sl][0][s], fa[i_], acc[i_][0], 0, 0, 0); \
       acc[i_][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wr[sl][1][s], fa[i_], acc[i_][1], 0, 0, 0); \
       fa[i_] = __builtin_bit_cast(bf16x8, smem[(srd) * ASTAGE + i_ * 32 * CH + cread[s2]]); \
-      MOE_SB();                                                                       \
     }                                                                                 \
     if (LOAD) MOE_LW(kl, ((sl) + 3) & 3, s);                                          \
     MOE_SB();                                                                         \
