@@ -12,6 +12,9 @@
 // so the 32 rows a fragment read touches fall in distinct banks, and double
 // buffered with one barrier per K step. float32 path (float32 layers): a
 // plain FMA kernel over the same tile map.
+#include <atomic>
+#include <mutex>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -960,17 +963,17 @@ constexpr int kStreamMaxRows = 1536;  // groups with more rows use the tiled ker
 constexpr int kStreamSharedMaxRows = 4096;   // except a shared group of up to this many
 constexpr int kStreamLds = 10240;     // u32x4 (160 KB)
 // Work items of the streaming GEMM: group g with rows in (0, max_rows]
-// contributes ns slabs x ceil(rows / 256) parts. Lane l of every wave holds
-// groups 5 l .. 5 l + 4 (first row, row count, item count) and the prefix of
-// items before them.
+// ((min_last, max_last] for the last group, g = G - 1) contributes ns slabs x
+// ceil(rows / 256) parts. Lane l of every wave holds groups 5 l .. 5 l + 4
+// (first row, row count, item count) and the prefix of items before them.
 struct StreamSpace {
   int s[5], r[5], n[5];
   int excl, incl, total;
 };
 
 __device__ __forceinline__ void stream_space_init(StreamSpace& ss, const int32_t* __restrict__ offsets,
-                                                  int G, int rows_max, int min_rows, int max_rows,
-                                                  int ns) {
+                                                  int G, int rows_max, int max_rows, int min_last,
+                                                  int max_last, int ns) {
   constexpr int PER = 5;
   const int lane = threadIdx.x & 63;
   const int g0 = lane * PER;
@@ -985,7 +988,7 @@ __device__ __forceinline__ void stream_space_init(StreamSpace& ss, const int32_t
   for (int i = 0; i < PER; ++i) {
     const int gi = g0 + i;
     const int rows = (gi < G && o[i + 1] > o[i]) ? o[i + 1] - o[i] : 0;
-    const bool mine = rows > 0 && rows > min_rows && rows <= max_rows;
+    const bool mine = gi == G - 1 ? rows > min_last && rows <= max_last : rows > 0 && rows <= max_rows;
     ss.s[i] = o[i];
     ss.r[i] = mine ? rows : 0;
     ss.n[i] = mine ? (rows + kStreamRows - 1) / kStreamRows * ns : 0;
@@ -1134,11 +1137,12 @@ __device__ __forceinline__ void stream_epilogue_lds(const f32x16 (&acc)[MF][2], 
 }
 
 template <int EPI, bool HAS_BIAS, int MF>
-__device__ __forceinline__ void stream_tile(u32x4* __restrict__ smem, const bf16* __restrict__ A,
-                                            uint32_t a_bytes, const int32_t* __restrict__ arows,
-                                            const bf16* __restrict__ Wg, const bf16* __restrict__ W3g,
-                                            const float* __restrict__ bg, int row0, int mrows,
-                                            int n0, bf16* __restrict__ C, int N, int K) {
+__device__ __forceinline__ int stream_tile(u32x4* __restrict__ smem, const bf16* __restrict__ A,
+                                           uint32_t a_bytes, const int32_t* __restrict__ arows,
+                                           const bf16* __restrict__ Wg, const bf16* __restrict__ W3g,
+                                           const float* __restrict__ bg, int row0, int mrows,
+                                           int n0, bf16* __restrict__ C, int N, int K,
+                                           int* __restrict__ done) {
   constexpr bool GATED = EPI == EPI_SWIGLU;
   constexpr int CH = 8;                        // 16-byte chunks per 128-byte LDS row
   constexpr int WAREA = 64 * CH;               // u32x4: one wave's 64 weight rows
@@ -1310,7 +1314,11 @@ __device__ __forceinline__ void stream_tile(u32x4* __restrict__ smem, const bf16
 #undef MOE_LDS
 #undef MOE_SB
 
+  // the block's count into the work queue's done counter, its round trip
+  // under the epilogue's stores
+  const int dn = threadIdx.x == 0 && done ? atomicAdd(done, 1) : -1;
   stream_epilogue<EPI, HAS_BIAS, MF>(acc, bg, row0, mrows, n0, C, N);
+  return dn;
 }
 
 // The same tile on a packed copy of the weights (moe_pack_weights): per slab
@@ -1321,13 +1329,13 @@ __device__ __forceinline__ void stream_tile(u32x4* __restrict__ smem, const bf16
 // three K steps ahead, with no trip through LDS; only the token rows are
 // staged in LDS (four stages, three ahead).
 template <int EPI, bool HAS_BIAS, int MF>
-__device__ __forceinline__ void stream_tile_packed(u32x4* __restrict__ smem,
+__device__ __forceinline__ int stream_tile_packed(u32x4* __restrict__ smem,
                                                    const bf16* __restrict__ A, uint32_t a_bytes,
                                                    const int32_t* __restrict__ arows,
                                                    const bf16* __restrict__ Wpg, int slab,
                                                    const float* __restrict__ bg, int row0,
                                                    int mrows, int n0, bf16* __restrict__ C, int N,
-                                                   int K) {
+                                                   int K, int* __restrict__ done) {
   constexpr int CH = 8;
   constexpr int ASTAGE = 32 * MF * CH;         // u32x4 per token-row stage
   constexpr int NW = 8, NA = MF, NL = NW + NA;
@@ -1459,31 +1467,28 @@ __device__ __forceinline__ void stream_tile_packed(u32x4* __restrict__ smem,
 #undef MOE_LW
 #undef MOE_LDS
 #undef MOE_SB
+  // the block's count into the work queue's done counter, its round trip
+  // under the epilogue's stores
+  const int dn = threadIdx.x == 0 && done ? atomicAdd(done, 1) : -1;
   stream_epilogue_lds<EPI, HAS_BIAS, MF>(acc, smem, bg, row0, mrows, n0, C, N);
+  return dn;
 }
 
-// One launch over every group with rows in (min_rows, max_rows]: work items (group,
-// slab, part) in the XCD-aware order; blocks past the item count exit.
-// Requires N a multiple of 256, K a multiple of 256, and the A operand
-// addressable with 32-bit byte offsets (a_bytes < 2^32; checked by the host).
+// Work item t of the streaming GEMM (group, rows, slab from the item space ss):
+// one tile. Returns the block's count into the done counter (thread 0; -1
+// without one).
 template <int EPI, bool HAS_BIAS>
-__global__ __launch_bounds__(256, 1) void gemm_stream_kernel(
-    const bf16* __restrict__ A, const bf16* __restrict__ W, const bf16* __restrict__ W3,
-    const float* __restrict__ bias, const bf16* __restrict__ Ws, const bf16* __restrict__ Ws3,
-    const float* __restrict__ bias_s, int E, int G, const int32_t* __restrict__ offsets,
-    int rows_max, bf16* __restrict__ C, int N, int K, const int32_t* __restrict__ arows,
-    uint32_t a_bytes, int min_rows, int max_rows, const bf16* __restrict__ Wp) {
+__device__ __forceinline__ int stream_item(u32x4* __restrict__ smem, const StreamSpace& ss, int t,
+                                           int ns, const bf16* __restrict__ A,
+                                           const bf16* __restrict__ W, const bf16* __restrict__ W3,
+                                           const float* __restrict__ bias,
+                                           const bf16* __restrict__ Ws, const bf16* __restrict__ Ws3,
+                                           const float* __restrict__ bias_s, int E,
+                                           bf16* __restrict__ C, int N, int K,
+                                           const int32_t* __restrict__ arows, uint32_t a_bytes,
+                                           const bf16* __restrict__ Wp, int* __restrict__ done) {
   constexpr bool GATED = EPI == EPI_SWIGLU;
-  constexpr int BNO = GATED ? 128 : 256;   // output columns per slab
-  __shared__ u32x4 smem[kStreamLds];   // the K-step stages (160 KB)
-  const int ns = N / BNO;
-  StreamSpace ss;
-  stream_space_init(ss, offsets, G, rows_max, min_rows, max_rows, ns);
-  const int items = __builtin_amdgcn_readfirstlane(ss.total);
-  const int b = blockIdx.x;
-  if (b >= items) return;
-  const int t8 = items & ~7;
-  const int t = b < t8 ? (b & 7) * (t8 >> 3) + (b >> 3) : b;
+  constexpr int BNO = GATED ? 128 : 256;
   int g, row0, nrows, slab;
   stream_lookup(ss, t, ns, g, row0, nrows, slab);
   g = __builtin_amdgcn_readfirstlane(g);
@@ -1495,33 +1500,159 @@ __global__ __launch_bounds__(256, 1) void gemm_stream_kernel(
   const bf16* W3g = GATED ? (g < E ? W3 + (int64_t)g * N * K : Ws3) : Wg;
   const float* bg = HAS_BIAS ? (g < E ? bias + (int64_t)g * N : bias_s) : nullptr;
   const int mf = (nrows + 31) / 32;
+  // packed weights of group g: (SwiGLU: 2 x) N x K elements per group; with
+  // them, rows rounded up to the next multiple of 32 (MF = 1 .. 8 fragments)
+  const bf16* Wpg = Wp ? Wp + (int64_t)g * (GATED ? 2 : 1) * N * K : nullptr;
+  int dn;   // this block's count into the done counter (thread 0)
   if (Wp) {
-    // packed weights of group g: (SwiGLU: 2 x) N x K elements per group
-    const bf16* Wpg = Wp + (int64_t)g * (GATED ? 2 : 1) * N * K;
-    // rows rounded up to the next multiple of 32 (MF = 1 .. 8 fragments)
 #define MOE_PT(M)                                                                     \
-  stream_tile_packed<EPI, HAS_BIAS, M>(smem, A, a_bytes, arows, Wpg, slab, bg, row0, nrows, n0, C, N, K)
+  stream_tile_packed<EPI, HAS_BIAS, M>(smem, A, a_bytes, arows, Wpg, slab, bg, row0, nrows, n0, C, N, K, \
+                                       done)
     switch (mf) {
-      case 1: MOE_PT(1); break;
-      case 2: MOE_PT(2); break;
-      case 3: MOE_PT(3); break;
-      case 4: MOE_PT(4); break;
-      case 5: MOE_PT(5); break;
-      case 6: MOE_PT(6); break;
-      case 7: MOE_PT(7); break;
-      default: MOE_PT(8); break;
+      case 1: dn = MOE_PT(1); break;
+      case 2: dn = MOE_PT(2); break;
+      case 3: dn = MOE_PT(3); break;
+      case 4: dn = MOE_PT(4); break;
+      case 5: dn = MOE_PT(5); break;
+      case 6: dn = MOE_PT(6); break;
+      case 7: dn = MOE_PT(7); break;
+      default: dn = MOE_PT(8); break;
     }
 #undef MOE_PT
-    return;
+  } else if (mf <= 2) {
+    dn = stream_tile<EPI, HAS_BIAS, 2>(smem, A, a_bytes, arows, Wg, W3g, bg, row0, nrows, n0, C, N, K, done);
+  } else if (mf <= 4) {
+    dn = stream_tile<EPI, HAS_BIAS, 4>(smem, A, a_bytes, arows, Wg, W3g, bg, row0, nrows, n0, C, N, K, done);
+  } else if (mf <= 6) {
+    dn = stream_tile<EPI, HAS_BIAS, 6>(smem, A, a_bytes, arows, Wg, W3g, bg, row0, nrows, n0, C, N, K, done);
+  } else {
+    dn = stream_tile<EPI, HAS_BIAS, 8>(smem, A, a_bytes, arows, Wg, W3g, bg, row0, nrows, n0, C, N, K, done);
   }
-  if (mf <= 2)
-    stream_tile<EPI, HAS_BIAS, 2>(smem, A, a_bytes, arows, Wg, W3g, bg, row0, nrows, n0, C, N, K);
-  else if (mf <= 4)
-    stream_tile<EPI, HAS_BIAS, 4>(smem, A, a_bytes, arows, Wg, W3g, bg, row0, nrows, n0, C, N, K);
-  else if (mf <= 6)
-    stream_tile<EPI, HAS_BIAS, 6>(smem, A, a_bytes, arows, Wg, W3g, bg, row0, nrows, n0, C, N, K);
-  else
-    stream_tile<EPI, HAS_BIAS, 8>(smem, A, a_bytes, arows, Wg, W3g, bg, row0, nrows, n0, C, N, K);
+  return dn;
+}
+
+// Work-queue counters of the streaming GEMM: kSchedSlots slots per device of
+// 9 counters (the 8 per-XCD ticket counters, then the count of blocks done
+// with the queue), each in a 64-byte line of its own (kSchedStride ints
+// apart) so that atomics on different counters do not queue behind each
+// other; zero when the library is loaded and put back to zero by the last
+// block of each launch. Launches take the slots in turn, so launches in
+// flight at the same time (on other streams) use different slots as long as
+// fewer than kSchedSlots of them overlap.
+constexpr int kSchedSlots = 256;
+constexpr int kSchedStride = 16;
+constexpr int kSchedSlotInts = 16 * kSchedStride;
+__device__ int g_stream_sched[kSchedSlots * kSchedSlotInts];
+
+// One launch over every group with rows in (0, max_rows] ((min_last, max_last]
+// for the last group). The work items (group, slab, part) in group order are split
+// into 8 ranges of equal count, one per XCD. A block takes a ticket of its own
+// XCD's range: the range's counter hands out its items in reverse order, so
+// that the last range starts with the last group (the shared expert's items,
+// the heaviest). A block whose range is used up reads the other ranges'
+// counters and takes a ticket of one that still has items, until it gets an
+// item or reads every range used up (then it exits). The grid has at least as
+// many blocks as items, so every item is taken: a block leaves without one
+// only after reading every counter at its range's size. Items of one group,
+// and the parts of one slab, thus mostly run at the same time on one XCD and
+// share its L2, while a range whose items are heavier than the others' is
+// finished by the blocks of the other XCDs.
+// The counters are those of the slot at sched, zero on entry; every block adds
+// one to the done counter after its last ticket (a working block at the start
+// of its epilogue), and the block that adds the last puts them back to zero.
+// In a launch with no items every block gives its ticket back instead.
+// With sched null the order is static: block b takes item (b % 8) n / 8 +
+// b / 8 of the n items (blocks are dispatched to the XCDs round-robin), and
+// blocks past the item count exit.
+// Requires N a multiple of 256, K a multiple of 256, and the A operand
+// addressable with 32-bit byte offsets (a_bytes < 2^32; checked by the host).
+template <int EPI, bool HAS_BIAS>
+__global__ __launch_bounds__(256, 1) void gemm_stream_kernel(
+    const bf16* __restrict__ A, const bf16* __restrict__ W, const bf16* __restrict__ W3,
+    const float* __restrict__ bias, const bf16* __restrict__ Ws, const bf16* __restrict__ Ws3,
+    const float* __restrict__ bias_s, int E, int G, const int32_t* __restrict__ offsets,
+    int rows_max, bf16* __restrict__ C, int N, int K, const int32_t* __restrict__ arows,
+    uint32_t a_bytes, int max_rows, int min_last, int max_last, const bf16* __restrict__ Wp,
+    int* __restrict__ sched) {
+  constexpr bool GATED = EPI == EPI_SWIGLU;
+  constexpr int BNO = GATED ? 128 : 256;   // output columns per slab
+  __shared__ u32x4 smem[kStreamLds];   // the K-step stages (160 KB, all of the CU's LDS)
+  const int ns = N / BNO;
+  StreamSpace ss;
+  int t;
+  if (!sched) {
+    // static order: block b takes item b of the XCD-aware order (blocks are
+    // dispatched to the XCDs round-robin, and XCD b % 8 runs range b % 8 of
+    // the items, in order); blocks past the item count exit
+    stream_space_init(ss, offsets, G, rows_max, max_rows, min_last, max_last, ns);
+    const int items = __builtin_amdgcn_readfirstlane(ss.total);
+    const int b = blockIdx.x;
+    if (b >= items) return;
+    const int t8 = items & ~7;
+    t = b < t8 ? (b & 7) * (t8 >> 3) + (b >> 3) : b;
+  } else {
+    // a ticket of this block's XCD range first (hardware register XCC_ID); its
+    // round trip overlaps the offsets' loads
+    int xcc = 0, tk = 0;
+    if (threadIdx.x == 0) {
+      xcc = (int)(__builtin_amdgcn_s_getreg((20) | (0 << 6) | (3 << 11)) & 7u);
+      tk = atomicAdd(&sched[xcc * kSchedStride], 1);
+    }
+    stream_space_init(ss, offsets, G, rows_max, max_rows, min_last, max_last, ns);
+    const int items = __builtin_amdgcn_readfirstlane(ss.total);
+    if (items == 0) {
+      // nothing to do in this launch (every block sees the same offsets): give
+      // the ticket back, so the counters end at zero without the done count
+      if (threadIdx.x == 0) atomicSub(&sched[xcc * kSchedStride], 1);
+      return;
+    }
+    if (threadIdx.x == 0) {
+      auto lo_of = [&](int x) { return (int)((int64_t)items * x / 8); };
+      int item = -1;
+      if (tk < lo_of(xcc + 1) - lo_of(xcc)) {
+        item = lo_of(xcc + 1) - 1 - tk;
+      } else {
+        // own range used up: read all eight counters (one round trip), take a
+        // ticket of the first other range that still has items, and read again
+        // if someone was quicker; a block that reads every range used up exits
+        for (;;) {
+          int c[8];
+#pragma unroll
+          for (int x = 0; x < 8; ++x)
+            c[x] = __hip_atomic_load(&sched[x * kSchedStride], __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+          int pick = -1;
+#pragma unroll
+          for (int q = 1; q < 8; ++q) {
+            const int x = (xcc + q) & 7;
+            if (pick < 0 && c[x] < lo_of(x + 1) - lo_of(x)) pick = x;
+          }
+          if (pick < 0) break;
+          const int tq = atomicAdd(&sched[pick * kSchedStride], 1);
+          if (tq < lo_of(pick + 1) - lo_of(pick)) {
+            item = lo_of(pick + 1) - 1 - tq;
+            break;
+          }
+        }
+      }
+      reinterpret_cast<int*>(smem)[0] = item;   // broadcast through LDS
+      if (item < 0) {
+        // no item: done with the queue now
+        __threadfence();
+        if (atomicAdd(&sched[8 * kSchedStride], 1) == (int)gridDim.x - 1)
+          for (int x = 0; x < 9; ++x) atomicExch(&sched[x * kSchedStride], 0);
+      }
+    }
+    __syncthreads();
+    t = __builtin_amdgcn_readfirstlane(reinterpret_cast<const int*>(smem)[0]);
+    __syncthreads();   // read by every wave before the tile's loads land in LDS
+    if (t < 0) return;
+  }
+  const int dn = stream_item<EPI, HAS_BIAS>(smem, ss, t, ns, A, W, W3, bias, Ws, Ws3, bias_s, E, C,
+                                            N, K, arows, a_bytes, Wp,
+                                            sched ? sched + 8 * kSchedStride : nullptr);
+  if (sched && threadIdx.x == 0 && dn == (int)gridDim.x - 1)
+    for (int x = 0; x < 9; ++x) atomicExch(&sched[x * kSchedStride], 0);
 }
 
 // float32 layers: one thread per (row, column) of a tile, plain FMA loop.
@@ -1587,6 +1718,25 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(
   }
 }
 
+// Device address of this launch's slot of g_stream_sched (slots taken in turn;
+// the array's address resolved once per device), or nullptr on failure.
+static int* stream_sched_slot() {
+  static std::mutex mu;
+  static int* base[64] = {nullptr};
+  static std::atomic<unsigned> next{0};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    if (!base[dev]) {
+      void* p = nullptr;
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_stream_sched)) != hipSuccess || !p) return nullptr;
+      base[dev] = static_cast<int*>(p);
+    }
+  }
+  return base[dev] + (next.fetch_add(1) % kSchedSlots) * kSchedSlotInts;
+}
+
 // Block slots of the persistent 128 x 128 kernel on the current device: two
 // per CU, a multiple of 8 (one share per XCD), cached per device.
 static int gemm_slots() {
@@ -1634,6 +1784,9 @@ static hipError_t gemm_launch(const moe_config& c, const ET* A, const void* W, c
                                 EPI == EPI_NONE;
     const int64_t a_span = arows ? a_bytes : rows * (int64_t)K * 2;
     const int skip = kStreamEpi && a_span < ((int64_t)1 << 32) ? kStreamMaxRows : 0;
+    // a shared expert (the last group, nominally T rows) of up to
+    // kStreamSharedMaxRows rows is streamed too (at the DeepSeek-V3 shape,
+    // T = 4096 and K = 7168, faster than on the tiled kernels)
     const int skip_last =
         skip > 0 && G > E && c.tokens > skip && c.tokens <= kStreamSharedMaxRows ? kStreamSharedMaxRows
                                                                                   : skip;
@@ -1641,29 +1794,47 @@ static hipError_t gemm_launch(const moe_config& c, const ET* A, const void* W, c
       if (skip > 0) {
         constexpr int BNO = EPI == EPI_SWIGLU ? 128 : 256;
         // items: parts x N / BNO slabs, where the parts, ceil(r_g / 256) summed
-        // over the groups with r_g in (0, skip] rows, are at most
+        // over the groups taken (r_g in (0, skip]), are at most
         // (rows + 255 G) / 256 and at most ceil(skip / 256) G
+        // The work queue (see gemm_stream_kernel) where the routed groups
+        // average 512 rows or more (several parts per slab: the Mixtral shape,
+        // both GEMM stages 4-6 % faster, paired timing on one MI355X); the
+        // static order for fine-grained experts (the DeepSeek-V3 shape, whose
+        // many short items pay more for the queue's atomics than its balance
+        // gains: GEMM 2 stage 2-4 % slower with it).
+        int* sched = nullptr;
+        if ((int64_t)c.top_k * c.tokens >= (int64_t)512 * E) {
+          sched = stream_sched_slot();
+          if (!sched) return hipErrorInvalidSymbol;
+        }
         const int64_t parts = std::min<int64_t>((rows + (int64_t)(kStreamRows - 1) * G) / kStreamRows,
                                                 (int64_t)G * ((skip + kStreamRows - 1) / kStreamRows));
         const int64_t items = parts * (N / BNO);
         if (items > 0)
-        hipLaunchKernelGGL((gemm_stream_kernel<EPI, HB>), dim3((unsigned)items), dim3(256), 0, s, A,
-                           (const bf16*)W, (const bf16*)W3, bias, (const bf16*)Ws, (const bf16*)Ws3,
-                           bias_s, E, G, offsets, (int)rows, C, N, K, arows, (uint32_t)a_span, 0,
-                           skip, (const bf16*)wpacked);
-        // A shared expert (group E, nominally T rows) of more than kStreamMaxRows
-        // and at most kStreamSharedMaxRows rows: a streaming launch of its own,
-        // over group E alone (at most 16 parts of 256 rows per slab), in place of
-        // the tiled kernels (at the DeepSeek-V3 shape, T = 4096 and K = 7168:
-        // GEMM 1 stage 2.76 -> 2.69 ms, paired timing on one MI355X).
+          hipLaunchKernelGGL((gemm_stream_kernel<EPI, HB>), dim3((unsigned)items), dim3(256), 0, s,
+                             A, (const bf16*)W, (const bf16*)W3, bias, (const bf16*)Ws,
+                             (const bf16*)Ws3, bias_s, E, G, offsets, (int)rows, C, N, K, arows,
+                             (uint32_t)a_span, skip, 0, skip, (const bf16*)wpacked, sched);
+        // The shared expert (group E, nominally T rows) with more than skip and
+        // at most skip_last rows: a launch of its own over group E alone (at
+        // most 16 parts of 256 rows per slab), in place of the tiled kernels
+        // (at the DeepSeek-V3 shape, T = 4096 and K = 7168: GEMM 1 stage
+        // 2.76 -> 2.69 ms, paired timing on one MI355X). Separate rather than
+        // in the launch above: there the heavy shared items made GEMM 2 slower.
         if (skip_last > skip) {
+          int* sched2 = nullptr;
+          if (sched) {
+            sched2 = stream_sched_slot();
+            if (!sched2) return hipErrorInvalidSymbol;
+          }
           const size_t per_group = (size_t)(EPI == EPI_SWIGLU ? 2 : 1) * N * K;
           hipLaunchKernelGGL((gemm_stream_kernel<EPI, HB>),
                              dim3((unsigned)(kStreamSharedMaxRows / kStreamRows * (N / BNO))),
                              dim3(256), 0, s, A, (const bf16*)W, (const bf16*)W3, bias,
                              (const bf16*)Ws, (const bf16*)Ws3, bias_s, 0, 1, offsets + E,
-                             (int)rows, C, N, K, arows, (uint32_t)a_span, skip, skip_last,
-                             wpacked ? (const bf16*)wpacked + (size_t)E * per_group : nullptr);
+                             (int)rows, C, N, K, arows, (uint32_t)a_span, skip, skip, skip_last,
+                             wpacked ? (const bf16*)wpacked + (size_t)E * per_group : nullptr,
+                             sched2);
         }
       }
     }
