@@ -1889,8 +1889,9 @@ int router_kparts(const moe_config& c) {
   const int64_t tiles = (c.tokens + 127) / 128 * (c.num_experts / 128);
   const int nk = (int)(c.d_model / 64);
   int kp = 1;
-  // about 512 work items, each range at least 4 (even) K steps
-  while (tiles * kp * 2 <= 512 && nk % (kp * 2) == 0 && nk / (kp * 2) >= 4 &&
+  // about 256 work items (one per CU; 512 were 3 us slower at the DeepSeek-V3
+  // shape), each range at least 4 (even) K steps
+  while (tiles * kp * 2 <= 256 && nk % (kp * 2) == 0 && nk / (kp * 2) >= 4 &&
          (nk / (kp * 2)) % 2 == 0)
     kp *= 2;
   return kp;
