@@ -320,6 +320,10 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB float32 copy kernel (torch.neg) three times, "
                          "so that hardware byte counters can be scaled by a kernel of known traffic")
+    ap.add_argument("--only", choices=("train", "expert_choice"),
+                    help="measure only the training step or only expert-choice routing of "
+                         "--workload (after a short forward measurement that sets them up) and "
+                         "print that figure as a JSON line; for focused kernel traces")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the layer runs "
@@ -341,6 +345,14 @@ def main():
         del src, dst
 
     w = WORKLOADS[args.workload]
+    if args.only:
+        head, cfg, sets, ws = measure_forward(A, torch, w, args.sets, 2, 1)
+        if args.only == "train":
+            r = train_step(A, torch, w, cfg, sets, ws, args.steps, args.warmup, head["kept_rows"])
+        else:
+            r = expert_choice_step(A, torch, w, cfg, sets, args.steps, args.warmup)
+        print(json.dumps({"only": args.only, **r}), flush=True)
+        return
     head, cfg, sets, ws = measure_forward(A, torch, w, args.sets, args.steps, args.warmup)
     T, d, F, E, k = w.tokens, w.d_model, w.d_ff, w.num_experts, w.top_k
     result = {
