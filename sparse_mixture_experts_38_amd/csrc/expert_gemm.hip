@@ -1797,13 +1797,16 @@ static hipError_t gemm_launch(const moe_config& c, const ET* A, const void* W, c
         // over the groups taken (r_g in (0, skip]), are at most
         // (rows + 255 G) / 256 and at most ceil(skip / 256) G
         // The work queue (see gemm_stream_kernel) where the routed groups
-        // average 512 rows or more (several parts per slab: the Mixtral shape,
+        // average 512 to 1536 rows (several parts per slab: the Mixtral shape,
         // both GEMM stages 4-6 % faster, paired timing on one MI355X); the
         // static order for fine-grained experts (the DeepSeek-V3 shape, whose
         // many short items pay more for the queue's atomics than its balance
-        // gains: GEMM 2 stage 2-4 % slower with it).
+        // gains: GEMM 2 stage 2-4 % slower with it), and where the groups are
+        // expected to be too large for this kernel (an empty launch is cheaper
+        // without tickets).
         int* sched = nullptr;
-        if ((int64_t)c.top_k * c.tokens >= (int64_t)512 * E) {
+        const int64_t assigned = (int64_t)c.top_k * c.tokens;
+        if (assigned >= (int64_t)512 * E && assigned <= (int64_t)skip * E) {
           sched = stream_sched_slot();
           if (!sched) return hipErrorInvalidSymbol;
         }
