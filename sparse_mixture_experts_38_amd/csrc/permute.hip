@@ -74,9 +74,20 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(
   const int e = threadIdx.x;
   int pre = 0;
   if (e < E) {
-    for (int c = 0; c < chunks; ++c) {
-      chunk_base[(int64_t)c * E + e] = pre;
-      pre += chunk_hist[(int64_t)c * E + e];
+    // eight chunk counts loaded together per round, unconditionally (past the
+    // last chunk: the last one again, not added), so their round trips overlap
+    for (int c0 = 0; c0 < chunks; c0 += 8) {
+      int h[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        h[u] = chunk_hist[(int64_t)min(c0 + u, chunks - 1) * E + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (c0 + u < chunks) {
+          chunk_base[(int64_t)(c0 + u) * E + e] = pre;
+          pre += h[u];
+        }
+      }
     }
   }
   const int kept = (e < E) ? (cap < 0 ? pre : (int)((int64_t)pre < cap ? pre : cap)) : 0;
@@ -151,6 +162,32 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     *reinterpret_cast<uint4*>(dst + off) = *reinterpret_cast<const uint4*>(src + off);
 }
 
+// The maps alone (no row copy: the forward's GEMM 1 gathers the token rows
+// itself): one thread per assignment (and per shared-expert row).
+__global__ __launch_bounds__(256) void dispatch_maps_kernel(
+    const int32_t* __restrict__ topk_idx, int64_t T, int k, int E, int S, int64_t cap,
+    const int32_t* __restrict__ local_rank, const int32_t* __restrict__ chunk_base,
+    const int32_t* __restrict__ expert_offsets, int32_t* __restrict__ row_token,
+    int32_t* __restrict__ assign_row) {
+  const int64_t A = T * k;
+  const int64_t a = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (a < A) {
+    const int64_t j = a / T;
+    const int64_t t = a - j * T;
+    const int e = topk_idx[t * k + j];
+    int64_t row = -1;
+    if (e >= 0 && e < E) {
+      const int64_t pos = (int64_t)chunk_base[(a / kRankChunk) * E + e] + local_rank[a];
+      if (cap < 0 || pos < cap) row = (int64_t)expert_offsets[e] + pos;
+    }
+    assign_row[t * k + j] = (int32_t)row;
+    if (row >= 0) row_token[row] = (int32_t)t;
+  } else if (S && a < A + T) {
+    const int64_t t = a - A;
+    row_token[(int64_t)expert_offsets[E] + t] = (int32_t)t;
+  }
+}
+
 hipError_t launch_permute(const moe_config& c, const WsLayout& L, int64_t cap,
                           const int32_t* topk_idx, const void* x, int32_t* expert_offsets,
                           int32_t* row_token, int32_t* assign_row, void* x_perm, moe_stats* stats,
@@ -170,6 +207,12 @@ hipError_t launch_permute(const moe_config& c, const WsLayout& L, int64_t cap,
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int64_t waves = A + S * T;
+  if (!x_perm) {
+    hipLaunchKernelGGL(dispatch_maps_kernel, dim3((unsigned)((waves + 255) / 256)), dim3(256), 0, s,
+                       topk_idx, T, k, E, S, cap, local_rank, chunk_base, expert_offsets, row_token,
+                       assign_row);
+    return hipGetLastError();
+  }
   const unsigned blocks = (unsigned)((waves + 3) / 4);
   if (c.act_dtype == MOE_BF16)
     hipLaunchKernelGGL((dispatch_scatter_kernel<bf16>), dim3(blocks), dim3(256), 0, s, topk_idx,
