@@ -28,7 +28,13 @@
  *   - Pointers named x, w*, b*, logits, topk_*, expert_offsets, row_token,
  *     assign_row, x_perm, y_perm, y, stats and workspace are DEVICE pointers; cfg
  *     and the structs passed by pointer are HOST memory. The caller owns every
- *     buffer; the library allocates nothing and keeps no state between calls.
+ *     buffer; the library allocates nothing and keeps no state between calls,
+ *     except two kinds of static device memory per GPU, both reserved when the
+ *     library is loaded: the work-queue counters of the weight-streaming GEMM
+ *     (256 slots of 1 KB, taken in turn by its launches and left at zero by
+ *     each; calls on different streams may run at the same time as long as
+ *     fewer than 256 such launches are in flight at once) and the workspace of
+ *     moe_forward_noalloc.
  *   - stream is a hipStream_t passed as void*; NULL means the default stream.
  *     All device work is enqueued on it asynchronously; no entry point
  *     synchronises. Host-only helpers do no device work at all.
