@@ -663,8 +663,9 @@ def backward(x, params, w, dy, aux_coef: float = 0.0, z_coef: float = 0.0, fwd=N
 # READINGS: the score an expert ranks tokens by is the router logit (the page's
 # router(x) is the logit, as in its top-1 code), in float32; equal scores go to
 # the lower token index first; the weight of an expert's output for a token is
-# the softmax probability p[t, e] over experts (the token-choice gate p =
-# Softmax(h(x)) of MoE From Scratch to DeepSeek V3; there is no top-k set to
+# the router score: the softmax probability p[t, e] over experts (the
+# token-choice gate p = Softmax(h(x)) of MoE From Scratch to DeepSeek V3), or for
+# the sigmoid router the sigmoid score s[t, e] (there is no top-k set to
 # renormalise over); a token no expert picks gets zero (plus the shared expert);
 # C is the capacity rule of capacity() with k the average experts per token,
 # ceil(k T / E) when dropping is off, and never more than T; an expert's rows are
