@@ -243,42 +243,6 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(
 }
 
 // ------------------------------------------------------------------ transposes
-// Batched bf16 transpose in[b][M][N] -> out[b][n][col0 + m] (out rows of ldo
-// elements, so two matrices can be placed side by side) through a 64 x 64 LDS
-// tile (16-byte loads and stores; M and N multiples of 64).
-__global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16* __restrict__ in,
-                                                             bf16* __restrict__ out, int M, int N,
-                                                             int ldo, int col0) {
-  __shared__ uint16_t tile[64][66];
-  const int n0 = blockIdx.x * 64, m0 = blockIdx.y * 64;
-  const int64_t b = blockIdx.z;
-  const bf16* src = in + b * (int64_t)M * N;
-  bf16* dst = out + b * (int64_t)N * ldo + col0;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = (tid >> 3) + 32 * i, c = (tid & 7) * 8;
-    const uint4 u = *reinterpret_cast<const uint4*>(src + (int64_t)(m0 + r) * N + n0 + c);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      tile[r][c + 2 * e] = (uint16_t)(w[e] & 0xffffu);
-      tile[r][c + 2 * e + 1] = (uint16_t)(w[e] >> 16);
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = (tid >> 3) + 32 * i, c = (tid & 7) * 8;   // r: row of out (n), c: first m
-    uint4 u;
-    u.x = (uint32_t)tile[c + 0][r] | ((uint32_t)tile[c + 1][r] << 16);
-    u.y = (uint32_t)tile[c + 2][r] | ((uint32_t)tile[c + 3][r] << 16);
-    u.z = (uint32_t)tile[c + 4][r] | ((uint32_t)tile[c + 5][r] << 16);
-    u.w = (uint32_t)tile[c + 6][r] | ((uint32_t)tile[c + 7][r] << 16);
-    *reinterpret_cast<uint4*>(dst + (int64_t)(n0 + r) * ldo + m0 + c) = u;
-  }
-}
-
 // so[g]: expert_offsets clamped to [0, rows_max] and made non-decreasing, so the
 // groups' rows never sum past rows_max; po[g] = sum over g' < g of the padded
 // row count of group g' (its rows rounded up to a multiple of 128, at least
@@ -675,29 +639,11 @@ hipError_t launch_backward_misc(const moe_config& c, const BwdLayout& B, const v
   int32_t* po = (int32_t*)(ws + B.po);
   int32_t* so = po + (G + 1);
   if (phase == 0) {
-    // combine and router backward, weight transposes
+    // combine and router backward, padded offsets
     hipError_t e = launch_combine_backward(c, dy, sv.y_perm, r, dyp, dgate, s);
     if (e != hipSuccess) return e;
     e = launch_router_backward(c, r, stats, dgate, aux_coef, z_coef, dlogits, s);
     if (e != hipSuccess) return e;
-    // W2^T [E][F][d]; W1^T [E][d][F], for SwiGLU [W1^T | W3^T] as [E][d][2F]
-    const int NZ = c.activation == MOE_ACT_SWIGLU ? 2 : 1;
-    hipLaunchKernelGGL(transpose_bf16_kernel, dim3(F / 64, d / 64, E), dim3(256), 0, s,
-                       (const bf16*)w.w2, (bf16*)(ws + B.w2t), d, F, d, 0);
-    hipLaunchKernelGGL(transpose_bf16_kernel, dim3(d / 64, F / 64, E), dim3(256), 0, s,
-                       (const bf16*)w.w1, (bf16*)(ws + B.w1t), F, d, NZ * F, 0);
-    if (NZ == 2)
-      hipLaunchKernelGGL(transpose_bf16_kernel, dim3(d / 64, F / 64, E), dim3(256), 0, s,
-                         (const bf16*)w.w3, (bf16*)(ws + B.w1t), F, d, 2 * F, F);
-    if (S) {
-      hipLaunchKernelGGL(transpose_bf16_kernel, dim3(F / 64, d / 64, 1), dim3(256), 0, s,
-                         (const bf16*)w.ws2, (bf16*)(ws + B.ws2t), d, F, d, 0);
-      hipLaunchKernelGGL(transpose_bf16_kernel, dim3(d / 64, F / 64, 1), dim3(256), 0, s,
-                         (const bf16*)w.ws1, (bf16*)(ws + B.ws1t), F, d, NZ * F, 0);
-      if (NZ == 2)
-        hipLaunchKernelGGL(transpose_bf16_kernel, dim3(d / 64, F / 64, 1), dim3(256), 0, s,
-                           (const bf16*)w.ws3, (bf16*)(ws + B.ws1t), F, d, 2 * F, F);
-    }
     hipLaunchKernelGGL(pad_offsets_kernel, dim3(1), dim3(64), 0, s, r.expert_offsets, G, rmax, po,
                        so);
     return hipGetLastError();

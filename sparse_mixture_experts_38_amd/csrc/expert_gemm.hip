@@ -179,6 +179,20 @@ __device__ __forceinline__ float epilogue_bf16(float z1, float z3) {
   return z1;
 }
 
+// One 8-element K fragment of v_mfma_f32_32x32x16_bf16 read transposed out of
+// a row-major LDS tile: two ds_read_b64_tr_b16, the second 4 rows (1024 bytes)
+// after the first (lane layout: gemm_bf16_kernel's KMB note).
+__device__ __forceinline__ bf16x8 lds_tr_frag(const u32x4* smem, uint32_t byte) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  lds_s16x4* p = (lds_s16x4*)((__attribute__((address_space(3))) char*)smem + byte);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p);
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p + 128);
+  const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 // Grouped GEMM, C[r, n] = epi(sum_k A[r, k] W_g[n, k] + b_g[n]); group g < E
 // takes expert weights W + g N K, group E (shared expert) takes Ws.
 //
@@ -200,14 +214,28 @@ __device__ __forceinline__ float epilogue_bf16(float z1, float z3) {
 // segments. Blocks are dispatched to the 8 XCDs round-robin; the block id is
 // remapped so that each XCD runs a contiguous range of tiles, ordered in
 // groups of 8 M tiles, whose operands then meet in that XCD's L2.
-template <int EPI, bool HAS_BIAS>
+//
+// KMB (backward dZ and dX GEMMs): the weights are read as stored, K-major,
+//   C[r, n] = epi(sum_k A[r, k] W_g[k, n]),
+// W_g [K][N] at W + g ksplit N for K steps below ksplit and W3_g at
+// W3 + g ksplit N for the rest (SwiGLU's dX, K = 2F over [W1; W3]; ksplit = K
+// otherwise); the shared expert takes Ws / Ws3. The B part of a stage then
+// holds 64 K rows of 256 bytes (128 columns), 16-byte chunk c of row k at
+// c ^ 4 (k & 3), and each B fragment is two ds_read_b64_tr_b16: in each group
+// of 16 lanes, lane 4a + b receives element b of the 8-byte pieces addressed
+// by lanes a, a + 4, a + 8 and a + 12, so lane x addresses row x / 4 (of four
+// consecutive K rows) and columns 4 (x % 4) .. + 3 to receive four consecutive
+// K values of column x. The four rows of a 32-lane half land in four distinct
+// 64-byte bank groups.
+template <int EPI, bool HAS_BIAS, bool KMB = false>
 __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
     const bf16* __restrict__ A, const bf16* __restrict__ W, const bf16* __restrict__ W3,
     const float* __restrict__ bias, const bf16* __restrict__ Ws, const bf16* __restrict__ Ws3,
     const float* __restrict__ bias_s, int E, int G, const int32_t* __restrict__ offsets,
     int rows_max, void* __restrict__ Cv, int N, int K, int part, const int32_t* __restrict__ arows,
-    int kparts, const bf16* __restrict__ Zin, int skip_rows, int skip_last) {
+    int kparts, const bf16* __restrict__ Zin, int skip_rows, int skip_last, int ksplit) {
   constexpr bool GATED = EPI == EPI_SWIGLU;
+  static_assert(!KMB || (!GATED && EPI != EPI_PARTIAL), "K-major weights: ungated backward GEMMs");
   constexpr bool DACT = EPI == EPI_DGELU || EPI == EPI_DRELU;
   constexpr int BM = 128, BK = 64, CH = BK / 8;   // 8 chunks of 16 B per LDS row
   constexpr int NB = GATED ? 2 : 1;
@@ -288,11 +316,19 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
     row0 = __builtin_amdgcn_readfirstlane(row0);
     nrows = __builtin_amdgcn_readfirstlane(nrows);
     n0 = nt * BN;
-    Wg = g < E ? W + (int64_t)g * N * K : Ws;
-    W3g = GATED ? (g < E ? W3 + (int64_t)g * N * K : Ws3) : Wg;
-    bg = HAS_BIAS ? (g < E ? bias + (int64_t)g * N : bias_s) : nullptr;
-    b_s = reinterpret_cast<const char*>(Wg + (int64_t)n0 * K);
-    b3_s = GATED ? reinterpret_cast<const char*>(W3g + (int64_t)(n0 - BN) * K) : b_s;
+    if constexpr (KMB) {
+      Wg = g < E ? W + (int64_t)g * ksplit * N : Ws;
+      W3g = g < E ? (W3 ? W3 + (int64_t)g * ksplit * N : nullptr) : Ws3;
+      bg = HAS_BIAS ? (g < E ? bias + (int64_t)g * N : bias_s) : nullptr;
+      b_s = reinterpret_cast<const char*>(Wg + n0);
+      b3_s = W3g ? reinterpret_cast<const char*>(W3g + n0) : b_s;
+    } else {
+      Wg = g < E ? W + (int64_t)g * N * K : Ws;
+      W3g = GATED ? (g < E ? W3 + (int64_t)g * N * K : Ws3) : Wg;
+      bg = HAS_BIAS ? (g < E ? bias + (int64_t)g * N : bias_s) : nullptr;
+      b_s = reinterpret_cast<const char*>(Wg + (int64_t)n0 * K);
+      b3_s = GATED ? reinterpret_cast<const char*>(W3g + (int64_t)(n0 - BN) * K) : b_s;
+    }
     int rr[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -305,10 +341,16 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
     ar2 = reinterpret_cast<const char*>(a0 + (int64_t)rr[2] * K);
     ar3 = reinterpret_cast<const char*>(a0 + (int64_t)rr[3] * K);
   };
-  const uint32_t bo0 = (uint32_t)(lr * K + lc * 8) * 2u;
-  const uint32_t bo1 = bo0 + (uint32_t)(64 * K);    // + 32 rows
-  const uint32_t bo2 = bo0 + (uint32_t)(128 * K);
-  const uint32_t bo3 = bo0 + (uint32_t)(192 * K);
+  // B loads: K-major, thread t covers chunk t & 15 of K rows (t >> 4) + 16 i
+  // (byte offsets within one K step's 64 rows); else chunk t & 7 of rows
+  // (t >> 3) + 32 i of the [N][K] tile
+  const uint32_t bo0 = KMB ? (uint32_t)((tid >> 4) * N + (tid & 15) * 8) * 2u
+                           : (uint32_t)(lr * K + lc * 8) * 2u;
+  const uint32_t bstep = KMB ? (uint32_t)(32 * N) : (uint32_t)(64 * K);   // 16 / 32 rows
+  const uint32_t bo1 = bo0 + bstep;
+  const uint32_t bo2 = bo0 + 2 * bstep;
+  const uint32_t bo3 = bo0 + 3 * bstep;
+  const int wslot_b = BM * CH + (tid >> 4) * 16 + ((tid & 15) ^ (((tid >> 4) & 3) << 2));
 
   // LDS fragment rows: f = 0, 1 are A sub-tiles i = f; f = 2, 3 are B sub-tiles
   // jb = f - 2 (column block j of W, or W1 / W3 for SwiGLU).
@@ -325,6 +367,17 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
   int cidx[4];
 #pragma unroll
   for (int s4 = 0; s4 < 4; ++s4) cidx[s4] = (s4 * 2 + fk) ^ rsw;
+  // K-major B fragments (jb = 0, 1): byte offset in the stage of the lane's
+  // first transposed read (K rows 8 (lane / 32) + (lane % 16) / 4 of the
+  // sub-step; the second read is 4 rows on)
+  uint32_t toff[2];
+#pragma unroll
+  for (int jb = 0; jb < 2; ++jb) {
+    const int x = lane & 15, hq = (lane >> 4) & 1;
+    const int krow = 8 * fk + (x >> 2);
+    const int chunk = (wn * WN + jb * 32) / 8 + 2 * hq + ((x & 3) >> 1);
+    toff[jb] = (uint32_t)((BM * CH + krow * 16 + (chunk ^ ((krow & 3) << 2))) * 16 + (x & 1) * 8);
+  }
 
   // register stages for even / odd K steps (named registers, not arrays, so
   // that they stay in VGPRs)
@@ -341,25 +394,48 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
     if ((i) == 1) R.v1 = *reinterpret_cast<const u32x4*>(ar1 + kb_);                 \
     if ((i) == 2) R.v2 = *reinterpret_cast<const u32x4*>(ar2 + kb_);                 \
     if ((i) == 3) R.v3 = *reinterpret_cast<const u32x4*>(ar3 + kb_);                 \
-    if ((i) == 4) R.v4 = *reinterpret_cast<const u32x4*>(b_s + kb_ + bo0);           \
-    if ((i) == 5) R.v5 = *reinterpret_cast<const u32x4*>(b_s + kb_ + bo1);           \
-    if ((i) == 6) R.v6 = *reinterpret_cast<const u32x4*>(b3_s + kb_ + bo2);          \
-    if ((i) == 7) R.v7 = *reinterpret_cast<const u32x4*>(b3_s + kb_ + bo3);          \
+    if constexpr (KMB) {                                                             \
+      const int kg_ = (kbase + (kt)) * BK;                                           \
+      const char* bk_ = kg_ < ksplit ? b_s + (int64_t)kg_ * N * 2                    \
+                                     : b3_s + (int64_t)(kg_ - ksplit) * N * 2;       \
+      if ((i) == 4) R.v4 = *reinterpret_cast<const u32x4*>(bk_ + bo0);               \
+      if ((i) == 5) R.v5 = *reinterpret_cast<const u32x4*>(bk_ + bo1);               \
+      if ((i) == 6) R.v6 = *reinterpret_cast<const u32x4*>(bk_ + bo2);               \
+      if ((i) == 7) R.v7 = *reinterpret_cast<const u32x4*>(bk_ + bo3);               \
+    } else {                                                                         \
+      if ((i) == 4) R.v4 = *reinterpret_cast<const u32x4*>(b_s + kb_ + bo0);         \
+      if ((i) == 5) R.v5 = *reinterpret_cast<const u32x4*>(b_s + kb_ + bo1);         \
+      if ((i) == 6) R.v6 = *reinterpret_cast<const u32x4*>(b3_s + kb_ + bo2);        \
+      if ((i) == 7) R.v7 = *reinterpret_cast<const u32x4*>(b3_s + kb_ + bo3);        \
+    }                                                                                \
   } while (0)
 #define MOE_W(R, st, i)                                                              \
   do {                                                                               \
     u32x4* d_ = smem + (st) * STAGE + wslot;                                         \
+    u32x4* db_ = smem + (st) * STAGE + wslot_b;                                      \
     if ((i) == 0) d_[0] = R.v0;                                                      \
     if ((i) == 1) d_[32 * CH] = R.v1;                                                \
     if ((i) == 2) d_[64 * CH] = R.v2;                                                \
     if ((i) == 3) d_[96 * CH] = R.v3;                                                \
-    if ((i) == 4) d_[BM * CH] = R.v4;                                                \
-    if ((i) == 5) d_[(BM + 32) * CH] = R.v5;                                         \
-    if ((i) == 6) d_[(BM + 64) * CH] = R.v6;                                         \
-    if ((i) == 7) d_[(BM + 96) * CH] = R.v7;                                         \
+    if constexpr (KMB) {                                                             \
+      if ((i) == 4) db_[0] = R.v4;                                                   \
+      if ((i) == 5) db_[16 * 16] = R.v5;                                             \
+      if ((i) == 6) db_[32 * 16] = R.v6;                                             \
+      if ((i) == 7) db_[48 * 16] = R.v7;                                             \
+    } else {                                                                         \
+      if ((i) == 4) d_[BM * CH] = R.v4;                                              \
+      if ((i) == 5) d_[(BM + 32) * CH] = R.v5;                                       \
+      if ((i) == 6) d_[(BM + 64) * CH] = R.v6;                                       \
+      if ((i) == 7) d_[(BM + 96) * CH] = R.v7;                                       \
+    }                                                                                \
   } while (0)
 #define MOE_R(F, st, s4, f)                                                          \
-  F[f] = __builtin_bit_cast(bf16x8, smem[(st) * STAGE + fbase[f] + cidx[s4]])
+  do {                                                                               \
+    if (KMB && (f) >= 2)                                                             \
+      F[f] = lds_tr_frag(smem, (uint32_t)((st) * STAGE * 16 + (s4) * 4096) + toff[(f) & 1]); \
+    else                                                                             \
+      F[f] = __builtin_bit_cast(bf16x8, smem[(st) * STAGE + fbase[f] + cidx[s4]]);   \
+  } while (0)
 #define MOE_M(F, q)                                                                  \
   acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F[2 + ((q) >> 1)], F[(q) & 1], acc[q], 0, 0, 0)
   // One K step from LDS stage st: 16 MFMAs in four sub-steps, MFMA q taking
@@ -597,6 +673,10 @@ __global__ __launch_bounds__(256, 2) void gemm_wgrad_kernel(
   int cidx[4];
 #pragma unroll
   for (int s4 = 0; s4 < 4; ++s4) cidx[s4] = (s4 * 2 + fk) ^ rsw;
+  // both operands K-contiguous: the K-major path of the shared macros is off
+  constexpr bool KMB = false;
+  constexpr int ksplit = 0, wslot_b = 0;
+  constexpr uint32_t toff[2] = {0u, 0u};
   struct Regs { u32x4 v0, v1, v2, v3, v4, v5, v6, v7; };
   Regs r0, r1;
   bf16x8 fr0[4], fr1[4];
@@ -1753,12 +1833,16 @@ static int gemm_slots() {
   return cached[dev];
 }
 
-template <typename ET, int EPI, bool HB>
+// KMB: bf16 weights read K-major as stored ([K][N] per group, W3 / Ws3 for K
+// steps from ksplit on), on the 128 x 128 kernel only (backward dZ and dX).
+template <typename ET, int EPI, bool HB, bool KMB = false>
 static hipError_t gemm_launch(const moe_config& c, const ET* A, const void* W, const void* W3,
                               const float* bias, const void* Ws, const void* Ws3,
                               const float* bias_s, const int32_t* offsets, ET* C, int N, int K,
                               hipStream_t s, const int32_t* arows = nullptr,
-                              const bf16* zin = nullptr, const void* wpacked = nullptr) {
+                              const bf16* zin = nullptr, const void* wpacked = nullptr,
+                              int ksplit = 0) {
+  static_assert(!KMB || sizeof(ET) == 2, "K-major weights: bf16 only");
   const int E = c.num_experts, G = c.num_experts + c.num_shared_experts;
   const int64_t rows = rows_max(c);
   if constexpr (sizeof(ET) == 2) {
@@ -1780,8 +1864,8 @@ static hipError_t gemm_launch(const moe_config& c, const ET* A, const void* W, c
     // Groups of at most kStreamMaxRows rows go to the weight-streaming kernel
     // (forward epilogues; its A operand addressed with 32-bit byte offsets),
     // the others to the 256 x 256 and 128 x 128 kernels below.
-    constexpr bool kStreamEpi = EPI == EPI_GELU || EPI == EPI_RELU || EPI == EPI_SWIGLU ||
-                                EPI == EPI_NONE;
+    constexpr bool kStreamEpi = !KMB && (EPI == EPI_GELU || EPI == EPI_RELU ||
+                                         EPI == EPI_SWIGLU || EPI == EPI_NONE);
     const int64_t a_span = arows ? a_bytes : rows * (int64_t)K * 2;
     const int skip = kStreamEpi && a_span < ((int64_t)1 << 32) ? kStreamMaxRows : 0;
     // a shared expert (the last group, nominally T rows) of up to
@@ -1842,13 +1926,13 @@ static hipError_t gemm_launch(const moe_config& c, const ET* A, const void* W, c
       }
     }
     // (the backward epilogues EPI_DGELU / EPI_DRELU exist in the 128 x 128 kernel only)
-    const bool big = rows >= kGemmBigBM && EPI == EPI_NONE && N <= 4096 &&
+    const bool big = !KMB && rows >= kGemmBigBM && EPI == EPI_NONE && N <= 4096 &&
                      EPI != EPI_DGELU && EPI != EPI_DRELU && a_bytes < ((int64_t)1 << 32);
     if (big) {
       // full 256-row tiles of each group, then the rows left over (< 256 per
       // group) in 128-row tiles; both grids are bounds, surplus blocks exit
       const unsigned big_tiles = (unsigned)(rows / kGemmBigBM) * (unsigned)(N / BNB);
-      if constexpr (EPI != EPI_DGELU && EPI != EPI_DRELU)
+      if constexpr (EPI != EPI_DGELU && EPI != EPI_DRELU && !KMB)
         hipLaunchKernelGGL((gemm_bf16_big_kernel<EPI, HB>), dim3(big_tiles), dim3(256), 0, s, A,
                            (const bf16*)W, (const bf16*)W3, bias, (const bf16*)Ws, (const bf16*)Ws3,
                            bias_s, E, G, offsets, (int)rows, C, N, K, arows, (uint32_t)a_bytes,
@@ -1857,17 +1941,17 @@ static hipError_t gemm_launch(const moe_config& c, const ET* A, const void* W, c
       // tiles number at most ceil(rows / 128) + G
       const int64_t rest = (rows + 127) / 128 + G < 2 * G ? (rows + 127) / 128 + G : 2 * G;
       const int64_t rgrid = rest * (N / BN) < slots ? rest * (N / BN) : slots;
-      hipLaunchKernelGGL((gemm_bf16_kernel<EPI, HB>), dim3((unsigned)rgrid), dim3(256), 0, s, A,
+      hipLaunchKernelGGL((gemm_bf16_kernel<EPI, HB, KMB>), dim3((unsigned)rgrid), dim3(256), 0, s, A,
                          (const bf16*)W, (const bf16*)W3, bias, (const bf16*)Ws, (const bf16*)Ws3,
                          bias_s, E, G, offsets, (int)rows, C, N, K, 2, arows, 1, zin, skip,
-                         skip_last);
+                         skip_last, ksplit);
     } else {
       const int64_t tiles = ((rows + 127) / 128 + G) * (N / BN);
       const int64_t grid = tiles < slots ? tiles : slots;
-      hipLaunchKernelGGL((gemm_bf16_kernel<EPI, HB>), dim3((unsigned)grid), dim3(256), 0, s, A,
+      hipLaunchKernelGGL((gemm_bf16_kernel<EPI, HB, KMB>), dim3((unsigned)grid), dim3(256), 0, s, A,
                          (const bf16*)W, (const bf16*)W3, bias, (const bf16*)Ws, (const bf16*)Ws3,
                          bias_s, E, G, offsets, (int)rows, C, N, K, 0, arows, 1, zin, skip,
-                         skip_last);
+                         skip_last, ksplit);
     }
   } else {
     const unsigned mtiles = (unsigned)((rows + kGemmBM - 1) / kGemmBM) + G;
@@ -1930,7 +2014,7 @@ hipError_t launch_router_gemm(const moe_config& c, const void* x, const void* w_
                      (const bf16*)x, (const bf16*)w_gate, (const bf16*)nullptr, (const float*)nullptr,
                      (const bf16*)nullptr, (const bf16*)nullptr, (const float*)nullptr, 1, 1,
                      (const int32_t*)nullptr, (int)T, (void*)partials, E, K, 0,
-                     (const int32_t*)nullptr, kp, (const bf16*)nullptr, 0, 0);
+                     (const int32_t*)nullptr, kp, (const bf16*)nullptr, 0, 0, 0);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int64_t n4 = T * E / 4;
@@ -1986,21 +2070,23 @@ hipError_t launch_expert_down(const moe_config& c, const void* h, const int32_t*
 }
 
 // ------------------------------------------------------------------ backward
+// W2 [d][F] per group is the K-major B operand of dYp W2 (K = d, N = F).
 hipError_t launch_backward_dz(const moe_config& c, const void* dyp, const int32_t* offsets,
-                              const void* w2t, const void* ws2t, const void* z, void* dz,
+                              const void* w2, const void* ws2, const void* z, void* dz,
                               hipStream_t s) {
   const int N = (int)c.d_ff, K = (int)c.d_model;
   if (c.activation == MOE_ACT_GELU)
-    return gemm_launch<bf16, EPI_DGELU, false>(c, (const bf16*)dyp, w2t, nullptr, nullptr, ws2t,
-                                               nullptr, nullptr, offsets, (bf16*)dz, N, K, s,
-                                               nullptr, (const bf16*)z);
+    return gemm_launch<bf16, EPI_DGELU, false, true>(c, (const bf16*)dyp, w2, nullptr, nullptr, ws2,
+                                                     nullptr, nullptr, offsets, (bf16*)dz, N, K, s,
+                                                     nullptr, (const bf16*)z, nullptr, K);
   if (c.activation == MOE_ACT_RELU)
-    return gemm_launch<bf16, EPI_DRELU, false>(c, (const bf16*)dyp, w2t, nullptr, nullptr, ws2t,
-                                               nullptr, nullptr, offsets, (bf16*)dz, N, K, s,
-                                               nullptr, (const bf16*)z);
+    return gemm_launch<bf16, EPI_DRELU, false, true>(c, (const bf16*)dyp, w2, nullptr, nullptr, ws2,
+                                                     nullptr, nullptr, offsets, (bf16*)dz, N, K, s,
+                                                     nullptr, (const bf16*)z, nullptr, K);
   // SwiGLU: dH itself (the elementwise step forms dz1 and du)
-  return gemm_launch<bf16, EPI_NONE, false>(c, (const bf16*)dyp, w2t, nullptr, nullptr, ws2t,
-                                            nullptr, nullptr, offsets, (bf16*)dz, N, K, s);
+  return gemm_launch<bf16, EPI_NONE, false, true>(c, (const bf16*)dyp, w2, nullptr, nullptr, ws2,
+                                                  nullptr, nullptr, offsets, (bf16*)dz, N, K, s,
+                                                  nullptr, nullptr, nullptr, K);
 }
 
 hipError_t launch_linear_rows(const moe_config& c, const void* a, const int32_t* offsets,
@@ -2031,12 +2117,17 @@ hipError_t launch_expert_up_linear(const moe_config& c, const void* a, const int
                             (char*)z + (size_t)rows_max(c) * c.d_ff * es, N, K, s, arows);
 }
 
+// W1 [F][d] per group is the K-major B operand of dZ W1 (K = F, N = d); for
+// SwiGLU the K steps from F on take W3 (dZ = [dz1 | du]).
 hipError_t launch_backward_dx(const moe_config& c, const void* dz, const int32_t* offsets,
-                              const void* w1t, const void* ws1t, void* dxp, hipStream_t s) {
-  const int N = (int)c.d_model;
-  const int K = (int)c.d_ff * (c.activation == MOE_ACT_SWIGLU ? 2 : 1);
-  return gemm_launch<bf16, EPI_NONE, false>(c, (const bf16*)dz, w1t, nullptr, nullptr, ws1t, nullptr,
-                                            nullptr, offsets, (bf16*)dxp, N, K, s);
+                              const void* w1, const void* w3, const void* ws1, const void* ws3,
+                              void* dxp, hipStream_t s) {
+  const int N = (int)c.d_model, F = (int)c.d_ff;
+  const bool sw = c.activation == MOE_ACT_SWIGLU;
+  return gemm_launch<bf16, EPI_NONE, false, true>(c, (const bf16*)dz, w1, sw ? w3 : nullptr, nullptr,
+                                                  ws1, sw ? ws3 : nullptr, nullptr, offsets,
+                                                  (bf16*)dxp, N, sw ? 2 * F : F, s, nullptr, nullptr,
+                                                  nullptr, F);
 }
 
 size_t packed_weights_bytes(const moe_config& c, int which) {

@@ -67,10 +67,6 @@ BwdLayout backward_layout(const moe_config& c) {
   B.dgate = take((size_t)(T * k * 4));
   B.dlogits = take((size_t)(T * E * 4));
   const int64_t NZ = c.activation == MOE_ACT_SWIGLU ? 2 : 1;   // SwiGLU: [dz1 | du]
-  B.w1t = take((size_t)(E * d * NZ * F * 2));
-  B.w2t = take((size_t)E * F * d * 2);
-  B.ws1t = take((size_t)(S * d * NZ * F * 2));
-  B.ws2t = take((size_t)S * F * d * 2);
   B.dz = take((size_t)(rmax * NZ * F * 2));
   B.dh = take(NZ == 2 ? (size_t)(rmax * F * 2) : 0);
   B.dxp = take((size_t)(rmax * d * 2));
@@ -615,14 +611,15 @@ int moe_backward(const moe_config* cfg, const void* x, const moe_weights* w, con
   hipError_t e = launch_backward_misc(*cfg, B, x, *w, *r, stats, *saved, dy, aux_coef, z_coef, *g,
                                       ws, s, 0);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  e = launch_backward_dz(*cfg, ws + B.dyp, r->expert_offsets, ws + B.w2t, ws + B.ws2t, saved->z,
+  e = launch_backward_dz(*cfg, ws + B.dyp, r->expert_offsets, w->w2, w->ws2, saved->z,
                          ws + (swiglu ? B.dh : B.dz), s);
   if (e != hipSuccess) return MOE_ERR_HIP;
   if (swiglu) {
     e = launch_dswiglu(*cfg, ws + B.dh, saved->z, ws + B.dz, r->expert_offsets, s);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
-  e = launch_backward_dx(*cfg, ws + B.dz, r->expert_offsets, ws + B.w1t, ws + B.ws1t, ws + B.dxp, s);
+  e = launch_backward_dx(*cfg, ws + B.dz, r->expert_offsets, w->w1, w->w3, w->ws1, w->ws3,
+                         ws + B.dxp, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
   return hip_status(launch_backward_misc(*cfg, B, x, *w, *r, stats, *saved, dy, aux_coef, z_coef,
                                          *g, ws, s, 1));

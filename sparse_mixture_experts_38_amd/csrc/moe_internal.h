@@ -227,7 +227,7 @@ hipError_t launch_expert_choice_forward(const moe_config& c, const EcLayout& L, 
 // transposed, group-padded row buffers (each group's rows rounded up to a
 // multiple of 128, at least 128).
 struct BwdLayout {
-  size_t dyp, dgate, dlogits, w1t, w2t, ws1t, ws2t, dz, dh, dxp, po;   // po: padded then sanitized offsets
+  size_t dyp, dgate, dlogits, dz, dh, dxp, po;   // po: padded then sanitized offsets
   size_t dypT, hT, dzT, xT, colsum1, colsum2, gate_partial, total;
   int64_t ldk;
   int gate_slices, gate_slice_len;
@@ -261,25 +261,27 @@ hipError_t launch_backward_f32(const moe_config& c, const BwdLayout& B, const vo
                                const moe_saved& sv, const void* dy, float aux_coef, float z_coef,
                                const moe_grads& gr, char* ws, hipStream_t stream);
 // The non-GEMM steps of the backward: phase 0 (combine and router backward,
-// weight transposes, padded offsets) before the dZ / dX GEMMs, phase 1 (row
+// padded offsets) before the dZ / dX GEMMs, phase 1 (row
 // transposes, weight, bias and router gradients, dx) after them.
 hipError_t launch_backward_misc(const moe_config& c, const BwdLayout& B, const void* x,
                                 const moe_weights& w, const moe_routing& r, const moe_stats* stats,
                                 const moe_saved& sv, const void* dy, float aux_coef, float z_coef,
                                 const moe_grads& gr, char* ws, hipStream_t stream, int phase);
 
-// dZ = (dYp W2) * act'(z) per group: dYp [rows][d], w2t [E][F][d] (W2 transposed),
-// ws2t [F][d] (shared expert), z and dZ [rows][F] bf16 (GELU, ReLU); for SwiGLU the
-// product dH = dYp W2 alone, which launch_dswiglu turns into dZ = [dz1 | du].
+// dZ = (dYp W2) * act'(z) per group: dYp [rows][d], W2 [E][d][F] and Ws2 [d][F]
+// (the shared expert) as stored, z and dZ [rows][F] bf16 (GELU, ReLU); for
+// SwiGLU the product dH = dYp W2 alone, which launch_dswiglu turns into
+// dZ = [dz1 | du].
 hipError_t launch_backward_dz(const moe_config& c, const void* dyp, const int32_t* expert_offsets,
-                              const void* w2t, const void* ws2t, const void* z, void* dz,
+                              const void* w2, const void* ws2, const void* z, void* dz,
                               hipStream_t stream);
-// dXp = dZ W1 per group: w1t [E][d][F] (W1 transposed; SwiGLU: [W1^T | W3^T], K = 2F),
-// ws1t [d][F] (or [d][2F]); dXp [rows][d] bf16.
+// dXp = dZ W1 per group (SwiGLU: [dz1 | du] [W1; W3], K = 2F): W1, W3 [E][F][d]
+// and Ws1, Ws3 [F][d] as stored; dXp [rows][d] bf16.
 hipError_t launch_dswiglu(const moe_config& c, const void* dh, const void* z, void* dz,
                           const int32_t* expert_offsets, hipStream_t stream);
 hipError_t launch_backward_dx(const moe_config& c, const void* dz, const int32_t* expert_offsets,
-                              const void* w1t, const void* ws1t, void* dxp, hipStream_t stream);
+                              const void* w1, const void* w3, const void* ws1, const void* ws3,
+                              void* dxp, hipStream_t stream);
 // Ragged-K grouped weight gradient C_g = A[:, po[g]:po[g+1]] B[:, po[g]:po[g+1]]^T,
 // A [M][ldk], B [N][ldk] bf16; C float32 [E][M][N], Cs [M][N] for group E.
 hipError_t launch_wgrad(const void* a, const void* b, const int32_t* po, int G, int E, int M, int N,
