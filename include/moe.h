@@ -482,6 +482,8 @@ typedef struct moe_saved {
   void* z;      /* [T k + S T, F] act_dtype: W1 x + b1 per expert-sorted row;
                    SwiGLU: [2, T k + S T, F], the planes W1 x + b1 and W3 x       */
   void* y_perm; /* [T k + S T, d] act_dtype: the expert outputs E_e(x) per row  */
+  void* h;      /* [T k + S T, F] act_dtype: act(z) per row (SwiGLU: silu(z1) u),
+                   the input of the second expert GEMM                           */
 } moe_saved;
 
 /* Gradients written by moe_backward (device buffers; float32 except dx). Every
@@ -506,10 +508,11 @@ typedef struct moe_grads {
 
 /*
  * The layer forward of moe_forward that also keeps what the backward needs:
- * routing->logits (required here) and saved->z, saved->y_perm. The expert
- * activation is applied to z after its rounding to act_dtype, so the backward
- * recomputes exactly the h the second GEMM used (SwiGLU: h = silu(z1) u from the
- * two rounded planes). Same arguments and workspace as moe_forward.
+ * routing->logits (required here) and saved->z, saved->y_perm, saved->h (every
+ * saved buffer required). The expert activation is applied to z after its
+ * rounding to act_dtype and h is kept as rounded, so the backward uses exactly
+ * the h the second GEMM read (SwiGLU: h = silu(z1) u from the two rounded
+ * planes). Same arguments and workspace as moe_forward.
  */
 int moe_forward_train(const moe_config* cfg, const void* x, const moe_weights* w, void* y,
                       const moe_routing* routing, moe_stats* stats, const moe_saved* saved,

@@ -52,7 +52,7 @@ class MoeEcRouting(ctypes.Structure):
 
 
 class MoeSaved(ctypes.Structure):
-    _fields_ = [(n, c_void_p) for n in ("z", "y_perm")]
+    _fields_ = [(n, c_void_p) for n in ("z", "y_perm", "h")]
 
 
 class MoeGrads(ctypes.Structure):
@@ -552,10 +552,11 @@ def _need_saved(cfg, saved):
     zshape = (2, rows, F) if cfg.activation == ACTIVATION["swiglu"] else (rows, F)
     _need(saved.get("z"), "saved z", zshape, act)
     _need(saved.get("y_perm"), "saved y_perm", (rows, d), act)
+    _need(saved.get("h"), "saved h", (rows, F), act)
 
 
 def forward_train(cfg, x, weights, y, routing, stats, saved, workspace):
-    """moe_forward_train: the forward that also keeps logits, z and y_perm."""
+    """moe_forward_train: the forward that also keeps logits, z, y_perm and h."""
     T, d, F, E, k, S, act, rdt = _sizes(cfg)
     _need(x, "x", (T, d), act)
     _need(y, "y", (T, d), act)
@@ -627,7 +628,8 @@ def alloc_saved(cfg, device="cuda") -> Dict[str, torch.Tensor]:
     rows = T * k + S * T
     zshape = (2, rows, F) if cfg.activation == ACTIVATION["swiglu"] else (rows, F)
     return dict(z=torch.empty(*zshape, dtype=act, device=device),
-                y_perm=torch.empty(rows, d, dtype=act, device=device))
+                y_perm=torch.empty(rows, d, dtype=act, device=device),
+                h=torch.empty(rows, F, dtype=act, device=device))
 
 
 def alloc_grads(cfg, device="cuda") -> Dict[str, Optional[torch.Tensor]]:

@@ -242,7 +242,7 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(
   }
 }
 
-// ------------------------------------------------------------------ transposes
+// ------------------------------------------------------------------ weight and bias gradients
 // so[g]: expert_offsets clamped to [0, rows_max] and made non-decreasing, so the
 // groups' rows never sum past rows_max; po[g] = sum over g' < g of the padded
 // row count of group g' (its rows rounded up to a multiple of 128, at least
@@ -265,72 +265,72 @@ __global__ void pad_offsets_kernel(const int32_t* __restrict__ off, int G, int64
   }
 }
 
-// Expert-sorted rows -> transposed, group-padded layout for the weight
-// gradient: out[c][k] for k in group g's padded range [po[g], po[g+1]) holds
-// row r = so[g] + (k - po[g]) of the source (zero past the group's rows; so
-// and po as written by pad_offsets_kernel).
-// MODE 0: rows of src [rows][C]; MODE 1: token rows of src (x [T][C]) through
-// row_token; MODE 2: act(src) (src = z, the saved pre-activation); MODE 3:
-// silu(src) src2 (SwiGLU, src = z1, src2 = u). With
-// partial != nullptr also writes the 64-row column sums of the (bf16) values
-// of its block to partial[k / 64][c] (bias gradients).
-template <int MODE>
-__global__ __launch_bounds__(256) void transpose_rows_kernel(
-    const bf16* __restrict__ src, const bf16* __restrict__ src2, const int32_t* __restrict__ row_token,
-    const int32_t* __restrict__ so, const int32_t* __restrict__ po, int G, int64_t src_rows, int C,
-    int ldk, int act, bf16* __restrict__ out, float* __restrict__ partial) {
-  __shared__ float tile[64][65];
+// xp[r] = x[row_token[r]] for the kept rows r < so[G] (the expert-sorted copy of
+// the token rows that the weight gradient of W1 / W3 reads; row_token clamped to
+// [0, T)). 16 bytes per thread.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const bf16* __restrict__ x,
+                                                          const int32_t* __restrict__ row_token,
+                                                          const int32_t* __restrict__ so, int G,
+                                                          int64_t T, int d, bf16* __restrict__ xp) {
+  const int64_t R = so[G];
+  const int c8 = d / 8;
+  const int64_t n = R * c8;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / c8;
+    const int c = (int)(i - r * c8) * 8;
+    int64_t t = row_token[r];
+    t = t < 0 ? 0 : (t >= T ? T - 1 : t);
+    *reinterpret_cast<uint4*>(xp + r * d + c) = *reinterpret_cast<const uint4*>(x + t * d + c);
+  }
+}
+
+// Column sums of the expert-sorted rows of src ([rows][ld], columns 0..C-1)
+// for the bias gradients, in blocks of 64 rows of the padded row space (so and
+// po as written by pad_offsets_kernel): block (kb, cs) adds the rows
+// so[g] + k - po[g] of its group g for k in [64 kb, 64 kb + 64) that lie inside
+// the group, over columns 512 cs .. + 511, and writes partial[kb][c]. Thread:
+// 8 columns, one of 4 row lanes (16 rows each, in order); the 4 lanes are then
+// added in order (deterministic).
+__global__ __launch_bounds__(256) void colsum_rows_kernel(const bf16* __restrict__ src, int ld,
+                                                          int C, const int32_t* __restrict__ so,
+                                                          const int32_t* __restrict__ po, int G,
+                                                          float* __restrict__ partial) {
+  __shared__ float red[4][512];
   const int k0 = blockIdx.x * 64;
-  const int c0 = blockIdx.y * 64;
   if (k0 >= po[G]) return;
-  int lo = 0, hi = G;   // group of column k0: po[lo] <= k0 < po[lo + 1]
+  int lo = 0, hi = G;   // group of row k0: po[lo] <= k0 < po[lo + 1]
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
     if (po[mid] <= k0) lo = mid; else hi = mid;
   }
   const int g = lo;
-  const int gs = so[g];
-  const int R = so[g + 1] - gs;
-  const int tid = threadIdx.x;
+  const int local = k0 - po[g];
+  const int nr = so[g + 1] - so[g];
+  const int rl = threadIdx.x >> 6;
+  const int cl = (threadIdx.x & 63) * 8;
+  const int c = blockIdx.y * 512 + cl;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (c < C) {
+    for (int j = 0; j < 16; ++j) {
+      const int lr = local + rl * 16 + j;
+      if (lr >= nr) break;
+      float v[8];
+      load8(src + (int64_t)(so[g] + lr) * ld + c, v);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int kk = (tid >> 3) + 32 * i, c = (tid & 7) * 8;
-    const int local = k0 + kk - po[g];
-    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (local < R) {
-      int64_t row = gs + local;
-      if (MODE == 1) {
-        row = row_token[row];
-        row = row < 0 ? 0 : (row >= src_rows ? src_rows - 1 : row);
-      }
-      load8(src + row * C + c0 + c, v);
-      if (MODE == 2) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = bf16_bits_to_f32(f32_to_bf16_bits(act_bf16(act, v[e])));
-      }
-      if (MODE == 3) {
-        float w[8];
-        load8(src2 + row * C + c0 + c, w);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = bf16_bits_to_f32(f32_to_bf16_bits(swiglu_h(v[e], w[e])));
-      }
+      for (int e = 0; e < 8; ++e) acc[e] += v[e];
     }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) tile[kk][c + e] = v[e];
   }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[rl][cl + e] = acc[e];
   __syncthreads();
+  const int t = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = (tid >> 3) + 32 * i, kc = (tid & 7) * 8;   // r: column of src, kc: first k
-    float v[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = tile[kc + e][r];
-    store8(out + (int64_t)(c0 + r) * ldk + k0 + kc, v);
-  }
-  if (partial && tid < 64) {
-    float sum = 0.f;
-    for (int kk = 0; kk < 64; ++kk) sum += tile[kk][tid];
-    partial[(int64_t)blockIdx.x * C + c0 + tid] = sum;
+  for (int h = 0; h < 2; ++h) {
+    const int cc = t + 256 * h;
+    const int col = blockIdx.y * 512 + cc;
+    if (col < C)
+      partial[(int64_t)blockIdx.x * C + col] = ((red[0][cc] + red[1][cc]) + red[2][cc]) + red[3][cc];
   }
 }
 
@@ -648,52 +648,40 @@ hipError_t launch_backward_misc(const moe_config& c, const BwdLayout& B, const v
                        so);
     return hipGetLastError();
   }
-  // phase 1 (after the dZ and dX GEMMs): transposed row buffers, weight
-  // gradients, bias gradients, router weights, dx
-  const int ldk = (int)B.ldk;
+  // phase 1 (after the dZ and dX GEMMs): weight gradients from the row buffers
+  // (expert-sorted x rows gathered first), bias gradients, router weights, dx
   const unsigned kb = (unsigned)(B.ldk / 64);
-  const bool bias = c.has_bias;
-  float* p2 = bias ? (float*)(ws + B.colsum2) : nullptr;
-  float* p1 = bias ? (float*)(ws + B.colsum1) : nullptr;
   const bool sw = c.activation == MOE_ACT_SWIGLU;
   const int NZ = sw ? 2 : 1;   // dZ = [dz1 | du] for SwiGLU
-  const bf16* z1 = (const bf16*)sv.z;
-  const bf16* u = sw ? z1 + rmax * F : nullptr;
-  hipLaunchKernelGGL((transpose_rows_kernel<0>), dim3(kb, d / 64), dim3(256), 0, s,
-                     (const bf16*)dyp, (const bf16*)nullptr, (const int32_t*)nullptr,
-                     (const int32_t*)so, po, G, rmax, d, ldk, c.activation, (bf16*)(ws + B.dypT),
-                     p2);
-  if (sw)
-    hipLaunchKernelGGL((transpose_rows_kernel<3>), dim3(kb, F / 64), dim3(256), 0, s, z1, u,
-                       (const int32_t*)nullptr, (const int32_t*)so, po, G, rmax, F, ldk,
-                       c.activation, (bf16*)(ws + B.hT), (float*)nullptr);
-  else
-    hipLaunchKernelGGL((transpose_rows_kernel<2>), dim3(kb, F / 64), dim3(256), 0, s, z1,
-                       (const bf16*)nullptr, (const int32_t*)nullptr, (const int32_t*)so, po, G, rmax,
-                       F, ldk, c.activation, (bf16*)(ws + B.hT), (float*)nullptr);
-  hipLaunchKernelGGL((transpose_rows_kernel<0>), dim3(kb, NZ * F / 64), dim3(256), 0, s,
-                     (const bf16*)(ws + B.dz), (const bf16*)nullptr, (const int32_t*)nullptr,
-                     (const int32_t*)so, po, G, rmax, NZ * F, ldk, c.activation,
-                     (bf16*)(ws + B.dzT), p1);
-  hipLaunchKernelGGL((transpose_rows_kernel<1>), dim3(kb, d / 64), dim3(256), 0, s, (const bf16*)x,
-                     (const bf16*)nullptr, r.row_token, (const int32_t*)so, po, G, T, d, ldk,
-                     c.activation, (bf16*)(ws + B.xT), (float*)nullptr);
-  hipError_t e = launch_wgrad(ws + B.dypT, ws + B.hT, po, G, E, d, F, ldk, gr.dw2, gr.dws2, s);
+  const bf16* dz = (const bf16*)(ws + B.dz);
+  bf16* xp = (bf16*)(ws + B.xp);
+  {
+    const int64_t n = rmax * (d / 8);
+    const int64_t blocks = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
+    hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)(blocks > 0 ? blocks : 1)), dim3(256), 0, s,
+                       (const bf16*)x, r.row_token, (const int32_t*)so, G, T, d, xp);
+  }
+  // dW2 = dYp^T H, dW1 = dz1^T Xp (dW3 = du^T Xp)
+  hipError_t e = launch_wgrad(dyp, d, sv.h, F, so, G, E, d, F, gr.dw2, gr.dws2, s);
   if (e != hipSuccess) return e;
-  e = launch_wgrad(ws + B.dzT, ws + B.xT, po, G, E, F, d, ldk, gr.dw1, gr.dws1, s);
+  e = launch_wgrad(dz, NZ * F, xp, d, so, G, E, F, d, gr.dw1, gr.dws1, s);
   if (e != hipSuccess) return e;
   if (sw) {
-    // dW3 from the du rows of dZ^T
-    e = launch_wgrad(ws + B.dzT + (size_t)F * ldk * 2, ws + B.xT, po, G, E, F, d, ldk, gr.dw3,
-                     gr.dws3, s);
+    e = launch_wgrad(dz + F, 2 * F, xp, d, so, G, E, F, d, gr.dw3, gr.dws3, s);
     if (e != hipSuccess) return e;
   }
-  if (bias) {
+  if (c.has_bias) {
+    float* p2 = (float*)(ws + B.colsum2);
+    float* p1 = (float*)(ws + B.colsum1);
+    hipLaunchKernelGGL(colsum_rows_kernel, dim3(kb, (d + 511) / 512), dim3(256), 0, s,
+                       (const bf16*)dyp, d, d, (const int32_t*)so, (const int32_t*)po, G, p2);
     hipLaunchKernelGGL(colsum_reduce_kernel, dim3((d + 255) / 256, G), dim3(256), 0, s,
                        (const float*)p2, d, (const int32_t*)po, d, E, gr.db2, gr.dbs2);
     // b1 sits on W1 only: the dz1 columns
+    hipLaunchKernelGGL(colsum_rows_kernel, dim3(kb, (F + 511) / 512), dim3(256), 0, s, dz, NZ * F,
+                       F, (const int32_t*)so, (const int32_t*)po, G, p1);
     hipLaunchKernelGGL(colsum_reduce_kernel, dim3((F + 255) / 256, G), dim3(256), 0, s,
-                       (const float*)p1, NZ * F, (const int32_t*)po, F, E, gr.db1, gr.dbs1);
+                       (const float*)p1, F, (const int32_t*)po, F, E, gr.db1, gr.dbs1);
   }
   hipLaunchKernelGGL(gate_wgrad_kernel, dim3((E + 7) / 8, (d + 1023) / 1024, B.gate_slices), dim3(256), 0, s,
                      (const bf16*)x, (const float*)dlogits, T, d, E, (int)B.gate_slice_len,

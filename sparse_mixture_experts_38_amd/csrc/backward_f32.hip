@@ -169,7 +169,6 @@ BwdLayout backward_layout_f32(const moe_config& c) {
   B.dlogits = take((size_t)(T * c.num_experts * 4));
   B.dz = take((size_t)(rmax * NZ * F * 4));
   B.dh = take(NZ == 2 ? (size_t)(rmax * F * 4) : 0);
-  B.hT = take((size_t)(rmax * F * 4));   // h = act(z), row-major (not transposed here)
   B.dxp = take((size_t)(rmax * d * 4));
   B.total = off;
   return B;
@@ -188,7 +187,7 @@ hipError_t launch_backward_f32(const moe_config& c, const BwdLayout& B, const vo
   float* dgate = (float*)(ws + B.dgate);
   float* dlogits = (float*)(ws + B.dlogits);
   float* dz = (float*)(ws + B.dz);
-  float* h = (float*)(ws + B.hT);
+  const float* h = (const float*)sv.h;   // act(z) as the training forward kept it
   float* dxp = (float*)(ws + B.dxp);
   const float* z1 = (const float*)sv.z;
   const float* u = sw ? z1 + rmax * F : nullptr;
@@ -196,8 +195,6 @@ hipError_t launch_backward_f32(const moe_config& c, const BwdLayout& B, const vo
   hipError_t e = launch_combine_backward(c, dy, sv.y_perm, r, dyp, dgate, s);
   if (e != hipSuccess) return e;
   e = launch_router_backward(c, r, stats, dgate, aux_coef, z_coef, dlogits, s);
-  if (e != hipSuccess) return e;
-  e = launch_act_rows_f32(c, sv.z, off, h, s);
   if (e != hipSuccess) return e;
   const unsigned rows = (unsigned)(rmax > 0 ? rmax : 1);
   // dZ (GELU, ReLU: the activation derivative applied in the product's epilogue)

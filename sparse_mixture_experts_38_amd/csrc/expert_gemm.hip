@@ -608,23 +608,36 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
   }
 }
 
-// Weight-gradient GEMM with a ragged K range per group (backward pass): for
-// group g,
-//   C_g[m, n] = sum over k in [po[g], po[g + 1]) of A[m, k] B[n, k],
-// A [M][ldk] and B [N][ldk] bf16 hold the expert-sorted row buffers transposed,
-// each group's rows padded with zeros to a multiple of 128 columns (at least
-// 128), so every K range is a whole, even number of 64-deep steps. C_g is
-// float32 [M][N] at C + g M N for a routed expert (g < E) and Cs for the shared
-// expert (g == E). Same 128 x 128 tile, LDS layout, fragment order and two-step
-// register pipeline as gemm_bf16_kernel (its macros), one tile per block; the
-// XCD-aware order keeps a group's tiles on one XCD in groups of 8 M tiles.
-// Requires M, N multiples of 128 and 256 ldk < 2^31 (checked by the host).
-__global__ __launch_bounds__(256, 2) void gemm_wgrad_kernel(
-    const bf16* __restrict__ A, const bf16* __restrict__ B, const int32_t* __restrict__ po, int G,
-    int E, int M, int N, int ldk, float* __restrict__ C, float* __restrict__ Cs) {
-  constexpr int BM = 128, BN = 128, BK = 64, CH = BK / 8;
-  constexpr int WN = BN / 2, TM = 2, TN = WN / 32;
-  constexpr int ROWS = BM + BN, STAGE = ROWS * CH, GROUP_M = 8;
+#undef MOE_SB
+#undef MOE_G
+#undef MOE_W
+#undef MOE_R
+#undef MOE_M
+#undef MOE_STEP
+
+// Weight gradient straight from the expert-sorted row buffers (backward pass):
+// for group g,
+//   C_g[m, n] = sum over rows r in [so[g], so[g + 1]) of A[r, m] B[r, n],
+// A [rows][lda] and B [rows][ldb] bf16 row-major, C_g float32 [M][N] at
+// C + g M N for a routed expert (g < E) and Cs for the shared expert (g == E).
+// Both operands are K-major (K runs over rows), so a stage holds two tiles of
+// 64 rows x 128 columns (A's, then B's), 16-byte chunk c of row k at
+// c ^ 4 (k & 3), and every MFMA fragment is two ds_read_b64_tr_b16
+// (lds_tr_frag; lane layout in gemm_bf16_kernel's KMB note). Rows past the
+// group's end are loaded as zeros (buffer loads range-checked against the
+// group's rows) and an empty group yields C_g = 0. 128 x 128 tile, four
+// waves of 64 x 64, K step 64 with the next two steps in registers, one tile per
+// block, the B fragment first in each MFMA so that a lane's accumulators hold
+// four consecutive columns n; XCD-aware tile order (a group's tiles in groups of
+// 8 M tiles on one XCD). Requires M, N multiples of 128 and lda, ldb < 2^24.
+__global__ __launch_bounds__(256, 2) void gemm_wgrad_tn_kernel(
+    const bf16* __restrict__ A, int lda, const bf16* __restrict__ B, int ldb,
+    const int32_t* __restrict__ so, int G, int E, int M, int N, float* __restrict__ C,
+    float* __restrict__ Cs) {
+  constexpr int BM = 128, BN = 128, BK = 64, TC = 16;   // 16 chunks of 16 B per LDS row
+  constexpr int HALF = BK * TC;                          // chunks of one operand tile
+  constexpr int STAGE = 2 * HALF;                        // 32 KB
+  constexpr int GROUP_M = 8;
   __shared__ u32x4 smem[2 * STAGE];
   const int mtn = M / BM, ntn = N / BN, per = mtn * ntn;
   const int tiles = G * per;
@@ -638,89 +651,158 @@ __global__ __launch_bounds__(256, 2) void gemm_wgrad_kernel(
   const int first_m = grp * GROUP_M;
   const int gm = min(mtn - first_m, GROUP_M);
   const int in2 = in - grp * GROUP_M * ntn;
-  const int row0 = (first_m + in2 % gm) * BM;
+  const int m0 = (first_m + in2 % gm) * BM;
   const int n0 = (in2 / gm) * BN;
-  const int kbase = po[g] / BK;
-  const int len = (po[g + 1] - po[g]) / BK;   // even, >= 2
+  // uniform over the block: scalar registers (the buffer descriptors below
+  // must be scalar)
+  const int r0 = __builtin_amdgcn_readfirstlane(so[g]);
+  const int nr = __builtin_amdgcn_readfirstlane(so[g + 1]) - r0;   // the group's rows
+  int len = (nr + BK - 1) / BK;   // K steps, made even and at least 2
+  len = len < 2 ? 2 : (len + 1) & ~1;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int fr = lane & 31;
   const int fk = lane >> 5;
-  const int lr = tid >> 3;
-  const int lc = tid & 7;
-  const int wslot = lr * CH + (lc ^ ((tid >> 4) & 7));
-  const int rsw = (fr >> 1) & 7;
-  const bf16* a0 = A + lc * 8;
-  const char* ar0 = reinterpret_cast<const char*>(a0 + (int64_t)(row0 + lr) * ldk);
-  const char* ar1 = reinterpret_cast<const char*>(a0 + (int64_t)(row0 + lr + 32) * ldk);
-  const char* ar2 = reinterpret_cast<const char*>(a0 + (int64_t)(row0 + lr + 64) * ldk);
-  const char* ar3 = reinterpret_cast<const char*>(a0 + (int64_t)(row0 + lr + 96) * ldk);
-  const char* b_s = reinterpret_cast<const char*>(B + (int64_t)n0 * ldk);
-  const char* b3_s = b_s;
-  const uint32_t bo0 = (uint32_t)(lr * ldk + lc * 8) * 2u;
-  const uint32_t bo1 = bo0 + (uint32_t)(64 * ldk);
-  const uint32_t bo2 = bo0 + (uint32_t)(128 * ldk);
-  const uint32_t bo3 = bo0 + (uint32_t)(192 * ldk);
-  int fbase[4];
+  // loads: thread t covers chunk t & 15 of rows (t >> 4) + 16 i, i = 0..3, of
+  // both tiles
+  const int lr = tid >> 4;
+  const int lc = tid & 15;
+  const int wslot = lr * TC + (lc ^ ((lr & 3) << 2));
+  const uint32_t ao = (uint32_t)(lr * lda + m0 + lc * 8) * 2u;   // within a step's rows
+  const uint32_t bo = (uint32_t)(lr * ldb + n0 + lc * 8) * 2u;
+  const uint32_t astep = (uint32_t)(32 * lda), bstep = (uint32_t)(32 * ldb);   // 16 rows
+  // fragment byte offsets in a stage (sub-tile j of the wave's A / B columns;
+  // + 4096 per 16-row sub-step)
+  uint32_t fa[2], fb[2];
 #pragma unroll
-  for (int f = 0; f < 4; ++f) {
-    const int row = f < 2 ? wm * 64 + f * 32 + fr : BM + wn * WN + (f - 2) * 32 + fr;
-    fbase[f] = row * CH;
+  for (int j = 0; j < 2; ++j) {
+    const int x = lane & 15, hq = (lane >> 4) & 1;
+    const int krow = 8 * fk + (x >> 2);
+    const int sw = (krow & 3) << 2;
+    const int ca = (wm * 64 + j * 32) / 8 + 2 * hq + ((x & 3) >> 1);
+    const int cb = (wn * 64 + j * 32) / 8 + 2 * hq + ((x & 3) >> 1);
+    fa[j] = (uint32_t)((krow * TC + (ca ^ sw)) * 16 + (x & 1) * 8);
+    fb[j] = (uint32_t)((HALF + krow * TC + (cb ^ sw)) * 16 + (x & 1) * 8);
   }
-  constexpr int kRO[4] = {0, 2, 1, 3};
-  int cidx[4];
-#pragma unroll
-  for (int s4 = 0; s4 < 4; ++s4) cidx[s4] = (s4 * 2 + fk) ^ rsw;
-  // both operands K-contiguous: the K-major path of the shared macros is off
-  constexpr bool KMB = false;
-  constexpr int ksplit = 0, wslot_b = 0;
-  constexpr uint32_t toff[2] = {0u, 0u};
+  constexpr int kRO[4] = {0, 2, 1, 3};   // fragment read order: A0 B0 A1 B1
   struct Regs { u32x4 v0, v1, v2, v3, v4, v5, v6, v7; };
-  Regs r0, r1;
-  bf16x8 fr0[4], fr1[4];
-  f32x16 acc[4];
+  Regs r0v, r1v;
+  bf16x8 fr0[4], fr1[4];   // [0], [1]: A sub-tiles; [2], [3]: B sub-tiles
+  f32x16 acc[4];           // acc[i + 2 j] = B sub-tile j times A sub-tile i
 #pragma unroll
   for (int k4 = 0; k4 < 4; ++k4)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[k4][r] = 0.f;
+
+#define WT_SB() __builtin_amdgcn_sched_barrier(0)
+  // register set R <- K step kt: loads i = 0..3 from A, 4..7 from B, through
+  // buffer descriptors that span only the step's rows inside the group, so the
+  // rows past its end read as zeros (the hardware's range check; nothing past
+  // the group is touched)
+#define WT_G(R, kt, i)                                                               \
+  do {                                                                               \
+    const int kk_ = (kt) * BK;                                                       \
+    const int vr_ = min(max(nr - kk_, 0), BK);                                       \
+    const int na_ = __builtin_amdgcn_readfirstlane(vr_ * lda * 2);                   \
+    const int nb_ = __builtin_amdgcn_readfirstlane(vr_ * ldb * 2);                   \
+    const __amdgpu_buffer_rsrc_t ra_ = __builtin_amdgcn_make_buffer_rsrc(            \
+        (void*)(A + (int64_t)(r0 + kk_) * lda), (short)0, na_, 0x00020000);           \
+    const __amdgpu_buffer_rsrc_t rb_ = __builtin_amdgcn_make_buffer_rsrc(            \
+        (void*)(B + (int64_t)(r0 + kk_) * ldb), (short)0, nb_, 0x00020000);           \
+    if ((i) == 0) R.v0 = __builtin_amdgcn_raw_buffer_load_b128(ra_, ao, 0, 0);       \
+    if ((i) == 1) R.v1 = __builtin_amdgcn_raw_buffer_load_b128(ra_, ao + astep, 0, 0); \
+    if ((i) == 2) R.v2 = __builtin_amdgcn_raw_buffer_load_b128(ra_, ao + 2 * astep, 0, 0); \
+    if ((i) == 3) R.v3 = __builtin_amdgcn_raw_buffer_load_b128(ra_, ao + 3 * astep, 0, 0); \
+    if ((i) == 4) R.v4 = __builtin_amdgcn_raw_buffer_load_b128(rb_, bo, 0, 0);       \
+    if ((i) == 5) R.v5 = __builtin_amdgcn_raw_buffer_load_b128(rb_, bo + bstep, 0, 0); \
+    if ((i) == 6) R.v6 = __builtin_amdgcn_raw_buffer_load_b128(rb_, bo + 2 * bstep, 0, 0); \
+    if ((i) == 7) R.v7 = __builtin_amdgcn_raw_buffer_load_b128(rb_, bo + 3 * bstep, 0, 0); \
+  } while (0)
+#define WT_W(R, st, i)                                                               \
+  do {                                                                               \
+    u32x4* d_ = smem + (st) * STAGE + wslot;                                         \
+    if ((i) == 0) d_[0] = R.v0;                                                      \
+    if ((i) == 1) d_[16 * TC] = R.v1;                                                \
+    if ((i) == 2) d_[32 * TC] = R.v2;                                                \
+    if ((i) == 3) d_[48 * TC] = R.v3;                                                \
+    if ((i) == 4) d_[HALF] = R.v4;                                                   \
+    if ((i) == 5) d_[HALF + 16 * TC] = R.v5;                                         \
+    if ((i) == 6) d_[HALF + 32 * TC] = R.v6;                                         \
+    if ((i) == 7) d_[HALF + 48 * TC] = R.v7;                                         \
+  } while (0)
+#define WT_R(F, st, s4, f)                                                           \
+  F[f] = lds_tr_frag(smem, (uint32_t)((st) * STAGE * 16 + (s4) * 4096) +             \
+                               ((f) < 2 ? fa[(f) & 1] : fb[(f) & 1]))
+#define WT_M(F, q)                                                                   \
+  acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F[2 + ((q) >> 1)], F[(q) & 1], acc[q], 0, 0, 0)
+  // one K step from stage st (as the forward kernel's: four sub-steps of four
+  // MFMAs, each followed by a fragment read of the next sub-step; global loads
+  // of set RG (step KL) in sub-steps 0 / 1, LDS writes of set RW to the other
+  // stage in sub-steps 2 / 3)
+#define WT_STEP(st, RG, KL, LD, RW, WR)                                              \
+  do {                                                                               \
+    WT_R(fr0, st, 0, 0); WT_R(fr0, st, 0, 2); WT_R(fr0, st, 0, 1);                   \
+    WT_R(fr0, st, 0, 3); WT_SB();                                                    \
+    _Pragma("unroll") for (int k_ = 0; k_ < 4; ++k_) {                               \
+      WT_M(fr0, k_); WT_SB(); WT_R(fr1, st, 1, kRO[k_]); WT_SB();                    \
+      if (LD) { WT_G(RG, KL, 2 * k_); WT_G(RG, KL, 2 * k_ + 1); }                    \
+      WT_SB();                                                                       \
+    }                                                                                \
+    _Pragma("unroll") for (int k_ = 0; k_ < 4; ++k_) {                               \
+      WT_M(fr1, k_); WT_SB(); WT_R(fr0, st, 2, kRO[k_]); WT_SB();                    \
+    }                                                                                \
+    _Pragma("unroll") for (int k_ = 0; k_ < 4; ++k_) {                               \
+      WT_M(fr0, k_); WT_SB(); WT_R(fr1, st, 3, kRO[k_]); WT_SB();                    \
+      if (WR) WT_W(RW, 1 - (st), k_);                                                \
+      WT_SB();                                                                       \
+    }                                                                                \
+    _Pragma("unroll") for (int k_ = 0; k_ < 4; ++k_) {                               \
+      WT_M(fr1, k_); WT_SB();                                                        \
+      if (WR) WT_W(RW, 1 - (st), 4 + k_);                                            \
+      WT_SB();                                                                       \
+    }                                                                                \
+  } while (0)
+
 #pragma unroll
-  for (int i = 0; i < 8; ++i) MOE_G(r0, 0, i);
+  for (int i = 0; i < 8; ++i) WT_G(r0v, 0, i);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) MOE_G(r1, 1, i);
+  for (int i = 0; i < 8; ++i) WT_G(r1v, 1, i);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) MOE_W(r0, 0, i);
+  for (int i = 0; i < 8; ++i) WT_W(r0v, 0, i);
   __syncthreads();
   for (int kt = 0; kt < len - 2; kt += 2) {
-    MOE_STEP(0, r0, kt + 2, true, r1, true);
+    WT_STEP(0, r0v, kt + 2, true, r1v, true);
     __syncthreads();
-    MOE_STEP(1, r1, kt + 3, true, r0, true);
+    WT_STEP(1, r1v, kt + 3, true, r0v, true);
     __syncthreads();
   }
-  MOE_STEP(0, r0, 0, false, r1, true);
+  WT_STEP(0, r0v, 0, false, r1v, true);
   __syncthreads();
-  MOE_STEP(1, r1, 0, false, r0, false);
+  WT_STEP(1, r1v, 0, false, r0v, false);
+#undef WT_SB
+#undef WT_G
+#undef WT_W
+#undef WT_R
+#undef WT_M
+#undef WT_STEP
+  // lane (fr, fk) of accumulator (i, j) holds row m0 + wm 64 + 32 i + fr and
+  // columns n0 + wn 64 + 32 j + 8 qd + 4 fk .. + 3 of C_g
   float* __restrict__ Cg = g < E ? C + (int64_t)g * M * N : Cs;
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
+  for (int i = 0; i < 2; ++i) {
     const int m = wm * 64 + i * 32 + fr;
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int qd = 0; qd < 4; ++qd) {
         const f32x4 v = {acc[i + 2 * j][qd * 4 + 0], acc[i + 2 * j][qd * 4 + 1],
                          acc[i + 2 * j][qd * 4 + 2], acc[i + 2 * j][qd * 4 + 3]};
-        *reinterpret_cast<f32x4*>(Cg + (int64_t)(row0 + m) * N + n0 + wn * WN + j * 32 + qd * 8 +
+        *reinterpret_cast<f32x4*>(Cg + (int64_t)(m0 + m) * N + n0 + wn * 64 + j * 32 + qd * 8 +
                                   fk * 4) = v;
       }
   }
-#undef MOE_SB
-#undef MOE_G
-#undef MOE_W
-#undef MOE_R
-#undef MOE_M
-#undef MOE_STEP
 }
 
 // Grouped GEMM on the full 256-row tiles of each group (part 1 of the row
@@ -2166,12 +2248,12 @@ hipError_t launch_pack_weights(const moe_config& c, const moe_weights& w, void* 
   return hipSuccess;
 }
 
-hipError_t launch_wgrad(const void* a, const void* b, const int32_t* po, int G, int E, int M, int N,
-                        int ldk, float* C, float* Cs, hipStream_t s) {
+hipError_t launch_wgrad(const void* a, int lda, const void* b, int ldb, const int32_t* so, int G,
+                        int E, int M, int N, float* C, float* Cs, hipStream_t s) {
   const int64_t tiles = (int64_t)G * (M / 128) * (N / 128);
   if (tiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL(gemm_wgrad_kernel, dim3((unsigned)tiles), dim3(256), 0, s, (const bf16*)a,
-                     (const bf16*)b, po, G, E, M, N, ldk, C, Cs);
+  hipLaunchKernelGGL(gemm_wgrad_tn_kernel, dim3((unsigned)tiles), dim3(256), 0, s, (const bf16*)a,
+                     lda, (const bf16*)b, ldb, so, G, E, M, N, C, Cs);
   return hipGetLastError();
 }
 

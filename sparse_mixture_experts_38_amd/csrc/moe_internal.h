@@ -223,12 +223,12 @@ hipError_t launch_expert_choice_forward(const moe_config& c, const EcLayout& L, 
                                         hipStream_t stream);
 
 // ------------------------------------------------------------------ backward
-// Workspace of moe_backward (byte offsets). ldk is the row length of the
-// transposed, group-padded row buffers (each group's rows rounded up to a
-// multiple of 128, at least 128).
+// Workspace of moe_backward (byte offsets). ldk is the length of the padded
+// row space of the bias column sums (each group's rows rounded up to a multiple
+// of 128, at least 128); xp holds the expert-sorted x rows.
 struct BwdLayout {
   size_t dyp, dgate, dlogits, dz, dh, dxp, po;   // po: padded then sanitized offsets
-  size_t dypT, hT, dzT, xT, colsum1, colsum2, gate_partial, total;
+  size_t xp, colsum1, colsum2, gate_partial, total;
   int64_t ldk;
   int gate_slices, gate_slice_len;
 };
@@ -252,7 +252,7 @@ hipError_t launch_router_bias_and_dx(const moe_config& c, const float* dlogits, 
                                      const moe_routing& r, const moe_weights& w,
                                      const moe_grads& gr, hipStream_t s);
 // float32 layers: h = act(z) of the training forward, the backward workspace
-// layout (dyp, dgate, dlogits, dz, dh, hT = h row-major, dxp) and the whole backward.
+// layout (dyp, dgate, dlogits, dz, dh, dxp) and the whole backward.
 hipError_t launch_act_rows_f32(const moe_config& c, const void* z, const int32_t* expert_offsets,
                                void* h, hipStream_t stream);
 BwdLayout backward_layout_f32(const moe_config& c);
@@ -282,9 +282,10 @@ hipError_t launch_dswiglu(const moe_config& c, const void* dh, const void* z, vo
 hipError_t launch_backward_dx(const moe_config& c, const void* dz, const int32_t* expert_offsets,
                               const void* w1, const void* w3, const void* ws1, const void* ws3,
                               void* dxp, hipStream_t stream);
-// Ragged-K grouped weight gradient C_g = A[:, po[g]:po[g+1]] B[:, po[g]:po[g+1]]^T,
-// A [M][ldk], B [N][ldk] bf16; C float32 [E][M][N], Cs [M][N] for group E.
-hipError_t launch_wgrad(const void* a, const void* b, const int32_t* po, int G, int E, int M, int N,
-                        int ldk, float* C, float* Cs, hipStream_t stream);
+// Grouped weight gradient over the rows of each group,
+// C_g = A[so[g]:so[g+1], 0:M]^T B[so[g]:so[g+1], 0:N]: A [rows][lda], B [rows][ldb]
+// bf16 row-major; C float32 [E][M][N], Cs [M][N] for group E.
+hipError_t launch_wgrad(const void* a, int lda, const void* b, int ldb, const int32_t* so, int G,
+                        int E, int M, int N, float* C, float* Cs, hipStream_t stream);
 
 }  // namespace moe

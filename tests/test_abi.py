@@ -183,7 +183,8 @@ def test_training_entry_points_validate_before_any_launch():
     assert lib.moe_backward_workspace_size(ctypes.byref(f32), ctypes.byref(n)) == A.MOE_OK
     T, d, F, k = f32.tokens, 32, 200, f32.top_k
     rows = T * k
-    assert n.value >= 4 * (rows * d * 2 + rows * F * 2 + T * k + T * f32.num_experts)
+    # dyp and dxp (rows x d), dz (rows x F), dgate, dlogits (h is the saved one)
+    assert n.value >= 4 * (rows * d * 2 + rows * F + T * k + T * f32.num_experts)
     assert lib.moe_backward(ctypes.byref(f32), None, None, None, None, None, None, 0.0, 0.0,
                             None, None, 0, None) == A.MOE_ERR_INVALID_ARG
     assert lib.moe_forward_train(ctypes.byref(f32), None, None, None, None, None, None, None, 0,
@@ -200,7 +201,7 @@ def test_backward_workspace_too_small_is_reported():
     fake = ctypes.c_void_p(0x1000)   # never dereferenced: the size check comes first
     w = A.MoeWeights(w_gate=fake, w1=fake, w2=fake, b1=fake, b2=fake)
     r = A.MoeRouting(*([fake] * 6))
-    sv = A.MoeSaved(fake, fake)
+    sv = A.MoeSaved(fake, fake, fake)
     g = A.MoeGrads(dx=fake, dw_gate=fake, dw1=fake, dw2=fake, db1=fake, db2=fake)
     st = lib.moe_backward(ctypes.byref(cfg), fake, ctypes.byref(w), ctypes.byref(r), fake,
                           ctypes.byref(sv), fake, 0.0, 0.0, ctypes.byref(g), fake, 16, None)
