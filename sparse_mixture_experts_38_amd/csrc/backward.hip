@@ -135,7 +135,11 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
 }
 
 // ------------------------------------------------------------------ router backward
-// One wavefront per token; lane l holds experts l, l + 64, l + 128, l + 192.
+// W lanes per token (W = the power of two >= E, at most 64; 64 / W tokens per
+// wavefront); lane l of a token's W holds experts l, l + 64, l + 128, l + 192
+// (only l when E <= 64). The reductions over a token's lanes are xor trees of
+// width W, which add the same terms in the same order as a 64-wide tree over
+// the zero-padded row.
 // Gates g_j = s_{i_j} / S (S = sum of the selected scores) give
 // ds_{i_j} = (dg_j - sum_m dg_m g_m) / S; L_aux = E sum_i f_i P_i adds
 // dq_i = aux_coef E f_i / T to the probabilities it averages (softmax: p;
@@ -147,8 +151,9 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(
     const float* __restrict__ logits, const int32_t* __restrict__ topk_idx,
     const float* __restrict__ dgate, const int32_t* __restrict__ counts_pre, int64_t T, int E,
     int k, int sigmoid, float aux_coef, float z_coef, float* __restrict__ dlogits) {
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
+  const int W = E <= 8 ? 8 : (E <= 16 ? 16 : (E <= 32 ? 32 : 64));
+  const int64_t t = ((int64_t)blockIdx.x * 256 + threadIdx.x) / W;
+  const int lane = threadIdx.x & (W - 1);
   if (t >= T) return;
   const float* h = logits + t * E;
   float hv[4];
@@ -160,7 +165,7 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(
     m = fmaxf(m, hv[i]);
   }
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  for (int o = W >> 1; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
   float se = 0.f;
   float ex[4];
 #pragma unroll
@@ -169,7 +174,7 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(
     se += ex[i];
   }
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) se += __shfl_xor(se, o, 64);
+  for (int o = W >> 1; o > 0; o >>= 1) se += __shfl_xor(se, o, 64);
   const float lse = m + logf(se);
   const float inv_se = 1.0f / se;
   // selected scores and the renormalised gates
@@ -217,17 +222,17 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(
       dot += ds[i] * p[i];
     }
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) dot += __shfl_xor(dot, o, 64);
+    for (int o = W >> 1; o > 0; o >>= 1) dot += __shfl_xor(dot, o, 64);
 #pragma unroll
     for (int i = 0; i < 4; ++i) dh[i] = p[i] * (ds[i] - dot);
   } else {
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) tot += __shfl_xor(tot, o, 64);
+    for (int o = W >> 1; o > 0; o >>= 1) tot += __shfl_xor(tot, o, 64);
     float dotq = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) dotq += dq[i] * (s[i] / tot);
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) dotq += __shfl_xor(dotq, o, 64);
+    for (int o = W >> 1; o > 0; o >>= 1) dotq += __shfl_xor(dotq, o, 64);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       ds[i] += (dq[i] - dotq) / tot;
@@ -311,14 +316,20 @@ __global__ __launch_bounds__(256) void colsum_rows_kernel(const bf16* __restrict
   const int cl = (threadIdx.x & 63) * 8;
   const int c = blockIdx.y * 512 + cl;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if (c < C) {
-    for (int j = 0; j < 16; ++j) {
-      const int lr = local + rl * 16 + j;
-      if (lr >= nr) break;
-      float v[8];
-      load8(src + (int64_t)(so[g] + lr) * ld + c, v);
+  if (c < C && local < nr) {
+    // the 16 rows' loads issued together (rows past the group re-read its last
+    // row and are not added)
+    float v[16][8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += v[e];
+    for (int j = 0; j < 16; ++j) {
+      const int lr = min(local + rl * 16 + j, nr - 1);
+      load8(src + (int64_t)(so[g] + lr) * ld + c, v[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const bool in = local + rl * 16 + j < nr;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += in ? v[j][e] : 0.f;
     }
   }
 #pragma unroll
@@ -360,19 +371,20 @@ __global__ __launch_bounds__(256) void colsum_reduce_kernel(const float* __restr
 }
 
 // ------------------------------------------------------------------ router weights
-// dW_g[e][c] = sum_t dlogits[t][e] x[t][c]. Block (8 experts, 1024 columns, a
-// token slice): thread = 8 consecutive columns (one 16-byte load per token) x 8
-// experts, the two halves of the block take alternate tokens and are added in
-// LDS; the block's sums go to partial[slice][e][c] and
-// gate_wgrad_reduce_kernel adds the slices in order.
+// dW_g[e][c] = sum_t dlogits[t][e] x[t][c]. Block (8 experts, 512 columns, a
+// token slice); wave w takes the slice's tokens w, w + 4, w + 8, ..., lane =
+// 8 consecutive columns (one 16-byte load per token) x 8 experts. Waves 1..3
+// hand their sums to wave 0 through LDS, which adds them in wave order and
+// writes partial[slice][e][c]; gate_wgrad_reduce_kernel adds the slices in
+// order (deterministic).
 __global__ __launch_bounds__(256) void gate_wgrad_kernel(const bf16* __restrict__ x,
                                                          const float* __restrict__ dlogits,
                                                          int64_t T, int d, int E, int slice_len,
                                                          float* __restrict__ partial) {
-  __shared__ float red[128][65];
+  __shared__ float red[3][64][65];
   const int e0 = blockIdx.x * 8;
-  const int half = threadIdx.x >> 7;
-  const int c = (blockIdx.y * 128 + (threadIdx.x & 127)) * 8;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int c = (blockIdx.y * 64 + lane) * 8;
   const int64_t t0 = (int64_t)blockIdx.z * slice_len;
   const int64_t t1 = t0 + slice_len < T ? t0 + slice_len : T;
   float acc[8][8];
@@ -382,11 +394,11 @@ __global__ __launch_bounds__(256) void gate_wgrad_kernel(const bf16* __restrict_
     for (int u = 0; u < 8; ++u) acc[e][u] = 0.f;
   if (c < d) {
     // four tokens per iteration, their loads issued together
-    for (int64_t tb = t0 + half; tb < t1; tb += 8) {
+    for (int64_t tb = t0 + wave; tb < t1; tb += 16) {
       float xv[4][8];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int64_t t = tb + 2 * q;
+        const int64_t t = tb + 4 * q;
         if (t < t1) {
           load8(x + t * d + c, xv[q]);
         } else {
@@ -396,7 +408,7 @@ __global__ __launch_bounds__(256) void gate_wgrad_kernel(const bf16* __restrict_
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int64_t t = tb + 2 * q;
+        const int64_t t = tb + 4 * q;
         if (t < t1) {
           const float* dl = dlogits + t * E + e0;
 #pragma unroll
@@ -409,42 +421,55 @@ __global__ __launch_bounds__(256) void gate_wgrad_kernel(const bf16* __restrict_
       }
     }
   }
-  if (half == 1) {
+  if (wave > 0) {
 #pragma unroll
     for (int e = 0; e < 8; ++e)
 #pragma unroll
-      for (int u = 0; u < 8; ++u) red[threadIdx.x & 127][e * 8 + u] = acc[e][u];
+      for (int u = 0; u < 8; ++u) red[wave - 1][lane][e * 8 + u] = acc[e][u];
   }
   __syncthreads();
-  if (half == 0 && c < d) {
+  if (wave == 0 && c < d) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       if (e0 + e < E) {
         float v[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = acc[e][u] + red[threadIdx.x][e * 8 + u];
+        for (int u = 0; u < 8; ++u)
+          v[u] = ((acc[e][u] + red[0][lane][e * 8 + u]) + red[1][lane][e * 8 + u]) +
+                 red[2][lane][e * 8 + u];
         store8(partial + ((int64_t)blockIdx.z * E + e0 + e) * d + c, v);
       }
     }
   }
 }
 
+// dw[i] = sum over the slices of partial[slice][i], in slice order: block = 64
+// outputs x 4 slice lanes (lane q adds slices [q S', (q + 1) S') in order,
+// S' = ceil(slices / 4)), the lanes' sums then added in lane order.
 __global__ __launch_bounds__(256) void gate_wgrad_reduce_kernel(const float* __restrict__ partial,
                                                                 int slices, int64_t n,
                                                                 float* __restrict__ dw) {
-  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (i >= n) return;
+  __shared__ float red[4][64];
+  const int q = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t i = blockIdx.x * (int64_t)64 + lane;
+  const int per = (slices + 3) / 4;
+  const int z0 = q * per;
+  const int z1 = z0 + per < slices ? z0 + per : slices;
   float s = 0.f;
-  int z = 0;
-  for (; z + 8 <= slices; z += 8) {
-    float v[8];
+  if (i < n) {
+    int z = z0;
+    for (; z + 8 <= z1; z += 8) {
+      float v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = partial[(z + u) * n + i];
+      for (int u = 0; u < 8; ++u) v[u] = partial[(z + u) * n + i];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) s += v[u];
+      for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; z < z1; ++z) s += partial[z * n + i];
   }
-  for (; z < slices; ++z) s += partial[z * n + i];
-  dw[i] = s;
+  red[q][lane] = s;
+  __syncthreads();
+  if (q == 0 && i < n) dw[i] = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
 }
 
 // db_g[e] = sum_t dlogits[t][e]: one block per expert, a fixed-order tree.
@@ -500,6 +525,14 @@ __global__ __launch_bounds__(256) void unpermute_dx_kernel(
     if (!live[j]) rj[j] = first;
   const float* dl = dlogits + t * E;
   for (int c = lane * 8; c < d; c += 512) {
+    // the expert-row loads (from HBM) issued first, the router term's weight
+    // rows (cached) after them
+    float a[KM][8], as[8];
+    if (first >= 0) {
+#pragma unroll
+      for (int j = 0; j < KM; ++j) load8(dxp + rj[j] * d + c, a[j]);
+      load8(dxp + (shared ? rs : first) * d + c, as);
+    }
     float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int e0 = 0; e0 < E; e0 += 8) {
       float wv[8][8], g[8];
@@ -515,10 +548,6 @@ __global__ __launch_bounds__(256) void unpermute_dx_kernel(
         for (int q = 0; q < 8; ++q) v[q] = e0 + u < E ? fmaf(g[u], wv[u][q], v[q]) : v[q];
     }
     if (first >= 0) {
-      float a[KM][8], as[8];
-#pragma unroll
-      for (int j = 0; j < KM; ++j) load8(dxp + rj[j] * d + c, a[j]);
-      load8(dxp + (shared ? rs : first) * d + c, as);
 #pragma unroll
       for (int j = 0; j < KM; ++j)
 #pragma unroll
@@ -568,7 +597,9 @@ hipError_t launch_router_backward(const moe_config& c, const moe_routing& r, con
                                   const float* dgate, float aux_coef, float z_coef, float* dlogits,
                                   hipStream_t s) {
   const int64_t T = c.tokens;
-  hipLaunchKernelGGL(router_bwd_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, r.logits,
+  const int E = c.num_experts;
+  const int64_t per_block = 256 / (E <= 8 ? 8 : (E <= 16 ? 16 : (E <= 32 ? 32 : 64)));   // tokens
+  hipLaunchKernelGGL(router_bwd_kernel, dim3((unsigned)((T + per_block - 1) / per_block)), dim3(256), 0, s, r.logits,
                      r.topk_idx, dgate, stats->counts_pre, T, c.num_experts, c.top_k,
                      (int)(c.score_fn == MOE_SCORE_SIGMOID), aux_coef, z_coef, dlogits);
   return hipGetLastError();
@@ -683,11 +714,11 @@ hipError_t launch_backward_misc(const moe_config& c, const BwdLayout& B, const v
     hipLaunchKernelGGL(colsum_reduce_kernel, dim3((F + 255) / 256, G), dim3(256), 0, s,
                        (const float*)p1, F, (const int32_t*)po, F, E, gr.db1, gr.dbs1);
   }
-  hipLaunchKernelGGL(gate_wgrad_kernel, dim3((E + 7) / 8, (d + 1023) / 1024, B.gate_slices), dim3(256), 0, s,
+  hipLaunchKernelGGL(gate_wgrad_kernel, dim3((E + 7) / 8, (d + 511) / 512, B.gate_slices), dim3(256), 0, s,
                      (const bf16*)x, (const float*)dlogits, T, d, E, (int)B.gate_slice_len,
                      (float*)(ws + B.gate_partial));
   const int64_t n = (int64_t)E * d;
-  hipLaunchKernelGGL(gate_wgrad_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+  hipLaunchKernelGGL(gate_wgrad_reduce_kernel, dim3((unsigned)((n + 63) / 64)), dim3(256), 0, s,
                      (const float*)(ws + B.gate_partial), (int)B.gate_slices, n, gr.dw_gate);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -74,11 +74,12 @@ BwdLayout backward_layout(const moe_config& c) {
   B.xp = take((size_t)(rmax * d * 2));
   B.colsum1 = take(c.has_bias ? (size_t)(B.ldk / 64 * F * 4) : 0);
   B.colsum2 = take(c.has_bias ? (size_t)(B.ldk / 64 * d * 4) : 0);
-  // router weight gradient: about 512 blocks of (8 experts x 1024 columns x a token slice)
-  const int64_t xy = (int64_t)((E + 7) / 8) * ((d + 1023) / 1024);
-  int64_t slices = 512 / xy;
+  // router weight gradient: about 256 blocks of (8 experts x 512 columns x a
+  // token slice), slices of at least 64 tokens
+  const int64_t xy = (int64_t)((E + 7) / 8) * ((d + 511) / 512);
+  int64_t slices = 256 / xy;
   slices = slices < 1 ? 1 : (slices > 256 ? 256 : slices);
-  if (slices > T) slices = T > 0 ? T : 1;
+  if (slices > T / 64) slices = T / 64 > 0 ? T / 64 : 1;
   const int64_t slice_len = T > 0 ? (T + slices - 1) / slices : 1;
   B.gate_slice_len = (int)slice_len;
   B.gate_slices = (int)(T > 0 ? (T + slice_len - 1) / slice_len : 1);
