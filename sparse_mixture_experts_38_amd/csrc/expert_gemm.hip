@@ -529,6 +529,59 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
           }
       }
     }
+  } else if constexpr (DACT) {
+    // Backward epilogue C = acc * act'(z) (no bias): the float32 tile is staged
+    // in LDS (64 KB: both operand stages), 16-byte chunk q (0..31) of row m at
+    // q ^ (m & 31), so that 16 consecutive lanes of a write or a read hit 16
+    // distinct chunks; then thread t takes 8 consecutive columns of rows
+    // t / 16 + 16 p, reading z and writing dZ with whole 256-byte row segments.
+    // The z loads are issued right after the staging writes (the accumulators
+    // are free then), so that their latency is spent in the barrier.
+    __syncthreads();   // every wave is done reading the operand stages
+    f32x4* st4 = reinterpret_cast<f32x4*>(smem);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int m = wm * 64 + i * 32 + fr;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          const int q = wn * (WN / 4) + j * 8 + qd * 2 + fk;
+          const f32x4 v = {acc[i + 2 * j][qd * 4 + 0], acc[i + 2 * j][qd * 4 + 1],
+                           acc[i + 2 * j][qd * 4 + 2], acc[i + 2 * j][qd * 4 + 3]};
+          st4[m * 32 + (q ^ (m & 31))] = v;
+        }
+    }
+    u32x4 zq[8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int m = (tid >> 4) + 16 * p;
+      const u32x4 z0 = {0u, 0u, 0u, 0u};
+      zq[p] = m < cur_nrows ? *reinterpret_cast<const u32x4*>(Zin + (int64_t)(cur_row0 + m) * N +
+                                                                cur_n0 + (tid & 15) * 8)
+                            : z0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int m = (tid >> 4) + 16 * p;
+      const int c2 = (tid & 15) * 2;
+      if (m < cur_nrows) {
+        const f32x4 a = st4[m * 32 + (c2 ^ (m & 31))];
+        const f32x4 b = st4[m * 32 + ((c2 + 1) ^ (m & 31))];
+        const float dh[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        const uint32_t zw[4] = {zq[p].x, zq[p].y, zq[p].z, zq[p].w};
+        uint32_t o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float lo = epilogue_bf16<EPI>(dh[2 * e], bf16_bits_to_f32(zw[e] & 0xffffu));
+          const float hi = epilogue_bf16<EPI>(dh[2 * e + 1], bf16_bits_to_f32(zw[e] >> 16));
+          o[e] = pack_bf16x2(lo, hi);
+        }
+        const u32x4 ov = {o[0], o[1], o[2], o[3]};
+        *reinterpret_cast<u32x4*>(C + (int64_t)(cur_row0 + m) * N + cur_n0 + (tid & 15) * 8) = ov;
+      }
+    }
   } else {
   // Epilogue. Register r of a 32x32 accumulator holds row (lane % 32) and
   // column 8 (r / 4) + 4 (lane / 32) + r % 4 of the sub-tile, so lane (fr, fk)
@@ -540,22 +593,6 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
     for (int qd = 0; qd < 4; ++qd)
       bv[j][qd] = HAS_BIAS ? *reinterpret_cast<const float4*>(cur_bg + cur_n0 + wn * WN + j * 32 + qd * 8 + fk * 4)
                            : make_float4(0.f, 0.f, 0.f, 0.f);
-  // backward epilogues: the 4 saved pre-activations of each accumulator quad
-  uint2 zv[DACT ? TM : 1][DACT ? TN : 1][4];
-  if constexpr (DACT) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int m = wm * 64 + i * 32 + fr;
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int qd = 0; qd < 4; ++qd)
-          zv[i][j][qd] = m < cur_nrows
-                             ? *reinterpret_cast<const uint2*>(Zin + (int64_t)(cur_row0 + m) * N + cur_n0 +
-                                                               wn * WN + j * 32 + qd * 8 + fk * 4)
-                             : make_uint2(0u, 0u);
-    }
-  }
   __syncthreads();   // every wave is done reading the operand stages
   // bf16 tile staged as BM rows of CQ chunks; chunk q of row m at q ^ swz(m)
   uint2* st8 = reinterpret_cast<uint2*>(smem);
@@ -571,15 +608,9 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
         const float z[4] = {acc[i + 2 * j][qd * 4 + 0] + bq.x, acc[i + 2 * j][qd * 4 + 1] + bq.y,
                             acc[i + 2 * j][qd * 4 + 2] + bq.z, acc[i + 2 * j][qd * 4 + 3] + bq.w};
         float v[4];
-        float zs[4] = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (DACT) {
-          const uint2 u = zv[i][j][qd];
-          zs[0] = bf16_bits_to_f32(u.x & 0xffffu); zs[1] = bf16_bits_to_f32(u.x >> 16);
-          zs[2] = bf16_bits_to_f32(u.y & 0xffffu); zs[3] = bf16_bits_to_f32(u.y >> 16);
-        }
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          v[e] = epilogue_bf16<EPI>(z[e], GATED ? acc[i + 2][qd * 4 + e] : zs[e]);
+          v[e] = epilogue_bf16<EPI>(z[e], GATED ? acc[i + 2][qd * 4 + e] : 0.f);
         uint2 u;
         u.x = pack_bf16x2(v[0], v[1]);
         u.y = pack_bf16x2(v[2], v[3]);
