@@ -180,15 +180,17 @@ __device__ __forceinline__ float epilogue_bf16(float z1, float z3) {
 }
 
 // One 8-element K fragment of v_mfma_f32_32x32x16_bf16 read transposed out of
-// a row-major LDS tile: two ds_read_b64_tr_b16, the second 4 rows (1024 bytes)
-// after the first (lane layout: gemm_bf16_kernel's KMB note).
+// a row-major LDS tile: two ds_read_b64_tr_b16, the second 4 rows after the
+// first (lane layout: gemm_bf16_kernel's KMB note).
+// PITCH: bytes per LDS row.
+template <int PITCH = 256>
 __device__ __forceinline__ bf16x8 lds_tr_frag(const u32x4* smem, uint32_t byte) {
   typedef short s16x4 __attribute__((ext_vector_type(4)));
   typedef short s16x8 __attribute__((ext_vector_type(8)));
   typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
   lds_s16x4* p = (lds_s16x4*)((__attribute__((address_space(3))) char*)smem + byte);
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p);
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p + 128);
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p + PITCH / 2);
   const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8, v);
 }
@@ -831,6 +833,192 @@ __global__ __launch_bounds__(256, 2) void gemm_wgrad_tn_kernel(
         const f32x4 v = {acc[i + 2 * j][qd * 4 + 0], acc[i + 2 * j][qd * 4 + 1],
                          acc[i + 2 * j][qd * 4 + 2], acc[i + 2 * j][qd * 4 + 3]};
         *reinterpret_cast<f32x4*>(Cg + (int64_t)(m0 + m) * N + n0 + wn * 64 + j * 32 + qd * 8 +
+                                  fk * 4) = v;
+      }
+  }
+}
+
+// The weight gradient of gemm_wgrad_tn_kernel on 256 x 256 tiles: one block
+// of four waves per CU, each wave 128 x 128 with its 256 float32 accumulators
+// in the accumulation registers (half the LDS bytes per FLOP of the 128 x 128
+// tile, whose fragment reads bound it). Operands go global -> LDS directly
+// (buffer_load ... lds, 16 bytes per lane): a stage holds the A and the B
+// tile, 64 rows x 512 bytes each (32 KB), in two LDS arrays of two stages;
+// waves 0 / 1 load A rows 0..31 / 32..63, waves 2 / 3 the B rows, two rows per
+// instruction. Lane l of an instruction lands at physical chunk l & 31 of its
+// row, which holds logical chunk (l & 31) ^ 4 (row & 3), so the transposed
+// fragment reads (lds_tr_frag, 512-byte rows) see four rows in four distinct
+// bank groups. Each K step's buffer descriptors span only its rows inside the
+// group, so rows past the group's end land in LDS as zeros. One barrier per K
+// step, as in gemm_bf16_big_kernel: the step's last sub-step runs from
+// registers while the next step's first fragments are read and the loads of
+// the step after go to the other stage.
+__global__ __launch_bounds__(256, 1) void gemm_wgrad_tn_big_kernel(
+    const bf16* __restrict__ A, int lda, const bf16* __restrict__ B, int ldb,
+    const int32_t* __restrict__ so, int G, int E, int M, int N, float* __restrict__ C,
+    float* __restrict__ Cs) {
+  constexpr int BM = 256, BN = 256, BK = 64, TC = 32;   // 32 chunks of 16 B per LDS row
+  constexpr int HALF = BK * TC;                          // chunks of one operand tile (32 KB)
+  constexpr int STAGE = 2 * HALF;
+  constexpr int GROUP_M = 8;
+  __shared__ u32x4 sm0[STAGE], sm1[STAGE];
+  const int mtn = M / BM, ntn = N / BN, per = mtn * ntn;
+  const int tiles = G * per;
+  const int b = blockIdx.x;
+  if (b >= tiles) return;
+  const int t8 = tiles & ~7;
+  const int t = b < t8 ? (b & 7) * (t8 >> 3) + (b >> 3) : b;
+  const int g = t / per;
+  const int in = t - g * per;
+  const int grp = in / (GROUP_M * ntn);
+  const int first_m = grp * GROUP_M;
+  const int gm = min(mtn - first_m, GROUP_M);
+  const int in2 = in - grp * GROUP_M * ntn;
+  const int m0 = (first_m + in2 % gm) * BM;
+  const int n0 = (in2 / gm) * BN;
+  const int r0 = __builtin_amdgcn_readfirstlane(so[g]);
+  const int nr = __builtin_amdgcn_readfirstlane(so[g + 1]) - r0;   // the group's rows
+  int nk = (nr + BK - 1) / BK;   // K steps, made even and at least 2
+  nk = nk < 2 ? 2 : (nk + 1) & ~1;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int fr = lane & 31;
+  const int fk = lane >> 5;
+
+  // this wave's operand (uniform): A for waves 0 / 1, B for 2 / 3
+  const bf16* X = wave < 2 ? A : B;
+  const int ld = wave < 2 ? lda : ldb;
+  const int c0 = wave < 2 ? m0 : n0;
+  uint32_t doff[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int row = 32 * (wave & 1) + 2 * i + (lane >> 5);
+    const int lch = (lane & 31) ^ ((row & 3) << 2);
+    doff[i] = (uint32_t)(row * ld + c0 + lch * 8) * 2u;
+  }
+  const int dl = wave * 1024;   // this wave's first chunk in a stage
+  // fragment byte offsets in a stage: A sub-tile i, B sub-tile j (+ 8192 per
+  // 16-row sub-step)
+  uint32_t fo[8];
+#pragma unroll
+  for (int f = 0; f < 8; ++f) {
+    const int x = lane & 15, hq = (lane >> 4) & 1;
+    const int krow = 8 * fk + (x >> 2);
+    const int ch = (f < 4 ? wm * 16 + f * 4 : wn * 16 + (f - 4) * 4) + 2 * hq + ((x & 3) >> 1);
+    fo[f] = (uint32_t)(((f < 4 ? 0 : HALF) + krow * TC + (ch ^ ((krow & 3) << 2))) * 16 + (x & 1) * 8);
+  }
+  constexpr int kRO[8] = {0, 4, 1, 2, 3, 5, 6, 7};   // read order: A0 B0 A1 A2 A3 B1 B2 B3
+
+  bf16x8 fa[8], fb[8];   // [0..3]: A sub-tiles, [4..7]: B sub-tiles
+  f32x16 acc[16];        // acc[i + 4 j] = B sub-tile j times A sub-tile i
+#pragma unroll
+  for (int q = 0; q < 16; ++q)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[q][r] = 0.f;
+
+#define WB_SB() __builtin_amdgcn_sched_barrier(0)
+#define WB_SM(x) ((x) == 0 ? sm0 : sm1)
+#define WB_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+  // the buffer descriptor of K step kt (scalar: rows of the step inside the group)
+#define WB_RSRC(kt)                                                                  \
+  __builtin_amdgcn_make_buffer_rsrc(                                                 \
+      (void*)(X + (int64_t)(r0 + (kt) * BK) * ld), (short)0,                         \
+      __builtin_amdgcn_readfirstlane(min(max(nr - (kt) * BK, 0), BK) * ld * 2), 0x00020000)
+#define WB_D(x, rs, i)                                                               \
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, WB_LDS(WB_SM(x) + dl + (i) * 64), 16, doff[i], 0, 0, 0)
+#define WB_R(F, x, s4, f)                                                            \
+  F[f] = lds_tr_frag<512>(WB_SM(x), (uint32_t)((s4) * 8192) + fo[f])
+#define WB_M(F, q)                                                                   \
+  acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F[4 + ((q) >> 2)], F[(q) & 3], acc[q], 0, 0, 0)
+  // wait for this wave's direct-to-LDS loads (vmcnt 0, expcnt and lgkmcnt free)
+#define WB_WAIT_LOADS() __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8))
+  // one sub-step: 16 MFMAs, the first 8 followed by a fragment read of the next
+  // sub-step (RD), every second one by one of 8 loads d0 .. d0 + 7 of step KN
+  // into the other stage (LD)
+#define WB_SUB(FC, FN, x, s4n, RD, LD, rs, d0)                                       \
+  _Pragma("unroll") for (int q_ = 0; q_ < 16; ++q_) {                                \
+    WB_M(FC, q_); WB_SB();                                                           \
+    if ((RD) && q_ < 8) WB_R(FN, x, s4n, kRO[q_]);                                   \
+    if ((LD) && (q_ & 1)) WB_D(1 - (x), rs, (d0) + (q_ >> 1));                       \
+    WB_SB();                                                                         \
+  }
+  // phase k: sub-step 3 of step k - 1 while step k's first fragments are read
+  // from stage x and step KN's loads go to the other stage, then sub-steps
+  // 0..2 of step k, the wait for this wave's loads and the barrier
+#define WB_PHASE(x, KN, LD)                                                          \
+  do {                                                                               \
+    const __amdgpu_buffer_rsrc_t rs_ = WB_RSRC(KN);                                  \
+    WB_SUB(fb, fa, x, 0, true, LD, rs_, 0)                                           \
+    WB_SUB(fa, fb, x, 1, true, LD, rs_, 8)                                           \
+    WB_SUB(fb, fa, x, 2, true, false, rs_, 0)                                        \
+    WB_SUB(fa, fb, x, 3, true, false, rs_, 0)                                        \
+    WB_WAIT_LOADS();                                                                 \
+    __builtin_amdgcn_s_barrier();                                                    \
+    WB_SB();                                                                         \
+  } while (0)
+
+  {
+    const __amdgpu_buffer_rsrc_t rs0 = WB_RSRC(0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) WB_D(0, rs0, i);
+  }
+  WB_WAIT_LOADS();
+  __builtin_amdgcn_s_barrier();
+  WB_SB();
+  // phase 0: no previous step; all 16 loads of step 1 go out in sub-step 0
+#pragma unroll
+  for (int f = 0; f < 8; ++f) WB_R(fa, 0, 0, kRO[f]);
+  WB_SB();
+  {
+    const __amdgpu_buffer_rsrc_t rs1 = WB_RSRC(1);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      WB_M(fa, q); WB_SB();
+      if (q < 8) WB_R(fb, 0, 1, kRO[q]);
+      WB_D(1, rs1, q);
+      WB_SB();
+    }
+    WB_SUB(fb, fa, 0, 2, true, false, rs1, 0)
+    WB_SUB(fa, fb, 0, 3, true, false, rs1, 0)
+  }
+  WB_WAIT_LOADS();
+  __builtin_amdgcn_s_barrier();
+  WB_SB();
+  // phases 1 .. nk - 1 (nk even)
+  for (int kt = 1; kt < nk - 1; kt += 2) {
+    WB_PHASE(1, kt + 1, true);
+    WB_PHASE(0, kt + 2, true);
+  }
+  WB_PHASE(1, 0, false);
+  // sub-step 3 of the last step
+#pragma unroll
+  for (int q = 0; q < 16; ++q) { WB_M(fb, q); WB_SB(); }
+#undef WB_SB
+#undef WB_SM
+#undef WB_LDS
+#undef WB_RSRC
+#undef WB_D
+#undef WB_R
+#undef WB_M
+#undef WB_WAIT_LOADS
+#undef WB_SUB
+#undef WB_PHASE
+
+  // lane (fr, fk) of accumulator (i, j) holds row m0 + wm 128 + 32 i + fr and
+  // columns n0 + wn 128 + 32 j + 8 qd + 4 fk .. + 3 of C_g
+  float* __restrict__ Cg = g < E ? C + (int64_t)g * M * N : Cs;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = wm * 128 + i * 32 + fr;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        const f32x16& a = acc[i + 4 * j];
+        const f32x4 v = {a[qd * 4 + 0], a[qd * 4 + 1], a[qd * 4 + 2], a[qd * 4 + 3]};
+        *reinterpret_cast<f32x4*>(Cg + (int64_t)(m0 + m) * N + n0 + wn * 128 + j * 32 + qd * 8 +
                                   fk * 4) = v;
       }
   }
@@ -2283,8 +2471,14 @@ hipError_t launch_wgrad(const void* a, int lda, const void* b, int ldb, const in
                         int E, int M, int N, float* C, float* Cs, hipStream_t s) {
   const int64_t tiles = (int64_t)G * (M / 128) * (N / 128);
   if (tiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL(gemm_wgrad_tn_kernel, dim3((unsigned)tiles), dim3(256), 0, s, (const bf16*)a,
-                     lda, (const bf16*)b, ldb, so, G, E, M, N, C, Cs);
+  // 256 x 256 tiles where they number at least one per CU
+  const int64_t big = M % 256 == 0 && N % 256 == 0 ? (int64_t)G * (M / 256) * (N / 256) : 0;
+  if (big >= 256)
+    hipLaunchKernelGGL(gemm_wgrad_tn_big_kernel, dim3((unsigned)big), dim3(256), 0, s,
+                       (const bf16*)a, lda, (const bf16*)b, ldb, so, G, E, M, N, C, Cs);
+  else
+    hipLaunchKernelGGL(gemm_wgrad_tn_kernel, dim3((unsigned)tiles), dim3(256), 0, s, (const bf16*)a,
+                       lda, (const bf16*)b, ldb, so, G, E, M, N, C, Cs);
   return hipGetLastError();
 }
 
