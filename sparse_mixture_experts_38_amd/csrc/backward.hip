@@ -383,7 +383,8 @@ __global__ __launch_bounds__(256) void gate_wgrad_kernel(const bf16* __restrict_
                                                          float* __restrict__ partial) {
   __shared__ float red[3][64][65];
   const int e0 = blockIdx.x * 8;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // the wave index is uniform: the token rows of dlogits are read with scalar loads
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int c = (blockIdx.y * 64 + lane) * 8;
   const int64_t t0 = (int64_t)blockIdx.z * slice_len;
   const int64_t t1 = t0 + slice_len < T ? t0 + slice_len : T;
@@ -393,21 +394,17 @@ __global__ __launch_bounds__(256) void gate_wgrad_kernel(const bf16* __restrict_
 #pragma unroll
     for (int u = 0; u < 8; ++u) acc[e][u] = 0.f;
   if (c < d) {
-    // four tokens per iteration, their loads issued together
-    for (int64_t tb = t0 + wave; tb < t1; tb += 16) {
-      float xv[4][8];
+    // eight tokens per iteration, their loads issued together (tokens past the
+    // slice re-read its last token and are not added)
+    for (int64_t tb = t0 + wave; tb < t1; tb += 32) {
+      float xv[8][8];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t t = tb + 4 * q;
-        if (t < t1) {
-          load8(x + t * d + c, xv[q]);
-        } else {
-#pragma unroll
-          for (int u = 0; u < 8; ++u) xv[q][u] = 0.f;
-        }
+      for (int q = 0; q < 8; ++q) {
+        const int64_t t = min(tb + 4 * q, t1 - 1);
+        load8(x + t * d + c, xv[q]);
       }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < 8; ++q) {
         const int64_t t = tb + 4 * q;
         if (t < t1) {
           const float* dl = dlogits + t * E + e0;

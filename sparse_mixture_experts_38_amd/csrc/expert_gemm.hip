@@ -1043,14 +1043,15 @@ __global__ __launch_bounds__(256, 1) void gemm_wgrad_tn_big_kernel(
 // same conflict-free layout as the 128 x 128 kernel. The epilogue adds the
 // bias, applies the activation, stages the bf16 tile in LDS and writes whole
 // 512-byte row segments.
-template <int EPI, bool HAS_BIAS>
+template <int EPI, bool HAS_BIAS, bool KMB = false>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(
     const bf16* __restrict__ A, const bf16* __restrict__ W, const bf16* __restrict__ W3,
     const float* __restrict__ bias, const bf16* __restrict__ Ws, const bf16* __restrict__ Ws3,
     const float* __restrict__ bias_s, int E, int G, const int32_t* __restrict__ offsets,
     int rows_max, bf16* __restrict__ C, int N, int K, const int32_t* __restrict__ arows,
-    uint32_t a_bytes, int skip_rows, int skip_last) {
+    uint32_t a_bytes, int skip_rows, int skip_last, int ksplit) {
   constexpr bool GATED = EPI == EPI_SWIGLU;
+  static_assert(!KMB || !GATED, "K-major weights: ungated GEMMs");
   constexpr int BM = 256, BK = 64, CH = BK / 8;   // 8 chunks of 16 B per LDS row
   constexpr int NB = GATED ? 2 : 1;
   constexpr int BN = GATED ? 128 : 256;           // columns per B operand = output columns
@@ -1086,8 +1087,12 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(
   row0 = __builtin_amdgcn_readfirstlane(row0);
   nrows = __builtin_amdgcn_readfirstlane(nrows);   // BM: part 1 has only full tiles
   const int n0 = nt * BN;
-  const bf16* Wg = g < E ? W + (int64_t)g * N * K : Ws;
-  const bf16* W3g = GATED ? (g < E ? W3 + (int64_t)g * N * K : Ws3) : Wg;
+  // KMB: W_g [K][N] at W + g ksplit N for K rows below ksplit, W3_g for the
+  // rest (as gemm_bf16_kernel's KMB)
+  const bf16* Wg = KMB ? (g < E ? W + (int64_t)g * ksplit * N : Ws)
+                       : (g < E ? W + (int64_t)g * N * K : Ws);
+  const bf16* W3g = KMB ? (g < E ? (W3 ? W3 + (int64_t)g * ksplit * N : Wg) : (Ws3 ? Ws3 : Wg))
+                        : (GATED ? (g < E ? W3 + (int64_t)g * N * K : Ws3) : Wg);
   const float* bg = HAS_BIAS ? (g < E ? bias + (int64_t)g * N : bias_s) : nullptr;
 
   const int tid = threadIdx.x;
@@ -1113,6 +1118,9 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(
     wbase = arows ? reinterpret_cast<const char*>(A)
                   : reinterpret_cast<const char*>(A + (int64_t)(row0 + wave * 128) * K);
     wbytes = arows ? a_bytes : 128u * (uint32_t)K * 2u;
+  } else if (KMB) {
+    wbase = reinterpret_cast<const char*>(Wg + n0);   // per K step: MOE_KRS
+    wbytes = 0u;
   } else {
     wbase = reinterpret_cast<const char*>(GATED ? (wave == 2 ? Wg : W3g) + (int64_t)n0 * K
                                                 : Wg + (int64_t)(n0 + (wave - 2) * 128) * K);
@@ -1127,7 +1135,21 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(
     const uint32_t rowoff = wave < 2 && arows ? (uint32_t)arows[row0 + wave * 128 + rl] * (uint32_t)K * 2u
                                               : (uint32_t)rl * (uint32_t)K * 2u;
     doff[i] = rowoff + (uint32_t)(pc ^ ((4 * (i & 1) + lq) & 7)) * 16u;
+    if (KMB && wave >= 2) {
+      // K-major W: K rows 32 (wave - 2) + 2 i + lane / 32 of the step, 512 bytes
+      // (256 columns) each, physical chunk lane & 31 holding logical chunk
+      // (lane & 31) ^ 4 (row & 3)
+      const int kr = 32 * (wave - 2) + 2 * i + (lane >> 5);
+      doff[i] = (uint32_t)(kr * N + ((lane & 31) ^ ((kr & 3) << 2)) * 8) * 2u;
+    }
   }
+  // KMB: the buffer descriptor of K step kt for the W waves (64 K rows of W_g,
+  // or of W3_g from ksplit on, columns n0 ..; scalar)
+#define MOE_KRS(kt)                                                                  \
+  __builtin_amdgcn_make_buffer_rsrc(                                                 \
+      (void*)(((kt) * BK < ksplit ? Wg + (int64_t)(kt) * BK * N                      \
+                                  : W3g + (int64_t)((kt) * BK - ksplit) * N) + n0),  \
+      (short)0, BK * N * 2, 0x00020000)
   const int dl = wave * 128 * CH;
   // L2 prefetch: in phase k (below), which loads step k + 1, each lane also
   // loads one dword of the 128-byte K chunk of step k + 3 for rows l and
@@ -1141,9 +1163,22 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(
     const int rl = lane + 64 * j;
     pfo[j] = wave < 2 && arows ? (uint32_t)arows[row0 + wave * 128 + rl] * (uint32_t)K * 2u
                                : (uint32_t)rl * (uint32_t)K * 2u;
+    // KMB W waves: one dword of each 128-byte line of the wave's 32 K rows
+    if (KMB && wave >= 2)
+      pfo[j] = (uint32_t)((32 * (wave - 2) + (rl >> 2)) * N + (rl & 3) * 64) * 2u;
   }
   const int nk = K / BK;   // K is a multiple of 256, so nk >= 4 and even
 
+  // KMB: byte offsets of the W fragments (f = 4..7, W sub-tile f - 4) in a
+  // stage, read transposed (+ 8192 per 16-row sub-step)
+  uint32_t fo[4];
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb) {
+    const int x = lane & 15, hq = (lane >> 4) & 1;
+    const int krow = 8 * fk + (x >> 2);
+    const int ch = wn * 16 + jb * 4 + 2 * hq + ((x & 3) >> 1);
+    fo[jb] = (uint32_t)((256 * CH + krow * 32 + (ch ^ ((krow & 3) << 2))) * 16 + (x & 1) * 8);
+  }
   int fbase[8];
 #pragma unroll
   for (int f = 0; f < 8; ++f) {
@@ -1169,10 +1204,16 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(
 #define MOE_SM(x) ((x) == 0 ? sm0 : sm1)
 #define MOE_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 #define MOE_D(x, kt, i)                                                              \
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, MOE_LDS(MOE_SM(x) + dl + (i) * 8 * CH), 16, \
-                                           doff[i], (uint32_t)(kt) * (BK * 2), 0, 0)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(KMB && wave >= 2 ? MOE_KRS(kt) : rsrc,   \
+                                           MOE_LDS(MOE_SM(x) + dl + (i) * 8 * CH), 16, doff[i], \
+                                           KMB && wave >= 2 ? 0u : (uint32_t)(kt) * (BK * 2), 0, 0)
 #define MOE_R(F, x, s4, f)                                                           \
-  F[f] = __builtin_bit_cast(bf16x8, MOE_SM(x)[fbase[f] + cidx[s4]])
+  do {                                                                               \
+    if (KMB && (f) >= 4)                                                             \
+      F[f] = lds_tr_frag<512>(MOE_SM(x), (uint32_t)((s4) * 8192) + fo[(f) & 3]);    \
+    else                                                                             \
+      F[f] = __builtin_bit_cast(bf16x8, MOE_SM(x)[fbase[f] + cidx[s4]]);            \
+  } while (0)
 #define MOE_M(F, q)                                                                  \
   acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F[4 + ((q) >> 2)], F[(q) & 3], acc[q], 0, 0, 0)
   // wait for this wave's direct-to-LDS loads (vmcnt 0, expcnt and lgkmcnt free)
@@ -1181,9 +1222,11 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(
 #define MOE_WAIT_LOADS_PF() __builtin_amdgcn_s_waitcnt(2 | (7 << 4) | (15 << 8))
 #define MOE_PF(kt)                                                                   \
   do {                                                                               \
-    const uint32_t o_ = (uint32_t)min((kt), nk - 1) * (BK * 2);                      \
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, MOE_LDS(pf_lds + wave * 128), 4, pfo[0], o_, 0, 0); \
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, MOE_LDS(pf_lds + wave * 128 + 64), 4, pfo[1], o_, 0, 0); \
+    const bool kw_ = KMB && wave >= 2;                                               \
+    const __amdgpu_buffer_rsrc_t r_ = kw_ ? MOE_KRS(min((kt), nk - 1)) : rsrc;      \
+    const uint32_t o_ = kw_ ? 0u : (uint32_t)min((kt), nk - 1) * (BK * 2);           \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r_, MOE_LDS(pf_lds + wave * 128), 4, pfo[0], o_, 0, 0); \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r_, MOE_LDS(pf_lds + wave * 128 + 64), 4, pfo[1], o_, 0, 0); \
   } while (0)
   // One K step from stage x: 64 MFMAs in four sub-steps; each MFMA is
   // followed by one fragment read of the next sub-step, and every third of
@@ -1259,6 +1302,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(
 #undef MOE_LDS
 #undef MOE_SUB
 #undef MOE_PHASE
+#undef MOE_KRS
 
   // Epilogue: rows 0..127 of the tile are staged in sm0, rows 128..255 in sm1
   // (wave row half wm); chunk q of row m at q ^ (m & 15). Every fragment read
@@ -2227,17 +2271,17 @@ static hipError_t gemm_launch(const moe_config& c, const ET* A, const void* W, c
       }
     }
     // (the backward epilogues EPI_DGELU / EPI_DRELU exist in the 128 x 128 kernel only)
-    const bool big = !KMB && rows >= kGemmBigBM && EPI == EPI_NONE && N <= 4096 &&
+    const bool big = rows >= kGemmBigBM && EPI == EPI_NONE && N <= 4096 &&
                      EPI != EPI_DGELU && EPI != EPI_DRELU && a_bytes < ((int64_t)1 << 32);
     if (big) {
       // full 256-row tiles of each group, then the rows left over (< 256 per
       // group) in 128-row tiles; both grids are bounds, surplus blocks exit
       const unsigned big_tiles = (unsigned)(rows / kGemmBigBM) * (unsigned)(N / BNB);
-      if constexpr (EPI != EPI_DGELU && EPI != EPI_DRELU && !KMB)
-        hipLaunchKernelGGL((gemm_bf16_big_kernel<EPI, HB>), dim3(big_tiles), dim3(256), 0, s, A,
+      if constexpr (EPI != EPI_DGELU && EPI != EPI_DRELU)
+        hipLaunchKernelGGL((gemm_bf16_big_kernel<EPI, HB, KMB>), dim3(big_tiles), dim3(256), 0, s, A,
                            (const bf16*)W, (const bf16*)W3, bias, (const bf16*)Ws, (const bf16*)Ws3,
                            bias_s, E, G, offsets, (int)rows, C, N, K, arows, (uint32_t)a_bytes,
-                           skip, skip_last);
+                           skip, skip_last, ksplit);
       // each group leaves at most 255 rows, i.e. at most 2 tiles, and the
       // tiles number at most ceil(rows / 128) + G
       const int64_t rest = (rows + 127) / 128 + G < 2 * G ? (rows + 127) / 128 + G : 2 * G;
