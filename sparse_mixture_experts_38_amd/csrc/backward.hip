@@ -345,6 +345,39 @@ __global__ __launch_bounds__(256) void colsum_rows_kernel(const bf16* __restrict
   }
 }
 
+// db[g][c] = sum of the column sums of group g's 128-row M tiles (written by
+// the dZ GEMM), in tile order. Group g's tiles follow those of the groups
+// before it, ceil(rows / 128) tiles for a group of rows = o[g + 1] - o[g] > 0
+// (o: offsets clamped to [0, rows_max]), as the GEMM's tile space counts them;
+// tiles past cap (the partial buffer: only with malformed offsets) are left
+// out. Routed groups write db + g C, the shared expert (g == E) writes dbs.
+__global__ __launch_bounds__(256) void colsum_tiles_reduce_kernel(
+    const float* __restrict__ partial, const int32_t* __restrict__ off, int G, int E,
+    int64_t rows_max, int C, int cap, float* __restrict__ db, float* __restrict__ dbs) {
+  __shared__ int s_first, s_n;
+  const int g = blockIdx.y;
+  if (threadIdx.x == 0) {
+    int first = 0, prev = clamp_off(off, 0, rows_max);
+    for (int gi = 0; gi < g; ++gi) {
+      const int nx = clamp_off(off, gi + 1, rows_max);
+      first += nx > prev ? (nx - prev + 127) / 128 : 0;
+      prev = nx;
+    }
+    const int nx = clamp_off(off, g + 1, rows_max);
+    s_first = first;
+    s_n = nx > prev ? (nx - prev + 127) / 128 : 0;
+  }
+  __syncthreads();
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= C) return;
+  const int first = s_first;
+  const int n = first + s_n <= cap ? s_n : (first < cap ? cap - first : 0);
+  float acc = 0.f;
+  for (int i = 0; i < n; ++i) acc += partial[(int64_t)(first + i) * C + c];
+  if (g < E) db[(int64_t)g * C + c] = acc;
+  else dbs[c] = acc;
+}
+
 // db[g][c] = sum of the column-sum partials of group g's 64-row blocks, in
 // block order (deterministic). Routed groups write db + g C, the shared expert
 // (g == E) writes dbs.
@@ -705,11 +738,17 @@ hipError_t launch_backward_misc(const moe_config& c, const BwdLayout& B, const v
                        (const bf16*)dyp, d, d, (const int32_t*)so, (const int32_t*)po, G, p2);
     hipLaunchKernelGGL(colsum_reduce_kernel, dim3((d + 255) / 256, G), dim3(256), 0, s,
                        (const float*)p2, d, (const int32_t*)po, d, E, gr.db2, gr.dbs2);
-    // b1 sits on W1 only: the dz1 columns
-    hipLaunchKernelGGL(colsum_rows_kernel, dim3(kb, (F + 511) / 512), dim3(256), 0, s, dz, NZ * F,
-                       F, (const int32_t*)so, (const int32_t*)po, G, p1);
-    hipLaunchKernelGGL(colsum_reduce_kernel, dim3((F + 255) / 256, G), dim3(256), 0, s,
-                       (const float*)p1, F, (const int32_t*)po, F, E, gr.db1, gr.dbs1);
+    // b1 sits on W1 only: the dz1 columns (GELU / ReLU: tile sums from the dZ GEMM)
+    if (sw) {
+      hipLaunchKernelGGL(colsum_rows_kernel, dim3(kb, (F + 511) / 512), dim3(256), 0, s, dz, NZ * F,
+                         F, (const int32_t*)so, (const int32_t*)po, G, p1);
+      hipLaunchKernelGGL(colsum_reduce_kernel, dim3((F + 255) / 256, G), dim3(256), 0, s,
+                         (const float*)p1, F, (const int32_t*)po, F, E, gr.db1, gr.dbs1);
+    } else {
+      hipLaunchKernelGGL(colsum_tiles_reduce_kernel, dim3((F + 255) / 256, G), dim3(256), 0, s,
+                         (const float*)p1, r.expert_offsets, G, E, rmax, F,
+                         (int)(B.ldk / 64), gr.db1, gr.dbs1);
+    }
   }
   hipLaunchKernelGGL(gate_wgrad_kernel, dim3((E + 7) / 8, (d + 511) / 512, B.gate_slices), dim3(256), 0, s,
                      (const bf16*)x, (const float*)dlogits, T, d, E, (int)B.gate_slice_len,

@@ -235,7 +235,8 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
     const float* __restrict__ bias, const bf16* __restrict__ Ws, const bf16* __restrict__ Ws3,
     const float* __restrict__ bias_s, int E, int G, const int32_t* __restrict__ offsets,
     int rows_max, void* __restrict__ Cv, int N, int K, int part, const int32_t* __restrict__ arows,
-    int kparts, const bf16* __restrict__ Zin, int skip_rows, int skip_last, int ksplit) {
+    int kparts, const bf16* __restrict__ Zin, int skip_rows, int skip_last, int ksplit,
+    float* __restrict__ colsum, int colsum_tiles) {
   constexpr bool GATED = EPI == EPI_SWIGLU;
   static_assert(!KMB || (!GATED && EPI != EPI_PARTIAL), "K-major weights: ungated backward GEMMs");
   constexpr bool DACT = EPI == EPI_DGELU || EPI == EPI_DRELU;
@@ -270,7 +271,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
   if (it >= items) return;
   const int t8 = tiles & ~7;
   const int per_group = GROUP_M * ntn;
-  int g, row0, nrows, n0;
+  int g, row0, nrows, n0, mtile;
   const bf16* Wg;
   const bf16* W3g;
   const float* bg;
@@ -312,6 +313,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
     const int gm = min(mtiles - first_m, GROUP_M);
     const int mt = first_m + in % gm;
     const int nt = in / gm;
+    mtile = mt;
     tile_lookup(ts, mt, BM, g, row0, nrows);
     // uniform over the block: keep them in scalar registers
     g = __builtin_amdgcn_readfirstlane(g);
@@ -500,7 +502,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
   // The registers r0 / r1 are free now: the first two K steps of this block's
   // next tile are loaded into them before the epilogue of this one, so their
   // latency is spent under the epilogue instead of before the next K loop.
-  const int cur_row0 = row0, cur_nrows = nrows, cur_n0 = n0, cur_kp = kp;
+  const int cur_row0 = row0, cur_nrows = nrows, cur_n0 = n0, cur_kp = kp, cur_mt = mtile;
   const float* cur_bg = bg;
   const int itn = it + P;
   const bool more = itn < items;
@@ -538,7 +540,10 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
     // distinct chunks; then thread t takes 8 consecutive columns of rows
     // t / 16 + 16 p, reading z and writing dZ with whole 256-byte row segments.
     // The z loads are issued right after the staging writes (the accumulators
-    // are free then), so that their latency is spent in the barrier.
+    // are free then), so that their latency is spent in the barrier. With
+    // colsum, the tile's column sums of the rounded dZ (rows in order: each
+    // thread's 8 rows, then the 16 row groups) go to colsum[mt][n] for M tile mt
+    // of the tile space (the bias gradient adds a group's tiles in order).
     __syncthreads();   // every wave is done reading the operand stages
     f32x4* st4 = reinterpret_cast<f32x4*>(smem);
 #pragma unroll
@@ -564,6 +569,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
                             : z0;
     }
     __syncthreads();
+    float cs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
       const int m = (tid >> 4) + 16 * p;
@@ -582,6 +588,26 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
         }
         const u32x4 ov = {o[0], o[1], o[2], o[3]};
         *reinterpret_cast<u32x4*>(C + (int64_t)(cur_row0 + m) * N + cur_n0 + (tid & 15) * 8) = ov;
+        if (colsum) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            cs[2 * e] += bf16_bits_to_f32(o[e] & 0xffffu);
+            cs[2 * e + 1] += bf16_bits_to_f32(o[e] >> 16);
+          }
+        }
+      }
+    }
+    if (colsum) {
+      __syncthreads();   // the staged tile has been read
+      float* red = reinterpret_cast<float*>(smem);   // [16 row groups][128 columns]
+#pragma unroll
+      for (int e = 0; e < 8; ++e) red[(tid >> 4) * 128 + (tid & 15) * 8 + e] = cs[e];
+      __syncthreads();
+      if (tid < 128 && cur_mt < colsum_tiles) {   // (tiles past the buffer: malformed offsets)
+        float sum = 0.f;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) sum += red[q * 128 + tid];
+        colsum[(int64_t)cur_mt * N + cur_n0 + tid] = sum;
       }
     }
   } else {
@@ -2186,7 +2212,7 @@ static hipError_t gemm_launch(const moe_config& c, const ET* A, const void* W, c
                               const float* bias_s, const int32_t* offsets, ET* C, int N, int K,
                               hipStream_t s, const int32_t* arows = nullptr,
                               const bf16* zin = nullptr, const void* wpacked = nullptr,
-                              int ksplit = 0) {
+                              int ksplit = 0, float* colsum = nullptr, int colsum_tiles = 0) {
   static_assert(!KMB || sizeof(ET) == 2, "K-major weights: bf16 only");
   const int E = c.num_experts, G = c.num_experts + c.num_shared_experts;
   const int64_t rows = rows_max(c);
@@ -2289,14 +2315,14 @@ static hipError_t gemm_launch(const moe_config& c, const ET* A, const void* W, c
       hipLaunchKernelGGL((gemm_bf16_kernel<EPI, HB, KMB>), dim3((unsigned)rgrid), dim3(256), 0, s, A,
                          (const bf16*)W, (const bf16*)W3, bias, (const bf16*)Ws, (const bf16*)Ws3,
                          bias_s, E, G, offsets, (int)rows, C, N, K, 2, arows, 1, zin, skip,
-                         skip_last, ksplit);
+                         skip_last, ksplit, (float*)nullptr, 0);
     } else {
       const int64_t tiles = ((rows + 127) / 128 + G) * (N / BN);
       const int64_t grid = tiles < slots ? tiles : slots;
       hipLaunchKernelGGL((gemm_bf16_kernel<EPI, HB, KMB>), dim3((unsigned)grid), dim3(256), 0, s, A,
                          (const bf16*)W, (const bf16*)W3, bias, (const bf16*)Ws, (const bf16*)Ws3,
                          bias_s, E, G, offsets, (int)rows, C, N, K, 0, arows, 1, zin, skip,
-                         skip_last, ksplit);
+                         skip_last, ksplit, colsum, colsum_tiles);
     }
   } else {
     const unsigned mtiles = (unsigned)((rows + kGemmBM - 1) / kGemmBM) + G;
@@ -2359,7 +2385,7 @@ hipError_t launch_router_gemm(const moe_config& c, const void* x, const void* w_
                      (const bf16*)x, (const bf16*)w_gate, (const bf16*)nullptr, (const float*)nullptr,
                      (const bf16*)nullptr, (const bf16*)nullptr, (const float*)nullptr, 1, 1,
                      (const int32_t*)nullptr, (int)T, (void*)partials, E, K, 0,
-                     (const int32_t*)nullptr, kp, (const bf16*)nullptr, 0, 0, 0);
+                     (const int32_t*)nullptr, kp, (const bf16*)nullptr, 0, 0, 0, (float*)nullptr, 0);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int64_t n4 = T * E / 4;
@@ -2418,16 +2444,16 @@ hipError_t launch_expert_down(const moe_config& c, const void* h, const int32_t*
 // W2 [d][F] per group is the K-major B operand of dYp W2 (K = d, N = F).
 hipError_t launch_backward_dz(const moe_config& c, const void* dyp, const int32_t* offsets,
                               const void* w2, const void* ws2, const void* z, void* dz,
-                              hipStream_t s) {
+                              float* colsum, int colsum_tiles, hipStream_t s) {
   const int N = (int)c.d_ff, K = (int)c.d_model;
   if (c.activation == MOE_ACT_GELU)
     return gemm_launch<bf16, EPI_DGELU, false, true>(c, (const bf16*)dyp, w2, nullptr, nullptr, ws2,
                                                      nullptr, nullptr, offsets, (bf16*)dz, N, K, s,
-                                                     nullptr, (const bf16*)z, nullptr, K);
+                                                     nullptr, (const bf16*)z, nullptr, K, colsum, colsum_tiles);
   if (c.activation == MOE_ACT_RELU)
     return gemm_launch<bf16, EPI_DRELU, false, true>(c, (const bf16*)dyp, w2, nullptr, nullptr, ws2,
                                                      nullptr, nullptr, offsets, (bf16*)dz, N, K, s,
-                                                     nullptr, (const bf16*)z, nullptr, K);
+                                                     nullptr, (const bf16*)z, nullptr, K, colsum, colsum_tiles);
   // SwiGLU: dH itself (the elementwise step forms dz1 and du)
   return gemm_launch<bf16, EPI_NONE, false, true>(c, (const bf16*)dyp, w2, nullptr, nullptr, ws2,
                                                   nullptr, nullptr, offsets, (bf16*)dz, N, K, s,

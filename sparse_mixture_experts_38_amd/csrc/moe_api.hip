@@ -602,8 +602,11 @@ int moe_backward(const moe_config* cfg, const void* x, const moe_weights* w, con
   hipError_t e = launch_backward_misc(*cfg, B, x, *w, *r, stats, *saved, dy, aux_coef, z_coef, *g,
                                       ws, s, 0);
   if (e != hipSuccess) return MOE_ERR_HIP;
+  // GELU / ReLU with biases: the dZ GEMM also writes the column sums of its tiles
   e = launch_backward_dz(*cfg, ws + B.dyp, r->expert_offsets, w->w2, w->ws2, saved->z,
-                         ws + (swiglu ? B.dh : B.dz), s);
+                         ws + (swiglu ? B.dh : B.dz),
+                         cfg->has_bias && !swiglu ? (float*)(ws + B.colsum1) : nullptr,
+                         (int)(B.ldk / 64), s);
   if (e != hipSuccess) return MOE_ERR_HIP;
   if (swiglu) {
     e = launch_dswiglu(*cfg, ws + B.dh, saved->z, ws + B.dz, r->expert_offsets, s);

@@ -271,10 +271,13 @@ hipError_t launch_backward_misc(const moe_config& c, const BwdLayout& B, const v
 // dZ = (dYp W2) * act'(z) per group: dYp [rows][d], W2 [E][d][F] and Ws2 [d][F]
 // (the shared expert) as stored, z and dZ [rows][F] bf16 (GELU, ReLU); for
 // SwiGLU the product dH = dYp W2 alone, which launch_dswiglu turns into
-// dZ = [dz1 | du].
+// dZ = [dz1 | du]. GELU / ReLU with colsum != nullptr: also the column sums of
+// each 128-row M tile of dZ, colsum[mt][F] (mt: the tile's index in group
+// order, ceil(rows_g / 128) tiles per group; colsum_tiles_reduce_kernel adds
+// them per group) for the tiles mt < colsum_tiles.
 hipError_t launch_backward_dz(const moe_config& c, const void* dyp, const int32_t* expert_offsets,
                               const void* w2, const void* ws2, const void* z, void* dz,
-                              hipStream_t stream);
+                              float* colsum, int colsum_tiles, hipStream_t stream);
 // dXp = dZ W1 per group (SwiGLU: [dz1 | du] [W1; W3], K = 2F): W1, W3 [E][F][d]
 // and Ws1, Ws3 [F][d] as stored; dXp [rows][d] bf16.
 hipError_t launch_dswiglu(const moe_config& c, const void* dh, const void* z, void* dz,
