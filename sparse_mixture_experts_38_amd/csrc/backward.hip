@@ -354,18 +354,19 @@ __global__ __launch_bounds__(256) void colsum_rows_kernel(const bf16* __restrict
 __global__ __launch_bounds__(256) void colsum_tiles_reduce_kernel(
     const float* __restrict__ partial, const int32_t* __restrict__ off, int G, int E,
     int64_t rows_max, int C, int cap, float* __restrict__ db, float* __restrict__ dbs) {
+  __shared__ int s_tiles[MOE_MAX_EXPERTS + 1];
   __shared__ int s_first, s_n;
   const int g = blockIdx.y;
+  for (int gi = threadIdx.x; gi < G; gi += blockDim.x) {
+    const int a = clamp_off(off, gi, rows_max), b = clamp_off(off, gi + 1, rows_max);
+    s_tiles[gi] = b > a ? (b - a + 127) / 128 : 0;
+  }
+  __syncthreads();
   if (threadIdx.x == 0) {
-    int first = 0, prev = clamp_off(off, 0, rows_max);
-    for (int gi = 0; gi < g; ++gi) {
-      const int nx = clamp_off(off, gi + 1, rows_max);
-      first += nx > prev ? (nx - prev + 127) / 128 : 0;
-      prev = nx;
-    }
-    const int nx = clamp_off(off, g + 1, rows_max);
+    int first = 0;
+    for (int gi = 0; gi < g; ++gi) first += s_tiles[gi];
     s_first = first;
-    s_n = nx > prev ? (nx - prev + 127) / 128 : 0;
+    s_n = s_tiles[g];
   }
   __syncthreads();
   const int c = blockIdx.x * 256 + threadIdx.x;
@@ -373,7 +374,15 @@ __global__ __launch_bounds__(256) void colsum_tiles_reduce_kernel(
   const int first = s_first;
   const int n = first + s_n <= cap ? s_n : (first < cap ? cap - first : 0);
   float acc = 0.f;
-  for (int i = 0; i < n; ++i) acc += partial[(int64_t)(first + i) * C + c];
+  int i = 0;
+  for (; i + 8 <= n; i += 8) {   // eight loads in flight, added in tile order
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = partial[(int64_t)(first + i + u) * C + c];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += v[u];
+  }
+  for (; i < n; ++i) acc += partial[(int64_t)(first + i) * C + c];
   if (g < E) db[(int64_t)g * C + c] = acc;
   else dbs[c] = acc;
 }

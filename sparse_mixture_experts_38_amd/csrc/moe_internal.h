@@ -261,8 +261,8 @@ hipError_t launch_backward_f32(const moe_config& c, const BwdLayout& B, const vo
                                const moe_saved& sv, const void* dy, float aux_coef, float z_coef,
                                const moe_grads& gr, char* ws, hipStream_t stream);
 // The non-GEMM steps of the backward: phase 0 (combine and router backward,
-// padded offsets) before the dZ / dX GEMMs, phase 1 (row
-// transposes, weight, bias and router gradients, dx) after them.
+// padded offsets) before the dZ / dX GEMMs, phase 1 (the expert-sorted x rows,
+// weight, bias and router gradients, dx) after them.
 hipError_t launch_backward_misc(const moe_config& c, const BwdLayout& B, const void* x,
                                 const moe_weights& w, const moe_routing& r, const moe_stats* stats,
                                 const moe_saved& sv, const void* dy, float aux_coef, float z_coef,
