@@ -236,9 +236,9 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
     const float* __restrict__ bias_s, int E, int G, const int32_t* __restrict__ offsets,
     int rows_max, void* __restrict__ Cv, int N, int K, int part, const int32_t* __restrict__ arows,
     int kparts, const bf16* __restrict__ Zin, int skip_rows, int skip_last, int ksplit,
-    float* __restrict__ colsum, int colsum_tiles) {
+    float* __restrict__ colsum, int aux_tiles) {
   constexpr bool GATED = EPI == EPI_SWIGLU;
-  static_assert(!KMB || (!GATED && EPI != EPI_PARTIAL), "K-major weights: ungated backward GEMMs");
+  static_assert(!KMB || !GATED, "K-major weights: ungated backward GEMMs");
   constexpr bool DACT = EPI == EPI_DGELU || EPI == EPI_DRELU;
   constexpr int BM = 128, BK = 64, CH = BK / 8;   // 8 chunks of 16 B per LDS row
   constexpr int NB = GATED ? 2 : 1;
@@ -515,21 +515,26 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
   }
 
   if constexpr (EPI == EPI_PARTIAL) {
-    // float32 sums straight to plane cur_kp of C ([kparts][rows_max][N]):
-    // lane (fr, fk) holds 4 consecutive columns of each 8-column group
-    float* __restrict__ Cp = reinterpret_cast<float*>(Cv) + (int64_t)cur_kp * rows_max * N;
+    // float32 sums straight to plane cur_kp of C: [kparts][rows_max][N] by row,
+    // or with aux_tiles > 0 [kparts][aux_tiles * 128][N] by M tile (row
+    // 128 mt + m; tiles from aux_tiles on are not written: only malformed
+    // offsets make that many). Lane (fr, fk) holds 4 consecutive columns of each
+    // 8-column group.
+    const int64_t prow = aux_tiles > 0 ? (int64_t)cur_mt * BM : cur_row0;
+    const int64_t plane = aux_tiles > 0 ? (int64_t)aux_tiles * BM : rows_max;
+    float* __restrict__ Cp = reinterpret_cast<float*>(Cv) + (int64_t)cur_kp * plane * N;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int m = wm * 64 + i * 32 + fr;
-      if (m < cur_nrows) {
+      if (m < cur_nrows && (aux_tiles == 0 || cur_mt < aux_tiles)) {
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
           for (int qd = 0; qd < 4; ++qd) {
             const f32x4 v = {acc[i + 2 * j][qd * 4 + 0], acc[i + 2 * j][qd * 4 + 1],
                              acc[i + 2 * j][qd * 4 + 2], acc[i + 2 * j][qd * 4 + 3]};
-            *reinterpret_cast<f32x4*>(Cp + (int64_t)(cur_row0 + m) * N + cur_n0 + wn * WN + j * 32 +
-                                      qd * 8 + fk * 4) = v;
+            *reinterpret_cast<f32x4*>(Cp + (prow + m) * N + cur_n0 + wn * WN + j * 32 + qd * 8 +
+                                      fk * 4) = v;
           }
       }
     }
@@ -603,7 +608,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) red[(tid >> 4) * 128 + (tid & 15) * 8 + e] = cs[e];
       __syncthreads();
-      if (tid < 128 && cur_mt < colsum_tiles) {   // (tiles past the buffer: malformed offsets)
+      if (tid < 128 && cur_mt < aux_tiles) {   // (tiles past the buffer: malformed offsets)
         float sum = 0.f;
 #pragma unroll
         for (int q = 0; q < 16; ++q) sum += red[q * 128 + tid];
@@ -2190,6 +2195,83 @@ static int* stream_sched_slot() {
 
 // Block slots of the persistent 128 x 128 kernel on the current device: two
 // per CU, a multiple of 8 (one share per XCD), cached per device.
+// Left-over rows of the tiled path (tile space part 2: each group's rows past
+// its full 256-row tiles) split along K: kparts float32 planes of the rest
+// tiles, [kparts][cap 128][N] by M tile, written by gemm_bf16_kernel<EPI_PARTIAL>
+// and added here in plane order, then the bias and the rounding:
+// C[row0 + m][n] = bf16(sum_kp P[kp][128 mt + m][n] + b_g[n]). Block: M tile
+// blockIdx.x, 4 of its rows (blockIdx.y), 8 columns per thread, the planes'
+// loads issued together.
+template <bool HAS_BIAS>
+__global__ __launch_bounds__(256) void rest_reduce_kernel(
+    const float* __restrict__ P, int kparts, int cap, const int32_t* __restrict__ offsets, int G,
+    int E, int rows_max, int skip_rows, int skip_last, const float* __restrict__ bias,
+    const float* __restrict__ bias_s, int N, bf16* __restrict__ C) {
+  TileSpace ts;
+  tile_space_init(ts, offsets, G, rows_max, 128, 2, kGemmBigBM, skip_rows, skip_last);
+  const int mt = blockIdx.x;
+  if (mt >= ts.total || mt >= cap) return;
+  int g, row0, nrows;
+  tile_lookup(ts, mt, 128, g, row0, nrows);
+  const float* bg = HAS_BIAS ? (g < E ? bias + (int64_t)g * N : bias_s) : nullptr;
+  const int c8 = N / 8;
+  const int64_t plane = (int64_t)cap * 128 * N;
+  for (int idx = threadIdx.x; idx < 4 * c8; idx += 256) {
+    const int m = blockIdx.y * 4 + idx / c8;
+    const int c = (idx % c8) * 8;
+    if (m >= nrows) continue;
+    const float* p0 = P + ((int64_t)mt * 128 + m) * N + c;
+    float v[8], w[3][8];
+    load8(p0, v);
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {   // planes 1..3 (kparts <= 4)
+      if (q + 1 < kparts) {
+        load8(p0 + (q + 1) * plane, w[q]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[q][e] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+      if (q + 1 < kparts) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] += w[q][e];
+      }
+    if (HAS_BIAS) {
+      float b[8];
+      load8(bg + c, b);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] += b[e];
+    }
+    store8(C + (int64_t)(row0 + m) * N + c, v);
+  }
+}
+
+// Plan of that split for a GEMM of N columns and K depth whose groups of at
+// most skip rows are streamed (skip 0: none): the rest tiles number at most
+// cap = 2 per group on the tiled path (groups of more than skip rows, at most
+// rows_max / (skip + 1) of them); split into kparts = 4 (2) ranges of at least
+// 4 K steps when they would otherwise fill under a quarter of the CU slots
+// (at most 256 tiles) and their planes fit 64 MiB. kparts 1: no split.
+RestSplit rest_split_plan(const moe_config& c, int N, int K, int skip) {
+  RestSplit r{1, 0, 0};
+  if (c.act_dtype != MOE_BF16 || N % 128 || K % 64) return r;
+  const int64_t G = c.num_experts + c.num_shared_experts;
+  const int64_t rows = rows_max(c);
+  int64_t cap = 2 * G;
+  if (skip > 0) cap = std::min<int64_t>(cap, 2 * (rows / (skip + 1)) + 2);
+  if (cap <= 0 || cap * (N / 128) > 256) return r;
+  const int nk = K / 64;
+  const int kp = nk % 8 == 0 && nk / 4 >= 4 ? 4 : (nk % 4 == 0 && nk / 2 >= 4 ? 2 : 1);
+  const size_t bytes = (size_t)kp * cap * 128 * N * 4;
+  if (kp == 1 || bytes > ((size_t)64 << 20)) return r;
+  r.kparts = kp;
+  r.cap = (int)cap;
+  r.bytes = bytes;
+  return r;
+}
+
 static int gemm_slots() {
   static int cached[64] = {0};
   int dev = 0;
@@ -2212,7 +2294,8 @@ static hipError_t gemm_launch(const moe_config& c, const ET* A, const void* W, c
                               const float* bias_s, const int32_t* offsets, ET* C, int N, int K,
                               hipStream_t s, const int32_t* arows = nullptr,
                               const bf16* zin = nullptr, const void* wpacked = nullptr,
-                              int ksplit = 0, float* colsum = nullptr, int colsum_tiles = 0) {
+                              int ksplit = 0, float* colsum = nullptr, int colsum_tiles = 0,
+                              float* rest_partial = nullptr, size_t rest_bytes = 0) {
   static_assert(!KMB || sizeof(ET) == 2, "K-major weights: bf16 only");
   const int E = c.num_experts, G = c.num_experts + c.num_shared_experts;
   const int64_t rows = rows_max(c);
@@ -2311,11 +2394,27 @@ static hipError_t gemm_launch(const moe_config& c, const ET* A, const void* W, c
       // each group leaves at most 255 rows, i.e. at most 2 tiles, and the
       // tiles number at most ceil(rows / 128) + G
       const int64_t rest = (rows + 127) / 128 + G < 2 * G ? (rows + 127) / 128 + G : 2 * G;
-      const int64_t rgrid = rest * (N / BN) < slots ? rest * (N / BN) : slots;
-      hipLaunchKernelGGL((gemm_bf16_kernel<EPI, HB, KMB>), dim3((unsigned)rgrid), dim3(256), 0, s, A,
-                         (const bf16*)W, (const bf16*)W3, bias, (const bf16*)Ws, (const bf16*)Ws3,
-                         bias_s, E, G, offsets, (int)rows, C, N, K, 2, arows, 1, zin, skip,
-                         skip_last, ksplit, (float*)nullptr, 0);
+      const RestSplit rs = rest_partial ? rest_split_plan(c, N, K, skip) : RestSplit{1, 0, 0};
+      if (rs.kparts > 1 && rs.bytes <= rest_bytes) {
+        // few left-over tiles with a long K (the DeepSpeed-GPT shape's GEMM 2
+        // and dX): split along K into float32 planes, then add them
+        const int64_t items = (int64_t)rs.cap * (N / 128) * rs.kparts;
+        hipLaunchKernelGGL((gemm_bf16_kernel<EPI_PARTIAL, false, KMB>),
+                           dim3((unsigned)(items < slots ? items : slots)), dim3(256), 0, s, A,
+                           (const bf16*)W, (const bf16*)W3, (const float*)nullptr, (const bf16*)Ws,
+                           (const bf16*)Ws3, (const float*)nullptr, E, G, offsets, (int)rows,
+                           (void*)rest_partial, N, K, 2, arows, rs.kparts, (const bf16*)nullptr,
+                           skip, skip_last, ksplit, (float*)nullptr, rs.cap);
+        hipLaunchKernelGGL((rest_reduce_kernel<HB>), dim3((unsigned)rs.cap, 32), dim3(256), 0, s,
+                           (const float*)rest_partial, rs.kparts, rs.cap, offsets, G, E, (int)rows,
+                           skip, skip_last, bias, bias_s, N, (bf16*)C);
+      } else {
+        const int64_t rgrid = rest * (N / BN) < slots ? rest * (N / BN) : slots;
+        hipLaunchKernelGGL((gemm_bf16_kernel<EPI, HB, KMB>), dim3((unsigned)rgrid), dim3(256), 0, s, A,
+                           (const bf16*)W, (const bf16*)W3, bias, (const bf16*)Ws, (const bf16*)Ws3,
+                           bias_s, E, G, offsets, (int)rows, C, N, K, 2, arows, 1, zin, skip,
+                           skip_last, ksplit, (float*)nullptr, 0);
+      }
     } else {
       const int64_t tiles = ((rows + 127) / 128 + G) * (N / BN);
       const int64_t grid = tiles < slots ? tiles : slots;
@@ -2422,16 +2521,20 @@ hipError_t launch_expert_up(const moe_config& c, const void* a, const int32_t* o
 }
 
 hipError_t launch_expert_down(const moe_config& c, const void* h, const int32_t* offsets,
-                              const ExpertWeights& w, void* y_perm, hipStream_t s) {
+                              const ExpertWeights& w, void* y_perm, hipStream_t s,
+                              void* rest_partial, size_t rest_bytes) {
   const int N = (int)c.d_model, K = (int)c.d_ff;
+  float* rp = (float*)rest_partial;
   if (c.act_dtype == MOE_BF16)
     return c.has_bias
                ? gemm_launch<bf16, EPI_NONE, true>(c, (const bf16*)h, w.w2, nullptr, w.b2, w.ws2,
                                                    nullptr, w.bs2, offsets, (bf16*)y_perm, N, K, s,
-                                                   nullptr, nullptr, w.down_packed)
+                                                   nullptr, nullptr, w.down_packed, 0, nullptr, 0,
+                                                   rp, rest_bytes)
                : gemm_launch<bf16, EPI_NONE, false>(c, (const bf16*)h, w.w2, nullptr, w.b2, w.ws2,
                                                     nullptr, w.bs2, offsets, (bf16*)y_perm, N, K,
-                                                    s, nullptr, nullptr, w.down_packed);
+                                                    s, nullptr, nullptr, w.down_packed, 0, nullptr,
+                                                    0, rp, rest_bytes);
   return c.has_bias
              ? gemm_launch<float, EPI_NONE, true>(c, (const float*)h, w.w2, nullptr, w.b2, w.ws2,
                                                   nullptr, w.bs2, offsets, (float*)y_perm, N, K, s)
@@ -2492,13 +2595,28 @@ hipError_t launch_expert_up_linear(const moe_config& c, const void* a, const int
 // SwiGLU the K steps from F on take W3 (dZ = [dz1 | du]).
 hipError_t launch_backward_dx(const moe_config& c, const void* dz, const int32_t* offsets,
                               const void* w1, const void* w3, const void* ws1, const void* ws3,
-                              void* dxp, hipStream_t s) {
+                              void* dxp, hipStream_t s, void* rest_partial, size_t rest_bytes) {
   const int N = (int)c.d_model, F = (int)c.d_ff;
   const bool sw = c.activation == MOE_ACT_SWIGLU;
   return gemm_launch<bf16, EPI_NONE, false, true>(c, (const bf16*)dz, w1, sw ? w3 : nullptr, nullptr,
                                                   ws1, sw ? ws3 : nullptr, nullptr, offsets,
                                                   (bf16*)dxp, N, sw ? 2 * F : F, s, nullptr, nullptr,
-                                                  nullptr, F);
+                                                  nullptr, F, nullptr, 0, (float*)rest_partial,
+                                                  rest_bytes);
+}
+
+// The streaming threshold gemm_launch applies: groups of at most kStreamMaxRows
+// rows are streamed for the forward epilogues when the A operand spans less
+// than 4 GiB; the K-major backward GEMMs stream nothing.
+size_t rest_partial_bytes(const moe_config& c, int which) {
+  if (c.act_dtype != MOE_BF16) return 0;
+  const int N = (int)c.d_model, F = (int)c.d_ff;
+  if (which == 0) {
+    const int64_t a_span = rows_max(c) * (int64_t)F * 2;
+    return rest_split_plan(c, N, F, a_span < ((int64_t)1 << 32) ? kStreamMaxRows : 0).bytes;
+  }
+  const int K = c.activation == MOE_ACT_SWIGLU ? 2 * F : F;
+  return rest_split_plan(c, N, K, 0).bytes;
 }
 
 size_t packed_weights_bytes(const moe_config& c, int which) {

@@ -44,6 +44,8 @@ WsLayout workspace_layout(const moe_config& c) {
   L.rows_max = A + (int64_t)S * T;
   const size_t es = c.act_dtype == MOE_BF16 ? 2 : 4;
   L.h = take((size_t)L.rows_max * c.d_ff * es);
+  L.rest_bytes = rest_partial_bytes(c, 0);
+  L.rest_partial = take(L.rest_bytes);
   L.end_ffn = off;
   L.y_perm = take((size_t)L.rows_max * c.d_model * es);
   L.total = off;
@@ -84,6 +86,8 @@ BwdLayout backward_layout(const moe_config& c) {
   B.gate_slice_len = (int)slice_len;
   B.gate_slices = (int)(T > 0 ? (T + slice_len - 1) / slice_len : 1);
   B.gate_partial = take((size_t)B.gate_slices * E * d * 4);
+  B.rest_bytes = rest_partial_bytes(c, 1);
+  B.rest_partial = take(B.rest_bytes);
   B.total = off;
   return B;
 }
@@ -321,7 +325,8 @@ int moe_expert_ffn(const moe_config* cfg, const void* x_perm, const int32_t* exp
   void* h = (char*)workspace + L.h;
   const hipError_t e = launch_expert_up(*cfg, x_perm, expert_offsets, w, h, (hipStream_t)stream);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  return hip_status(launch_expert_down(*cfg, h, expert_offsets, w, y_perm, (hipStream_t)stream));
+  return hip_status(launch_expert_down(*cfg, h, expert_offsets, w, y_perm, (hipStream_t)stream,
+                                       (char*)workspace + L.rest_partial, L.rest_bytes));
 }
 
 int moe_expert_up(const moe_config* cfg, const void* x_perm, const int32_t* expert_offsets,
@@ -403,7 +408,8 @@ int moe_forward_profiled(const moe_config* cfg, const void* x, const moe_weights
   void* h = ws + L.h;
   e = launch_expert_up(*cfg, x, r->expert_offsets, ew, h, s, r->row_token);
   if (e != hipSuccess || mark(MOE_EV_UP) != hipSuccess) return MOE_ERR_HIP;
-  e = launch_expert_down(*cfg, h, r->expert_offsets, ew, y_perm, s);
+  e = launch_expert_down(*cfg, h, r->expert_offsets, ew, y_perm, s, ws + L.rest_partial,
+                         L.rest_bytes);
   if (e != hipSuccess || mark(MOE_EV_DOWN) != hipSuccess) return MOE_ERR_HIP;
   e = launch_combine(*cfg, y_perm, r->expert_offsets, r->assign_row, r->topk_gate, y, s);
   if (e != hipSuccess || mark(MOE_EV_END) != hipSuccess) return MOE_ERR_HIP;
@@ -474,7 +480,8 @@ int moe_forward_hash(const moe_config* cfg, const void* x, const int32_t* token_
   void* h = ws + L.h;
   e = launch_expert_up(*cfg, x, r->expert_offsets, ew, h, s, r->row_token);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  e = launch_expert_down(*cfg, h, r->expert_offsets, ew, ws + L.y_perm, s);
+  e = launch_expert_down(*cfg, h, r->expert_offsets, ew, ws + L.y_perm, s, ws + L.rest_partial,
+                         L.rest_bytes);
   if (e != hipSuccess) return MOE_ERR_HIP;
   return hip_status(launch_combine(*cfg, ws + L.y_perm, r->expert_offsets, r->assign_row,
                                    r->topk_gate, y, s));
@@ -556,7 +563,8 @@ int moe_forward_train(const moe_config* cfg, const void* x, const moe_weights* w
   if (e != hipSuccess) return MOE_ERR_HIP;
   e = launch_act_rows(*cfg, saved->z, r->expert_offsets, saved->h, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  e = launch_expert_down(*cfg, saved->h, r->expert_offsets, ew, saved->y_perm, s);
+  e = launch_expert_down(*cfg, saved->h, r->expert_offsets, ew, saved->y_perm, s,
+                         ws + L.rest_partial, L.rest_bytes);
   if (e != hipSuccess) return MOE_ERR_HIP;
   e = launch_combine(*cfg, saved->y_perm, r->expert_offsets, r->assign_row, r->topk_gate, y, s);
   return hip_status(e);
@@ -613,7 +621,7 @@ int moe_backward(const moe_config* cfg, const void* x, const moe_weights* w, con
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   e = launch_backward_dx(*cfg, ws + B.dz, r->expert_offsets, w->w1, w->w3, w->ws1, w->ws3,
-                         ws + B.dxp, s);
+                         ws + B.dxp, s, ws + B.rest_partial, B.rest_bytes);
   if (e != hipSuccess) return MOE_ERR_HIP;
   return hip_status(launch_backward_misc(*cfg, B, x, *w, *r, stats, *saved, dy, aux_coef, z_coef,
                                          *g, ws, s, 1));

@@ -130,13 +130,26 @@ struct WsLayout {
   size_t chunk_base;      // int32 [chunks][E]
   size_t local_rank;      // int32 [T k]
   size_t h;               // act [rows_max][F]
+  size_t rest_partial;    // float planes of GEMM 2's split left-over rows (rest_bytes)
   size_t y_perm;          // act [rows_max][d]
-  size_t end_route, end_permute, end_ffn, total;
+  size_t end_route, end_permute, end_ffn, total, rest_bytes;
   int route_blocks, route_iters, chunks;
   int64_t rows_max;
 };
 
 WsLayout workspace_layout(const moe_config& c);
+
+// Split along K of the tiled path's left-over rows (groups of more than
+// 1536 rows leave up to 255 rows past their full 256-row tiles): kparts float32
+// planes of up to cap 128-row tiles, bytes in all (kparts 1: no split).
+struct RestSplit {
+  int kparts, cap;
+  size_t bytes;
+};
+RestSplit rest_split_plan(const moe_config& c, int N, int K, int skip);
+// Bytes of those planes for GEMM 2 of the forward (which 0) or the backward's
+// dX GEMM (which 1); 0 where that GEMM does not split.
+size_t rest_partial_bytes(const moe_config& c, int which);
 
 // Lanes of a wavefront that cooperate on one token in the top-k kernel.
 int route_lanes(int E);
@@ -191,9 +204,11 @@ hipError_t launch_expert_up(const moe_config& c, const void* a, const int32_t* e
                             const ExpertWeights& w, void* h, hipStream_t stream,
                             const int32_t* arows = nullptr);
 
-// Grouped GEMM 2: y_perm = h W2^T + b2 per group.
+// Grouped GEMM 2: y_perm = h W2^T + b2 per group (rest_partial: rest_bytes of
+// workspace for the split left-over rows, or null).
 hipError_t launch_expert_down(const moe_config& c, const void* h, const int32_t* expert_offsets,
-                              const ExpertWeights& w, void* y_perm, hipStream_t stream);
+                              const ExpertWeights& w, void* y_perm, hipStream_t stream,
+                              void* rest_partial = nullptr, size_t rest_bytes = 0);
 
 hipError_t launch_combine(const moe_config& c, const void* y_perm, const int32_t* expert_offsets,
                           const int32_t* assign_row, const float* topk_gate, void* y,
@@ -228,7 +243,7 @@ hipError_t launch_expert_choice_forward(const moe_config& c, const EcLayout& L, 
 // of 128, at least 128); xp holds the expert-sorted x rows.
 struct BwdLayout {
   size_t dyp, dgate, dlogits, dz, dh, dxp, po;   // po: padded then sanitized offsets
-  size_t xp, colsum1, colsum2, gate_partial, total;
+  size_t xp, colsum1, colsum2, gate_partial, rest_partial, rest_bytes, total;
   int64_t ldk;
   int gate_slices, gate_slice_len;
 };
@@ -284,7 +299,8 @@ hipError_t launch_dswiglu(const moe_config& c, const void* dh, const void* z, vo
                           const int32_t* expert_offsets, hipStream_t stream);
 hipError_t launch_backward_dx(const moe_config& c, const void* dz, const int32_t* expert_offsets,
                               const void* w1, const void* w3, const void* ws1, const void* ws3,
-                              void* dxp, hipStream_t stream);
+                              void* dxp, hipStream_t stream, void* rest_partial = nullptr,
+                              size_t rest_bytes = 0);
 // Grouped weight gradient over the rows of each group,
 // C_g = A[so[g]:so[g+1], 0:M]^T B[so[g]:so[g+1], 0:N]: A [rows][lda], B [rows][ldb]
 // bf16 row-major; C float32 [E][M][N], Cs [M][N] for group E.
