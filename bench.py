@@ -385,6 +385,11 @@ def main():
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, sets[0])
+    if not args.no_train and A.lib().moe_backward_workspace_size(
+            ctypes.byref(cfg), ctypes.byref(ctypes.c_size_t(0))) == A.MOE_OK:
+        # a training step of the headline layer itself
+        result["train_" + w.name] = train_step(A, torch, w, cfg, sets, ws, max(5, args.steps // 4),
+                                               2, head["kept_rows"])
     sets = ws = None
     release(torch)
     if head["weights"] == "packed" and not args.no_standard_layout:

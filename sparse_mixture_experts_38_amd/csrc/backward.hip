@@ -732,12 +732,12 @@ hipError_t launch_backward_misc(const moe_config& c, const BwdLayout& B, const v
                        (const bf16*)x, r.row_token, (const int32_t*)so, G, T, d, xp);
   }
   // dW2 = dYp^T H, dW1 = dz1^T Xp (dW3 = du^T Xp)
-  hipError_t e = launch_wgrad(dyp, d, sv.h, F, so, G, E, d, F, gr.dw2, gr.dws2, s);
+  hipError_t e = launch_wgrad(dyp, d, sv.h, F, so, G, E, d, F, rmax, gr.dw2, gr.dws2, s);
   if (e != hipSuccess) return e;
-  e = launch_wgrad(dz, NZ * F, xp, d, so, G, E, F, d, gr.dw1, gr.dws1, s);
+  e = launch_wgrad(dz, NZ * F, xp, d, so, G, E, F, d, rmax, gr.dw1, gr.dws1, s);
   if (e != hipSuccess) return e;
   if (sw) {
-    e = launch_wgrad(dz + F, 2 * F, xp, d, so, G, E, F, d, gr.dw3, gr.dws3, s);
+    e = launch_wgrad(dz + F, 2 * F, xp, d, so, G, E, F, d, rmax, gr.dw3, gr.dws3, s);
     if (e != hipSuccess) return e;
   }
   if (c.has_bias) {

@@ -851,9 +851,14 @@ __global__ __launch_bounds__(256, 2) void gemm_wgrad_tn_kernel(
 #undef WT_R
 #undef WT_M
 #undef WT_STEP
-  // lane (fr, fk) of accumulator (i, j) holds row m0 + wm 64 + 32 i + fr and
-  // columns n0 + wn 64 + 32 j + 8 qd + 4 fk .. + 3 of C_g
+  // lane (fr, fk) of accumulator (i, j) holds row wm 64 + 32 i + fr and
+  // columns wn 64 + 32 j + 8 qd + 4 fk .. + 3 of the tile. The float32 tile
+  // (64 KB, both stages) leaves through LDS, 16-byte chunk q of row m at
+  // q ^ (m & 31), so that each store instruction writes whole 512-byte row
+  // segments of C_g.
   float* __restrict__ Cg = g < E ? C + (int64_t)g * M * N : Cs;
+  f32x4* st4 = reinterpret_cast<f32x4*>(smem);
+  __syncthreads();   // every wave is done reading the operand stages
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int m = wm * 64 + i * 32 + fr;
@@ -863,9 +868,17 @@ __global__ __launch_bounds__(256, 2) void gemm_wgrad_tn_kernel(
       for (int qd = 0; qd < 4; ++qd) {
         const f32x4 v = {acc[i + 2 * j][qd * 4 + 0], acc[i + 2 * j][qd * 4 + 1],
                          acc[i + 2 * j][qd * 4 + 2], acc[i + 2 * j][qd * 4 + 3]};
-        *reinterpret_cast<f32x4*>(Cg + (int64_t)(m0 + m) * N + n0 + wn * 64 + j * 32 + qd * 8 +
-                                  fk * 4) = v;
+        const int q = wn * 16 + j * 8 + qd * 2 + fk;
+        st4[m * 32 + (q ^ (m & 31))] = v;
       }
+  }
+  __syncthreads();
+  const int q = tid & 31;
+  float* crow = Cg + (int64_t)m0 * N + n0 + q * 4;
+#pragma unroll 4
+  for (int p = 0; p < 16; ++p) {
+    const int m = p * 8 + (tid >> 5);
+    *reinterpret_cast<f32x4*>(crow + (int64_t)m * N) = st4[m * 32 + (q ^ (m & 31))];
   }
 }
 
@@ -1037,21 +1050,47 @@ __global__ __launch_bounds__(256, 1) void gemm_wgrad_tn_big_kernel(
 #undef WB_SUB
 #undef WB_PHASE
 
-  // lane (fr, fk) of accumulator (i, j) holds row m0 + wm 128 + 32 i + fr and
-  // columns n0 + wn 128 + 32 j + 8 qd + 4 fk .. + 3 of C_g
+  // lane (fr, fk) of accumulator (i, j) holds row wm 128 + 32 i + fr and
+  // columns wn 128 + 32 j + 8 qd + 4 fk .. + 3 of the tile. The float32 tile
+  // (256 KB) leaves through LDS in two halves of 128 rows (the waves with
+  // wm = 0, then wm = 1, stage theirs: rows 0..63 of the half in sm0, 64..127
+  // in sm1, 16-byte chunk q of row m at q ^ (m & 31)), so that each store
+  // instruction writes whole 1 KB row segments of C_g.
   float* __restrict__ Cg = g < E ? C + (int64_t)g * M * N : Cs;
+  f32x4* st_lo = reinterpret_cast<f32x4*>(sm0);
+  f32x4* st_hi = reinterpret_cast<f32x4*>(sm1);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = wm * 128 + i * 32 + fr;
+  for (int half = 0; half < 2; ++half) {
+    if (wm == half) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+      for (int i = 0; i < 4; ++i) {
+        const int m = i * 32 + fr;   // row of the half
+        f32x4* st = i < 2 ? st_lo : st_hi;
 #pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {
-        const f32x16& a = acc[i + 4 * j];
-        const f32x4 v = {a[qd * 4 + 0], a[qd * 4 + 1], a[qd * 4 + 2], a[qd * 4 + 3]};
-        *reinterpret_cast<f32x4*>(Cg + (int64_t)(m0 + m) * N + n0 + wn * 128 + j * 32 + qd * 8 +
-                                  fk * 4) = v;
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd) {
+            const f32x16& a = acc[i + 4 * j];
+            const f32x4 v = {a[qd * 4 + 0], a[qd * 4 + 1], a[qd * 4 + 2], a[qd * 4 + 3]};
+            const int q = wn * 32 + j * 8 + qd * 2 + fk;
+            st[(m & 63) * 64 + (q ^ (m & 31))] = v;
+          }
       }
+    }
+    __syncthreads();
+    const int q = tid & 63;
+    float* crow = Cg + (int64_t)(m0 + half * 128) * N + n0 + q * 4;
+#pragma unroll 4
+    for (int p = 0; p < 16; ++p) {
+      const int m = p * 4 + (tid >> 6);
+      *reinterpret_cast<f32x4*>(crow + (int64_t)m * N) = st_lo[m * 64 + (q ^ (m & 31))];
+    }
+#pragma unroll 4
+    for (int p = 0; p < 16; ++p) {
+      const int m = p * 4 + (tid >> 6);
+      *reinterpret_cast<f32x4*>(crow + (int64_t)(64 + m) * N) = st_hi[m * 64 + ((q ^ (m & 31)))];
+    }
+    __syncthreads();
   }
 }
 
@@ -2656,12 +2695,15 @@ hipError_t launch_pack_weights(const moe_config& c, const moe_weights& w, void* 
 }
 
 hipError_t launch_wgrad(const void* a, int lda, const void* b, int ldb, const int32_t* so, int G,
-                        int E, int M, int N, float* C, float* Cs, hipStream_t s) {
+                        int E, int M, int N, int64_t rows, float* C, float* Cs, hipStream_t s) {
   const int64_t tiles = (int64_t)G * (M / 128) * (N / 128);
   if (tiles <= 0) return hipSuccess;
-  // 256 x 256 tiles where they number at least one per CU
+  // 256 x 256 tiles where they number at least one per CU and the groups
+  // average at least 512 rows (8 K steps); with fewer rows per group (the
+  // DeepSeek-V3 shape: ~140) a tile is mostly its float32 output, which two
+  // 128 x 128 blocks per CU overlap with each other's loads
   const int64_t big = M % 256 == 0 && N % 256 == 0 ? (int64_t)G * (M / 256) * (N / 256) : 0;
-  if (big >= 256)
+  if (big >= 256 && rows >= (int64_t)512 * G)
     hipLaunchKernelGGL(gemm_wgrad_tn_big_kernel, dim3((unsigned)big), dim3(256), 0, s,
                        (const bf16*)a, lda, (const bf16*)b, ldb, so, G, E, M, N, C, Cs);
   else

@@ -303,8 +303,9 @@ hipError_t launch_backward_dx(const moe_config& c, const void* dz, const int32_t
                               size_t rest_bytes = 0);
 // Grouped weight gradient over the rows of each group,
 // C_g = A[so[g]:so[g+1], 0:M]^T B[so[g]:so[g+1], 0:N]: A [rows][lda], B [rows][ldb]
-// bf16 row-major; C float32 [E][M][N], Cs [M][N] for group E.
+// bf16 row-major (rows: the rows of all groups, for the choice of tile);
+// C float32 [E][M][N], Cs [M][N] for group E.
 hipError_t launch_wgrad(const void* a, int lda, const void* b, int ldb, const int32_t* so, int G,
-                        int E, int M, int N, float* C, float* Cs, hipStream_t stream);
+                        int E, int M, int N, int64_t rows, float* C, float* Cs, hipStream_t stream);
 
 }  // namespace moe

@@ -381,3 +381,110 @@ def test_backward_full_size_mixtral_sampled_tokens():
                 continue
             assert rel_err(got, ref) <= tol, f"{name}[{e}]"
     print(f"[case] mixtral training: {len(sample)} tokens, {len(rows)} rows checked", flush=True)
+
+
+def test_backward_full_size_deepseek_v3_sampled_tokens():
+    """DeepSeek-V3 layer at its full size (T = 4096, d = 7168, 256 routed SwiGLU
+    experts of F = 2048 plus one shared, sigmoid + selection bias, top-8), trained
+    on a dy that is zero except on 32 sampled tokens, with aux_coef = z_coef = 0:
+    then only those tokens' routed rows and shared rows carry gradient, and the
+    oracle computes every compared entry from those rows alone (x, the weights,
+    the GPU's routing): dx in full (zero off the sample), dW_g in full, the shared
+    expert's dW1, dW3, dW2 in full, and the routed experts' for four experts with
+    sampled rows and two without (all zero), plus the saved planes on the sampled
+    rows. The gradients stay on the GPU; only the compared tensors are copied."""
+    w = W["deepseek_v3"]
+    print("[case] backward full-size deepseek_v3 (sampled tokens)", flush=True)
+    inp = make_inputs(w, seed=0, device="cuda")
+    T, d, F, E, k = w.tokens, w.d_model, w.d_ff, w.num_experts, w.top_k
+    rng = np.random.default_rng(1)
+    sample = np.sort(rng.choice(T, 32, replace=False))
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(78)
+    dy = torch.zeros(T, d, dtype=torch.bfloat16)
+    dy[torch.from_numpy(sample)] = torch.randn(len(sample), d, generator=gen).to(torch.bfloat16)
+    cfg = A.make_config(w)
+    R = A.alloc_routing(cfg)
+    stats = A.alloc_stats()
+    ws = A.alloc_workspace(cfg)
+    saved = A.alloc_saved(cfg)
+    y = torch.empty(T, d, dtype=torch.bfloat16, device="cuda")
+    A.forward_train(cfg, inp["x"], A.weights_of(inp), y, R, stats, saved, ws)
+    del ws
+    grads = A.alloc_grads(cfg)
+    bws = A.alloc_backward_workspace(cfg)
+    A.backward(cfg, inp["x"], A.weights_of(inp), R, stats, saved, dy.cuda(), 0.0, 0.0, grads, bws)
+    torch.cuda.synchronize()
+    del bws
+    out = {n: v.cpu() for n, v in R.items() if v is not None}
+    out["stats"] = A.read_stats(stats, E)
+    dsp = check_dispatch(w, out)
+    idx = out["topk_idx"].numpy()
+    logits = out["logits"].numpy()
+    gates = O.renormalised_gates(O.route(logits, k, w.score_fn)["scores"], idx)
+    off = out["expert_offsets"].numpy().astype(np.int64)
+    x = np64(inp["x"][torch.from_numpy(sample).cuda()])   # the sampled tokens' rows
+    dys = np64(dy[torch.from_numpy(sample)])
+    P = oracle_params(inp)
+    tol = TOL["bf16"]
+
+    def ffn(W1, W3, W2, xs, dY):
+        z1, u = xs @ W1.T, xs @ W3.T
+        h = O.silu(z1) * u
+        dH = dY @ W2
+        dz1, du = dH * u * O.silu_grad(z1), dH * O.silu(z1)
+        return z1, u, h @ W2.T, dz1 @ W1 + du @ W3, dz1.T @ xs, du.T @ xs, dY.T @ h
+
+    dgate = np.zeros((len(sample), k))
+    dxp = np.zeros((len(sample), d))
+    ref_w = {}
+    check_experts = []
+    rows_z1, rows_ref = [], []
+    zplanes = saved["z"]
+    by_expert = {}
+    for si in range(len(sample)):
+        for j in range(k):
+            by_expert.setdefault(int(idx[sample[si], j]), []).append((si, j))
+    with_rows = sorted(by_expert)
+    check_experts = with_rows[:: max(1, len(with_rows) // 4)][:4]
+    without = [e for e in range(E) if e not in by_expert][:2]
+    for e, sel in by_expert.items():
+        sis = np.array([si for si, _ in sel])
+        g = np.array([gates[sample[si], j] for si, j in sel])
+        z1, u, ye, dxe, dw1, dw3, dw2 = ffn(P["w1"][e], P["w3"][e], P["w2"][e], x[sis],
+                                            g[:, None] * dys[sis])
+        for q, (si, j) in enumerate(sel):
+            dgate[si, j] = dys[si] @ ye[q]
+            dxp[si] += dxe[q]
+        if e in check_experts:
+            ref_w[e] = (dw1, dw3, dw2)
+            rows = [int(dsp["assign_row"][sample[si], j]) for si, j in sel]
+            rows_z1.append((rows, z1, u))
+    # shared expert: every sampled token's shared row (gate 1)
+    s1, s3, s2 = (np64(inp[n].reshape(inp[n].shape[-2:])) for n in ("ws1", "ws3", "ws2"))
+    z1s, us, _, dxs, dws1, dws3, dws2 = ffn(s1, s3, s2, x, dys)
+    dxp += dxs
+    srows = off[E] + sample
+    del s1, s3, s2
+    for rows, z1, u in rows_z1 + [(list(srows), z1s, us)]:
+        ridx = torch.tensor(rows, dtype=torch.long, device="cuda")
+        assert rel_err(zplanes[0][ridx].float().cpu().numpy(), z1) <= tol, "saved z1"
+        assert rel_err(zplanes[1][ridx].float().cpu().numpy(), u) <= tol, "saved u"
+    f = dsp["counts_pre"] / float(T * k)
+    dlog = O.router_backward(logits[sample].astype(np.float64), idx[sample], w.score_fn, dgate,
+                             f, 0.0, 0.0)
+    assert rel_err(grads["dw_gate"].cpu().numpy(), dlog.T @ x) <= tol, "dw_gate"
+    dx = grads["dx"].float().cpu().numpy()
+    assert rel_err(dx[sample], dxp + dlog @ P["w_gate"]) <= tol, "dx"
+    others = np.setdiff1d(np.arange(T), sample)
+    assert float(np.abs(dx[others]).max()) == 0.0, "dx off the sample"
+    for name, ref in (("dws1", dws1), ("dws3", dws3), ("dws2", dws2)):
+        assert rel_err(grads[name].cpu().numpy(), ref) <= tol, name
+    for e in check_experts:
+        for name, ref in zip(("dw1", "dw3", "dw2"), ref_w[e]):
+            assert rel_err(grads[name][e].cpu().numpy(), ref) <= tol, f"{name}[{e}]"
+    for e in without:
+        for name in ("dw1", "dw3", "dw2"):
+            assert float(grads[name][e].abs().max()) == 0.0, f"{name}[{e}] without rows"
+    print(f"[case] deepseek_v3 training: {len(sample)} tokens, {len(by_expert)} routed experts, "
+          f"checked {check_experts} and {without}", flush=True)
