@@ -258,7 +258,10 @@ def train_step(A, torch, w, cfg, sets, ws, steps, warmup, rows):
     """One training step of the layer: moe_forward_train then moe_backward (with
     L_aux and z-loss weights 0.01 and 0.001), on the same rotated input sets.
     The backward's algorithmic FLOPs are its expert GEMMs, 4 x 2 R d F (dH and
-    dX, dW2 and dW1; 6 x 2 R d F for SwiGLU: dX at K = 2F and dW3), R = kept rows."""
+    dX, dW2 and dW1; 6 x 2 R d F for SwiGLU: dX at K = 2F and dW3), R = kept rows.
+    The weights are read in their standard layout only: an optimizer step
+    changes them every step, so a packed copy would have to be rebuilt each
+    time (the forward figures use it as a stored layout of fixed weights)."""
     T, d, F = w.tokens, w.d_model, w.d_ff
     act = A.TORCH_DTYPE[cfg.act_dtype]
     grads = A.alloc_grads(cfg)
@@ -269,7 +272,9 @@ def train_step(A, torch, w, cfg, sets, ws, steps, warmup, rows):
         gen.manual_seed(1000 + i)
         dy = torch.randn(T, d, generator=gen, device="cuda").to(act)
         R = A.alloc_routing(cfg)
-        tplans.append(A.TrainPlan(cfg, s["x"], A.weights_of(s), torch.empty(T, d, dtype=act, device="cuda"),
+        wstd = {k: (None if k in ("up_packed", "down_packed") else v)
+                for k, v in A.weights_of(s).items()}
+        tplans.append(A.TrainPlan(cfg, s["x"], wstd, torch.empty(T, d, dtype=act, device="cuda"),
                                   R, A.alloc_stats(), A.alloc_saved(cfg), ws, dy, grads, bws))
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     for i in range(warmup):
@@ -291,7 +296,7 @@ def train_step(A, torch, w, cfg, sets, ws, steps, warmup, rows):
     # dH and dX (K = 2F for SwiGLU), dW2 and dW1 (+ dW3 for SwiGLU)
     bwd_flop = (6 if w.activation == "swiglu" else 4) * 2.0 * rows * d * F
     tf = bwd_flop / (bwd_ms * 1e-3) / 1e12
-    return {"workload": w.name, "step_ms": step_ms, "forward_train_ms": fwd_ms,
+    return {"workload": w.name, "weights": "standard", "step_ms": step_ms, "forward_train_ms": fwd_ms,
             "backward_ms": bwd_ms, "tokens_per_s": T / (step_ms * 1e-3),
             "backward_gemm_flop": bwd_flop, "backward_tflops": tf,
             "backward_frac_of_peak": tf / PEAK_BF16_TFLOPS, "aux_coef": 0.01, "z_coef": 0.001}

@@ -528,6 +528,27 @@ __global__ __launch_bounds__(256) void gate_bias_grad_kernel(const float* __rest
   if (threadIdx.x == 0) db[e] = red[0];
 }
 
+// dlogits [T][E] float32 as two bf16 planes, dlp[t][e] = hi = bf16(v) and
+// dlp[t][E + e] = lo = bf16(v - hi) (v - hi is exact; hi + lo = v to within
+// 2^-17 |v|), so that a bf16 GEMM with float32 accumulation multiplies v by a
+// bf16 operand with the products exact; block 0 also writes the bounds of
+// `slices` equal token slices, gso[i] = i T / slices.
+__global__ __launch_bounds__(256) void dlogit_planes_kernel(const float* __restrict__ dl, int64_t T,
+                                                            int E, int slices,
+                                                            bf16* __restrict__ dlp,
+                                                            int32_t* __restrict__ gso) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (blockIdx.x == 0 && (int)threadIdx.x <= slices)
+    gso[threadIdx.x] = (int32_t)(T * (int64_t)threadIdx.x / slices);
+  if (i >= T * E) return;
+  const int64_t t = i / E;
+  const int e = (int)(i - t * E);
+  const float v = dl[i];
+  const bf16 hi = (bf16)v;
+  dlp[t * 2 * E + e] = hi;
+  dlp[t * 2 * E + E + e] = (bf16)(v - (float)hi);
+}
+
 // ------------------------------------------------------------------ dx
 // dx[t] = sum_j dXp[assign_row[t, j]] (kept choices, j order) + dXp[off[E] + t]
 // (shared expert) + sum_e dlogits[t][e] W_g[e] (router), float32 sums, one
@@ -537,11 +558,13 @@ __global__ __launch_bounds__(256) void gate_bias_grad_kernel(const float* __rest
 // of its own): W_g rows in batches of 8 (rows past E reread row E - 1), and
 // row slots that are dropped or past k reread the token's first live row; all
 // of them are masked out of the sums, which keep the order above.
+// With xr, the router term is read from xr [T][d] (computed on MFMA) instead.
 template <typename ET, typename WT, int KM>
 __global__ __launch_bounds__(256) void unpermute_dx_kernel(
     const ET* __restrict__ dxp, const int32_t* __restrict__ assign_row,
     const int32_t* __restrict__ off, const float* __restrict__ dlogits, const WT* __restrict__ wg,
-    int64_t T, int d, int k, int E, int S, int64_t rows_max, ET* __restrict__ dx) {
+    int64_t T, int d, int k, int E, int S, int64_t rows_max, ET* __restrict__ dx,
+    const float* __restrict__ xr) {
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (t >= T) return;
@@ -573,7 +596,8 @@ __global__ __launch_bounds__(256) void unpermute_dx_kernel(
       load8(dxp + (shared ? rs : first) * d + c, as);
     }
     float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int e0 = 0; e0 < E; e0 += 8) {
+    if (xr) load8(xr + t * d + c, v);
+    for (int e0 = 0; e0 < (xr ? 0 : E); e0 += 8) {
       float wv[8][8], g[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -601,16 +625,17 @@ __global__ __launch_bounds__(256) void unpermute_dx_kernel(
 template <typename ET, typename WT>
 static void launch_unpermute_dx(dim3 grid, hipStream_t s, const ET* dxp, const int32_t* assign_row,
                                 const int32_t* off, const float* dlogits, const WT* wg, int64_t T,
-                                int d, int k, int E, int S, int64_t rows_max, ET* dx) {
+                                int d, int k, int E, int S, int64_t rows_max, ET* dx,
+                                const float* xr) {
   if (k <= 2)
     hipLaunchKernelGGL((unpermute_dx_kernel<ET, WT, 2>), grid, dim3(256), 0, s, dxp, assign_row,
-                       off, dlogits, wg, T, d, k, E, S, rows_max, dx);
+                       off, dlogits, wg, T, d, k, E, S, rows_max, dx, xr);
   else if (k <= 4)
     hipLaunchKernelGGL((unpermute_dx_kernel<ET, WT, 4>), grid, dim3(256), 0, s, dxp, assign_row,
-                       off, dlogits, wg, T, d, k, E, S, rows_max, dx);
+                       off, dlogits, wg, T, d, k, E, S, rows_max, dx, xr);
   else
     hipLaunchKernelGGL((unpermute_dx_kernel<ET, WT, MOE_MAX_TOP_K>), grid, dim3(256), 0, s, dxp,
-                       assign_row, off, dlogits, wg, T, d, k, E, S, rows_max, dx);
+                       assign_row, off, dlogits, wg, T, d, k, E, S, rows_max, dx, xr);
 }
 
 template <typename ET>
@@ -646,28 +671,28 @@ hipError_t launch_router_backward(const moe_config& c, const moe_routing& r, con
 
 template <typename ET>
 static void dx_t(const moe_config& c, const float* dlogits, const void* dxp, const moe_routing& r,
-                 const moe_weights& w, const moe_grads& gr, hipStream_t s) {
+                 const moe_weights& w, const moe_grads& gr, hipStream_t s, const float* xr) {
   const int64_t T = c.tokens;
   const dim3 ug((unsigned)((T + 3) / 4));
   const int d = (int)c.d_model, k = c.top_k, E = c.num_experts, S = c.num_shared_experts;
   if (c.router_dtype == MOE_BF16)
     launch_unpermute_dx<ET, bf16>(ug, s, (const ET*)dxp, r.assign_row, r.expert_offsets, dlogits,
-                                  (const bf16*)w.w_gate, T, d, k, E, S, rows_max(c), (ET*)gr.dx);
+                                  (const bf16*)w.w_gate, T, d, k, E, S, rows_max(c), (ET*)gr.dx, xr);
   else
     launch_unpermute_dx<ET, float>(ug, s, (const ET*)dxp, r.assign_row, r.expert_offsets, dlogits,
-                                   (const float*)w.w_gate, T, d, k, E, S, rows_max(c), (ET*)gr.dx);
+                                   (const float*)w.w_gate, T, d, k, E, S, rows_max(c), (ET*)gr.dx, xr);
 }
 
 hipError_t launch_router_bias_and_dx(const moe_config& c, const float* dlogits, const void* dxp,
                                      const moe_routing& r, const moe_weights& w,
-                                     const moe_grads& gr, hipStream_t s) {
+                                     const moe_grads& gr, hipStream_t s, const float* xr) {
   if (c.has_gate_bias)
     hipLaunchKernelGGL(gate_bias_grad_kernel, dim3(c.num_experts), dim3(256), 0, s, dlogits,
                        (int64_t)c.tokens, c.num_experts, gr.db_gate);
   if (c.act_dtype == MOE_BF16)
-    dx_t<bf16>(c, dlogits, dxp, r, w, gr, s);
+    dx_t<bf16>(c, dlogits, dxp, r, w, gr, s, xr);
   else
-    dx_t<float>(c, dlogits, dxp, r, w, gr, s);
+    dx_t<float>(c, dlogits, dxp, r, w, gr, s, xr);
   return hipGetLastError();
 }
 
@@ -759,10 +784,29 @@ hipError_t launch_backward_misc(const moe_config& c, const BwdLayout& B, const v
                          (int)(B.ldk / 64), gr.db1, gr.dbs1);
     }
   }
+  const int64_t n = (int64_t)E * d;
+  if (B.gate_mfma) {
+    // dlogits as two bf16 planes; dW_g = sum over token slices of the planes'
+    // products with x (weight-gradient kernel, one group per slice, planes
+    // [slice][hi, lo][E][d] added in that order); x's router term on MFMA
+    bf16* dlp = (bf16*)(ws + B.dlp);
+    int32_t* gso = (int32_t*)(ws + B.gso);
+    const int64_t ne = T * E;
+    hipLaunchKernelGGL(dlogit_planes_kernel, dim3((unsigned)((ne + 255) / 256)), dim3(256), 0, s,
+                       (const float*)dlogits, T, E, B.gate_slices, dlp, gso);
+    e = launch_wgrad(dlp, 2 * E, x, d, gso, B.gate_slices, B.gate_slices, 2 * E, d, T,
+                     (float*)(ws + B.gate_partial), nullptr, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(gate_wgrad_reduce_kernel, dim3((unsigned)((n + 63) / 64)), dim3(256), 0, s,
+                       (const float*)(ws + B.gate_partial), 2 * B.gate_slices, n, gr.dw_gate);
+    e = launch_router_dx_gemm(c, dlp, w.w_gate, (float*)(ws + B.xr), s);
+    if (e != hipSuccess) return e;
+    return launch_router_bias_and_dx(c, dlogits, ws + B.dxp, r, w, gr, s,
+                                     (const float*)(ws + B.xr));
+  }
   hipLaunchKernelGGL(gate_wgrad_kernel, dim3((E + 7) / 8, (d + 511) / 512, B.gate_slices), dim3(256), 0, s,
                      (const bf16*)x, (const float*)dlogits, T, d, E, (int)B.gate_slice_len,
                      (float*)(ws + B.gate_partial));
-  const int64_t n = (int64_t)E * d;
   hipLaunchKernelGGL(gate_wgrad_reduce_kernel, dim3((unsigned)((n + 63) / 64)), dim3(256), 0, s,
                      (const float*)(ws + B.gate_partial), (int)B.gate_slices, n, gr.dw_gate);
   e = hipGetLastError();

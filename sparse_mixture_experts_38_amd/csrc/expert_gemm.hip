@@ -703,7 +703,9 @@ __global__ __launch_bounds__(256, 2) void gemm_wgrad_tn_kernel(
   constexpr int STAGE = 2 * HALF;                        // 32 KB
   constexpr int GROUP_M = 8;
   __shared__ u32x4 smem[2 * STAGE];
-  const int mtn = M / BM, ntn = N / BN, per = mtn * ntn;
+  const int mtn = M / BM, ntn = N / BN;
+  const int ntb = wgrad_run(ntn);            // consecutive n tiles per block
+  const int nrun = ntn / ntb, per = mtn * nrun;
   const int tiles = G * per;
   const int b = blockIdx.x;
   if (b >= tiles) return;
@@ -711,12 +713,12 @@ __global__ __launch_bounds__(256, 2) void gemm_wgrad_tn_kernel(
   const int t = b < t8 ? (b & 7) * (t8 >> 3) + (b >> 3) : b;
   const int g = t / per;
   const int in = t - g * per;
-  const int grp = in / (GROUP_M * ntn);
+  const int grp = in / (GROUP_M * nrun);
   const int first_m = grp * GROUP_M;
   const int gm = min(mtn - first_m, GROUP_M);
-  const int in2 = in - grp * GROUP_M * ntn;
+  const int in2 = in - grp * GROUP_M * nrun;
   const int m0 = (first_m + in2 % gm) * BM;
-  const int n0 = (in2 / gm) * BN;
+  int n0 = (in2 / gm) * ntb * BN;
   // uniform over the block: scalar registers (the buffer descriptors below
   // must be scalar)
   const int r0 = __builtin_amdgcn_readfirstlane(so[g]);
@@ -724,6 +726,19 @@ __global__ __launch_bounds__(256, 2) void gemm_wgrad_tn_kernel(
   int len = (nr + BK - 1) / BK;   // K steps, made even and at least 2
   len = len < 2 ? 2 : (len + 1) & ~1;
   const int tid = threadIdx.x;
+  if (nr <= 0) {
+    // a group without rows (an expert that received no token): its gradient
+    // is zero; the tile is stored straight away, in the row segments of the
+    // epilogue below, with no operand loads
+    float* __restrict__ Cz = (g < E ? C + (int64_t)g * M * N : Cs) + (int64_t)m0 * N + n0 +
+                             (tid & 31) * 4;
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    for (int it = 0; it < ntb; ++it)
+#pragma unroll
+      for (int p = 0; p < 16; ++p)
+        __builtin_nontemporal_store(zero, reinterpret_cast<f32x4*>(Cz + it * BN + (int64_t)(p * 8 + (tid >> 5)) * N));
+    return;
+  }
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -735,7 +750,7 @@ __global__ __launch_bounds__(256, 2) void gemm_wgrad_tn_kernel(
   const int lc = tid & 15;
   const int wslot = lr * TC + (lc ^ ((lr & 3) << 2));
   const uint32_t ao = (uint32_t)(lr * lda + m0 + lc * 8) * 2u;   // within a step's rows
-  const uint32_t bo = (uint32_t)(lr * ldb + n0 + lc * 8) * 2u;
+  uint32_t bo = (uint32_t)(lr * ldb + n0 + lc * 8) * 2u;          // (+ 256 per n tile)
   const uint32_t astep = (uint32_t)(32 * lda), bstep = (uint32_t)(32 * ldb);   // 16 rows
   // fragment byte offsets in a stage (sub-tile j of the wave's A / B columns;
   // + 4096 per 16-row sub-step)
@@ -755,10 +770,6 @@ __global__ __launch_bounds__(256, 2) void gemm_wgrad_tn_kernel(
   Regs r0v, r1v;
   bf16x8 fr0[4], fr1[4];   // [0], [1]: A sub-tiles; [2], [3]: B sub-tiles
   f32x16 acc[4];           // acc[i + 2 j] = B sub-tile j times A sub-tile i
-#pragma unroll
-  for (int k4 = 0; k4 < 4; ++k4)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[k4][r] = 0.f;
 
 #define WT_SB() __builtin_amdgcn_sched_barrier(0)
   // register set R <- K step kt: loads i = 0..3 from A, 4..7 from B, through
@@ -829,10 +840,21 @@ __global__ __launch_bounds__(256, 2) void gemm_wgrad_tn_kernel(
     }                                                                                \
   } while (0)
 
+  float* __restrict__ Cg = g < E ? C + (int64_t)g * M * N : Cs;
+  f32x4* st4 = reinterpret_cast<f32x4*>(smem);
+  const int qo = tid & 31;   // 16-byte chunk of a row segment that this thread stores
 #pragma unroll
   for (int i = 0; i < 8; ++i) WT_G(r0v, 0, i);
 #pragma unroll
   for (int i = 0; i < 8; ++i) WT_G(r1v, 1, i);
+  // n tiles n0, n0 + 128, ... of the run; the first two K steps of the next
+  // tile are loaded before this tile's stores, so they arrive while the
+  // stores drain
+  for (int it = 0; it < ntb; ++it) {
+#pragma unroll
+  for (int k4 = 0; k4 < 4; ++k4)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[k4][r] = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) WT_W(r0v, 0, i);
   __syncthreads();
@@ -845,19 +867,11 @@ __global__ __launch_bounds__(256, 2) void gemm_wgrad_tn_kernel(
   WT_STEP(0, r0v, 0, false, r1v, true);
   __syncthreads();
   WT_STEP(1, r1v, 0, false, r0v, false);
-#undef WT_SB
-#undef WT_G
-#undef WT_W
-#undef WT_R
-#undef WT_M
-#undef WT_STEP
   // lane (fr, fk) of accumulator (i, j) holds row wm 64 + 32 i + fr and
   // columns wn 64 + 32 j + 8 qd + 4 fk .. + 3 of the tile. The float32 tile
   // (64 KB, both stages) leaves through LDS, 16-byte chunk q of row m at
   // q ^ (m & 31), so that each store instruction writes whole 512-byte row
   // segments of C_g.
-  float* __restrict__ Cg = g < E ? C + (int64_t)g * M * N : Cs;
-  f32x4* st4 = reinterpret_cast<f32x4*>(smem);
   __syncthreads();   // every wave is done reading the operand stages
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -873,13 +887,28 @@ __global__ __launch_bounds__(256, 2) void gemm_wgrad_tn_kernel(
       }
   }
   __syncthreads();
-  const int q = tid & 31;
-  float* crow = Cg + (int64_t)m0 * N + n0 + q * 4;
+  if (it + 1 < ntb) {
+    bo += BN * 2;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) WT_G(r0v, 0, i);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) WT_G(r1v, 1, i);
+  }
+  float* crow = Cg + (int64_t)m0 * N + n0 + qo * 4;
 #pragma unroll 4
   for (int p = 0; p < 16; ++p) {
     const int m = p * 8 + (tid >> 5);
-    *reinterpret_cast<f32x4*>(crow + (int64_t)m * N) = st4[m * 32 + (q ^ (m & 31))];
+    __builtin_nontemporal_store(st4[m * 32 + (qo ^ (m & 31))], reinterpret_cast<f32x4*>(crow + (int64_t)m * N));
   }
+  n0 += BN;
+  __syncthreads();   // the staged tile has been read before stage 0 is refilled
+  }
+#undef WT_SB
+#undef WT_G
+#undef WT_W
+#undef WT_R
+#undef WT_M
+#undef WT_STEP
 }
 
 // The weight gradient of gemm_wgrad_tn_kernel on 256 x 256 tiles: one block
@@ -1631,13 +1660,25 @@ __device__ __forceinline__ void stream_epilogue_lds(const f32x16 (&acc)[MF][2], 
   }
 }
 
-template <int EPI, bool HAS_BIAS, int MF>
+// KMB (backward dH and dX, EPI_NONE): the weights are read as stored,
+// K-major, C[r, n] = sum_k A[r, k] W_g[k, n], W_g [ksplit][N] for the K steps
+// below ksplit and W3g [K - ksplit][N] for the rest (SwiGLU's dX over
+// [W1; W3]). Wave w's part of a K step is then 64 K rows x 128 bytes (its 64
+// columns): eight whole-line loads of 8 rows each, stored as they arrived
+// into the wave's LDS area (16-byte chunk c of row k at c ^ 4 ((k >> 1) & 1)),
+// and every weight fragment is two ds_read_b64_tr_b16 (lds_tr_frag) that
+// hand lane (fr, fh) column 32 j + fr at the K rows 32 fh + 8 s .. + 7 of
+// sub-step s, the rows its token fragment covers. The four rows a 16-lane
+// group reads and the two chunk pairs of a 32-lane half fall on 64 distinct
+// banks.
+template <int EPI, bool HAS_BIAS, int MF, bool KMB = false>
 __device__ __forceinline__ int stream_tile(u32x4* __restrict__ smem, const bf16* __restrict__ A,
                                            uint32_t a_bytes, const int32_t* __restrict__ arows,
                                            const bf16* __restrict__ Wg, const bf16* __restrict__ W3g,
                                            const float* __restrict__ bg, int row0, int mrows,
                                            int n0, bf16* __restrict__ C, int N, int K,
-                                           int* __restrict__ done) {
+                                           int* __restrict__ done, int ksplit = 0) {
+  static_assert(!KMB || EPI == EPI_NONE, "K-major streaming: linear epilogue only");
   constexpr bool GATED = EPI == EPI_SWIGLU;
   constexpr int CH = 8;                        // 16-byte chunks per 128-byte LDS row
   constexpr int WAREA = 64 * CH;               // u32x4: one wave's 64 weight rows
@@ -1670,23 +1711,46 @@ __device__ __forceinline__ int stream_tile(u32x4* __restrict__ smem, const bf16*
   // j = 0 of W1, j = 1 of W3); load i (fragment i / 4) brings rows 8 (i % 4) + lr
   // of the fragment, chunk lc, into registers, then into the wave's LDS area
   // at row 8 i + lr, chunk lc ^ ((row >> 1) & 7)
-  const bf16* wrow0 = GATED ? Wg + (int64_t)(n0 + 32 * wave) * K
-                            : Wg + (int64_t)(n0 + 64 * wave) * K;
-  const bf16* wrow1 = GATED ? W3g + (int64_t)(n0 + 32 * wave) * K
-                            : Wg + (int64_t)(n0 + 64 * wave + 32) * K;
+  // (KMB: rw0 spans this wave's columns of W_g's ksplit K rows, rw1 those of
+  // W3g; load i brings K row 8 i + lr of the step, chunk lc)
+  const int kcol = KMB ? n0 + 64 * wave : 0;
+  const bf16* wrow0 = KMB ? Wg + kcol
+                          : GATED ? Wg + (int64_t)(n0 + 32 * wave) * K
+                                  : Wg + (int64_t)(n0 + 64 * wave) * K;
+  const bf16* wrow1 = KMB ? (W3g ? W3g : Wg) + kcol
+                          : GATED ? W3g + (int64_t)(n0 + 32 * wave) * K
+                                  : Wg + (int64_t)(n0 + 64 * wave + 32) * K;
+  const int wbytes0 = KMB ? (ksplit * N - kcol) * 2 : 32 * K * 2;
+  const int wbytes1 = KMB ? ((W3g ? K - ksplit : ksplit) * N - kcol) * 2 : 32 * K * 2;
   const __amdgpu_buffer_rsrc_t rw0 =
-      __builtin_amdgcn_make_buffer_rsrc((void*)wrow0, (short)0, 32 * K * 2, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)wrow0, (short)0, wbytes0, 0x00020000);
   const __amdgpu_buffer_rsrc_t rw1 =
-      __builtin_amdgcn_make_buffer_rsrc((void*)wrow1, (short)0, 32 * K * 2, 0x00020000);
-  uint32_t woff[4];
+      __builtin_amdgcn_make_buffer_rsrc((void*)wrow1, (short)0, wbytes1, 0x00020000);
+  const int kw = KMB ? ksplit / 64 : 0;   // K steps taken from W_g
+  uint32_t woff[KMB ? NW : 4];
   int wput[NW];
+  if constexpr (KMB) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q) woff[q] = (uint32_t)(8 * q + lr) * (uint32_t)K * 2u + (uint32_t)lc * 16u;
+    for (int i = 0; i < NW; ++i) woff[i] = ((uint32_t)(8 * i + lr) * (uint32_t)N + (uint32_t)lc * 8u) * 2u;
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) woff[q] = (uint32_t)(8 * q + lr) * (uint32_t)K * 2u + (uint32_t)lc * 16u;
+  }
   const int warea = wave * WAREA;
 #pragma unroll
   for (int i = 0; i < NW; ++i) {
     const int rw = 8 * i + lr;
-    wput[i] = warea + rw * CH + (lc ^ ((rw >> 1) & 7));
+    wput[i] = warea + rw * CH + (KMB ? (lc ^ (((rw >> 1) & 1) << 2)) : (lc ^ ((rw >> 1) & 7)));
+  }
+  // KMB fragment reads: byte offset of fragment j's first transposed read at
+  // sub-step 0 (+ 1024 bytes per sub-step)
+  uint32_t twb[2];
+  {
+    const int x = lane & 15, hq = (lane >> 4) & 1, sbit = (x >> 3) & 1;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      twb[j] = (uint32_t)(warea * 16 + (32 * fh + (x >> 2)) * 128 +
+                          (4 * (j ^ sbit) + 2 * hq + ((x & 3) >> 1)) * 16 + (x & 1) * 8);
   }
   // fragment reads: row 32 i + fr of a 32-row block, logical chunk 4 fh + s
   const int rsw = (fr >> 1) & 7;
@@ -1710,9 +1774,17 @@ __device__ __forceinline__ int stream_tile(u32x4* __restrict__ smem, const bf16*
   // weight loads of K step kt into register slot sl (non-temporal: read once)
 #define MOE_LW(kt, sl, i0, i1)                                                        \
   do {                                                                                \
-    _Pragma("unroll") for (int i_ = (i0); i_ < (i1); ++i_)                            \
-      wr[sl][i_] = __builtin_amdgcn_raw_buffer_load_b128(i_ < 4 ? rw0 : rw1, woff[i_ & 3], \
-                                                         (kt) * 128, 2);             \
+    if constexpr (KMB) {                                                              \
+      const int kq_ = (kt);                                                           \
+      const bool hi_ = kq_ >= kw;                                                     \
+      const int so_ = (hi_ ? kq_ - kw : kq_) * 128 * N;                               \
+      _Pragma("unroll") for (int i_ = (i0); i_ < (i1); ++i_)                          \
+        wr[sl][i_] = __builtin_amdgcn_raw_buffer_load_b128(hi_ ? rw1 : rw0, woff[i_], so_, 2); \
+    } else {                                                                          \
+      _Pragma("unroll") for (int i_ = (i0); i_ < (i1); ++i_)                          \
+        wr[sl][i_] = __builtin_amdgcn_raw_buffer_load_b128(i_ < 4 ? rw0 : rw1, woff[i_ & 3], \
+                                                           (kt) * 128, 2);           \
+    }                                                                                 \
   } while (0)
   // token-row loads of K step kt into stage st (cached: the group's other slabs
   // read the same rows)
@@ -1729,8 +1801,13 @@ __device__ __forceinline__ int stream_tile(u32x4* __restrict__ smem, const bf16*
   } while (0)
 #define MOE_RD(b, st, s)                                                              \
   do {                                                                                \
-    fw[b][0] = __builtin_bit_cast(bf16x8, smem[warea + cread[s]]);                    \
-    fw[b][1] = __builtin_bit_cast(bf16x8, smem[warea + 32 * CH + cread[s]]);          \
+    if constexpr (KMB) {                                                              \
+      fw[b][0] = lds_tr_frag<128>(smem, twb[0] + (s) * 1024);                         \
+      fw[b][1] = lds_tr_frag<128>(smem, twb[1] + (s) * 1024);                         \
+    } else {                                                                          \
+      fw[b][0] = __builtin_bit_cast(bf16x8, smem[warea + cread[s]]);                  \
+      fw[b][1] = __builtin_bit_cast(bf16x8, smem[warea + 32 * CH + cread[s]]);        \
+    }                                                                                 \
     _Pragma("unroll") for (int i_ = 0; i_ < MF; ++i_)                                 \
       fa[b][i_] = __builtin_bit_cast(bf16x8, smem[ABASE + (st) * ASTAGE + i_ * 32 * CH + cread[s]]); \
   } while (0)
@@ -1972,7 +2049,9 @@ __device__ __forceinline__ int stream_tile_packed(u32x4* __restrict__ smem,
 // Work item t of the streaming GEMM (group, rows, slab from the item space ss):
 // one tile. Returns the block's count into the done counter (thread 0; -1
 // without one).
-template <int EPI, bool HAS_BIAS>
+// KMB: K-major weights as stream_tile's KMB (W_g = W + g ksplit N, W3_g =
+// W3 + g (K - ksplit) N; the shared expert Ws / Ws3), standard layout only.
+template <int EPI, bool HAS_BIAS, bool KMB = false>
 __device__ __forceinline__ int stream_item(u32x4* __restrict__ smem, const StreamSpace& ss, int t,
                                            int ns, const bf16* __restrict__ A,
                                            const bf16* __restrict__ W, const bf16* __restrict__ W3,
@@ -1981,7 +2060,8 @@ __device__ __forceinline__ int stream_item(u32x4* __restrict__ smem, const Strea
                                            const float* __restrict__ bias_s, int E,
                                            bf16* __restrict__ C, int N, int K,
                                            const int32_t* __restrict__ arows, uint32_t a_bytes,
-                                           const bf16* __restrict__ Wp, int* __restrict__ done) {
+                                           const bf16* __restrict__ Wp, int* __restrict__ done,
+                                           int ksplit = 0) {
   constexpr bool GATED = EPI == EPI_SWIGLU;
   constexpr int BNO = GATED ? 128 : 256;
   int g, row0, nrows, slab;
@@ -1991,6 +2071,22 @@ __device__ __forceinline__ int stream_item(u32x4* __restrict__ smem, const Strea
   nrows = __builtin_amdgcn_readfirstlane(nrows);
   slab = __builtin_amdgcn_readfirstlane(slab);
   const int n0 = slab * BNO;
+  if constexpr (KMB) {
+    const bf16* Wk = g < E ? W + (int64_t)g * ksplit * N : Ws;
+    const bf16* W3k = W3 ? (g < E ? W3 + (int64_t)g * (K - ksplit) * N : Ws3) : nullptr;
+    const int mfk = (nrows + 31) / 32;
+    if (mfk <= 2)
+      return stream_tile<EPI, HAS_BIAS, 2, true>(smem, A, a_bytes, arows, Wk, W3k, nullptr, row0,
+                                                 nrows, n0, C, N, K, done, ksplit);
+    if (mfk <= 4)
+      return stream_tile<EPI, HAS_BIAS, 4, true>(smem, A, a_bytes, arows, Wk, W3k, nullptr, row0,
+                                                 nrows, n0, C, N, K, done, ksplit);
+    if (mfk <= 6)
+      return stream_tile<EPI, HAS_BIAS, 6, true>(smem, A, a_bytes, arows, Wk, W3k, nullptr, row0,
+                                                 nrows, n0, C, N, K, done, ksplit);
+    return stream_tile<EPI, HAS_BIAS, 8, true>(smem, A, a_bytes, arows, Wk, W3k, nullptr, row0,
+                                               nrows, n0, C, N, K, done, ksplit);
+  } else {
   const bf16* Wg = g < E ? W + (int64_t)g * N * K : Ws;
   const bf16* W3g = GATED ? (g < E ? W3 + (int64_t)g * N * K : Ws3) : Wg;
   const float* bg = HAS_BIAS ? (g < E ? bias + (int64_t)g * N : bias_s) : nullptr;
@@ -2024,6 +2120,7 @@ __device__ __forceinline__ int stream_item(u32x4* __restrict__ smem, const Strea
     dn = stream_tile<EPI, HAS_BIAS, 8>(smem, A, a_bytes, arows, Wg, W3g, bg, row0, nrows, n0, C, N, K, done);
   }
   return dn;
+  }
 }
 
 // Work-queue counters of the streaming GEMM: kSchedSlots slots per device of
@@ -2061,14 +2158,15 @@ __device__ int g_stream_sched[kSchedSlots * kSchedSlotInts];
 // blocks past the item count exit.
 // Requires N a multiple of 256, K a multiple of 256, and the A operand
 // addressable with 32-bit byte offsets (a_bytes < 2^32; checked by the host).
-template <int EPI, bool HAS_BIAS>
+// KMB: the weights K-major as stored (stream_item's KMB; ksplit as there).
+template <int EPI, bool HAS_BIAS, bool KMB = false>
 __global__ __launch_bounds__(256, 1) void gemm_stream_kernel(
     const bf16* __restrict__ A, const bf16* __restrict__ W, const bf16* __restrict__ W3,
     const float* __restrict__ bias, const bf16* __restrict__ Ws, const bf16* __restrict__ Ws3,
     const float* __restrict__ bias_s, int E, int G, const int32_t* __restrict__ offsets,
     int rows_max, bf16* __restrict__ C, int N, int K, const int32_t* __restrict__ arows,
     uint32_t a_bytes, int max_rows, int min_last, int max_last, const bf16* __restrict__ Wp,
-    int* __restrict__ sched) {
+    int* __restrict__ sched, int ksplit) {
   constexpr bool GATED = EPI == EPI_SWIGLU;
   constexpr int BNO = GATED ? 128 : 256;   // output columns per slab
   __shared__ u32x4 smem[kStreamLds];   // the K-step stages (160 KB, all of the CU's LDS)
@@ -2143,9 +2241,9 @@ __global__ __launch_bounds__(256, 1) void gemm_stream_kernel(
     __syncthreads();   // read by every wave before the tile's loads land in LDS
     if (t < 0) return;
   }
-  const int dn = stream_item<EPI, HAS_BIAS>(smem, ss, t, ns, A, W, W3, bias, Ws, Ws3, bias_s, E, C,
-                                            N, K, arows, a_bytes, Wp,
-                                            sched ? sched + 8 * kSchedStride : nullptr);
+  const int dn = stream_item<EPI, HAS_BIAS, KMB>(smem, ss, t, ns, A, W, W3, bias, Ws, Ws3, bias_s,
+                                                 E, C, N, K, arows, a_bytes, Wp,
+                                                 sched ? sched + 8 * kSchedStride : nullptr, ksplit);
   if (sched && threadIdx.x == 0 && dn == (int)gridDim.x - 1)
     for (int x = 0; x < 9; ++x) atomicExch(&sched[x * kSchedStride], 0);
 }
@@ -2326,7 +2424,9 @@ static int gemm_slots() {
 }
 
 // KMB: bf16 weights read K-major as stored ([K][N] per group, W3 / Ws3 for K
-// steps from ksplit on), on the 128 x 128 kernel only (backward dZ and dX).
+// steps from ksplit on; backward dZ and dX): groups of at most kStreamMaxRows
+// rows on the weight-streaming kernel where the epilogue is linear, the rest
+// on the tiled kernels.
 template <typename ET, int EPI, bool HB, bool KMB = false>
 static hipError_t gemm_launch(const moe_config& c, const ET* A, const void* W, const void* W3,
                               const float* bias, const void* Ws, const void* Ws3,
@@ -2357,8 +2457,10 @@ static hipError_t gemm_launch(const moe_config& c, const ET* A, const void* W, c
     // Groups of at most kStreamMaxRows rows go to the weight-streaming kernel
     // (forward epilogues; its A operand addressed with 32-bit byte offsets),
     // the others to the 256 x 256 and 128 x 128 kernels below.
-    constexpr bool kStreamEpi = !KMB && (EPI == EPI_GELU || EPI == EPI_RELU ||
-                                         EPI == EPI_SWIGLU || EPI == EPI_NONE);
+    // (K-major weights, the backward's dH and dX: the linear epilogue only)
+    constexpr bool kStreamEpi = KMB ? EPI == EPI_NONE
+                                    : (EPI == EPI_GELU || EPI == EPI_RELU || EPI == EPI_SWIGLU ||
+                                       EPI == EPI_NONE);
     const int64_t a_span = arows ? a_bytes : rows * (int64_t)K * 2;
     const int skip = kStreamEpi && a_span < ((int64_t)1 << 32) ? kStreamMaxRows : 0;
     // a shared expert (the last group, nominally T rows) of up to
@@ -2391,10 +2493,10 @@ static hipError_t gemm_launch(const moe_config& c, const ET* A, const void* W, c
                                                 (int64_t)G * ((skip + kStreamRows - 1) / kStreamRows));
         const int64_t items = parts * (N / BNO);
         if (items > 0)
-          hipLaunchKernelGGL((gemm_stream_kernel<EPI, HB>), dim3((unsigned)items), dim3(256), 0, s,
-                             A, (const bf16*)W, (const bf16*)W3, bias, (const bf16*)Ws,
+          hipLaunchKernelGGL((gemm_stream_kernel<EPI, HB, KMB>), dim3((unsigned)items), dim3(256), 0,
+                             s, A, (const bf16*)W, (const bf16*)W3, bias, (const bf16*)Ws,
                              (const bf16*)Ws3, bias_s, E, G, offsets, (int)rows, C, N, K, arows,
-                             (uint32_t)a_span, skip, 0, skip, (const bf16*)wpacked, sched);
+                             (uint32_t)a_span, skip, 0, skip, (const bf16*)wpacked, sched, ksplit);
         // The shared expert (group E, nominally T rows) with more than skip and
         // at most skip_last rows: a launch of its own over group E alone (at
         // most 16 parts of 256 rows per slab), in place of the tiled kernels
@@ -2408,13 +2510,13 @@ static hipError_t gemm_launch(const moe_config& c, const ET* A, const void* W, c
             if (!sched2) return hipErrorInvalidSymbol;
           }
           const size_t per_group = (size_t)(EPI == EPI_SWIGLU ? 2 : 1) * N * K;
-          hipLaunchKernelGGL((gemm_stream_kernel<EPI, HB>),
+          hipLaunchKernelGGL((gemm_stream_kernel<EPI, HB, KMB>),
                              dim3((unsigned)(kStreamSharedMaxRows / kStreamRows * (N / BNO))),
                              dim3(256), 0, s, A, (const bf16*)W, (const bf16*)W3, bias,
                              (const bf16*)Ws, (const bf16*)Ws3, bias_s, 0, 1, offsets + E,
                              (int)rows, C, N, K, arows, (uint32_t)a_span, skip, skip, skip_last,
                              wpacked ? (const bf16*)wpacked + (size_t)E * per_group : nullptr,
-                             sched2);
+                             sched2, ksplit);
         }
       }
     }
@@ -2533,6 +2635,25 @@ hipError_t launch_router_gemm(const moe_config& c, const void* x, const void* w_
   return hipGetLastError();
 }
 
+// x's router term of the backward, dlp [T][2E] (dlogits as two bf16 planes)
+// times W_g for both halves of K (ksplit = E, W3 = W_g), on the 128 x 128
+// kernel with K-major weights over the single group of T rows, float32 out.
+hipError_t launch_router_dx_gemm(const moe_config& c, const void* dlp, const void* w_gate, float* xr,
+                                 hipStream_t s) {
+  const int E = c.num_experts, N = (int)c.d_model;
+  const int64_t T = c.tokens;
+  const int64_t tiles = (T + 127) / 128 * (N / 128);
+  const int slots = gemm_slots();
+  hipLaunchKernelGGL((gemm_bf16_kernel<EPI_PARTIAL, false, true>),
+                     dim3((unsigned)(tiles < slots ? tiles : slots)), dim3(256), 0, s,
+                     (const bf16*)dlp, (const bf16*)w_gate, (const bf16*)w_gate,
+                     (const float*)nullptr, (const bf16*)nullptr, (const bf16*)nullptr,
+                     (const float*)nullptr, 1, 1, (const int32_t*)nullptr, (int)T, (void*)xr, N,
+                     2 * E, 0, (const int32_t*)nullptr, 1, (const bf16*)nullptr, 0, 0, E,
+                     (float*)nullptr, 0);
+  return hipGetLastError();
+}
+
 template <typename ET, bool HB>
 static hipError_t up_typed(const moe_config& c, const ET* a, const int32_t* arows,
                            const int32_t* off, const ExpertWeights& w, ET* h, hipStream_t s) {
@@ -2646,7 +2767,8 @@ hipError_t launch_backward_dx(const moe_config& c, const void* dz, const int32_t
 
 // The streaming threshold gemm_launch applies: groups of at most kStreamMaxRows
 // rows are streamed for the forward epilogues when the A operand spans less
-// than 4 GiB; the K-major backward GEMMs stream nothing.
+// than 4 GiB; the K-major backward GEMMs stream their groups of at most as
+// many rows too (linear epilogue), which only lowers the plan below.
 size_t rest_partial_bytes(const moe_config& c, int which) {
   if (c.act_dtype != MOE_BF16) return 0;
   const int N = (int)c.d_model, F = (int)c.d_ff;
@@ -2707,8 +2829,8 @@ hipError_t launch_wgrad(const void* a, int lda, const void* b, int ldb, const in
     hipLaunchKernelGGL(gemm_wgrad_tn_big_kernel, dim3((unsigned)big), dim3(256), 0, s,
                        (const bf16*)a, lda, (const bf16*)b, ldb, so, G, E, M, N, C, Cs);
   else
-    hipLaunchKernelGGL(gemm_wgrad_tn_kernel, dim3((unsigned)tiles), dim3(256), 0, s, (const bf16*)a,
-                       lda, (const bf16*)b, ldb, so, G, E, M, N, C, Cs);
+    hipLaunchKernelGGL(gemm_wgrad_tn_kernel, dim3((unsigned)(tiles / wgrad_run(N / 128))), dim3(256),
+                       0, s, (const bf16*)a, lda, (const bf16*)b, ldb, so, G, E, M, N, C, Cs);
   return hipGetLastError();
 }
 

@@ -85,7 +85,22 @@ BwdLayout backward_layout(const moe_config& c) {
   const int64_t slice_len = T > 0 ? (T + slices - 1) / slices : 1;
   B.gate_slice_len = (int)slice_len;
   B.gate_slices = (int)(T > 0 ? (T + slice_len - 1) / slice_len : 1);
-  B.gate_partial = take((size_t)B.gate_slices * E * d * 4);
+  B.gate_mfma = router_bwd_mfma(c) ? 1 : 0;
+  if (B.gate_mfma) {
+    // router weight gradient on the weight-gradient kernel: token slices of at
+    // least 128 rows, about 256 blocks in all, each slice's two planes (hi and
+    // lo parts of dlogits) [2E][d] float32
+    const int64_t per_slice = (2 * E / 128) * (d / 128) / wgrad_run((int)(d / 128));
+    int64_t sl = per_slice > 0 ? 256 / per_slice : 1;
+    if (sl > T / 128) sl = T / 128;
+    B.gate_slices = (int)(sl < 1 ? 1 : sl);
+    B.gate_partial = take((size_t)B.gate_slices * 2 * E * d * 4);
+    B.dlp = take((size_t)(T * 2 * E * 2));
+    B.xr = take((size_t)(T * d * 4));
+    B.gso = take((size_t)(B.gate_slices + 1) * 4);
+  } else {
+    B.gate_partial = take((size_t)B.gate_slices * E * d * 4);
+  }
   B.rest_bytes = rest_partial_bytes(c, 1);
   B.rest_partial = take(B.rest_bytes);
   B.total = off;

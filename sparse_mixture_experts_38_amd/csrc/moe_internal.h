@@ -241,11 +241,15 @@ hipError_t launch_expert_choice_forward(const moe_config& c, const EcLayout& L, 
 // Workspace of moe_backward (byte offsets). ldk is the length of the padded
 // row space of the bias column sums (each group's rows rounded up to a multiple
 // of 128, at least 128); xp holds the expert-sorted x rows.
+// gate_mfma: the router's backward terms on MFMA (router_bwd_mfma): dlp the
+// two bf16 planes of dlogits [T][2E], xr x's router term [T][d] float32, gso
+// the gate_slices + 1 token-slice bounds of the router weight gradient.
 struct BwdLayout {
   size_t dyp, dgate, dlogits, dz, dh, dxp, po;   // po: padded then sanitized offsets
   size_t xp, colsum1, colsum2, gate_partial, rest_partial, rest_bytes, total;
+  size_t dlp, xr, gso;
   int64_t ldk;
-  int gate_slices, gate_slice_len;
+  int gate_slices, gate_slice_len, gate_mfma;
 };
 BwdLayout backward_layout(const moe_config& c);
 
@@ -263,9 +267,11 @@ hipError_t launch_combine_backward(const moe_config& c, const void* dy, const vo
 hipError_t launch_router_backward(const moe_config& c, const moe_routing& r, const moe_stats* stats,
                                   const float* dgate, float aux_coef, float z_coef, float* dlogits,
                                   hipStream_t s);
+// (xr: x's router term precomputed, [T][d] float32, or null: computed here)
 hipError_t launch_router_bias_and_dx(const moe_config& c, const float* dlogits, const void* dxp,
                                      const moe_routing& r, const moe_weights& w,
-                                     const moe_grads& gr, hipStream_t s);
+                                     const moe_grads& gr, hipStream_t s,
+                                     const float* xr = nullptr);
 // float32 layers: h = act(z) of the training forward, the backward workspace
 // layout (dyp, dgate, dlogits, dz, dh, dxp) and the whole backward.
 hipError_t launch_act_rows_f32(const moe_config& c, const void* z, const int32_t* expert_offsets,
@@ -307,5 +313,20 @@ hipError_t launch_backward_dx(const moe_config& c, const void* dz, const int32_t
 // C float32 [E][M][N], Cs [M][N] for group E.
 hipError_t launch_wgrad(const void* a, int lda, const void* b, int ldb, const int32_t* so, int G,
                         int E, int M, int N, int64_t rows, float* C, float* Cs, hipStream_t stream);
+// n tiles of 128 columns that one block of the 128 x 128 weight-gradient
+// kernel runs in turn (ntn = N / 128 tiles in a row of its output).
+__host__ __device__ inline int wgrad_run(int ntn) {
+  return ntn % 4 == 0 ? 4 : (ntn % 2 == 0 ? 2 : 1);
+}
+// The router's backward terms on MFMA where its weights are bf16 and E is a
+// multiple of 128 (the layers whose router GEMM runs on MFMA in the forward).
+inline bool router_bwd_mfma(const moe_config& c) {
+  return c.act_dtype == MOE_BF16 && c.router_dtype == MOE_BF16 && c.num_experts % 128 == 0 &&
+         c.tokens > 0;
+}
+// x's router term xr [T][d] float32 = dlp [T][2E] times W_g (both K halves;
+// W_g [E][d] bf16 as stored, K-major).
+hipError_t launch_router_dx_gemm(const moe_config& c, const void* dlp, const void* w_gate, float* xr,
+                                 hipStream_t stream);
 
 }  // namespace moe
