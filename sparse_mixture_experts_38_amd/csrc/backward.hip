@@ -248,25 +248,67 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(
 }
 
 // ------------------------------------------------------------------ weight and bias gradients
-// so[g]: expert_offsets clamped to [0, rows_max] and made non-decreasing, so the
-// groups' rows never sum past rows_max; po[g] = sum over g' < g of the padded
-// row count of group g' (its rows rounded up to a multiple of 128, at least
-// 128), hence po[G] <= rows_max + 128 G (one thread; G <= 257).
-__global__ void pad_offsets_kernel(const int32_t* __restrict__ off, int G, int64_t rows_max,
-                                   int32_t* __restrict__ po, int32_t* __restrict__ so) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
-  int acc = 0, prev = clamp_off(off, 0, rows_max);
-  po[0] = 0;
-  so[0] = prev;
-  for (int g = 0; g < G; ++g) {
-    int hi = clamp_off(off, g + 1, rows_max);
-    hi = hi < prev ? prev : hi;
-    const int r = hi - prev;
-    const int p = r <= 128 ? 128 : (r + 127) & ~127;
-    acc += p;
-    po[g + 1] = acc;
-    so[g + 1] = hi;
-    prev = hi;
+// so[g]: expert_offsets clamped to [0, rows_max] and made non-decreasing (a
+// running maximum), so the groups' rows never sum past rows_max; po[g] = sum
+// over g' < g of the padded row count of group g' (its rows rounded up to a
+// multiple of 128, at least 128), hence po[G] <= rows_max + 128 G. One wave:
+// lane l takes groups 5 l .. 5 l + 4 (G <= 257), then a prefix maximum and a
+// prefix sum over the lanes.
+__global__ __launch_bounds__(64) void pad_offsets_kernel(const int32_t* __restrict__ off, int G,
+                                                         int64_t rows_max, int32_t* __restrict__ po,
+                                                         int32_t* __restrict__ so) {
+  constexpr int PER = 5;
+  const int lane = threadIdx.x;
+  if (blockIdx.x != 0 || lane >= 64) return;
+  const int base = clamp_off(off, 0, rows_max);
+  int hi[PER];
+  int m = base;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int g = lane * PER + i;
+    const int v = g < G ? clamp_off(off, g + 1, rows_max) : base;
+    m = v > m ? v : m;
+    hi[i] = m;
+  }
+  int incl = m;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl = t > incl ? t : incl;
+  }
+  const int up = __shfl_up(incl, 1, 64);
+  const int before = lane == 0 ? base : up;   // so of this lane's first group
+  int prev = before, sum = 0;
+  int pad[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int g = lane * PER + i;
+    const int h = hi[i] > before ? hi[i] : before;
+    const int r = h - prev;
+    pad[i] = g < G ? (r <= 128 ? 128 : (r + 127) & ~127) : 0;
+    sum += pad[i];
+    hi[i] = h;
+    prev = h;
+  }
+  int isum = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(isum, o, 64);
+    if (lane >= o) isum += t;
+  }
+  int acc = isum - sum;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int g = lane * PER + i;
+    acc += pad[i];
+    if (g < G) {
+      po[g + 1] = acc;
+      so[g + 1] = hi[i];
+    }
+  }
+  if (lane == 0) {
+    po[0] = 0;
+    so[0] = base;
   }
 }
 
