@@ -70,6 +70,49 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const XT* __restrict
   }
 }
 
+// Butterfly exchange over groups of L lanes (L a power of two <= 64), level
+// by level: lane i receives the value of its partner at levels 1 and 2 (DPP
+// quad permutations, lanes i ^ 1 and i ^ 2), 4 (DPP mirror within 8 lanes,
+// i ^ 7) and 8 (DPP mirror within 16 lanes, i ^ 15), then lanes i ^ 16 and
+// i ^ 32 (LDS permute). The first four are plain ALU moves; after levels
+// 1, 2, 4, 8, ... every lane of a group has combined all of the group's
+// values, as with partners i ^ 1, i ^ 2, i ^ 4, i ^ 8. Every lane of the
+// wave must be active.
+template <int LVL>
+__device__ __forceinline__ int lane_xchg(int v) {
+  if constexpr (LVL == 1) return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);
+  else if constexpr (LVL == 2) return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);
+  else if constexpr (LVL == 4) return __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false);
+  else if constexpr (LVL == 8) return __builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, false);
+  else return __shfl_xor(v, LVL, 64);
+}
+template <int LVL>
+__device__ __forceinline__ float lane_xchg(float v) {
+  return __int_as_float(lane_xchg<LVL>(__float_as_int(v)));
+}
+template <int L>
+__device__ __forceinline__ float group_max(float v) {
+  if constexpr (L > 1) v = fmaxf(v, lane_xchg<1>(v));
+  if constexpr (L > 2) v = fmaxf(v, lane_xchg<2>(v));
+  if constexpr (L > 4) v = fmaxf(v, lane_xchg<4>(v));
+  if constexpr (L > 8) v = fmaxf(v, lane_xchg<8>(v));
+  if constexpr (L > 16) v = fmaxf(v, lane_xchg<16>(v));
+  if constexpr (L > 32) v = fmaxf(v, lane_xchg<32>(v));
+  return v;
+}
+// (every lane of a group ends with the same sum: each level adds two equal
+// partial sums in either order)
+template <int L>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (L > 1) v += lane_xchg<1>(v);
+  if constexpr (L > 2) v += lane_xchg<2>(v);
+  if constexpr (L > 4) v += lane_xchg<4>(v);
+  if constexpr (L > 8) v += lane_xchg<8>(v);
+  if constexpr (L > 16) v += lane_xchg<16>(v);
+  if constexpr (L > 32) v += lane_xchg<32>(v);
+  return v;
+}
+
 // (key, index) order used for selection: larger key first, then lower index.
 // An out-of-range index (>= E) never beats an in-range one.
 __device__ __forceinline__ bool better(float ka, int ia, float kb, int ib, int E) {
@@ -98,8 +141,7 @@ __device__ __forceinline__ void route_token(const float l[J], bool valid, int64_
     taken[jj] = false;
     if (e < E) m = fmaxf(m, l[jj]);
   }
-#pragma unroll
-  for (int off = L / 2; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, L));
+  m = group_max<L>(m);
   float ex[J];
   float s = 0.f;
 #pragma unroll
@@ -108,8 +150,7 @@ __device__ __forceinline__ void route_token(const float l[J], bool valid, int64_
     ex[jj] = (e < E) ? expf(l[jj] - m) : 0.f;
     s += ex[jj];
   }
-#pragma unroll
-  for (int off = L / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off, L);
+  s = group_sum<L>(s);
   const float lse = m + logf(s);
   float ssum = 0.f;
   if (!sigmoid) {
@@ -132,8 +173,7 @@ __device__ __forceinline__ void route_token(const float l[J], bool valid, int64_
       }
       ssum += sc[jj];
     }
-#pragma unroll
-    for (int off = L / 2; off >= 1; off >>= 1) ssum += __shfl_xor(ssum, off, L);
+    ssum = group_sum<L>(ssum);
   }
 
   int sel_idx[MOE_MAX_TOP_K];
@@ -153,15 +193,23 @@ __device__ __forceinline__ void route_token(const float l[J], bool valid, int64_
           bi = e;
         }
       }
-#pragma unroll
-      for (int off = L / 2; off >= 1; off >>= 1) {
-        const float ok = __shfl_xor(bk, off, L);
-        const int oi = __shfl_xor(bi, off, L);
-        if (better(ok, oi, bk, bi, E)) {
-          bk = ok;
-          bi = oi;
-        }
-      }
+      // (key, index) maximum over the group, level by level
+#define MOE_ARGMAX_LVL(LVL)                                                           \
+  if constexpr (L > (LVL)) {                                                          \
+    const float ok = lane_xchg<LVL>(bk);                                              \
+    const int oi = lane_xchg<LVL>(bi);                                                \
+    if (better(ok, oi, bk, bi, E)) {                                                  \
+      bk = ok;                                                                        \
+      bi = oi;                                                                        \
+    }                                                                                 \
+  }
+      MOE_ARGMAX_LVL(1)
+      MOE_ARGMAX_LVL(2)
+      MOE_ARGMAX_LVL(4)
+      MOE_ARGMAX_LVL(8)
+      MOE_ARGMAX_LVL(16)
+      MOE_ARGMAX_LVL(32)
+#undef MOE_ARGMAX_LVL
       // bi is uniform over the group; fetch its score from the owning lane.
       const int owner_j = bi / L;
       float mine = 0.f;
