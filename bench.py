@@ -317,7 +317,7 @@ def main():
     ap.add_argument("--sets", type=int, default=2, help="rotated input/weight sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
-                    help="only the headline workload (no other workloads, training or expert choice)")
+                    help="only the headline workload's forward (no other workloads, training or expert choice)")
     ap.add_argument("--no-expert-choice", action="store_true")
     ap.add_argument("--no-train", action="store_true")
     ap.add_argument("--no-standard-layout", action="store_true",
@@ -390,7 +390,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, sets[0])
-    if not args.no_train and A.lib().moe_backward_workspace_size(
+    if not args.no_train and not args.no_extras and A.lib().moe_backward_workspace_size(
             ctypes.byref(cfg), ctypes.byref(ctypes.c_size_t(0))) == A.MOE_OK:
         # a training step of the headline layer itself
         result["train_" + w.name] = train_step(A, torch, w, cfg, sets, ws, max(5, args.steps // 4),
