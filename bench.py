@@ -90,8 +90,10 @@ def gemm_work(w, counts_kept):
     return {"expert_up": up, "expert_down": down, "rows": rows, "groups_with_rows": used}
 
 
-def roofline(w, work, stage_ms):
-    """Roofline of the longer GEMM stage: bound by its algorithmic intensity."""
+def roofline(w, work, stage_ms, packed=True):
+    """Roofline of the longer GEMM stage: bound by its algorithmic intensity.
+    The counter bytes (traffic) were taken on the packed weights; for the
+    standard layout they are not known (null)."""
     dom = max(("expert_up", "expert_down"), key=lambda s: stage_ms[s])
     flop, byts, ms = work[dom]["flop"], work[dom]["bytes"], stage_ms[dom]
     intensity = flop / byts
@@ -100,7 +102,8 @@ def roofline(w, work, stage_ms):
     r = hbm if intensity < RIDGE else mfma
     out = {"bound": "hbm" if intensity < RIDGE else "mfma", "kernel": dom,
            "achieved": r["achieved"], "peak": r["peak"], "unit": r["unit"],
-           "frac": r["achieved"] / r["peak"], "traffic": read_traffic(dom, w.name),
+           "frac": r["achieved"] / r["peak"],
+           "traffic": read_traffic(dom, w.name) if packed else None,
            "algorithmic_bytes": byts, "algorithmic_flop": flop,
            "intensity_flop_per_byte": intensity, "stage_ms": ms}
     # the other roofline of the same stage, for context
@@ -172,7 +175,7 @@ def measure_forward(A, torch, w, n_sets, steps, warmup, packed=True):
            "weights": "packed" if "up_packed" in sets[0] else "standard",
            "stages_ms": stage_ms, "kept_rows": statistics.mean(int(sum(kc)) for kc in kept),
            "groups_with_rows": work["groups_with_rows"], "wall_s": wall,
-           "roofline": roofline(w, work, stage_ms)}
+           "roofline": roofline(w, work, stage_ms, packed="up_packed" in sets[0])}
     return res, cfg, sets, ws
 
 
