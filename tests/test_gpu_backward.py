@@ -216,6 +216,47 @@ def test_backward_edge_cases():
     check_backward(w, inp, dy, out)
 
 
+def test_backward_router_mfma_edge_cases():
+    """The router terms of the backward on MFMA (bf16 router, E a multiple of
+    128: dlogits as two bf16 planes, the router weight gradient over token
+    slices, x's router term as a GEMM) at the token counts where the slices
+    degenerate: one token, fewer tokens than one 128-row slice, and a count that
+    is not a multiple of the slice size; DeepSeek-V3 recipe (sigmoid, top-8 of
+    256, SwiGLU, shared expert) and a softmax router with 128 experts."""
+    ds = W["deepseek_v3"].scaled(d_model=256, d_ff=256)
+    cases = {
+        "ds_one_token": ds.scaled(tokens=1),
+        "ds_100_tokens": ds.scaled(tokens=100),
+        "ds_517_tokens": ds.scaled(tokens=517),
+        "softmax_128_experts": W["deepspeed_gpt_moe"].scaled(
+            tokens=300, d_model=256, d_ff=256, num_experts=128, top_k=2, router_dtype="bf16",
+            drop_tokens=False),
+    }
+    for name, w in cases.items():
+        print(f"[case] backward router-mfma edge {name}", flush=True)
+        inp = make_inputs(w, seed=6, device="cpu")
+        dy = make_dy(w, 6)
+        out = gpu_train_step(w, to_gpu(inp), dy.cuda())
+        check_backward(w, inp, dy, out)
+
+
+def test_backward_stream_and_tiled_groups():
+    """dH and dX with one group above the streaming kernel's 1536-row limit (tiled
+    kernels) and one below it (weight-streaming kernel with K-major weights) in the
+    same launches: Mixtral recipe (SwiGLU, K = 2F for dX over [W1; W3]), 2 experts,
+    top-1, a gate bias that sends most tokens to expert 0."""
+    w = W["mixtral_8x7b"].scaled(tokens=2000, d_model=256, d_ff=512, num_experts=2, top_k=1,
+                                 has_gate_bias=True)
+    print("[case] backward streamed + tiled groups", flush=True)
+    inp = make_inputs(w, seed=7, device="cpu")
+    inp["b_gate"] = torch.tensor([0.5, 0.0])
+    dy = make_dy(w, 7)
+    out = gpu_train_step(w, to_gpu(inp), dy.cuda())
+    kept = [int(v) for v in out["stats"]["counts_kept"][:2]]
+    assert max(kept) > 1536 and min(kept) <= 1536, kept
+    check_backward(w, inp, dy, out)
+
+
 def test_backward_full_size_sampled():
     """DeepSpeed GPT-MoE at its full size (T = 8192, d = 1024, F = 4096, 8 experts):
     the router weight gradient in full and sampled rows of every other gradient,
