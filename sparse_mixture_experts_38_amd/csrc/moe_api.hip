@@ -409,14 +409,17 @@ int moe_forward_profiled(const moe_config* cfg, const void* x, const moe_weights
     return events && events[i] ? hipEventRecord((hipEvent_t)events[i], s) : hipSuccess;
   };
   if (mark(MOE_EV_START) != hipSuccess) return MOE_ERR_HIP;
+  // (the reduction of the router statistics runs inside the dispatch's first
+  // launch)
+  int route_blocks = 0;
   hipError_t e = launch_route(*cfg, L, x, w->w_gate, w->b_gate, w->e_bias, r->logits, r->topk_idx,
-                              r->topk_gate, stats, ws, s);
+                              r->topk_gate, stats, ws, s, &route_blocks);
   if (e != hipSuccess || mark(MOE_EV_ROUTED) != hipSuccess) return MOE_ERR_HIP;
   void* y_perm = ws + L.y_perm;
   // the expert-sorted token rows are not copied: GEMM 1 gathers them from x
   // through row_token
   e = launch_permute(*cfg, L, capacity_exact(*cfg), r->topk_idx, x, r->expert_offsets,
-                     r->row_token, r->assign_row, nullptr, stats, ws, s);
+                     r->row_token, r->assign_row, nullptr, stats, ws, s, route_blocks);
   if (e != hipSuccess || mark(MOE_EV_DISPATCHED) != hipSuccess) return MOE_ERR_HIP;
   const ExpertWeights ew{w->w1,  w->w3,  w->w2,  w->b1,  w->b2,        w->ws1,
                          w->ws3, w->ws2, w->bs1, w->bs2, w->up_packed, w->down_packed};
@@ -567,11 +570,12 @@ int moe_forward_train(const moe_config* cfg, const void* x, const moe_weights* w
   if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
   char* ws = (char*)workspace;
   const hipStream_t s = (hipStream_t)stream;
+  int route_blocks = 0;
   hipError_t e = launch_route(*cfg, L, x, w->w_gate, w->b_gate, w->e_bias, r->logits, r->topk_idx,
-                              r->topk_gate, stats, ws, s);
+                              r->topk_gate, stats, ws, s, &route_blocks);
   if (e != hipSuccess) return MOE_ERR_HIP;
   e = launch_permute(*cfg, L, capacity_exact(*cfg), r->topk_idx, x, r->expert_offsets,
-                     r->row_token, r->assign_row, nullptr, stats, ws, s);
+                     r->row_token, r->assign_row, nullptr, stats, ws, s, route_blocks);
   if (e != hipSuccess) return MOE_ERR_HIP;
   const ExpertWeights ew{w->w1, w->w3, w->w2, w->b1, w->b2, w->ws1, w->ws3, w->ws2, w->bs1, w->bs2};
   e = launch_expert_up_linear(*cfg, x, r->expert_offsets, ew, saved->z, s, r->row_token);

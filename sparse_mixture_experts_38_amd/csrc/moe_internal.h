@@ -173,14 +173,49 @@ hipError_t launch_router_logits(const moe_config& c, const void* x, const void* 
                                 const float* b_gate, float* logits, float* router_planes,
                                 hipStream_t stream);
 
+// With defer_stats non-null the reduction of the router's per-block partials
+// into P_i and z is left to launch_permute (the number of partial rows is
+// written to *defer_stats), which then runs it inside its first launch.
 hipError_t launch_route(const moe_config& c, const WsLayout& L, const void* x, const void* w_gate,
                         const float* b_gate, const float* e_bias, float* logits, int32_t* topk_idx,
-                        float* topk_gate, moe_stats* stats, char* ws, hipStream_t stream);
+                        float* topk_gate, moe_stats* stats, char* ws, hipStream_t stream,
+                        int* defer_stats = nullptr);
 
+// route_blocks > 0: also reduce that many rows of the router's partials (a
+// launch_route with defer_stats) into P_i and z, before the statistics that
+// need them.
 hipError_t launch_permute(const moe_config& c, const WsLayout& L, int64_t capacity,
                           const int32_t* topk_idx, const void* x, int32_t* expert_offsets,
                           int32_t* row_token, int32_t* assign_row, void* x_perm, moe_stats* stats,
-                          char* ws, hipStream_t stream);
+                          char* ws, hipStream_t stream, int route_blocks = 0);
+
+// Column col of the router statistics (one block of 256 threads): P_col =
+// (1/T) sum of the nblocks per-block partials of column col (col < E), z =
+// (1/T) sum of the lse^2 column (col == E), or the zero fill of the unused
+// expert slots (col == E + 1); a strided float64 pass per thread, then a tree
+// in LDS: deterministic. red: 256 doubles of LDS.
+__device__ __forceinline__ void route_stats_column(const float* __restrict__ partials, int nblocks,
+                                                   int E, int64_t T, moe_stats* __restrict__ stats,
+                                                   int col, double* red) {
+  const int tid = threadIdx.x;
+  if (col == E + 1) {
+    for (int e = E + tid; e < MOE_MAX_EXPERTS; e += 256) stats->prob_mean[e] = 0.f;
+    return;
+  }
+  double s = 0.0;
+  for (int b = tid; b < nblocks; b += 256) s += partials[(int64_t)b * (E + 1) + col];
+  red[tid] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) red[tid] += red[tid + w];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    const float v = (float)(red[0] / (double)T);
+    if (col < E) stats->prob_mean[col] = v;
+    else stats->z_loss = v;
+  }
+}
 
 struct ExpertWeights {
   const void *w1, *w3, *w2;

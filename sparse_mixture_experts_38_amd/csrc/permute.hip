@@ -15,62 +15,13 @@
 
 namespace moe {
 
-// One block ranks kRankChunk consecutive assignments, 256 per round.
-__global__ __launch_bounds__(256) void dispatch_rank_kernel(const int32_t* __restrict__ topk_idx,
-                                                            int64_t T, int k, int E, int64_t A,
-                                                            int32_t* __restrict__ local_rank,
-                                                            int32_t* __restrict__ chunk_hist) {
-  __shared__ int hist[MOE_MAX_EXPERTS];
-  __shared__ int wcount[4][MOE_MAX_EXPERTS];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = tid >> 6;
-  hist[tid] = 0;
-  const int64_t a0 = (int64_t)blockIdx.x * kRankChunk;
-  for (int r = 0; r < kRankChunk / 256; ++r) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) wcount[i][tid] = 0;
-    __syncthreads();
-    const int64_t a = a0 + r * 256 + tid;
-    int e = 511;  // sentinel: no assignment / index out of range
-    if (a < A) {
-      const int64_t j = a / T;
-      const int64_t t = a - j * T;
-      const int v = topk_idx[t * k + j];
-      if (v >= 0 && v < E) e = v;
-    }
-    // lanes holding the same expert id
-    uint64_t peers = ~0ull;
-#pragma unroll
-    for (int b = 0; b < 9; ++b) {
-      const bool bit = (e >> b) & 1;
-      const uint64_t bal = __ballot(bit);
-      peers &= bit ? bal : ~bal;
-    }
-    const int rank_w = __popcll(peers & ((1ull << lane) - 1ull));
-    if (e < E && rank_w == 0) wcount[w][e] = __popcll(peers);
-    __syncthreads();
-    if (e < E) {
-      int rank = hist[e] + rank_w;
-      for (int ww = 0; ww < w; ++ww) rank += wcount[ww][e];
-      local_rank[a] = rank;
-    }
-    __syncthreads();
-    hist[tid] += wcount[0][tid] + wcount[1][tid] + wcount[2][tid] + wcount[3][tid];
-    __syncthreads();
-  }
-  if (tid < E) chunk_hist[(int64_t)blockIdx.x * E + tid] = hist[tid];
-}
-
-// Single block: per-expert exclusive scan over chunks (queue base of each
-// chunk), counts before and after capacity, expert offsets, and the
-// statistics that need the counts (f_i, L_aux with the router's P_i).
-__global__ __launch_bounds__(256) void dispatch_scan_kernel(
+// Per-expert exclusive scan over chunks (queue base of each chunk), counts
+// before and after capacity, expert offsets, and the statistics that need the
+// counts (f_i, L_aux with the router's P_i); one block of 256 threads.
+__device__ __forceinline__ void dispatch_scan_block(
     const int32_t* __restrict__ chunk_hist, int32_t* __restrict__ chunk_base, int chunks, int E,
     int64_t T, int k, int S, int64_t cap, int32_t* __restrict__ expert_offsets,
-    moe_stats* __restrict__ stats) {
-  __shared__ int sc[256];
-  __shared__ double red[256];
+    moe_stats* __restrict__ stats, int* sc, double* red) {
   const int e = threadIdx.x;
   int pre = 0;
   if (e < E) {
@@ -121,6 +72,77 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(
     stats->dropped = (int)(A - R);
     stats->reserved[0] = stats->reserved[1] = stats->reserved[2] = 0;
   }
+}
+
+// Blocks b < chunks: block b ranks kRankChunk consecutive assignments, 256 per
+// round, and writes its chunk's per-expert counts. Blocks chunks .. chunks +
+// E + 1 (route_blocks > 0): column b - chunks of the router statistics
+// (route_stats_column over route_blocks partial rows), which the scan kernel
+// after this launch reads for L_aux.
+__global__ __launch_bounds__(256) void dispatch_rank_kernel(const int32_t* __restrict__ topk_idx,
+                                                            int64_t T, int k, int E, int64_t A,
+                                                            int32_t* __restrict__ local_rank,
+                                                            int32_t* __restrict__ chunk_hist,
+                                                            int chunks, const float* __restrict__ rp,
+                                                            int route_blocks,
+                                                            moe_stats* __restrict__ stats) {
+  __shared__ int hist[MOE_MAX_EXPERTS];
+  __shared__ int wcount[4][MOE_MAX_EXPERTS];
+  __shared__ double red[256];
+  const int tid = threadIdx.x;
+  if ((int)blockIdx.x < chunks) {
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  hist[tid] = 0;
+  const int64_t a0 = (int64_t)blockIdx.x * kRankChunk;
+  for (int r = 0; r < kRankChunk / 256; ++r) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wcount[i][tid] = 0;
+    __syncthreads();
+    const int64_t a = a0 + r * 256 + tid;
+    int e = 511;  // sentinel: no assignment / index out of range
+    if (a < A) {
+      const int64_t j = a / T;
+      const int64_t t = a - j * T;
+      const int v = topk_idx[t * k + j];
+      if (v >= 0 && v < E) e = v;
+    }
+    // lanes holding the same expert id
+    uint64_t peers = ~0ull;
+#pragma unroll
+    for (int b = 0; b < 9; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t bal = __ballot(bit);
+      peers &= bit ? bal : ~bal;
+    }
+    const int rank_w = __popcll(peers & ((1ull << lane) - 1ull));
+    if (e < E && rank_w == 0) wcount[w][e] = __popcll(peers);
+    __syncthreads();
+    if (e < E) {
+      int rank = hist[e] + rank_w;
+      for (int ww = 0; ww < w; ++ww) rank += wcount[ww][e];
+      local_rank[a] = rank;
+    }
+    __syncthreads();
+    hist[tid] += wcount[0][tid] + wcount[1][tid] + wcount[2][tid] + wcount[3][tid];
+    __syncthreads();
+  }
+  if (tid < E) chunk_hist[(int64_t)blockIdx.x * E + tid] = hist[tid];
+  } else {
+    route_stats_column(rp, route_blocks, E, T, stats, (int)blockIdx.x - chunks, red);
+  }
+}
+
+// Single block: the chunk scan, counts, offsets and statistics
+// (dispatch_scan_block).
+__global__ __launch_bounds__(256) void dispatch_scan_kernel(
+    const int32_t* __restrict__ chunk_hist, int32_t* __restrict__ chunk_base, int chunks, int E,
+    int64_t T, int k, int S, int64_t cap, int32_t* __restrict__ expert_offsets,
+    moe_stats* __restrict__ stats) {
+  __shared__ int sc[256];
+  __shared__ double red[256];
+  dispatch_scan_block(chunk_hist, chunk_base, chunks, E, T, k, S, cap, expert_offsets, stats, sc,
+                      red);
 }
 
 // One wavefront per assignment (and per shared-expert row): writes the maps
@@ -191,15 +213,17 @@ __global__ __launch_bounds__(256) void dispatch_maps_kernel(
 hipError_t launch_permute(const moe_config& c, const WsLayout& L, int64_t cap,
                           const int32_t* topk_idx, const void* x, int32_t* expert_offsets,
                           int32_t* row_token, int32_t* assign_row, void* x_perm, moe_stats* stats,
-                          char* ws, hipStream_t s) {
+                          char* ws, hipStream_t s, int route_blocks) {
   const int64_t T = c.tokens;
   const int k = c.top_k, E = c.num_experts, S = c.num_shared_experts;
   const int64_t A = T * k;
   int32_t* local_rank = reinterpret_cast<int32_t*>(ws + L.local_rank);
   int32_t* chunk_hist = reinterpret_cast<int32_t*>(ws + L.chunk_hist);
   int32_t* chunk_base = reinterpret_cast<int32_t*>(ws + L.chunk_base);
-  hipLaunchKernelGGL(dispatch_rank_kernel, dim3(L.chunks), dim3(256), 0, s, topk_idx, T, k, E, A,
-                     local_rank, chunk_hist);
+  const int extra = route_blocks > 0 ? E + 2 : 0;
+  hipLaunchKernelGGL(dispatch_rank_kernel, dim3((unsigned)(L.chunks + extra)), dim3(256), 0, s,
+                     topk_idx, T, k, E, A, local_rank, chunk_hist, L.chunks,
+                     reinterpret_cast<const float*>(ws + L.route_partials), route_blocks, stats);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(256), 0, s, chunk_hist, chunk_base,

@@ -446,34 +446,14 @@ __global__ __launch_bounds__(256) void router_logits_mfma_kernel(
   }
 }
 
-// P_i = (1/T) sum of the per-block partials and z = (1/T) sum_t lse_t^2.
-// Block e < E reduces column e, block E the lse^2 column, and block E + 1
-// zero-fills the unused expert slots; each block sums in a fixed order (a
-// strided float64 pass per thread, then a tree in LDS), so the result is
-// deterministic.
+// P_i = (1/T) sum of the per-block partials and z = (1/T) sum_t lse_t^2:
+// block e < E reduces column e, block E the lse^2 column, and block E + 1
+// zero-fills the unused expert slots (route_stats_column).
 __global__ __launch_bounds__(256) void route_stats_kernel(const float* __restrict__ partials,
                                                           int nblocks, int E, int64_t T,
                                                           moe_stats* __restrict__ stats) {
   __shared__ double red[256];
-  const int col = blockIdx.x;
-  const int tid = threadIdx.x;
-  if (col == E + 1) {
-    for (int e = E + tid; e < MOE_MAX_EXPERTS; e += 256) stats->prob_mean[e] = 0.f;
-    return;
-  }
-  double s = 0.0;
-  for (int b = tid; b < nblocks; b += 256) s += partials[(int64_t)b * (E + 1) + col];
-  red[tid] = s;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (tid < w) red[tid] += red[tid + w];
-    __syncthreads();
-  }
-  if (tid == 0) {
-    const float v = (float)(red[0] / (double)T);
-    if (col < E) stats->prob_mean[col] = v;
-    else stats->z_loss = v;
-  }
+  route_stats_column(partials, nblocks, E, T, stats, (int)blockIdx.x, red);
 }
 
 template <int L, int J>
@@ -545,7 +525,8 @@ hipError_t launch_router_logits(const moe_config& c, const void* x, const void* 
 
 hipError_t launch_route(const moe_config& c, const WsLayout& L, const void* x, const void* w_gate,
                         const float* b_gate, const float* e_bias, float* logits, int32_t* topk_idx,
-                        float* topk_gate, moe_stats* stats, char* ws, hipStream_t s) {
+                        float* topk_gate, moe_stats* stats, char* ws, hipStream_t s,
+                        int* defer_stats) {
   const int E = c.num_experts;
   float* lg = logits ? logits : reinterpret_cast<float*>(ws + L.logits);
   float* partials = reinterpret_cast<float*>(ws + L.route_partials);
@@ -569,8 +550,13 @@ hipError_t launch_route(const moe_config& c, const WsLayout& L, const void* x, c
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(route_stats_kernel, dim3(E + 2), dim3(256), 0, s, partials,
-                       (int)((c.tokens + 31) / 32), E, (int64_t)c.tokens, stats);
+    const int pb = (int)((c.tokens + 31) / 32);
+    if (defer_stats) {
+      *defer_stats = pb;
+      return hipSuccess;
+    }
+    hipLaunchKernelGGL(route_stats_kernel, dim3(E + 2), dim3(256), 0, s, partials, pb, E,
+                       (int64_t)c.tokens, stats);
     return hipGetLastError();
   }
   hipError_t err = launch_router_logits(c, x, w_gate, b_gate, lg,
@@ -594,6 +580,10 @@ hipError_t launch_route(const moe_config& c, const WsLayout& L, const void* x, c
   }
   err = hipGetLastError();
   if (err != hipSuccess) return err;
+  if (defer_stats) {
+    *defer_stats = L.route_blocks;
+    return hipSuccess;
+  }
   hipLaunchKernelGGL(route_stats_kernel, dim3(E + 2), dim3(256), 0, s, partials,
                      L.route_blocks, E, (int64_t)c.tokens, stats);
   return hipGetLastError();
