@@ -67,7 +67,7 @@ extern "C" {
 enum moe_status {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARG = 1, /* null pointer, out-of-range field, inconsistent sizes */
-  MOE_ERR_UNSUPPORTED = 2, /* valid layer this build does not run (shape multiple) */
+  MOE_ERR_UNSUPPORTED = 2, /* valid layer this library does not run (shape multiple) */
   MOE_ERR_WORKSPACE = 3,   /* workspace smaller than moe_workspace_size() */
   MOE_ERR_HIP = 4          /* a HIP launch or runtime call failed */
 };

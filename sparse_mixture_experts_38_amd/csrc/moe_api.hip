@@ -127,7 +127,7 @@ static int validate(const moe_config* c) {
     if (!(cf >= 1e-9 && cf <= 1e6)) return MOE_ERR_INVALID_ARG;  // also rejects NaN
     if (c->min_capacity < 0) return MOE_ERR_INVALID_ARG;
   }
-  // Sizes this build runs: 32-bit row indices, 16-byte row vectors, and the
+  // Sizes this library runs: 32-bit row indices, 16-byte row vectors, and the
   // MFMA tile multiples of the bf16 expert GEMM.
   const int64_t rows = c->tokens * c->top_k + (int64_t)c->num_shared_experts * c->tokens;
   if (c->tokens > (int64_t)1 << 28 || rows >= ((int64_t)1 << 31) - 4096) return MOE_ERR_UNSUPPORTED;
@@ -200,7 +200,7 @@ const char* moe_status_string(int status) {
   switch (status) {
     case MOE_OK: return "MOE_OK";
     case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: invalid argument";
-    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: layer shape not supported by this build";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: layer shape not supported by this library";
     case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace smaller than moe_workspace_size()";
     case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP launch or runtime call failed";
     default: return "unknown moe status";
