@@ -2462,7 +2462,10 @@ static hipError_t gemm_launch(const moe_config& c, const ET* A, const void* W, c
                                     : (EPI == EPI_GELU || EPI == EPI_RELU || EPI == EPI_SWIGLU ||
                                        EPI == EPI_NONE);
     const int64_t a_span = arows ? a_bytes : rows * (int64_t)K * 2;
-    const int skip = kStreamEpi && a_span < ((int64_t)1 << 32) ? kStreamMaxRows : 0;
+    // (K-major: the streaming tile addresses a group's weights, K x N bf16, with
+    // 32-bit signed byte counts)
+    const bool kmb_fits = !KMB || (int64_t)K * N * 2 < ((int64_t)1 << 31);
+    const int skip = kStreamEpi && kmb_fits && a_span < ((int64_t)1 << 32) ? kStreamMaxRows : 0;
     // a shared expert (the last group, nominally T rows) of up to
     // kStreamSharedMaxRows rows is streamed too (at the DeepSeek-V3 shape,
     // T = 4096 and K = 7168, faster than on the tiled kernels)
